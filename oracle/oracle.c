@@ -1,0 +1,172 @@
+/*
+ * oracle.c -- fp64 CPU reference implementation (TEST INFRASTRUCTURE ONLY).
+ *
+ * Written from the pages' definitions, one routine per definition, with no
+ * blocking, chunking or reordering beyond what each definition states.
+ * See oracle.h for the sources, the array conventions and the feature order.
+ * Shares no code with the HIP library.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_features(int d) { return 1 + d + d * d; }
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* [BASED s4 "Taylor Linear Attention"]: 2nd-order Taylor feature map on the
+ * projected dim d.  The input is pre-scaled by d^(-1/4) so that
+ * phi(q).phi(k) = 1 + (q.k)/sqrt(d) + ((q.k)/sqrt(d))^2 / 2. */
+void oracle_taylor_features(const double *x, int d, double *out) {
+    const double pre = pow((double)d, -0.25);
+    const double inv_sqrt2 = 1.0 / sqrt(2.0);
+    out[0] = 1.0;
+    for (int a = 0; a < d; ++a) out[1 + a] = x[a] * pre;
+    for (int a = 0; a < d; ++a)
+        for (int b = 0; b < d; ++b)
+            out[1 + d + a * d + b] = (x[a] * pre) * (x[b] * pre) * inv_sqrt2;
+}
+
+/* [BASED s2] linear attention written as masked pairwise weights, with the
+ * Taylor kernel in closed form (never forms phi).  Normaliser: the sum of
+ * the same weights plus eps ([BASED App. D.4 "State size": denominator). */
+void oracle_la_quadratic(const double *q, const double *k, const double *v,
+                         int BH, int L, int d, int dv, double eps, double *y) {
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < BH; ++h) {
+        const double *qh = q + (size_t)h * L * d;
+        const double *kh = k + (size_t)h * L * d;
+        const double *vh = v + (size_t)h * L * dv;
+        double *yh = y + (size_t)h * L * dv;
+        double *num = (double *)malloc(sizeof(double) * dv);
+        for (int i = 0; i < L; ++i) {
+            double den = 0.0;
+            for (int c = 0; c < dv; ++c) num[c] = 0.0;
+            for (int j = 0; j <= i; ++j) {
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e) dot += qh[(size_t)i * d + e] * kh[(size_t)j * d + e];
+                const double s = dot * inv_sqrt_d;
+                const double a = 1.0 + s + 0.5 * s * s;
+                den += a;
+                for (int c = 0; c < dv; ++c) num[c] += a * vh[(size_t)j * dv + c];
+            }
+            for (int c = 0; c < dv; ++c) yh[(size_t)i * dv + c] = num[c] / (den + eps);
+        }
+        free(num);
+    }
+}
+
+/* One token of the recurrent form on one head: update the state with
+ * (k_t, v_t), then read it out with q_t.  [BASED s2]: constant-memory,
+ * O(1)-per-token generation; [GSA App. A]: S += phi(k) v^T; [BASED App. D.4]:
+ * the K-state z gives the denominator. */
+static void recurrent_token(const double *qt, const double *kt, const double *vt,
+                            int d, int dv, double eps, double *S, double *z,
+                            double *yt, double *phiq, double *phik) {
+    const int F = oracle_num_features(d);
+    oracle_taylor_features(kt, d, phik);
+    oracle_taylor_features(qt, d, phiq);
+    for (int f = 0; f < F; ++f) {
+        z[f] += phik[f];
+        double *Sf = S + (size_t)f * dv;
+        for (int c = 0; c < dv; ++c) Sf[c] += phik[f] * vt[c];
+    }
+    if (!yt) return;
+    double den = 0.0;
+    for (int f = 0; f < F; ++f) den += phiq[f] * z[f];
+    for (int c = 0; c < dv; ++c) {
+        double num = 0.0;
+        for (int f = 0; f < F; ++f) num += phiq[f] * S[(size_t)f * dv + c];
+        yt[c] = num / (den + eps);
+    }
+}
+
+void oracle_la_recurrent(const double *q, const double *k, const double *v,
+                         int BH, int L, int d, int dv, double eps,
+                         const double *S_init, const double *z_init,
+                         double *y, double *S_out, double *z_out) {
+    const int F = oracle_num_features(d);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < BH; ++h) {
+        double *S = (double *)calloc((size_t)F * dv, sizeof(double));
+        double *z = (double *)calloc((size_t)F, sizeof(double));
+        double *phiq = (double *)malloc(sizeof(double) * F);
+        double *phik = (double *)malloc(sizeof(double) * F);
+        if (S_init) memcpy(S, S_init + (size_t)h * F * dv, sizeof(double) * F * dv);
+        if (z_init) memcpy(z, z_init + (size_t)h * F, sizeof(double) * F);
+        for (int t = 0; t < L; ++t) {
+            const size_t tok = (size_t)h * L + t;
+            recurrent_token(q + tok * d, k + tok * d, v + tok * dv, d, dv, eps, S, z,
+                            y ? y + tok * dv : NULL, phiq, phik);
+        }
+        if (S_out) memcpy(S_out + (size_t)h * F * dv, S, sizeof(double) * F * dv);
+        if (z_out) memcpy(z_out + (size_t)h * F, z, sizeof(double) * F);
+        free(S); free(z); free(phiq); free(phik);
+    }
+}
+
+/* [BASED App. B "Next Token Prediction"]: the KV-state update plus readout
+ * for one new token, in place on the caller's state. */
+void oracle_decode_step(const double *q, const double *k, const double *v,
+                        int BH, int d, int dv, double eps,
+                        double *S, double *z, double *y) {
+    const int F = oracle_num_features(d);
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < BH; ++h) {
+        double *phiq = (double *)malloc(sizeof(double) * F);
+        double *phik = (double *)malloc(sizeof(double) * F);
+        recurrent_token(q + (size_t)h * d, k + (size_t)h * d, v + (size_t)h * dv, d, dv, eps,
+                        S + (size_t)h * F * dv, z + (size_t)h * F, y + (size_t)h * dv, phiq, phik);
+        free(phiq); free(phik);
+    }
+}
+
+/* [BASED s4 "Local Exact Attention"]: exact softmax attention over the
+ * preceding `window` keys (the query's own key included), causal. */
+void oracle_swa(const double *q, const double *k, const double *v,
+                int BH, int L, int dqk, int dv, int window, double scale,
+                double *y) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < BH; ++h) {
+        const double *qh = q + (size_t)h * L * dqk;
+        const double *kh = k + (size_t)h * L * dqk;
+        const double *vh = v + (size_t)h * L * dv;
+        double *yh = y + (size_t)h * L * dv;
+        double *logit = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        for (int i = 0; i < L; ++i) {
+            const int j0 = i - window + 1 > 0 ? i - window + 1 : 0;
+            const int n = i - j0 + 1;
+            double m = -INFINITY;
+            for (int jj = 0; jj < n; ++jj) {
+                const int j = j0 + jj;
+                double dot = 0.0;
+                for (int e = 0; e < dqk; ++e) dot += qh[(size_t)i * dqk + e] * kh[(size_t)j * dqk + e];
+                logit[jj] = scale * dot;
+                if (logit[jj] > m) m = logit[jj];
+            }
+            double l = 0.0;
+            for (int jj = 0; jj < n; ++jj) {
+                logit[jj] = exp(logit[jj] - m);
+                l += logit[jj];
+            }
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int jj = 0; jj < n; ++jj) acc += logit[jj] * vh[(size_t)(j0 + jj) * dv + c];
+                yh[(size_t)i * dv + c] = acc / l;
+            }
+        }
+        free(logit);
+    }
+}

@@ -1,0 +1,82 @@
+"""Plant plausible mistakes in a copy of the oracle's C source and check that
+the pins in test_oracle_pins.py catch every one of them.
+
+Each mutant is built from a textual edit of oracle.c in a temporary
+directory (the committed oracle is never touched) and loaded as a separate
+module object.  A mutant "survives" if every pin still passes; the test fails
+if any mutant survives.
+"""
+import importlib.util
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import tests.test_oracle_pins as pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ORACLE_DIR = os.path.join(ROOT, "oracle")
+
+MUTANTS = {
+    "drop_inv_sqrt2": ("(x[a] * pre) * (x[b] * pre) * inv_sqrt2;", "(x[a] * pre) * (x[b] * pre);"),
+    "wrong_prescale": ("pow((double)d, -0.25)", "pow((double)d, -0.5)"),
+    "drop_linear_feature": ("out[1 + a] = x[a] * pre;", "out[1 + a] = 0.0 * x[a];"),
+    "drop_constant_feature": ("out[0] = 1.0;", "out[0] = 0.0;"),
+    "quadratic_exclusive_causal": ("for (int j = 0; j <= i; ++j) {", "for (int j = 0; j < i; ++j) {"),
+    "quadratic_no_half": ("const double a = 1.0 + s + 0.5 * s * s;", "const double a = 1.0 + s + s * s;"),
+    "quadratic_sign": ("const double a = 1.0 + s + 0.5 * s * s;", "const double a = 1.0 - s + 0.5 * s * s;"),
+    "eps_outside": ("num[c] / (den + eps);", "num[c] / den + eps;"),
+    "z_from_query": ("z[f] += phik[f];", "z[f] += phiq[f];"),
+    "state_transposed_value": ("Sf[c] += phik[f] * vt[c];", "Sf[c] += phik[f] * vt[dv - 1 - c];"),
+    "window_one_extra_key": ("const int j0 = i - window + 1 > 0 ? i - window + 1 : 0;",
+                             "const int j0 = i - window > 0 ? i - window : 0;"),
+    "window_no_exp": ("logit[jj] = exp(logit[jj] - m);", "logit[jj] = 1.0 + logit[jj] - m;"),
+}
+
+# pins that take only the oracle module
+PIN_FUNCS = [
+    lambda m: pins.test_p1_features_taylor_limit(m, 16),
+    pins.test_p1_kernel_identity_random,
+    lambda m: pins.test_p2_quadratic_equals_recurrent(m, 37, 64),
+    pins.test_p3_normaliser_state,
+    pins.test_p4_zero_query_is_running_mean,
+    pins.test_p4_constant_values,
+    pins.test_p4_linearity_and_columns,
+    lambda m: pins.test_p5_window_matches_library_softmax(m, 5, 16),
+    pins.test_p5_window_special_cases,
+    pins.test_p6_decode_continues_prefill,
+    pins.test_p7_small_logits_approach_softmax,
+    pins.test_hand_taylor_cases,
+    pins.test_hand_window_cases,
+]
+
+
+def _mutant_module(tmpdir, name, old, new):
+    src = open(os.path.join(ORACLE_DIR, "oracle.c")).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/absent"
+    d = os.path.join(tmpdir, name)
+    os.makedirs(d)
+    shutil.copy(os.path.join(ORACLE_DIR, "oracle.h"), d)
+    shutil.copy(os.path.join(ORACLE_DIR, "__init__.py"), d)
+    with open(os.path.join(d, "oracle.c"), "w") as f:
+        f.write(src.replace(old, new))
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                    os.path.join(d, "oracle.c"), "-o", os.path.join(d, "liboracle.so"), "-lm"], check=True)
+    spec = importlib.util.spec_from_file_location(f"oracle_mutant_{name}", os.path.join(d, "__init__.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_killed(tmp_path, name):
+    old, new = MUTANTS[name]
+    mod = _mutant_module(str(tmp_path), name, old, new)
+    killed_by = []
+    for fn in PIN_FUNCS:
+        try:
+            fn(mod)
+        except AssertionError:
+            killed_by.append(getattr(fn, "__name__", "lambda"))
+    assert killed_by, f"planted mistake {name!r} survived every pin"
