@@ -1,0 +1,321 @@
+"""Throughput of the Taylor linear attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra]
+
+A step is one ``based_prefill`` call over one batch of the workload
+(default: the BASED-360M-shaped prefill layer, B=8, H=16, L=2048, d'=16,
+d_v=64, bf16, chunk 64), inputs already resident in HBM.  Steps cycle over
+four distinct input/output buffer sets so that consecutive steps do not
+re-read the previous step's data from the 256 MB Infinity Cache.  Rank 0
+prints one JSON line with:
+
+* value: tokens/s (tokens = B*L per step, each token covering all H heads);
+* roofline: the prefill kernel's algorithmic bytes per launch / its mean
+  HIP-event duration in the timed loop, against 8 TB/s HBM (the kernel's
+  arithmetic intensity is below the bf16 MFMA ridge), plus its algorithmic
+  flop rate against the 2.5 PFLOP/s dense bf16 MFMA peak; `traffic` comes
+  from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary when that
+  summary was taken on the current kernel source;
+* cpu_baseline: the fp64 oracle (recurrent form) timed on the host cores on
+  a sample of whole heads of the same workload;
+* extra: the next-token step (1.3B-shaped decode, 1024 steps), the w=64
+  window kernel with fused add, and the 64K-token prefill, each with its
+  own HBM roofline fraction.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synthetic_inputs as si  # noqa: E402
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16
+METRIC = "tokens/sec for Taylor lin-attn prefill & decode; % of HBM / MFMA peak"
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "linear_attention_sequence_taylor_amd", "csrc")
+N_SETS = 4
+F = 273
+
+
+# ---------------------------------------------------------------- algorithmic work
+def prefill_bytes(wl) -> int:
+    """q,k,v read once, y written once (fp32), final state written once."""
+    es = 2 if wl.dtype == "bf16" else 4
+    tok_heads = wl.B * wl.H * wl.L
+    per_tok = 2 * wl.d * es + wl.dv * es + wl.dv * 4
+    state = (F * wl.dv + F) * 4
+    return tok_heads * per_tok + wl.B * wl.H * state
+
+
+def prefill_flops(wl) -> int:
+    """Per token-head: 4*F*d_v (state update + readout, 2 flop per MAC) plus
+    the causal on-diagonal term (C+1)*(d'+d_v)."""
+    return wl.B * wl.H * wl.L * (4 * F * wl.dv + (wl.chunk + 1) * (wl.d + wl.dv))
+
+
+def decode_bytes(wl) -> int:
+    es = 2
+    per_head = 2 * (F * wl.dv + F) * 4 + 2 * wl.d * es + wl.dv * es + wl.dv * 4
+    return wl.B * wl.H * per_head
+
+
+def swa_bytes(wl) -> int:
+    es = 2
+    per_tok = 2 * wl.d_qk * es + wl.dv * es + 2 * wl.dv * 4
+    return wl.B * wl.H * wl.L * per_tok
+
+
+# ---------------------------------------------------------------- helpers
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(summary: str, digest: str, launches_per_kernel: int = 1):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
+    if absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256_16") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class EventTimer:
+    """Mean duration of launches bracketed on the current stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        return e0
+
+    def stop(self, e0):
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_s(self) -> float:
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in self.pairs]
+        return sum(ts) / len(ts) / 1e3
+
+
+def make_sets(tensors, n):
+    out = [tuple(t.to("cuda") for t in tensors)]
+    for _ in range(n - 1):
+        out.append(tuple(t.clone() for t in out[0]))
+    return out
+
+
+# ---------------------------------------------------------------- legs
+def bench_prefill(based, wl, steps, warmup):
+    q, k, v = si.linear_inputs(wl)
+    ins = make_sets((q, k, v), N_SETS)
+    outs = []
+    for _ in range(N_SETS):
+        outs.append((torch.empty(wl.B, wl.H, wl.L, wl.dv, device="cuda"),
+                     torch.empty(wl.B, wl.H, F, wl.dv, device="cuda"),
+                     torch.empty(wl.B, wl.H, F, device="cuda")))
+    nbytes = based.based_prefill_workspace_bytes(wl.B, wl.H, wl.L, wl.dv)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step(i, timer=None):
+        (qq, kk, vv), (y, S, z) = ins[i % N_SETS], outs[i % N_SETS]
+        e0 = timer.start() if timer else None
+        based.based_prefill(qq, kk, vv, chunk=wl.chunk, eps=wl.eps, y=y, S=S, z=z, workspace=ws)
+        if timer:
+            timer.stop(e0)
+
+    for i in range(warmup):
+        step(i)
+    timer = EventTimer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / steps, timer.mean_s()
+
+
+def bench_decode(based, wl, n_steps):
+    q, k, v = si.linear_inputs(wl)
+    _, S, z = based.based_prefill(*(t.cuda() for t in (q, k, v)), chunk=wl.chunk, eps=wl.eps)
+    del q, k, v
+    step_in = [tuple(t.cuda() for t in si.decode_inputs(wl, t)) for t in range(n_steps)]
+    y = torch.empty(wl.B, wl.H, wl.dv, device="cuda")
+    for t in range(3):  # warm-up on a copy of the state
+        S2, z2 = S.clone(), z.clone()
+        based.based_decode_step(*step_in[t], S2, z2, eps=wl.eps, y=y)
+    del S2, z2
+    timer = EventTimer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(n_steps):
+        e0 = timer.start()
+        based.based_decode_step(*step_in[t], S, z, eps=wl.eps, y=y)
+        timer.stop(e0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / n_steps, timer.mean_s()
+
+
+def bench_swa(based, wl, reps):
+    q, k, v = si.linear_inputs(wl)
+    qw, kw = si.window_inputs(wl)
+    sets = make_sets((qw, kw, v), 2)
+    del q, k
+    adds = [torch.randn(wl.B, wl.H, wl.L, wl.dv, device="cuda") for _ in range(2)]
+    ys = [torch.empty_like(adds[0]) for _ in range(2)]
+    for i in range(3):
+        based.swa_forward(*sets[i % 2], window=wl.window, scale=wl.swa_scale, add=adds[i % 2], y=ys[i % 2])
+    timer = EventTimer()
+    for i in range(reps):
+        e0 = timer.start()
+        based.swa_forward(*sets[i % 2], window=wl.window, scale=wl.swa_scale, add=adds[i % 2], y=ys[i % 2])
+        timer.stop(e0)
+    return timer.mean_s()
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """Oracle recurrent form on whole heads of the workload, sized to about
+    budget_s of host time (at most the full workload)."""
+    import oracle
+
+    oracle.build()
+    q, k, v = (t.reshape(-1, wl.L, t.shape[-1]) for t in si.linear_inputs(wl))
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    oracle.la_recurrent(q[:2], k[:2], v[:2], eps=wl.eps)  # two heads run on two threads
+    per_head = time.perf_counter() - t0
+    rounds = max(1, int(budget_s / max(per_head, 1e-9)))
+    n_heads = min(q.shape[0], threads * rounds)
+    t0 = time.perf_counter()
+    oracle.la_recurrent(q[:n_heads], k[:n_heads], v[:n_heads], eps=wl.eps)
+    dt = time.perf_counter() - t0
+    tokens = n_heads * wl.L / wl.H  # a token covers all H heads
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_heads} of {q.shape[0]} heads x {wl.L} tokens of {wl.name} "
+                      f"(fp64 recurrent form, OpenMP over heads), {dt:.1f} s; tokens = head-tokens / H"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_360m", choices=["prefill_360m", "long_64k"])
+    ap.add_argument("--no-extra", action="store_true", help="skip decode/window/64K legs")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(every (batch, head) is independent; sharding is described in DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import linear_attention_sequence_taylor_amd as based
+
+    wl = si.WORKLOADS[args.workload]
+    print(f"[bench] workload {wl.name}: {wl.description}", file=sys.stderr, flush=True)
+    step_s, kern_s = bench_prefill(based, wl, args.steps, args.warmup)
+    tokens = wl.B * wl.L
+    abytes, aflops = prefill_bytes(wl), prefill_flops(wl)
+    digest = source_digest("prefill_mfma.hip", "common.hpp")
+    achieved = abytes / kern_s
+    line = {
+        "metric": METRIC,
+        "value": tokens / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1)*scale, bf16-rounded)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d_feat": wl.d,
+                   "d_v": wl.dv, "chunk": wl.chunk, "scale": wl.scale, "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved / 1e9,
+            "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK,
+            "traffic": read_traffic(f"prefill_mfma_{wl.name}_pmc.txt", digest),
+            "kernel": "based_prefill (bf16 MFMA)",
+            "kernel_ms": kern_s * 1e3,
+            "algorithmic_bytes": abytes,
+            "algorithmic_flops": aflops,
+            "mfma_tflops": aflops / kern_s / 1e12,
+            "mfma_frac": aflops / kern_s / MFMA_BF16_PEAK,
+            "kernel_source_sha256_16": digest,
+        },
+    }
+    print(f"[bench] prefill {wl.name}: {kern_s*1e6:.1f} us/launch, {achieved/1e9:.0f} GB/s", file=sys.stderr,
+          flush=True)
+
+    if not args.no_extra:
+        extra = {}
+        wd = si.WORKLOADS["decode_1p3b"]
+        dstep, dkern = bench_decode(based, wd, args.decode_steps)
+        db = decode_bytes(wd)
+        extra["decode_1p3b"] = {
+            "tokens_per_s": wd.B / dstep, "ms_per_step": dstep * 1e3, "kernel_us": dkern * 1e6,
+            "hbm_GBps": db / dkern / 1e9, "hbm_frac": db / dkern / HBM_PEAK, "algorithmic_bytes": db,
+            "steps": args.decode_steps, "note": "1024-token prefill then next-token steps; fp32 state"}
+        print(f"[bench] decode: {dkern*1e6:.1f} us/step, {db/dkern/1e9:.0f} GB/s", file=sys.stderr, flush=True)
+        ww = si.WORKLOADS["window_8k"]
+        skern = bench_swa(based, ww, 20)
+        sb = swa_bytes(ww)
+        extra["window_8k_swa"] = {"tokens_per_s": ww.B * ww.L / skern, "kernel_us": skern * 1e6,
+                                  "hbm_GBps": sb / skern / 1e9, "hbm_frac": sb / skern / HBM_PEAK,
+                                  "algorithmic_bytes": sb}
+        print(f"[bench] swa: {skern*1e6:.1f} us, {sb/skern/1e9:.0f} GB/s", file=sys.stderr, flush=True)
+        if wl.name != "long_64k":
+            wlong = si.WORKLOADS["long_64k"]
+            lstep, lkern = bench_prefill(based, wlong, 10, 2)
+            lb = prefill_bytes(wlong)
+            extra["long_64k_prefill"] = {"tokens_per_s": wlong.B * wlong.L / lstep, "kernel_ms": lkern * 1e3,
+                                         "hbm_GBps": lb / lkern / 1e9, "hbm_frac": lb / lkern / HBM_PEAK,
+                                         "mfma_frac": prefill_flops(wlong) / lkern / MFMA_BF16_PEAK}
+            print(f"[bench] long prefill: {lkern*1e3:.3f} ms", file=sys.stderr, flush=True)
+        line["extra"] = extra
+
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

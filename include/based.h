@@ -1,0 +1,157 @@
+/*
+ * based.h -- C ABI of the MI355X (gfx950) Taylor linear attention library.
+ *
+ * Three operations, as the BASED paper frames inference [1]:
+ *   based_prefill      "prompt processing": causal Taylor linear attention
+ *                      over a whole sequence, returning the outputs and the
+ *                      recurrent state ([1] s5 "Execution stages";
+ *                      App. B "Forward / Generation Prefill").
+ *   based_decode_step  "next-token prediction": one recurrent KV-state update
+ *                      plus readout per head ([1] App. B "Next Token
+ *                      Prediction"; s2 constant-memory, O(1)-per-token
+ *                      generation).
+ *   swa_forward        causal sliding-window softmax attention, each query
+ *                      seeing the preceding `window` keys ([1] s4 "Local
+ *                      Exact Attention"), with an optional fused add of the
+ *                      linear-attention output (BASED pairs the two).
+ *
+ * [1] "Simple linear attention language models balance the recall-throughput
+ *     tradeoff" (arXiv 2402.18668v2).
+ *
+ * Definitions (every routine computes exactly these, up to rounding):
+ *   d' = d_feat = 16.  x~ = x * d'^(-1/4) (the library applies this itself
+ *   to raw q and k).  Taylor features ([1] s4 "Taylor Linear Attention",
+ *   2nd order), F = 1 + d' + d'^2 = 273 rows in this order:
+ *       row 0                     1
+ *       row 1 + a                 x~_a                    a = 0..d'-1
+ *       row 1 + d' + a*d' + b     x~_a * x~_b / sqrt(2)   a-major
+ *   so phi(q).phi(k) = 1 + s + s^2/2 with s = q.k / sqrt(d').
+ *   Linear attention ([1] s2): y_i = sum_{j<=i} phi(q_i).phi(k_j) v_j /
+ *   (sum_{j<=i} phi(q_i).phi(k_j) + eps); the sum of phi(k_j) is the extra
+ *   K-state that gives the denominator ([1] App. D.4 "State size").
+ *   State per (batch, head): S = sum_j phi(k_j) v_j^T  [F x d_v] and
+ *   z = sum_j phi(k_j) [F], both fp32.
+ *
+ * Memory, layout, ownership (all entry points):
+ *   - Every pointer argument is a DEVICE pointer (HIP global memory) unless
+ *     stated otherwise.  The caller allocates, owns and frees every buffer;
+ *     the library never allocates or frees device memory, keeps no pointer
+ *     after a call returns and holds no global state.  Calls are reentrant.
+ *   - Tensors are dense and row-major: [B, H, L, dim] (prefill, window) or
+ *     [B, H, dim] (decode).  Element type of q, k, v is `dtype`; outputs and
+ *     state are always fp32.  Pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued on it asynchronously; no call synchronises the stream.
+ *
+ * Errors: arguments are checked before anything is launched; a bad argument
+ * returns BASED_E_INVALID (malformed) or BASED_E_UNSUPPORTED (well formed
+ * but outside what the kernels implement) and touches no memory.  A failed
+ * kernel launch returns BASED_E_LAUNCH.  Faults during execution surface at
+ * the caller's next synchronisation of `stream`.  NaN/Inf inputs are not
+ * checked; they propagate to the outputs.
+ */
+#ifndef BASED_H
+#define BASED_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BASED_OK = 0,
+    BASED_E_INVALID = 1,     /* null/misaligned pointer, non-positive size, overflow */
+    BASED_E_UNSUPPORTED = 2, /* d_feat, d_v, d_qk, chunk or dtype not implemented */
+    BASED_E_LAUNCH = 3       /* the HIP runtime rejected a kernel launch */
+} based_status_t;
+
+typedef enum { BASED_F32 = 0, BASED_BF16 = 1 } based_dtype_t;
+
+/* Number of Taylor features for feature dim d_feat: 1 + d + d*d (273 for
+ * 16), i.e. the row count of the state S and z.  Returns -1 if d_feat < 1. */
+int based_num_features(int d_feat);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *based_status_string(based_status_t s);
+
+/* Size in bytes of the optional workspace that lets based_prefill split
+ * long sequences into segments processed in parallel (carried states are
+ * combined by a prefix sum over segments).  0 means the call never uses a
+ * workspace for this shape.  Host-only; launches nothing. */
+size_t based_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
+
+/*
+ * based_prefill -- causal Taylor linear attention over a full sequence.
+ * [1] App. B "Forward / Generation Prefill": the sequence is processed in
+ * chunks; within a chunk the masked pairwise weights 1 + s + s^2/2 are used
+ * directly (on-diagonal term), earlier chunks enter through the cumulative
+ * state (off-diagonal term), and the state is carried to the next chunk.
+ *
+ *   q, k   [B,H,L,d_feat] dtype       raw (not pre-scaled) queries/keys
+ *   v      [B,H,L,d_v]    dtype
+ *   chunk  chunk length: 64 (both dtypes); 16 or 32 also for BASED_F32
+ *   eps    denominator guard (1e-6 in BASED layers)
+ *   y      [B,H,L,d_v]    fp32, written
+ *   S      [B,H,F,d_v]    fp32 state; read as the initial state when
+ *   z      [B,H,F]        fp32  use_initial_state != 0 (else zero), and
+ *                               always overwritten with the state after the
+ *                               last token (the handoff to based_decode_step)
+ *   workspace, workspace_bytes  optional scratch (may be NULL/0); see
+ *          based_prefill_workspace_bytes.  With too small a workspace the
+ *          call still runs, without the segment split.
+ * Supported: d_feat = 16; d_v in {64, 128}; L >= 1 (any, not only multiples
+ * of chunk).  y must not alias q, k, v, S or z.
+ */
+based_status_t based_prefill(const void *q, const void *k, const void *v,
+                             based_dtype_t dtype, int B, int H, int L,
+                             int d_feat, int d_v, int chunk, float eps,
+                             float *y, float *S, float *z,
+                             int use_initial_state,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * based_decode_step -- one next-token step for every (batch, head), in
+ * place on the state ([1] App. B "Next Token Prediction"):
+ *   S' = S + phi(k) v^T,  z' = z + phi(k),
+ *   y  = phi(q)^T S' / (phi(q).z' + eps)
+ * (update first, so the current token attends to itself, as in prefill).
+ * Each state element is read once and written once.
+ *
+ *   q, k [B,H,d_feat] dtype;  v [B,H,d_v] dtype
+ *   S    [B,H,F,d_v] fp32 in/out;  z [B,H,F] fp32 in/out
+ *   y    [B,H,d_v]   fp32 out (must not alias the state)
+ * Supported: d_feat = 16; d_v in {64, 128}.
+ */
+based_status_t based_decode_step(const void *q, const void *k, const void *v,
+                                 based_dtype_t dtype, int B, int H,
+                                 int d_feat, int d_v, float eps,
+                                 float *S, float *z, float *y,
+                                 void *stream);
+
+/*
+ * swa_forward -- causal sliding-window softmax attention ([1] s4 "Local
+ * Exact Attention"; O(L*window) work):
+ *   y_i = add_i + sum_{j=max(0,i-window+1)}^{i} e_ij v_j / sum_j e_ij,
+ *   e_ij = exp(scale * q_i.k_j - m_i),  m_i = max_j scale * q_i.k_j.
+ * The window holds `window` keys including the query's own.
+ *
+ *   q, k   [B,H,L,d_qk] dtype;  v [B,H,L,d_v] dtype
+ *   window >= 1 (64 in BASED layers)
+ *   scale  logit scale (1/sqrt(d_qk) for standard attention)
+ *   add    optional [B,H,L,d_v] fp32 added to the output (e.g. the linear
+ *          attention output of the same layer); NULL for none; may equal y
+ *          for an in-place accumulate
+ *   y      [B,H,L,d_v] fp32 out
+ * Supported: d_qk in {16, 64}; d_v = 64; 1 <= window <= 64.
+ */
+based_status_t swa_forward(const void *q, const void *k, const void *v,
+                           based_dtype_t dtype, int B, int H, int L,
+                           int d_qk, int d_v, int window, float scale,
+                           const float *add, float *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BASED_H */

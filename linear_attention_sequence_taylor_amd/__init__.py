@@ -1,0 +1,151 @@
+"""Taylor linear attention (BASED) on MI355X: Python binding of libbased.so.
+
+Thin marshalling over the C ABI in include/based.h: these functions check
+device, dtype, shape and contiguity, allocate outputs with torch (device
+memory only), pass raw pointers and the current HIP stream, and turn a
+status code into an exception.  Every step of the computation runs in the
+HIP kernels of libbased.so; nothing here computes.
+
+    based_prefill(q, k, v)            -> (y, S, z)     prompt processing
+    based_decode_step(q, k, v, S, z)  -> y             next-token step (S, z in place)
+    swa_forward(q, k, v, window=64)   -> y             sliding-window softmax
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+__all__ = ["based_prefill", "based_decode_step", "swa_forward", "based_num_features",
+           "based_prefill_workspace_bytes", "BasedError", "library_path"]
+
+BasedError = _lib.BasedError
+library_path = _lib.LIB_PATH
+D_FEAT = 16
+
+_DTYPES = {torch.float32: _lib.BASED_F32, torch.bfloat16: _lib.BASED_BF16}
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_tensor(name, t, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+
+
+def based_num_features(d_feat: int = D_FEAT) -> int:
+    return _lib.lib().based_num_features(d_feat)
+
+
+def based_prefill_workspace_bytes(B: int, H: int, L: int, d_v: int, d_feat: int = D_FEAT) -> int:
+    return _lib.lib().based_prefill_workspace_bytes(B, H, L, d_feat, d_v)
+
+
+def based_prefill(q, k, v, *, chunk: int = 64, eps: float = 1e-6, initial_state=None,
+                  y=None, S=None, z=None, workspace=None):
+    """Causal Taylor linear attention over [B,H,L,*] inputs.
+
+    Returns (y, S, z): y [B,H,L,d_v] fp32 and the final state S [B,H,273,d_v],
+    z [B,H,273] (fp32).  ``initial_state=(S0, z0)`` starts from a carried
+    state (copied into S, z unless they are the same tensors).  ``workspace``
+    (a uint8 device tensor) enables the segment split for long sequences;
+    by default one is allocated when the shape can use it.
+    """
+    _check_tensor("q", q, ndim=4)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor("k", k, dt, 4)
+    _check_tensor("v", v, dt, 4)
+    B, H, L, d = q.shape
+    d_v = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != (B, H, L):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    F = based_num_features(d)
+    dev = q.device
+    if y is None:
+        y = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev)
+    if S is None:
+        S = torch.empty((B, H, F, d_v), dtype=torch.float32, device=dev)
+    if z is None:
+        z = torch.empty((B, H, F), dtype=torch.float32, device=dev)
+    _check_tensor("y", y, torch.float32)
+    _check_tensor("S", S, torch.float32)
+    _check_tensor("z", z, torch.float32)
+    use_init = 0
+    if initial_state is not None:
+        S0, z0 = initial_state
+        if S0.data_ptr() != S.data_ptr():
+            S.copy_(S0)
+        if z0.data_ptr() != z.data_ptr():
+            z.copy_(z0)
+        use_init = 1
+    if workspace is None:
+        nbytes = based_prefill_workspace_bytes(B, H, L, d_v, d)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    st = _lib.lib().based_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[dt], B, H, L, d,
+                                  d_v, chunk, eps, y.data_ptr(), S.data_ptr(), z.data_ptr(), use_init,
+                                  ws_ptr, ws_bytes, _stream_ptr(dev))
+    _lib.check("based_prefill", st)
+    return y, S, z
+
+
+def based_decode_step(q, k, v, S, z, *, eps: float = 1e-6, y=None):
+    """One next-token step: q,k [B,H,16], v [B,H,d_v]; S [B,H,273,d_v] and
+    z [B,H,273] (fp32) are updated in place.  Returns y [B,H,d_v] fp32."""
+    _check_tensor("q", q, ndim=3)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor("k", k, dt, 3)
+    _check_tensor("v", v, dt, 3)
+    _check_tensor("S", S, torch.float32, 4)
+    _check_tensor("z", z, torch.float32, 3)
+    B, H, d = q.shape
+    d_v = v.shape[-1]
+    if y is None:
+        y = torch.empty((B, H, d_v), dtype=torch.float32, device=q.device)
+    _check_tensor("y", y, torch.float32)
+    st = _lib.lib().based_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[dt], B, H, d,
+                                      d_v, eps, S.data_ptr(), z.data_ptr(), y.data_ptr(),
+                                      _stream_ptr(q.device))
+    _lib.check("based_decode_step", st)
+    return y
+
+
+def swa_forward(q, k, v, *, window: int = 64, scale: float | None = None, add=None, y=None):
+    """Causal sliding-window softmax attention (window keys including self),
+    plus ``add`` (fp32, same shape as the output) if given.  ``add`` may be
+    ``y`` itself for an in-place accumulate.  Returns y [B,H,L,d_v] fp32."""
+    _check_tensor("q", q, ndim=4)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor("k", k, dt, 4)
+    _check_tensor("v", v, dt, 4)
+    B, H, L, d_qk = q.shape
+    d_v = v.shape[-1]
+    if scale is None:
+        scale = d_qk ** -0.5
+    if y is None:
+        y = torch.empty((B, H, L, d_v), dtype=torch.float32, device=q.device)
+    _check_tensor("y", y, torch.float32)
+    if add is not None:
+        _check_tensor("add", add, torch.float32)
+    st = _lib.lib().swa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[dt], B, H, L, d_qk,
+                                d_v, int(window), float(scale), None if add is None else add.data_ptr(),
+                                y.data_ptr(), _stream_ptr(q.device))
+    _lib.check("swa_forward", st)
+    return y

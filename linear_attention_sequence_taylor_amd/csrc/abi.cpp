@@ -1,0 +1,162 @@
+// abi.cpp -- the C ABI of libbased.so (declared in include/based.h).
+//
+// Responsibilities: validate every argument before anything is launched
+// (so a rejected call touches no memory), choose the kernel for the dtype
+// and shape, launch it on the caller's stream, and map the HIP launch status
+// to based_status_t.  No allocation, no synchronisation, no global state.
+#include "based.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+#define BASED_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kDFeatSupported = 16;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Product of non-negative factors with overflow detection (false = overflow).
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
+    if (a != 0 && b > UINT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// Byte ranges [p, p + n) overlap?
+bool overlaps(const void* p, uint64_t n, const void* q, uint64_t m) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + m && b < a + n;
+}
+
+size_t elem_size(based_dtype_t t) { return t == BASED_BF16 ? 2 : 4; }
+
+based_status_t launch_status(hipError_t e) { return e == hipSuccess ? BASED_OK : BASED_E_LAUNCH; }
+
+// Common shape checks; fills element counts.  Returns BASED_OK or an error.
+based_status_t check_dims(int B, int H, int L, uint64_t* BH, uint64_t* BHL) {
+    if (B < 1 || H < 1 || L < 1) return BASED_E_INVALID;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, BH) || *BH > (uint64_t)INT32_MAX) return BASED_E_INVALID;
+    if (!mul_ok(*BH, (uint64_t)L, BHL) || *BHL > ((uint64_t)1 << 40)) return BASED_E_INVALID;
+    return BASED_OK;
+}
+
+}  // namespace
+
+BASED_API int based_num_features(int d_feat) {
+    if (d_feat < 1 || d_feat > 46340) return -1;
+    return 1 + d_feat + d_feat * d_feat;
+}
+
+BASED_API const char* based_status_string(based_status_t s) {
+    switch (s) {
+        case BASED_OK: return "BASED_OK";
+        case BASED_E_INVALID: return "BASED_E_INVALID: malformed argument (null/misaligned pointer, bad size, overlap)";
+        case BASED_E_UNSUPPORTED: return "BASED_E_UNSUPPORTED: shape, dtype or chunk not implemented";
+        case BASED_E_LAUNCH: return "BASED_E_LAUNCH: HIP kernel launch failed";
+    }
+    return "BASED_E_UNKNOWN";
+}
+
+BASED_API size_t based_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v) {
+    uint64_t BH, BHL;
+    if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return 0;
+    if (d_feat != kDFeatSupported || (d_v != 64 && d_v != 128)) return 0;
+    return based::prefill_mfma_workspace_bytes((int)BH, L, d_v);
+}
+
+BASED_API based_status_t based_prefill(const void* q, const void* k, const void* v,
+                                       based_dtype_t dtype, int B, int H, int L, int d_feat,
+                                       int d_v, int chunk, float eps, float* y, float* S, float* z,
+                                       int use_initial_state, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_E_INVALID;
+    if (!q || !k || !v || !y || !S || !z) return BASED_E_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) || !aligned16(S) ||
+        !aligned16(z))
+        return BASED_E_INVALID;
+    if (!isfinite(eps) || chunk < 1 || d_feat < 1 || d_v < 1) return BASED_E_INVALID;
+    uint64_t BH, BHL;
+    if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
+    if (d_feat != kDFeatSupported) return BASED_E_UNSUPPORTED;
+    if (d_v != 64 && d_v != 128) return BASED_E_UNSUPPORTED;
+    const bool bf16 = dtype == BASED_BF16;
+    if (chunk != 64 && (bf16 || (chunk != 16 && chunk != 32))) return BASED_E_UNSUPPORTED;
+
+    const uint64_t es = elem_size(dtype);
+    const uint64_t F = (uint64_t)based_num_features(d_feat);
+    const uint64_t qk_bytes = BHL * d_feat * es, v_bytes = BHL * d_v * es;
+    const uint64_t y_bytes = BHL * d_v * 4, S_bytes = BH * F * d_v * 4, z_bytes = BH * F * 4;
+    if (overlaps(y, y_bytes, q, qk_bytes) || overlaps(y, y_bytes, k, qk_bytes) ||
+        overlaps(y, y_bytes, v, v_bytes) || overlaps(y, y_bytes, S, S_bytes) ||
+        overlaps(y, y_bytes, z, z_bytes) || overlaps(S, S_bytes, z, z_bytes) ||
+        overlaps(S, S_bytes, q, qk_bytes) || overlaps(S, S_bytes, k, qk_bytes) ||
+        overlaps(S, S_bytes, v, v_bytes) || overlaps(z, z_bytes, q, qk_bytes) ||
+        overlaps(z, z_bytes, k, qk_bytes) || overlaps(z, z_bytes, v, v_bytes))
+        return BASED_E_INVALID;
+    if (workspace && !aligned16(workspace)) return BASED_E_INVALID;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int init = use_initial_state ? 1 : 0;
+    if (bf16 && chunk == 64)
+        return launch_status(based::launch_prefill_mfma(q, k, v, (int)BH, L, d_v, eps, y, S, z, init,
+                                                        workspace, workspace_bytes, st));
+    return launch_status(
+        based::launch_prefill_valu(q, k, v, bf16, (int)BH, L, d_v, chunk, eps, y, S, z, init, st));
+}
+
+BASED_API based_status_t based_decode_step(const void* q, const void* k, const void* v,
+                                           based_dtype_t dtype, int B, int H, int d_feat, int d_v,
+                                           float eps, float* S, float* z, float* y, void* stream) {
+    if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_E_INVALID;
+    if (!q || !k || !v || !y || !S || !z) return BASED_E_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) || !aligned16(S) ||
+        !aligned16(z))
+        return BASED_E_INVALID;
+    if (!isfinite(eps) || d_feat < 1 || d_v < 1) return BASED_E_INVALID;
+    uint64_t BH, BHL;
+    if (check_dims(B, H, 1, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
+    if (d_feat != kDFeatSupported) return BASED_E_UNSUPPORTED;
+    if (d_v != 64 && d_v != 128) return BASED_E_UNSUPPORTED;
+    const uint64_t F = (uint64_t)based_num_features(d_feat);
+    const uint64_t S_bytes = BH * F * d_v * 4, z_bytes = BH * F * 4, y_bytes = BH * d_v * 4;
+    if (overlaps(y, y_bytes, S, S_bytes) || overlaps(y, y_bytes, z, z_bytes) ||
+        overlaps(S, S_bytes, z, z_bytes))
+        return BASED_E_INVALID;
+    return launch_status(based::launch_decode_step(q, k, v, dtype == BASED_BF16, (int)BH, d_v, eps,
+                                                   S, z, y, static_cast<hipStream_t>(stream)));
+}
+
+BASED_API based_status_t swa_forward(const void* q, const void* k, const void* v,
+                                     based_dtype_t dtype, int B, int H, int L, int d_qk, int d_v,
+                                     int window, float scale, const float* add, float* y,
+                                     void* stream) {
+    if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_E_INVALID;
+    if (!q || !k || !v || !y) return BASED_E_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
+        (add && !aligned16(add)))
+        return BASED_E_INVALID;
+    if (!isfinite(scale) || window < 1 || d_qk < 1 || d_v < 1) return BASED_E_INVALID;
+    uint64_t BH, BHL;
+    if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
+    if (d_qk != 16 && d_qk != 64) return BASED_E_UNSUPPORTED;
+    if (d_v != 64 || window > 64) return BASED_E_UNSUPPORTED;
+    const uint64_t es = elem_size(dtype);
+    const uint64_t qk_bytes = BHL * d_qk * es, v_bytes = BHL * d_v * es, y_bytes = BHL * d_v * 4;
+    if (overlaps(y, y_bytes, q, qk_bytes) || overlaps(y, y_bytes, k, qk_bytes) ||
+        overlaps(y, y_bytes, v, v_bytes))
+        return BASED_E_INVALID;
+    if (add && add != y && overlaps(add, y_bytes, y, y_bytes)) return BASED_E_INVALID;
+    const uint64_t tiles = (uint64_t)(L + 63) / 64;
+    if (BH * tiles > (uint64_t)INT32_MAX / 2) return BASED_E_INVALID;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == BASED_BF16)
+        return launch_status(
+            based::launch_swa_mfma(q, k, v, (int)BH, L, d_qk, window, scale, add, y, st));
+    return launch_status(
+        based::launch_swa_valu(q, k, v, false, (int)BH, L, d_qk, window, scale, add, y, st));
+}

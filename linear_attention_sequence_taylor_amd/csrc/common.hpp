@@ -1,0 +1,66 @@
+// common.hpp -- small device helpers shared by the gfx950 kernels.
+//
+// Element types: bf16 inputs are handled as raw 16-bit patterns (uint16_t);
+// widening to fp32 is exact (shift into the high half).  Narrowing uses the
+// hardware round-to-nearest-even conversion (v_cvt_pk_bf16_f32 on gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace based {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Taylor feature count for feature dim d: 1 + d + d*d.
+constexpr int kDFeat = 16;
+constexpr int kNumFeat = 1 + kDFeat + kDFeat * kDFeat;  // 273
+// d'^(-1/4) for d' = 16 is exactly 1/2.
+constexpr float kPreScale = 0.5f;
+constexpr float kInvSqrt2 = 0.70710678118654752440f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Widening loads from either element type.
+__device__ __forceinline__ float load_elem(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t* p, size_t i) {
+    return bf16_bits_to_f32(p[i]);
+}
+
+// Round two floats to a packed bf16 pair (RNE), as raw bits (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Value of the low / high bf16 of a packed pair, widened to fp32 (exact).
+__device__ __forceinline__ float bf16lo_f32(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16hi_f32(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// Sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Taylor feature f (0..272) of a pre-scaled vector xs[16], feature order:
+// 0 -> 1; 1+a -> xs[a]; 17+16a+b -> xs[a]*xs[b]/sqrt2.
+__device__ __forceinline__ float taylor_feature(const float* xs, int f) {
+    if (f == 0) return 1.0f;
+    if (f <= kDFeat) return xs[f - 1];
+    const int r = f - 1 - kDFeat;
+    return xs[r >> 4] * xs[r & 15] * kInvSqrt2;
+}
+
+}  // namespace based

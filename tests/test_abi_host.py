@@ -1,0 +1,155 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+* libbased.so loads and exports every function include/based.h declares;
+* argument validation returns the documented status before any launch
+  (every call here is built to fail validation, so no device memory is
+  touched);
+* the product package never imports the oracle and fails loudly when the
+  library is missing.
+"""
+import ast
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "based.h")
+PKG = os.path.join(ROOT, "linear_attention_sequence_taylor_amd")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from linear_attention_sequence_taylor_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from linear_attention_sequence_taylor_amd import build
+
+        build.build(verbose=False)
+    return _lib.lib()
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for want in ("based_prefill", "based_decode_step", "swa_forward", "based_num_features",
+                 "based_prefill_workspace_bytes", "based_status_string"):
+        assert want in names, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from linear_attention_sequence_taylor_amd import _lib
+
+    names = _declared_functions()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in based.h but not exported"
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_num_features_and_strings(lib):
+    assert lib.based_num_features(16) == 273
+    assert lib.based_num_features(8) == 73
+    assert lib.based_num_features(0) == -1
+    for s in range(4):
+        assert lib.based_status_string(s)
+    assert b"UNKNOWN" in lib.based_status_string(99)
+
+
+def test_workspace_bytes_host_only(lib):
+    assert lib.based_prefill_workspace_bytes(1, 1, 256, 16, 64) >= 0
+    assert lib.based_prefill_workspace_bytes(0, 1, 256, 16, 64) == 0
+    assert lib.based_prefill_workspace_bytes(1, 1, 256, 8, 64) == 0
+
+
+# Fake, never-dereferenced device addresses; each call below fails validation.
+A = 0x7F0000000000
+B_ = 0x7F1000000000
+C = 0x7F2000000000
+Y = 0x7F3000000000
+S = 0x7F4000000000
+Z = 0x7F5000000000
+
+
+def _prefill(lib, **kw):
+    a = dict(q=A, k=B_, v=C, dtype=1, B=1, H=1, L=64, d=16, dv=64, chunk=64, eps=1e-6, y=Y, S=S, z=Z,
+             init=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.based_prefill(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["H"], a["L"], a["d"], a["dv"],
+                             a["chunk"], a["eps"], a["y"], a["S"], a["z"], a["init"], a["ws"], a["wsb"],
+                             a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), 1), (dict(y=None), 1), (dict(S=None), 1), (dict(z=None), 1),
+    (dict(q=A + 2), 1), (dict(y=Y + 4), 1),
+    (dict(dtype=7), 1), (dict(B=0), 1), (dict(H=-1), 1), (dict(L=0), 1),
+    (dict(B=1 << 20, H=1 << 20), 1), (dict(chunk=0), 1), (dict(eps=float("nan")), 1),
+    (dict(d=8), 2), (dict(dv=96), 2), (dict(chunk=32), 2), (dict(dtype=0, chunk=48), 2),
+    (dict(y=A), 1), (dict(S=Y), 1), (dict(z=S + 64), 1),
+])
+def test_prefill_rejects(lib, kw, want):
+    assert _prefill(lib, **kw) == want
+
+
+def _decode(lib, **kw):
+    a = dict(q=A, k=B_, v=C, dtype=1, B=2, H=3, d=16, dv=128, eps=1e-6, S=S, z=Z, y=Y, stream=None)
+    a.update(kw)
+    return lib.based_decode_step(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["H"], a["d"], a["dv"],
+                                 a["eps"], a["S"], a["z"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(v=None), 1), (dict(S=S + 8), 1), (dict(B=0), 1), (dict(eps=float("inf")), 1),
+    (dict(d=32), 2), (dict(dv=32), 2), (dict(y=S), 1), (dict(z=S + 16), 1), (dict(dtype=-1), 1),
+])
+def test_decode_rejects(lib, kw, want):
+    assert _decode(lib, **kw) == want
+
+
+def _swa(lib, **kw):
+    a = dict(q=A, k=B_, v=C, dtype=1, B=1, H=2, L=100, dqk=64, dv=64, window=64, scale=0.125, add=None,
+             y=Y, stream=None)
+    a.update(kw)
+    return lib.swa_forward(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["H"], a["L"], a["dqk"],
+                           a["dv"], a["window"], a["scale"], a["add"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(k=None), 1), (dict(add=S + 4), 1), (dict(window=0), 1), (dict(scale=float("nan")), 1),
+    (dict(L=0), 1), (dict(dqk=32), 2), (dict(dv=128), 2), (dict(window=65), 2),
+    (dict(y=A), 1), (dict(add=Y + 256), 1),
+])
+def test_swa_rejects(lib, kw, want):
+    assert _swa(lib, **kw) == want
+
+
+def test_product_never_imports_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for fn in files:
+            if not fn.endswith(".py"):
+                continue
+            tree = ast.parse(open(os.path.join(dirpath, fn)).read())
+            for node in ast.walk(tree):
+                if isinstance(node, ast.Import):
+                    assert not any(a.name.split(".")[0] == "oracle" for a in node.names), fn
+                if isinstance(node, ast.ImportFrom):
+                    assert (node.module or "").split(".")[0] != "oracle", fn
+    for dirpath, _, files in os.walk(os.path.join(PKG, "csrc")):
+        for fn in files:
+            assert "oracle" not in open(os.path.join(dirpath, fn)).read().lower(), fn
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    from linear_attention_sequence_taylor_amd import _lib
+
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libbased.so")
+    with pytest.raises(ImportError):
+        _lib.lib()

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle on
+the same seeded inputs.
+
+Bar (max-abs error as a multiple of the oracle output's RMS over the
+compared tensor): 1e-4 for fp32 inputs, 2e-2 for bf16 inputs.  Full-size
+workloads are run on the GPU exactly as the benchmark launches them; the
+oracle then recomputes a sample of whole (batch, head) pairs, which is exact
+because every (batch, head) is independent.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    oracle.build()
+    import linear_attention_sequence_taylor_amd as based  # noqa: F401  (fails loudly without the .so)
+
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+
+
+def based_mod():
+    import linear_attention_sequence_taylor_amd as based
+
+    return based
+
+
+def ratio(got, want):
+    got = np.asarray(got.detach().cpu().double() if isinstance(got, torch.Tensor) else got, np.float64)
+    want = np.asarray(want, np.float64)
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    return float(np.abs(got - want).max()) / rms
+
+
+def report(name, r, tol):
+    print(f"[parity] {name}: max_err/rms = {r:.3e} (bar {tol:.0e})", flush=True)
+    assert r <= tol, f"{name}: {r:.3e} > {tol:.0e}"
+
+
+def dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+# ---------------------------------------------------------------- prefill
+@pytest.mark.parametrize("L", [1, 17, 63, 64, 65, 130, 1000])
+@pytest.mark.parametrize("dv", [64, 128])
+def test_prefill_bf16_shapes(L, dv):
+    based = based_mod()
+    q, k, v = si.custom((2, 3, L, 16), (2, 3, L, dv), seed=500 + L + dv, scale=0.5)
+    y, S, z = based.based_prefill(*dev(q, k, v))
+    torch.cuda.synchronize()
+    yo, So, zo = oracle.la_recurrent(q, k, v)
+    report(f"prefill bf16 L={L} dv={dv} y", ratio(y, yo), 2e-2)
+    report(f"prefill bf16 L={L} dv={dv} S", ratio(S, So), 2e-2)
+    report(f"prefill bf16 L={L} dv={dv} z", ratio(z, zo), 2e-2)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("dv", [64, 128])
+def test_prefill_f32_chunks(chunk, dv):
+    based = based_mod()
+    q, k, v = si.custom((1, 2, 100, 16), (1, 2, 100, dv), seed=600 + chunk, scale=1.0, dtype=torch.float32)
+    y, S, z = based.based_prefill(*dev(q, k, v), chunk=chunk)
+    yo, So, zo = oracle.la_recurrent(q, k, v)
+    report(f"prefill f32 chunk={chunk} dv={dv} y", ratio(y, yo), 1e-4)
+    report(f"prefill f32 chunk={chunk} dv={dv} S", ratio(S, So), 1e-4)
+    report(f"prefill f32 chunk={chunk} dv={dv} z", ratio(z, zo), 1e-4)
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, 2e-2), (torch.float32, 1e-4)])
+def test_prefill_resume_from_state(dtype, tol):
+    based = based_mod()
+    L1, L2 = 130, 77
+    q, k, v = si.custom((1, 4, L1 + L2, 16), (1, 4, L1 + L2, 64), seed=700, scale=0.5, dtype=dtype)
+    qd, kd, vd = dev(q, k, v)
+    _, S1, z1 = based.based_prefill(qd[:, :, :L1].contiguous(), kd[:, :, :L1].contiguous(),
+                                    vd[:, :, :L1].contiguous())
+    y2, S2, z2 = based.based_prefill(qd[:, :, L1:].contiguous(), kd[:, :, L1:].contiguous(),
+                                     vd[:, :, L1:].contiguous(), initial_state=(S1, z1))
+    yo, So, zo = oracle.la_recurrent(q, k, v)
+    report(f"resume {dtype} y", ratio(y2, yo[:, :, L1:]), tol)
+    report(f"resume {dtype} S", ratio(S2, So), tol)
+    report(f"resume {dtype} z", ratio(z2, zo), tol)
+
+
+def test_prefill_deterministic():
+    based = based_mod()
+    q, k, v = dev(*si.custom((2, 2, 300, 16), (2, 2, 300, 64), seed=800, scale=0.5))
+    a = [t.clone() for t in based.based_prefill(q, k, v)]
+    b = based.based_prefill(q, k, v)
+    for x, w in zip(a, b):
+        assert torch.equal(x, w)
+
+
+# ---------------------------------------------------------------- decode
+@pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, 2e-2), (torch.float32, 1e-4)])
+@pytest.mark.parametrize("dv", [64, 128])
+def test_decode_from_oracle_state(dtype, tol, dv):
+    """One step from a state built by the oracle (independent of prefill)."""
+    based = based_mod()
+    L = 50
+    q, k, v = si.custom((3, 2, L + 1, 16), (3, 2, L + 1, dv), seed=900 + dv, scale=1.0, dtype=dtype)
+    _, S0, z0 = oracle.la_recurrent(q[:, :, :L], k[:, :, :L], v[:, :, :L], want_y=False)
+    S_in = torch.from_numpy(S0).float()
+    z_in = torch.from_numpy(z0).float()
+    S, z = S_in.to(DEV), z_in.to(DEV)
+    qt, kt, vt = (t[:, :, L].contiguous() for t in (q, k, v))
+    y = based.based_decode_step(*dev(qt, kt, vt), S, z)
+    yo, So, zo = oracle.decode_step(qt, kt, vt, S_in, z_in)
+    report(f"decode {dtype} dv={dv} y", ratio(y, yo), tol)
+    report(f"decode {dtype} dv={dv} S", ratio(S, So), tol)
+    report(f"decode {dtype} dv={dv} z", ratio(z, zo), tol)
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, 2e-2), (torch.float32, 1e-4)])
+def test_prefill_then_decode_equals_longer_prefill(dtype, tol):
+    based = based_mod()
+    L1, T = 64 * 3 + 5, 40
+    q, k, v = si.custom((2, 2, L1 + T, 16), (2, 2, L1 + T, 128), seed=1000, scale=1.0, dtype=dtype)
+    qd, kd, vd = dev(q, k, v)
+    _, S, z = based.based_prefill(qd[:, :, :L1].contiguous(), kd[:, :, :L1].contiguous(),
+                                  vd[:, :, :L1].contiguous())
+    ys = []
+    for t in range(L1, L1 + T):
+        ys.append(based.based_decode_step(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(),
+                                          vd[:, :, t].contiguous(), S, z).clone())
+    got = torch.stack(ys, dim=2)
+    yo = oracle.la_quadratic(q, k, v)
+    report(f"prefill+decode {dtype}", ratio(got, yo[:, :, L1:]), tol)
+
+
+# ---------------------------------------------------------------- window
+@pytest.mark.parametrize("dqk", [16, 64])
+@pytest.mark.parametrize("window", [1, 7, 64])
+@pytest.mark.parametrize("L", [1, 50, 64, 129, 300])
+def test_swa_bf16_shapes(dqk, window, L):
+    based = based_mod()
+    q, k, v = si.custom((1, 3, L, dqk), (1, 3, L, 64), seed=1100 + L + window, scale=1.0)
+    scale = dqk ** -0.5
+    y = based.swa_forward(*dev(q, k, v), window=window, scale=scale)
+    report(f"swa bf16 dqk={dqk} w={window} L={L}", ratio(y, oracle.swa(q, k, v, window, scale)), 2e-2)
+
+
+@pytest.mark.parametrize("dqk", [16, 64])
+def test_swa_f32(dqk):
+    based = based_mod()
+    q, k, v = si.custom((2, 2, 200, dqk), (2, 2, 200, 64), seed=1200, scale=1.0, dtype=torch.float32)
+    y = based.swa_forward(*dev(q, k, v), window=64, scale=dqk ** -0.5)
+    report(f"swa f32 dqk={dqk}", ratio(y, oracle.swa(q, k, v, 64, dqk ** -0.5)), 1e-4)
+
+
+def test_swa_add_modes():
+    based = based_mod()
+    q, k, v = si.custom((1, 2, 130, 64), (1, 2, 130, 64), seed=1300, scale=1.0)
+    qd, kd, vd = dev(q, k, v)
+    base = torch.randn(1, 2, 130, 64, generator=torch.Generator().manual_seed(5)).to(DEV)
+    y_plain = based.swa_forward(qd, kd, vd)
+    y_add = based.swa_forward(qd, kd, vd, add=base)
+    y_inplace = base.clone()
+    based.swa_forward(qd, kd, vd, add=y_inplace, y=y_inplace)
+    assert torch.allclose(y_add, y_plain + base, rtol=0, atol=1e-6)
+    assert torch.equal(y_inplace, y_add)
+
+
+# ---------------------------------------------------------------- workloads
+def test_workload_tiny_f32_layer():
+    """B=1,H=1,L=256 fp32: Taylor linear attention + w=64 window, summed."""
+    based = based_mod()
+    wl = si.WORKLOADS["tiny_f32"]
+    q, k, v = si.linear_inputs(wl)
+    qd, kd, vd = dev(q, k, v)
+    want = oracle.la_quadratic(q, k, v, eps=wl.eps) + oracle.swa(q, k, v, wl.window, wl.swa_scale)
+    for chunk in (16, 32, 64):
+        y, _, _ = based.based_prefill(qd, kd, vd, chunk=chunk, eps=wl.eps)
+        based.swa_forward(qd, kd, vd, window=wl.window, scale=wl.swa_scale, add=y, y=y)
+        report(f"tiny_f32 layer chunk={chunk}", ratio(y, want), wl.tol)
+
+
+def _sample_heads(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(B * H, size=min(n, B * H), replace=False)
+    return sorted((int(i) // H, int(i) % H) for i in idx)
+
+
+def test_workload_prefill_360m():
+    based = based_mod()
+    wl = si.WORKLOADS["prefill_360m"]
+    q, k, v = si.linear_inputs(wl)
+    y, S, z = based.based_prefill(*dev(q, k, v), chunk=wl.chunk, eps=wl.eps)
+    torch.cuda.synchronize()
+    heads = _sample_heads(wl.B, wl.H, 16, 1)
+    bi = [b for b, _ in heads]
+    hi = [h for _, h in heads]
+    yo, So, zo = oracle.la_recurrent(q[bi, hi], k[bi, hi], v[bi, hi], eps=wl.eps)
+    report("prefill_360m y (16 sampled heads)", ratio(y[bi, hi], yo), wl.tol)
+    report("prefill_360m S (16 sampled heads)", ratio(S[bi, hi], So), wl.tol)
+
+
+def test_workload_long_64k():
+    based = based_mod()
+    wl = si.WORKLOADS["long_64k"]
+    q, k, v = si.linear_inputs(wl)
+    y, S, z = based.based_prefill(*dev(q, k, v), chunk=wl.chunk, eps=wl.eps)
+    torch.cuda.synchronize()
+    hs = [3, 12]
+    yo, So, zo = oracle.la_recurrent(q[0, hs], k[0, hs], v[0, hs], eps=wl.eps)
+    report("long_64k y (2 sampled heads)", ratio(y[0, hs], yo), wl.tol)
+    report("long_64k S (2 sampled heads)", ratio(S[0, hs], So), wl.tol)
+
+
+def test_workload_window_8k():
+    based = based_mod()
+    wl = si.WORKLOADS["window_8k"]
+    q, k, v = si.linear_inputs(wl)
+    qw, kw = si.window_inputs(wl)
+    qd, kd, vd, qwd, kwd = dev(q, k, v, qw, kw)
+    y, _, _ = based.based_prefill(qd, kd, vd, chunk=wl.chunk, eps=wl.eps)
+    based.swa_forward(qwd, kwd, vd, window=wl.window, scale=wl.swa_scale, add=y, y=y)
+    torch.cuda.synchronize()
+    heads = _sample_heads(wl.B, wl.H, 3, 2)
+    bi = [b for b, _ in heads]
+    hi = [h for _, h in heads]
+    want = oracle.la_recurrent(q[bi, hi], k[bi, hi], v[bi, hi], eps=wl.eps)[0] + oracle.swa(
+        qw[bi, hi], kw[bi, hi], v[bi, hi], wl.window, wl.swa_scale)
+    report("window_8k layer (3 sampled heads)", ratio(y[bi, hi], want), wl.tol)
+
+
+def test_workload_decode_1p3b():
+    """1024-token prefill then 1024 next-token steps; every step's output on
+    8 sampled heads is compared, across all steps at once."""
+    based = based_mod()
+    wl = si.WORKLOADS["decode_1p3b"]
+    q, k, v = si.linear_inputs(wl)
+    _, S, z = based.based_prefill(*dev(q, k, v), chunk=wl.chunk, eps=wl.eps)
+    heads = _sample_heads(wl.B, wl.H, 8, 3)
+    bi = [b for b, _ in heads]
+    hi = [h for _, h in heads]
+    _, So, zo = oracle.la_recurrent(q[bi, hi], k[bi, hi], v[bi, hi], eps=wl.eps, want_y=False)
+    got, want = [], []
+    for t in range(wl.decode_steps):
+        qt, kt, vt = si.decode_inputs(wl, t)
+        y = based.based_decode_step(*dev(qt, kt, vt), S, z, eps=wl.eps)
+        got.append(y[bi, hi].cpu())
+        yo, So, zo = oracle.decode_step(qt[bi, hi], kt[bi, hi], vt[bi, hi], So, zo, eps=wl.eps)
+        want.append(yo)
+    report("decode_1p3b y (8 heads x 1024 steps)", ratio(torch.stack(got), np.stack(want)), wl.tol)
+    report("decode_1p3b final S", ratio(S[bi, hi], So), wl.tol)
