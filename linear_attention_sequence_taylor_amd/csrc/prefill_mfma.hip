@@ -1,12 +1,657 @@
-// prefill_mfma.hip -- placeholder while the MFMA kernel is written: forwards
-// to the vector-ALU path.
+// prefill_mfma.hip -- chunked causal Taylor linear attention on the gfx950
+// matrix cores (bf16 operands, fp32 accumulation), chunk length 64.
+//
+// Method: "Simple linear attention language models balance the
+// recall-throughput tradeoff", App. B "Forward / Generation Prefill" and s5:
+// the feature map and the causal dot product are fused (features never
+// reach HBM); per chunk, the on-diagonal term uses the causally masked
+// pairwise weights, the off-diagonal term reads the cumulative Taylor-order
+// state, and the state is carried to the next chunk ("Gated Slot Attention
+// ...", App. A, chunkwise form, has the same inter/intra split).
+//
+// MI355X design
+//  * One workgroup (4 waves) per (batch, head) walks the chunks in order.
+//    The state lives in MFMA accumulators (fp32) for the whole sequence.
+//  * Symmetric features.  phi(q).phi(k) only needs the 136 distinct
+//    products k_a k_b (a <= b) plus 16 linear terms and the constant:
+//    153 feature rows, padded to 160 = 10 "rotation tiles" of 16 rows.
+//    Tile t < 8 row r holds the pair (r, (r+t) mod 16); tile 8 holds the
+//    pairs (r, r+8) for r < 8 and the constant in row 8; tile 9 holds the
+//    linear terms.  Features are built from raw bf16 values; the pre-scale
+//    d'^(-1/4) = 1/2, the 1/sqrt2 and the pair multiplicity are exact
+//    powers of two (and one 1/sqrt2 pair) folded into the state scaling.
+//  * psi(K)^T (row = feature, 8 tokens per lane) is formed in registers
+//    with DPP row rotations: lane r of a 16-lane row holds k_r of its 8
+//    tokens, and row_ror brings k_(r+t) from lane (r+t) mod 16.
+//  * The normaliser z is an extra 16-column accumulator tile driven by a
+//    ones operand, so phi(q).z and the on-diagonal row sums come out of the
+//    same MFMAs in the same register layout as the numerator.
+//  * Readout of chunk c uses the state before c: after each chunk's update
+//    the owners round the state to bf16 into LDS (double-buffered for
+//    d_v = 64), where every wave reads it as the B operand of
+//    psi(Q) x S.  The linear/constant rows (and the last feature k-step)
+//    are stored as a hi/lo bf16 pair; the on-diagonal weights
+//    1 + s + s^2/2 are used as a hi/lo bf16 pair too (fp32-like precision
+//    where outputs are most sensitive).
+//  * Wave w owns query tile w (16 rows) for the on-diagonal and readout
+//    terms and rotation tiles {w, w+4, w+8} of the state, which balances
+//    the MFMA count across the four waves.
+//  * Q, K, V of chunk c+1 are fetched into registers while chunk c is
+//    computed, then written to the other LDS buffer (V and K transposed).
 #include "common.hpp"
 #include "kernels.hpp"
+
 namespace based {
+namespace {
+
+constexpr int kC = 64;        // chunk length
+constexpr int kSlots = 160;   // 10 rotation tiles x 16 feature rows
+constexpr int kSRow = 168;    // LDS row stride (bf16) of the state operand [col][slot]
+constexpr int kLoSlots = 32;  // slots of the last feature k-step (tiles 8, 9)
+constexpr int kLoRow = 40;    // LDS row stride (bf16) of their lo parts
+constexpr int kTRow = 72;     // LDS row stride (bf16) of V^T and K^T [row][token]
+constexpr int kQRow = 20;     // LDS row stride (bf16) of Q and K [token][dim]
+constexpr float kSqrt2 = 1.41421356237309504880f;
+constexpr uint16_t kBf16One = 0x3F80;
+
+template <int DV>
+struct PrefillSmem {
+    static constexpr int kSBufs = DV == 64 ? 2 : 1;  // state operand buffers
+    alignas(16) uint16_t q[2][kC * kQRow];
+    alignas(16) uint16_t k[2][kC * kQRow];
+    alignas(16) uint16_t kt[2][kDFeat * kTRow];
+    alignas(16) uint16_t vt[2][DV * kTRow];
+    alignas(16) uint16_t s_hi[kSBufs][DV * kSRow];
+    alignas(16) uint16_t s_lo[kSBufs][DV * kLoRow];
+    alignas(16) uint16_t z_hi[kSBufs][kSlots];
+    alignas(16) uint16_t z_lo[kSBufs][kLoSlots];
+};
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Value of lane (r - N) mod 16 of this lane's 16-lane row.
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float (&a)[8]) {
+    u32x4 u = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
+               pack_bf16x2(a[6], a[7])};
+    return __builtin_bit_cast(bf16x8, u);
+}
+// hi = bf16(a), lo = bf16(a - hi): a ~= hi + lo to ~16 mantissa bits.
+__device__ __forceinline__ void pack8_hilo(const float (&a)[8], bf16x8& hi, bf16x8& lo) {
+    float l[8];
+    u32x4 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t p = pack_bf16x2(a[2 * i], a[2 * i + 1]);
+        h[i] = p;
+        l[2 * i] = a[2 * i] - bf16lo_f32(p);
+        l[2 * i + 1] = a[2 * i + 1] - bf16hi_f32(p);
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = pack8(l);
+}
+__device__ __forceinline__ void unpack8(const u32x4& u, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16lo_f32(u[i]);
+        x[2 * i + 1] = bf16hi_f32(u[i]);
+    }
+}
+__device__ __forceinline__ bf16x8 lds_bf16x8(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ bf16x4 lds_bf16x4(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(p));
+}
+__device__ __forceinline__ bf16x8 join44(const uint16_t* p0, const uint16_t* p1) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p0);
+    const uint2 b = *reinterpret_cast<const uint2*>(p1);
+    u32x4 u = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8, u);
+}
+// 1/x: hardware reciprocal refined by one Newton step (~0.5 ulp).
+__device__ __forceinline__ float fast_rcp(float x) {
+    const float r = __builtin_amdgcn_rcpf(x);
+    return fmaf(r, fmaf(-x, r, 1.f), r);
+}
+__device__ __forceinline__ bf16x8 ones8() {
+    u32x4 u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// Readout slot of rotation tile T, rows 4g..4g+3 (4 consecutive slots).
+template <int T>
+__device__ __forceinline__ int readout_slot(int g) {
+    constexpr int j = T >> 1;
+    return (T & 1) ? 32 * j + 8 * ((g + 3) & 3) + 4 : 32 * j + 8 * g;
+}
+
+// ---------------------------------------------------------------- 273-row state map
+// Rows of the caller's state for rotation tile T, row r.  Returns the
+// number of rows (0, 1 or 2: a pair a != b has two mirror rows).
+template <int T>
+__device__ __forceinline__ int state_rows(int r, int& r0, int& r1) {
+    if (T == 9) { r0 = 1 + r; return 1; }
+    if (T == 8 && r == 8) { r0 = 0; return 1; }
+    if (T == 8 && r > 8) return 0;
+    const int a = r, b = (r + T) & 15;
+    r0 = 1 + kDFeat + a * kDFeat + b;
+    r1 = 1 + kDFeat + b * kDFeat + a;
+    return T == 0 ? 1 : 2;
+}
+// ---------------------------------------------------------------- feature operands
+// psi(Q) for readout k-step J: lane (query row, group g) holds slots
+// 32J + 8g + i, i.e. rotation tile 2J + (i>>2), row (4g + i) mod 16.
+// qr[m] = raw q_((4g + m) mod 16) of the lane's query.
+template <int J>
+__device__ __forceinline__ void psi_q(const float (&qr)[16], int g, float (&a)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int T = 2 * J + (i >> 2);
+        if (T == 0) {
+            a[i] = qr[i] * qr[i];
+        } else if (T < 8) {
+            a[i] = qr[i] * qr[(i + T) & 15];
+        } else if (T == 8) {
+            const float p = qr[i] * qr[(i + 8) & 15];
+            a[i] = g < 2 ? p : ((g == 2 && i == 0) ? 1.f : 0.f);
+        } else {
+            a[i] = qr[i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- per-wave bodies
+// Accumulators hold the state in readout units (the k pre-scale 1/4, the
+// 1/sqrt2 of the diagonal and the pair multiplicity are folded in when the
+// features of K are formed), so publishing the state operand is a plain
+// rounding to bf16.  state_scale converts to the caller's 273-row units
+// (one mirror row of a pair).
+template <int T>
+__device__ __forceinline__ float state_scale(int r) {
+    if (T == 0) return 4.f * kSqrt2;
+    if (T == 9) return 2.f;
+    if (T == 8 && r == 8) return 1.f;
+    return 2.f * kSqrt2;
+}
+
+template <int T, int DV>
+__device__ __forceinline__ void publish_state(const f32x4 (&acc)[DV / 16 + 1], PrefillSmem<DV>& sm,
+                                              int sbuf, int g, int r) {
+    constexpr int kNV = DV / 16;
+    const int slot = readout_slot<T>(g);
+#pragma unroll
+    for (int ct = 0; ct <= kNV; ++ct) {
+        if (ct == kNV && r != 0) continue;  // the normaliser tile has 16 equal columns
+        const uint32_t h01 = pack_bf16x2(acc[ct][0], acc[ct][1]);
+        const uint32_t h23 = pack_bf16x2(acc[ct][2], acc[ct][3]);
+        uint2* hi = ct < kNV ? reinterpret_cast<uint2*>(&sm.s_hi[sbuf][(16 * ct + r) * kSRow + slot])
+                             : reinterpret_cast<uint2*>(&sm.z_hi[sbuf][slot]);
+        *hi = make_uint2(h01, h23);
+        if (T >= 8) {
+            const uint32_t l01 = pack_bf16x2(acc[ct][0] - bf16lo_f32(h01), acc[ct][1] - bf16hi_f32(h01));
+            const uint32_t l23 = pack_bf16x2(acc[ct][2] - bf16lo_f32(h23), acc[ct][3] - bf16hi_f32(h23));
+            uint2* lo = ct < kNV ? reinterpret_cast<uint2*>(&sm.s_lo[sbuf][(16 * ct + r) * kLoRow + slot - 128])
+                                 : reinterpret_cast<uint2*>(&sm.z_lo[sbuf][slot - 128]);
+            *lo = make_uint2(l01, l23);
+        }
+    }
+}
+
+template <int T, int DV>
+__device__ __forceinline__ void load_initial(f32x4 (&acc)[DV / 16 + 1], const float* Sh, const float* zh,
+                                             int g, int r) {
+    constexpr int kNV = DV / 16;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        int r0 = 0, r1 = 0;
+        const int n = state_rows<T>(4 * g + m, r0, r1);
+        const float inv = 1.f / state_scale<T>(4 * g + m);
+#pragma unroll
+        for (int ct = 0; ct <= kNV; ++ct) {
+            float x = 0.f;
+            if (n > 0) {
+                if (ct < kNV) {
+                    const int col = 16 * ct + r;
+                    x = Sh[(size_t)r0 * DV + col];
+                    if (n == 2) x = 0.5f * (x + Sh[(size_t)r1 * DV + col]);
+                } else {
+                    x = zh[r0];
+                    if (n == 2) x = 0.5f * (x + zh[r1]);
+                }
+            }
+            acc[ct][m] = x * inv;
+        }
+    }
+}
+
+template <int T, int DV>
+__device__ __forceinline__ void store_final(const f32x4 (&acc)[DV / 16 + 1], float* Sh, float* zh,
+                                            int use_init, int g, int r) {
+    constexpr int kNV = DV / 16;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        int r0 = 0, r1 = 0;
+        const int n = state_rows<T>(4 * g + m, r0, r1);
+        if (n == 0) continue;
+        const float sc = state_scale<T>(4 * g + m);
+#pragma unroll
+        for (int ct = 0; ct <= kNV; ++ct) {
+            if (ct == kNV && r != 0) continue;
+            float* base = ct < kNV ? Sh + 16 * ct + r : zh;
+            const size_t stride = ct < kNV ? (size_t)DV : 1;
+            if (!use_init) {
+                base[r0 * stride] = acc[ct][m] * sc;
+                if (n == 2) base[r1 * stride] = acc[ct][m] * sc;
+            } else {
+                // Initial rows were folded in as their symmetric mean; add
+                // only this call's increment so an asymmetric initial state
+                // keeps its antisymmetric part.
+                const float x0 = base[r0 * stride];
+                const float x1 = n == 2 ? base[r1 * stride] : x0;
+                const float mean = n == 2 ? 0.5f * (x0 + x1) : x0;
+                const float inc = acc[ct][m] * sc - mean;
+                base[r0 * stride] = x0 + inc;
+                if (n == 2) base[r1 * stride] = x1 + inc;
+            }
+        }
+    }
+}
+
+// psi(K)^T for rotation tile T: lane (row r, group g) holds feature row r
+// for 8 tokens; kv[] = k_r / 4 of those tokens.
+template <int T>
+__device__ __forceinline__ bf16x8 psi_k(const float (&kv)[8], int r, const float (&valid)[8]) {
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (T == 0) {
+            a[i] = (0.5f * kv[i]) * kv[i];
+        } else if (T < 8) {
+            a[i] = kv[i] * row_ror<16 - T>(kv[i]);
+        } else if (T == 8) {
+            const float p = kv[i] * row_ror<8>(kv[i]);
+            a[i] = r < 8 ? p : (r == 8 ? valid[i] : 0.f);
+        } else {
+            a[i] = kv[i];
+        }
+    }
+    return pack8(a);
+}
+
+// ---- staging split: readout waves stage Q and K (+K^T), update waves V^T.
+struct QKStage {
+    u32x4 a0, a1;
+};
+template <int DV>
+struct VStage {
+    static constexpr int kPass = DV / 64;
+    u32x4 v0[kPass], v1[kPass];
+};
+
+__device__ __forceinline__ u32x4 keep_if(const u32x4& x, bool ok) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = ok ? x[i] : 0u;
+    return r;
+}
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+// Unconditional 16-byte loads: rows past the end are clamped to the last
+// row and zeroed when stored, so no branch sits between prefetch and use.
+// t (0..127 of the readout waves): t < 64 loads K, else Q; token pair
+// p = t & 31, dims 8*((t >> 5) & 1) .. +8.
+__device__ __forceinline__ void qk_load(QKStage& st, const uint16_t* qh, const uint16_t* kh, int t0, int L,
+                                        int t) {
+    const int p = t & 31;
+    const int ta = min(t0 + 2 * p, L - 1), tb = min(t0 + 2 * p + 1, L - 1);
+    const uint16_t* src = t < 64 ? kh : qh;
+    const int db = (t >> 5) & 1;
+    st.a0 = *reinterpret_cast<const u32x4*>(src + (size_t)ta * kDFeat + 8 * db);
+    st.a1 = *reinterpret_cast<const u32x4*>(src + (size_t)tb * kDFeat + 8 * db);
+}
+template <int DV>
+__device__ __forceinline__ void qk_store(const QKStage& in, PrefillSmem<DV>& sm, int buf, int t0, int L, int t) {
+    const int p = t & 31;
+    const u32x4 a0 = keep_if(in.a0, t0 + 2 * p < L), a1 = keep_if(in.a1, t0 + 2 * p + 1 < L);
+    const int db = (t >> 5) & 1;
+    uint16_t* rowm = t < 64 ? &sm.k[buf][0] : &sm.q[buf][0];
+    uint2* ra = reinterpret_cast<uint2*>(rowm + (2 * p) * kQRow + 8 * db);
+    uint2* rb = reinterpret_cast<uint2*>(rowm + (2 * p + 1) * kQRow + 8 * db);
+    ra[0] = make_uint2(a0[0], a0[1]);
+    ra[1] = make_uint2(a0[2], a0[3]);
+    rb[0] = make_uint2(a1[0], a1[1]);
+    rb[1] = make_uint2(a1[2], a1[3]);
+    if (t < 64) {
+        uint32_t* kt = reinterpret_cast<uint32_t*>(&sm.kt[buf][0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kt[((8 * db + 2 * e) * kTRow + 2 * p) >> 1] = lo_pair(a0[e], a1[e]);
+            kt[((8 * db + 2 * e + 1) * kTRow + 2 * p) >> 1] = hi_pair(a0[e], a1[e]);
+        }
+    }
+}
+// u (0..255 of the update waves): token pair p = u & 31, column blocks
+// (u >> 5) + 8*pass of 8 columns.
+template <int DV>
+__device__ __forceinline__ void v_load(VStage<DV>& st, const uint16_t* vh, int t0, int L, int u) {
+    const int p = u & 31;
+    const int ta = min(t0 + 2 * p, L - 1), tb = min(t0 + 2 * p + 1, L - 1);
+#pragma unroll
+    for (int ps = 0; ps < VStage<DV>::kPass; ++ps) {
+        const int cb = (u >> 5) + 8 * ps;
+        st.v0[ps] = *reinterpret_cast<const u32x4*>(vh + (size_t)ta * DV + 8 * cb);
+        st.v1[ps] = *reinterpret_cast<const u32x4*>(vh + (size_t)tb * DV + 8 * cb);
+    }
+}
+template <int DV>
+__device__ __forceinline__ void v_store(const VStage<DV>& st, PrefillSmem<DV>& sm, int buf, int t0, int L, int u) {
+    const int p = u & 31;
+    const bool oka = t0 + 2 * p < L, okb = t0 + 2 * p + 1 < L;
+    uint32_t* vt = reinterpret_cast<uint32_t*>(&sm.vt[buf][0]);
+#pragma unroll
+    for (int ps = 0; ps < VStage<DV>::kPass; ++ps) {
+        const int cb = (u >> 5) + 8 * ps;
+        const u32x4 v0 = keep_if(st.v0[ps], oka), v1 = keep_if(st.v1[ps], okb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vt[((8 * cb + 2 * e) * kTRow + 2 * p) >> 1] = lo_pair(v0[e], v1[e]);
+            vt[((8 * cb + 2 * e + 1) * kTRow + 2 * p) >> 1] = hi_pair(v0[e], v1[e]);
+        }
+    }
+}
+
+// ---- readout wave W: query tile W (rows 16W..16W+15) of every chunk.
+template <int W, int DV>
+__device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, const uint16_t* __restrict__ kh,
+                                             int L, float eps, float* __restrict__ yh, PrefillSmem<DV>& sm) {
+    constexpr int kNV = DV / 16, kNCT = kNV + 1;
+    constexpr int kSBufs = PrefillSmem<DV>::kSBufs;
+    const int t = threadIdx.x;  // 0..255
+    const int lane = t & 63, g = lane >> 4, r = lane & 15;
+    const int nchunks = (L + kC - 1) / kC;
+    const bool stager = t < 128;
+
+    QKStage st;
+    if (stager) {
+        qk_load(st, qh, kh, 0, L, t);
+        qk_store<DV>(st, sm, 0, 0, L, t);
+        if (nchunks > 1) qk_load(st, qh, kh, kC, L, t);
+    }
+    __syncthreads();
+
+    const bf16x8 ones = ones8();
+    for (int c = 0; c < nchunks; ++c) {
+        const int buf = c & 1;
+        const int sbuf = kSBufs == 2 ? buf : 0;
+        const int t0 = c * kC;
+        const int n = min(kC, L - t0);
+        const uint16_t* q_l = &sm.q[buf][0];
+        const uint16_t* k_l = &sm.k[buf][0];
+        const uint16_t* vt_l = &sm.vt[buf][0];
+
+        f32x4 y[kNCT];
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct) y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // ---- on-diagonal term: s^T for key tiles 0..W, weights 1+s+s^2/2
+        {
+            const bf16x4 qb = lds_bf16x4(q_l + (16 * W + r) * kQRow + 4 * g);
+            float wgt[W + 1][4];
+#pragma unroll
+            for (int j = 0; j <= W; ++j) {
+                const bf16x4 ka = lds_bf16x4(k_l + (16 * j + r) * kQRow + 4 * g);
+                const f32x4 s = mfma16(ka, qb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    // s[m] = q_query . k_key (raw), key = 16j + 4g + m, query = 16W + r
+                    const float w = fmaf(s[m], fmaf(s[m], 1.f / 32.f, 0.25f), 1.f);
+                    wgt[j][m] = (j == W && 4 * g + m > r) ? 0.f : w;
+                }
+            }
+#pragma unroll
+            for (int p = 0; p <= W / 2; ++p) {
+                float a[8];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    a[m] = wgt[2 * p][m];
+                    a[4 + m] = (2 * p + 1 <= W) ? wgt[(2 * p + 1 <= W) ? 2 * p + 1 : 0][m] : 0.f;
+                }
+                bf16x8 ahi, alo;
+                pack8_hilo(a, ahi, alo);
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) {
+                    const uint16_t* vrow = vt_l + (16 * ct + r) * kTRow + 32 * p;
+                    const bf16x8 vb = join44(vrow + 4 * g, vrow + 16 + 4 * g);
+                    y[ct] = mfma32(ahi, vb, y[ct]);
+                    y[ct] = mfma32(alo, vb, y[ct]);
+                }
+                y[kNV] = mfma32(ahi, ones, y[kNV]);
+                y[kNV] = mfma32(alo, ones, y[kNV]);
+            }
+        }
+
+        // ---- off-diagonal term: psi(Q) x (state before this chunk)
+        {
+            float qr[16];
+            const uint16_t* qrow = q_l + (16 * W + r) * kQRow;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const uint2 u = *reinterpret_cast<const uint2*>(qrow + 4 * ((g + cc) & 3));
+                qr[4 * cc + 0] = bf16lo_f32(u.x);
+                qr[4 * cc + 1] = bf16hi_f32(u.x);
+                qr[4 * cc + 2] = bf16lo_f32(u.y);
+                qr[4 * cc + 3] = bf16hi_f32(u.y);
+            }
+            const uint16_t* shi = &sm.s_hi[sbuf][0];
+            const uint16_t* slo = &sm.s_lo[sbuf][0];
+#define BASED_READOUT_STEP(J)                                                                   \
+    {                                                                                          \
+        float a[8];                                                                            \
+        psi_q<J>(qr, g, a);                                                                    \
+        bf16x8 ahi, alo;                                                                       \
+        if (J == 4) pack8_hilo(a, ahi, alo); else ahi = pack8(a);                              \
+        _Pragma("unroll") for (int ct = 0; ct < kNV; ++ct) {                                   \
+            const uint16_t* srow = shi + (16 * ct + r) * kSRow + 32 * (J) + 8 * g;             \
+            const bf16x8 sb = lds_bf16x8(srow);                                                \
+            y[ct] = mfma32(ahi, sb, y[ct]);                                                    \
+            if (J == 4) {                                                                      \
+                y[ct] = mfma32(ahi, lds_bf16x8(slo + (16 * ct + r) * kLoRow + 8 * g), y[ct]); \
+                y[ct] = mfma32(alo, sb, y[ct]);                                                \
+            }                                                                                  \
+        }                                                                                      \
+        const bf16x8 zb = lds_bf16x8(&sm.z_hi[sbuf][32 * (J) + 8 * g]);                        \
+        y[kNV] = mfma32(ahi, zb, y[kNV]);                                                      \
+        if (J == 4) {                                                                          \
+            y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_lo[sbuf][8 * g]), y[kNV]);                   \
+            y[kNV] = mfma32(alo, zb, y[kNV]);                                                  \
+        }                                                                                      \
+    }
+            BASED_READOUT_STEP(0)
+            BASED_READOUT_STEP(1)
+            BASED_READOUT_STEP(2)
+            BASED_READOUT_STEP(3)
+            BASED_READOUT_STEP(4)
+#undef BASED_READOUT_STEP
+        }
+
+        // ---- stage the next chunk's Q/K (loaded one chunk ago) and start
+        // loading the one after, before this chunk's output stores: loads
+        // and stores retire through one in-order counter, so the next wait
+        // for these loads must not also wait for the stores.
+        if (stager && c + 1 < nchunks) {
+            qk_store<DV>(st, sm, buf ^ 1, t0 + kC, L, t);
+            if (c + 2 < nchunks) qk_load(st, qh, kh, t0 + 2 * kC, L, t);
+        }
+
+        // ---- normalise and store this chunk's outputs (rows 16W + 4g + m)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int tq = 16 * W + 4 * g + m;
+            if (tq < n) {
+                const float inv = fast_rcp(y[kNV][m] + eps);
+                float* yrow = yh + (size_t)(t0 + tq) * DV + r;
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) yrow[16 * ct] = y[ct][m] * inv;
+            }
+        }
+        if (kSBufs == 1) __syncthreads();  // readouts done: the state operand may be overwritten
+        __syncthreads();
+    }
+}
+
+// ---- update wave U: state rotation tiles U, U+4 (, U+8).
+template <int U, int DV>
+__device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int L, float* __restrict__ Sh,
+                                            float* __restrict__ zh, int use_init, PrefillSmem<DV>& sm) {
+    constexpr int kNV = DV / 16, kNCT = kNV + 1;
+    constexpr int kNT = U < 2 ? 3 : 2;
+    constexpr int kSBufs = PrefillSmem<DV>::kSBufs;
+    const int u = threadIdx.x - 256;  // 0..255
+    const int lane = u & 63, g = lane >> 4, r = lane & 15;
+    const int nchunks = (L + kC - 1) / kC;
+
+    f32x4 acc[kNT][kNCT];
+#pragma unroll
+    for (int ti = 0; ti < kNT; ++ti)
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct) acc[ti][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (use_init) {
+        load_initial<U, DV>(acc[0], Sh, zh, g, r);
+        load_initial<U + 4, DV>(acc[1], Sh, zh, g, r);
+        if constexpr (kNT == 3) load_initial<U + 8, DV>(acc[2], Sh, zh, g, r);
+    }
+
+    VStage<DV> st;
+    v_load<DV>(st, vh, 0, L, u);
+    v_store<DV>(st, sm, 0, 0, L, u);
+    if (nchunks > 1) v_load<DV>(st, vh, kC, L, u);
+    publish_state<U, DV>(acc[0], sm, 0, g, r);
+    publish_state<U + 4, DV>(acc[1], sm, 0, g, r);
+    if constexpr (kNT == 3) publish_state<U + 8, DV>(acc[2], sm, 0, g, r);
+    __syncthreads();
+
+    const bf16x8 ones = ones8();
+    for (int c = 0; c < nchunks; ++c) {
+        const int buf = c & 1;
+        const int t0 = c * kC;
+        const int n = min(kC, L - t0);
+        const uint16_t* kt_l = &sm.kt[buf][0];
+        const uint16_t* vt_l = &sm.vt[buf][0];
+
+        // ---- S += psi(K)^T V, z += psi(K)^T 1 over this chunk's 64 tokens
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            float kv[8], valid[8];
+            const u32x4 ku = *reinterpret_cast<const u32x4*>(kt_l + r * kTRow + 32 * s + 8 * g);
+            unpack8(ku, kv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                kv[i] *= 0.25f;
+                valid[i] = (32 * s + 8 * g + i < n) ? 1.f : 0.f;
+            }
+            bf16x8 vb[kNV];
+#pragma unroll
+            for (int ct = 0; ct < kNV; ++ct)
+                vb[ct] = lds_bf16x8(vt_l + (16 * ct + r) * kTRow + 32 * s + 8 * g);
+            {
+                const bf16x8 a = psi_k<U>(kv, r, valid);
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) acc[0][ct] = mfma32(a, vb[ct], acc[0][ct]);
+                acc[0][kNV] = mfma32(a, ones, acc[0][kNV]);
+            }
+            {
+                const bf16x8 a = psi_k<U + 4>(kv, r, valid);
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) acc[1][ct] = mfma32(a, vb[ct], acc[1][ct]);
+                acc[1][kNV] = mfma32(a, ones, acc[1][kNV]);
+            }
+            if constexpr (kNT == 3) {
+                const bf16x8 a = psi_k<U + 8>(kv, r, valid);
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) acc[2][ct] = mfma32(a, vb[ct], acc[2][ct]);
+                acc[2][kNV] = mfma32(a, ones, acc[2][kNV]);
+            }
+        }
+
+        // ---- stage the next chunk's V^T, start loading the one after
+        if (c + 1 < nchunks) {
+            v_store<DV>(st, sm, buf ^ 1, t0 + kC, L, u);
+            if (c + 2 < nchunks) v_load<DV>(st, vh, t0 + 2 * kC, L, u);
+        }
+
+        // ---- publish the state after this chunk for the next readout
+        if (kSBufs == 1) __syncthreads();  // wait until every readout of this chunk is done
+        const int wbuf = kSBufs == 2 ? (buf ^ 1) : 0;
+        publish_state<U, DV>(acc[0], sm, wbuf, g, r);
+        publish_state<U + 4, DV>(acc[1], sm, wbuf, g, r);
+        if constexpr (kNT == 3) publish_state<U + 8, DV>(acc[2], sm, wbuf, g, r);
+        __syncthreads();
+    }
+
+    store_final<U, DV>(acc[0], Sh, zh, use_init, g, r);
+    store_final<U + 4, DV>(acc[1], Sh, zh, use_init, g, r);
+    if constexpr (kNT == 3) store_final<U + 8, DV>(acc[2], Sh, zh, use_init, g, r);
+}
+
+template <int DV>
+__global__ __launch_bounds__(512, 1) void prefill_mfma_kernel(const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v, int L,
+                                                              float eps, float* __restrict__ y,
+                                                              float* __restrict__ S,
+                                                              float* __restrict__ z, int use_init) {
+    __shared__ PrefillSmem<DV> sm;
+    const int head = blockIdx.x;
+    const uint16_t* qh = q + (size_t)head * L * kDFeat;
+    const uint16_t* kh = k + (size_t)head * L * kDFeat;
+    const uint16_t* vh = v + (size_t)head * L * DV;
+    float* yh = y + (size_t)head * L * DV;
+    float* Sh = S + (size_t)head * kNumFeat * DV;
+    float* zh = z + (size_t)head * kNumFeat;
+    // Waves 0-3 and 4-7 land on SIMDs 0-3 in pairs; readout wave W shares
+    // its SIMD with update wave W (the lighter on-diagonal work of W = 0, 1
+    // pairs with the three-tile update waves).
+    switch (threadIdx.x >> 6) {
+        case 0: readout_wave<0, DV>(qh, kh, L, eps, yh, sm); break;
+        case 1: readout_wave<1, DV>(qh, kh, L, eps, yh, sm); break;
+        case 2: readout_wave<2, DV>(qh, kh, L, eps, yh, sm); break;
+        case 3: readout_wave<3, DV>(qh, kh, L, eps, yh, sm); break;
+        case 4: update_wave<0, DV>(vh, L, Sh, zh, use_init, sm); break;
+        case 5: update_wave<1, DV>(vh, L, Sh, zh, use_init, sm); break;
+        case 6: update_wave<2, DV>(vh, L, Sh, zh, use_init, sm); break;
+        default: update_wave<3, DV>(vh, L, Sh, zh, use_init, sm); break;
+    }
+}
+
+}  // namespace
+
 size_t prefill_mfma_workspace_bytes(int, int, int) { return 0; }
+
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int BH, int L, int dv,
                                float eps, float* y, float* S, float* z, int use_init, void*, size_t,
                                hipStream_t st) {
-    return launch_prefill_valu(q, k, v, true, BH, L, dv, 64, eps, y, S, z, use_init, st);
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const uint16_t* kk = static_cast<const uint16_t*>(k);
+    const uint16_t* vv = static_cast<const uint16_t*>(v);
+    if (dv == 64)
+        hipLaunchKernelGGL((prefill_mfma_kernel<64>), dim3(BH), dim3(512), 0, st, qq, kk, vv, L, eps, y, S,
+                           z, use_init);
+    else
+        hipLaunchKernelGGL((prefill_mfma_kernel<128>), dim3(BH), dim3(512), 0, st, qq, kk, vv, L, eps, y,
+                           S, z, use_init);
+    return hipGetLastError();
 }
+
 }  // namespace based
