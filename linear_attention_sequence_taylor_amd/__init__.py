@@ -90,7 +90,7 @@ def based_prefill(q, k, v, *, chunk: int = 64, eps: float = 1e-6, initial_state=
         if z0.data_ptr() != z.data_ptr():
             z.copy_(z0)
         use_init = 1
-    if workspace is None:
+    if workspace is None and dt == torch.bfloat16:
         nbytes = based_prefill_workspace_bytes(B, H, L, d_v, d)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)

@@ -51,6 +51,8 @@ constexpr int kLoSlots = 32;  // slots of the last feature k-step (tiles 8, 9)
 constexpr int kLoRow = 40;    // LDS row stride (bf16) of their lo parts
 constexpr int kTRow = 72;     // LDS row stride (bf16) of V^T and K^T [row][token]
 constexpr int kQRow = 20;     // LDS row stride (bf16) of Q and K [token][dim]
+constexpr int kKtRow = 68;    // LDS row stride (fp32) of K^T/4 [dim][token]
+constexpr int kQfRow = 20;    // LDS row stride (fp32) of Q [token][dim]
 constexpr float kSqrt2 = 1.41421356237309504880f;
 constexpr uint16_t kBf16One = 0x3F80;
 
@@ -59,13 +61,21 @@ struct PrefillSmem {
     static constexpr int kSBufs = DV == 64 ? 2 : 1;  // state operand buffers
     alignas(16) uint16_t q[2][kC * kQRow];
     alignas(16) uint16_t k[2][kC * kQRow];
-    alignas(16) uint16_t kt[2][kDFeat * kTRow];
+    alignas(16) float ktf[2][kDFeat * kKtRow];  // K^T scaled by 1/4 (update waves)
+    alignas(16) float qf[2][kC * kQfRow];       // Q as fp32 (readout features)
     alignas(16) uint16_t vt[2][DV * kTRow];
     alignas(16) uint16_t s_hi[kSBufs][DV * kSRow];
     alignas(16) uint16_t s_lo[kSBufs][DV * kLoRow];
     alignas(16) uint16_t z_hi[kSBufs][kSlots];
     alignas(16) uint16_t z_lo[kSBufs][kLoSlots];
 };
+
+enum { kModeFull = 0, kModeState = 1, kModeSegment = 2 };
+
+template <int T, int DV>
+__device__ __forceinline__ void ws_store(const f32x4 (&acc)[DV / 16 + 1], float* slot, int lane);
+template <int T, int DV>
+__device__ __forceinline__ void ws_load(f32x4 (&acc)[DV / 16 + 1], const float* slot, int lane);
 
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -269,9 +279,10 @@ __device__ __forceinline__ void store_final(const f32x4 (&acc)[DV / 16 + 1], flo
 }
 
 // psi(K)^T for rotation tile T: lane (row r, group g) holds feature row r
-// for 8 tokens; kv[] = k_r / 4 of those tokens.
+// for 8 tokens; kv[] = k_r / 4 of those tokens.  For tile 8, pmask selects
+// the pair rows and cst[] is the constant row's value (0 on padding).
 template <int T>
-__device__ __forceinline__ bf16x8 psi_k(const float (&kv)[8], int r, const float (&valid)[8]) {
+__device__ __forceinline__ bf16x8 psi_k(const float (&kv)[8], float pmask, const float (&cst)[8]) {
     float a[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -280,8 +291,7 @@ __device__ __forceinline__ bf16x8 psi_k(const float (&kv)[8], int r, const float
         } else if (T < 8) {
             a[i] = kv[i] * row_ror<16 - T>(kv[i]);
         } else if (T == 8) {
-            const float p = kv[i] * row_ror<8>(kv[i]);
-            a[i] = r < 8 ? p : (r == 8 ? valid[i] : 0.f);
+            a[i] = fmaf(kv[i] * row_ror<8>(kv[i]), pmask, cst[i]);
         } else {
             a[i] = kv[i];
         }
@@ -334,12 +344,27 @@ __device__ __forceinline__ void qk_store(const QKStage& in, PrefillSmem<DV>& sm,
     rb[0] = make_uint2(a1[0], a1[1]);
     rb[1] = make_uint2(a1[2], a1[3]);
     if (t < 64) {
-        uint32_t* kt = reinterpret_cast<uint32_t*>(&sm.kt[buf][0]);
+        float* kt = &sm.ktf[buf][0];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            kt[((8 * db + 2 * e) * kTRow + 2 * p) >> 1] = lo_pair(a0[e], a1[e]);
-            kt[((8 * db + 2 * e + 1) * kTRow + 2 * p) >> 1] = hi_pair(a0[e], a1[e]);
+            const int d0 = 8 * db + 2 * e;
+            *reinterpret_cast<float2*>(kt + d0 * kKtRow + 2 * p) =
+                make_float2(0.25f * bf16lo_f32(a0[e]), 0.25f * bf16lo_f32(a1[e]));
+            *reinterpret_cast<float2*>(kt + (d0 + 1) * kKtRow + 2 * p) =
+                make_float2(0.25f * bf16hi_f32(a0[e]), 0.25f * bf16hi_f32(a1[e]));
         }
+    } else {
+        float* qa = &sm.qf[buf][(2 * p) * kQfRow + 8 * db];
+        float* qb = &sm.qf[buf][(2 * p + 1) * kQfRow + 8 * db];
+        f32x4 x;
+        x = f32x4{bf16lo_f32(a0[0]), bf16hi_f32(a0[0]), bf16lo_f32(a0[1]), bf16hi_f32(a0[1])};
+        *reinterpret_cast<f32x4*>(qa) = x;
+        x = f32x4{bf16lo_f32(a0[2]), bf16hi_f32(a0[2]), bf16lo_f32(a0[3]), bf16hi_f32(a0[3])};
+        *reinterpret_cast<f32x4*>(qa + 4) = x;
+        x = f32x4{bf16lo_f32(a1[0]), bf16hi_f32(a1[0]), bf16lo_f32(a1[1]), bf16hi_f32(a1[1])};
+        *reinterpret_cast<f32x4*>(qb) = x;
+        x = f32x4{bf16lo_f32(a1[2]), bf16hi_f32(a1[2]), bf16lo_f32(a1[3]), bf16hi_f32(a1[3])};
+        *reinterpret_cast<f32x4*>(qb + 4) = x;
     }
 }
 // u (0..255 of the update waves): token pair p = u & 31, column blocks
@@ -373,7 +398,7 @@ __device__ __forceinline__ void v_store(const VStage<DV>& st, PrefillSmem<DV>& s
 }
 
 // ---- readout wave W: query tile W (rows 16W..16W+15) of every chunk.
-template <int W, int DV>
+template <int W, int DV, int MODE>
 __device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, const uint16_t* __restrict__ kh,
                                              int L, float eps, float* __restrict__ yh, PrefillSmem<DV>& sm) {
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
@@ -381,7 +406,8 @@ __device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, co
     const int t = threadIdx.x;  // 0..255
     const int lane = t & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (L + kC - 1) / kC;
-    const bool stager = t < 128;
+    // The state-only pass needs K (and K^T) but not Q.
+    const bool stager = MODE == kModeState ? t < 64 : t < 128;
 
     QKStage st;
     if (stager) {
@@ -390,6 +416,17 @@ __device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, co
         if (nchunks > 1) qk_load(st, qh, kh, kC, L, t);
     }
     __syncthreads();
+
+    if constexpr (MODE == kModeState) {
+        for (int c = 0; c < nchunks; ++c) {
+            if (stager && c + 1 < nchunks) {
+                qk_store<DV>(st, sm, (c & 1) ^ 1, (c + 1) * kC, L, t);
+                if (c + 2 < nchunks) qk_load(st, qh, kh, (c + 2) * kC, L, t);
+            }
+            __syncthreads();
+        }
+        return;
+    }
 
     const bf16x8 ones = ones8();
     for (int c = 0; c < nchunks; ++c) {
@@ -430,14 +467,19 @@ __device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, co
                 }
                 bf16x8 ahi, alo;
                 pack8_hilo(a, ahi, alo);
+                bf16x8 vb[kNV];
 #pragma unroll
                 for (int ct = 0; ct < kNV; ++ct) {
                     const uint16_t* vrow = vt_l + (16 * ct + r) * kTRow + 32 * p;
-                    const bf16x8 vb = join44(vrow + 4 * g, vrow + 16 + 4 * g);
-                    y[ct] = mfma32(ahi, vb, y[ct]);
-                    y[ct] = mfma32(alo, vb, y[ct]);
+                    vb[ct] = join44(vrow + 4 * g, vrow + 16 + 4 * g);
                 }
+                // hi parts of every column tile first, then the lo parts, so
+                // consecutive MFMAs never depend on each other
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) y[ct] = mfma32(ahi, vb[ct], y[ct]);
                 y[kNV] = mfma32(ahi, ones, y[kNV]);
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) y[ct] = mfma32(alo, vb[ct], y[ct]);
                 y[kNV] = mfma32(alo, ones, y[kNV]);
             }
         }
@@ -445,14 +487,14 @@ __device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, co
         // ---- off-diagonal term: psi(Q) x (state before this chunk)
         {
             float qr[16];
-            const uint16_t* qrow = q_l + (16 * W + r) * kQRow;
+            const float* qrow = &sm.qf[buf][(16 * W + r) * kQfRow];
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
-                const uint2 u = *reinterpret_cast<const uint2*>(qrow + 4 * ((g + cc) & 3));
-                qr[4 * cc + 0] = bf16lo_f32(u.x);
-                qr[4 * cc + 1] = bf16hi_f32(u.x);
-                qr[4 * cc + 2] = bf16lo_f32(u.y);
-                qr[4 * cc + 3] = bf16hi_f32(u.y);
+                const f32x4 x = *reinterpret_cast<const f32x4*>(qrow + 4 * ((g + cc) & 3));
+                qr[4 * cc + 0] = x[0];
+                qr[4 * cc + 1] = x[1];
+                qr[4 * cc + 2] = x[2];
+                qr[4 * cc + 3] = x[3];
             }
             const uint16_t* shi = &sm.s_hi[sbuf][0];
             const uint16_t* slo = &sm.s_lo[sbuf][0];
@@ -460,29 +502,34 @@ __device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, co
     {                                                                                          \
         float a[8];                                                                            \
         psi_q<J>(qr, g, a);                                                                    \
-        bf16x8 ahi, alo;                                                                       \
-        if (J == 4) pack8_hilo(a, ahi, alo); else ahi = pack8(a);                              \
-        _Pragma("unroll") for (int ct = 0; ct < kNV; ++ct) {                                   \
-            const uint16_t* srow = shi + (16 * ct + r) * kSRow + 32 * (J) + 8 * g;             \
-            const bf16x8 sb = lds_bf16x8(srow);                                                \
-            y[ct] = mfma32(ahi, sb, y[ct]);                                                    \
-            if (J == 4) {                                                                      \
-                y[ct] = mfma32(ahi, lds_bf16x8(slo + (16 * ct + r) * kLoRow + 8 * g), y[ct]); \
-                y[ct] = mfma32(alo, sb, y[ct]);                                                \
-            }                                                                                  \
-        }                                                                                      \
-        const bf16x8 zb = lds_bf16x8(&sm.z_hi[sbuf][32 * (J) + 8 * g]);                        \
-        y[kNV] = mfma32(ahi, zb, y[kNV]);                                                      \
-        if (J == 4) {                                                                          \
-            y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_lo[sbuf][8 * g]), y[kNV]);                   \
-            y[kNV] = mfma32(alo, zb, y[kNV]);                                                  \
-        }                                                                                      \
+        const bf16x8 ahi = pack8(a);                                                           \
+        _Pragma("unroll") for (int ct = 0; ct < kNV; ++ct)                                     \
+            y[ct] = mfma32(ahi, lds_bf16x8(shi + (16 * ct + r) * kSRow + 32 * (J) + 8 * g), y[ct]); \
+        y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_hi[sbuf][32 * (J) + 8 * g]), y[kNV]);             \
     }
             BASED_READOUT_STEP(0)
             BASED_READOUT_STEP(1)
             BASED_READOUT_STEP(2)
             BASED_READOUT_STEP(3)
-            BASED_READOUT_STEP(4)
+            {
+                // last feature k-step (pairs (r, r+8), constant, linear): hi/lo on both sides
+                float a[8];
+                psi_q<4>(qr, g, a);
+                bf16x8 ahi, alo;
+                pack8_hilo(a, ahi, alo);
+                bf16x8 sb[kNV + 1];
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) sb[ct] = lds_bf16x8(shi + (16 * ct + r) * kSRow + 128 + 8 * g);
+                sb[kNV] = lds_bf16x8(&sm.z_hi[sbuf][128 + 8 * g]);
+#pragma unroll
+                for (int ct = 0; ct <= kNV; ++ct) y[ct] = mfma32(ahi, sb[ct], y[ct]);
+#pragma unroll
+                for (int ct = 0; ct <= kNV; ++ct) y[ct] = mfma32(alo, sb[ct], y[ct]);
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct)
+                    y[ct] = mfma32(ahi, lds_bf16x8(slo + (16 * ct + r) * kLoRow + 8 * g), y[ct]);
+                y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_lo[sbuf][8 * g]), y[kNV]);
+            }
 #undef BASED_READOUT_STEP
         }
 
@@ -512,22 +559,30 @@ __device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, co
 }
 
 // ---- update wave U: state rotation tiles U, U+4 (, U+8).
-template <int U, int DV>
+template <int U, int DV, int MODE>
 __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int L, float* __restrict__ Sh,
-                                            float* __restrict__ zh, int use_init, PrefillSmem<DV>& sm) {
+                                            float* __restrict__ zh, int use_init, PrefillSmem<DV>& sm,
+                                            const float* ws_in, float* ws_out, bool write_final) {
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
     constexpr int kNT = U < 2 ? 3 : 2;
     constexpr int kSBufs = PrefillSmem<DV>::kSBufs;
     const int u = threadIdx.x - 256;  // 0..255
     const int lane = u & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (L + kC - 1) / kC;
+    // rotation tile 8: rows 0..7 are the pairs (r, r+8), row 8 the constant
+    const float pmask = r < 8 ? 1.f : 0.f;
+    const float cmask = r == 8 ? 1.f : 0.f;
 
     f32x4 acc[kNT][kNCT];
 #pragma unroll
     for (int ti = 0; ti < kNT; ++ti)
 #pragma unroll
         for (int ct = 0; ct < kNCT; ++ct) acc[ti][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (use_init) {
+    if (MODE == kModeSegment) {
+        ws_load<U, DV>(acc[0], ws_in, lane);
+        ws_load<U + 4, DV>(acc[1], ws_in, lane);
+        if constexpr (kNT == 3) ws_load<U + 8, DV>(acc[2], ws_in, lane);
+    } else if (MODE == kModeFull && use_init) {
         load_initial<U, DV>(acc[0], Sh, zh, g, r);
         load_initial<U + 4, DV>(acc[1], Sh, zh, g, r);
         if constexpr (kNT == 3) load_initial<U + 8, DV>(acc[2], Sh, zh, g, r);
@@ -537,9 +592,11 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int
     v_load<DV>(st, vh, 0, L, u);
     v_store<DV>(st, sm, 0, 0, L, u);
     if (nchunks > 1) v_load<DV>(st, vh, kC, L, u);
-    publish_state<U, DV>(acc[0], sm, 0, g, r);
-    publish_state<U + 4, DV>(acc[1], sm, 0, g, r);
-    if constexpr (kNT == 3) publish_state<U + 8, DV>(acc[2], sm, 0, g, r);
+    if (MODE != kModeState) {
+        publish_state<U, DV>(acc[0], sm, 0, g, r);
+        publish_state<U + 4, DV>(acc[1], sm, 0, g, r);
+        if constexpr (kNT == 3) publish_state<U + 8, DV>(acc[2], sm, 0, g, r);
+    }
     __syncthreads();
 
     const bf16x8 ones = ones8();
@@ -547,38 +604,46 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int
         const int buf = c & 1;
         const int t0 = c * kC;
         const int n = min(kC, L - t0);
-        const uint16_t* kt_l = &sm.kt[buf][0];
+        const float* kt_l = &sm.ktf[buf][0];
         const uint16_t* vt_l = &sm.vt[buf][0];
 
         // ---- S += psi(K)^T V, z += psi(K)^T 1 over this chunk's 64 tokens
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            float kv[8], valid[8];
-            const u32x4 ku = *reinterpret_cast<const u32x4*>(kt_l + r * kTRow + 32 * s + 8 * g);
-            unpack8(ku, kv);
+            float kv[8], cst[8];
+            const float* krow = kt_l + r * kKtRow + 32 * s + 8 * g;
+            const f32x4 k0 = *reinterpret_cast<const f32x4*>(krow);
+            const f32x4 k1 = *reinterpret_cast<const f32x4*>(krow + 4);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                kv[i] *= 0.25f;
-                valid[i] = (32 * s + 8 * g + i < n) ? 1.f : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                kv[i] = k0[i];
+                kv[4 + i] = k1[i];
+            }
+            // constant feature row of tile 8: 1 for real tokens, 0 for padding
+#pragma unroll
+            for (int i = 0; i < 8; ++i) cst[i] = cmask;
+            if (n < kC) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) cst[i] = (32 * s + 8 * g + i < n) ? cmask : 0.f;
             }
             bf16x8 vb[kNV];
 #pragma unroll
             for (int ct = 0; ct < kNV; ++ct)
                 vb[ct] = lds_bf16x8(vt_l + (16 * ct + r) * kTRow + 32 * s + 8 * g);
             {
-                const bf16x8 a = psi_k<U>(kv, r, valid);
+                const bf16x8 a = psi_k<U>(kv, pmask, cst);
 #pragma unroll
                 for (int ct = 0; ct < kNV; ++ct) acc[0][ct] = mfma32(a, vb[ct], acc[0][ct]);
                 acc[0][kNV] = mfma32(a, ones, acc[0][kNV]);
             }
             {
-                const bf16x8 a = psi_k<U + 4>(kv, r, valid);
+                const bf16x8 a = psi_k<U + 4>(kv, pmask, cst);
 #pragma unroll
                 for (int ct = 0; ct < kNV; ++ct) acc[1][ct] = mfma32(a, vb[ct], acc[1][ct]);
                 acc[1][kNV] = mfma32(a, ones, acc[1][kNV]);
             }
             if constexpr (kNT == 3) {
-                const bf16x8 a = psi_k<U + 8>(kv, r, valid);
+                const bf16x8 a = psi_k<U + 8>(kv, pmask, cst);
 #pragma unroll
                 for (int ct = 0; ct < kNV; ++ct) acc[2][ct] = mfma32(a, vb[ct], acc[2][ct]);
                 acc[2][kNV] = mfma32(a, ones, acc[2][kNV]);
@@ -592,66 +657,205 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int
         }
 
         // ---- publish the state after this chunk for the next readout
-        if (kSBufs == 1) __syncthreads();  // wait until every readout of this chunk is done
-        const int wbuf = kSBufs == 2 ? (buf ^ 1) : 0;
-        publish_state<U, DV>(acc[0], sm, wbuf, g, r);
-        publish_state<U + 4, DV>(acc[1], sm, wbuf, g, r);
-        if constexpr (kNT == 3) publish_state<U + 8, DV>(acc[2], sm, wbuf, g, r);
+        if (MODE != kModeState) {
+            if (kSBufs == 1) __syncthreads();  // wait until every readout of this chunk is done
+            const int wbuf = kSBufs == 2 ? (buf ^ 1) : 0;
+            publish_state<U, DV>(acc[0], sm, wbuf, g, r);
+            publish_state<U + 4, DV>(acc[1], sm, wbuf, g, r);
+            if constexpr (kNT == 3) publish_state<U + 8, DV>(acc[2], sm, wbuf, g, r);
+        }
         __syncthreads();
     }
 
-    store_final<U, DV>(acc[0], Sh, zh, use_init, g, r);
-    store_final<U + 4, DV>(acc[1], Sh, zh, use_init, g, r);
-    if constexpr (kNT == 3) store_final<U + 8, DV>(acc[2], Sh, zh, use_init, g, r);
+    if (MODE == kModeState) {
+        ws_store<U, DV>(acc[0], ws_out, lane);
+        ws_store<U + 4, DV>(acc[1], ws_out, lane);
+        if constexpr (kNT == 3) ws_store<U + 8, DV>(acc[2], ws_out, lane);
+    } else if (write_final) {
+        store_final<U, DV>(acc[0], Sh, zh, use_init, g, r);
+        store_final<U + 4, DV>(acc[1], Sh, zh, use_init, g, r);
+        if constexpr (kNT == 3) store_final<U + 8, DV>(acc[2], Sh, zh, use_init, g, r);
+    }
 }
 
+// Initial state of every segment split (state-only pass, last segment slot):
+// the caller's state in readout units, or zero.
+template <int U, int DV>
+__device__ __forceinline__ void init_to_workspace(const float* Sh, const float* zh, int use_init, float* ws_out) {
+    constexpr int kNCT = DV / 16 + 1;
+    constexpr int kNT = U < 2 ? 3 : 2;
+    const int lane = (threadIdx.x - 256) & 63, g = lane >> 4, r = lane & 15;
+    f32x4 acc[kNT][kNCT];
+#pragma unroll
+    for (int ti = 0; ti < kNT; ++ti)
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct) acc[ti][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (use_init) {
+        load_initial<U, DV>(acc[0], Sh, zh, g, r);
+        load_initial<U + 4, DV>(acc[1], Sh, zh, g, r);
+        if constexpr (kNT == 3) load_initial<U + 8, DV>(acc[2], Sh, zh, g, r);
+    }
+    ws_store<U, DV>(acc[0], ws_out, lane);
+    ws_store<U + 4, DV>(acc[1], ws_out, lane);
+    if constexpr (kNT == 3) ws_store<U + 8, DV>(acc[2], ws_out, lane);
+}
+
+// Workspace: one state per (segment slot, head) in accumulator layout,
+// [slot][head][tile 0..9][column tile][lane] f32x4, readout units.
 template <int DV>
+__host__ __device__ constexpr size_t ws_slot_floats() {
+    return (size_t)10 * (DV / 16 + 1) * 64 * 4;
+}
+template <int T, int DV>
+__device__ __forceinline__ void ws_store(const f32x4 (&acc)[DV / 16 + 1], float* slot, int lane) {
+    constexpr int kNCT = DV / 16 + 1;
+    f32x4* p = reinterpret_cast<f32x4*>(slot) + (size_t)T * kNCT * 64 + lane;
+#pragma unroll
+    for (int ct = 0; ct < kNCT; ++ct) p[ct * 64] = acc[ct];
+}
+template <int T, int DV>
+__device__ __forceinline__ void ws_load(f32x4 (&acc)[DV / 16 + 1], const float* slot, int lane) {
+    constexpr int kNCT = DV / 16 + 1;
+    const f32x4* p = reinterpret_cast<const f32x4*>(slot) + (size_t)T * kNCT * 64 + lane;
+#pragma unroll
+    for (int ct = 0; ct < kNCT; ++ct) acc[ct] = p[ct * 64];
+}
+
+// One workgroup = 8 waves.  MODE
+//   kModeFull:    one workgroup per head walks the whole sequence.
+//   kModeState:   workgroup (head, s), s < nseg-1: state increment of
+//                 segment s into slot s+1; s = nseg-1: the initial state
+//                 into slot 0.
+//   kModeSegment: workgroup (head, s): outputs of segment s starting from
+//                 slot s (after the prefix sum); the last segment writes the
+//                 final state.
+template <int DV, int MODE>
 __global__ __launch_bounds__(512, 1) void prefill_mfma_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v, int L,
-                                                              float eps, float* __restrict__ y,
-                                                              float* __restrict__ S,
-                                                              float* __restrict__ z, int use_init) {
+                                                              int seg_len, int nseg, float eps,
+                                                              float* __restrict__ y, float* __restrict__ S,
+                                                              float* __restrict__ z, int use_init,
+                                                              float* __restrict__ ws) {
     __shared__ PrefillSmem<DV> sm;
-    const int head = blockIdx.x;
-    const uint16_t* qh = q + (size_t)head * L * kDFeat;
-    const uint16_t* kh = k + (size_t)head * L * kDFeat;
-    const uint16_t* vh = v + (size_t)head * L * DV;
-    float* yh = y + (size_t)head * L * DV;
+    const int head = MODE == kModeFull ? blockIdx.x : blockIdx.x / nseg;
+    const int seg = MODE == kModeFull ? 0 : blockIdx.x % nseg;
+    const int BH = MODE == kModeFull ? gridDim.x : gridDim.x / nseg;
+    const int tb = seg * seg_len;
+    const int len = MODE == kModeFull ? L : min(seg_len, L - tb);
+    const uint16_t* qh = q + ((size_t)head * L + tb) * kDFeat;
+    const uint16_t* kh = k + ((size_t)head * L + tb) * kDFeat;
+    const uint16_t* vh = v + ((size_t)head * L + tb) * DV;
+    float* yh = y + ((size_t)head * L + tb) * DV;
     float* Sh = S + (size_t)head * kNumFeat * DV;
     float* zh = z + (size_t)head * kNumFeat;
+    float* ws_in = nullptr;
+    float* ws_out = nullptr;
+    if (MODE != kModeFull) {
+        ws_in = ws + ((size_t)seg * BH + head) * ws_slot_floats<DV>();
+        ws_out = ws + ((size_t)((seg + 1) % nseg) * BH + head) * ws_slot_floats<DV>();
+    }
+    const int w = threadIdx.x >> 6;
+    if (MODE == kModeState && seg == nseg - 1) {
+        // This workgroup's slot job is the initial state (no sweep, no barrier).
+        if (w >= 4) {
+            switch (w) {
+                case 4: init_to_workspace<0, DV>(Sh, zh, use_init, ws_out); break;
+                case 5: init_to_workspace<1, DV>(Sh, zh, use_init, ws_out); break;
+                case 6: init_to_workspace<2, DV>(Sh, zh, use_init, ws_out); break;
+                default: init_to_workspace<3, DV>(Sh, zh, use_init, ws_out); break;
+            }
+        }
+        return;
+    }
+    const bool write_final = MODE == kModeFull || seg == nseg - 1;
     // Waves 0-3 and 4-7 land on SIMDs 0-3 in pairs; readout wave W shares
     // its SIMD with update wave W (the lighter on-diagonal work of W = 0, 1
     // pairs with the three-tile update waves).
-    switch (threadIdx.x >> 6) {
-        case 0: readout_wave<0, DV>(qh, kh, L, eps, yh, sm); break;
-        case 1: readout_wave<1, DV>(qh, kh, L, eps, yh, sm); break;
-        case 2: readout_wave<2, DV>(qh, kh, L, eps, yh, sm); break;
-        case 3: readout_wave<3, DV>(qh, kh, L, eps, yh, sm); break;
-        case 4: update_wave<0, DV>(vh, L, Sh, zh, use_init, sm); break;
-        case 5: update_wave<1, DV>(vh, L, Sh, zh, use_init, sm); break;
-        case 6: update_wave<2, DV>(vh, L, Sh, zh, use_init, sm); break;
-        default: update_wave<3, DV>(vh, L, Sh, zh, use_init, sm); break;
+    switch (w) {
+        case 0: readout_wave<0, DV, MODE>(qh, kh, len, eps, yh, sm); break;
+        case 1: readout_wave<1, DV, MODE>(qh, kh, len, eps, yh, sm); break;
+        case 2: readout_wave<2, DV, MODE>(qh, kh, len, eps, yh, sm); break;
+        case 3: readout_wave<3, DV, MODE>(qh, kh, len, eps, yh, sm); break;
+        case 4: update_wave<0, DV, MODE>(vh, len, Sh, zh, use_init, sm, ws_in, ws_out, write_final); break;
+        case 5: update_wave<1, DV, MODE>(vh, len, Sh, zh, use_init, sm, ws_in, ws_out, write_final); break;
+        case 6: update_wave<2, DV, MODE>(vh, len, Sh, zh, use_init, sm, ws_in, ws_out, write_final); break;
+        default: update_wave<3, DV, MODE>(vh, len, Sh, zh, use_init, sm, ws_in, ws_out, write_final); break;
     }
+}
+
+// Inclusive prefix over segment slots, per head: slot s <- slot s-1 + slot s.
+// After it, slot s holds the state entering segment s.
+__global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ ws, int nseg, int BH,
+                                                           size_t slot_floats) {
+    const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int head = blockIdx.y;
+    if (e >= slot_floats) return;
+    f32x4* p = reinterpret_cast<f32x4*>(ws + (size_t)head * slot_floats + e);
+    const size_t stride = (size_t)BH * slot_floats / 4;  // in f32x4
+    f32x4 run = p[0];
+    for (int sidx = 1; sidx < nseg; ++sidx) {
+        f32x4 x = p[sidx * stride];
+        run += x;
+        p[sidx * stride] = run;
+    }
+}
+
+// Segments per head: enough workgroups for one per compute unit (the LDS
+// footprint allows one resident workgroup per CU), segments of at least two
+// chunks.
+constexpr int kTargetWorkgroups = 256;
+int choose_segments(int BH, int L) {
+    const int nchunks = (L + kC - 1) / kC;
+    if (BH >= kTargetWorkgroups || nchunks < 4) return 1;
+    int nseg = (kTargetWorkgroups + BH - 1) / BH;
+    nseg = min(nseg, nchunks / 2);
+    return max(nseg, 1);
+}
+
+template <int DV>
+size_t workspace_bytes_dv(int BH, int nseg) {
+    return nseg <= 1 ? 0 : (size_t)nseg * BH * ws_slot_floats<DV>() * sizeof(float);
+}
+
+template <int DV>
+hipError_t launch_dv(const uint16_t* q, const uint16_t* k, const uint16_t* v, int BH, int L, float eps, float* y,
+                     float* S, float* z, int use_init, void* ws, size_t ws_bytes, hipStream_t st) {
+    const int nseg = choose_segments(BH, L);
+    if (nseg <= 1 || ws == nullptr || ws_bytes < workspace_bytes_dv<DV>(BH, nseg)) {
+        hipLaunchKernelGGL((prefill_mfma_kernel<DV, kModeFull>), dim3(BH), dim3(512), 0, st, q, k, v, L, L, 1, eps,
+                           y, S, z, use_init, nullptr);
+        return hipGetLastError();
+    }
+    const int nchunks = (L + kC - 1) / kC;
+    const int seg_len = ((nchunks + nseg - 1) / nseg) * kC;
+    const int nseg_eff = (L + seg_len - 1) / seg_len;
+    float* wsf = static_cast<float*>(ws);
+    hipLaunchKernelGGL((prefill_mfma_kernel<DV, kModeState>), dim3(BH * nseg_eff), dim3(512), 0, st, q, k, v, L,
+                       seg_len, nseg_eff, eps, y, S, z, use_init, wsf);
+    const size_t slot = ws_slot_floats<DV>();
+    hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH), dim3(256), 0, st, wsf,
+                       nseg_eff, BH, slot);
+    hipLaunchKernelGGL((prefill_mfma_kernel<DV, kModeSegment>), dim3(BH * nseg_eff), dim3(512), 0, st, q, k, v,
+                       L, seg_len, nseg_eff, eps, y, S, z, use_init, wsf);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-size_t prefill_mfma_workspace_bytes(int, int, int) { return 0; }
+size_t prefill_mfma_workspace_bytes(int BH, int L, int dv) {
+    const int nseg = choose_segments(BH, L);
+    return dv == 64 ? workspace_bytes_dv<64>(BH, nseg) : workspace_bytes_dv<128>(BH, nseg);
+}
 
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int BH, int L, int dv,
-                               float eps, float* y, float* S, float* z, int use_init, void*, size_t,
-                               hipStream_t st) {
+                               float eps, float* y, float* S, float* z, int use_init, void* ws,
+                               size_t ws_bytes, hipStream_t st) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     const uint16_t* vv = static_cast<const uint16_t*>(v);
-    if (dv == 64)
-        hipLaunchKernelGGL((prefill_mfma_kernel<64>), dim3(BH), dim3(512), 0, st, qq, kk, vv, L, eps, y, S,
-                           z, use_init);
-    else
-        hipLaunchKernelGGL((prefill_mfma_kernel<128>), dim3(BH), dim3(512), 0, st, qq, kk, vv, L, eps, y,
-                           S, z, use_init);
-    return hipGetLastError();
+    if (dv == 64) return launch_dv<64>(qq, kk, vv, BH, L, eps, y, S, z, use_init, ws, ws_bytes, st);
+    return launch_dv<128>(qq, kk, vv, BH, L, eps, y, S, z, use_init, ws, ws_bytes, st);
 }
 
 }  // namespace based

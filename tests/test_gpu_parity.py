@@ -80,7 +80,7 @@ def test_prefill_f32_chunks(chunk, dv):
 @pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, 2e-2), (torch.float32, 1e-4)])
 def test_prefill_resume_from_state(dtype, tol):
     based = based_mod()
-    L1, L2 = 130, 77
+    L1, L2 = 130, 700  # the second call is long enough to be split into segments (bf16)
     q, k, v = si.custom((1, 4, L1 + L2, 16), (1, 4, L1 + L2, 64), seed=700, scale=0.5, dtype=dtype)
     qd, kd, vd = dev(q, k, v)
     _, S1, z1 = based.based_prefill(qd[:, :, :L1].contiguous(), kd[:, :, :L1].contiguous(),
