@@ -803,11 +803,12 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
 
 // Segments per head: enough workgroups for one per compute unit (the LDS
 // footprint allows one resident workgroup per CU), segments of at least two
-// chunks.
+// chunks.  From half the chip upwards the extra state pass costs about what
+// the added parallelism gains, so such shapes run unsplit.
 constexpr int kTargetWorkgroups = 256;
 int choose_segments(int BH, int L) {
     const int nchunks = (L + kC - 1) / kC;
-    if (BH >= kTargetWorkgroups || nchunks < 4) return 1;
+    if (2 * BH >= kTargetWorkgroups || nchunks < 4) return 1;
     int nseg = (kTargetWorkgroups + BH - 1) / BH;
     nseg = min(nseg, nchunks / 2);
     return max(nseg, 1);
