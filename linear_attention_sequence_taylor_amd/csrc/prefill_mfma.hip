@@ -58,7 +58,7 @@ constexpr uint16_t kBf16One = 0x3F80;
 
 template <int DV>
 struct PrefillSmem {
-    static constexpr int kSBufs = DV == 64 ? 2 : 1;  // state operand buffers
+    static constexpr int kSBufs = DV <= 64 ? 2 : 1;  // state operand buffers
     alignas(16) uint16_t q[2][kC * kQRow];
     alignas(16) uint16_t k[2][kC * kQRow];
     alignas(16) float ktf[2][kDFeat * kKtRow];  // K^T scaled by 1/4 (update waves)
@@ -220,7 +220,7 @@ __device__ __forceinline__ void publish_state(const f32x4 (&acc)[DV / 16 + 1], P
 
 template <int T, int DV>
 __device__ __forceinline__ void load_initial(f32x4 (&acc)[DV / 16 + 1], const float* Sh, const float* zh,
-                                             int g, int r) {
+                                             int ldv, int g, int r) {
     constexpr int kNV = DV / 16;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -233,8 +233,8 @@ __device__ __forceinline__ void load_initial(f32x4 (&acc)[DV / 16 + 1], const fl
             if (n > 0) {
                 if (ct < kNV) {
                     const int col = 16 * ct + r;
-                    x = Sh[(size_t)r0 * DV + col];
-                    if (n == 2) x = 0.5f * (x + Sh[(size_t)r1 * DV + col]);
+                    x = Sh[(size_t)r0 * ldv + col];
+                    if (n == 2) x = 0.5f * (x + Sh[(size_t)r1 * ldv + col]);
                 } else {
                     x = zh[r0];
                     if (n == 2) x = 0.5f * (x + zh[r1]);
@@ -247,7 +247,7 @@ __device__ __forceinline__ void load_initial(f32x4 (&acc)[DV / 16 + 1], const fl
 
 template <int T, int DV>
 __device__ __forceinline__ void store_final(const f32x4 (&acc)[DV / 16 + 1], float* Sh, float* zh,
-                                            int use_init, int g, int r) {
+                                            int ldv, bool own_z, int use_init, int g, int r) {
     constexpr int kNV = DV / 16;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -257,9 +257,9 @@ __device__ __forceinline__ void store_final(const f32x4 (&acc)[DV / 16 + 1], flo
         const float sc = state_scale<T>(4 * g + m);
 #pragma unroll
         for (int ct = 0; ct <= kNV; ++ct) {
-            if (ct == kNV && r != 0) continue;
+            if (ct == kNV && (r != 0 || !own_z)) continue;
             float* base = ct < kNV ? Sh + 16 * ct + r : zh;
-            const size_t stride = ct < kNV ? (size_t)DV : 1;
+            const size_t stride = ct < kNV ? (size_t)ldv : 1;
             if (!use_init) {
                 base[r0 * stride] = acc[ct][m] * sc;
                 if (n == 2) base[r1 * stride] = acc[ct][m] * sc;
@@ -305,7 +305,7 @@ struct QKStage {
 };
 template <int DV>
 struct VStage {
-    static constexpr int kPass = DV / 64;
+    static constexpr int kPass = DV >= 64 ? DV / 64 : 1;
     u32x4 v0[kPass], v1[kPass];
 };
 
@@ -368,16 +368,18 @@ __device__ __forceinline__ void qk_store(const QKStage& in, PrefillSmem<DV>& sm,
     }
 }
 // u (0..255 of the update waves): token pair p = u & 31, column blocks
-// (u >> 5) + 8*pass of 8 columns.
+// (u >> 5) + 8*pass of 8 columns (a 32-column group uses threads 0..127).
+// ldv is the row stride of v in the caller's tensor.
 template <int DV>
-__device__ __forceinline__ void v_load(VStage<DV>& st, const uint16_t* vh, int t0, int L, int u) {
+__device__ __forceinline__ void v_load(VStage<DV>& st, const uint16_t* vh, int ldv, int t0, int L, int u) {
     const int p = u & 31;
     const int ta = min(t0 + 2 * p, L - 1), tb = min(t0 + 2 * p + 1, L - 1);
 #pragma unroll
     for (int ps = 0; ps < VStage<DV>::kPass; ++ps) {
         const int cb = (u >> 5) + 8 * ps;
-        st.v0[ps] = *reinterpret_cast<const u32x4*>(vh + (size_t)ta * DV + 8 * cb);
-        st.v1[ps] = *reinterpret_cast<const u32x4*>(vh + (size_t)tb * DV + 8 * cb);
+        if (8 * cb >= DV) continue;
+        st.v0[ps] = *reinterpret_cast<const u32x4*>(vh + (size_t)ta * ldv + 8 * cb);
+        st.v1[ps] = *reinterpret_cast<const u32x4*>(vh + (size_t)tb * ldv + 8 * cb);
     }
 }
 template <int DV>
@@ -388,6 +390,7 @@ __device__ __forceinline__ void v_store(const VStage<DV>& st, PrefillSmem<DV>& s
 #pragma unroll
     for (int ps = 0; ps < VStage<DV>::kPass; ++ps) {
         const int cb = (u >> 5) + 8 * ps;
+        if (8 * cb >= DV) continue;
         const u32x4 v0 = keep_if(st.v0[ps], oka), v1 = keep_if(st.v1[ps], okb);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -399,34 +402,39 @@ __device__ __forceinline__ void v_store(const VStage<DV>& st, PrefillSmem<DV>& s
 
 // ---- readout wave W: query tile W (rows 16W..16W+15) of every chunk.
 template <int W, int DV, int MODE>
-__device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, const uint16_t* __restrict__ kh,
-                                             int L, float eps, float* __restrict__ yh, PrefillSmem<DV>& sm) {
+__device__ __forceinline__ void readout_wave(int L, int ldv, float eps, float* __restrict__ yh,
+                                             PrefillSmem<DV>& sm) {
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
     constexpr int kSBufs = PrefillSmem<DV>::kSBufs;
     const int t = threadIdx.x;  // 0..255
     const int lane = t & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (L + kC - 1) / kC;
-    // The state-only pass needs K (and K^T) but not Q.
-    const bool stager = MODE == kModeState ? t < 64 : t < 128;
 
-    QKStage st;
-    if (stager) {
-        qk_load(st, qh, kh, 0, L, t);
-        qk_store<DV>(st, sm, 0, 0, L, t);
-        if (nchunks > 1) qk_load(st, qh, kh, kC, L, t);
-    }
-    __syncthreads();
-
+    __syncthreads();  // first chunk staged, initial state published
     if constexpr (MODE == kModeState) {
-        for (int c = 0; c < nchunks; ++c) {
-            if (stager && c + 1 < nchunks) {
-                qk_store<DV>(st, sm, (c & 1) ^ 1, (c + 1) * kC, L, t);
-                if (c + 2 < nchunks) qk_load(st, qh, kh, (c + 2) * kC, L, t);
-            }
-            __syncthreads();
-        }
+        for (int c = 0; c < nchunks; ++c) __syncthreads();
         return;
     }
+
+    // Outputs of chunk c are normalised and stored during chunk c+1, after
+    // that chunk's first MFMAs are issued, so the MFMA tail of chunk c is
+    // never waited for.
+    f32x4 yprev[kNCT];
+    int prev_t0 = -1;
+    auto store_prev = [&]() {
+        if (prev_t0 < 0) return;
+        const int nprev = min(kC, L - prev_t0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int tq = 16 * W + 4 * g + m;
+            if (tq < nprev) {
+                const float inv = fast_rcp(yprev[kNV][m] + eps);
+                float* yrow = yh + (size_t)(prev_t0 + tq) * ldv + r;
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) yrow[16 * ct] = yprev[ct][m] * inv;
+            }
+        }
+    };
 
     const bf16x8 ones = ones8();
     for (int c = 0; c < nchunks; ++c) {
@@ -484,6 +492,8 @@ __device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, co
             }
         }
 
+        store_prev();  // previous chunk's outputs, behind this chunk's first MFMAs
+
         // ---- off-diagonal term: psi(Q) x (state before this chunk)
         {
             float qr[16];
@@ -533,35 +543,44 @@ __device__ __forceinline__ void readout_wave(const uint16_t* __restrict__ qh, co
 #undef BASED_READOUT_STEP
         }
 
-        // ---- stage the next chunk's Q/K (loaded one chunk ago) and start
-        // loading the one after, before this chunk's output stores: loads
-        // and stores retire through one in-order counter, so the next wait
-        // for these loads must not also wait for the stores.
-        if (stager && c + 1 < nchunks) {
-            qk_store<DV>(st, sm, buf ^ 1, t0 + kC, L, t);
-            if (c + 2 < nchunks) qk_load(st, qh, kh, t0 + 2 * kC, L, t);
-        }
-
-        // ---- normalise and store this chunk's outputs (rows 16W + 4g + m)
+        // ---- hand this chunk's accumulators to the deferred store
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int tq = 16 * W + 4 * g + m;
-            if (tq < n) {
-                const float inv = fast_rcp(y[kNV][m] + eps);
-                float* yrow = yh + (size_t)(t0 + tq) * DV + r;
-#pragma unroll
-                for (int ct = 0; ct < kNV; ++ct) yrow[16 * ct] = y[ct][m] * inv;
-            }
-        }
+        for (int ct = 0; ct < kNCT; ++ct) yprev[ct] = y[ct];
+        prev_t0 = t0;
         if (kSBufs == 1) __syncthreads();  // readouts done: the state operand may be overwritten
         __syncthreads();
     }
+    store_prev();
 }
 
 // ---- update wave U: state rotation tiles U, U+4 (, U+8).
+// Staging registers of one chunk held by an update-wave thread: V^T
+// (every thread) and Q/K (threads 128..255 of the update waves).
+template <int DV>
+struct ChunkRegs {
+    VStage<DV> v;
+    QKStage qk;
+};
+
+template <int DV, int MODE>
+__device__ __forceinline__ void chunk_load(ChunkRegs<DV>& cr, const uint16_t* qh, const uint16_t* kh,
+                                           const uint16_t* vh, int ldv, int t0, int L, int u) {
+    v_load<DV>(cr.v, vh, ldv, t0, L, u);
+    const int t = u - 128;
+    if (t >= 0 && (MODE != kModeState || t < 64)) qk_load(cr.qk, qh, kh, t0, L, t);
+}
+template <int DV, int MODE>
+__device__ __forceinline__ void chunk_store(const ChunkRegs<DV>& cr, PrefillSmem<DV>& sm, int buf, int t0,
+                                            int L, int u) {
+    v_store<DV>(cr.v, sm, buf, t0, L, u);
+    const int t = u - 128;
+    if (t >= 0 && (MODE != kModeState || t < 64)) qk_store<DV>(cr.qk, sm, buf, t0, L, t);
+}
+
 template <int U, int DV, int MODE>
-__device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int L, float* __restrict__ Sh,
-                                            float* __restrict__ zh, int use_init, PrefillSmem<DV>& sm,
+__device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, const uint16_t* __restrict__ kh,
+                                            const uint16_t* __restrict__ vh, int L, int ldv, float* __restrict__ Sh,
+                                            float* __restrict__ zh, bool own_z, int use_init, PrefillSmem<DV>& sm,
                                             const float* ws_in, float* ws_out, bool write_final) {
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
     constexpr int kNT = U < 2 ? 3 : 2;
@@ -583,15 +602,21 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int
         ws_load<U + 4, DV>(acc[1], ws_in, lane);
         if constexpr (kNT == 3) ws_load<U + 8, DV>(acc[2], ws_in, lane);
     } else if (MODE == kModeFull && use_init) {
-        load_initial<U, DV>(acc[0], Sh, zh, g, r);
-        load_initial<U + 4, DV>(acc[1], Sh, zh, g, r);
-        if constexpr (kNT == 3) load_initial<U + 8, DV>(acc[2], Sh, zh, g, r);
+        load_initial<U, DV>(acc[0], Sh, zh, ldv, g, r);
+        load_initial<U + 4, DV>(acc[1], Sh, zh, ldv, g, r);
+        if constexpr (kNT == 3) load_initial<U + 8, DV>(acc[2], Sh, zh, ldv, g, r);
     }
 
-    VStage<DV> st;
-    v_load<DV>(st, vh, 0, L, u);
-    v_store<DV>(st, sm, 0, 0, L, u);
-    if (nchunks > 1) v_load<DV>(st, vh, kC, L, u);
+    // Chunks are prefetched kAhead - 1 chunks beyond the one being staged.
+    // With two register sets (d_v = 64), set A holds the odd chunks and set
+    // B the even ones, so no register copy ever waits on a load in flight;
+    // d_v = 128 has room for one set only.
+    constexpr int kAhead = DV <= 64 ? 3 : 2;
+    ChunkRegs<DV> setA, setB;
+    chunk_load<DV, MODE>(setB, qh, kh, vh, ldv, 0, L, u);
+    if (nchunks > 1) chunk_load<DV, MODE>(setA, qh, kh, vh, ldv, kC, L, u);
+    chunk_store<DV, MODE>(setB, sm, 0, 0, L, u);
+    if (kAhead == 3 && nchunks > 2) chunk_load<DV, MODE>(setB, qh, kh, vh, ldv, 2 * kC, L, u);
     if (MODE != kModeState) {
         publish_state<U, DV>(acc[0], sm, 0, g, r);
         publish_state<U + 4, DV>(acc[1], sm, 0, g, r);
@@ -600,7 +625,9 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int
     __syncthreads();
 
     const bf16x8 ones = ones8();
-    for (int c = 0; c < nchunks; ++c) {
+    // One chunk: update with chunk c, stage chunk c+1 from `regs` (it holds
+    // chunk c+1) and refill `regs` with chunk c+kAhead, publish the state.
+    auto step = [&](int c, ChunkRegs<DV>& regs) {
         const int buf = c & 1;
         const int t0 = c * kC;
         const int n = min(kC, L - t0);
@@ -650,10 +677,10 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int
             }
         }
 
-        // ---- stage the next chunk's V^T, start loading the one after
+        // ---- stage chunk c+1 (loaded kAhead - 1 chunks ago), refill with chunk c+kAhead
         if (c + 1 < nchunks) {
-            v_store<DV>(st, sm, buf ^ 1, t0 + kC, L, u);
-            if (c + 2 < nchunks) v_load<DV>(st, vh, t0 + 2 * kC, L, u);
+            chunk_store<DV, MODE>(regs, sm, buf ^ 1, t0 + kC, L, u);
+            if (c + kAhead < nchunks) chunk_load<DV, MODE>(regs, qh, kh, vh, ldv, t0 + kAhead * kC, L, u);
         }
 
         // ---- publish the state after this chunk for the next readout
@@ -665,6 +692,14 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int
             if constexpr (kNT == 3) publish_state<U + 8, DV>(acc[2], sm, wbuf, g, r);
         }
         __syncthreads();
+    };
+    if constexpr (kAhead == 3) {
+        for (int c = 0; c < nchunks; c += 2) {
+            step(c, setA);                           // chunk c+1 (odd) is in set A
+            if (c + 1 < nchunks) step(c + 1, setB);  // chunk c+2 (even) is in set B
+        }
+    } else {
+        for (int c = 0; c < nchunks; ++c) step(c, setA);
     }
 
     if (MODE == kModeState) {
@@ -672,16 +707,17 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ vh, int
         ws_store<U + 4, DV>(acc[1], ws_out, lane);
         if constexpr (kNT == 3) ws_store<U + 8, DV>(acc[2], ws_out, lane);
     } else if (write_final) {
-        store_final<U, DV>(acc[0], Sh, zh, use_init, g, r);
-        store_final<U + 4, DV>(acc[1], Sh, zh, use_init, g, r);
-        if constexpr (kNT == 3) store_final<U + 8, DV>(acc[2], Sh, zh, use_init, g, r);
+        store_final<U, DV>(acc[0], Sh, zh, ldv, own_z, use_init, g, r);
+        store_final<U + 4, DV>(acc[1], Sh, zh, ldv, own_z, use_init, g, r);
+        if constexpr (kNT == 3) store_final<U + 8, DV>(acc[2], Sh, zh, ldv, own_z, use_init, g, r);
     }
 }
 
 // Initial state of every segment split (state-only pass, last segment slot):
 // the caller's state in readout units, or zero.
 template <int U, int DV>
-__device__ __forceinline__ void init_to_workspace(const float* Sh, const float* zh, int use_init, float* ws_out) {
+__device__ __forceinline__ void init_to_workspace(const float* Sh, const float* zh, int ldv, int use_init,
+                                                  float* ws_out) {
     constexpr int kNCT = DV / 16 + 1;
     constexpr int kNT = U < 2 ? 3 : 2;
     const int lane = (threadIdx.x - 256) & 63, g = lane >> 4, r = lane & 15;
@@ -691,9 +727,9 @@ __device__ __forceinline__ void init_to_workspace(const float* Sh, const float* 
 #pragma unroll
         for (int ct = 0; ct < kNCT; ++ct) acc[ti][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (use_init) {
-        load_initial<U, DV>(acc[0], Sh, zh, g, r);
-        load_initial<U + 4, DV>(acc[1], Sh, zh, g, r);
-        if constexpr (kNT == 3) load_initial<U + 8, DV>(acc[2], Sh, zh, g, r);
+        load_initial<U, DV>(acc[0], Sh, zh, ldv, g, r);
+        load_initial<U + 4, DV>(acc[1], Sh, zh, ldv, g, r);
+        if constexpr (kNT == 3) load_initial<U + 8, DV>(acc[2], Sh, zh, ldv, g, r);
     }
     ws_store<U, DV>(acc[0], ws_out, lane);
     ws_store<U + 4, DV>(acc[1], ws_out, lane);
@@ -733,37 +769,47 @@ template <int DV, int MODE>
 __global__ __launch_bounds__(512, 1) void prefill_mfma_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v, int L,
-                                                              int seg_len, int nseg, float eps,
-                                                              float* __restrict__ y, float* __restrict__ S,
-                                                              float* __restrict__ z, int use_init,
-                                                              float* __restrict__ ws) {
+                                                              int ldv, int ncg, int seg_len, int nseg,
+                                                              float eps, float* __restrict__ y,
+                                                              float* __restrict__ S, float* __restrict__ z,
+                                                              int use_init, float* __restrict__ ws) {
     __shared__ PrefillSmem<DV> sm;
-    const int head = MODE == kModeFull ? blockIdx.x : blockIdx.x / nseg;
-    const int seg = MODE == kModeFull ? 0 : blockIdx.x % nseg;
-    const int BH = MODE == kModeFull ? gridDim.x : gridDim.x / nseg;
+    // Workgroup -> (head, segment, column group), column group fastest.  The
+    // 8 XCDs take workgroups round-robin; the remap gives each XCD a
+    // contiguous run, so the column groups of a head (same Q, K) share an L2.
+    const int total = gridDim.x;
+    int b = blockIdx.x;
+    if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);
+    const int cg = b % ncg;
+    const int hs = b / ncg;
+    const int seg = MODE == kModeFull ? 0 : hs % nseg;
+    const int head = MODE == kModeFull ? hs : hs / nseg;
+    const int BH = total / (ncg * (MODE == kModeFull ? 1 : nseg));
     const int tb = seg * seg_len;
     const int len = MODE == kModeFull ? L : min(seg_len, L - tb);
+    const int col0 = cg * DV;
     const uint16_t* qh = q + ((size_t)head * L + tb) * kDFeat;
     const uint16_t* kh = k + ((size_t)head * L + tb) * kDFeat;
-    const uint16_t* vh = v + ((size_t)head * L + tb) * DV;
-    float* yh = y + ((size_t)head * L + tb) * DV;
-    float* Sh = S + (size_t)head * kNumFeat * DV;
+    const uint16_t* vh = v + ((size_t)head * L + tb) * ldv + col0;
+    float* yh = y + ((size_t)head * L + tb) * ldv + col0;
+    float* Sh = S + (size_t)head * kNumFeat * ldv + col0;
     float* zh = z + (size_t)head * kNumFeat;
+    const bool own_z = cg == 0;  // every column group carries z; the first writes it
     float* ws_in = nullptr;
     float* ws_out = nullptr;
     if (MODE != kModeFull) {
-        ws_in = ws + ((size_t)seg * BH + head) * ws_slot_floats<DV>();
-        ws_out = ws + ((size_t)((seg + 1) % nseg) * BH + head) * ws_slot_floats<DV>();
+        ws_in = ws + (((size_t)seg * BH + head) * ncg + cg) * ws_slot_floats<DV>();
+        ws_out = ws + (((size_t)((seg + 1) % nseg) * BH + head) * ncg + cg) * ws_slot_floats<DV>();
     }
     const int w = threadIdx.x >> 6;
     if (MODE == kModeState && seg == nseg - 1) {
         // This workgroup's slot job is the initial state (no sweep, no barrier).
         if (w >= 4) {
             switch (w) {
-                case 4: init_to_workspace<0, DV>(Sh, zh, use_init, ws_out); break;
-                case 5: init_to_workspace<1, DV>(Sh, zh, use_init, ws_out); break;
-                case 6: init_to_workspace<2, DV>(Sh, zh, use_init, ws_out); break;
-                default: init_to_workspace<3, DV>(Sh, zh, use_init, ws_out); break;
+                case 4: init_to_workspace<0, DV>(Sh, zh, ldv, use_init, ws_out); break;
+                case 5: init_to_workspace<1, DV>(Sh, zh, ldv, use_init, ws_out); break;
+                case 6: init_to_workspace<2, DV>(Sh, zh, ldv, use_init, ws_out); break;
+                default: init_to_workspace<3, DV>(Sh, zh, ldv, use_init, ws_out); break;
             }
         }
         return;
@@ -773,14 +819,14 @@ __global__ __launch_bounds__(512, 1) void prefill_mfma_kernel(const uint16_t* __
     // its SIMD with update wave W (the lighter on-diagonal work of W = 0, 1
     // pairs with the three-tile update waves).
     switch (w) {
-        case 0: readout_wave<0, DV, MODE>(qh, kh, len, eps, yh, sm); break;
-        case 1: readout_wave<1, DV, MODE>(qh, kh, len, eps, yh, sm); break;
-        case 2: readout_wave<2, DV, MODE>(qh, kh, len, eps, yh, sm); break;
-        case 3: readout_wave<3, DV, MODE>(qh, kh, len, eps, yh, sm); break;
-        case 4: update_wave<0, DV, MODE>(vh, len, Sh, zh, use_init, sm, ws_in, ws_out, write_final); break;
-        case 5: update_wave<1, DV, MODE>(vh, len, Sh, zh, use_init, sm, ws_in, ws_out, write_final); break;
-        case 6: update_wave<2, DV, MODE>(vh, len, Sh, zh, use_init, sm, ws_in, ws_out, write_final); break;
-        default: update_wave<3, DV, MODE>(vh, len, Sh, zh, use_init, sm, ws_in, ws_out, write_final); break;
+        case 0: readout_wave<0, DV, MODE>(len, ldv, eps, yh, sm); break;
+        case 1: readout_wave<1, DV, MODE>(len, ldv, eps, yh, sm); break;
+        case 2: readout_wave<2, DV, MODE>(len, ldv, eps, yh, sm); break;
+        case 3: readout_wave<3, DV, MODE>(len, ldv, eps, yh, sm); break;
+        case 4: update_wave<0, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
+        case 5: update_wave<1, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
+        case 6: update_wave<2, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
+        default: update_wave<3, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
     }
 }
 
@@ -801,52 +847,82 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
     }
 }
 
-// Segments per head: enough workgroups for one per compute unit (the LDS
-// footprint allows one resident workgroup per CU), segments of at least two
-// chunks.  From half the chip upwards the extra state pass costs about what
-// the added parallelism gains, so such shapes run unsplit.
+// Launch shape.  Value columns are split into groups of `dvl` (each group
+// carries its own copy of the normaliser tile and recomputes the features),
+// and long sequences into segments, until there are enough workgroups for
+// one per compute unit (the LDS footprint allows one resident workgroup per
+// CU).  Segments cost an extra state pass, so they are added only when the
+// heads x column groups fill less than the chip.
 constexpr int kTargetWorkgroups = 256;
-int choose_segments(int BH, int L) {
+struct PrefillPlan {
+    int dvl, ncg, nseg;
+};
+PrefillPlan plan_prefill(int BH, int L, int dv, bool use_init, bool have_ws) {
+    PrefillPlan pl;
+    pl.dvl = (dv == 128 && BH * 4 > 1024) ? 64 : 32;
+    pl.ncg = dv / pl.dvl;
     const int nchunks = (L + kC - 1) / kC;
-    if (2 * BH >= kTargetWorkgroups || nchunks < 4) return 1;
-    int nseg = (kTargetWorkgroups + BH - 1) / BH;
-    nseg = min(nseg, nchunks / 2);
-    return max(nseg, 1);
+    const int units = BH * pl.ncg;
+    pl.nseg = 1;
+    if (units < kTargetWorkgroups && nchunks >= 4)
+        pl.nseg = max(1, min((kTargetWorkgroups + units - 1) / units, nchunks / 2));
+    // With an initial state and several column groups, the carried state
+    // goes through the workspace (no group may overwrite z while another
+    // still reads it); without a workspace, fall back to one group.
+    const bool need_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
+    if (need_ws && !have_ws) {
+        pl.dvl = dv;
+        pl.ncg = 1;
+        pl.nseg = 1;
+    }
+    return pl;
 }
 
-template <int DV>
-size_t workspace_bytes_dv(int BH, int nseg) {
-    return nseg <= 1 ? 0 : (size_t)nseg * BH * ws_slot_floats<DV>() * sizeof(float);
+template <int DVL>
+size_t workspace_bytes_dvl(int BH, int ncg, int nseg) {
+    return (size_t)nseg * BH * ncg * ws_slot_floats<DVL>() * sizeof(float);
 }
 
-template <int DV>
-hipError_t launch_dv(const uint16_t* q, const uint16_t* k, const uint16_t* v, int BH, int L, float eps, float* y,
-                     float* S, float* z, int use_init, void* ws, size_t ws_bytes, hipStream_t st) {
-    const int nseg = choose_segments(BH, L);
-    if (nseg <= 1 || ws == nullptr || ws_bytes < workspace_bytes_dv<DV>(BH, nseg)) {
-        hipLaunchKernelGGL((prefill_mfma_kernel<DV, kModeFull>), dim3(BH), dim3(512), 0, st, q, k, v, L, L, 1, eps,
-                           y, S, z, use_init, nullptr);
+size_t plan_workspace_bytes(const PrefillPlan& pl, int BH) {
+    switch (pl.dvl) {
+        case 32: return workspace_bytes_dvl<32>(BH, pl.ncg, pl.nseg);
+        case 64: return workspace_bytes_dvl<64>(BH, pl.ncg, pl.nseg);
+        default: return workspace_bytes_dvl<128>(BH, pl.ncg, pl.nseg);
+    }
+}
+
+template <int DVL>
+hipError_t launch_plan(const PrefillPlan& pl, const uint16_t* q, const uint16_t* k, const uint16_t* v, int BH,
+                       int L, int dv, float eps, float* y, float* S, float* z, int use_init, void* ws,
+                       hipStream_t st) {
+    const bool via_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
+    if (!via_ws) {
+        hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeFull>), dim3(BH * pl.ncg), dim3(512), 0, st, q, k, v, L,
+                           dv, pl.ncg, L, 1, eps, y, S, z, use_init, nullptr);
         return hipGetLastError();
     }
     const int nchunks = (L + kC - 1) / kC;
-    const int seg_len = ((nchunks + nseg - 1) / nseg) * kC;
-    const int nseg_eff = (L + seg_len - 1) / seg_len;
+    const int seg_len = ((nchunks + pl.nseg - 1) / pl.nseg) * kC;
+    const int nseg = (L + seg_len - 1) / seg_len;
     float* wsf = static_cast<float*>(ws);
-    hipLaunchKernelGGL((prefill_mfma_kernel<DV, kModeState>), dim3(BH * nseg_eff), dim3(512), 0, st, q, k, v, L,
-                       seg_len, nseg_eff, eps, y, S, z, use_init, wsf);
-    const size_t slot = ws_slot_floats<DV>();
-    hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH), dim3(256), 0, st, wsf,
-                       nseg_eff, BH, slot);
-    hipLaunchKernelGGL((prefill_mfma_kernel<DV, kModeSegment>), dim3(BH * nseg_eff), dim3(512), 0, st, q, k, v,
-                       L, seg_len, nseg_eff, eps, y, S, z, use_init, wsf);
+    const dim3 grid(BH * pl.ncg * nseg);
+    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeState>), grid, dim3(512), 0, st, q, k, v, L, dv, pl.ncg,
+                       seg_len, nseg, eps, y, S, z, use_init, wsf);
+    const size_t slot = ws_slot_floats<DVL>();
+    hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH * pl.ncg), dim3(256), 0, st,
+                       wsf, nseg, BH * pl.ncg, slot);
+    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeSegment>), grid, dim3(512), 0, st, q, k, v, L, dv, pl.ncg,
+                       seg_len, nseg, eps, y, S, z, use_init, wsf);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t prefill_mfma_workspace_bytes(int BH, int L, int dv) {
-    const int nseg = choose_segments(BH, L);
-    return dv == 64 ? workspace_bytes_dv<64>(BH, nseg) : workspace_bytes_dv<128>(BH, nseg);
+    // Enough for any plan this shape can take (an initial state may need it).
+    const PrefillPlan pl = plan_prefill(BH, L, dv, true, true);
+    const bool via_ws = pl.nseg > 1 || pl.ncg > 1;
+    return via_ws ? plan_workspace_bytes(pl, BH) : 0;
 }
 
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int BH, int L, int dv,
@@ -855,8 +931,14 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int 
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     const uint16_t* vv = static_cast<const uint16_t*>(v);
-    if (dv == 64) return launch_dv<64>(qq, kk, vv, BH, L, eps, y, S, z, use_init, ws, ws_bytes, st);
-    return launch_dv<128>(qq, kk, vv, BH, L, eps, y, S, z, use_init, ws, ws_bytes, st);
+    PrefillPlan pl = plan_prefill(BH, L, dv, use_init != 0, ws != nullptr);
+    const bool via_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
+    if (via_ws && ws_bytes < plan_workspace_bytes(pl, BH)) pl = plan_prefill(BH, L, dv, use_init != 0, false);
+    switch (pl.dvl) {
+        case 32: return launch_plan<32>(pl, qq, kk, vv, BH, L, dv, eps, y, S, z, use_init, ws, st);
+        case 64: return launch_plan<64>(pl, qq, kk, vv, BH, L, dv, eps, y, S, z, use_init, ws, st);
+        default: return launch_plan<128>(pl, qq, kk, vv, BH, L, dv, eps, y, S, z, use_init, ws, st);
+    }
 }
 
 }  // namespace based

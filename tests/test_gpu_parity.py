@@ -93,6 +93,51 @@ def test_prefill_resume_from_state(dtype, tol):
     report(f"resume {dtype} z", ratio(z2, zo), tol)
 
 
+@pytest.mark.parametrize("L", [70, 900])
+@pytest.mark.parametrize("dv", [64, 128])
+@pytest.mark.parametrize("ws", ["auto", "none"])
+def test_prefill_random_initial_state(L, dv, ws):
+    """An arbitrary (asymmetric) carried state: outputs see its symmetric
+    part, the returned state is the initial one plus this call's increment.
+    ws="none" hands over an empty workspace, which must fall back to a
+    launch shape that needs none."""
+    based = based_mod()
+    q, k, v = si.custom((1, 3, L, 16), (1, 3, L, dv), seed=710 + L + dv, scale=0.5)
+    # a reachable state (oracle state after a 50-token prefix, so every
+    # denominator stays positive) plus an antisymmetric part in the pair rows
+    qp, kp, vp = si.custom((1, 3, 50, 16), (1, 3, 50, dv), seed=712 + L, scale=0.5)
+    _, S0, z0 = oracle.la_recurrent(qp, kp, vp, want_y=False)
+    S0, z0 = torch.as_tensor(S0, dtype=torch.float32), torch.as_tensor(z0, dtype=torch.float32)
+    g = torch.Generator().manual_seed(711 + L)
+    P = torch.randn((1, 3, 16, 16, dv), generator=g)
+    S0[:, :, 17:] += (P - P.transpose(2, 3)).reshape(1, 3, 256, dv)
+    Pz = torch.randn((1, 3, 16, 16), generator=g)
+    z0[:, :, 17:] += (Pz - Pz.transpose(2, 3)).reshape(1, 3, 256)
+    kw = {} if ws == "auto" else {"workspace": torch.empty(0, dtype=torch.uint8, device=DEV)}
+    y, S, z = based.based_prefill(*dev(q, k, v), initial_state=tuple(dev(S0, z0)), **kw)
+    yo, So, zo = oracle.la_recurrent(q, k, v, S0=S0, z0=z0)
+    report(f"init-state L={L} dv={dv} ws={ws} y", ratio(y, yo), 2e-2)
+    report(f"init-state L={L} dv={dv} ws={ws} S", ratio(S, So), 2e-2)
+    report(f"init-state L={L} dv={dv} ws={ws} z", ratio(z, zo), 2e-2)
+
+
+@pytest.mark.parametrize("dv", [64, 128])
+def test_prefill_many_heads(dv):
+    """Enough heads that each one runs unsplit in length (and, for d_v = 128,
+    in wider column groups)."""
+    based = based_mod()
+    q, k, v = si.custom((2, 132, 70, 16), (2, 132, 70, dv), seed=720 + dv, scale=0.5)
+    y, S, z = based.based_prefill(*dev(q, k, v))
+    torch.cuda.synchronize()
+    pick = [(0, 0), (0, 131), (1, 64), (1, 131)]
+    for b, h in pick:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        yo, So, zo = oracle.la_recurrent(q[sl], k[sl], v[sl])
+        report(f"many-heads dv={dv} ({b},{h}) y", ratio(y[sl], yo), 2e-2)
+        report(f"many-heads dv={dv} ({b},{h}) S", ratio(S[sl], So), 2e-2)
+        report(f"many-heads dv={dv} ({b},{h}) z", ratio(z[sl], zo), 2e-2)
+
+
 def test_prefill_deterministic():
     based = based_mod()
     q, k, v = dev(*si.custom((2, 2, 300, 16), (2, 2, 300, 64), seed=800, scale=0.5))
