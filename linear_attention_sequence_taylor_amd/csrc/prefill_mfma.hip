@@ -46,19 +46,37 @@ namespace {
 
 constexpr int kC = 64;        // chunk length
 constexpr int kSlots = 160;   // 10 rotation tiles x 16 feature rows
-constexpr int kSRow = 168;    // LDS row stride (bf16) of the state operand [col][slot]
+constexpr int kSRow = 176;    // LDS row stride (bf16) of the state operand [col][slot]
 constexpr int kLoSlots = 32;  // slots of the last feature k-step (tiles 8, 9)
-constexpr int kLoRow = 40;    // LDS row stride (bf16) of their lo parts
-constexpr int kTRow = 72;     // LDS row stride (bf16) of V^T and K^T [row][token]
-constexpr int kQRow = 20;     // LDS row stride (bf16) of Q and K [token][dim]
-constexpr int kKtRow = 68;    // LDS row stride (fp32) of K^T/4 [dim][token]
-constexpr int kQfRow = 20;    // LDS row stride (fp32) of Q [token][dim]
+constexpr int kLoRow = 48;    // LDS row stride (bf16) of their lo parts
+constexpr int kTRow = 64;     // LDS row stride (bf16) of V^T [col][token]
+constexpr int kQRow = 24;     // LDS row stride (bf16) of Q and K [token][dim]
+constexpr int kKtRow = 72;    // LDS row stride (fp32) of K^T/4 [dim][token]
+constexpr int kQfRow = 16;    // LDS row stride (fp32) of Q [token][dim]
 constexpr float kSqrt2 = 1.41421356237309504880f;
-constexpr uint16_t kBf16One = 0x3F80;
+
+// Staging layouts.  Each row is cut into 16-byte units whose order is
+// XOR-swizzled by a few row bits, chosen (by the gfx950 LDS bank mapping:
+// 64 banks for 16-byte reads serviced 16 lanes at a time, 32 banks for
+// writes) so that every read and write pattern below is conflict-free or
+// at most two-way.  All vector accesses stay inside one unit.
+__device__ __forceinline__ int vt_idx(int row, int tok) {  // V^T: 8 tokens per unit
+    return row * kTRow + 8 * ((tok >> 3) ^ ((row >> 1) & 7)) + (tok & 7);
+}
+__device__ __forceinline__ int kt_idx(int row, int tok) {  // K^T fp32: 4 tokens per unit
+    return row * kKtRow + 4 * ((tok >> 2) ^ (row & 1)) + (tok & 3);
+}
+__device__ __forceinline__ int qf_idx(int row, int dim) {  // Q fp32: 4 dims per unit
+    return row * kQfRow + 4 * ((dim >> 2) ^ ((row >> 1) & 3)) + (dim & 3);
+}
+__device__ __forceinline__ int qk_idx(int row, int dim) {  // Q, K bf16: 8 dims per unit
+    return row * kQRow + 8 * ((dim >> 3) ^ ((row >> 3) & 1)) + (dim & 7);
+}
 
 template <int DV>
 struct PrefillSmem {
-    static constexpr int kSBufs = DV <= 64 ? 2 : 1;  // state operand buffers
+    static_assert(DV == 32 || DV == 64, "column group width");
+    static constexpr int kSBufs = 2;  // state operand buffers
     alignas(16) uint16_t q[2][kC * kQRow];
     alignas(16) uint16_t k[2][kC * kQRow];
     alignas(16) float ktf[2][kDFeat * kKtRow];  // K^T scaled by 1/4 (update waves)
@@ -68,6 +86,8 @@ struct PrefillSmem {
     alignas(16) uint16_t s_lo[kSBufs][DV * kLoRow];
     alignas(16) uint16_t z_hi[kSBufs][kSlots];
     alignas(16) uint16_t z_lo[kSBufs][kLoSlots];
+    // off-diagonal hand-off: [chunk parity][query tile][column tile][lane] f32x4
+    alignas(16) float hand[2][4][(DV / 16 + 1) * 64 * 4];
 };
 
 enum { kModeFull = 0, kModeState = 1, kModeSegment = 2 };
@@ -129,22 +149,20 @@ __device__ __forceinline__ bf16x8 join44(const uint16_t* p0, const uint16_t* p1)
     u32x4 u = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(bf16x8, u);
 }
-// 1/x: hardware reciprocal refined by one Newton step (~0.5 ulp).
-__device__ __forceinline__ float fast_rcp(float x) {
-    const float r = __builtin_amdgcn_rcpf(x);
-    return fmaf(r, fmaf(-x, r, 1.f), r);
-}
 __device__ __forceinline__ bf16x8 ones8() {
     u32x4 u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     return __builtin_bit_cast(bf16x8, u);
 }
 
-// Readout slot of rotation tile T, rows 4g..4g+3 (4 consecutive slots).
-template <int T>
-__device__ __forceinline__ int readout_slot(int g) {
-    constexpr int j = T >> 1;
-    return (T & 1) ? 32 * j + 8 * ((g + 3) & 3) + 4 : 32 * j + 8 * g;
-}
+// State operand layout.  The contraction index of readout k-step J
+// (32 slots) is k = 8g + i: tile J (i < 4) or J + 4 (i >= 4) for J < 4,
+// tiles 8 and 9 for J = 4, row 4g + (i & 3).  Those are exactly the rows
+// update lane (g, r) holds in its accumulators for tiles U and U + 4, so
+// each lane publishes a whole 16-byte unit (unit 4J + g of row r).  Within
+// a row the 16-byte units are XOR-swizzled by bit 2 of the row so that the
+// readout's 16-byte reads (row r = lane & 15) and the publish writes are
+// free of LDS bank conflicts.
+__device__ __forceinline__ int unit_swz(int u, int row) { return u ^ ((row >> 2) & 1); }
 
 // ---------------------------------------------------------------- 273-row state map
 // Rows of the caller's state for rotation tile T, row r.  Returns the
@@ -160,23 +178,22 @@ __device__ __forceinline__ int state_rows(int r, int& r0, int& r1) {
     return T == 0 ? 1 : 2;
 }
 // ---------------------------------------------------------------- feature operands
-// psi(Q) for readout k-step J: lane (query row, group g) holds slots
-// 32J + 8g + i, i.e. rotation tile 2J + (i>>2), row (4g + i) mod 16.
+// psi(Q) for readout k-step J: lane (query row, group g) holds the
+// features k = 8g + i of the state operand layout above.
 // qr[m] = raw q_((4g + m) mod 16) of the lane's query.
 template <int J>
 __device__ __forceinline__ void psi_q(const float (&qr)[16], int g, float (&a)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int T = 2 * J + (i >> 2);
-        if (T == 0) {
-            a[i] = qr[i] * qr[i];
-        } else if (T < 8) {
-            a[i] = qr[i] * qr[(i + T) & 15];
-        } else if (T == 8) {
-            const float p = qr[i] * qr[(i + 8) & 15];
-            a[i] = g < 2 ? p : ((g == 2 && i == 0) ? 1.f : 0.f);
+        const int m = i & 3;
+        if (J < 4) {
+            const int T = i < 4 ? J : J + 4;  // pair (row, row + T)
+            a[i] = T == 0 ? qr[m] * qr[m] : qr[m] * qr[m + T];
+        } else if (i < 4) {
+            // tile 8: pairs (row, row + 8) for rows < 8, the constant at row 8
+            a[i] = g < 2 ? qr[m] * qr[m + 8] : ((g == 2 && m == 0) ? 1.f : 0.f);
         } else {
-            a[i] = qr[i];
+            a[i] = qr[m];  // tile 9: linear terms
         }
     }
 }
@@ -195,26 +212,41 @@ __device__ __forceinline__ float state_scale(int r) {
     return 2.f * kSqrt2;
 }
 
-template <int T, int DV>
-__device__ __forceinline__ void publish_state(const f32x4 (&acc)[DV / 16 + 1], PrefillSmem<DV>& sm,
-                                              int sbuf, int g, int r) {
+// Tiles J and J + 4 (J < 4): one 16-byte unit per lane and column tile.
+template <int J, int DV>
+__device__ __forceinline__ void publish_pair(const f32x4 (&a)[DV / 16 + 1], const f32x4 (&b)[DV / 16 + 1],
+                                             PrefillSmem<DV>& sm, int sbuf, int g, int r) {
     constexpr int kNV = DV / 16;
-    const int slot = readout_slot<T>(g);
+    const int u = 4 * J + g;
 #pragma unroll
     for (int ct = 0; ct <= kNV; ++ct) {
         if (ct == kNV && r != 0) continue;  // the normaliser tile has 16 equal columns
-        const uint32_t h01 = pack_bf16x2(acc[ct][0], acc[ct][1]);
-        const uint32_t h23 = pack_bf16x2(acc[ct][2], acc[ct][3]);
-        uint2* hi = ct < kNV ? reinterpret_cast<uint2*>(&sm.s_hi[sbuf][(16 * ct + r) * kSRow + slot])
-                             : reinterpret_cast<uint2*>(&sm.z_hi[sbuf][slot]);
+        const u32x4 x = {pack_bf16x2(a[ct][0], a[ct][1]), pack_bf16x2(a[ct][2], a[ct][3]),
+                         pack_bf16x2(b[ct][0], b[ct][1]), pack_bf16x2(b[ct][2], b[ct][3])};
+        u32x4* dst = ct < kNV ? reinterpret_cast<u32x4*>(&sm.s_hi[sbuf][(16 * ct + r) * kSRow + 8 * unit_swz(u, r)])
+                              : reinterpret_cast<u32x4*>(&sm.z_hi[sbuf][8 * u]);
+        *dst = x;
+    }
+}
+// Tile 8 (H = 0) or 9 (H = 1): half H of unit 16 + g, as a hi/lo pair.
+template <int H, int DV>
+__device__ __forceinline__ void publish_last(const f32x4 (&a)[DV / 16 + 1], PrefillSmem<DV>& sm, int sbuf, int g,
+                                             int r) {
+    constexpr int kNV = DV / 16;
+#pragma unroll
+    for (int ct = 0; ct <= kNV; ++ct) {
+        if (ct == kNV && r != 0) continue;
+        const uint32_t h01 = pack_bf16x2(a[ct][0], a[ct][1]);
+        const uint32_t h23 = pack_bf16x2(a[ct][2], a[ct][3]);
+        const uint32_t l01 = pack_bf16x2(a[ct][0] - bf16lo_f32(h01), a[ct][1] - bf16hi_f32(h01));
+        const uint32_t l23 = pack_bf16x2(a[ct][2] - bf16lo_f32(h23), a[ct][3] - bf16hi_f32(h23));
+        uint2* hi = ct < kNV
+                        ? reinterpret_cast<uint2*>(&sm.s_hi[sbuf][(16 * ct + r) * kSRow + 8 * unit_swz(16 + g, r) + 4 * H])
+                        : reinterpret_cast<uint2*>(&sm.z_hi[sbuf][8 * (16 + g) + 4 * H]);
+        uint2* lo = ct < kNV ? reinterpret_cast<uint2*>(&sm.s_lo[sbuf][(16 * ct + r) * kLoRow + 8 * unit_swz(g, r) + 4 * H])
+                             : reinterpret_cast<uint2*>(&sm.z_lo[sbuf][8 * g + 4 * H]);
         *hi = make_uint2(h01, h23);
-        if (T >= 8) {
-            const uint32_t l01 = pack_bf16x2(acc[ct][0] - bf16lo_f32(h01), acc[ct][1] - bf16hi_f32(h01));
-            const uint32_t l23 = pack_bf16x2(acc[ct][2] - bf16lo_f32(h23), acc[ct][3] - bf16hi_f32(h23));
-            uint2* lo = ct < kNV ? reinterpret_cast<uint2*>(&sm.s_lo[sbuf][(16 * ct + r) * kLoRow + slot - 128])
-                                 : reinterpret_cast<uint2*>(&sm.z_lo[sbuf][slot - 128]);
-            *lo = make_uint2(l01, l23);
-        }
+        *lo = make_uint2(l01, l23);
     }
 }
 
@@ -337,8 +369,8 @@ __device__ __forceinline__ void qk_store(const QKStage& in, PrefillSmem<DV>& sm,
     const u32x4 a0 = keep_if(in.a0, t0 + 2 * p < L), a1 = keep_if(in.a1, t0 + 2 * p + 1 < L);
     const int db = (t >> 5) & 1;
     uint16_t* rowm = t < 64 ? &sm.k[buf][0] : &sm.q[buf][0];
-    uint2* ra = reinterpret_cast<uint2*>(rowm + (2 * p) * kQRow + 8 * db);
-    uint2* rb = reinterpret_cast<uint2*>(rowm + (2 * p + 1) * kQRow + 8 * db);
+    uint2* ra = reinterpret_cast<uint2*>(rowm + qk_idx(2 * p, 8 * db));
+    uint2* rb = reinterpret_cast<uint2*>(rowm + qk_idx(2 * p + 1, 8 * db));
     ra[0] = make_uint2(a0[0], a0[1]);
     ra[1] = make_uint2(a0[2], a0[3]);
     rb[0] = make_uint2(a1[0], a1[1]);
@@ -348,27 +380,26 @@ __device__ __forceinline__ void qk_store(const QKStage& in, PrefillSmem<DV>& sm,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int d0 = 8 * db + 2 * e;
-            *reinterpret_cast<float2*>(kt + d0 * kKtRow + 2 * p) =
+            *reinterpret_cast<float2*>(kt + kt_idx(d0, 2 * p)) =
                 make_float2(0.25f * bf16lo_f32(a0[e]), 0.25f * bf16lo_f32(a1[e]));
-            *reinterpret_cast<float2*>(kt + (d0 + 1) * kKtRow + 2 * p) =
+            *reinterpret_cast<float2*>(kt + kt_idx(d0 + 1, 2 * p)) =
                 make_float2(0.25f * bf16hi_f32(a0[e]), 0.25f * bf16hi_f32(a1[e]));
         }
     } else {
-        float* qa = &sm.qf[buf][(2 * p) * kQfRow + 8 * db];
-        float* qb = &sm.qf[buf][(2 * p + 1) * kQfRow + 8 * db];
+        float* qf = &sm.qf[buf][0];
         f32x4 x;
         x = f32x4{bf16lo_f32(a0[0]), bf16hi_f32(a0[0]), bf16lo_f32(a0[1]), bf16hi_f32(a0[1])};
-        *reinterpret_cast<f32x4*>(qa) = x;
+        *reinterpret_cast<f32x4*>(qf + qf_idx(2 * p, 8 * db)) = x;
         x = f32x4{bf16lo_f32(a0[2]), bf16hi_f32(a0[2]), bf16lo_f32(a0[3]), bf16hi_f32(a0[3])};
-        *reinterpret_cast<f32x4*>(qa + 4) = x;
+        *reinterpret_cast<f32x4*>(qf + qf_idx(2 * p, 8 * db + 4)) = x;
         x = f32x4{bf16lo_f32(a1[0]), bf16hi_f32(a1[0]), bf16lo_f32(a1[1]), bf16hi_f32(a1[1])};
-        *reinterpret_cast<f32x4*>(qb) = x;
+        *reinterpret_cast<f32x4*>(qf + qf_idx(2 * p + 1, 8 * db)) = x;
         x = f32x4{bf16lo_f32(a1[2]), bf16hi_f32(a1[2]), bf16lo_f32(a1[3]), bf16hi_f32(a1[3])};
-        *reinterpret_cast<f32x4*>(qb + 4) = x;
+        *reinterpret_cast<f32x4*>(qf + qf_idx(2 * p + 1, 8 * db + 4)) = x;
     }
 }
-// u (0..255 of the update waves): token pair p = u & 31, column blocks
-// (u >> 5) + 8*pass of 8 columns (a 32-column group uses threads 0..127).
+// u (0..255, or 0..127 for a 32-column group): token pair p = u & 31,
+// column blocks (u >> 5) + 8*pass of 8 columns.
 // ldv is the row stride of v in the caller's tensor.
 template <int DV>
 __device__ __forceinline__ void v_load(VStage<DV>& st, const uint16_t* vh, int ldv, int t0, int L, int u) {
@@ -394,20 +425,194 @@ __device__ __forceinline__ void v_store(const VStage<DV>& st, PrefillSmem<DV>& s
         const u32x4 v0 = keep_if(st.v0[ps], oka), v1 = keep_if(st.v1[ps], okb);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            vt[((8 * cb + 2 * e) * kTRow + 2 * p) >> 1] = lo_pair(v0[e], v1[e]);
-            vt[((8 * cb + 2 * e + 1) * kTRow + 2 * p) >> 1] = hi_pair(v0[e], v1[e]);
+            vt[vt_idx(8 * cb + 2 * e, 2 * p) >> 1] = lo_pair(v0[e], v1[e]);
+            vt[vt_idx(8 * cb + 2 * e + 1, 2 * p) >> 1] = hi_pair(v0[e], v1[e]);
         }
     }
 }
 
-// ---- readout wave W: query tile W (rows 16W..16W+15) of every chunk.
+// ---- staging pipeline: chunk c+1 is written to LDS during interval c from
+// registers loaded two intervals earlier; two register sets alternate (set
+// A holds the odd chunks, set B the even ones), so no register copy waits on
+// a load in flight.  V^T is staged by update-wave threads (vu >= 0), Q and K
+// by off-diagonal-wave threads (t >= 0, K for t < 64).
+template <int DV, bool DO_V, bool DO_QK>
+struct StagePipe {
+    struct Regs {
+        VStage<DV> v;
+        QKStage qk;
+    };
+    Regs a, b;
+    int vu, t;
+    const uint16_t *qh, *kh, *vh;
+    int ldv, L;
+
+    __device__ __forceinline__ void load(Regs& rg, int t0) {
+        if (DO_V && vu >= 0) v_load<DV>(rg.v, vh, ldv, t0, L, vu);
+        if (DO_QK && t >= 0) qk_load(rg.qk, qh, kh, t0, L, t);
+    }
+    __device__ __forceinline__ void store(const Regs& rg, PrefillSmem<DV>& sm, int buf, int t0) {
+        if (DO_V && vu >= 0) v_store<DV>(rg.v, sm, buf, t0, L, vu);
+        if (DO_QK && t >= 0) qk_store<DV>(rg.qk, sm, buf, t0, L, t);
+    }
+    // chunk 0 into LDS buffer 0; chunks 1 and 2 in flight
+    __device__ __forceinline__ void prologue(PrefillSmem<DV>& sm, int nchunks) {
+        load(b, 0);
+        if (nchunks > 1) load(a, kC);
+        store(b, sm, 0, 0);
+        if (nchunks > 2) load(b, 2 * kC);
+    }
+    // interval c: stage chunk c+1 (held in rg) and refill rg with chunk c+3
+    __device__ __forceinline__ void advance(Regs& rg, PrefillSmem<DV>& sm, int c, int nchunks) {
+        if (c + 1 < nchunks) {
+            store(rg, sm, (c + 1) & 1, (c + 1) * kC);
+            if (c + 3 < nchunks) load(rg, (c + 3) * kC);
+        }
+    }
+};
+
+// ---- on-diagonal term of query tile DQ (rows 16DQ..16DQ+15) of one chunk:
+// s^T for key tiles 0..DQ, causal weights 1 + s + s^2/2 (hi/lo bf16 pair)
+// times V and the ones column, in MFMA accumulator layout.
+template <int DQ, int DV>
+__device__ __forceinline__ void diag_block(const PrefillSmem<DV>& sm, int buf, int lane, int g, int r,
+                                          f32x4 (&y)[DV / 16 + 1]) {
+    constexpr int kNV = DV / 16, kNCT = kNV + 1;
+    const uint16_t* q_l = &sm.q[buf][0];
+    const uint16_t* k_l = &sm.k[buf][0];
+    const uint16_t* vt_l = &sm.vt[buf][0];
+    const bf16x8 ones = ones8();
+#pragma unroll
+    for (int ct = 0; ct < kNCT; ++ct) y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16x4 qb = lds_bf16x4(q_l + qk_idx(16 * DQ + r, 4 * g));
+    float wgt[DQ + 1][4];
+#pragma unroll
+    for (int j = 0; j <= DQ; ++j) {
+        const bf16x4 ka = lds_bf16x4(k_l + qk_idx(16 * j + r, 4 * g));
+        const f32x4 s = mfma16(ka, qb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            // s[m] = q_query . k_key (raw), key = 16j + 4g + m, query = 16DQ + r
+            const float w = fmaf(s[m], fmaf(s[m], 1.f / 32.f, 0.25f), 1.f);
+            wgt[j][m] = (j == DQ && 4 * g + m > r) ? 0.f : w;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p <= DQ / 2; ++p) {
+        float a[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            a[m] = wgt[2 * p][m];
+            a[4 + m] = (2 * p + 1 <= DQ) ? wgt[(2 * p + 1 <= DQ) ? 2 * p + 1 : 0][m] : 0.f;
+        }
+        bf16x8 ahi, alo;
+        pack8_hilo(a, ahi, alo);
+        bf16x8 vb[kNV];
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct)
+            vb[ct] = join44(vt_l + vt_idx(16 * ct + r, 32 * p + 4 * g), vt_l + vt_idx(16 * ct + r, 32 * p + 16 + 4 * g));
+        // hi parts of every column tile first, then the lo parts, so
+        // consecutive MFMAs never depend on each other
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) y[ct] = mfma32(ahi, vb[ct], y[ct]);
+        y[kNV] = mfma32(ahi, ones, y[kNV]);
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) y[ct] = mfma32(alo, vb[ct], y[ct]);
+        y[kNV] = mfma32(alo, ones, y[kNV]);
+    }
+}
+
+// ---- off-diagonal wave W: psi(Q_c) x S_c (state before chunk c) for query
+// tile W (rows 16W..16W+15), handed to the on-diagonal wave of that tile.
 template <int W, int DV, int MODE>
-__device__ __forceinline__ void readout_wave(int L, int ldv, float eps, float* __restrict__ yh,
+__device__ __forceinline__ void offdiag_wave(const uint16_t* __restrict__ qh, const uint16_t* __restrict__ kh, int L,
                                              PrefillSmem<DV>& sm) {
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
-    constexpr int kSBufs = PrefillSmem<DV>::kSBufs;
-    const int t = threadIdx.x;  // 0..255
-    const int lane = t & 63, g = lane >> 4, r = lane & 15;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const int nchunks = (L + kC - 1) / kC;
+    // Q and K staging: waves 2 (K) and 3 (Q); only K without outputs
+    StagePipe<DV, false, true> pipe;
+    pipe.vu = -1;
+    pipe.t = W < 2 ? -1 : ((MODE == kModeState && W == 3) ? -1 : (int)threadIdx.x - 128);
+    pipe.qh = qh;
+    pipe.kh = kh;
+    pipe.vh = nullptr;
+    pipe.ldv = 0;
+    pipe.L = L;
+    if (W >= 2) pipe.prologue(sm, nchunks);
+
+    __syncthreads();  // first chunk staged, initial state published
+    auto step = [&](int c, typename StagePipe<DV, false, true>::Regs& regs) {
+        if (MODE != kModeState) {
+            const int buf = c & 1;
+            f32x4 y[kNCT];
+#pragma unroll
+            for (int ct = 0; ct < kNCT; ++ct) y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float qr[16];
+            const float* qf = &sm.qf[buf][0];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(qf + qf_idx(16 * W + r, 4 * ((g + cc) & 3)));
+                qr[4 * cc + 0] = x[0];
+                qr[4 * cc + 1] = x[1];
+                qr[4 * cc + 2] = x[2];
+                qr[4 * cc + 3] = x[3];
+            }
+            const uint16_t* shi = &sm.s_hi[buf][0];
+            const uint16_t* slo = &sm.s_lo[buf][0];
+#define BASED_READOUT_STEP(J)                                                                             \
+    {                                                                                                     \
+        float a[8];                                                                                       \
+        psi_q<J>(qr, g, a);                                                                               \
+        const bf16x8 ahi = pack8(a);                                                                      \
+        _Pragma("unroll") for (int ct = 0; ct < kNV; ++ct)                                                \
+            y[ct] = mfma32(ahi, lds_bf16x8(shi + (16 * ct + r) * kSRow + 8 * unit_swz(4 * (J) + g, r)), y[ct]); \
+        y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_hi[buf][8 * (4 * (J) + g)]), y[kNV]);                       \
+    }
+            BASED_READOUT_STEP(0)
+            BASED_READOUT_STEP(1)
+            BASED_READOUT_STEP(2)
+            BASED_READOUT_STEP(3)
+#undef BASED_READOUT_STEP
+            // last feature k-step (pairs (r, r+8), constant, linear): hi/lo on both sides
+            float a[8];
+            psi_q<4>(qr, g, a);
+            bf16x8 ahi, alo;
+            pack8_hilo(a, ahi, alo);
+            bf16x8 sb[kNCT];
+#pragma unroll
+            for (int ct = 0; ct < kNV; ++ct) sb[ct] = lds_bf16x8(shi + (16 * ct + r) * kSRow + 8 * unit_swz(16 + g, r));
+            sb[kNV] = lds_bf16x8(&sm.z_hi[buf][8 * (16 + g)]);
+#pragma unroll
+            for (int ct = 0; ct < kNCT; ++ct) y[ct] = mfma32(ahi, sb[ct], y[ct]);
+#pragma unroll
+            for (int ct = 0; ct < kNCT; ++ct) y[ct] = mfma32(alo, sb[ct], y[ct]);
+#pragma unroll
+            for (int ct = 0; ct < kNV; ++ct)
+                y[ct] = mfma32(ahi, lds_bf16x8(slo + (16 * ct + r) * kLoRow + 8 * unit_swz(g, r)), y[ct]);
+            y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_lo[buf][8 * g]), y[kNV]);
+            f32x4* dst = reinterpret_cast<f32x4*>(&sm.hand[buf][W][0]);
+#pragma unroll
+            for (int ct = 0; ct < kNCT; ++ct) dst[ct * 64 + lane] = y[ct];
+        }
+        if (W >= 2) pipe.advance(regs, sm, c, nchunks);
+        __syncthreads();
+    };
+    for (int c = 0; c < nchunks; c += 2) {
+        step(c, pipe.a);
+        if (c + 1 < nchunks) step(c + 1, pipe.b);
+    }
+}
+
+// ---- on-diagonal wave DQ: the intra-chunk term of query tile DQ.  Interval
+// c computes it for chunk c and finishes chunk c-1: the off-diagonal part
+// (handed over during interval c-1) is added, the rows are normalised and
+// stored.
+template <int DQ, int DV, int MODE>
+__device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps, float* __restrict__ yh,
+                                            PrefillSmem<DV>& sm) {
+    constexpr int kNV = DV / 16, kNCT = kNV + 1;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (L + kC - 1) / kC;
 
     __syncthreads();  // first chunk staged, initial state published
@@ -415,168 +620,39 @@ __device__ __forceinline__ void readout_wave(int L, int ldv, float eps, float* _
         for (int c = 0; c < nchunks; ++c) __syncthreads();
         return;
     }
-
-    // Outputs of chunk c are normalised and stored during chunk c+1, after
-    // that chunk's first MFMAs are issued, so the MFMA tail of chunk c is
-    // never waited for.
-    f32x4 yprev[kNCT];
-    int prev_t0 = -1;
-    auto store_prev = [&]() {
-        if (prev_t0 < 0) return;
-        const int nprev = min(kC, L - prev_t0);
+    // Chunk c's rows: add the off-diagonal part, normalise, store.  nrows
+    // is the number of valid rows of the chunk (64 except at the end).
+    auto finish = [&](int c, const f32x4 (&yd)[kNCT], int nrows) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(&sm.hand[c & 1][DQ][0]);
+        f32x4 y[kNCT];
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct) y[ct] = src[ct * 64 + lane] + yd[ct];
+        float* ybase = yh + (size_t)c * kC * ldv;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int tq = 16 * W + 4 * g + m;
-            if (tq < nprev) {
-                const float inv = fast_rcp(yprev[kNV][m] + eps);
-                float* yrow = yh + (size_t)(prev_t0 + tq) * ldv + r;
+            const int tq = 16 * DQ + 4 * g + m;
+            const float inv = __builtin_amdgcn_rcpf(y[kNV][m] + eps);
+            if (tq < nrows) {
 #pragma unroll
-                for (int ct = 0; ct < kNV; ++ct) yrow[16 * ct] = yprev[ct][m] * inv;
+                for (int ct = 0; ct < kNV; ++ct) ybase[tq * ldv + 16 * ct + r] = y[ct][m] * inv;
             }
         }
     };
-
-    const bf16x8 ones = ones8();
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        const int sbuf = kSBufs == 2 ? buf : 0;
-        const int t0 = c * kC;
-        const int n = min(kC, L - t0);
-        const uint16_t* q_l = &sm.q[buf][0];
-        const uint16_t* k_l = &sm.k[buf][0];
-        const uint16_t* vt_l = &sm.vt[buf][0];
-
-        f32x4 y[kNCT];
+    f32x4 ydprev[kNCT];
+    diag_block<DQ, DV>(sm, 0, lane, g, r, ydprev);
+    __syncthreads();
+    for (int c = 1; c < nchunks; ++c) {
+        f32x4 yd[kNCT];
+        diag_block<DQ, DV>(sm, c & 1, lane, g, r, yd);
+        finish(c - 1, ydprev, kC);
 #pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct) y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        // ---- on-diagonal term: s^T for key tiles 0..W, weights 1+s+s^2/2
-        {
-            const bf16x4 qb = lds_bf16x4(q_l + (16 * W + r) * kQRow + 4 * g);
-            float wgt[W + 1][4];
-#pragma unroll
-            for (int j = 0; j <= W; ++j) {
-                const bf16x4 ka = lds_bf16x4(k_l + (16 * j + r) * kQRow + 4 * g);
-                const f32x4 s = mfma16(ka, qb, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    // s[m] = q_query . k_key (raw), key = 16j + 4g + m, query = 16W + r
-                    const float w = fmaf(s[m], fmaf(s[m], 1.f / 32.f, 0.25f), 1.f);
-                    wgt[j][m] = (j == W && 4 * g + m > r) ? 0.f : w;
-                }
-            }
-#pragma unroll
-            for (int p = 0; p <= W / 2; ++p) {
-                float a[8];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    a[m] = wgt[2 * p][m];
-                    a[4 + m] = (2 * p + 1 <= W) ? wgt[(2 * p + 1 <= W) ? 2 * p + 1 : 0][m] : 0.f;
-                }
-                bf16x8 ahi, alo;
-                pack8_hilo(a, ahi, alo);
-                bf16x8 vb[kNV];
-#pragma unroll
-                for (int ct = 0; ct < kNV; ++ct) {
-                    const uint16_t* vrow = vt_l + (16 * ct + r) * kTRow + 32 * p;
-                    vb[ct] = join44(vrow + 4 * g, vrow + 16 + 4 * g);
-                }
-                // hi parts of every column tile first, then the lo parts, so
-                // consecutive MFMAs never depend on each other
-#pragma unroll
-                for (int ct = 0; ct < kNV; ++ct) y[ct] = mfma32(ahi, vb[ct], y[ct]);
-                y[kNV] = mfma32(ahi, ones, y[kNV]);
-#pragma unroll
-                for (int ct = 0; ct < kNV; ++ct) y[ct] = mfma32(alo, vb[ct], y[ct]);
-                y[kNV] = mfma32(alo, ones, y[kNV]);
-            }
-        }
-
-        store_prev();  // previous chunk's outputs, behind this chunk's first MFMAs
-
-        // ---- off-diagonal term: psi(Q) x (state before this chunk)
-        {
-            float qr[16];
-            const float* qrow = &sm.qf[buf][(16 * W + r) * kQfRow];
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(qrow + 4 * ((g + cc) & 3));
-                qr[4 * cc + 0] = x[0];
-                qr[4 * cc + 1] = x[1];
-                qr[4 * cc + 2] = x[2];
-                qr[4 * cc + 3] = x[3];
-            }
-            const uint16_t* shi = &sm.s_hi[sbuf][0];
-            const uint16_t* slo = &sm.s_lo[sbuf][0];
-#define BASED_READOUT_STEP(J)                                                                   \
-    {                                                                                          \
-        float a[8];                                                                            \
-        psi_q<J>(qr, g, a);                                                                    \
-        const bf16x8 ahi = pack8(a);                                                           \
-        _Pragma("unroll") for (int ct = 0; ct < kNV; ++ct)                                     \
-            y[ct] = mfma32(ahi, lds_bf16x8(shi + (16 * ct + r) * kSRow + 32 * (J) + 8 * g), y[ct]); \
-        y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_hi[sbuf][32 * (J) + 8 * g]), y[kNV]);             \
-    }
-            BASED_READOUT_STEP(0)
-            BASED_READOUT_STEP(1)
-            BASED_READOUT_STEP(2)
-            BASED_READOUT_STEP(3)
-            {
-                // last feature k-step (pairs (r, r+8), constant, linear): hi/lo on both sides
-                float a[8];
-                psi_q<4>(qr, g, a);
-                bf16x8 ahi, alo;
-                pack8_hilo(a, ahi, alo);
-                bf16x8 sb[kNV + 1];
-#pragma unroll
-                for (int ct = 0; ct < kNV; ++ct) sb[ct] = lds_bf16x8(shi + (16 * ct + r) * kSRow + 128 + 8 * g);
-                sb[kNV] = lds_bf16x8(&sm.z_hi[sbuf][128 + 8 * g]);
-#pragma unroll
-                for (int ct = 0; ct <= kNV; ++ct) y[ct] = mfma32(ahi, sb[ct], y[ct]);
-#pragma unroll
-                for (int ct = 0; ct <= kNV; ++ct) y[ct] = mfma32(alo, sb[ct], y[ct]);
-#pragma unroll
-                for (int ct = 0; ct < kNV; ++ct)
-                    y[ct] = mfma32(ahi, lds_bf16x8(slo + (16 * ct + r) * kLoRow + 8 * g), y[ct]);
-                y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_lo[sbuf][8 * g]), y[kNV]);
-            }
-#undef BASED_READOUT_STEP
-        }
-
-        // ---- hand this chunk's accumulators to the deferred store
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct) yprev[ct] = y[ct];
-        prev_t0 = t0;
-        if (kSBufs == 1) __syncthreads();  // readouts done: the state operand may be overwritten
+        for (int ct = 0; ct < kNCT; ++ct) ydprev[ct] = yd[ct];
         __syncthreads();
     }
-    store_prev();
+    finish(nchunks - 1, ydprev, L - (nchunks - 1) * kC);
 }
 
 // ---- update wave U: state rotation tiles U, U+4 (, U+8).
-// Staging registers of one chunk held by an update-wave thread: V^T
-// (every thread) and Q/K (threads 128..255 of the update waves).
-template <int DV>
-struct ChunkRegs {
-    VStage<DV> v;
-    QKStage qk;
-};
-
-template <int DV, int MODE>
-__device__ __forceinline__ void chunk_load(ChunkRegs<DV>& cr, const uint16_t* qh, const uint16_t* kh,
-                                           const uint16_t* vh, int ldv, int t0, int L, int u) {
-    v_load<DV>(cr.v, vh, ldv, t0, L, u);
-    const int t = u - 128;
-    if (t >= 0 && (MODE != kModeState || t < 64)) qk_load(cr.qk, qh, kh, t0, L, t);
-}
-template <int DV, int MODE>
-__device__ __forceinline__ void chunk_store(const ChunkRegs<DV>& cr, PrefillSmem<DV>& sm, int buf, int t0,
-                                            int L, int u) {
-    v_store<DV>(cr.v, sm, buf, t0, L, u);
-    const int t = u - 128;
-    if (t >= 0 && (MODE != kModeState || t < 64)) qk_store<DV>(cr.qk, sm, buf, t0, L, t);
-}
-
 template <int U, int DV, int MODE>
 __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, const uint16_t* __restrict__ kh,
                                             const uint16_t* __restrict__ vh, int L, int ldv, float* __restrict__ Sh,
@@ -584,7 +660,6 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
                                             const float* ws_in, float* ws_out, bool write_final) {
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
     constexpr int kNT = U < 2 ? 3 : 2;
-    constexpr int kSBufs = PrefillSmem<DV>::kSBufs;
     const int u = threadIdx.x - 256;  // 0..255
     const int lane = u & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (L + kC - 1) / kC;
@@ -607,27 +682,26 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
         if constexpr (kNT == 3) load_initial<U + 8, DV>(acc[2], Sh, zh, ldv, g, r);
     }
 
-    // Chunks are prefetched kAhead - 1 chunks beyond the one being staged.
-    // With two register sets (d_v = 64), set A holds the odd chunks and set
-    // B the even ones, so no register copy ever waits on a load in flight;
-    // d_v = 128 has room for one set only.
-    constexpr int kAhead = DV <= 64 ? 3 : 2;
-    ChunkRegs<DV> setA, setB;
-    chunk_load<DV, MODE>(setB, qh, kh, vh, ldv, 0, L, u);
-    if (nchunks > 1) chunk_load<DV, MODE>(setA, qh, kh, vh, ldv, kC, L, u);
-    chunk_store<DV, MODE>(setB, sm, 0, 0, L, u);
-    if (kAhead == 3 && nchunks > 2) chunk_load<DV, MODE>(setB, qh, kh, vh, ldv, 2 * kC, L, u);
+    // V^T staging: a 32-column group uses the threads of update waves 2, 3
+    StagePipe<DV, true, false> pipe;
+    pipe.vu = DV == 32 ? u - 128 : u;
+    pipe.t = -1;
+    pipe.qh = qh;
+    pipe.kh = kh;
+    pipe.vh = vh;
+    pipe.ldv = ldv;
+    pipe.L = L;
+    pipe.prologue(sm, nchunks);
     if (MODE != kModeState) {
-        publish_state<U, DV>(acc[0], sm, 0, g, r);
-        publish_state<U + 4, DV>(acc[1], sm, 0, g, r);
-        if constexpr (kNT == 3) publish_state<U + 8, DV>(acc[2], sm, 0, g, r);
+        publish_pair<U, DV>(acc[0], acc[1], sm, 0, g, r);
+        if constexpr (kNT == 3) publish_last<U, DV>(acc[2], sm, 0, g, r);
     }
     __syncthreads();
 
     const bf16x8 ones = ones8();
     // One chunk: update with chunk c, stage chunk c+1 from `regs` (it holds
     // chunk c+1) and refill `regs` with chunk c+kAhead, publish the state.
-    auto step = [&](int c, ChunkRegs<DV>& regs) {
+    auto step = [&](int c, typename StagePipe<DV, true, false>::Regs& regs) {
         const int buf = c & 1;
         const int t0 = c * kC;
         const int n = min(kC, L - t0);
@@ -638,9 +712,8 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             float kv[8], cst[8];
-            const float* krow = kt_l + r * kKtRow + 32 * s + 8 * g;
-            const f32x4 k0 = *reinterpret_cast<const f32x4*>(krow);
-            const f32x4 k1 = *reinterpret_cast<const f32x4*>(krow + 4);
+            const f32x4 k0 = *reinterpret_cast<const f32x4*>(kt_l + kt_idx(r, 32 * s + 8 * g));
+            const f32x4 k1 = *reinterpret_cast<const f32x4*>(kt_l + kt_idx(r, 32 * s + 8 * g + 4));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 kv[i] = k0[i];
@@ -656,7 +729,7 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
             bf16x8 vb[kNV];
 #pragma unroll
             for (int ct = 0; ct < kNV; ++ct)
-                vb[ct] = lds_bf16x8(vt_l + (16 * ct + r) * kTRow + 32 * s + 8 * g);
+                vb[ct] = lds_bf16x8(vt_l + vt_idx(16 * ct + r, 32 * s + 8 * g));
             {
                 const bf16x8 a = psi_k<U>(kv, pmask, cst);
 #pragma unroll
@@ -677,29 +750,20 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
             }
         }
 
-        // ---- stage chunk c+1 (loaded kAhead - 1 chunks ago), refill with chunk c+kAhead
-        if (c + 1 < nchunks) {
-            chunk_store<DV, MODE>(regs, sm, buf ^ 1, t0 + kC, L, u);
-            if (c + kAhead < nchunks) chunk_load<DV, MODE>(regs, qh, kh, vh, ldv, t0 + kAhead * kC, L, u);
-        }
+        // ---- stage chunk c+1, refill with chunk c+3
+        pipe.advance(regs, sm, c, nchunks);
 
         // ---- publish the state after this chunk for the next readout
         if (MODE != kModeState) {
-            if (kSBufs == 1) __syncthreads();  // wait until every readout of this chunk is done
-            const int wbuf = kSBufs == 2 ? (buf ^ 1) : 0;
-            publish_state<U, DV>(acc[0], sm, wbuf, g, r);
-            publish_state<U + 4, DV>(acc[1], sm, wbuf, g, r);
-            if constexpr (kNT == 3) publish_state<U + 8, DV>(acc[2], sm, wbuf, g, r);
+            const int wbuf = buf ^ 1;
+            publish_pair<U, DV>(acc[0], acc[1], sm, wbuf, g, r);
+            if constexpr (kNT == 3) publish_last<U, DV>(acc[2], sm, wbuf, g, r);
         }
         __syncthreads();
     };
-    if constexpr (kAhead == 3) {
-        for (int c = 0; c < nchunks; c += 2) {
-            step(c, setA);                           // chunk c+1 (odd) is in set A
-            if (c + 1 < nchunks) step(c + 1, setB);  // chunk c+2 (even) is in set B
-        }
-    } else {
-        for (int c = 0; c < nchunks; ++c) step(c, setA);
+    for (int c = 0; c < nchunks; c += 2) {
+        step(c, pipe.a);                           // chunk c+1 (odd) is in set A
+        if (c + 1 < nchunks) step(c + 1, pipe.b);  // chunk c+2 (even) is in set B
     }
 
     if (MODE == kModeState) {
@@ -766,7 +830,7 @@ __device__ __forceinline__ void ws_load(f32x4 (&acc)[DV / 16 + 1], const float* 
 //                 slot s (after the prefix sum); the last segment writes the
 //                 final state.
 template <int DV, int MODE>
-__global__ __launch_bounds__(512, 1) void prefill_mfma_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(768, 1) void prefill_mfma_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v, int L,
                                                               int ldv, int ncg, int seg_len, int nseg,
@@ -804,29 +868,33 @@ __global__ __launch_bounds__(512, 1) void prefill_mfma_kernel(const uint16_t* __
     const int w = threadIdx.x >> 6;
     if (MODE == kModeState && seg == nseg - 1) {
         // This workgroup's slot job is the initial state (no sweep, no barrier).
-        if (w >= 4) {
-            switch (w) {
-                case 4: init_to_workspace<0, DV>(Sh, zh, ldv, use_init, ws_out); break;
-                case 5: init_to_workspace<1, DV>(Sh, zh, ldv, use_init, ws_out); break;
-                case 6: init_to_workspace<2, DV>(Sh, zh, ldv, use_init, ws_out); break;
-                default: init_to_workspace<3, DV>(Sh, zh, ldv, use_init, ws_out); break;
-            }
+        switch (w) {
+            case 4: init_to_workspace<0, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 5: init_to_workspace<1, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 6: init_to_workspace<2, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 7: init_to_workspace<3, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            default: break;
         }
         return;
     }
     const bool write_final = MODE == kModeFull || seg == nseg - 1;
-    // Waves 0-3 and 4-7 land on SIMDs 0-3 in pairs; readout wave W shares
-    // its SIMD with update wave W (the lighter on-diagonal work of W = 0, 1
-    // pairs with the three-tile update waves).
+    // Waves w, w + 4 and w + 8 share a SIMD: the off-diagonal wave of query
+    // tile w, update wave w (three state tiles for w < 2) and the
+    // on-diagonal wave of query tile w (heavier for larger w).
     switch (w) {
-        case 0: readout_wave<0, DV, MODE>(len, ldv, eps, yh, sm); break;
-        case 1: readout_wave<1, DV, MODE>(len, ldv, eps, yh, sm); break;
-        case 2: readout_wave<2, DV, MODE>(len, ldv, eps, yh, sm); break;
-        case 3: readout_wave<3, DV, MODE>(len, ldv, eps, yh, sm); break;
+        case 0: offdiag_wave<0, DV, MODE>(qh, kh, len, sm); break;
+        case 1: offdiag_wave<1, DV, MODE>(qh, kh, len, sm); break;
+        case 2: offdiag_wave<2, DV, MODE>(qh, kh, len, sm); break;
+        case 3: offdiag_wave<3, DV, MODE>(qh, kh, len, sm); break;
+        case 8: ondiag_wave<0, DV, MODE>(len, ldv, eps, yh, sm); break;
+        case 9: ondiag_wave<1, DV, MODE>(len, ldv, eps, yh, sm); break;
+        case 10: ondiag_wave<2, DV, MODE>(len, ldv, eps, yh, sm); break;
+        case 11: ondiag_wave<3, DV, MODE>(len, ldv, eps, yh, sm); break;
         case 4: update_wave<0, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
         case 5: update_wave<1, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
         case 6: update_wave<2, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
-        default: update_wave<3, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
+        case 7: update_wave<3, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
+        default: break;
     }
 }
 
@@ -868,12 +936,15 @@ PrefillPlan plan_prefill(int BH, int L, int dv, bool use_init, bool have_ws) {
         pl.nseg = max(1, min((kTargetWorkgroups + units - 1) / units, nchunks / 2));
     // With an initial state and several column groups, the carried state
     // goes through the workspace (no group may overwrite z while another
-    // still reads it); without a workspace, fall back to one group.
+    // still reads it).  Without a workspace: one 64-wide group for d_v = 64;
+    // d_v = 128 with an initial state has no MFMA plan (dvl = 0).
     const bool need_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
     if (need_ws && !have_ws) {
-        pl.dvl = dv;
-        pl.ncg = 1;
         pl.nseg = 1;
+        if (use_init) {
+            pl.dvl = dv == 64 ? 64 : 0;
+            pl.ncg = 1;
+        }
     }
     return pl;
 }
@@ -884,11 +955,7 @@ size_t workspace_bytes_dvl(int BH, int ncg, int nseg) {
 }
 
 size_t plan_workspace_bytes(const PrefillPlan& pl, int BH) {
-    switch (pl.dvl) {
-        case 32: return workspace_bytes_dvl<32>(BH, pl.ncg, pl.nseg);
-        case 64: return workspace_bytes_dvl<64>(BH, pl.ncg, pl.nseg);
-        default: return workspace_bytes_dvl<128>(BH, pl.ncg, pl.nseg);
-    }
+    return pl.dvl == 32 ? workspace_bytes_dvl<32>(BH, pl.ncg, pl.nseg) : workspace_bytes_dvl<64>(BH, pl.ncg, pl.nseg);
 }
 
 template <int DVL>
@@ -897,7 +964,7 @@ hipError_t launch_plan(const PrefillPlan& pl, const uint16_t* q, const uint16_t*
                        hipStream_t st) {
     const bool via_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
     if (!via_ws) {
-        hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeFull>), dim3(BH * pl.ncg), dim3(512), 0, st, q, k, v, L,
+        hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeFull>), dim3(BH * pl.ncg), dim3(768), 0, st, q, k, v, L,
                            dv, pl.ncg, L, 1, eps, y, S, z, use_init, nullptr);
         return hipGetLastError();
     }
@@ -906,12 +973,12 @@ hipError_t launch_plan(const PrefillPlan& pl, const uint16_t* q, const uint16_t*
     const int nseg = (L + seg_len - 1) / seg_len;
     float* wsf = static_cast<float*>(ws);
     const dim3 grid(BH * pl.ncg * nseg);
-    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeState>), grid, dim3(512), 0, st, q, k, v, L, dv, pl.ncg,
+    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeState>), grid, dim3(768), 0, st, q, k, v, L, dv, pl.ncg,
                        seg_len, nseg, eps, y, S, z, use_init, wsf);
     const size_t slot = ws_slot_floats<DVL>();
     hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH * pl.ncg), dim3(256), 0, st,
                        wsf, nseg, BH * pl.ncg, slot);
-    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeSegment>), grid, dim3(512), 0, st, q, k, v, L, dv, pl.ncg,
+    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeSegment>), grid, dim3(768), 0, st, q, k, v, L, dv, pl.ncg,
                        seg_len, nseg, eps, y, S, z, use_init, wsf);
     return hipGetLastError();
 }
@@ -937,7 +1004,8 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int 
     switch (pl.dvl) {
         case 32: return launch_plan<32>(pl, qq, kk, vv, BH, L, dv, eps, y, S, z, use_init, ws, st);
         case 64: return launch_plan<64>(pl, qq, kk, vv, BH, L, dv, eps, y, S, z, use_init, ws, st);
-        default: return launch_plan<128>(pl, qq, kk, vv, BH, L, dv, eps, y, S, z, use_init, ws, st);
+        default:  // no workspace for a carried d_v = 128 state: exact fp32 chunked kernel
+            return launch_prefill_valu(q, k, v, true, BH, L, dv, kC, eps, y, S, z, use_init, st);
     }
 }
 
