@@ -188,7 +188,7 @@ __device__ __forceinline__ void psi_q(const float (&qr)[16], int g, float (&a)[8
         const int m = i & 3;
         if (J < 4) {
             const int T = i < 4 ? J : J + 4;  // pair (row, row + T)
-            a[i] = T == 0 ? qr[m] * qr[m] : qr[m] * qr[m + T];
+            a[i] = T == 0 ? (0.5f * qr[m]) * qr[m] : qr[m] * qr[m + T];
         } else if (i < 4) {
             // tile 8: pairs (row, row + 8) for rows < 8, the constant at row 8
             a[i] = g < 2 ? qr[m] * qr[m + 8] : ((g == 2 && m == 0) ? 1.f : 0.f);
@@ -199,14 +199,14 @@ __device__ __forceinline__ void psi_q(const float (&qr)[16], int g, float (&a)[8
 }
 
 // ---------------------------------------------------------------- per-wave bodies
-// Accumulators hold the state in readout units (the k pre-scale 1/4, the
-// 1/sqrt2 of the diagonal and the pair multiplicity are folded in when the
-// features of K are formed), so publishing the state operand is a plain
-// rounding to bf16.  state_scale converts to the caller's 273-row units
+// Accumulators hold the state in readout units (the k pre-scale 1/4 and
+// the pair multiplicity are folded in when the features of K are formed,
+// the 1/2 of the diagonal terms into the query features), so publishing
+// the state operand is a plain rounding to bf16.  state_scale converts to the caller's 273-row units
 // (one mirror row of a pair).
 template <int T>
 __device__ __forceinline__ float state_scale(int r) {
-    if (T == 0) return 4.f * kSqrt2;
+    if (T == 0) return 2.f * kSqrt2;
     if (T == 9) return 2.f;
     if (T == 8 && r == 8) return 1.f;
     return 2.f * kSqrt2;
@@ -310,22 +310,47 @@ __device__ __forceinline__ void store_final(const f32x4 (&acc)[DV / 16 + 1], flo
     }
 }
 
+// Tile 8 rows: d = k_r * k_(r+8) on lanes r < 8 of each 16-lane row (DPP
+// bank mask); lanes r >= 8 keep their old value, which holds the constant
+// feature (1 on row 8, 0 below it).  The s_nop covers the DPP read hazard.
+__device__ __forceinline__ void tile8_rows(const float (&kv)[8], float (&d)[8]) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mul_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+        "v_mul_f32_dpp %1, %9, %9 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+        "v_mul_f32_dpp %2, %10, %10 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+        "v_mul_f32_dpp %3, %11, %11 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+        "v_mul_f32_dpp %4, %12, %12 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+        "v_mul_f32_dpp %5, %13, %13 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+        "v_mul_f32_dpp %6, %14, %14 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+        "v_mul_f32_dpp %7, %15, %15 row_ror:8 row_mask:0xf bank_mask:0x3"
+        : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]), "+v"(d[4]), "+v"(d[5]), "+v"(d[6]), "+v"(d[7])
+        : "v"(kv[0]), "v"(kv[1]), "v"(kv[2]), "v"(kv[3]), "v"(kv[4]), "v"(kv[5]), "v"(kv[6]), "v"(kv[7]));
+}
+
 // psi(K)^T for rotation tile T: lane (row r, group g) holds feature row r
-// for 8 tokens; kv[] = k_r / 4 of those tokens.  For tile 8, pmask selects
-// the pair rows and cst[] is the constant row's value (0 on padding).
+// for 8 tokens; kv[] = k_r / 4 of those tokens.  Tile 8 comes from
+// tile8_rows (t8); its constant row is 1 for every token of the chunk,
+// padding included (padded tokens have v = 0, so only the normaliser's
+// constant row counts them; that count is taken off before the state
+// leaves the kernel).
 template <int T>
-__device__ __forceinline__ bf16x8 psi_k(const float (&kv)[8], float pmask, const float (&cst)[8]) {
+__device__ __forceinline__ bf16x8 psi_k(const float (&kv)[8], float (&t8)[8]) {
     float a[8];
+    if constexpr (T == 8) {
+        tile8_rows(kv, t8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (T == 0) {
-            a[i] = (0.5f * kv[i]) * kv[i];
-        } else if (T < 8) {
-            a[i] = kv[i] * row_ror<16 - T>(kv[i]);
-        } else if (T == 8) {
-            a[i] = fmaf(kv[i] * row_ror<8>(kv[i]), pmask, cst[i]);
-        } else {
-            a[i] = kv[i];
+        for (int i = 0; i < 8; ++i) a[i] = t8[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (T == 0) {
+                a[i] = kv[i] * kv[i];  // the 1/2 of the diagonal is on the query side
+            } else if (T < 8) {
+                a[i] = kv[i] * row_ror<16 - T>(kv[i]);
+            } else {
+                a[i] = kv[i];
+            }
         }
     }
     return pack8(a);
@@ -333,7 +358,7 @@ __device__ __forceinline__ bf16x8 psi_k(const float (&kv)[8], float pmask, const
 
 // ---- staging split: readout waves stage Q and K (+K^T), update waves V^T.
 struct QKStage {
-    u32x4 a0, a1;
+    u32x4 a;
 };
 template <int DV>
 struct VStage {
@@ -352,50 +377,33 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a 
 
 // Unconditional 16-byte loads: rows past the end are clamped to the last
 // row and zeroed when stored, so no branch sits between prefetch and use.
-// t (0..127 of the readout waves): t < 64 loads K, else Q; token pair
-// p = t & 31, dims 8*((t >> 5) & 1) .. +8.
+// t (0..255 of the off-diagonal waves): t < 128 stages K, else Q; token
+// (t & 127) >> 1, dims 8*(t & 1) .. +8.
 __device__ __forceinline__ void qk_load(QKStage& st, const uint16_t* qh, const uint16_t* kh, int t0, int L,
                                         int t) {
-    const int p = t & 31;
-    const int ta = min(t0 + 2 * p, L - 1), tb = min(t0 + 2 * p + 1, L - 1);
-    const uint16_t* src = t < 64 ? kh : qh;
-    const int db = (t >> 5) & 1;
-    st.a0 = *reinterpret_cast<const u32x4*>(src + (size_t)ta * kDFeat + 8 * db);
-    st.a1 = *reinterpret_cast<const u32x4*>(src + (size_t)tb * kDFeat + 8 * db);
+    const int tok = min(t0 + ((t & 127) >> 1), L - 1);
+    const uint16_t* src = t < 128 ? kh : qh;
+    st.a = *reinterpret_cast<const u32x4*>(src + (size_t)tok * kDFeat + 8 * (t & 1));
 }
 template <int DV>
 __device__ __forceinline__ void qk_store(const QKStage& in, PrefillSmem<DV>& sm, int buf, int t0, int L, int t) {
-    const int p = t & 31;
-    const u32x4 a0 = keep_if(in.a0, t0 + 2 * p < L), a1 = keep_if(in.a1, t0 + 2 * p + 1 < L);
-    const int db = (t >> 5) & 1;
-    uint16_t* rowm = t < 64 ? &sm.k[buf][0] : &sm.q[buf][0];
-    uint2* ra = reinterpret_cast<uint2*>(rowm + qk_idx(2 * p, 8 * db));
-    uint2* rb = reinterpret_cast<uint2*>(rowm + qk_idx(2 * p + 1, 8 * db));
-    ra[0] = make_uint2(a0[0], a0[1]);
-    ra[1] = make_uint2(a0[2], a0[3]);
-    rb[0] = make_uint2(a1[0], a1[1]);
-    rb[1] = make_uint2(a1[2], a1[3]);
-    if (t < 64) {
+    const int tok = (t & 127) >> 1, half = t & 1;
+    const u32x4 a = keep_if(in.a, t0 + tok < L);
+    uint16_t* rowm = t < 128 ? &sm.k[buf][0] : &sm.q[buf][0];
+    *reinterpret_cast<u32x4*>(rowm + qk_idx(tok, 8 * half)) = a;
+    if (t < 128) {
         float* kt = &sm.ktf[buf][0];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int d0 = 8 * db + 2 * e;
-            *reinterpret_cast<float2*>(kt + kt_idx(d0, 2 * p)) =
-                make_float2(0.25f * bf16lo_f32(a0[e]), 0.25f * bf16lo_f32(a1[e]));
-            *reinterpret_cast<float2*>(kt + kt_idx(d0 + 1, 2 * p)) =
-                make_float2(0.25f * bf16hi_f32(a0[e]), 0.25f * bf16hi_f32(a1[e]));
+            kt[kt_idx(8 * half + 2 * e, tok)] = 0.25f * bf16lo_f32(a[e]);
+            kt[kt_idx(8 * half + 2 * e + 1, tok)] = 0.25f * bf16hi_f32(a[e]);
         }
     } else {
         float* qf = &sm.qf[buf][0];
-        f32x4 x;
-        x = f32x4{bf16lo_f32(a0[0]), bf16hi_f32(a0[0]), bf16lo_f32(a0[1]), bf16hi_f32(a0[1])};
-        *reinterpret_cast<f32x4*>(qf + qf_idx(2 * p, 8 * db)) = x;
-        x = f32x4{bf16lo_f32(a0[2]), bf16hi_f32(a0[2]), bf16lo_f32(a0[3]), bf16hi_f32(a0[3])};
-        *reinterpret_cast<f32x4*>(qf + qf_idx(2 * p, 8 * db + 4)) = x;
-        x = f32x4{bf16lo_f32(a1[0]), bf16hi_f32(a1[0]), bf16lo_f32(a1[1]), bf16hi_f32(a1[1])};
-        *reinterpret_cast<f32x4*>(qf + qf_idx(2 * p + 1, 8 * db)) = x;
-        x = f32x4{bf16lo_f32(a1[2]), bf16hi_f32(a1[2]), bf16lo_f32(a1[3]), bf16hi_f32(a1[3])};
-        *reinterpret_cast<f32x4*>(qf + qf_idx(2 * p + 1, 8 * db + 4)) = x;
+        *reinterpret_cast<f32x4*>(qf + qf_idx(tok, 8 * half)) =
+            f32x4{bf16lo_f32(a[0]), bf16hi_f32(a[0]), bf16lo_f32(a[1]), bf16hi_f32(a[1])};
+        *reinterpret_cast<f32x4*>(qf + qf_idx(tok, 8 * half + 4)) =
+            f32x4{bf16lo_f32(a[2]), bf16hi_f32(a[2]), bf16lo_f32(a[3]), bf16hi_f32(a[3])};
     }
 }
 // u (0..255, or 0..127 for a 32-column group): token pair p = u & 31,
@@ -435,7 +443,7 @@ __device__ __forceinline__ void v_store(const VStage<DV>& st, PrefillSmem<DV>& s
 // registers loaded two intervals earlier; two register sets alternate (set
 // A holds the odd chunks, set B the even ones), so no register copy waits on
 // a load in flight.  V^T is staged by update-wave threads (vu >= 0), Q and K
-// by off-diagonal-wave threads (t >= 0, K for t < 64).
+// by off-diagonal-wave threads (t >= 0, K for t < 128).
 template <int DV, bool DO_V, bool DO_QK>
 struct StagePipe {
     struct Regs {
@@ -530,16 +538,16 @@ __device__ __forceinline__ void offdiag_wave(const uint16_t* __restrict__ qh, co
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (L + kC - 1) / kC;
-    // Q and K staging: waves 2 (K) and 3 (Q); only K without outputs
+    // Q and K staging: waves 0, 1 (K) and 2, 3 (Q); only K without outputs
     StagePipe<DV, false, true> pipe;
     pipe.vu = -1;
-    pipe.t = W < 2 ? -1 : ((MODE == kModeState && W == 3) ? -1 : (int)threadIdx.x - 128);
+    pipe.t = (MODE == kModeState && W >= 2) ? -1 : (int)threadIdx.x;
     pipe.qh = qh;
     pipe.kh = kh;
     pipe.vh = nullptr;
     pipe.ldv = 0;
     pipe.L = L;
-    if (W >= 2) pipe.prologue(sm, nchunks);
+    pipe.prologue(sm, nchunks);
 
     __syncthreads();  // first chunk staged, initial state published
     auto step = [&](int c, typename StagePipe<DV, false, true>::Regs& regs) {
@@ -595,7 +603,7 @@ __device__ __forceinline__ void offdiag_wave(const uint16_t* __restrict__ qh, co
 #pragma unroll
             for (int ct = 0; ct < kNCT; ++ct) dst[ct * 64 + lane] = y[ct];
         }
-        if (W >= 2) pipe.advance(regs, sm, c, nchunks);
+        pipe.advance(regs, sm, c, nchunks);
         __syncthreads();
     };
     for (int c = 0; c < nchunks; c += 2) {
@@ -609,8 +617,8 @@ __device__ __forceinline__ void offdiag_wave(const uint16_t* __restrict__ qh, co
 // (handed over during interval c-1) is added, the rows are normalised and
 // stored.
 template <int DQ, int DV, int MODE>
-__device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps, float* __restrict__ yh,
-                                            PrefillSmem<DV>& sm) {
+__device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps,
+                                            float* __restrict__ yh, PrefillSmem<DV>& sm) {
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (L + kC - 1) / kC;
@@ -634,17 +642,16 @@ __device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps, float* __
             const float inv = __builtin_amdgcn_rcpf(y[kNV][m] + eps);
             if (tq < nrows) {
 #pragma unroll
-                for (int ct = 0; ct < kNV; ++ct) ybase[tq * ldv + 16 * ct + r] = y[ct][m] * inv;
+                for (int ct = 0; ct < kNV; ++ct)
+                    __builtin_nontemporal_store(y[ct][m] * inv, &ybase[tq * ldv + 16 * ct + r]);
             }
         }
     };
     f32x4 ydprev[kNCT];
-    diag_block<DQ, DV>(sm, 0, lane, g, r, ydprev);
-    __syncthreads();
-    for (int c = 1; c < nchunks; ++c) {
+    for (int c = 0; c < nchunks; ++c) {
         f32x4 yd[kNCT];
         diag_block<DQ, DV>(sm, c & 1, lane, g, r, yd);
-        finish(c - 1, ydprev, kC);
+        if (c > 0) finish(c - 1, ydprev, kC);
 #pragma unroll
         for (int ct = 0; ct < kNCT; ++ct) ydprev[ct] = yd[ct];
         __syncthreads();
@@ -664,8 +671,9 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
     const int lane = u & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (L + kC - 1) / kC;
     // rotation tile 8: rows 0..7 are the pairs (r, r+8), row 8 the constant
-    const float pmask = r < 8 ? 1.f : 0.f;
-    const float cmask = r == 8 ? 1.f : 0.f;
+    float t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t8[i] = r == 8 ? 1.f : 0.f;
 
     f32x4 acc[kNT][kNCT];
 #pragma unroll
@@ -682,7 +690,7 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
         if constexpr (kNT == 3) load_initial<U + 8, DV>(acc[2], Sh, zh, ldv, g, r);
     }
 
-    // V^T staging: a 32-column group uses the threads of update waves 2, 3
+    // V^T staging (a 32-column group uses update waves 2 and 3 only)
     StagePipe<DV, true, false> pipe;
     pipe.vu = DV == 32 ? u - 128 : u;
     pipe.t = -1;
@@ -699,19 +707,20 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
     __syncthreads();
 
     const bf16x8 ones = ones8();
-    // One chunk: update with chunk c, stage chunk c+1 from `regs` (it holds
-    // chunk c+1) and refill `regs` with chunk c+kAhead, publish the state.
+    // One chunk: update with chunk c, stage chunk c+1 from `regs` and
+    // refill it with chunk c+3, publish the state after chunk c.  (Staging
+    // stays on waves without global stores: on gfx9 the vector-memory
+    // counter also counts stores, so a wave that stores outputs would wait
+    // for them before it could use its prefetched loads.)
     auto step = [&](int c, typename StagePipe<DV, true, false>::Regs& regs) {
         const int buf = c & 1;
-        const int t0 = c * kC;
-        const int n = min(kC, L - t0);
         const float* kt_l = &sm.ktf[buf][0];
         const uint16_t* vt_l = &sm.vt[buf][0];
 
         // ---- S += psi(K)^T V, z += psi(K)^T 1 over this chunk's 64 tokens
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            float kv[8], cst[8];
+            float kv[8];
             const f32x4 k0 = *reinterpret_cast<const f32x4*>(kt_l + kt_idx(r, 32 * s + 8 * g));
             const f32x4 k1 = *reinterpret_cast<const f32x4*>(kt_l + kt_idx(r, 32 * s + 8 * g + 4));
 #pragma unroll
@@ -719,38 +728,30 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
                 kv[i] = k0[i];
                 kv[4 + i] = k1[i];
             }
-            // constant feature row of tile 8: 1 for real tokens, 0 for padding
-#pragma unroll
-            for (int i = 0; i < 8; ++i) cst[i] = cmask;
-            if (n < kC) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) cst[i] = (32 * s + 8 * g + i < n) ? cmask : 0.f;
-            }
             bf16x8 vb[kNV];
 #pragma unroll
             for (int ct = 0; ct < kNV; ++ct)
                 vb[ct] = lds_bf16x8(vt_l + vt_idx(16 * ct + r, 32 * s + 8 * g));
             {
-                const bf16x8 a = psi_k<U>(kv, pmask, cst);
+                const bf16x8 a = psi_k<U>(kv, t8);
 #pragma unroll
                 for (int ct = 0; ct < kNV; ++ct) acc[0][ct] = mfma32(a, vb[ct], acc[0][ct]);
                 acc[0][kNV] = mfma32(a, ones, acc[0][kNV]);
             }
             {
-                const bf16x8 a = psi_k<U + 4>(kv, pmask, cst);
+                const bf16x8 a = psi_k<U + 4>(kv, t8);
 #pragma unroll
                 for (int ct = 0; ct < kNV; ++ct) acc[1][ct] = mfma32(a, vb[ct], acc[1][ct]);
                 acc[1][kNV] = mfma32(a, ones, acc[1][kNV]);
             }
             if constexpr (kNT == 3) {
-                const bf16x8 a = psi_k<U + 8>(kv, pmask, cst);
+                const bf16x8 a = psi_k<U + 8>(kv, t8);
 #pragma unroll
                 for (int ct = 0; ct < kNV; ++ct) acc[2][ct] = mfma32(a, vb[ct], acc[2][ct]);
                 acc[2][kNV] = mfma32(a, ones, acc[2][kNV]);
             }
         }
 
-        // ---- stage chunk c+1, refill with chunk c+3
         pipe.advance(regs, sm, c, nchunks);
 
         // ---- publish the state after this chunk for the next readout
@@ -766,6 +767,11 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
         if (c + 1 < nchunks) step(c + 1, pipe.b);  // chunk c+2 (even) is in set B
     }
 
+    // padded tokens of the last chunk entered the constant row of the
+    // normaliser (tile 8, row 8 = lane group 2, element 0)
+    if constexpr (U == 0) {
+        if (g == 2) acc[2][kNV][0] -= (float)(nchunks * kC - L);
+    }
     if (MODE == kModeState) {
         ws_store<U, DV>(acc[0], ws_out, lane);
         ws_store<U + 4, DV>(acc[1], ws_out, lane);
