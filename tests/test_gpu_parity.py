@@ -138,6 +138,40 @@ def test_prefill_many_heads(dv):
         report(f"many-heads dv={dv} ({b},{h}) z", ratio(z[sl], zo), 2e-2)
 
 
+@pytest.mark.parametrize("L,H", [(300, 2), (2048, 4)])
+def test_prefill_graph_replay(L, H):
+    """Captured in a HIP graph (as the benchmark runs it), every replay gives
+    the eager result bit for bit, with eager work and synchronisation in
+    between replays.  (2048, 4) takes the segment split and its workspace."""
+    based = based_mod()
+    q, k, v = dev(*si.custom((1, H, L, 16), (1, H, L, 64), seed=810 + L, scale=0.5))
+    nbytes = based.based_prefill_workspace_bytes(1, H, L, 64)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    y = torch.empty(1, H, L, 64, device=DEV)
+    S = torch.empty(1, H, 273, 64, device=DEV)
+    z = torch.empty(1, H, 273, device=DEV)
+    ref = [t.clone() for t in based.based_prefill(q, k, v, y=y, S=S, z=z, workspace=ws)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        based.based_prefill(q, k, v, y=y, S=S, z=z, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        based.based_prefill(q, k, v, y=y, S=S, z=z, workspace=ws)
+    for rep in range(3):
+        for t in (y, S, z):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip("ySz", (y, S, z), ref):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager result"
+        based.based_prefill(q[:, :1].contiguous(), k[:, :1].contiguous(), v[:, :1].contiguous())  # eager work
+        torch.cuda.synchronize()
+
+
 def test_prefill_deterministic():
     based = based_mod()
     q, k, v = dev(*si.custom((2, 2, 300, 16), (2, 2, 300, 64), seed=800, scale=0.5))
