@@ -8,38 +8,90 @@
 // the kernel fuses y = add + softmax-window(q, k, v).
 //
 // MI355X design
-//  * One workgroup (4 waves) per (batch*head, 64-query tile); wave w owns
-//    queries i0+16w .. i0+16w+15, whose keys lie in 80 rows
-//    [i0+16w-64, i0+16w+16) = 5 key tiles of 16.
-//  * Q, K rows and V^T (transposed for the P.V operand) of the tile and its
-//    64-row halo are staged in LDS once; the workgroup's halo is the
-//    previous tile, which the block order keeps on the same XCD (its L2).
-//  * Scores are computed transposed, S^T = K Q^T (16x16xK MFMA), so each
-//    lane holds one query and 4 keys per tile: the probabilities are already
-//    in the A-operand layout of P.V (keys of two tiles form one 32-deep
-//    k-step).  Softmax runs in fp32 (exp2, max-subtracted); P enters the
-//    MFMA as a hi/lo bf16 pair so the weights carry ~16 bits.
-//  * The normaliser is the fp32 sum of the same probabilities; output is
-//    fp32 with the optional fused add.
+//  * A workgroup (4 waves) walks a run of 64-query tiles of one head.  K and
+//    V tiles live in a 3-slot LDS ring (the previous tile is the current
+//    tile's halo, so every K/V row is fetched from HBM once), Q in 2 slots.
+//    Tile t+1 is copied global -> LDS with asynchronous 16-byte LDS-DMA
+//    loads while tile t is computed; the fused-add input of tile t+1 is
+//    prefetched into registers at the same time.
+//  * LDS rows are 16-byte units XOR-swizzled by row, which makes the
+//    score-operand reads and the transposed V reads conflict-free.
+//  * Wave w owns queries i0+16w .. +15, whose keys lie in the 80 rows
+//    [i0+16w-64, i0+16w+16) = 5 key tiles of 16.  Scores are computed
+//    transposed, S^T = K Q^T, so each lane holds one query and 4 keys per
+//    tile: the probabilities are already in the A-operand layout of P.V
+//    (two key tiles form one 32-deep k-step).  The V operand comes from
+//    row-major V through transposed LDS reads (ds_read_b64_tr_b16).
+//  * Softmax runs in fp32 (exp2, max-subtracted); P enters the MFMA as a
+//    hi/lo bf16 pair so the weights carry ~16 bits; the normaliser is the
+//    fp32 sum of the same probabilities.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace based {
 namespace {
 
-constexpr int kQT = 64;        // queries per workgroup
-constexpr int kKR = 128;       // key rows staged: 64-row halo + the tile
+constexpr int kQT = 64;  // queries per tile = key rows per ring slot
 constexpr int kDV = 64;
-constexpr int kVtRow = 136;    // LDS row stride (bf16) of V^T [col][key]
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int DQK>
-struct SwaSmem {
-    static constexpr int kRow = DQK + 8;  // padded row stride (bf16) of Q and K
-    alignas(16) uint16_t q[kQT * kRow];
-    alignas(16) uint16_t k[kKR * kRow];
-    alignas(16) uint16_t vt[kDV * kVtRow];
+#define BASED_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// LDS slots of one step: K/V of the previous (halo) and current tile, Q of
+// the current tile, and the slots that receive tile t+1.  Each slot is its
+// own __shared__ array, so the compiler can tell the copies in flight from
+// the data being read.
+struct SwaSlots {
+    const uint16_t *kp, *kc, *vp, *vc, *qc;
+    uint16_t *kn, *vn, *qn;
 };
+
+// Element offset of (row, col) in a [64][D] bf16 tile whose 16-byte units
+// are XOR-swizzled by row bits.
+template <int D>
+__device__ __forceinline__ int tile_idx(int row, int col) {
+    const int sw = D == 64 ? (row & 7) : ((row >> 3) & 1);
+    return row * D + 8 * ((col >> 3) ^ sw) + (col & 7);
+}
+
+// Asynchronous copy of block b (1 KB = 64 lanes x 16 B) of a [64][D] tile:
+// rows row0.. of a [L][D] matrix (clamped into [0, L)) into an LDS tile.
+// The DMA puts lane l's 16 bytes at byte 16*l of the block, so each lane
+// fetches the source unit that the swizzle stores there.
+template <int D>
+__device__ __forceinline__ void dma_block(const uint16_t* mat, int L, int row0, uint16_t* tile, int b, int lane) {
+    constexpr int kUnits = D / 8;       // 16-byte units per row
+    constexpr int kRows = 64 / kUnits;  // rows per 1 KB block
+    const int row = kRows * b + lane / kUnits;
+    const int su = lane % kUnits;
+    const int sw = D == 64 ? (row & 7) : ((row >> 3) & 1);
+    const int gu = su ^ sw;
+    const int src = min(max(row0 + row, 0), L - 1);
+    __builtin_amdgcn_global_load_lds(mat + (size_t)src * D + 8 * gu, BASED_LDS(void, tile + 512 * b), 16, 0, 0);
+}
+
+// Copies of tile t into slots ks, vs (and qs), split over the four waves.
+// with_q = false for the halo before the run.
+template <int DQK>
+__device__ __forceinline__ void dma_tile(const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int L, int t,
+                                         uint16_t* ks, uint16_t* vs, uint16_t* qs, bool with_q, int w, int lane) {
+    const int row0 = t * kQT;
+    dma_block<kDV>(vh, L, row0, vs, 2 * w, lane);
+    dma_block<kDV>(vh, L, row0, vs, 2 * w + 1, lane);
+    if constexpr (DQK == 64) {
+        dma_block<64>(kh, L, row0, ks, 2 * w, lane);
+        dma_block<64>(kh, L, row0, ks, 2 * w + 1, lane);
+        if (with_q) {
+            dma_block<64>(qh, L, row0, qs, 2 * w, lane);
+            dma_block<64>(qh, L, row0, qs, 2 * w + 1, lane);
+        }
+    } else {
+        if (w < 2) dma_block<16>(kh, L, row0, ks, w, lane);
+        else if (with_q) dma_block<16>(qh, L, row0, qs, w - 2, lane);
+    }
+}
 
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -47,8 +99,6 @@ __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const 
 __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
 
 __device__ __forceinline__ void pack8_hilo(const float (&a)[8], bf16x8& hi, bf16x8& lo) {
     u32x4 h, l;
@@ -61,131 +111,134 @@ __device__ __forceinline__ void pack8_hilo(const float (&a)[8], bf16x8& hi, bf16
     lo = __builtin_bit_cast(bf16x8, l);
 }
 
-// Stage Q (64 rows), K (128 rows) row-major and V^T (64 x 128) into LDS.
-// Rows outside [0, L) are zero.
+// S^T tile: rows = 16 keys (rows kr0.. of key slot ks), cols = the wave's 16
+// queries (rows qr0.. of q slot qs).  Lane (g, r): query r, keys 4g..4g+3.
 template <int DQK>
-__device__ __forceinline__ void swa_stage(const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int L,
-                                          int i0, SwaSmem<DQK>& sm) {
-    constexpr int kRow = SwaSmem<DQK>::kRow;
-    constexpr int kVec = DQK / 8;  // 16-byte vectors per q/k row
-    const int tid = threadIdx.x;
-    const int kbase = i0 - 64;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    // Q rows
-    for (int e = tid; e < kQT * kVec; e += 256) {
-        const int row = e / kVec, c8 = e % kVec, qi = i0 + row;
-        const u32x4 x = qi < L ? *reinterpret_cast<const u32x4*>(qh + (size_t)qi * DQK + 8 * c8) : zero;
-        uint2* d = reinterpret_cast<uint2*>(&sm.q[row * kRow + 8 * c8]);
-        d[0] = make_uint2(x[0], x[1]);
-        d[1] = make_uint2(x[2], x[3]);
-    }
-    // K rows
-    for (int e = tid; e < kKR * kVec; e += 256) {
-        const int row = e / kVec, c8 = e % kVec, kj = kbase + row;
-        const u32x4 x =
-            (kj >= 0 && kj < L) ? *reinterpret_cast<const u32x4*>(kh + (size_t)kj * DQK + 8 * c8) : zero;
-        uint2* d = reinterpret_cast<uint2*>(&sm.k[row * kRow + 8 * c8]);
-        d[0] = make_uint2(x[0], x[1]);
-        d[1] = make_uint2(x[2], x[3]);
-    }
-    // V^T: each thread takes a pair of key rows and 8 columns.
-    for (int e = tid; e < (kKR / 2) * (kDV / 8); e += 256) {
-        const int p = e % (kKR / 2), cb = e / (kKR / 2);
-        const int ka = kbase + 2 * p, kb = ka + 1;
-        const u32x4 a = (ka >= 0 && ka < L) ? *reinterpret_cast<const u32x4*>(vh + (size_t)ka * kDV + 8 * cb) : zero;
-        const u32x4 b = (kb >= 0 && kb < L) ? *reinterpret_cast<const u32x4*>(vh + (size_t)kb * kDV + 8 * cb) : zero;
-        uint32_t* vt = reinterpret_cast<uint32_t*>(&sm.vt[0]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            vt[((8 * cb + 2 * i) * kVtRow + 2 * p) >> 1] = lo_pair(a[i], b[i]);
-            vt[((8 * cb + 2 * i + 1) * kVtRow + 2 * p) >> 1] = hi_pair(a[i], b[i]);
-        }
-    }
-}
-
-// S^T tile: rows = 16 keys (LDS rows kr0..kr0+15), cols = the wave's 16
-// queries (LDS rows qr0..qr0+15).  Lane (g, r): query r, keys 4g..4g+3.
-template <int DQK>
-__device__ __forceinline__ f32x4 score_tile(const SwaSmem<DQK>& sm, int kr0, int qr0, int g, int r) {
-    constexpr int kRow = SwaSmem<DQK>::kRow;
+__device__ __forceinline__ f32x4 score_tile(const uint16_t* ks, int kr0, const uint16_t* qs, int qr0, int g, int r) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (DQK == 16) {
-        const bf16x4 a = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sm.k[(kr0 + r) * kRow + 4 * g]));
-        const bf16x4 b = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sm.q[(qr0 + r) * kRow + 4 * g]));
+        const bf16x4 a = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(ks + tile_idx<16>(kr0 + r, 4 * g)));
+        const bf16x4 b = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(qs + tile_idx<16>(qr0 + r, 4 * g)));
         acc = mfma16(a, b, acc);
     } else {
 #pragma unroll
         for (int kk = 0; kk < DQK / 32; ++kk) {
-            const uint16_t* ka = &sm.k[(kr0 + r) * kRow + 32 * kk + 8 * g];
-            const uint16_t* qb = &sm.q[(qr0 + r) * kRow + 32 * kk + 8 * g];
-            const uint2 a0 = reinterpret_cast<const uint2*>(ka)[0], a1 = reinterpret_cast<const uint2*>(ka)[1];
-            const uint2 b0 = reinterpret_cast<const uint2*>(qb)[0], b1 = reinterpret_cast<const uint2*>(qb)[1];
-            const u32x4 au = {a0.x, a0.y, a1.x, a1.y}, bu = {b0.x, b0.y, b1.x, b1.y};
-            acc = mfma32(__builtin_bit_cast(bf16x8, au), __builtin_bit_cast(bf16x8, bu), acc);
+            const bf16x8 a =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + tile_idx<64>(kr0 + r, 32 * kk + 8 * g)));
+            const bf16x8 b =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qs + tile_idx<64>(qr0 + r, 32 * kk + 8 * g)));
+            acc = mfma32(a, b, acc);
         }
     }
     return acc;
 }
 
+// LDS byte address of the 8 bytes that lane c of a 16-lane group supplies
+// to a transposed 16-bit read of value rows rb..rb+3, column tile ct: row
+// rb + (c >> 2), columns 16ct + 4(c & 3) .. +3.  The read returns to lane c
+// the 4 rows of column 16ct + c.
+__device__ __forceinline__ uint32_t v_tr_addr(const uint16_t* vs, int rb, int ct, int c) {
+    const uint16_t* p = vs + tile_idx<64>(rb + (c >> 2), 16 * ct + 4 * (c & 3));
+    return (uint32_t)(uintptr_t)BASED_LDS(void, p);
+}
+
+// B operands of one P.V k-step for the 4 column tiles: keys (rows) r1..r1+3
+// of slot v1 (first half) and r2..r2+3 of slot v2 (second half, zero when
+// TWO is false).  Written as one asm block (with its own wait) because the
+// compiler, unable to tell these reads from the LDS copies in flight,
+// would otherwise wait for every outstanding memory operation first.  The
+// outputs are early-clobber: a read's data may land while later reads of
+// the block have not issued yet, so no output may share a register with an
+// address.
+template <bool TWO>
+__device__ __forceinline__ void v_kstep(const uint16_t* v1, int r1, const uint16_t* v2, int r2, int c,
+                                        bf16x8 (&vb)[4]) {
+    uint2 x[8];
+    if constexpr (TWO) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %9\n\t"
+            "ds_read_b64_tr_b16 %2, %10\n\t"
+            "ds_read_b64_tr_b16 %3, %11\n\t"
+            "ds_read_b64_tr_b16 %4, %12\n\t"
+            "ds_read_b64_tr_b16 %5, %13\n\t"
+            "ds_read_b64_tr_b16 %6, %14\n\t"
+            "ds_read_b64_tr_b16 %7, %15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+            : "v"(v_tr_addr(v1, r1, 0, c)), "v"(v_tr_addr(v1, r1, 1, c)), "v"(v_tr_addr(v1, r1, 2, c)),
+              "v"(v_tr_addr(v1, r1, 3, c)), "v"(v_tr_addr(v2, r2, 0, c)), "v"(v_tr_addr(v2, r2, 1, c)),
+              "v"(v_tr_addr(v2, r2, 2, c)), "v"(v_tr_addr(v2, r2, 3, c))
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4\n\t"
+            "ds_read_b64_tr_b16 %1, %5\n\t"
+            "ds_read_b64_tr_b16 %2, %6\n\t"
+            "ds_read_b64_tr_b16 %3, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+            : "v"(v_tr_addr(v1, r1, 0, c)), "v"(v_tr_addr(v1, r1, 1, c)), "v"(v_tr_addr(v1, r1, 2, c)),
+              "v"(v_tr_addr(v1, r1, 3, c))
+            : "memory");
+        x[4] = x[5] = x[6] = x[7] = make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        const u32x4 u = {x[ct].x, x[ct].y, x[4 + ct].x, x[4 + ct].y};
+        vb[ct] = __builtin_bit_cast(bf16x8, u);
+    }
+}
+
+// One 64-query tile for wave w: y rows in yacc (P.V, unnormalised) and the
+// normaliser l of this lane's query.
 template <int DQK>
-__global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ v, int L, int ntiles,
-                                                       int total, int window, float scale, const float* add,
-                                                       float* y) {
-    __shared__ SwaSmem<DQK> sm;
-    // Block order: the 8 XCDs take blocks round-robin, so give XCD x a
-    // contiguous run of tiles (each tile's halo is its predecessor, already
-    // in that XCD's L2).
-    int b = blockIdx.x;
-    if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);
-    const int head = b / ntiles;
-    const int i0 = (b % ntiles) * kQT;
-    const uint16_t* qh = q + (size_t)head * L * DQK;
-    const uint16_t* kh = k + (size_t)head * L * DQK;
-    const uint16_t* vh = v + (size_t)head * L * kDV;
-    swa_stage<DQK>(qh, kh, vh, L, i0, sm);
-    __syncthreads();
+__device__ __forceinline__ void swa_tile(const SwaSlots& sl, int t, int window, float sl2, int w, int g, int r,
+                                         f32x4 (&yacc)[4], float& l) {
+    const uint16_t* prev_k = sl.kp;
+    const uint16_t* cur_k = sl.kc;
+    const uint16_t* prev_v = sl.vp;
+    const uint16_t* cur_v = sl.vc;
+    const uint16_t* qs = sl.qc;
+    const int q0 = t * kQT + 16 * w;  // first query of the wave
+    const int qi = q0 + r;            // this lane's query
 
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-    const int q0 = i0 + 16 * w;           // first query of the wave
-    const int qi = q0 + r;                // this lane's query
-    const float sl2 = scale * kLog2e;
-
-    // Scores for key tiles t = 0..4: keys q0 - 64 + 16t + 4g + m.
+    // Scores for key tiles j = 0..4: keys q0 - 64 + 16j + 4g + m, which sit
+    // in rows 16w + 16j of the [prev | cur] window.
     float s[5][4];
 #pragma unroll
-    for (int t = 0; t < 5; ++t) {
-        const f32x4 st = score_tile<DQK>(sm, 16 * w + 16 * t, 16 * w, g, r);
+    for (int j = 0; j < 5; ++j) {
+        const int R = 16 * w + 16 * j;
+        const f32x4 st = R < 64 ? score_tile<DQK>(prev_k, R, qs, 16 * w, g, r)
+                                : score_tile<DQK>(cur_k, R - 64, qs, 16 * w, g, r);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int kj = q0 - 64 + 16 * t + 4 * g + m;
+            const int kj = q0 - 64 + 16 * j + 4 * g + m;
             const bool ok = kj >= 0 && kj <= qi && kj > qi - window;
-            s[t][m] = ok ? st[m] * sl2 : -INFINITY;
+            s[j][m] = ok ? st[m] * sl2 : -INFINITY;
         }
     }
     // Row max over all 80 keys: this lane's 20, then across the 4 lane groups.
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 5; ++t)
+    for (int j = 0; j < 5; ++j)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) mx = fmaxf(mx, s[t][m]);
+        for (int m = 0; m < 4; ++m) mx = fmaxf(mx, s[j][m]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float l = 0.f;
+    l = 0.f;
 #pragma unroll
-    for (int t = 0; t < 5; ++t)
+    for (int j = 0; j < 5; ++j)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const float p = exp2f(s[t][m] - mx);  // masked keys: exp2(-inf) = 0
-            s[t][m] = p;
+            const float p = exp2f(s[j][m] - mx);  // masked keys: exp2(-inf) = 0
+            s[j][m] = p;
             l += p;
         }
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
 
     // Y = P V over 3 k-steps of 32 keys (tiles 2p, 2p+1; tile 5 is empty).
-    f32x4 yacc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) yacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -198,39 +251,153 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
         }
         bf16x8 ahi, alo;
         pack8_hilo(a, ahi, alo);
+        // key rows of this lane group: R1 + 4g .. +3 (tile 2p), R2 + 4g .. +3 (tile 2p+1)
+        const int R1 = 16 * w + 32 * p, R2 = R1 + 16;
+        const uint16_t* v1 = R1 < 64 ? prev_v : cur_v;
+        const uint16_t* v2 = R2 < 64 ? prev_v : cur_v;
+        const int r1 = (R1 & 63) + 4 * g, r2 = (R2 & 63) + 4 * g;
         bf16x8 vb[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            // keys (LDS rows) 16w + 32p + 4g .. +3 and 16w + 32p + 16 + 4g .. +3
-            const uint16_t* vr = &sm.vt[(16 * ct + r) * kVtRow + 16 * w + 32 * p + 4 * g];
-            const uint2 x0 = *reinterpret_cast<const uint2*>(vr);
-            // k-step 2 has no second key tile: its half of the operand is zero
-            // (and must not be read: it would run past the staged keys).
-            const uint2 x1 = 2 * p + 1 < 5 ? *reinterpret_cast<const uint2*>(vr + 16) : make_uint2(0u, 0u);
-            const u32x4 u = {x0.x, x0.y, x1.x, x1.y};
-            vb[ct] = __builtin_bit_cast(bf16x8, u);
-        }
+        // k-step 2 has no second key tile: that half of the operand is zero
+        if (p < 2) v_kstep<true>(v1, r1, v2, r2, r, vb);
+        else v_kstep<false>(v1, r1, v2, r2, r, vb);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) yacc[ct] = mfma32(ahi, vb[ct], yacc[ct]);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) yacc[ct] = mfma32(alo, vb[ct], yacc[ct]);
     }
+}
 
-    // Rows of yacc are queries q0 + 4g + m; the normaliser of query q0+j
-    // lives in lane group (j >> 2)... every lane of row group j holds it
-    // for its own query r, so fetch l of query 4g + m from lane 4g + m.
-    const size_t base = (size_t)head * L;
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8; the other counters left at "no wait").  Issued
+// through the builtin so that the compiler's own wait insertion knows
+// which memory operations have completed.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// Byte offset of (query row, column) in a head's [L][64] fp32 array.
+__device__ __forceinline__ int out_off(int row, int col) { return (row * kDV + col) * 4; }
+constexpr int kNT = 2;  // buffer access: streaming (nontemporal)
+
+// Fused-add input of one tile for this lane: rows q0 + 4g + m, columns
+// 16ct + r.  Buffer loads: rows past the end read as 0 (range-checked by
+// the resource), so the access needs no branch.
+__device__ __forceinline__ void load_add(__amdgpu_buffer_rsrc_t ra, int q0, int g, int r, float (&a)[16]) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int qq = q0 + 4 * g + m;
-        const float lq = __shfl(l, 4 * g + m, 64);
-        if (qq < L) {
-            const float inv = 1.f / lq;
-            const size_t o = (base + qq) * kDV + r;
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+            a[4 * m + ct] =
+                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, out_off(q0 + 4 * g + m, 16 * ct + r), 0, kNT));
+}
+
+// Barrier without the compiler's release/acquire fences (which would wait
+// for every outstanding copy); the waits are explicit in the pipeline.
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int DQK, bool ADD>
+__global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restrict__ q,
+                                                       const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v, int L, int ntiles,
+                                                       int tiles_per_wg, int wg_per_head, int window, float scale,
+                                                       const float* add, float* y) {
+    // K/V ring: tile tb - 1 + j lives in slot j mod 3; Q of tile tb + j in slot j mod 2.
+    __shared__ alignas(16) uint16_t k0[kQT * DQK], k1[kQT * DQK], k2[kQT * DQK];
+    __shared__ alignas(16) uint16_t v0[kQT * kDV], v1[kQT * kDV], v2[kQT * kDV];
+    __shared__ alignas(16) uint16_t q0s[kQT * DQK], q1s[kQT * DQK];
+    uint16_t* const ks[3] = {k0, k1, k2};
+    uint16_t* const vs[3] = {v0, v1, v2};
+    uint16_t* const qs[2] = {q0s, q1s};
+
+    const int head = blockIdx.x / wg_per_head;
+    const int tb = (blockIdx.x % wg_per_head) * tiles_per_wg;
+    const int te = min(tb + tiles_per_wg, ntiles);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const uint16_t* qh = q + (size_t)head * L * DQK;
+    const uint16_t* kh = k + (size_t)head * L * DQK;
+    const uint16_t* vh = v + (size_t)head * L * kDV;
+    // Outputs (and the fused-add input) through buffer resources covering
+    // exactly this head: rows past L are dropped (stores) or read as 0, so
+    // every step issues the same memory instructions, with no branches.
+    const int head_bytes = L * kDV * 4;
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(y + (size_t)head * L * kDV, (short)0, head_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        ADD ? (void*)(add + (size_t)head * L * kDV) : (void*)y, (short)0, ADD ? head_bytes : 0, 0x00020000);
+    const float sl2 = scale * kLog2e;
+
+    // Prologue: halo tile tb-1 (K, V) into slot 0 and tile tb into slot 1;
+    // add of tile tb.  The vector-memory counter retires in issue order, so
+    // waiting until only the 16 add loads remain means every copy landed.
+    float adda[16], addb[16];
+    dma_tile<DQK>(qh, kh, vh, L, tb - 1, k0, v0, nullptr, false, w, lane);
+    dma_tile<DQK>(qh, kh, vh, L, tb, k1, v1, q0s, true, w, lane);
+    if (ADD) {
+        load_add(ra, tb * kQT + 16 * w, g, r, adda);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
+    } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    raw_barrier();
+
+    // Step j of the run (tile t = tb + j): start the copies (and the add
+    // loads) of tile t+1 (past the run they are harmless re-reads of valid
+    // rows into unused slots), compute and store tile t, then wait for tile
+    // t+1's copies -- the 16 add loads and 16 stores issued after them may
+    // stay in flight -- before the barrier.
+    auto step = [&](auto J, int t, const float (&cur_add)[16], float (&next_add)[16]) {
+        constexpr int j = decltype(J)::value;
+        SwaSlots sl;
+        sl.kp = ks[j % 3];
+        sl.kc = ks[(j + 1) % 3];
+        sl.vp = vs[j % 3];
+        sl.vc = vs[(j + 1) % 3];
+        sl.qc = qs[j % 2];
+        sl.kn = ks[(j + 2) % 3];
+        sl.vn = vs[(j + 2) % 3];
+        sl.qn = qs[(j + 1) % 2];
+        dma_tile<DQK>(qh, kh, vh, L, t + 1, sl.kn, sl.vn, sl.qn, true, w, lane);
+        if (ADD) load_add(ra, (t + 1) * kQT + 16 * w, g, r, next_add);
+        f32x4 yacc[4];
+        float l;
+        swa_tile<DQK>(sl, t, window, sl2, w, g, r, yacc, l);
+        const int q0 = t * kQT + 16 * w;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float inv = __builtin_amdgcn_rcpf(__shfl(l, 4 * g + m, 64));  // l >= 1: the max key has p = 1
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
-                const float prev = add ? add[o + 16 * ct] : 0.f;
-                y[o + 16 * ct] = prev + yacc[ct][m] * inv;
+                const float o = yacc[ct][m] * inv + (ADD ? cur_add[4 * m + ct] : 0.f);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), ry, out_off(q0 + 4 * g + m, 16 * ct + r), 0,
+                                                      kNT);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(ADD ? 32 : 16));
+        raw_barrier();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    // Six steps per iteration (slot indices repeat every 6 tiles), nested so
+    // that each step follows exactly one other in the control flow.
+    for (int t = tb; t < te; t += 6) {
+        step(I0{}, t, adda, addb);
+        if (t + 1 < te) {
+            step(I1{}, t + 1, addb, adda);
+            if (t + 2 < te) {
+                step(I2{}, t + 2, adda, addb);
+                if (t + 3 < te) {
+                    step(I3{}, t + 3, addb, adda);
+                    if (t + 4 < te) {
+                        step(I4{}, t + 4, adda, addb);
+                        if (t + 5 < te) step(I5{}, t + 5, addb, adda);
+                    }
+                }
             }
         }
     }
@@ -241,16 +408,29 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
 hipError_t launch_swa_mfma(const void* q, const void* k, const void* v, int BH, int L, int dqk, int window,
                            float scale, const float* add, float* y, hipStream_t st) {
     const int ntiles = (L + kQT - 1) / kQT;
-    const int total = BH * ntiles;
+    // Tiles per workgroup: long runs amortise the halo and the pipeline
+    // fill; keep about two workgroups per compute unit.
+    const int tpw = max(1, min(16, (BH * ntiles + 511) / 512));
+    const int wg_per_head = (ntiles + tpw - 1) / tpw;
+    const dim3 grid(BH * wg_per_head);
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     const uint16_t* vv = static_cast<const uint16_t*>(v);
-    if (dqk == 16)
-        hipLaunchKernelGGL((swa_mfma_kernel<16>), dim3(total), dim3(256), 0, st, qq, kk, vv, L, ntiles, total,
-                           window, scale, add, y);
-    else
-        hipLaunchKernelGGL((swa_mfma_kernel<64>), dim3(total), dim3(256), 0, st, qq, kk, vv, L, ntiles, total,
-                           window, scale, add, y);
+    if (dqk == 16) {
+        if (add)
+            hipLaunchKernelGGL((swa_mfma_kernel<16, true>), grid, dim3(256), 0, st, qq, kk, vv, L, ntiles, tpw,
+                               wg_per_head, window, scale, add, y);
+        else
+            hipLaunchKernelGGL((swa_mfma_kernel<16, false>), grid, dim3(256), 0, st, qq, kk, vv, L, ntiles, tpw,
+                               wg_per_head, window, scale, add, y);
+    } else {
+        if (add)
+            hipLaunchKernelGGL((swa_mfma_kernel<64, true>), grid, dim3(256), 0, st, qq, kk, vv, L, ntiles, tpw,
+                               wg_per_head, window, scale, add, y);
+        else
+            hipLaunchKernelGGL((swa_mfma_kernel<64, false>), grid, dim3(256), 0, st, qq, kk, vv, L, ntiles, tpw,
+                               wg_per_head, window, scale, add, y);
+    }
     return hipGetLastError();
 }
 

@@ -251,6 +251,30 @@ def test_swa_add_modes():
     assert torch.equal(y_inplace, y_add)
 
 
+@pytest.mark.parametrize("dqk,add", [(64, False), (16, True)])
+def test_swa_long_runs(dqk, add):
+    """Many 64-query tiles per workgroup (B*H=128, 38 tiles a head: runs of
+    10 tiles, the last one 8, ending in a ragged tile), so every slot
+    rotation of the K/V/Q ring is used; two launches must agree bit for bit."""
+    based = based_mod()
+    B, H, L = 2, 64, 64 * 37 + 5
+    q, k, v = si.custom((B, H, L, dqk), (B, H, L, 64), seed=1400 + dqk, scale=1.0)
+    qd, kd, vd = dev(q, k, v)
+    base = torch.randn(B, H, L, 64, generator=torch.Generator().manual_seed(6)) if add else None
+    scale = dqk ** -0.5
+    outs = [based.swa_forward(qd, kd, vd, window=64, scale=scale,
+                              add=base.to(DEV) if add else None) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    heads = _sample_heads(B, H, 4, 3)
+    bi = [b for b, _ in heads]
+    hi = [h for _, h in heads]
+    want = oracle.swa(q[bi, hi], k[bi, hi], v[bi, hi], 64, scale)
+    if add:
+        want = want + base[bi, hi].double().numpy()
+    report(f"swa long runs dqk={dqk} add={add} (4 sampled heads)", ratio(outs[0][bi, hi], want), 2e-2)
+
+
 # ---------------------------------------------------------------- workloads
 def test_workload_tiny_f32_layer():
     """B=1,H=1,L=256 fp32: Taylor linear attention + w=64 window, summed."""
