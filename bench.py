@@ -11,7 +11,8 @@ prints one JSON line with:
 
 * value: tokens/s (tokens = B*L per step, each token covering all H heads);
 * roofline: the prefill kernel's algorithmic bytes per launch / its mean
-  HIP-event duration in the timed loop, against 8 TB/s HBM (the kernel's
+  launch duration (HIP events on the launch stream around the timed loop,
+  over the number of launches), against 8 TB/s HBM (the kernel's
   arithmetic intensity is below the bf16 MFMA ridge), plus its algorithmic
   flop rate against the 2.5 PFLOP/s dense bf16 MFMA peak; `traffic` comes
   from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary when that
@@ -103,26 +104,43 @@ def read_traffic(summary: str, digest: str, launches_per_kernel: int = 1):
         return None
 
 
-class EventTimer:
-    """Mean duration of launches bracketed on the current stream."""
+class RegionTimer:
+    """HIP events on the launch stream around a whole timed region: the mean
+    launch duration is the region's GPU time over the launches in it, with
+    no event between launches (events between back-to-back launches add
+    their own gaps)."""
 
     def __init__(self):
-        self.pairs = []
+        self.e0 = torch.cuda.Event(enable_timing=True)
+        self.e1 = torch.cuda.Event(enable_timing=True)
 
     def start(self):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        return e0
+        self.e0.record(torch.cuda.current_stream())
 
-    def stop(self, e0):
-        e1 = torch.cuda.Event(enable_timing=True)
-        e1.record()
-        self.pairs.append((e0, e1))
+    def stop(self):
+        self.e1.record(torch.cuda.current_stream())
 
-    def mean_s(self) -> float:
-        torch.cuda.synchronize()
-        ts = [a.elapsed_time(b) for a, b in self.pairs]
-        return sum(ts) / len(ts) / 1e3
+    def seconds(self) -> float:
+        self.e1.synchronize()
+        return self.e0.elapsed_time(self.e1) / 1e3
+
+
+def launch_distribution(launch, n: int) -> dict:
+    """Median, p10 and p90 of single launches, each between its own pair of
+    events (created beforehand), in a pass after the timed region."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    st = torch.cuda.current_stream()
+    for i, (a, b) in enumerate(evs):
+        a.record(st)
+        launch(i)
+        b.record(st)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+    def pct(p):
+        return ts[min(len(ts) - 1, int(round(p * (len(ts) - 1))))]
+
+    return {"median_us": pct(0.5), "p10_us": pct(0.1), "p90_us": pct(0.9), "launches": n}
 
 
 def make_sets(tensors, n):
@@ -134,6 +152,8 @@ def make_sets(tensors, n):
 
 # ---------------------------------------------------------------- legs
 def bench_prefill(based, wl, steps, warmup):
+    """Returns (wall seconds per step, mean launch seconds from the events
+    around the timed region, per-launch distribution)."""
     q, k, v = si.linear_inputs(wl)
     ins = make_sets((q, k, v), N_SETS)
     outs = []
@@ -144,26 +164,28 @@ def bench_prefill(based, wl, steps, warmup):
     nbytes = based.based_prefill_workspace_bytes(wl.B, wl.H, wl.L, wl.dv)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
-    def step(i, timer=None):
+    def step(i):
         (qq, kk, vv), (y, S, z) = ins[i % N_SETS], outs[i % N_SETS]
-        e0 = timer.start() if timer else None
         based.based_prefill(qq, kk, vv, chunk=wl.chunk, eps=wl.eps, y=y, S=S, z=z, workspace=ws)
-        if timer:
-            timer.stop(e0)
 
     for i in range(warmup):
         step(i)
-    timer = EventTimer()
+    timer = RegionTimer()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    timer.start()
     for i in range(steps):
-        step(i, timer)
+        step(i)
+    timer.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall / steps, timer.mean_s()
+    dist = launch_distribution(step, min(max(steps, 20), 50))
+    return wall / steps, timer.seconds() / steps, dist
 
 
 def bench_decode(based, wl, n_steps):
+    """1024-token prefill, then n_steps next-token steps timed as one region.
+    Returns (wall seconds per step, event seconds per step)."""
     q, k, v = si.linear_inputs(wl)
     _, S, z = based.based_prefill(*(t.cuda() for t in (q, k, v)), chunk=wl.chunk, eps=wl.eps)
     del q, k, v
@@ -173,33 +195,40 @@ def bench_decode(based, wl, n_steps):
         S2, z2 = S.clone(), z.clone()
         based.based_decode_step(*step_in[t], S2, z2, eps=wl.eps, y=y)
     del S2, z2
-    timer = EventTimer()
+    timer = RegionTimer()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    timer.start()
     for t in range(n_steps):
-        e0 = timer.start()
         based.based_decode_step(*step_in[t], S, z, eps=wl.eps, y=y)
-        timer.stop(e0)
+    timer.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall / n_steps, timer.mean_s()
+    return wall / n_steps, timer.seconds() / n_steps
 
 
 def bench_swa(based, wl, reps):
+    """Window kernel with fused add, alternating two input/output sets;
+    returns event seconds per launch over the timed region."""
     q, k, v = si.linear_inputs(wl)
     qw, kw = si.window_inputs(wl)
     sets = make_sets((qw, kw, v), 2)
     del q, k
     adds = [torch.randn(wl.B, wl.H, wl.L, wl.dv, device="cuda") for _ in range(2)]
     ys = [torch.empty_like(adds[0]) for _ in range(2)]
+
+    def launch(i):
+        based.swa_forward(*sets[i % 2], window=wl.window, scale=wl.swa_scale, add=adds[i % 2], y=ys[i % 2])
+
     for i in range(3):
-        based.swa_forward(*sets[i % 2], window=wl.window, scale=wl.swa_scale, add=adds[i % 2], y=ys[i % 2])
-    timer = EventTimer()
+        launch(i)
+    timer = RegionTimer()
+    torch.cuda.synchronize()
+    timer.start()
     for i in range(reps):
-        e0 = timer.start()
-        based.swa_forward(*sets[i % 2], window=wl.window, scale=wl.swa_scale, add=adds[i % 2], y=ys[i % 2])
-        timer.stop(e0)
-    return timer.mean_s()
+        launch(i)
+    timer.stop()
+    return timer.seconds() / reps
 
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -258,7 +287,7 @@ def main():
 
     wl = si.WORKLOADS[args.workload]
     print(f"[bench] workload {wl.name}: {wl.description}", file=sys.stderr, flush=True)
-    step_s, kern_s = bench_prefill(based, wl, args.steps, args.warmup)
+    step_s, kern_s, dist = bench_prefill(based, wl, args.steps, args.warmup)
     tokens = wl.B * wl.L
     abytes, aflops = prefill_bytes(wl), prefill_flops(wl)
     digest = source_digest("prefill_mfma.hip", "common.hpp")
@@ -287,6 +316,8 @@ def main():
             "traffic": read_traffic(f"prefill_mfma_{wl.name}_pmc.txt", digest),
             "kernel": "based_prefill (bf16 MFMA)",
             "kernel_ms": kern_s * 1e3,
+            "kernel_timing": "HIP events around the timed region on the launch stream / steps",
+            "single_launch_us": dist,
             "algorithmic_bytes": abytes,
             "algorithmic_flops": aflops,
             "mfma_tflops": aflops / kern_s / 1e12,
@@ -316,7 +347,7 @@ def main():
         print(f"[bench] swa: {skern*1e6:.1f} us, {sb/skern/1e9:.0f} GB/s", file=sys.stderr, flush=True)
         if wl.name != "long_64k":
             wlong = si.WORKLOADS["long_64k"]
-            lstep, lkern = bench_prefill(based, wlong, 10, 2)
+            lstep, lkern, _ = bench_prefill(based, wlong, 10, 2)
             lb = prefill_bytes(wlong)
             extra["long_64k_prefill"] = {"tokens_per_s": wlong.B * wlong.L / lstep, "kernel_ms": lkern * 1e3,
                                          "hbm_GBps": lb / lkern / 1e9, "hbm_frac": lb / lkern / HBM_PEAK,
