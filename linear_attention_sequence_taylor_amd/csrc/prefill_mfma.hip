@@ -925,21 +925,27 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
 // carries its own copy of the normaliser tile and recomputes the features),
 // and long sequences into segments, until there are enough workgroups for
 // one per compute unit (the LDS footprint allows one resident workgroup per
-// CU).  Segments cost an extra state pass, so they are added only when the
-// heads x column groups fill less than the chip.
+// CU).  Segments cost an extra state pass; 32-wide groups cost a second
+// copy of all feature work.  So: 32-wide groups when they fill the chip
+// without segments; otherwise, if the sequence is long enough for segments
+// alone to fill it, 64-wide groups plus segments; otherwise 32-wide groups
+// plus as many segments as the length allows.
 constexpr int kTargetWorkgroups = 256;
 struct PrefillPlan {
     int dvl, ncg, nseg;
 };
 PrefillPlan plan_prefill(int BH, int L, int dv, bool use_init, bool have_ws) {
     PrefillPlan pl;
-    pl.dvl = (dv == 128 && BH * 4 > 1024) ? 64 : 32;
-    pl.ncg = dv / pl.dvl;
     const int nchunks = (L + kC - 1) / kC;
+    const int max_seg = nchunks / 2;  // segments of at least two chunks
+    const int units32 = BH * (dv / 32), units64 = BH * (dv / 64);
+    pl.dvl = (dv == 128 && BH * 4 > 1024) ? 64 : 32;
+    if (units32 < kTargetWorkgroups && have_ws && max_seg * units64 >= kTargetWorkgroups) pl.dvl = 64;
+    pl.ncg = dv / pl.dvl;
     const int units = BH * pl.ncg;
     pl.nseg = 1;
     if (units < kTargetWorkgroups && nchunks >= 4)
-        pl.nseg = max(1, min((kTargetWorkgroups + units - 1) / units, nchunks / 2));
+        pl.nseg = max(1, min((kTargetWorkgroups + units - 1) / units, max_seg));
     // With an initial state and several column groups, the carried state
     // goes through the workspace (no group may overwrite z while another
     // still reads it).  Without a workspace: one 64-wide group for d_v = 64;

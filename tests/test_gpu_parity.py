@@ -138,6 +138,30 @@ def test_prefill_many_heads(dv):
         report(f"many-heads dv={dv} ({b},{h}) z", ratio(z[sl], zo), 2e-2)
 
 
+@pytest.mark.parametrize("dv", [64, 128])
+@pytest.mark.parametrize("init", [False, True])
+def test_prefill_long_few_heads(dv, init):
+    """Few heads and a long ragged sequence: the launch takes 64-wide value
+    groups and ~100 sequence segments of three chunks (state pass, prefix
+    scan over segments, output pass), with and without a carried state."""
+    based = based_mod()
+    L = 64 * 300 + 17
+    q, k, v = si.custom((1, 2, L, 16), (1, 2, L, dv), seed=730 + dv + init, scale=0.5)
+    S0 = z0 = None
+    kw = {}
+    if init:
+        qp, kp, vp = si.custom((1, 2, 50, 16), (1, 2, 50, dv), seed=731 + dv, scale=0.5)
+        _, S0, z0 = oracle.la_recurrent(qp, kp, vp, want_y=False)
+        S0, z0 = torch.as_tensor(S0, dtype=torch.float32), torch.as_tensor(z0, dtype=torch.float32)
+        kw["initial_state"] = tuple(dev(S0, z0))
+    y, S, z = based.based_prefill(*dev(q, k, v), **kw)
+    torch.cuda.synchronize()
+    yo, So, zo = oracle.la_recurrent(q, k, v, S0=S0, z0=z0)
+    report(f"long few-heads dv={dv} init={init} y", ratio(y, yo), 2e-2)
+    report(f"long few-heads dv={dv} init={init} S", ratio(S, So), 2e-2)
+    report(f"long few-heads dv={dv} init={init} z", ratio(z, zo), 2e-2)
+
+
 @pytest.mark.parametrize("L,H", [(300, 2), (2048, 4)])
 def test_prefill_graph_replay(L, H):
     """Captured in a HIP graph (as the benchmark runs it), every replay gives
