@@ -10,8 +10,22 @@
 // ...", App. A, chunkwise form, has the same inter/intra split).
 //
 // MI355X design
-//  * One workgroup (4 waves) per (batch, head) walks the chunks in order.
-//    The state lives in MFMA accumulators (fp32) for the whole sequence.
+//  * One workgroup of 12 waves per (batch, head, value-column group[,
+//    sequence segment]) walks the 64-token chunks in order, one barrier
+//    per chunk.  The state lives in MFMA accumulators (fp32) for the whole
+//    sequence.  Waves w, w + 4 and w + 8 share a SIMD:
+//      - waves 0..3, off-diagonal: psi(Q) of query tile w (16 rows) times
+//        the state before the chunk, handed to the on-diagonal wave of the
+//        same tile through LDS; they also stage Q and K of the next chunk;
+//      - waves 4..7, update: rotation tiles w-4, w and (for w-4 < 2) w+4
+//        of [S | z] += psi(K)^T [V | 1], then the state rounded to bf16
+//        into LDS for the next chunk's readout; they stage V^T;
+//      - waves 8..11, on-diagonal: the causal intra-chunk term of query
+//        tile w-8, then (one chunk later) the sum with the hand-off, the
+//        normalisation and the fp32 stores.  Only these waves store to
+//        global memory, so the other waves' waits on the vector-memory
+//        counter (which counts loads and stores in issue order) never
+//        cover output stores.
 //  * Symmetric features.  phi(q).phi(k) only needs the 136 distinct
 //    products k_a k_b (a <= b) plus 16 linear terms and the constant:
 //    153 feature rows, padded to 160 = 10 "rotation tiles" of 16 rows.
@@ -26,18 +40,13 @@
 //  * The normaliser z is an extra 16-column accumulator tile driven by a
 //    ones operand, so phi(q).z and the on-diagonal row sums come out of the
 //    same MFMAs in the same register layout as the numerator.
-//  * Readout of chunk c uses the state before c: after each chunk's update
-//    the owners round the state to bf16 into LDS (double-buffered for
-//    d_v = 64), where every wave reads it as the B operand of
-//    psi(Q) x S.  The linear/constant rows (and the last feature k-step)
-//    are stored as a hi/lo bf16 pair; the on-diagonal weights
-//    1 + s + s^2/2 are used as a hi/lo bf16 pair too (fp32-like precision
-//    where outputs are most sensitive).
-//  * Wave w owns query tile w (16 rows) for the on-diagonal and readout
-//    terms and rotation tiles {w, w+4, w+8} of the state, which balances
-//    the MFMA count across the four waves.
-//  * Q, K, V of chunk c+1 are fetched into registers while chunk c is
-//    computed, then written to the other LDS buffer (V and K transposed).
+//  * Readout of chunk c uses the state before c, double-buffered in LDS.
+//    The linear/constant rows (the last feature k-step) are stored as a
+//    hi/lo bf16 pair and read against a hi/lo psi(Q); the on-diagonal
+//    weights 1 + s + s^2/2 are a hi/lo bf16 pair too.
+//  * Q, K, V of chunk c+1 are fetched into registers two chunks ahead and
+//    written to the other LDS buffer during chunk c (V and K transposed).
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -827,8 +836,9 @@ __device__ __forceinline__ void ws_load(f32x4 (&acc)[DV / 16 + 1], const float* 
     for (int ct = 0; ct < kNCT; ++ct) acc[ct] = p[ct * 64];
 }
 
-// One workgroup = 8 waves.  MODE
-//   kModeFull:    one workgroup per head walks the whole sequence.
+// One workgroup = 12 waves (roles above).  MODE
+//   kModeFull:    one workgroup per (head, column group) walks the whole
+//                 sequence.
 //   kModeState:   workgroup (head, s), s < nseg-1: state increment of
 //                 segment s into slot s+1; s = nseg-1: the initial state
 //                 into slot 0.

@@ -211,11 +211,23 @@ __device__ __forceinline__ void swa_tile(const SwaSlots& sl, int t, int window, 
         const int R = 16 * w + 16 * j;
         const f32x4 st = R < 64 ? score_tile<DQK>(prev_k, R, qs, 16 * w, g, r)
                                 : score_tile<DQK>(cur_k, R - 64, qs, 16 * w, g, r);
+        if (window == kQT && q0 >= kQT) {
+            // Full 64-key window, no key before the sequence start: key
+            // 16j + 4g + m of the 80 is in the window of query r iff it lies
+            // in (r, r + 64], so only the first and last key tiles are cut.
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int kj = q0 - 64 + 16 * j + 4 * g + m;
-            const bool ok = kj >= 0 && kj <= qi && kj > qi - window;
-            s[j][m] = ok ? st[m] * sl2 : -INFINITY;
+            for (int m = 0; m < 4; ++m) {
+                const int d = 16 * j + 4 * g + m;
+                const bool ok = j == 0 ? d > r : (j == 4 ? d <= r + 64 : true);
+                s[j][m] = ok ? st[m] * sl2 : -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int kj = q0 - 64 + 16 * j + 4 * g + m;
+                const bool ok = kj >= 0 && kj <= qi && kj > qi - window;
+                s[j][m] = ok ? st[m] * sl2 : -INFINITY;
+            }
         }
     }
     // Row max over all 80 keys: this lane's 20, then across the 4 lane groups.
@@ -231,7 +243,9 @@ __device__ __forceinline__ void swa_tile(const SwaSlots& sl, int t, int window, 
     for (int j = 0; j < 5; ++j)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const float p = exp2f(s[j][m] - mx);  // masked keys: exp2(-inf) = 0
+            // hardware 2^x: masked keys give 2^-inf = 0; arguments below -126
+            // (weights under 2^-126 of the row maximum) may flush to 0
+            const float p = __builtin_amdgcn_exp2f(s[j][m] - mx);
             s[j][m] = p;
             l += p;
         }
@@ -314,7 +328,10 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
     const int head = blockIdx.x / wg_per_head;
     const int tb = (blockIdx.x % wg_per_head) * tiles_per_wg;
     const int te = min(tb + tiles_per_wg, ntiles);
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    // The wave index is uniform across the wave: held in a scalar register,
+    // the slot choices below are scalar branches, not per-lane selects.
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const uint16_t* qh = q + (size_t)head * L * DQK;
     const uint16_t* kh = k + (size_t)head * L * DQK;
     const uint16_t* vh = v + (size_t)head * L * kDV;
@@ -343,10 +360,9 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
     raw_barrier();
 
     // Step j of the run (tile t = tb + j): start the copies (and the add
-    // loads) of tile t+1 (past the run they are harmless re-reads of valid
-    // rows into unused slots), compute and store tile t, then wait for tile
-    // t+1's copies -- the 16 add loads and 16 stores issued after them may
-    // stay in flight -- before the barrier.
+    // loads) of tile t+1 unless t is the run's last tile, compute and store
+    // tile t, then wait for tile t+1's copies -- the 16 add loads and 16
+    // stores issued after them may stay in flight -- before the barrier.
     auto step = [&](auto J, int t, const float (&cur_add)[16], float (&next_add)[16]) {
         constexpr int j = decltype(J)::value;
         SwaSlots sl;
@@ -358,8 +374,10 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
         sl.kn = ks[(j + 2) % 3];
         sl.vn = vs[(j + 2) % 3];
         sl.qn = qs[(j + 1) % 2];
-        dma_tile<DQK>(qh, kh, vh, L, t + 1, sl.kn, sl.vn, sl.qn, true, w, lane);
-        if (ADD) load_add(ra, (t + 1) * kQT + 16 * w, g, r, next_add);
+        if (t + 1 < te) {
+            dma_tile<DQK>(qh, kh, vh, L, t + 1, sl.kn, sl.vn, sl.qn, true, w, lane);
+            if (ADD) load_add(ra, (t + 1) * kQT + 16 * w, g, r, next_add);
+        }
         f32x4 yacc[4];
         float l;
         swa_tile<DQK>(sl, t, window, sl2, w, g, r, yacc, l);
