@@ -43,6 +43,9 @@
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *     enqueued on it asynchronously; no call synchronises the stream.
  *
+ * Sizes: B, H, L >= 1 with B*H <= 2^31 - 1, L <= 2^31 - 1024 and
+ * B*H*L <= 2^40; anything larger returns BASED_E_INVALID.
+ *
  * Errors: arguments are checked before anything is launched; a bad argument
  * returns BASED_E_INVALID (malformed) or BASED_E_UNSUPPORTED (well formed
  * but outside what the kernels implement) and touches no memory.  A failed

@@ -39,7 +39,9 @@ based_status_t launch_status(hipError_t e) { return e == hipSuccess ? BASED_OK :
 
 // Common shape checks; fills element counts.  Returns BASED_OK or an error.
 based_status_t check_dims(int B, int H, int L, uint64_t* BH, uint64_t* BHL) {
-    if (B < 1 || H < 1 || L < 1) return BASED_E_INVALID;
+    // L stays 1023 below INT32_MAX so that chunk and tile counts rounded up
+    // in int arithmetic (L + 63) / 64 cannot overflow.
+    if (B < 1 || H < 1 || L < 1 || L > INT32_MAX - 1023) return BASED_E_INVALID;
     if (!mul_ok((uint64_t)B, (uint64_t)H, BH) || *BH > (uint64_t)INT32_MAX) return BASED_E_INVALID;
     if (!mul_ok(*BH, (uint64_t)L, BHL) || *BHL > ((uint64_t)1 << 40)) return BASED_E_INVALID;
     return BASED_OK;
@@ -151,7 +153,7 @@ BASED_API based_status_t swa_forward(const void* q, const void* k, const void* v
         overlaps(y, y_bytes, v, v_bytes))
         return BASED_E_INVALID;
     if (add && add != y && overlaps(add, y_bytes, y, y_bytes)) return BASED_E_INVALID;
-    const uint64_t tiles = (uint64_t)(L + 63) / 64;
+    const uint64_t tiles = ((uint64_t)L + 63) / 64;
     if (BH * tiles > (uint64_t)INT32_MAX / 2) return BASED_E_INVALID;
     hipStream_t st = static_cast<hipStream_t>(stream);
     // The matrix-core kernel addresses a head's fp32 rows with 32-bit byte

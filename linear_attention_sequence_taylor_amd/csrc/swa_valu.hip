@@ -1,6 +1,6 @@
 // swa_valu.hip -- causal sliding-window softmax attention on the vector ALUs
-// in fp32 (gfx950): the exact-precision path for fp32 inputs.  bf16 inputs
-// take the MFMA kernel in swa_mfma.hip.
+// in fp32 (gfx950): the exact-precision path for fp32 inputs, and for bf16
+// heads too long for the 32-bit offsets of the MFMA kernel in swa_mfma.hip.
 //
 // "Simple linear attention language models balance the recall-throughput
 // tradeoff", s4 "Local Exact Attention": each query attends with exact

@@ -66,6 +66,7 @@ def test_workspace_bytes_host_only(lib):
     assert lib.based_prefill_workspace_bytes(1, 1, 256, 16, 64) >= 0
     assert lib.based_prefill_workspace_bytes(0, 1, 256, 16, 64) == 0
     assert lib.based_prefill_workspace_bytes(1, 1, 256, 8, 64) == 0
+    assert lib.based_prefill_workspace_bytes(1, 1, 2**31 - 1, 16, 64) == 0
 
 
 # Fake, never-dereferenced device addresses; each call below fails validation.
@@ -91,6 +92,7 @@ def _prefill(lib, **kw):
     (dict(q=A + 2), 1), (dict(y=Y + 4), 1),
     (dict(dtype=7), 1), (dict(B=0), 1), (dict(H=-1), 1), (dict(L=0), 1),
     (dict(B=1 << 20, H=1 << 20), 1), (dict(chunk=0), 1), (dict(eps=float("nan")), 1),
+    (dict(L=2**31 - 1), 1), (dict(L=2**31 - 1023), 1), (dict(B=1 << 10, H=1 << 10, L=1 << 21), 1),
     (dict(d=8), 2), (dict(dv=96), 2), (dict(chunk=32), 2), (dict(dtype=0, chunk=48), 2),
     (dict(y=A), 1), (dict(S=Y), 1), (dict(z=S + 64), 1),
 ])
@@ -124,7 +126,7 @@ def _swa(lib, **kw):
 @pytest.mark.parametrize("kw,want", [
     (dict(k=None), 1), (dict(add=S + 4), 1), (dict(window=0), 1), (dict(scale=float("nan")), 1),
     (dict(L=0), 1), (dict(dqk=32), 2), (dict(dv=128), 2), (dict(window=65), 2),
-    (dict(y=A), 1), (dict(add=Y + 256), 1),
+    (dict(y=A), 1), (dict(add=Y + 256), 1), (dict(L=2**31 - 1), 1), (dict(L=2**31 - 64), 1),
 ])
 def test_swa_rejects(lib, kw, want):
     assert _swa(lib, **kw) == want

@@ -299,6 +299,27 @@ def test_swa_long_runs(dqk, add):
     report(f"swa long runs dqk={dqk} add={add} (4 sampled heads)", ratio(outs[0][bi, hi], want), 2e-2)
 
 
+@pytest.mark.parametrize("L", [2**23 - 37, 2**23 + 29])
+def test_swa_longest_heads(L):
+    """Heads at the 32-bit offset limit of the matrix-core window kernel
+    (L * 256 bytes of fp32 output per head): just below it that kernel runs,
+    just above it the fp32-accumulating vector kernel takes bf16 inputs.  A
+    4096-row random block is repeated along L; sampled queries are checked
+    against the oracle on their own 64-key slice (a query sees nothing else)."""
+    based = based_mod()
+    P = 4096
+    blocks = si.custom((1, 1, P, 16), (1, 1, P, 64), seed=1500, scale=1.0)
+    reps = (L + P - 1) // P
+    q, k, v = (t.repeat(1, 1, reps, 1)[:, :, :L].contiguous() for t in blocks)
+    y = based.swa_forward(*dev(q, k, v), window=64, scale=0.25)
+    torch.cuda.synchronize()
+    rows = [0, 5, 63, 64, 4095, 4096, L // 2 + 7, 2**23 - 100, L - 65, L - 2, L - 1]
+    got = torch.stack([y[0, 0, i] for i in rows]).cpu()
+    want = np.stack([oracle.swa(q[:, :, max(0, i - 63):i + 1], k[:, :, max(0, i - 63):i + 1],
+                                v[:, :, max(0, i - 63):i + 1], 64, 0.25)[0, 0, -1] for i in rows])
+    report(f"swa longest head L={L} ({len(rows)} sampled queries)", ratio(got, want), 2e-2)
+
+
 # ---------------------------------------------------------------- workloads
 def test_workload_tiny_f32_layer():
     """B=1,H=1,L=256 fp32: Taylor linear attention + w=64 window, summed."""
