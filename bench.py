@@ -191,9 +191,10 @@ def bench_decode(based, wl, n_steps):
     del q, k, v
     step_in = [tuple(t.cuda() for t in si.decode_inputs(wl, t)) for t in range(n_steps)]
     y = torch.empty(wl.B, wl.H, wl.dv, device="cuda")
-    for t in range(3):  # warm-up on a copy of the state
-        S2, z2 = S.clone(), z.clone()
-        based.based_decode_step(*step_in[t], S2, z2, eps=wl.eps, y=y)
+    # untimed warm-up (~50 ms, out of the idle clock state) on a copy of the state
+    S2, z2 = S.clone(), z.clone()
+    for t in range(500):
+        based.based_decode_step(*step_in[t % n_steps], S2, z2, eps=wl.eps, y=y)
     del S2, z2
     timer = RegionTimer()
     torch.cuda.synchronize()
@@ -220,7 +221,7 @@ def bench_swa(based, wl, reps):
     def launch(i):
         based.swa_forward(*sets[i % 2], window=wl.window, scale=wl.swa_scale, add=adds[i % 2], y=ys[i % 2])
 
-    for i in range(3):
+    for i in range(500):  # untimed warm-up, ~45 ms
         launch(i)
     timer = RegionTimer()
     torch.cuda.synchronize()
@@ -256,8 +257,11 @@ def cpu_baseline(wl, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU leaves its idle clock state only after ~20 ms of continuous
+    # work (the first 50 prefill launches run ~75% slower), so the default
+    # untimed warm-up is 1000 steps (~45 ms) before 400 timed ones.
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="prefill_360m", choices=["prefill_360m", "long_64k"])
     ap.add_argument("--no-extra", action="store_true", help="skip decode/window/64K legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -339,7 +343,7 @@ def main():
             "steps": args.decode_steps, "note": "1024-token prefill then next-token steps; fp32 state"}
         print(f"[bench] decode: {dkern*1e6:.1f} us/step, {db/dkern/1e9:.0f} GB/s", file=sys.stderr, flush=True)
         ww = si.WORKLOADS["window_8k"]
-        skern = bench_swa(based, ww, 20)
+        skern = bench_swa(based, ww, 100)
         sb = swa_bytes(ww)
         extra["window_8k_swa"] = {"tokens_per_s": ww.B * ww.L / skern, "kernel_us": skern * 1e6,
                                   "hbm_GBps": sb / skern / 1e9, "hbm_frac": sb / skern / HBM_PEAK,
@@ -347,7 +351,7 @@ def main():
         print(f"[bench] swa: {skern*1e6:.1f} us, {sb/skern/1e9:.0f} GB/s", file=sys.stderr, flush=True)
         if wl.name != "long_64k":
             wlong = si.WORKLOADS["long_64k"]
-            lstep, lkern, _ = bench_prefill(based, wlong, 10, 2)
+            lstep, lkern, _ = bench_prefill(based, wlong, 50, 100)
             lb = prefill_bytes(wlong)
             extra["long_64k_prefill"] = {"tokens_per_s": wlong.B * wlong.L / lstep, "kernel_ms": lkern * 1e3,
                                          "hbm_GBps": lb / lkern / 1e9, "hbm_frac": lb / lkern / HBM_PEAK,
