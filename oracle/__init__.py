@@ -54,6 +54,9 @@ def _load():
         lib.oracle_la_recurrent.argtypes = [P, P, P, I, I, I, I, D, P, P, P, P, P]
         lib.oracle_decode_step.argtypes = [P, P, P, I, I, I, D, P, P, P]
         lib.oracle_swa.argtypes = [P, P, P, I, I, I, I, I, D, P]
+        lib.oracle_swa_cache_fill.argtypes = [P, P, I, I, I, I, I, P, P]
+        lib.oracle_swa_decode_step.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_longlong), I, I, I, I, D,
+                                               P, P, P]
         _lib = lib
     return _lib
 
@@ -156,3 +159,37 @@ def swa(q, k, v, window: int = 64, scale: float | None = None) -> np.ndarray:
     y = np.empty(tuple(lead) + (L, dv), np.float64)
     _load().oracle_swa(_ptr(q), _ptr(k), _ptr(v), BH, L, dqk, dv, int(window), float(scale), _ptr(y))
     return y
+
+
+def swa_cache_fill(k, v, window: int = 64, k_cache=None, v_cache=None):
+    """The window's key/value ring after a prefix k,v [...,L,*]: the token at
+    position p in slot p mod window.  Slots the prefix does not reach keep
+    the given caches' values (zeros by default).  Returns (k_cache, v_cache),
+    [..., window, *] float64."""
+    k, v = _f64(k), _f64(v)
+    *lead, L, dqk = k.shape
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    kc = np.zeros(tuple(lead) + (window, dqk)) if k_cache is None else _f64(k_cache).copy()
+    vc = np.zeros(tuple(lead) + (window, dv)) if v_cache is None else _f64(v_cache).copy()
+    _load().oracle_swa_cache_fill(_ptr(k), _ptr(v), BH, L, dqk, dv, int(window), _ptr(kc), _ptr(vc))
+    return kc, vc
+
+
+def swa_decode_step(q, k, v, k_cache, v_cache, pos, window: int = 64, scale: float | None = None):
+    """One next-token step of the window.  q,k [B,H,dqk], v [B,H,dv], caches
+    [B,H,window,*], pos [B] (position of each sequence's new token).
+    Returns (y, k_cache_new, v_cache_new); the inputs are not modified."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    B, H, dqk = q.shape
+    dv = v.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    pos = np.ascontiguousarray(np.repeat(np.asarray(pos, dtype=np.int64).reshape(B), H), dtype=np.int64)
+    assert (pos >= 0).all()
+    y = np.empty((B, H, dv), np.float64)
+    _load().oracle_swa_decode_step(_ptr(q), _ptr(k), _ptr(v),
+                                   pos.ctypes.data_as(ctypes.POINTER(ctypes.c_longlong)),
+                                   B * H, dqk, dv, int(window), float(scale), _ptr(kc), _ptr(vc), _ptr(y))
+    return y, kc, vc

@@ -170,3 +170,61 @@ void oracle_swa(const double *q, const double *k, const double *v,
         free(logit);
     }
 }
+
+/* [BASED s4 "Local Exact Attention"]: the window keeps a w-sized key/value
+ * cache.  Ring reading: the token at position p lives in slot p mod window,
+ * so a prefix of L tokens leaves its last min(L, window) tokens in their
+ * slots (other slots are left as they are). */
+void oracle_swa_cache_fill(const double *k, const double *v, int BH, int L, int dqk, int dv,
+                           int window, double *kc, double *vc) {
+    for (int h = 0; h < BH; ++h) {
+        const int p0 = L - window > 0 ? L - window : 0;
+        for (int p = p0; p < L; ++p) {
+            const int slot = p % window;
+            for (int e = 0; e < dqk; ++e)
+                kc[((size_t)h * window + slot) * dqk + e] = k[((size_t)h * L + p) * dqk + e];
+            for (int c = 0; c < dv; ++c)
+                vc[((size_t)h * window + slot) * dv + c] = v[((size_t)h * L + p) * dv + c];
+        }
+    }
+}
+
+/* One next-token step of the window for the token at position pos[h]: its
+ * key and value go into slot pos mod window, then it attends with exact
+ * softmax to positions max(0, pos-window+1) .. pos (its own included), each
+ * read from its slot -- the same sum as oracle_swa's row pos. */
+void oracle_swa_decode_step(const double *q, const double *k, const double *v,
+                            const long long *pos, int BH, int dqk, int dv, int window,
+                            double scale, double *kc, double *vc, double *y) {
+    double *logit = (double *)malloc(sizeof(double) * (size_t)window);
+    for (int h = 0; h < BH; ++h) {
+        const long long p = pos[h];
+        double *kh = kc + (size_t)h * window * dqk;
+        double *vh = vc + (size_t)h * window * dv;
+        const int slot = (int)(p % window);
+        for (int e = 0; e < dqk; ++e) kh[(size_t)slot * dqk + e] = k[(size_t)h * dqk + e];
+        for (int c = 0; c < dv; ++c) vh[(size_t)slot * dv + c] = v[(size_t)h * dv + c];
+        const long long t0 = p - window + 1 > 0 ? p - window + 1 : 0;
+        const int n = (int)(p - t0 + 1);
+        double m = -INFINITY;
+        for (int jj = 0; jj < n; ++jj) {
+            const int s = (int)((t0 + jj) % window);
+            double dot = 0.0;
+            for (int e = 0; e < dqk; ++e) dot += q[(size_t)h * dqk + e] * kh[(size_t)s * dqk + e];
+            logit[jj] = scale * dot;
+            if (logit[jj] > m) m = logit[jj];
+        }
+        double l = 0.0;
+        for (int jj = 0; jj < n; ++jj) {
+            const double e = exp(logit[jj] - m);
+            logit[jj] = e;
+            l += e;
+        }
+        for (int c = 0; c < dv; ++c) {
+            double acc = 0.0;
+            for (int jj = 0; jj < n; ++jj) acc += logit[jj] * vh[(size_t)((t0 + jj) % window) * dv + c];
+            y[(size_t)h * dv + c] = acc / l;
+        }
+    }
+    free(logit);
+}

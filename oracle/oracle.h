@@ -83,6 +83,21 @@ void oracle_swa(const double *q, const double *k, const double *v,
                 int BH, int L, int dqk, int dv, int window, double scale,
                 double *y);
 
+/* The window's key/value cache (ring of `window` slots per head; the token
+ * at position p lives in slot p mod window).  Fill from a prefix of L
+ * tokens: slots of its last min(L, window) tokens are written, the others
+ * are left untouched.  k: [BH,L,dqk]; kc: [BH,window,dqk]. */
+void oracle_swa_cache_fill(const double *k, const double *v, int BH, int L, int dqk, int dv,
+                           int window, double *kc, double *vc);
+
+/* One next-token step of the window for head h at position pos[h] >= 0:
+ * writes k, v into slot pos mod window, then y = exact softmax attention of
+ * q over positions max(0, pos-window+1) .. pos read from their slots.
+ * q,k: [BH,dqk]; v,y: [BH,dv]; kc/vc updated in place. */
+void oracle_swa_decode_step(const double *q, const double *k, const double *v,
+                            const long long *pos, int BH, int dqk, int dv, int window,
+                            double scale, double *kc, double *vc, double *y);
+
 /* Number of OpenMP threads the routines above use. */
 int oracle_num_threads(void);
 

@@ -32,6 +32,12 @@ MUTANTS = {
     "window_one_extra_key": ("const int j0 = i - window + 1 > 0 ? i - window + 1 : 0;",
                              "const int j0 = i - window > 0 ? i - window : 0;"),
     "window_no_exp": ("logit[jj] = exp(logit[jj] - m);", "logit[jj] = 1.0 + logit[jj] - m;"),
+    "ring_slot_shift": ("const int slot = (int)(p % window);", "const int slot = (int)((p + 1) % window);"),
+    "ring_one_key_short": ("p - window + 1 > 0 ? p - window + 1 : 0", "p - window + 2 > 0 ? p - window + 2 : 0"),
+    "ring_no_key_write": ("kh[(size_t)slot * dqk + e] = k[(size_t)h * dqk + e];",
+                          "kh[(size_t)slot * dqk + e] = kh[(size_t)slot * dqk + e];"),
+    "fill_wrong_slot": ("const int slot = p % window;", "const int slot = (p + 1) % window;"),
+    "ring_no_exp": ("const double e = exp(logit[jj] - m);", "const double e = 1.0 + logit[jj] - m;"),
 }
 
 # pins that take only the oracle module
@@ -47,6 +53,8 @@ PIN_FUNCS = [
     pins.test_p5_window_special_cases,
     pins.test_p6_decode_continues_prefill,
     pins.test_p7_small_logits_approach_softmax,
+    lambda m: pins.test_p8_window_decode_continues_window(m, 7, 30),
+    lambda m: pins.test_p8_window_decode_continues_window(m, 64, 10),
     pins.test_hand_taylor_cases,
     pins.test_hand_window_cases,
 ]

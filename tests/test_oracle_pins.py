@@ -16,6 +16,8 @@ Which pin guards which part of the oracle:
   P5  window: library softmax attention with a band mask; w=1; w>=L
   P6  decode step and state handoff/resume
   P7  small-logit limit: linear attention -> softmax attention
+  P8  window decode: ring cache filled from a prefix plus next-token steps
+      equals the library's band-masked softmax attention at each position
   hand hand-worked rational cases in tests/golden/hand_cases.json
 """
 import json
@@ -263,6 +265,37 @@ def test_p6_resume_from_state(oracle_mod):
     np.testing.assert_allclose(np.concatenate([y_a, y_b], axis=2), y_full, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(S_b, S_full, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(z_b, z_full, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P8
+@pytest.mark.parametrize("window,L", [(1, 5), (7, 0), (7, 3), (7, 30), (64, 10), (64, 64), (64, 150)])
+def test_p8_window_decode_continues_window(oracle_mod, window, L):
+    """The w-sized cache of the window [BASED s4 "Local Exact Attention"]:
+    fill it from a prefix, then take next-token steps; every step equals
+    torch's band-masked softmax attention over the whole sequence at that
+    position.  The two sequences of the batch sit at different positions,
+    and the caches start as NaN, so a slot read before it holds one of the
+    last `window` tokens poisons the result."""
+    rng = _rng(40 + window + L)
+    B, H, dqk, dv, lag = 2, 2, 16, 8, 5
+    T = 2 * window + 3
+    n = L + lag + T
+    q = 2 * rng.standard_normal((B, H, n, dqk))
+    k = 2 * rng.standard_normal((B, H, n, dqk))
+    v = rng.standard_normal((B, H, n, dv))
+    scale = 1 / math.sqrt(dqk)
+    full = _sdpa_band(q, k, v, window, scale)
+    starts = [L, L + lag]
+    kc = np.full((B, H, window, dqk), np.nan)
+    vc = np.full((B, H, window, dv), np.nan)
+    for b, L0 in enumerate(starts):
+        kc[b], vc[b] = oracle_mod.swa_cache_fill(k[b:b + 1, :, :L0], v[b:b + 1, :, :L0], window,
+                                                 kc[b:b + 1], vc[b:b + 1])
+    for t in range(T):
+        pos = np.array([L0 + t for L0 in starts])
+        pick = lambda x: np.stack([x[b, :, pos[b]] for b in range(B)])
+        y, kc, vc = oracle_mod.swa_decode_step(pick(q), pick(k), pick(v), kc, vc, pos, window, scale)
+        np.testing.assert_allclose(y, pick(full), rtol=1e-11, atol=1e-12)
 
 
 # ---------------------------------------------------------------- P7
