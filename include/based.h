@@ -1,7 +1,7 @@
 /*
  * based.h -- C ABI of the MI355X (gfx950) Taylor linear attention library.
  *
- * Three operations, as the BASED paper frames inference [1]:
+ * The operations, as the BASED paper frames inference [1]:
  *   based_prefill      "prompt processing": causal Taylor linear attention
  *                      over a whole sequence, returning the outputs and the
  *                      recurrent state ([1] s5 "Execution stages";
@@ -14,6 +14,9 @@
  *                      seeing the preceding `window` keys ([1] s4 "Local
  *                      Exact Attention"), with an optional fused add of the
  *                      linear-attention output (BASED pairs the two).
+ *   swa_cache_fill,    the window's next-token step on a w-sized key/value
+ *   swa_decode_step    ring cache (same section; App. B "Next Token
+ *                      Prediction").
  *
  * [1] "Simple linear attention language models balance the recall-throughput
  *     tradeoff" (arXiv 2402.18668v2).
@@ -153,6 +156,46 @@ based_status_t swa_forward(const void *q, const void *k, const void *v,
                            based_dtype_t dtype, int B, int H, int L,
                            int d_qk, int d_v, int window, float scale,
                            const float *add, float *y, void *stream);
+
+/*
+ * swa_cache_fill / swa_decode_step -- next-token generation for the
+ * sliding window ([1] s4 "Local Exact Attention": each query sees the
+ * preceding `window` keys through a w-sized key/value cache; App. B "Next
+ * Token Prediction").
+ *
+ * Cache: per (batch, head) a ring of `window` slots, k_cache
+ * [B,H,window,d_qk] and v_cache [B,H,window,d_v] in `dtype`, caller-owned.
+ * The token at position p (0-based) lives in slot p mod window.
+ *
+ * swa_cache_fill writes the slots of the last min(L, window) tokens of a
+ * prefix k [B,H,L,d_qk], v [B,H,L,d_v]; other slots are left untouched.
+ *
+ * swa_decode_step handles the token at position pos[b] of each sequence b:
+ *   1. k, v [B,H,d_qk] / [B,H,d_v] go into slot pos[b] mod window;
+ *   2. y = add + sum_{t=max(0,pos-window+1)}^{pos} e_t v_t / sum_t e_t,
+ *      e_t = exp(scale * q.k_t - m), m = max_t scale * q.k_t,
+ *      over the tokens t held in their slots (the new token included) --
+ *      exactly row pos of swa_forward on the whole sequence.
+ * A slot that does not hold one of those tokens is never read, so a cache
+ * only needs the fill (or nothing, when decoding starts at position 0).
+ *   q     [B,H,d_qk] dtype;  pos [B] int64 device array, not modified
+ *         (the caller advances it); pos[b] < 0 gives NaN outputs for b and
+ *         leaves its cache untouched
+ *   add   optional [B,H,d_v] fp32 added to y (e.g. the linear-attention
+ *         decode output); NULL or equal to y for in place
+ *   y     [B,H,d_v] fp32 out
+ * Supported: d_qk in {16, 64}; d_v in {64, 128}; 1 <= window <= 64.  The
+ * caches, y and the inputs must not overlap (add may equal y).
+ */
+based_status_t swa_cache_fill(const void *k, const void *v, based_dtype_t dtype,
+                              int B, int H, int L, int d_qk, int d_v, int window,
+                              void *k_cache, void *v_cache, void *stream);
+
+based_status_t swa_decode_step(const void *q, const void *k, const void *v,
+                               based_dtype_t dtype, int B, int H, int d_qk, int d_v,
+                               int window, float scale, const long long *pos,
+                               void *k_cache, void *v_cache, const float *add,
+                               float *y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,8 @@ HIP kernels of libbased.so; nothing here computes.
     based_prefill(q, k, v)            -> (y, S, z)     prompt processing
     based_decode_step(q, k, v, S, z)  -> y             next-token step (S, z in place)
     swa_forward(q, k, v, window=64)   -> y             sliding-window softmax
+    swa_cache_fill(k, v, window=64)   -> (kc, vc)      window key/value ring from a prefix
+    swa_decode_step(q, k, v, kc, vc, pos) -> y         window next-token step (kc, vc in place)
 """
 from __future__ import annotations
 
@@ -16,8 +18,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["based_prefill", "based_decode_step", "swa_forward", "based_num_features",
-           "based_prefill_workspace_bytes", "BasedError", "library_path"]
+__all__ = ["based_prefill", "based_decode_step", "swa_forward", "swa_cache_fill", "swa_decode_step",
+           "based_num_features", "based_prefill_workspace_bytes", "BasedError", "library_path"]
 
 BasedError = _lib.BasedError
 library_path = _lib.LIB_PATH
@@ -149,3 +151,67 @@ def swa_forward(q, k, v, *, window: int = 64, scale: float | None = None, add=No
                                 y.data_ptr(), _stream_ptr(q.device))
     _lib.check("swa_forward", st)
     return y
+
+
+def swa_cache_fill(k, v, *, window: int = 64, k_cache=None, v_cache=None):
+    """The window's key/value ring after a prefix k [B,H,L,d_qk], v [B,H,L,d_v]:
+    the token at position p in slot p mod window (the last min(L, window)
+    tokens are written, other slots are left as they are).  Returns
+    (k_cache, v_cache), [B,H,window,d] in the inputs' dtype."""
+    _check_tensor("k", k, ndim=4)
+    dt = k.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor("v", v, dt, 4)
+    B, H, L, d_qk = k.shape
+    d_v = v.shape[-1]
+    if k_cache is None:
+        k_cache = torch.zeros((B, H, window, d_qk), dtype=dt, device=k.device)
+    if v_cache is None:
+        v_cache = torch.zeros((B, H, window, d_v), dtype=dt, device=k.device)
+    _check_tensor("k_cache", k_cache, dt, 4)
+    _check_tensor("v_cache", v_cache, dt, 4)
+    if tuple(k_cache.shape) != (B, H, window, d_qk) or tuple(v_cache.shape) != (B, H, window, d_v):
+        raise ValueError("cache shapes must be [B,H,window,d]")
+    st = _lib.lib().swa_cache_fill(k.data_ptr(), v.data_ptr(), _DTYPES[dt], B, H, L, d_qk, d_v, int(window),
+                                   k_cache.data_ptr(), v_cache.data_ptr(), _stream_ptr(k.device))
+    _lib.check("swa_cache_fill", st)
+    return k_cache, v_cache
+
+
+def swa_decode_step(q, k, v, k_cache, v_cache, pos, *, scale: float | None = None, add=None, y=None):
+    """Next-token step of the window for the tokens at positions pos [B]
+    (int64 device tensor, not modified): q,k [B,H,d_qk], v [B,H,d_v] enter
+    their slot of the caches [B,H,window,*] (updated in place), and
+    y [B,H,d_v] fp32 is the softmax attention over the last `window` tokens
+    (+ ``add``, which may be ``y``).  window = k_cache.shape[2]."""
+    _check_tensor("q", q, ndim=3)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor("k", k, dt, 3)
+    _check_tensor("v", v, dt, 3)
+    _check_tensor("k_cache", k_cache, dt, 4)
+    _check_tensor("v_cache", v_cache, dt, 4)
+    _check_tensor("pos", pos, torch.int64, 1)
+    B, H, d_qk = q.shape
+    d_v = v.shape[-1]
+    window = k_cache.shape[2]
+    if k.shape != q.shape or v.shape[:2] != (B, H) or pos.shape[0] != B:
+        raise ValueError("shape mismatch")
+    if tuple(k_cache.shape) != (B, H, window, d_qk) or tuple(v_cache.shape) != (B, H, window, d_v):
+        raise ValueError("cache shapes must be [B,H,window,d]")
+    if scale is None:
+        scale = d_qk ** -0.5
+    if y is None:
+        y = torch.empty((B, H, d_v), dtype=torch.float32, device=q.device)
+    _check_tensor("y", y, torch.float32)
+    if add is not None:
+        _check_tensor("add", add, torch.float32)
+    st = _lib.lib().swa_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[dt], B, H, d_qk, d_v,
+                                    int(window), float(scale), pos.data_ptr(), k_cache.data_ptr(),
+                                    v_cache.data_ptr(), None if add is None else add.data_ptr(), y.data_ptr(),
+                                    _stream_ptr(q.device))
+    _lib.check("swa_decode_step", st)
+    return y
+

@@ -26,6 +26,8 @@ SIGNATURES = {
     "based_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P, _S, _P]),
     "based_decode_step": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P]),
     "swa_forward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
+    "swa_cache_fill": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "swa_decode_step": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None

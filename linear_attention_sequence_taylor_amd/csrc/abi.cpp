@@ -165,3 +165,70 @@ BASED_API based_status_t swa_forward(const void* q, const void* k, const void* v
     return launch_status(
         based::launch_swa_valu(q, k, v, bf16, (int)BH, L, d_qk, window, scale, add, y, st));
 }
+
+namespace {
+
+// Shared checks of the window cache entry points.
+based_status_t check_window_cache(based_dtype_t dtype, int d_qk, int d_v, int window) {
+    if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_E_INVALID;
+    if (window < 1 || d_qk < 1 || d_v < 1) return BASED_E_INVALID;
+    if (d_qk != 16 && d_qk != 64) return BASED_E_UNSUPPORTED;
+    if ((d_v != 64 && d_v != 128) || window > 64) return BASED_E_UNSUPPORTED;
+    return BASED_OK;
+}
+
+}  // namespace
+
+BASED_API based_status_t swa_cache_fill(const void* k, const void* v, based_dtype_t dtype, int B, int H, int L,
+                                        int d_qk, int d_v, int window, void* k_cache, void* v_cache,
+                                        void* stream) {
+    if (!k || !v || !k_cache || !v_cache) return BASED_E_INVALID;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return BASED_E_INVALID;
+    const based_status_t c = check_window_cache(dtype, d_qk, d_v, window);
+    if (c != BASED_OK) return c;
+    uint64_t BH, BHL;
+    if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
+    const uint64_t es = elem_size(dtype);
+    const uint64_t kc_bytes = BH * window * d_qk * es, vc_bytes = BH * window * d_v * es;
+    const uint64_t k_bytes = BHL * d_qk * es, v_bytes = BHL * d_v * es;
+    if (overlaps(k_cache, kc_bytes, v_cache, vc_bytes) || overlaps(k_cache, kc_bytes, k, k_bytes) ||
+        overlaps(k_cache, kc_bytes, v, v_bytes) || overlaps(v_cache, vc_bytes, k, k_bytes) ||
+        overlaps(v_cache, vc_bytes, v, v_bytes))
+        return BASED_E_INVALID;
+    return launch_status(based::launch_swa_cache_fill(k, v, dtype == BASED_BF16, (int)BH, L, d_qk, d_v, window,
+                                                      k_cache, v_cache, static_cast<hipStream_t>(stream)));
+}
+
+BASED_API based_status_t swa_decode_step(const void* q, const void* k, const void* v, based_dtype_t dtype, int B,
+                                         int H, int d_qk, int d_v, int window, float scale, const long long* pos,
+                                         void* k_cache, void* v_cache, const float* add, float* y,
+                                         void* stream) {
+    if (!q || !k || !v || !pos || !k_cache || !v_cache || !y) return BASED_E_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(y) || (add && !aligned16(add)) || (reinterpret_cast<uintptr_t>(pos) & 7u) != 0)
+        return BASED_E_INVALID;
+    if (!isfinite(scale)) return BASED_E_INVALID;
+    const based_status_t c = check_window_cache(dtype, d_qk, d_v, window);
+    if (c != BASED_OK) return c;
+    uint64_t BH, BHL;
+    if (check_dims(B, H, 1, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
+    const uint64_t es = elem_size(dtype);
+    const uint64_t kc_bytes = BH * window * d_qk * es, vc_bytes = BH * window * d_v * es;
+    const uint64_t qk_bytes = BH * d_qk * es, v_bytes = BH * d_v * es, y_bytes = BH * d_v * 4;
+    const uint64_t pos_bytes = (uint64_t)B * 8;
+    const void* outs[3] = {k_cache, v_cache, y};
+    const uint64_t out_bytes[3] = {kc_bytes, vc_bytes, y_bytes};
+    const void* ins[4] = {q, k, v, pos};
+    const uint64_t in_bytes[4] = {qk_bytes, qk_bytes, v_bytes, pos_bytes};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return BASED_E_INVALID;
+        for (int b = 0; b < 4; ++b)
+            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return BASED_E_INVALID;
+    }
+    if (add && add != y && overlaps(add, y_bytes, y, y_bytes)) return BASED_E_INVALID;
+    return launch_status(based::launch_swa_decode_step(q, k, v, dtype == BASED_BF16, pos, H, (int)BH, d_qk, d_v,
+                                                       window, scale, k_cache, v_cache, add, y,
+                                                       static_cast<hipStream_t>(stream)));
+}
+

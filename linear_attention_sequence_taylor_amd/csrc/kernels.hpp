@@ -34,4 +34,13 @@ hipError_t launch_swa_valu(const void* q, const void* k, const void* v, bool bf1
 hipError_t launch_swa_mfma(const void* q, const void* k, const void* v, int BH, int L, int dqk,
                            int window, float scale, const float* add, float* y, hipStream_t st);
 
+// Next-token step of the sliding window on its key/value ring cache, and the
+// fill of that cache from a prefix (swa_decode.hip).  dqk in {16, 64}, dv in
+// {64, 128}, window <= 64; pos is a device array [B].
+hipError_t launch_swa_decode_step(const void* q, const void* k, const void* v, bool bf16, const long long* pos,
+                                  int H, int BH, int dqk, int dv, int window, float scale, void* kc, void* vc,
+                                  const float* add, float* y, hipStream_t st);
+hipError_t launch_swa_cache_fill(const void* k, const void* v, bool bf16, int BH, int L, int dqk, int dv,
+                                 int window, void* kc, void* vc, hipStream_t st);
+
 }  // namespace based

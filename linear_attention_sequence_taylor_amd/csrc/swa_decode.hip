@@ -1,0 +1,248 @@
+// swa_decode.hip -- next-token step of the causal sliding window and the fill
+// of its key/value ring cache (gfx950).
+//
+// "Simple linear attention language models balance the recall-throughput
+// tradeoff", s4 "Local Exact Attention" (each query sees the preceding w
+// keys, its own included, through a w-sized key/value cache) and App. B
+// "Next Token Prediction" (the window's next-token kernel).
+//
+// Cache layout: per (batch, head) a ring of `window` slots, [B,H,window,d];
+// the token at position p lives in slot p mod window.
+//
+// Decode step: HBM-bound (each cached key and value is read once per step).
+// One wave per (batch, head), four per workgroup, no workgroup barrier.
+// Lane j scores slot j from its key row (16-byte loads); for P.V, lane
+// (key group kg, column group cg) accumulates 8 columns over the keys kg,
+// kg + KG, ... and the key groups are summed with lane shuffles.  Key and
+// value loads are all issued before any arithmetic, so a wave waits for
+// memory once.  The new token's key and value are taken from the inputs (and
+// written to their slot), so no lane reads a slot that the step overwrites.
+// Slots that do not hold one of the last `window` tokens are never read.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace based {
+namespace {
+
+constexpr int kMaxWindow = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 8 consecutive elements of a row: 16 bytes of bf16 or 32 of fp32, kept in
+// their loaded form until used.
+template <typename T>
+struct Chunk8;
+template <>
+struct Chunk8<uint16_t> {
+    u32x4 u;
+    __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void zero() { u = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ float get(int i) const {
+        return (i & 1) ? bf16hi_f32(u[i >> 1]) : bf16lo_f32(u[i >> 1]);
+    }
+};
+template <>
+struct Chunk8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const f32x4*>(p);
+        b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ void zero() { a = b = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ __forceinline__ float get(int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+// Copies n 16-byte units from src to dst, one unit per lane.
+__device__ __forceinline__ void copy_units(const void* src, void* dst, int n, int lane) {
+    if (lane < n) reinterpret_cast<u32x4*>(dst)[lane] = reinterpret_cast<const u32x4*>(src)[lane];
+}
+
+template <typename T, int DQK, int DV>
+__global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                         const T* __restrict__ v,
+                                                         const long long* __restrict__ pos, int H, int BH,
+                                                         int window, float scale, T* __restrict__ kc,
+                                                         T* __restrict__ vc, const float* add,
+                                                         float* __restrict__ y) {
+    constexpr int kQC = DQK / 8;               // chunks of 8 in a key row
+    constexpr int kCG = DV / 8;                // column groups of 8
+    constexpr int kKG = 64 / kCG;              // key groups in P.V
+    constexpr int kKPL = kMaxWindow / kKG;     // keys per lane in P.V
+    constexpr int kKU = DQK * sizeof(T) / 16;  // 16-byte units of a key row
+    constexpr int kVU = DV * sizeof(T) / 16;   // and of a value row
+    const int lane = threadIdx.x & 63;
+    const int head = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (head >= BH) return;
+    const int cg = lane % kCG, kg = lane / kCG;
+    float* yh = y + (size_t)head * DV;
+    const long long p = pos[head / H];
+    if (p < 0) {  // no valid position: NaN outputs, cache untouched
+        if (kg == 0) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) yh[8 * cg + c] = __builtin_nanf("");
+        }
+        return;
+    }
+    const int slot_new = (int)(p % window);
+    const int nvalid = p + 1 < window ? (int)p + 1 : window;  // slots 0..nvalid-1 hold the last tokens
+    const T* kn = k + (size_t)head * DQK;
+    const T* vn = v + (size_t)head * DV;
+    T* kch = kc + (size_t)head * window * DQK;
+    T* vch = vc + (size_t)head * window * DV;
+
+    // ---- loads: the query, the key of slot `lane`, this lane's value chunks
+    Chunk8<T> qr[kQC], kr[kQC], vr[kKPL];
+    const bool kvalid = lane < nvalid;
+    const T* krow = lane == slot_new ? kn : kch + (size_t)lane * DQK;
+#pragma unroll
+    for (int c = 0; c < kQC; ++c) {
+        qr[c].load(q + (size_t)head * DQK + 8 * c);
+        if (kvalid) kr[c].load(krow + 8 * c);
+        else kr[c].zero();
+    }
+#pragma unroll
+    for (int i = 0; i < kKPL; ++i) {
+        const int j = kg + kKG * i;
+        const T* vrow = j == slot_new ? vn : vch + (size_t)j * DV;
+        if (j < nvalid) vr[i].load(vrow + 8 * cg);
+        else vr[i].zero();
+    }
+    float ad[8];
+    if (add && kg == 0) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(add + (size_t)head * DV + 8 * cg);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(add + (size_t)head * DV + 8 * cg + 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            ad[c] = a0[c];
+            ad[4 + c] = a1[c];
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) ad[c] = 0.f;
+    }
+
+    // ---- scores and softmax over the valid slots (fp32, base 2)
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < kQC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = fmaf(qr[c].get(e), kr[c].get(e), dot);
+    const float s = kvalid ? dot * (scale * kLog2e) : -INFINITY;
+    const float m = wave_max(s);
+    const float pe = kvalid ? __builtin_amdgcn_exp2f(s - m) : 0.f;
+    const float l = wave_sum(pe);
+
+    // ---- P.V: this lane's keys, then the sum over key groups
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kKPL; ++i) {
+        const float pj = __shfl(pe, kg + kKG * i, 64);  // 0 for slots that are not valid
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = fmaf(pj, vr[i].get(c), acc[c]);
+    }
+#pragma unroll
+    for (int off = kCG; off < 64; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
+    if (kg == 0) {
+        const float inv = 1.f / l;  // l >= 1: the maximum key has weight 1
+        f32x4 o0, o1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            o0[c] = fmaf(acc[c], inv, ad[c]);
+            o1[c] = fmaf(acc[4 + c], inv, ad[4 + c]);
+        }
+        *reinterpret_cast<f32x4*>(yh + 8 * cg) = o0;
+        *reinterpret_cast<f32x4*>(yh + 8 * cg + 4) = o1;
+    }
+
+    // ---- the new token into its slot (no lane of this step reads that slot)
+    copy_units(kn, kch + (size_t)slot_new * DQK, kKU, lane);
+    copy_units(vn, vch + (size_t)slot_new * DV, kVU, lane);
+}
+
+// The slots of the last min(L, window) tokens of a prefix, one workgroup per
+// (batch, head).
+template <typename T, int DQK, int DV>
+__global__ __launch_bounds__(256) void swa_cache_fill_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                             int L, int window, T* __restrict__ kc,
+                                                             T* __restrict__ vc) {
+    constexpr int kKU = DQK * sizeof(T) / 16, kVU = DV * sizeof(T) / 16;
+    const size_t head = blockIdx.x;
+    const int n = L < window ? L : window, p0 = L - n;
+    for (int e = threadIdx.x; e < n * (kKU + kVU); e += 256) {
+        const int r = e / (kKU + kVU), u = e % (kKU + kVU);
+        const int p = p0 + r, slot = p % window;
+        if (u < kKU) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(k + (head * L + p) * DQK);
+            reinterpret_cast<u32x4*>(kc + (head * window + slot) * DQK)[u] = src[u];
+        } else {
+            const u32x4* src = reinterpret_cast<const u32x4*>(v + (head * L + p) * DV);
+            reinterpret_cast<u32x4*>(vc + (head * window + slot) * DV)[u - kKU] = src[u - kKU];
+        }
+    }
+}
+
+template <typename T, int DQK>
+hipError_t decode_dv(const void* q, const void* k, const void* v, const long long* pos, int H, int BH, int dv,
+                     int window, float scale, void* kc, void* vc, const float* add, float* y, hipStream_t st) {
+    const dim3 grid((BH + 3) / 4);
+    const T* qq = static_cast<const T*>(q);
+    const T* kk = static_cast<const T*>(k);
+    const T* vv = static_cast<const T*>(v);
+    T* kcc = static_cast<T*>(kc);
+    T* vcc = static_cast<T*>(vc);
+    if (dv == 64)
+        hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 64>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH, window,
+                           scale, kcc, vcc, add, y);
+    else
+        hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 128>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH, window,
+                           scale, kcc, vcc, add, y);
+    return hipGetLastError();
+}
+
+template <typename T, int DQK>
+hipError_t fill_dv(const void* k, const void* v, int BH, int L, int dv, int window, void* kc, void* vc,
+                   hipStream_t st) {
+    const T* kk = static_cast<const T*>(k);
+    const T* vv = static_cast<const T*>(v);
+    T* kcc = static_cast<T*>(kc);
+    T* vcc = static_cast<T*>(vc);
+    if (dv == 64)
+        hipLaunchKernelGGL((swa_cache_fill_kernel<T, DQK, 64>), dim3(BH), dim3(256), 0, st, kk, vv, L, window, kcc,
+                           vcc);
+    else
+        hipLaunchKernelGGL((swa_cache_fill_kernel<T, DQK, 128>), dim3(BH), dim3(256), 0, st, kk, vv, L, window, kcc,
+                           vcc);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_swa_decode_step(const void* q, const void* k, const void* v, bool bf16, const long long* pos,
+                                  int H, int BH, int dqk, int dv, int window, float scale, void* kc, void* vc,
+                                  const float* add, float* y, hipStream_t st) {
+    if (bf16)
+        return dqk == 16 ? decode_dv<uint16_t, 16>(q, k, v, pos, H, BH, dv, window, scale, kc, vc, add, y, st)
+                         : decode_dv<uint16_t, 64>(q, k, v, pos, H, BH, dv, window, scale, kc, vc, add, y, st);
+    return dqk == 16 ? decode_dv<float, 16>(q, k, v, pos, H, BH, dv, window, scale, kc, vc, add, y, st)
+                     : decode_dv<float, 64>(q, k, v, pos, H, BH, dv, window, scale, kc, vc, add, y, st);
+}
+
+hipError_t launch_swa_cache_fill(const void* k, const void* v, bool bf16, int BH, int L, int dqk, int dv,
+                                 int window, void* kc, void* vc, hipStream_t st) {
+    if (bf16)
+        return dqk == 16 ? fill_dv<uint16_t, 16>(k, v, BH, L, dv, window, kc, vc, st)
+                         : fill_dv<uint16_t, 64>(k, v, BH, L, dv, window, kc, vc, st);
+    return dqk == 16 ? fill_dv<float, 16>(k, v, BH, L, dv, window, kc, vc, st)
+                     : fill_dv<float, 64>(k, v, BH, L, dv, window, kc, vc, st);
+}
+
+}  // namespace based

@@ -12,7 +12,8 @@ Recipe (one torch CPU generator per tensor):
     0 = q, 1 = k, 2 = v (linear-attention branch), 3 = q, 4 = k (window
     branch when it has its own q, k).
   * Decode step ``t`` draws q, k, v in that order from one generator seeded
-    ``100000 + t``.
+    ``100000 + t``; a window decode step ``t`` draws its q, k (window dim)
+    and v from one generator seeded ``200000 + t``.
   * The long-sequence workload multiplies raw k by ``outlier_scale`` at
     0-based positions ``p % outlier_every == outlier_every - 1`` before the
     bf16 rounding (exact in bf16 for a power of two).
@@ -24,6 +25,7 @@ import dataclasses
 import torch
 
 DECODE_SEED_BASE = 100000
+WINDOW_DECODE_SEED_BASE = 200000
 
 
 @dataclasses.dataclass(frozen=True)
@@ -78,6 +80,11 @@ WORKLOADS = {
         "long_64k", 5, "bf16", B=1, H=16, L=65536, dv=64, scale=0.5, outlier_every=4096,
         outlier_scale=4.0,
         description="long-sequence chunked prefill with k outlier rows every 4096th position"),
+    "window_decode_1p3b": Workload(
+        "window_decode_1p3b", 6, "bf16", B=128, H=16, L=104, dv=128, scale=1.0, window=64, d_qk=64,
+        swa_scale=1.0 / 8.0, decode_steps=1024,
+        description="BASED-1.3B-shaped window next-token steps: w=64 ring filled from a 104-token "
+                    "prefix, then 1024 steps"),
 }
 
 
@@ -134,6 +141,18 @@ def decode_inputs(wl: Workload, t: int, B: int | None = None, H: int | None = No
     g = torch.Generator("cpu").manual_seed(DECODE_SEED_BASE + int(t))
     q = torch.randn((B, H, wl.d), generator=g) * wl.scale
     k = torch.randn((B, H, wl.d), generator=g) * wl.scale
+    v = torch.randn((B, H, wl.dv), generator=g) * wl.scale
+    dt = wl.torch_dtype
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
+def window_decode_inputs(wl: Workload, t: int, B: int | None = None, H: int | None = None):
+    """(q, k, v) of window next-token step t: q,k [B,H,d_qk], v [B,H,dv]."""
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    g = torch.Generator("cpu").manual_seed(WINDOW_DECODE_SEED_BASE + int(t))
+    q = torch.randn((B, H, wl.d_qk), generator=g) * wl.scale
+    k = torch.randn((B, H, wl.d_qk), generator=g) * wl.scale
     v = torch.randn((B, H, wl.dv), generator=g) * wl.scale
     dt = wl.torch_dtype
     return q.to(dt), k.to(dt), v.to(dt)

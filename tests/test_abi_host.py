@@ -39,8 +39,8 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
-    for want in ("based_prefill", "based_decode_step", "swa_forward", "based_num_features",
-                 "based_prefill_workspace_bytes", "based_status_string"):
+    for want in ("based_prefill", "based_decode_step", "swa_forward", "swa_cache_fill", "swa_decode_step",
+                 "based_num_features", "based_prefill_workspace_bytes", "based_status_string"):
         assert want in names, names
 
 
@@ -130,6 +130,40 @@ def _swa(lib, **kw):
 ])
 def test_swa_rejects(lib, kw, want):
     assert _swa(lib, **kw) == want
+
+
+def _swa_dec(lib, **kw):
+    a = dict(q=A, k=B_, v=C, dtype=1, B=2, H=3, dqk=64, dv=64, window=64, scale=0.125, pos=S, kc=Y, vc=Z,
+             add=None, y=S + (1 << 20), stream=None)
+    a.update(kw)
+    return lib.swa_decode_step(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["H"], a["dqk"], a["dv"],
+                               a["window"], a["scale"], a["pos"], a["kc"], a["vc"], a["add"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), 1), (dict(pos=None), 1), (dict(kc=None), 1), (dict(y=None), 1), (dict(pos=S + 4), 1),
+    (dict(kc=Y + 8), 1), (dict(dtype=3), 1), (dict(B=0), 1), (dict(window=0), 1), (dict(scale=float("inf")), 1),
+    (dict(dqk=32), 2), (dict(dv=96), 2), (dict(window=65), 2), (dict(vc=Y + 64), 1), (dict(y=Y), 1),
+    (dict(kc=A), 1), (dict(y=S), 1), (dict(add=S + (1 << 20) + 16), 1),
+])
+def test_swa_decode_rejects(lib, kw, want):
+    assert _swa_dec(lib, **kw) == want
+
+
+def _swa_fill(lib, **kw):
+    a = dict(k=A, v=B_, dtype=1, B=1, H=2, L=100, dqk=64, dv=64, window=64, kc=Y, vc=Z, stream=None)
+    a.update(kw)
+    return lib.swa_cache_fill(a["k"], a["v"], a["dtype"], a["B"], a["H"], a["L"], a["dqk"], a["dv"], a["window"],
+                              a["kc"], a["vc"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(k=None), 1), (dict(vc=None), 1), (dict(kc=Y + 2), 1), (dict(L=0), 1), (dict(window=0), 1),
+    (dict(dqk=8), 2), (dict(dv=32), 2), (dict(window=100), 2), (dict(vc=Y + 64), 1), (dict(kc=A), 1),
+    (dict(L=2**31 - 1), 1),
+])
+def test_swa_fill_rejects(lib, kw, want):
+    assert _swa_fill(lib, **kw) == want
 
 
 def test_product_never_imports_oracle():

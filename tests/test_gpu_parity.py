@@ -320,6 +320,105 @@ def test_swa_longest_heads(L):
     report(f"swa longest head L={L} ({len(rows)} sampled queries)", ratio(got, want), 2e-2)
 
 
+# ---------------------------------------------------------------- window decode
+def _nan_cache(B, H, window, d, dtype):
+    return torch.full((B, H, window, d), float("nan"), dtype=dtype, device=DEV)
+
+
+@pytest.mark.parametrize("dtype,dqk,dv,window,L", [
+    (torch.bfloat16, 64, 64, 64, 100), (torch.bfloat16, 16, 128, 64, 10), (torch.bfloat16, 64, 128, 7, 30),
+    (torch.bfloat16, 64, 64, 64, 0), (torch.float32, 64, 64, 64, 64), (torch.float32, 16, 128, 1, 5),
+    (torch.float32, 64, 128, 33, 200),
+])
+def test_swa_decode_continues_window(dtype, dqk, dv, window, L):
+    """Ring filled from a prefix (two sequences, prefixes L and L + 5; none
+    for L = 0, which starts decoding at position 0 on an empty ring), then
+    2*window + 3 next-token steps.  Every step's output is compared with the
+    oracle's brute-force window attention over the whole sequence at that
+    position; the caches start as NaN, so reading a slot that does not hold
+    one of the last `window` tokens would show.  The final caches must hold
+    exactly the oracle's ring."""
+    based = based_mod()
+    tol = 2e-2 if dtype == torch.bfloat16 else 1e-4
+    B, H, lag = 2, 3, 5
+    T = 2 * window + 3
+    n = L + lag + T
+    q, k, v = si.custom((B, H, n, dqk), (B, H, n, dv), seed=1600 + dqk + dv + window + L, scale=1.0, dtype=dtype)
+    qd, kd, vd = dev(q, k, v)
+    scale = dqk ** -0.5
+    full = oracle.swa(q, k, v, window, scale)
+    kc, vc = _nan_cache(B, H, window, dqk, dtype), _nan_cache(B, H, window, dv, dtype)
+    okc = np.full((B, H, window, dqk), np.nan)
+    ovc = np.full((B, H, window, dv), np.nan)
+    starts = [L, L + lag]
+    for b, L0 in enumerate(starts):
+        if L0 > 0:
+            based.swa_cache_fill(kd[b:b + 1, :, :L0].contiguous(), vd[b:b + 1, :, :L0].contiguous(),
+                                 window=window, k_cache=kc[b:b + 1], v_cache=vc[b:b + 1])
+            okc[b], ovc[b] = oracle.swa_cache_fill(k[b:b + 1, :, :L0], v[b:b + 1, :, :L0], window,
+                                                   okc[b:b + 1], ovc[b:b + 1])
+    got, want = [], []
+    for t in range(T):
+        p = [L0 + t for L0 in starts]
+        pick = lambda x: torch.stack([x[b, :, p[b]] for b in range(B)]).contiguous()
+        pos = torch.tensor(p, dtype=torch.int64, device=DEV)
+        got.append(based.swa_decode_step(pick(qd), pick(kd), pick(vd), kc, vc, pos, scale=scale).cpu())
+        want.append(np.stack([full[b, :, p[b]] for b in range(B)]))
+        _, okc, ovc = oracle.swa_decode_step(pick(q), pick(k), pick(v), okc, ovc, p, window, scale)
+    report(f"swa decode {dtype} dqk={dqk} dv={dv} w={window} L={L} ({T} steps)",
+           ratio(torch.stack(got), np.stack(want)), tol)
+    np.testing.assert_array_equal(kc.double().cpu().numpy(), okc)
+    np.testing.assert_array_equal(vc.double().cpu().numpy(), ovc)
+
+
+def test_swa_decode_add_and_invalid_position():
+    """add (fused sum, in place on y); a negative position gives NaN outputs
+    for its sequence and leaves that sequence's cache untouched."""
+    based = based_mod()
+    B, H, window = 2, 2, 64
+    q, k, v = si.custom((B, H, 64), (B, H, 64), seed=1700)
+    kp, vp = si.custom((B, H, 80, 64), (B, H, 80, 64), seed=1701)[1:]
+    kc, vc = based.swa_cache_fill(*dev(kp, vp), window=window)
+    kc0, vc0 = kc.clone(), vc.clone()
+    base = torch.randn(B, H, 64, generator=torch.Generator().manual_seed(7)).to(DEV)
+    pos = torch.tensor([80, -1], dtype=torch.int64, device=DEV)
+    y_plain = based.swa_decode_step(*dev(q, k, v), kc0, vc0, pos)
+    y = base.clone()
+    based.swa_decode_step(*dev(q, k, v), kc, vc, pos, add=y, y=y)
+    assert torch.allclose(y[0], y_plain[0] + base[0], rtol=0, atol=1e-6)
+    assert torch.isnan(y[1]).all() and torch.isnan(y_plain[1]).all()
+    assert torch.equal(kc[1], kc0[1]) and torch.equal(vc[1], vc0[1])
+    okc, ovc = oracle.swa_cache_fill(kp[:1], vp[:1], window)
+    yo, _, _ = oracle.swa_decode_step(q[:1], k[:1], v[:1], okc, ovc, [80], window, 0.125)
+    report("swa decode add (valid sequence)", ratio(y_plain[:1], yo), 2e-2)
+
+
+def test_workload_window_decode_1p3b():
+    """B=128, H=16, w=64 ring filled from a 104-token prefix, then 64 next-token
+    steps; every step on 8 sampled heads is compared with the oracle's steps."""
+    based = based_mod()
+    wl = si.WORKLOADS["window_decode_1p3b"]
+    _, k = si.window_inputs(wl)
+    v = si.linear_inputs(wl)[2]
+    kd, vd = dev(k, v)
+    kc, vc = based.swa_cache_fill(kd, vd, window=wl.window)
+    heads = _sample_heads(wl.B, wl.H, 8, 4)
+    bi = [b for b, _ in heads]
+    hi = [h for _, h in heads]
+    okc, ovc = oracle.swa_cache_fill(k[bi, hi][None], v[bi, hi][None], wl.window)
+    pos = torch.full((wl.B,), wl.L, dtype=torch.int64, device=DEV)
+    got, want = [], []
+    for t in range(64):
+        q1, k1, v1 = si.window_decode_inputs(wl, t)
+        y = based.swa_decode_step(*dev(q1, k1, v1), kc, vc, pos, scale=wl.swa_scale)
+        pos += 1
+        got.append(y[bi, hi].cpu())
+        yo, okc, ovc = oracle.swa_decode_step(q1[bi, hi][None], k1[bi, hi][None], v1[bi, hi][None], okc, ovc,
+                                              [wl.L + t], wl.window, wl.swa_scale)
+        want.append(yo[0])
+    report("window_decode_1p3b (8 sampled heads, 64 steps)", ratio(torch.stack(got), np.stack(want)), wl.tol)
+
+
 # ---------------------------------------------------------------- workloads
 def test_workload_tiny_f32_layer():
     """B=1,H=1,L=256 fp32: Taylor linear attention + w=64 window, summed."""
