@@ -20,8 +20,8 @@ prints one JSON line with:
 * cpu_baseline: the fp64 oracle (recurrent form) timed on the host cores on
   a sample of whole heads of the same workload;
 * extra: the next-token step (1.3B-shaped decode, 1024 steps), the w=64
-  window kernel with fused add, and the 64K-token prefill, each with its
-  own HBM roofline fraction.
+  window kernel with fused add, the window's next-token step on its ring
+  cache, and the 64K-token prefill, each with its own HBM roofline fraction.
 """
 from __future__ import annotations
 
@@ -74,6 +74,15 @@ def swa_bytes(wl) -> int:
     es = 2
     per_tok = 2 * wl.d_qk * es + wl.dv * es + 2 * wl.dv * 4
     return wl.B * wl.H * wl.L * per_tok
+
+
+def window_decode_bytes(wl) -> int:
+    """Per tok-head: the window-1 cached key/value rows read, the new row
+    written to its slot, q,k,v read, the fused-add input read and y written."""
+    es = 2
+    row = (wl.d_qk + wl.dv) * es
+    per_head = (wl.window - 1) * row + row + (2 * wl.d_qk + wl.dv) * es + 2 * wl.dv * 4
+    return wl.B * wl.H * per_head
 
 
 # ---------------------------------------------------------------- helpers
@@ -232,6 +241,48 @@ def bench_swa(based, wl, reps):
     return timer.seconds() / reps
 
 
+def bench_window_decode(based, wl, n_steps, graph_steps=64, n_sets=16):
+    """Window next-token steps (fused add of a fixed fp32 tensor standing in
+    for the linear-attention output), captured as a HIP graph of 64 steps and
+    replayed; the steps cycle over 16 filled cache sets (805 MB) so that every
+    step reads its ring from HBM, not from the 256 MB Infinity Cache.
+    Returns event seconds per step over the timed replays."""
+    _, k = si.window_inputs(wl)
+    v = si.linear_inputs(wl)[2]
+    kd, vd = k.cuda(), v.cuda()
+    caches = [based.swa_cache_fill(kd, vd, window=wl.window) for _ in range(n_sets)]
+    del kd, vd, k, v
+    steps = [tuple(t.cuda() for t in si.window_decode_inputs(wl, t)) for t in range(graph_steps)]
+    pos = [torch.full((wl.B,), wl.L + t, dtype=torch.int64, device="cuda") for t in range(graph_steps)]
+    add = torch.randn(wl.B, wl.H, wl.dv, device="cuda")
+    y = torch.empty_like(add)
+
+    def run_all():
+        for t in range(graph_steps):
+            kc, vc = caches[t % n_sets]
+            based.swa_decode_step(*steps[t], kc, vc, pos[t], scale=wl.swa_scale, add=add, y=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    for _ in range(100):  # untimed warm-up, ~50 ms
+        g.replay()
+    reps = max(1, n_steps // graph_steps)
+    timer = RegionTimer()
+    torch.cuda.synchronize()
+    timer.start()
+    for _ in range(reps):
+        g.replay()
+    timer.stop()
+    return timer.seconds() / (reps * graph_steps)
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """Oracle recurrent form on whole heads of the workload, sized to about
     budget_s of host time (at most the full workload)."""
@@ -266,6 +317,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip decode/window/64K legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--window-decode-steps", type=int, default=4096)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to calibrate "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE against known bytes")
@@ -349,6 +401,16 @@ def main():
                                   "hbm_GBps": sb / skern / 1e9, "hbm_frac": sb / skern / HBM_PEAK,
                                   "algorithmic_bytes": sb}
         print(f"[bench] swa: {skern*1e6:.1f} us, {sb/skern/1e9:.0f} GB/s", file=sys.stderr, flush=True)
+        wwd = si.WORKLOADS["window_decode_1p3b"]
+        wkern = bench_window_decode(based, wwd, args.window_decode_steps)
+        wb = window_decode_bytes(wwd)
+        extra["window_decode_1p3b"] = {
+            "tokens_per_s": wwd.B / wkern, "kernel_us": wkern * 1e6, "hbm_GBps": wb / wkern / 1e9,
+            "hbm_frac": wb / wkern / HBM_PEAK, "algorithmic_bytes": wb, "steps": args.window_decode_steps,
+            "note": "w=64 ring, B=128, H=16, d_qk=64, d_v=128, fused add; HIP graph of 64 steps "
+                    "replayed, 16 cache sets"}
+        print(f"[bench] window decode: {wkern*1e6:.1f} us/step, {wb/wkern/1e9:.0f} GB/s", file=sys.stderr,
+              flush=True)
         if wl.name != "long_64k":
             wlong = si.WORKLOADS["long_64k"]
             lstep, lkern, _ = bench_prefill(based, wlong, 50, 100)

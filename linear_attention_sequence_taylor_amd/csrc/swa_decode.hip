@@ -16,8 +16,10 @@
 // kg + KG, ... and the key groups are summed with lane shuffles.  Key and
 // value loads are all issued before any arithmetic, so a wave waits for
 // memory once.  The new token's key and value are taken from the inputs (and
-// written to their slot), so no lane reads a slot that the step overwrites.
-// Slots that do not hold one of the last `window` tokens are never read.
+// written to their slot).
+// Loads do not wait for the position: every slot of the ring is loaded at
+// once and slots that do not hold one of the last `window` tokens are then
+// replaced by zeros or -inf through selects.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -80,36 +82,28 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
     if (head >= BH) return;
     const int cg = lane % kCG, kg = lane / kCG;
     float* yh = y + (size_t)head * DV;
-    const long long p = pos[head / H];
-    if (p < 0) {  // no valid position: NaN outputs, cache untouched
-        if (kg == 0) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) yh[8 * cg + c] = __builtin_nanf("");
-        }
-        return;
-    }
-    const int slot_new = (int)(p % window);
-    const int nvalid = p + 1 < window ? (int)p + 1 : window;  // slots 0..nvalid-1 hold the last tokens
     const T* kn = k + (size_t)head * DQK;
     const T* vn = v + (size_t)head * DV;
     T* kch = kc + (size_t)head * window * DQK;
     T* vch = vc + (size_t)head * window * DV;
 
-    // ---- loads: the query, the key of slot `lane`, this lane's value chunks
-    Chunk8<T> qr[kQC], kr[kQC], vr[kKPL];
-    const bool kvalid = lane < nvalid;
-    const T* krow = lane == slot_new ? kn : kch + (size_t)lane * DQK;
+    // ---- loads, all issued before the position is known: the query, the
+    // new key and value, the key of slot `lane` and this lane's value chunks
+    // of every slot (the slot addresses do not depend on the position).
+    const long long p = pos[head / H];
+    Chunk8<T> qr[kQC], kr[kQC], knr[kQC], vr[kKPL], vnr;
 #pragma unroll
     for (int c = 0; c < kQC; ++c) {
         qr[c].load(q + (size_t)head * DQK + 8 * c);
-        if (kvalid) kr[c].load(krow + 8 * c);
+        knr[c].load(kn + 8 * c);
+        if (lane < window) kr[c].load(kch + (size_t)lane * DQK + 8 * c);
         else kr[c].zero();
     }
+    vnr.load(vn + 8 * cg);
 #pragma unroll
     for (int i = 0; i < kKPL; ++i) {
         const int j = kg + kKG * i;
-        const T* vrow = j == slot_new ? vn : vch + (size_t)j * DV;
-        if (j < nvalid) vr[i].load(vrow + 8 * cg);
+        if (j < window) vr[i].load(vch + (size_t)j * DV + 8 * cg);
         else vr[i].zero();
     }
     float ad[8];
@@ -124,6 +118,28 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
     } else {
 #pragma unroll
         for (int c = 0; c < 8; ++c) ad[c] = 0.f;
+    }
+    if (p < 0) {  // no valid position: NaN outputs, cache untouched
+        if (kg == 0) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) yh[8 * cg + c] = __builtin_nanf("");
+        }
+        return;
+    }
+    // Slots 0..nvalid-1 hold the last tokens; the new one goes to slot_new.
+    // Data of other slots was loaded but is replaced by selects (never
+    // multiplied), so whatever they hold cannot reach the result.
+    const int slot_new = (int)(p % window);
+    const int nvalid = p + 1 < window ? (int)p + 1 : window;
+    const bool kvalid = lane < nvalid;
+#pragma unroll
+    for (int c = 0; c < kQC; ++c)
+        if (lane == slot_new) kr[c] = knr[c];
+#pragma unroll
+    for (int i = 0; i < kKPL; ++i) {
+        const int j = kg + kKG * i;
+        if (j == slot_new) vr[i] = vnr;
+        else if (j >= nvalid) vr[i].zero();
     }
 
     // ---- scores and softmax over the valid slots (fp32, base 2)
