@@ -22,9 +22,11 @@
  *     tradeoff" (arXiv 2402.18668v2).
  *
  * Definitions (every routine computes exactly these, up to rounding):
- *   d' = d_feat = 16.  x~ = x * d'^(-1/4) (the library applies this itself
- *   to raw q and k).  Taylor features ([1] s4 "Taylor Linear Attention",
- *   2nd order), F = 1 + d' + d'^2 = 273 rows in this order:
+ *   d' = d_feat (16 in BASED layers; 8, 24 and 32 are the pages' ablation
+ *   sizes, [1] App. D.4).  x~ = x * d'^(-1/4) (the library applies this
+ *   itself to raw q and k).  Taylor features ([1] s4 "Taylor Linear
+ *   Attention", 2nd order), F = 1 + d' + d'^2 rows (273 for 16) in this
+ *   order:
  *       row 0                     1
  *       row 1 + a                 x~_a                    a = 0..d'-1
  *       row 1 + d' + a*d' + b     x~_a * x~_b / sqrt(2)   a-major
@@ -84,7 +86,8 @@ const char *based_status_string(based_status_t s);
 /* Size in bytes of the optional workspace that lets based_prefill split
  * long sequences into segments processed in parallel (carried states are
  * combined by a prefix sum over segments).  0 means the call never uses a
- * workspace for this shape.  Host-only; launches nothing. */
+ * workspace for this shape (always for d_feat != 16).  Host-only; launches
+ * nothing. */
 size_t based_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
 
 /*
@@ -96,7 +99,8 @@ size_t based_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
  *
  *   q, k   [B,H,L,d_feat] dtype       raw (not pre-scaled) queries/keys
  *   v      [B,H,L,d_v]    dtype
- *   chunk  chunk length: 64 (both dtypes); 16 or 32 also for BASED_F32
+ *   chunk  chunk length: 64; 16 or 32 too except for bf16 with d_feat = 16
+ *          (that case runs on the matrix cores, chunk 64)
  *   eps    denominator guard (1e-6 in BASED layers)
  *   y      [B,H,L,d_v]    fp32, written
  *   S      [B,H,F,d_v]    fp32 state; read as the initial state when
@@ -106,8 +110,10 @@ size_t based_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
  *   workspace, workspace_bytes  optional scratch (may be NULL/0); see
  *          based_prefill_workspace_bytes.  With too small a workspace the
  *          call still runs, without the segment split.
- * Supported: d_feat = 16; d_v in {64, 128}; L >= 1 (any, not only multiples
- * of chunk).  y must not alias q, k, v, S or z.
+ * Supported: d_feat in {8, 16, 24, 32} (16 with bf16 inputs on the matrix
+ * cores, the others on the vector ALUs in fp32, a slower path); d_v in
+ * {64, 128}; L >= 1 (any, not only multiples of chunk).  y must not alias
+ * q, k, v, S or z.
  */
 based_status_t based_prefill(const void *q, const void *k, const void *v,
                              based_dtype_t dtype, int B, int H, int L,
@@ -128,7 +134,7 @@ based_status_t based_prefill(const void *q, const void *k, const void *v,
  *   q, k [B,H,d_feat] dtype;  v [B,H,d_v] dtype
  *   S    [B,H,F,d_v] fp32 in/out;  z [B,H,F] fp32 in/out
  *   y    [B,H,d_v]   fp32 out (must not alias the state)
- * Supported: d_feat = 16; d_v in {64, 128}.
+ * Supported: d_feat in {8, 16, 24, 32}; d_v in {64, 128}.
  */
 based_status_t based_decode_step(const void *q, const void *k, const void *v,
                                  based_dtype_t dtype, int B, int H,
@@ -150,7 +156,9 @@ based_status_t based_decode_step(const void *q, const void *k, const void *v,
  *          attention output of the same layer); NULL for none; may equal y
  *          for an in-place accumulate
  *   y      [B,H,L,d_v] fp32 out
- * Supported: d_qk in {16, 64}; d_v = 64; 1 <= window <= 64.
+ * Supported: d_qk in {16, 64}; d_v = 64; 1 <= window <= 128 (bf16 windows
+ * up to 64 keys run on the matrix cores; wider ones, like fp32 inputs, on
+ * the vector ALUs in fp32).
  */
 based_status_t swa_forward(const void *q, const void *k, const void *v,
                            based_dtype_t dtype, int B, int H, int L,
@@ -184,7 +192,7 @@ based_status_t swa_forward(const void *q, const void *k, const void *v,
  *   add   optional [B,H,d_v] fp32 added to y (e.g. the linear-attention
  *         decode output); NULL or equal to y for in place
  *   y     [B,H,d_v] fp32 out
- * Supported: d_qk in {16, 64}; d_v in {64, 128}; 1 <= window <= 64.  The
+ * Supported: d_qk in {16, 64}; d_v in {64, 128}; 1 <= window <= 128.  The
  * caches, y and the inputs must not overlap (add may equal y).
  */
 based_status_t swa_cache_fill(const void *k, const void *v, based_dtype_t dtype,

@@ -16,7 +16,10 @@
 
 namespace {
 
-constexpr int kDFeatSupported = 16;
+// The feature dims every path supports; the bf16 matrix-core prefill is
+// built for 16 (its 16-row rotation tiles), the others run on the vector ALUs.
+constexpr int kDFeatMfma = 16;
+bool feat_dim_ok(int d) { return d == 8 || d == 16 || d == 24 || d == 32; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -67,7 +70,7 @@ BASED_API const char* based_status_string(based_status_t s) {
 BASED_API size_t based_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v) {
     uint64_t BH, BHL;
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return 0;
-    if (d_feat != kDFeatSupported || (d_v != 64 && d_v != 128)) return 0;
+    if (d_feat != kDFeatMfma || (d_v != 64 && d_v != 128)) return 0;
     return based::prefill_mfma_workspace_bytes((int)BH, L, d_v);
 }
 
@@ -84,10 +87,11 @@ BASED_API based_status_t based_prefill(const void* q, const void* k, const void*
     if (!isfinite(eps) || chunk < 1 || d_feat < 1 || d_v < 1) return BASED_E_INVALID;
     uint64_t BH, BHL;
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
-    if (d_feat != kDFeatSupported) return BASED_E_UNSUPPORTED;
+    if (!feat_dim_ok(d_feat)) return BASED_E_UNSUPPORTED;
     if (d_v != 64 && d_v != 128) return BASED_E_UNSUPPORTED;
     const bool bf16 = dtype == BASED_BF16;
-    if (chunk != 64 && (bf16 || (chunk != 16 && chunk != 32))) return BASED_E_UNSUPPORTED;
+    const bool mfma = bf16 && d_feat == kDFeatMfma;
+    if (chunk != 64 && (mfma || (chunk != 16 && chunk != 32))) return BASED_E_UNSUPPORTED;
 
     const uint64_t es = elem_size(dtype);
     const uint64_t F = (uint64_t)based_num_features(d_feat);
@@ -104,11 +108,11 @@ BASED_API based_status_t based_prefill(const void* q, const void* k, const void*
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int init = use_initial_state ? 1 : 0;
-    if (bf16 && chunk == 64)
+    if (mfma)
         return launch_status(based::launch_prefill_mfma(q, k, v, (int)BH, L, d_v, eps, y, S, z, init,
                                                         workspace, workspace_bytes, st));
     return launch_status(
-        based::launch_prefill_valu(q, k, v, bf16, (int)BH, L, d_v, chunk, eps, y, S, z, init, st));
+        based::launch_prefill_valu(q, k, v, bf16, (int)BH, L, d_feat, d_v, chunk, eps, y, S, z, init, st));
 }
 
 BASED_API based_status_t based_decode_step(const void* q, const void* k, const void* v,
@@ -122,14 +126,14 @@ BASED_API based_status_t based_decode_step(const void* q, const void* k, const v
     if (!isfinite(eps) || d_feat < 1 || d_v < 1) return BASED_E_INVALID;
     uint64_t BH, BHL;
     if (check_dims(B, H, 1, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
-    if (d_feat != kDFeatSupported) return BASED_E_UNSUPPORTED;
+    if (!feat_dim_ok(d_feat)) return BASED_E_UNSUPPORTED;
     if (d_v != 64 && d_v != 128) return BASED_E_UNSUPPORTED;
     const uint64_t F = (uint64_t)based_num_features(d_feat);
     const uint64_t S_bytes = BH * F * d_v * 4, z_bytes = BH * F * 4, y_bytes = BH * d_v * 4;
     if (overlaps(y, y_bytes, S, S_bytes) || overlaps(y, y_bytes, z, z_bytes) ||
         overlaps(S, S_bytes, z, z_bytes))
         return BASED_E_INVALID;
-    return launch_status(based::launch_decode_step(q, k, v, dtype == BASED_BF16, (int)BH, d_v, eps,
+    return launch_status(based::launch_decode_step(q, k, v, dtype == BASED_BF16, (int)BH, d_feat, d_v, eps,
                                                    S, z, y, static_cast<hipStream_t>(stream)));
 }
 
@@ -146,7 +150,7 @@ BASED_API based_status_t swa_forward(const void* q, const void* k, const void* v
     uint64_t BH, BHL;
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
     if (d_qk != 16 && d_qk != 64) return BASED_E_UNSUPPORTED;
-    if (d_v != 64 || window > 64) return BASED_E_UNSUPPORTED;
+    if (d_v != 64 || window > 128) return BASED_E_UNSUPPORTED;
     const uint64_t es = elem_size(dtype);
     const uint64_t qk_bytes = BHL * d_qk * es, v_bytes = BHL * d_v * es, y_bytes = BHL * d_v * 4;
     if (overlaps(y, y_bytes, q, qk_bytes) || overlaps(y, y_bytes, k, qk_bytes) ||
@@ -156,10 +160,11 @@ BASED_API based_status_t swa_forward(const void* q, const void* k, const void* v
     const uint64_t tiles = ((uint64_t)L + 63) / 64;
     if (BH * tiles > (uint64_t)INT32_MAX / 2) return BASED_E_INVALID;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    // The matrix-core kernel addresses a head's fp32 rows with 32-bit byte
-    // offsets (L * 256 bytes); longer heads take the fp32 kernel.
+    // The matrix-core kernel covers windows up to 64 keys and addresses a
+    // head's fp32 rows with 32-bit byte offsets (L * 256 bytes); wider
+    // windows and longer heads take the fp32 kernel.
     const bool bf16 = dtype == BASED_BF16;
-    if (bf16 && (uint64_t)L * 256 <= (uint64_t)INT32_MAX)
+    if (bf16 && window <= 64 && (uint64_t)L * 256 <= (uint64_t)INT32_MAX)
         return launch_status(
             based::launch_swa_mfma(q, k, v, (int)BH, L, d_qk, window, scale, add, y, st));
     return launch_status(
@@ -173,7 +178,7 @@ based_status_t check_window_cache(based_dtype_t dtype, int d_qk, int d_v, int wi
     if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_E_INVALID;
     if (window < 1 || d_qk < 1 || d_v < 1) return BASED_E_INVALID;
     if (d_qk != 16 && d_qk != 64) return BASED_E_UNSUPPORTED;
-    if ((d_v != 64 && d_v != 128) || window > 64) return BASED_E_UNSUPPORTED;
+    if ((d_v != 64 && d_v != 128) || window > 128) return BASED_E_UNSUPPORTED;
     return BASED_OK;
 }
 

@@ -54,13 +54,26 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// Taylor feature f (0..272) of a pre-scaled vector xs[16], feature order:
-// 0 -> 1; 1+a -> xs[a]; 17+16a+b -> xs[a]*xs[b]/sqrt2.
+// Feature geometry for feature dim D: F = 1 + D + D*D rows, pre-scale
+// D^(-1/4) (exactly 1/2 for D = 16; rounded to fp32 otherwise).
+template <int D>
+struct Feat {
+    static_assert(D == 8 || D == 16 || D == 24 || D == 32, "feature dims 8, 16, 24, 32");
+    static constexpr int kF = 1 + D + D * D;
+    static constexpr float kPre = D == 8 ? 0.5946035575013605f
+                                 : D == 16 ? 0.5f
+                                 : D == 24 ? 0.45180100180492244f
+                                           : 0.42044820762685725f;
+};
+
+// Taylor feature f (0..F-1) of a pre-scaled vector xs[D], feature order:
+// 0 -> 1; 1+a -> xs[a]; 1+D+a*D+b -> xs[a]*xs[b]/sqrt2.
+template <int D>
 __device__ __forceinline__ float taylor_feature(const float* xs, int f) {
     if (f == 0) return 1.0f;
-    if (f <= kDFeat) return xs[f - 1];
-    const int r = f - 1 - kDFeat;
-    return xs[r >> 4] * xs[r & 15] * kInvSqrt2;
+    if (f <= D) return xs[f - 1];
+    const int r = f - 1 - D;
+    return xs[r / D] * xs[r % D] * kInvSqrt2;
 }
 
 }  // namespace based

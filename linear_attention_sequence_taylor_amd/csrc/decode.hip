@@ -18,11 +18,12 @@
 
 namespace based {
 
-template <int DV>
+template <int DV, int D>
 struct DecodeShape {
+    static constexpr int kF = Feat<D>::kF;             // state rows
     static constexpr int kC4 = DV / 4;                 // float4 slots per state row
     static constexpr int kRowStep = 256 / kC4;         // rows covered per sweep
-    static constexpr int kIters = (kNumFeat + kRowStep - 1) / kRowStep;
+    static constexpr int kIters = (kF + kRowStep - 1) / kRowStep;
     static constexpr int kBatch = 6;                   // rows in flight per thread
 };
 
@@ -39,49 +40,52 @@ __device__ __forceinline__ f32x4 load_v4<uint16_t>(const uint16_t* v, size_t off
     return r;
 }
 
-template <typename T, int DV>
+template <typename T, int DV, int D>
 __global__ __launch_bounds__(256) void decode_step_kernel(const T* __restrict__ q,
                                                           const T* __restrict__ k,
                                                           const T* __restrict__ v, float eps,
                                                           float* __restrict__ S,
                                                           float* __restrict__ z,
                                                           float* __restrict__ y) {
-    using Sh = DecodeShape<DV>;
-    __shared__ float s_q[kDFeat];
-    __shared__ float s_k[kDFeat];
+    using Sh = DecodeShape<DV, D>;
+    constexpr int kF = Sh::kF;
+    __shared__ float s_q[D];
+    __shared__ float s_k[D];
     __shared__ float s_part[Sh::kRowStep][DV];
     __shared__ float s_den[4];
 
     const int h = blockIdx.x;
     const int tid = threadIdx.x;
-    if (tid < kDFeat) {
-        s_q[tid] = load_elem(q, (size_t)h * kDFeat + tid) * kPreScale;
-    } else if (tid < 2 * kDFeat) {
-        s_k[tid - kDFeat] = load_elem(k, (size_t)h * kDFeat + tid - kDFeat) * kPreScale;
+    if (tid < D) {
+        s_q[tid] = load_elem(q, (size_t)h * D + tid) * Feat<D>::kPre;
+    } else if (tid < 2 * D) {
+        s_k[tid - D] = load_elem(k, (size_t)h * D + tid - D) * Feat<D>::kPre;
     }
     __syncthreads();
 
     const int c4 = tid % Sh::kC4;
     const int r0 = tid / Sh::kC4;
     const f32x4 vv = load_v4<T>(v, (size_t)h * DV + c4 * 4);
-    f32x4* Sh4 = reinterpret_cast<f32x4*>(S + (size_t)h * kNumFeat * DV) + c4;
+    f32x4* Sh4 = reinterpret_cast<f32x4*>(S + (size_t)h * kF * DV) + c4;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+    // Fully unrolled for d' = 16 (at most 6 batches); capped for the larger
+    // feature maps so the batches in flight fit the register file.
+#pragma unroll 8
     for (int it0 = 0; it0 < Sh::kIters; it0 += Sh::kBatch) {
         f32x4 st[Sh::kBatch];
 #pragma unroll
         for (int b = 0; b < Sh::kBatch; ++b) {
             const int r = r0 + (it0 + b) * Sh::kRowStep;
-            if (it0 + b < Sh::kIters && r < kNumFeat)
+            if (it0 + b < Sh::kIters && r < kF)
                 st[b] = __builtin_nontemporal_load(Sh4 + (size_t)r * Sh::kC4);
         }
 #pragma unroll
         for (int b = 0; b < Sh::kBatch; ++b) {
             const int r = r0 + (it0 + b) * Sh::kRowStep;
-            if (it0 + b < Sh::kIters && r < kNumFeat) {
-                const float fk = taylor_feature(s_k, r);
-                const float fq = taylor_feature(s_q, r);
+            if (it0 + b < Sh::kIters && r < kF) {
+                const float fk = taylor_feature<D>(s_k, r);
+                const float fq = taylor_feature<D>(s_q, r);
                 f32x4 s = st[b];
                 s.x = fmaf(fk, vv.x, s.x);
                 s.y = fmaf(fk, vv.y, s.y);
@@ -98,11 +102,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const T* __restrict__ 
 
     // Normaliser: z rows tid and tid + 256.
     float den = 0.f;
-    float* zh = z + (size_t)h * kNumFeat;
-    for (int r = tid; r < kNumFeat; r += 256) {
-        const float zn = zh[r] + taylor_feature(s_k, r);
+    float* zh = z + (size_t)h * kF;
+    for (int r = tid; r < kF; r += 256) {
+        const float zn = zh[r] + taylor_feature<D>(s_k, r);
         zh[r] = zn;
-        den = fmaf(taylor_feature(s_q, r), zn, den);
+        den = fmaf(taylor_feature<D>(s_q, r), zn, den);
     }
     den = wave_sum(den);
     if ((tid & 63) == 0) s_den[tid >> 6] = den;
@@ -120,23 +124,34 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const T* __restrict__ 
     }
 }
 
+template <typename T, int D>
+static void launch_decode_d(const T* q, const T* k, const T* v, int BH, int dv, float eps, float* S, float* z,
+                            float* y, hipStream_t st) {
+    if (dv == 64)
+        hipLaunchKernelGGL((decode_step_kernel<T, 64, D>), dim3(BH), dim3(256), 0, st, q, k, v, eps, S, z, y);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<T, 128, D>), dim3(BH), dim3(256), 0, st, q, k, v, eps, S, z, y);
+}
+
 template <typename T>
-static hipError_t launch_decode_t(const void* q, const void* k, const void* v, int BH, int dv,
+static hipError_t launch_decode_t(const void* q, const void* k, const void* v, int BH, int d, int dv,
                                   float eps, float* S, float* z, float* y, hipStream_t st) {
     const T* qq = static_cast<const T*>(q);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
-    if (dv == 64)
-        hipLaunchKernelGGL((decode_step_kernel<T, 64>), dim3(BH), dim3(256), 0, st, qq, kk, vv, eps, S, z, y);
-    else
-        hipLaunchKernelGGL((decode_step_kernel<T, 128>), dim3(BH), dim3(256), 0, st, qq, kk, vv, eps, S, z, y);
+    switch (d) {
+        case 8: launch_decode_d<T, 8>(qq, kk, vv, BH, dv, eps, S, z, y, st); break;
+        case 24: launch_decode_d<T, 24>(qq, kk, vv, BH, dv, eps, S, z, y, st); break;
+        case 32: launch_decode_d<T, 32>(qq, kk, vv, BH, dv, eps, S, z, y, st); break;
+        default: launch_decode_d<T, 16>(qq, kk, vv, BH, dv, eps, S, z, y, st); break;
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool bf16, int BH,
+hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool bf16, int BH, int d,
                               int dv, float eps, float* S, float* z, float* y, hipStream_t st) {
-    return bf16 ? launch_decode_t<uint16_t>(q, k, v, BH, dv, eps, S, z, y, st)
-                : launch_decode_t<float>(q, k, v, BH, dv, eps, S, z, y, st);
+    return bf16 ? launch_decode_t<uint16_t>(q, k, v, BH, d, dv, eps, S, z, y, st)
+                : launch_decode_t<float>(q, k, v, BH, d, dv, eps, S, z, y, st);
 }
 
 }  // namespace based

@@ -8,12 +8,14 @@
 
 namespace based {
 
-// Fused next-token step (decode.hip).  dv in {64, 128}.
-hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool bf16, int BH,
+// Fused next-token step (decode.hip).  d (feature dim) in {8, 16, 24, 32},
+// dv in {64, 128}.
+hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool bf16, int BH, int d,
                               int dv, float eps, float* S, float* z, float* y, hipStream_t st);
 
-// fp32 vector-ALU chunked prefill (prefill_valu.hip).  chunk in {16,32,64}.
-hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, bool bf16, int BH, int L,
+// fp32 vector-ALU chunked prefill (prefill_valu.hip).  d in {8, 16, 24, 32},
+// chunk in {16, 32, 64}.
+hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, bool bf16, int BH, int L, int d,
                                int dv, int chunk, float eps, float* y, float* S, float* z,
                                int use_init, hipStream_t st);
 

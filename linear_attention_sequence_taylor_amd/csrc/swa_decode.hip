@@ -11,7 +11,8 @@
 //
 // Decode step: HBM-bound (each cached key and value is read once per step).
 // One wave per (batch, head), four per workgroup, no workgroup barrier.
-// Lane j scores slot j from its key row (16-byte loads); for P.V, lane
+// Lane j scores slot j (and j + 64 for windows over 64) from its key row
+// (16-byte loads); for P.V, lane
 // (key group kg, column group cg) accumulates 8 columns over the keys kg,
 // kg + KG, ... and the key groups are summed with lane shuffles.  Key and
 // value loads are all issued before any arithmetic, so a wave waits for
@@ -26,7 +27,6 @@
 namespace based {
 namespace {
 
-constexpr int kMaxWindow = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // 8 consecutive elements of a row: 16 bytes of bf16 or 32 of fp32, kept in
@@ -64,17 +64,19 @@ __device__ __forceinline__ void copy_units(const void* src, void* dst, int n, in
     if (lane < n) reinterpret_cast<u32x4*>(dst)[lane] = reinterpret_cast<const u32x4*>(src)[lane];
 }
 
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, int R>
 __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                          const T* __restrict__ v,
                                                          const long long* __restrict__ pos, int H, int BH,
                                                          int window, float scale, T* __restrict__ kc,
                                                          T* __restrict__ vc, const float* add,
                                                          float* __restrict__ y) {
+    // R rounds of 64 slots: window <= 64 R.  Lane `lane` scores slots
+    // lane + 64 r; P.V lane (kg, cg) covers keys kg + KG i, i < KPL.
     constexpr int kQC = DQK / 8;               // chunks of 8 in a key row
     constexpr int kCG = DV / 8;                // column groups of 8
     constexpr int kKG = 64 / kCG;              // key groups in P.V
-    constexpr int kKPL = kMaxWindow / kKG;     // keys per lane in P.V
+    constexpr int kKPL = 64 * R / kKG;         // keys per lane in P.V
     constexpr int kKU = DQK * sizeof(T) / 16;  // 16-byte units of a key row
     constexpr int kVU = DV * sizeof(T) / 16;   // and of a value row
     const int lane = threadIdx.x & 63;
@@ -88,16 +90,20 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
     T* vch = vc + (size_t)head * window * DV;
 
     // ---- loads, all issued before the position is known: the query, the
-    // new key and value, the key of slot `lane` and this lane's value chunks
+    // new key and value, the keys of this lane's slots and its value chunks
     // of every slot (the slot addresses do not depend on the position).
     const long long p = pos[head / H];
-    Chunk8<T> qr[kQC], kr[kQC], knr[kQC], vr[kKPL], vnr;
+    Chunk8<T> qr[kQC], kr[R][kQC], knr[kQC], vr[kKPL], vnr;
 #pragma unroll
     for (int c = 0; c < kQC; ++c) {
         qr[c].load(q + (size_t)head * DQK + 8 * c);
         knr[c].load(kn + 8 * c);
-        if (lane < window) kr[c].load(kch + (size_t)lane * DQK + 8 * c);
-        else kr[c].zero();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int slot = lane + 64 * r;
+            if (slot < window) kr[r][c].load(kch + (size_t)slot * DQK + 8 * c);
+            else kr[r][c].zero();
+        }
     }
     vnr.load(vn + 8 * cg);
 #pragma unroll
@@ -131,10 +137,11 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
     // multiplied), so whatever they hold cannot reach the result.
     const int slot_new = (int)(p % window);
     const int nvalid = p + 1 < window ? (int)p + 1 : window;
-    const bool kvalid = lane < nvalid;
 #pragma unroll
-    for (int c = 0; c < kQC; ++c)
-        if (lane == slot_new) kr[c] = knr[c];
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < kQC; ++c)
+            if (lane + 64 * r == slot_new) kr[r][c] = knr[c];
 #pragma unroll
     for (int i = 0; i < kKPL; ++i) {
         const int j = kg + kKG * i;
@@ -143,15 +150,26 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
     }
 
     // ---- scores and softmax over the valid slots (fp32, base 2)
-    float dot = 0.f;
+    float s[R];
+    float m = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < kQC; ++c)
+    for (int r = 0; r < R; ++r) {
+        float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot = fmaf(qr[c].get(e), kr[c].get(e), dot);
-    const float s = kvalid ? dot * (scale * kLog2e) : -INFINITY;
-    const float m = wave_max(s);
-    const float pe = kvalid ? __builtin_amdgcn_exp2f(s - m) : 0.f;
-    const float l = wave_sum(pe);
+        for (int c = 0; c < kQC; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = fmaf(qr[c].get(e), kr[r][c].get(e), dot);
+        s[r] = lane + 64 * r < nvalid ? dot * (scale * kLog2e) : -INFINITY;
+        m = fmaxf(m, s[r]);
+    }
+    m = wave_max(m);
+    float pe[R], l = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        pe[r] = lane + 64 * r < nvalid ? __builtin_amdgcn_exp2f(s[r] - m) : 0.f;
+        l += pe[r];
+    }
+    l = wave_sum(l);
 
     // ---- P.V: this lane's keys, then the sum over key groups
     float acc[8];
@@ -159,7 +177,12 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
     for (int c = 0; c < 8; ++c) acc[c] = 0.f;
 #pragma unroll
     for (int i = 0; i < kKPL; ++i) {
-        const float pj = __shfl(pe, kg + kKG * i, 64);  // 0 for slots that are not valid
+        const int j = kg + kKG * i;  // slot j's weight is on lane j % 64, round j / 64
+        float pj = __shfl(pe[0], j & 63, 64);
+        if constexpr (R == 2) {
+            const float pj1 = __shfl(pe[R - 1], j & 63, 64);
+            pj = j >= 64 ? pj1 : pj;
+        }
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = fmaf(pj, vr[i].get(c), acc[c]);
     }
@@ -215,12 +238,21 @@ hipError_t decode_dv(const void* q, const void* k, const void* v, const long lon
     const T* vv = static_cast<const T*>(v);
     T* kcc = static_cast<T*>(kc);
     T* vcc = static_cast<T*>(vc);
-    if (dv == 64)
-        hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 64>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH, window,
-                           scale, kcc, vcc, add, y);
-    else
-        hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 128>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH, window,
-                           scale, kcc, vcc, add, y);
+    if (window <= 64) {
+        if (dv == 64)
+            hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 64, 1>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH,
+                               window, scale, kcc, vcc, add, y);
+        else
+            hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 128, 1>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH,
+                               window, scale, kcc, vcc, add, y);
+    } else {
+        if (dv == 64)
+            hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 64, 2>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH,
+                               window, scale, kcc, vcc, add, y);
+        else
+            hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 128, 2>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH,
+                               window, scale, kcc, vcc, add, y);
+    }
     return hipGetLastError();
 }
 

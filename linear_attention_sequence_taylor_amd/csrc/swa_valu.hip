@@ -1,6 +1,7 @@
 // swa_valu.hip -- causal sliding-window softmax attention on the vector ALUs
 // in fp32 (gfx950): the exact-precision path for fp32 inputs, and for bf16
-// heads too long for the 32-bit offsets of the MFMA kernel in swa_mfma.hip.
+// heads too long for the 32-bit offsets of the MFMA kernel in swa_mfma.hip
+// or windows over 64 keys (up to 128).
 //
 // "Simple linear attention language models balance the recall-throughput
 // tradeoff", s4 "Local Exact Attention": each query attends with exact
@@ -16,16 +17,16 @@
 namespace based {
 
 constexpr int kSwaValuQ = 32;
-constexpr int kSwaMaxWindow = 64;
 
-template <typename T, int DQK>
+// MAXW: the largest window the staged key rows cover (64 or 128).
+template <typename T, int DQK, int MAXW>
 __global__ __launch_bounds__(256) void swa_valu_kernel(const T* __restrict__ q,
                                                        const T* __restrict__ k,
                                                        const T* __restrict__ v, int L, int window,
                                                        float scale, const float* add,
                                                        float* y) {
     constexpr int DV = 64;
-    constexpr int KR = kSwaValuQ + kSwaMaxWindow - 1;  // key rows staged
+    constexpr int KR = kSwaValuQ + MAXW - 1;  // key rows staged
     __shared__ float s_q[kSwaValuQ][DQK];
     __shared__ float s_k[KR][DQK];
     __shared__ float s_v[KR][DV];
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(256) void swa_valu_kernel(const T* __restrict__ q,
     const int head = blockIdx.x / ntiles;
     const int i0 = (blockIdx.x % ntiles) * kSwaValuQ;
     const int tid = threadIdx.x;
-    const int jbase = i0 - (kSwaMaxWindow - 1);  // key row of s_k[0]
+    const int jbase = i0 - (MAXW - 1);  // key row of s_k[0]
 
     const T* qh = q + (size_t)head * L * DQK;
     const T* kh = k + (size_t)head * L * DQK;
@@ -98,12 +99,21 @@ static hipError_t launch_swa_valu_t(const void* q, const void* k, const void* v,
     const T* qq = static_cast<const T*>(q);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
-    if (dqk == 16)
-        hipLaunchKernelGGL((swa_valu_kernel<T, 16>), grid, dim3(256), 0, st, qq, kk, vv, L, window,
-                           scale, add, y);
-    else
-        hipLaunchKernelGGL((swa_valu_kernel<T, 64>), grid, dim3(256), 0, st, qq, kk, vv, L, window,
-                           scale, add, y);
+    if (window <= 64) {
+        if (dqk == 16)
+            hipLaunchKernelGGL((swa_valu_kernel<T, 16, 64>), grid, dim3(256), 0, st, qq, kk, vv, L, window,
+                               scale, add, y);
+        else
+            hipLaunchKernelGGL((swa_valu_kernel<T, 64, 64>), grid, dim3(256), 0, st, qq, kk, vv, L, window,
+                               scale, add, y);
+    } else {
+        if (dqk == 16)
+            hipLaunchKernelGGL((swa_valu_kernel<T, 16, 128>), grid, dim3(256), 0, st, qq, kk, vv, L, window,
+                               scale, add, y);
+        else
+            hipLaunchKernelGGL((swa_valu_kernel<T, 64, 128>), grid, dim3(256), 0, st, qq, kk, vv, L, window,
+                               scale, add, y);
+    }
     return hipGetLastError();
 }
 

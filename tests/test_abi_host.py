@@ -93,7 +93,8 @@ def _prefill(lib, **kw):
     (dict(dtype=7), 1), (dict(B=0), 1), (dict(H=-1), 1), (dict(L=0), 1),
     (dict(B=1 << 20, H=1 << 20), 1), (dict(chunk=0), 1), (dict(eps=float("nan")), 1),
     (dict(L=2**31 - 1), 1), (dict(L=2**31 - 1023), 1), (dict(B=1 << 10, H=1 << 10, L=1 << 21), 1),
-    (dict(d=8), 2), (dict(dv=96), 2), (dict(chunk=32), 2), (dict(dtype=0, chunk=48), 2),
+    (dict(d=12), 2), (dict(d=64), 2), (dict(dv=96), 2), (dict(chunk=32), 2), (dict(dtype=0, chunk=48), 2),
+    (dict(d=8, chunk=48), 2),
     (dict(y=A), 1), (dict(S=Y), 1), (dict(z=S + 64), 1),
 ])
 def test_prefill_rejects(lib, kw, want):
@@ -109,7 +110,7 @@ def _decode(lib, **kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(v=None), 1), (dict(S=S + 8), 1), (dict(B=0), 1), (dict(eps=float("inf")), 1),
-    (dict(d=32), 2), (dict(dv=32), 2), (dict(y=S), 1), (dict(z=S + 16), 1), (dict(dtype=-1), 1),
+    (dict(d=20), 2), (dict(dv=32), 2), (dict(y=S), 1), (dict(z=S + 16), 1), (dict(dtype=-1), 1),
 ])
 def test_decode_rejects(lib, kw, want):
     assert _decode(lib, **kw) == want
@@ -125,7 +126,7 @@ def _swa(lib, **kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(k=None), 1), (dict(add=S + 4), 1), (dict(window=0), 1), (dict(scale=float("nan")), 1),
-    (dict(L=0), 1), (dict(dqk=32), 2), (dict(dv=128), 2), (dict(window=65), 2),
+    (dict(L=0), 1), (dict(dqk=32), 2), (dict(dv=128), 2), (dict(window=129), 2),
     (dict(y=A), 1), (dict(add=Y + 256), 1), (dict(L=2**31 - 1), 1), (dict(L=2**31 - 64), 1),
 ])
 def test_swa_rejects(lib, kw, want):
@@ -143,7 +144,7 @@ def _swa_dec(lib, **kw):
 @pytest.mark.parametrize("kw,want", [
     (dict(q=None), 1), (dict(pos=None), 1), (dict(kc=None), 1), (dict(y=None), 1), (dict(pos=S + 4), 1),
     (dict(kc=Y + 8), 1), (dict(dtype=3), 1), (dict(B=0), 1), (dict(window=0), 1), (dict(scale=float("inf")), 1),
-    (dict(dqk=32), 2), (dict(dv=96), 2), (dict(window=65), 2), (dict(vc=Y + 64), 1), (dict(y=Y), 1),
+    (dict(dqk=32), 2), (dict(dv=96), 2), (dict(window=129), 2), (dict(vc=Y + 64), 1), (dict(y=Y), 1),
     (dict(kc=A), 1), (dict(y=S), 1), (dict(add=S + (1 << 20) + 16), 1),
 ])
 def test_swa_decode_rejects(lib, kw, want):
@@ -159,7 +160,7 @@ def _swa_fill(lib, **kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(k=None), 1), (dict(vc=None), 1), (dict(kc=Y + 2), 1), (dict(L=0), 1), (dict(window=0), 1),
-    (dict(dqk=8), 2), (dict(dv=32), 2), (dict(window=100), 2), (dict(vc=Y + 64), 1), (dict(kc=A), 1),
+    (dict(dqk=8), 2), (dict(dv=32), 2), (dict(window=200), 2), (dict(vc=Y + 64), 1), (dict(kc=A), 1),
     (dict(L=2**31 - 1), 1),
 ])
 def test_swa_fill_rejects(lib, kw, want):

@@ -320,6 +320,51 @@ def test_swa_longest_heads(L):
     report(f"swa longest head L={L} ({len(rows)} sampled queries)", ratio(got, want), 2e-2)
 
 
+# ---------------------------------------------------------------- other feature and window sizes
+@pytest.mark.parametrize("d", [8, 24, 32])
+@pytest.mark.parametrize("dtype,tol,chunk,dv", [(torch.bfloat16, 2e-2, 64, 64), (torch.float32, 1e-4, 64, 128),
+                                                (torch.float32, 1e-4, 16, 64)])
+def test_prefill_feature_dims(d, dtype, tol, chunk, dv):
+    """Feature dims 8, 24 and 32 (F = 73, 601, 1057 rows), ragged length."""
+    based = based_mod()
+    q, k, v = si.custom((1, 2, 130, d), (1, 2, 130, dv), seed=1800 + d + dv + chunk, scale=0.5, dtype=dtype)
+    y, S, z = based.based_prefill(*dev(q, k, v), chunk=chunk)
+    torch.cuda.synchronize()
+    assert S.shape[-2] == 1 + d + d * d
+    yo, So, zo = oracle.la_recurrent(q, k, v)
+    report(f"prefill d={d} {dtype} chunk={chunk} dv={dv} y", ratio(y, yo), tol)
+    report(f"prefill d={d} {dtype} chunk={chunk} dv={dv} S", ratio(S, So), tol)
+    report(f"prefill d={d} {dtype} chunk={chunk} dv={dv} z", ratio(z, zo), tol)
+
+
+@pytest.mark.parametrize("d", [8, 24, 32])
+@pytest.mark.parametrize("dtype,tol,dv", [(torch.bfloat16, 2e-2, 128), (torch.float32, 1e-4, 64)])
+def test_prefill_then_decode_feature_dims(d, dtype, tol, dv):
+    """Prefill then next-token steps with feature dims 8, 24, 32: the steps
+    equal the longer sequence's outputs (the state handoff at 1 + d + d^2 rows)."""
+    based = based_mod()
+    L1, T = 70, 6
+    q, k, v = si.custom((2, 2, L1 + T, d), (2, 2, L1 + T, dv), seed=1850 + d + dv, scale=1.0, dtype=dtype)
+    qd, kd, vd = dev(q, k, v)
+    _, S, z = based.based_prefill(qd[:, :, :L1].contiguous(), kd[:, :, :L1].contiguous(), vd[:, :, :L1].contiguous())
+    ys = [based.based_decode_step(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(),
+                                  S, z).clone() for t in range(L1, L1 + T)]
+    yo = oracle.la_quadratic(q, k, v)
+    report(f"prefill+decode d={d} {dtype} dv={dv}", ratio(torch.stack(ys, dim=2), yo[:, :, L1:]), tol)
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, 2e-2), (torch.float32, 1e-4)])
+@pytest.mark.parametrize("dqk", [16, 64])
+@pytest.mark.parametrize("window,L", [(65, 129), (100, 300), (128, 1), (128, 300)])
+def test_swa_wide_windows(dtype, tol, dqk, window, L):
+    """Windows over 64 keys (up to 128, the pages' other design point)."""
+    based = based_mod()
+    q, k, v = si.custom((1, 3, L, dqk), (1, 3, L, 64), seed=1900 + window + L + dqk, scale=1.0, dtype=dtype)
+    scale = dqk ** -0.5
+    y = based.swa_forward(*dev(q, k, v), window=window, scale=scale)
+    report(f"swa {dtype} dqk={dqk} w={window} L={L}", ratio(y, oracle.swa(q, k, v, window, scale)), tol)
+
+
 # ---------------------------------------------------------------- window decode
 def _nan_cache(B, H, window, d, dtype):
     return torch.full((B, H, window, d), float("nan"), dtype=dtype, device=DEV)
@@ -328,7 +373,8 @@ def _nan_cache(B, H, window, d, dtype):
 @pytest.mark.parametrize("dtype,dqk,dv,window,L", [
     (torch.bfloat16, 64, 64, 64, 100), (torch.bfloat16, 16, 128, 64, 10), (torch.bfloat16, 64, 128, 7, 30),
     (torch.bfloat16, 64, 64, 64, 0), (torch.float32, 64, 64, 64, 64), (torch.float32, 16, 128, 1, 5),
-    (torch.float32, 64, 128, 33, 200),
+    (torch.float32, 64, 128, 33, 200), (torch.bfloat16, 64, 128, 128, 200), (torch.float32, 16, 64, 100, 10),
+    (torch.bfloat16, 64, 64, 128, 0),
 ])
 def test_swa_decode_continues_window(dtype, dqk, dv, window, L):
     """Ring filled from a prefix (two sequences, prefixes L and L + 5; none

@@ -41,7 +41,7 @@ def _frac(s):
 
 
 # ---------------------------------------------------------------- P1
-@pytest.mark.parametrize("d", [4, 16, 24])
+@pytest.mark.parametrize("d", [4, 8, 16, 24, 32])
 def test_p1_features_taylor_limit(oracle_mod, d):
     """phi(q).phi(k) must agree with exp(s), s = q.k/sqrt(d), up to the cubic
     term: (exp(s) - phi.phi) / s^3 -> 1/6 as s -> 0.  A wrong pre-scale, a
@@ -77,6 +77,21 @@ def test_p1_feature_count(oracle_mod):
 
 
 # ---------------------------------------------------------------- P2
+@pytest.mark.parametrize("d", [8, 24, 32])
+def test_p2_quadratic_equals_recurrent_feature_dims(oracle_mod, d):
+    """The ablation feature sizes (BASED App. D.4): the phi-free closed form
+    and the explicit (1 + d + d^2)-row recurrence agree for every d."""
+    rng = _rng(100 + d)
+    L = 45
+    q = rng.standard_normal((1, 2, L, d))
+    k = rng.standard_normal((1, 2, L, d))
+    v = rng.standard_normal((1, 2, L, 16))
+    yq = oracle_mod.la_quadratic(q, k, v)
+    yr, S, z = oracle_mod.la_recurrent(q, k, v)
+    np.testing.assert_allclose(yq, yr, rtol=1e-11, atol=1e-12)
+    assert S.shape[-2] == 1 + d + d * d and z[..., 0].tolist() == [[float(L)] * 2]
+
+
 @pytest.mark.parametrize("L,dv", [(1, 64), (37, 64), (64, 128), (65, 64), (200, 128)])
 def test_p2_quadratic_equals_recurrent(oracle_mod, L, dv):
     rng = _rng(L * 7 + dv)
