@@ -283,6 +283,69 @@ def bench_window_decode(based, wl, n_steps, graph_steps=64, n_sets=16):
     return timer.seconds() / (reps * graph_steps)
 
 
+def bench_other_sizes(based):
+    """The pages' other design points (feature dim 32, window 128), on the
+    paths that carry them: seeded inputs, event-timed regions.  Returns a
+    dict of legs (report only)."""
+    out = {}
+    # window 128 over the 8K window workload inputs (matrix cores, two-tile halo)
+    ww = si.WORKLOADS["window_8k"]
+    qw, kw = si.window_inputs(ww)
+    v = si.linear_inputs(ww)[2]
+    qd, kd, vd = qw.cuda(), kw.cuda(), v.cuda()
+    del qw, kw, v
+    y = torch.empty(ww.B, ww.H, ww.L, ww.dv, device="cuda")
+    for _ in range(20):
+        based.swa_forward(qd, kd, vd, window=128, scale=ww.swa_scale, add=y, y=y)
+    t = RegionTimer()
+    torch.cuda.synchronize()
+    t.start()
+    for _ in range(20):
+        based.swa_forward(qd, kd, vd, window=128, scale=ww.swa_scale, add=y, y=y)
+    t.stop()
+    sec = t.seconds() / 20
+    sb = swa_bytes(ww)
+    out["window_8k_w128"] = {"kernel_us": sec * 1e6, "hbm_GBps": sb / sec / 1e9, "hbm_frac": sb / sec / HBM_PEAK,
+                             "algorithmic_bytes": sb, "note": "w=128, fused add, matrix cores with a two-tile halo"}
+    del qd, kd, vd, y
+    # next-token step with feature dim 32 (F = 1057), the 1.3B decode batch
+    # (B=128, H=16, d_v=128; 1.1 GB of fp32 state), from a zero state
+    B, H, d, dv, F32 = 128, 16, 32, 128, 1 + 32 + 32 * 32
+    steps = [tuple(x.cuda() for x in si.custom((B, H, d), (B, H, dv), seed=2000 + i)) for i in range(16)]
+    S = torch.zeros(B, H, F32, dv, device="cuda")
+    z = torch.zeros(B, H, F32, device="cuda")
+    yd = torch.empty(B, H, dv, device="cuda")
+    for i in range(300):
+        based.based_decode_step(*steps[i % 16], S, z, y=yd)
+    t = RegionTimer()
+    torch.cuda.synchronize()
+    t.start()
+    for i in range(256):
+        based.based_decode_step(*steps[i % 16], S, z, y=yd)
+    t.stop()
+    sec = t.seconds() / 256
+    db = B * H * (2 * (F32 * dv + F32) * 4 + 2 * d * 2 + dv * 2 + dv * 4)
+    out["decode_d32"] = {"kernel_us": sec * 1e6, "hbm_GBps": db / sec / 1e9, "hbm_frac": db / sec / HBM_PEAK,
+                         "algorithmic_bytes": db, "note": "feature dim 32, B=128, H=16, d_v=128, bf16 inputs"}
+    del S, z, steps
+    # prefill with feature dim 32 (bf16 inputs, fp32 vector-ALU path), B=2, H=16, L=2048, d_v=64
+    B, H, L, dv = 2, 16, 2048, 64
+    q, k, v = (x.cuda() for x in si.custom((B, H, L, d), (B, H, L, dv), seed=2100, scale=0.5))
+    for _ in range(2):
+        based.based_prefill(q, k, v)
+    t = RegionTimer()
+    torch.cuda.synchronize()
+    t.start()
+    for _ in range(5):
+        based.based_prefill(q, k, v)
+    t.stop()
+    sec = t.seconds() / 5
+    pb = B * H * L * (2 * d * 2 + dv * 2 + dv * 4) + B * H * (F32 * dv + F32) * 4
+    out["prefill_d32"] = {"kernel_us": sec * 1e6, "tokens_per_s": B * L / sec, "hbm_frac": pb / sec / HBM_PEAK,
+                          "algorithmic_bytes": pb, "note": "feature dim 32, B=2, H=16, L=2048, fp32 vector-ALU path"}
+    return out
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """Oracle recurrent form on whole heads of the workload, sized to about
     budget_s of host time (at most the full workload)."""
@@ -419,6 +482,10 @@ def main():
                                          "hbm_GBps": lb / lkern / 1e9, "hbm_frac": lb / lkern / HBM_PEAK,
                                          "mfma_frac": prefill_flops(wlong) / lkern / MFMA_BF16_PEAK}
             print(f"[bench] long prefill: {lkern*1e3:.3f} ms", file=sys.stderr, flush=True)
+        other = bench_other_sizes(based)
+        extra.update(other)
+        print("[bench] other sizes: " + ", ".join(f"{k} {v['kernel_us']:.1f} us" for k, v in other.items()),
+              file=sys.stderr, flush=True)
         line["extra"] = extra
 
     if not args.no_cpu:

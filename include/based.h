@@ -156,9 +156,8 @@ based_status_t based_decode_step(const void *q, const void *k, const void *v,
  *          attention output of the same layer); NULL for none; may equal y
  *          for an in-place accumulate
  *   y      [B,H,L,d_v] fp32 out
- * Supported: d_qk in {16, 64}; d_v = 64; 1 <= window <= 128 (bf16 windows
- * up to 64 keys run on the matrix cores; wider ones, like fp32 inputs, on
- * the vector ALUs in fp32).
+ * Supported: d_qk in {16, 64}; d_v = 64; 1 <= window <= 128 (bf16 on the
+ * matrix cores, fp32 inputs on the vector ALUs in fp32).
  */
 based_status_t swa_forward(const void *q, const void *k, const void *v,
                            based_dtype_t dtype, int B, int H, int L,

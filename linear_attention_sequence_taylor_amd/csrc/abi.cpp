@@ -160,11 +160,10 @@ BASED_API based_status_t swa_forward(const void* q, const void* k, const void* v
     const uint64_t tiles = ((uint64_t)L + 63) / 64;
     if (BH * tiles > (uint64_t)INT32_MAX / 2) return BASED_E_INVALID;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    // The matrix-core kernel covers windows up to 64 keys and addresses a
-    // head's fp32 rows with 32-bit byte offsets (L * 256 bytes); wider
-    // windows and longer heads take the fp32 kernel.
+    // The matrix-core kernel addresses a head's fp32 rows with 32-bit byte
+    // offsets (L * 256 bytes); longer heads take the fp32 kernel.
     const bool bf16 = dtype == BASED_BF16;
-    if (bf16 && window <= 64 && (uint64_t)L * 256 <= (uint64_t)INT32_MAX)
+    if (bf16 && (uint64_t)L * 256 <= (uint64_t)INT32_MAX)
         return launch_status(
             based::launch_swa_mfma(q, k, v, (int)BH, L, d_qk, window, scale, add, y, st));
     return launch_status(

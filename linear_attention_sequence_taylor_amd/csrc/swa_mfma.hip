@@ -39,14 +39,26 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 #define BASED_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-// LDS slots of one step: K/V of the previous (halo) and current tile, Q of
-// the current tile, and the slots that receive tile t+1.  Each slot is its
-// own __shared__ array, so the compiler can tell the copies in flight from
-// the data being read.
+// LDS slots of one step: K/V of the HALO tiles before the current one and of
+// the current tile (oldest first), Q of the current tile, and the slots that
+// receive tile t+1.  Each slot is its own __shared__ array, so the compiler
+// can tell the copies in flight from the data being read.
+template <int HALO>
 struct SwaSlots {
-    const uint16_t *kp, *kc, *vp, *vc, *qc;
+    const uint16_t* k[HALO + 1];
+    const uint16_t* v[HALO + 1];
+    const uint16_t* qc;
     uint16_t *kn, *vn, *qn;
 };
+
+// a[i] for a wave-uniform i, as a chain of selects (no indexed local array).
+template <int N>
+__device__ __forceinline__ const uint16_t* pick_slot(const uint16_t* const (&a)[N], int i) {
+    const uint16_t* p = a[0];
+#pragma unroll
+    for (int n = 1; n < N; ++n) p = i == n ? a[n] : p;
+    return p;
+}
 
 // Element offset of (row, col) in a [64][D] bf16 tile whose 16-byte units
 // are XOR-swizzled by row bits.
@@ -191,56 +203,54 @@ __device__ __forceinline__ void v_kstep(const uint16_t* v1, int r1, const uint16
 }
 
 // One 64-query tile for wave w: y rows in yacc (P.V, unnormalised) and the
-// normaliser l of this lane's query.
-template <int DQK>
-__device__ __forceinline__ void swa_tile(const SwaSlots& sl, int t, int window, float sl2, int w, int g, int r,
-                                         f32x4 (&yacc)[4], float& l) {
-    const uint16_t* prev_k = sl.kp;
-    const uint16_t* cur_k = sl.kc;
-    const uint16_t* prev_v = sl.vp;
-    const uint16_t* cur_v = sl.vc;
+// normaliser l of this lane's query.  Keys: the 64*HALO before the wave's
+// first query and the wave's 16, i.e. 4*HALO + 1 key tiles of 16.
+template <int DQK, int HALO>
+__device__ __forceinline__ void swa_tile(const SwaSlots<HALO>& sl, int t, int window, float sl2, int w, int g,
+                                         int r, f32x4 (&yacc)[4], float& l) {
+    constexpr int kKT = 4 * HALO + 1;  // key tiles
+    constexpr int kHR = kQT * HALO;    // halo rows
     const uint16_t* qs = sl.qc;
     const int q0 = t * kQT + 16 * w;  // first query of the wave
     const int qi = q0 + r;            // this lane's query
 
-    // Scores for key tiles j = 0..4: keys q0 - 64 + 16j + 4g + m, which sit
-    // in rows 16w + 16j of the [prev | cur] window.
-    float s[5][4];
+    // Scores for key tiles j: keys q0 - 64*HALO + 16j + 4g + m, which sit in
+    // row 16w + 16j of the window [tile t-HALO | ... | tile t].
+    float s[kKT][4];
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
+    for (int j = 0; j < kKT; ++j) {
         const int R = 16 * w + 16 * j;
-        const f32x4 st = R < 64 ? score_tile<DQK>(prev_k, R, qs, 16 * w, g, r)
-                                : score_tile<DQK>(cur_k, R - 64, qs, 16 * w, g, r);
-        if (window == kQT && q0 >= kQT) {
-            // Full 64-key window, no key before the sequence start: key
-            // 16j + 4g + m of the 80 is in the window of query r iff it lies
-            // in (r, r + 64], so only the first and last key tiles are cut.
+        const f32x4 st = score_tile<DQK>(pick_slot(sl.k, R >> 6), R & 63, qs, 16 * w, g, r);
+        if (window == kHR && q0 >= kHR) {
+            // Full window, no key before the sequence start: key 16j + 4g + m
+            // is in the window of query r iff it lies in (r, r + 64*HALO], so
+            // only the first and last key tiles are cut.
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int d = 16 * j + 4 * g + m;
-                const bool ok = j == 0 ? d > r : (j == 4 ? d <= r + 64 : true);
+                const bool ok = j == 0 ? d > r : (j == kKT - 1 ? d <= r + kHR : true);
                 s[j][m] = ok ? st[m] * sl2 : -INFINITY;
             }
         } else {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int kj = q0 - 64 + 16 * j + 4 * g + m;
+                const int kj = q0 - kHR + 16 * j + 4 * g + m;
                 const bool ok = kj >= 0 && kj <= qi && kj > qi - window;
                 s[j][m] = ok ? st[m] * sl2 : -INFINITY;
             }
         }
     }
-    // Row max over all 80 keys: this lane's 20, then across the 4 lane groups.
+    // Row max over all keys: this lane's, then across the 4 lane groups.
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 5; ++j)
+    for (int j = 0; j < kKT; ++j)
 #pragma unroll
         for (int m = 0; m < 4; ++m) mx = fmaxf(mx, s[j][m]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     l = 0.f;
 #pragma unroll
-    for (int j = 0; j < 5; ++j)
+    for (int j = 0; j < kKT; ++j)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             // hardware 2^x: masked keys give 2^-inf = 0; arguments below -126
@@ -252,27 +262,28 @@ __device__ __forceinline__ void swa_tile(const SwaSlots& sl, int t, int window, 
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
 
-    // Y = P V over 3 k-steps of 32 keys (tiles 2p, 2p+1; tile 5 is empty).
+    // Y = P V over 2*HALO + 1 k-steps of 32 keys (tiles 2p, 2p+1; the last
+    // k-step has only tile 4*HALO).
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) yacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
+    for (int p = 0; p <= 2 * HALO; ++p) {
         float a[8];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             a[m] = s[2 * p][m];
-            a[4 + m] = 2 * p + 1 < 5 ? s[(2 * p + 1 < 5) ? 2 * p + 1 : 0][m] : 0.f;
+            a[4 + m] = 2 * p + 1 < kKT ? s[(2 * p + 1 < kKT) ? 2 * p + 1 : 0][m] : 0.f;
         }
         bf16x8 ahi, alo;
         pack8_hilo(a, ahi, alo);
         // key rows of this lane group: R1 + 4g .. +3 (tile 2p), R2 + 4g .. +3 (tile 2p+1)
         const int R1 = 16 * w + 32 * p, R2 = R1 + 16;
-        const uint16_t* v1 = R1 < 64 ? prev_v : cur_v;
-        const uint16_t* v2 = R2 < 64 ? prev_v : cur_v;
+        const uint16_t* v1 = pick_slot(sl.v, R1 >> 6);
+        const uint16_t* v2 = pick_slot(sl.v, R2 >> 6);
         const int r1 = (R1 & 63) + 4 * g, r2 = (R2 & 63) + 4 * g;
         bf16x8 vb[4];
-        // k-step 2 has no second key tile: that half of the operand is zero
-        if (p < 2) v_kstep<true>(v1, r1, v2, r2, r, vb);
+        // the last k-step has no second key tile: that half of the operand is zero
+        if (p < 2 * HALO) v_kstep<true>(v1, r1, v2, r2, r, vb);
         else v_kstep<false>(v1, r1, v2, r2, r, vb);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) yacc[ct] = mfma32(ahi, vb[ct], yacc[ct]);
@@ -311,18 +322,22 @@ __device__ __forceinline__ void raw_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int DQK, bool ADD>
+template <int DQK, bool ADD, int HALO>
 __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v, int L, int ntiles,
                                                        int tiles_per_wg, int wg_per_head, int window, float scale,
                                                        const float* add, float* y) {
-    // K/V ring: tile tb - 1 + j lives in slot j mod 3; Q of tile tb + j in slot j mod 2.
-    __shared__ alignas(16) uint16_t k0[kQT * DQK], k1[kQT * DQK], k2[kQT * DQK];
-    __shared__ alignas(16) uint16_t v0[kQT * kDV], v1[kQT * kDV], v2[kQT * kDV];
+    // K/V ring of HALO + 2 slots: tile tb - HALO + j lives in slot j mod
+    // (HALO + 2); Q of tile tb + j in slot j mod 2.  (The fourth slot is a
+    // placeholder when HALO = 1.)
+    constexpr int kNS = HALO + 2;
+    constexpr int kS3K = HALO == 2 ? kQT * DQK : 8, kS3V = HALO == 2 ? kQT * kDV : 8;
+    __shared__ alignas(16) uint16_t k0[kQT * DQK], k1[kQT * DQK], k2[kQT * DQK], k3[kS3K];
+    __shared__ alignas(16) uint16_t v0[kQT * kDV], v1[kQT * kDV], v2[kQT * kDV], v3[kS3V];
     __shared__ alignas(16) uint16_t q0s[kQT * DQK], q1s[kQT * DQK];
-    uint16_t* const ks[3] = {k0, k1, k2};
-    uint16_t* const vs[3] = {v0, v1, v2};
+    uint16_t* const ks[4] = {k0, k1, k2, k3};
+    uint16_t* const vs[4] = {v0, v1, v2, v3};
     uint16_t* const qs[2] = {q0s, q1s};
 
     const int head = blockIdx.x / wg_per_head;
@@ -345,12 +360,14 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
         ADD ? (void*)(add + (size_t)head * L * kDV) : (void*)y, (short)0, ADD ? head_bytes : 0, 0x00020000);
     const float sl2 = scale * kLog2e;
 
-    // Prologue: halo tile tb-1 (K, V) into slot 0 and tile tb into slot 1;
-    // add of tile tb.  The vector-memory counter retires in issue order, so
-    // waiting until only the 16 add loads remain means every copy landed.
+    // Prologue: halo tiles tb-HALO .. tb-1 (K, V) into slots 0 .. HALO-1 and
+    // tile tb into slot HALO; add of tile tb.  The vector-memory counter
+    // retires in issue order, so waiting until only the 16 add loads remain
+    // means every copy landed.
     float adda[16], addb[16];
-    dma_tile<DQK>(qh, kh, vh, L, tb - 1, k0, v0, nullptr, false, w, lane);
-    dma_tile<DQK>(qh, kh, vh, L, tb, k1, v1, q0s, true, w, lane);
+#pragma unroll
+    for (int h = 0; h < HALO; ++h) dma_tile<DQK>(qh, kh, vh, L, tb - HALO + h, ks[h], vs[h], nullptr, false, w, lane);
+    dma_tile<DQK>(qh, kh, vh, L, tb, ks[HALO], vs[HALO], q0s, true, w, lane);
     if (ADD) {
         load_add(ra, tb * kQT + 16 * w, g, r, adda);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
@@ -365,14 +382,15 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
     // stores issued after them may stay in flight -- before the barrier.
     auto step = [&](auto J, int t, const float (&cur_add)[16], float (&next_add)[16]) {
         constexpr int j = decltype(J)::value;
-        SwaSlots sl;
-        sl.kp = ks[j % 3];
-        sl.kc = ks[(j + 1) % 3];
-        sl.vp = vs[j % 3];
-        sl.vc = vs[(j + 1) % 3];
+        SwaSlots<HALO> sl;
+#pragma unroll
+        for (int h = 0; h <= HALO; ++h) {
+            sl.k[h] = ks[(j + h) % kNS];
+            sl.v[h] = vs[(j + h) % kNS];
+        }
         sl.qc = qs[j % 2];
-        sl.kn = ks[(j + 2) % 3];
-        sl.vn = vs[(j + 2) % 3];
+        sl.kn = ks[(j + HALO + 1) % kNS];
+        sl.vn = vs[(j + HALO + 1) % kNS];
         sl.qn = qs[(j + 1) % 2];
         if (t + 1 < te) {
             dma_tile<DQK>(qh, kh, vh, L, t + 1, sl.kn, sl.vn, sl.qn, true, w, lane);
@@ -380,7 +398,7 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
         }
         f32x4 yacc[4];
         float l;
-        swa_tile<DQK>(sl, t, window, sl2, w, g, r, yacc, l);
+        swa_tile<DQK, HALO>(sl, t, window, sl2, w, g, r, yacc, l);
         const int q0 = t * kQT + 16 * w;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -401,9 +419,11 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
     using I3 = std::integral_constant<int, 3>;
     using I4 = std::integral_constant<int, 4>;
     using I5 = std::integral_constant<int, 5>;
-    // Six steps per iteration (slot indices repeat every 6 tiles), nested so
-    // that each step follows exactly one other in the control flow.
-    for (int t = tb; t < te; t += 6) {
+    // Slot indices repeat every lcm(HALO + 2, 2) tiles: 6 steps per
+    // iteration for HALO = 1, 4 for HALO = 2, nested so that each step
+    // follows exactly one other in the control flow.
+    constexpr int kPeriod = HALO == 1 ? 6 : 4;
+    for (int t = tb; t < te; t += kPeriod) {
         step(I0{}, t, adda, addb);
         if (t + 1 < te) {
             step(I1{}, t + 1, addb, adda);
@@ -411,14 +431,27 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
                 step(I2{}, t + 2, adda, addb);
                 if (t + 3 < te) {
                     step(I3{}, t + 3, addb, adda);
-                    if (t + 4 < te) {
-                        step(I4{}, t + 4, adda, addb);
-                        if (t + 5 < te) step(I5{}, t + 5, addb, adda);
+                    if constexpr (kPeriod == 6) {
+                        if (t + 4 < te) {
+                            step(I4{}, t + 4, adda, addb);
+                            if (t + 5 < te) step(I5{}, t + 5, addb, adda);
+                        }
                     }
                 }
             }
         }
     }
+}
+
+template <int DQK, bool ADD>
+void launch_halo(int halo, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const uint16_t* v, int L,
+                 int ntiles, int tpw, int wg_per_head, int window, float scale, const float* add, float* y) {
+    if (halo == 1)
+        hipLaunchKernelGGL((swa_mfma_kernel<DQK, ADD, 1>), grid, dim3(256), 0, st, q, k, v, L, ntiles, tpw,
+                           wg_per_head, window, scale, add, y);
+    else
+        hipLaunchKernelGGL((swa_mfma_kernel<DQK, ADD, 2>), grid, dim3(256), 0, st, q, k, v, L, ntiles, tpw,
+                           wg_per_head, window, scale, add, y);
 }
 
 }  // namespace
@@ -431,23 +464,16 @@ hipError_t launch_swa_mfma(const void* q, const void* k, const void* v, int BH, 
     const int tpw = max(1, min(16, (BH * ntiles + 511) / 512));
     const int wg_per_head = (ntiles + tpw - 1) / tpw;
     const dim3 grid(BH * wg_per_head);
+    const int halo = window > kQT ? 2 : 1;  // key tiles of 64 before the query tile
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     const uint16_t* vv = static_cast<const uint16_t*>(v);
     if (dqk == 16) {
-        if (add)
-            hipLaunchKernelGGL((swa_mfma_kernel<16, true>), grid, dim3(256), 0, st, qq, kk, vv, L, ntiles, tpw,
-                               wg_per_head, window, scale, add, y);
-        else
-            hipLaunchKernelGGL((swa_mfma_kernel<16, false>), grid, dim3(256), 0, st, qq, kk, vv, L, ntiles, tpw,
-                               wg_per_head, window, scale, add, y);
+        if (add) launch_halo<16, true>(halo, grid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
+        else launch_halo<16, false>(halo, grid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
     } else {
-        if (add)
-            hipLaunchKernelGGL((swa_mfma_kernel<64, true>), grid, dim3(256), 0, st, qq, kk, vv, L, ntiles, tpw,
-                               wg_per_head, window, scale, add, y);
-        else
-            hipLaunchKernelGGL((swa_mfma_kernel<64, false>), grid, dim3(256), 0, st, qq, kk, vv, L, ntiles, tpw,
-                               wg_per_head, window, scale, add, y);
+        if (add) launch_halo<64, true>(halo, grid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
+        else launch_halo<64, false>(halo, grid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
     }
     return hipGetLastError();
 }

@@ -1,7 +1,7 @@
 // swa_valu.hip -- causal sliding-window softmax attention on the vector ALUs
 // in fp32 (gfx950): the exact-precision path for fp32 inputs, and for bf16
-// heads too long for the 32-bit offsets of the MFMA kernel in swa_mfma.hip
-// or windows over 64 keys (up to 128).
+// heads too long for the 32-bit offsets of the MFMA kernel in swa_mfma.hip;
+// windows up to 128 keys.
 //
 // "Simple linear attention language models balance the recall-throughput
 // tradeoff", s4 "Local Exact Attention": each query attends with exact

@@ -275,8 +275,8 @@ def test_swa_add_modes():
     assert torch.equal(y_inplace, y_add)
 
 
-@pytest.mark.parametrize("dqk,add", [(64, False), (16, True)])
-def test_swa_long_runs(dqk, add):
+@pytest.mark.parametrize("dqk,add,window", [(64, False, 64), (16, True, 64), (64, True, 128), (16, False, 100)])
+def test_swa_long_runs(dqk, add, window):
     """Many 64-query tiles per workgroup (B*H=128, 38 tiles a head: runs of
     10 tiles, the last one 8, ending in a ragged tile), so every slot
     rotation of the K/V/Q ring is used; two launches must agree bit for bit."""
@@ -286,17 +286,17 @@ def test_swa_long_runs(dqk, add):
     qd, kd, vd = dev(q, k, v)
     base = torch.randn(B, H, L, 64, generator=torch.Generator().manual_seed(6)) if add else None
     scale = dqk ** -0.5
-    outs = [based.swa_forward(qd, kd, vd, window=64, scale=scale,
+    outs = [based.swa_forward(qd, kd, vd, window=window, scale=scale,
                               add=base.to(DEV) if add else None) for _ in range(2)]
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
     heads = _sample_heads(B, H, 4, 3)
     bi = [b for b, _ in heads]
     hi = [h for _, h in heads]
-    want = oracle.swa(q[bi, hi], k[bi, hi], v[bi, hi], 64, scale)
+    want = oracle.swa(q[bi, hi], k[bi, hi], v[bi, hi], window, scale)
     if add:
         want = want + base[bi, hi].double().numpy()
-    report(f"swa long runs dqk={dqk} add={add} (4 sampled heads)", ratio(outs[0][bi, hi], want), 2e-2)
+    report(f"swa long runs dqk={dqk} add={add} w={window} (4 sampled heads)", ratio(outs[0][bi, hi], want), 2e-2)
 
 
 @pytest.mark.parametrize("L", [2**23 - 37, 2**23 + 29])
