@@ -55,6 +55,7 @@ def _load():
         lib.oracle_decode_step.argtypes = [P, P, P, I, I, I, D, P, P, P]
         lib.oracle_swa.argtypes = [P, P, P, I, I, I, I, I, D, P]
         lib.oracle_swa_cache_fill.argtypes = [P, P, I, I, I, I, I, P, P]
+        lib.oracle_la_backward.argtypes = [P, P, P, P, I, I, I, I, D, P, P, P]
         lib.oracle_swa_decode_step.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_longlong), I, I, I, I, D,
                                                P, P, P]
         _lib = lib
@@ -193,3 +194,18 @@ def swa_decode_step(q, k, v, k_cache, v_cache, pos, window: int = 64, scale: flo
                                    pos.ctypes.data_as(ctypes.POINTER(ctypes.c_longlong)),
                                    B * H, dqk, dv, int(window), float(scale), _ptr(kc), _ptr(vc), _ptr(y))
     return y, kc, vc
+
+
+def la_backward(q, k, v, dy, eps: float = 1e-6):
+    """Gradients (dq, dk, dv) of la_quadratic(q, k, v, eps) for the upstream
+    gradient dy (shapes as the inputs and the output)."""
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    *lead, L, d = q.shape
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dvo = np.empty_like(v)
+    _load().oracle_la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dy), BH, L, d, dv, eps, _ptr(dq), _ptr(dk), _ptr(dvo))
+    return dq, dk, dvo
+

@@ -228,3 +228,70 @@ void oracle_swa_decode_step(const double *q, const double *k, const double *v,
     }
     free(logit);
 }
+
+/* Gradients of the causal Taylor linear attention output for an upstream
+ * gradient dy (training-mode prefill: [BASED s5] notes prefill also serves
+ * training).  The chain rule through the closed form
+ *   y_i = N_i / D_i,  N_i = sum_{j<=i} a_ij v_j,  D_i = sum_{j<=i} a_ij + eps,
+ *   a_ij = 1 + s_ij + s_ij^2 / 2,  s_ij = q_i . k_j / sqrt(d):
+ *   gN_i = dy_i / D_i,  gD_i = -(dy_i . y_i) / D_i,
+ *   ga_ij = gN_i . v_j + gD_i,  gs_ij = ga_ij (1 + s_ij),
+ *   dq_i = sum_{j<=i} gs_ij k_j / sqrt(d),  dk_j = sum_{i>=j} gs_ij q_i / sqrt(d),
+ *   dv_j = sum_{i>=j} a_ij gN_i.
+ * O(L^2) per head; q,k [BH,L,d], v,dy [BH,L,dv]. */
+void oracle_la_backward(const double *q, const double *k, const double *v, const double *dy,
+                        int BH, int L, int d, int dv, double eps,
+                        double *dq, double *dk, double *dv_out) {
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < BH; ++h) {
+        const double *qh = q + (size_t)h * L * d;
+        const double *kh = k + (size_t)h * L * d;
+        const double *vh = v + (size_t)h * L * dv;
+        const double *dyh = dy + (size_t)h * L * dv;
+        double *dqh = dq + (size_t)h * L * d;
+        double *dkh = dk + (size_t)h * L * d;
+        double *dvh = dv_out + (size_t)h * L * dv;
+        double *gN = (double *)malloc(sizeof(double) * (size_t)L * dv);
+        double *gD = (double *)malloc(sizeof(double) * (size_t)L);
+        double *num = (double *)malloc(sizeof(double) * dv);
+        for (int i = 0; i < L; ++i) {  /* forward values and the gradients of N_i, D_i */
+            double Di = eps;
+            for (int c = 0; c < dv; ++c) num[c] = 0.0;
+            for (int j = 0; j < i + 1; ++j) {  /* keys up to and including i */
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e) dot += qh[(size_t)i * d + e] * kh[(size_t)j * d + e];
+                const double sij = dot * inv_sqrt_d;
+                const double aij = 1.0 + sij + 0.5 * sij * sij;
+                Di += aij;
+                for (int c = 0; c < dv; ++c) num[c] += aij * vh[(size_t)j * dv + c];
+            }
+            double dy_dot_y = 0.0;
+            for (int c = 0; c < dv; ++c) {
+                gN[(size_t)i * dv + c] = dyh[(size_t)i * dv + c] / Di;
+                dy_dot_y += dyh[(size_t)i * dv + c] * (num[c] / Di);
+            }
+            gD[i] = -dy_dot_y / Di;
+        }
+        for (size_t e = 0; e < (size_t)L * d; ++e) dqh[e] = dkh[e] = 0.0;
+        for (size_t e = 0; e < (size_t)L * dv; ++e) dvh[e] = 0.0;
+        for (int i = 0; i < L; ++i) {
+            for (int j = i; j >= 0; --j) {  /* the same keys, any order */
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e) dot += qh[(size_t)i * d + e] * kh[(size_t)j * d + e];
+                const double sij = dot * inv_sqrt_d;
+                const double aij = 1.0 + sij + 0.5 * sij * sij;
+                double ga = gD[i];
+                for (int c = 0; c < dv; ++c) ga += gN[(size_t)i * dv + c] * vh[(size_t)j * dv + c];
+                const double gs = ga * (1.0 + sij) * inv_sqrt_d;
+                for (int e = 0; e < d; ++e) {
+                    dqh[(size_t)i * d + e] += gs * kh[(size_t)j * d + e];
+                    dkh[(size_t)j * d + e] += gs * qh[(size_t)i * d + e];
+                }
+                for (int c = 0; c < dv; ++c) dvh[(size_t)j * dv + c] += aij * gN[(size_t)i * dv + c];
+            }
+        }
+        free(gN); free(gD); free(num);
+    }
+}
+

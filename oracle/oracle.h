@@ -98,6 +98,13 @@ void oracle_swa_decode_step(const double *q, const double *k, const double *v,
                             const long long *pos, int BH, int dqk, int dv, int window,
                             double scale, double *kc, double *vc, double *y);
 
+/* Gradients of la_quadratic's output for an upstream gradient dy (chain
+ * rule through the closed form; O(L^2) per head).  q,k,dq,dk [BH,L,d];
+ * v,dy,dv [BH,L,dv]. */
+void oracle_la_backward(const double *q, const double *k, const double *v, const double *dy,
+                        int BH, int L, int d, int dv, double eps,
+                        double *dq, double *dk, double *dv_out);
+
 /* Number of OpenMP threads the routines above use. */
 int oracle_num_threads(void);
 

@@ -38,6 +38,13 @@ MUTANTS = {
                           "kh[(size_t)slot * dqk + e] = kh[(size_t)slot * dqk + e];"),
     "fill_wrong_slot": ("const int slot = p % window;", "const int slot = (p + 1) % window;"),
     "ring_no_exp": ("const double e = exp(logit[jj] - m);", "const double e = 1.0 + logit[jj] - m;"),
+    "bwd_no_linear_term": ("const double gs = ga * (1.0 + sij) * inv_sqrt_d;", "const double gs = ga * sij * inv_sqrt_d;"),
+    "bwd_denominator_sign": ("gD[i] = -dy_dot_y / Di;", "gD[i] = dy_dot_y / Di;"),
+    "bwd_dv_unweighted": ("dvh[(size_t)j * dv + c] += aij * gN[(size_t)i * dv + c];",
+                          "dvh[(size_t)j * dv + c] += gN[(size_t)i * dv + c];"),
+    "bwd_exclusive_causal": ("for (int j = i; j >= 0; --j) {", "for (int j = i - 1; j >= 0; --j) {"),
+    "bwd_dk_from_key": ("dkh[(size_t)j * d + e] += gs * qh[(size_t)i * d + e];",
+                        "dkh[(size_t)j * d + e] += gs * kh[(size_t)i * d + e];"),
 }
 
 # pins that take only the oracle module
@@ -55,6 +62,8 @@ PIN_FUNCS = [
     pins.test_p7_small_logits_approach_softmax,
     lambda m: pins.test_p8_window_decode_continues_window(m, 7, 30),
     lambda m: pins.test_p8_window_decode_continues_window(m, 64, 10),
+    lambda m: pins.test_p9_backward_matches_autograd(m, 16, 37, 8),
+    pins.test_p9_backward_finite_differences,
     pins.test_hand_taylor_cases,
     pins.test_hand_window_cases,
 ]

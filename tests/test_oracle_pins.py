@@ -18,6 +18,8 @@ Which pin guards which part of the oracle:
   P7  small-logit limit: linear attention -> softmax attention
   P8  window decode: ring cache filled from a prefix plus next-token steps
       equals the library's band-masked softmax attention at each position
+  P9  gradients: torch autograd through a plain fp64 forward, and central
+      finite differences of the oracle's own forward
   hand hand-worked rational cases in tests/golden/hand_cases.json
 """
 import json
@@ -311,6 +313,56 @@ def test_p8_window_decode_continues_window(oracle_mod, window, L):
         pick = lambda x: np.stack([x[b, :, pos[b]] for b in range(B)])
         y, kc, vc = oracle_mod.swa_decode_step(pick(q), pick(k), pick(v), kc, vc, pos, window, scale)
         np.testing.assert_allclose(y, pick(full), rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P9
+def _torch_forward(q, k, v, eps):
+    """The causal Taylor linear attention forward written with torch ops
+    (fp64), for autograd to differentiate."""
+    d = q.shape[-1]
+    s = (q @ k.transpose(-1, -2)) / math.sqrt(d)
+    a = (1 + s + 0.5 * s * s) * torch.tril(torch.ones(q.shape[-2], q.shape[-2], dtype=q.dtype))
+    return (a @ v) / (a.sum(-1, keepdim=True) + eps)
+
+
+@pytest.mark.parametrize("d,L,dv", [(16, 37, 8), (8, 20, 16), (16, 1, 4)])
+def test_p9_backward_matches_autograd(oracle_mod, d, L, dv):
+    rng = _rng(60 + d + L)
+    q = rng.standard_normal((2, 2, L, d))
+    k = rng.standard_normal((2, 2, L, d))
+    v = rng.standard_normal((2, 2, L, dv))
+    dy = rng.standard_normal((2, 2, L, dv))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    (_torch_forward(tq, tk, tv, 1e-6) * torch.from_numpy(dy)).sum().backward()
+    dq, dk, dv_ = oracle_mod.la_backward(q, k, v, dy)
+    for got, want in ((dq, tq.grad), (dk, tk.grad), (dv_, tv.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def test_p9_backward_finite_differences(oracle_mod):
+    """Central differences of sum(y * dy), y from the oracle's closed-form
+    forward, at random coordinates of q, k and v."""
+    rng = _rng(70)
+    L, d, dv = 23, 16, 6
+    q = rng.standard_normal((1, 1, L, d))
+    k = rng.standard_normal((1, 1, L, d))
+    v = rng.standard_normal((1, 1, L, dv))
+    dy = rng.standard_normal((1, 1, L, dv))
+    grads = dict(zip("qkv", oracle_mod.la_backward(q, k, v, dy)))
+    loss = lambda a, b, c: float((oracle_mod.la_quadratic(a, b, c) * dy).sum())
+    h = 1e-5
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        for _ in range(8):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = dict(q=q, k=k, v=v)
+            args_m = dict(q=q, k=k, v=v)
+            args_p[name], args_m[name] = xp, xm
+            fd = (loss(**{"a": args_p["q"], "b": args_p["k"], "c": args_p["v"]})
+                  - loss(**{"a": args_m["q"], "b": args_m["k"], "c": args_m["v"]})) / (2 * h)
+            assert abs(fd - grads[name][idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grads[name][idx])
 
 
 # ---------------------------------------------------------------- P7
