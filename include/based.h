@@ -17,6 +17,8 @@
  *   swa_cache_fill,    the window's next-token step on a w-sized key/value
  *   swa_decode_step    ring cache (same section; App. B "Next Token
  *                      Prediction").
+ *   based_prefill_backward  gradients of the prefill output (training-mode
+ *                      prefill, s5).
  *
  * [1] "Simple linear attention language models balance the recall-throughput
  *     tradeoff" (arXiv 2402.18668v2).
@@ -203,6 +205,33 @@ based_status_t swa_decode_step(const void *q, const void *k, const void *v,
                                int window, float scale, const long long *pos,
                                void *k_cache, void *v_cache, const float *add,
                                float *y, void *stream);
+
+/*
+ * based_prefill_backward -- gradients of based_prefill's output y for an
+ * upstream gradient dy (training-mode prefill; [1] s5).  With
+ * s_ij = q_i.k_j/sqrt(d'), a_ij = 1 + s_ij + s_ij^2/2, y_i = N_i / D_i,
+ * N_i = sum_{j<=i} a_ij v_j, D_i = sum_{j<=i} a_ij + eps:
+ *   g_i = dy_i / D_i,  h_i = -(dy_i . y_i) / D_i,
+ *   e_ij = (g_i . v_j + h_i)(1 + s_ij) / sqrt(d'),
+ *   dq_i = sum_{j<=i} e_ij k_j,  dk_j = sum_{i>=j} e_ij q_i,
+ *   dv_j = sum_{i>=j} a_ij g_i
+ * (starting from a zero state; no gradient of an initial state).
+ *
+ *   q, k  [B,H,L,d_feat] dtype;  v [B,H,L,d_v] dtype
+ *   dy    [B,H,L,d_v] fp32
+ *   dq, dk [B,H,L,d_feat] fp32 out;  dv [B,H,L,d_v] fp32 out
+ *   workspace  required, at least based_prefill_backward_workspace_bytes
+ *          (else BASED_E_INVALID); must not overlap anything else
+ * Supported: d_feat in {8, 16, 24, 32}; d_v in {64, 128}.  Computed in fp32
+ * on the vector ALUs in the direct form (O(L^2) work per head).
+ */
+size_t based_prefill_backward_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
+
+based_status_t based_prefill_backward(const void *q, const void *k, const void *v,
+                                      const float *dy, based_dtype_t dtype, int B, int H,
+                                      int L, int d_feat, int d_v, float eps, float *dq,
+                                      float *dk, float *dv, void *workspace,
+                                      size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,7 @@ HIP kernels of libbased.so; nothing here computes.
     swa_forward(q, k, v, window=64)   -> y             sliding-window softmax
     swa_cache_fill(k, v, window=64)   -> (kc, vc)      window key/value ring from a prefix
     swa_decode_step(q, k, v, kc, vc, pos) -> y         window next-token step (kc, vc in place)
+    based_prefill_backward(q, k, v, dy) -> (dq, dk, dv) gradients of based_prefill's output
 """
 from __future__ import annotations
 
@@ -19,6 +20,7 @@ import torch
 from . import _lib
 
 __all__ = ["based_prefill", "based_decode_step", "swa_forward", "swa_cache_fill", "swa_decode_step",
+           "based_prefill_backward",
            "based_num_features", "based_prefill_workspace_bytes", "BasedError", "library_path"]
 
 BasedError = _lib.BasedError
@@ -214,4 +216,35 @@ def swa_decode_step(q, k, v, k_cache, v_cache, pos, *, scale: float | None = Non
                                     _stream_ptr(q.device))
     _lib.check("swa_decode_step", st)
     return y
+
+
+def based_prefill_backward(q, k, v, dy, *, eps: float = 1e-6, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv), fp32, of based_prefill's output y for the
+    upstream gradient dy [B,H,L,d_v] (fp32), from a zero initial state."""
+    _check_tensor("q", q, ndim=4)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor("k", k, dt, 4)
+    _check_tensor("v", v, dt, 4)
+    _check_tensor("dy", dy, torch.float32, 4)
+    B, H, L, d = q.shape
+    d_v = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != (B, H, L) or dy.shape != v.shape:
+        raise ValueError("shape mismatch")
+    dev = q.device
+    dq = torch.empty((B, H, L, d), dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty((B, H, L, d), dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, torch.float32)
+    if workspace is None:
+        nbytes = _lib.lib().based_prefill_backward_workspace_bytes(B, H, L, d, d_v)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    st = _lib.lib().based_prefill_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(), _DTYPES[dt], B,
+                                           H, L, d, d_v, eps, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                           _stream_ptr(dev))
+    _lib.check("based_prefill_backward", st)
+    return dq, dk, dv
 

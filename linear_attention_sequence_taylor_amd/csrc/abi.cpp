@@ -236,3 +236,43 @@ BASED_API based_status_t swa_decode_step(const void* q, const void* k, const voi
                                                        static_cast<hipStream_t>(stream)));
 }
 
+BASED_API size_t based_prefill_backward_workspace_bytes(int B, int H, int L, int d_feat, int d_v) {
+    uint64_t BH, BHL;
+    if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return 0;
+    if (!feat_dim_ok(d_feat) || (d_v != 64 && d_v != 128)) return 0;
+    return based::prefill_backward_workspace_bytes((int)BH, L, d_v);
+}
+
+BASED_API based_status_t based_prefill_backward(const void* q, const void* k, const void* v, const float* dy,
+                                                based_dtype_t dtype, int B, int H, int L, int d_feat, int d_v,
+                                                float eps, float* dq, float* dk, float* dv, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+    if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_E_INVALID;
+    if (!q || !k || !v || !dy || !dq || !dk || !dv || !workspace) return BASED_E_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dy) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv) || !aligned16(workspace))
+        return BASED_E_INVALID;
+    if (!isfinite(eps) || d_feat < 1 || d_v < 1) return BASED_E_INVALID;
+    uint64_t BH, BHL;
+    if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
+    if (!feat_dim_ok(d_feat) || (d_v != 64 && d_v != 128)) return BASED_E_UNSUPPORTED;
+    const uint64_t ws_need = based::prefill_backward_workspace_bytes((int)BH, L, d_v);
+    if (workspace_bytes < ws_need) return BASED_E_INVALID;
+    const uint64_t es = elem_size(dtype);
+    const uint64_t qk_bytes = BHL * d_feat * es, v_bytes = BHL * d_v * es;
+    const uint64_t dqk_bytes = BHL * d_feat * 4, dv_bytes = BHL * d_v * 4;
+    const void* outs[4] = {dq, dk, dv, workspace};
+    const uint64_t out_bytes[4] = {dqk_bytes, dqk_bytes, dv_bytes, ws_need};
+    const void* ins[4] = {q, k, v, dy};
+    const uint64_t in_bytes[4] = {qk_bytes, qk_bytes, v_bytes, dv_bytes};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return BASED_E_INVALID;
+        for (int b = 0; b < 4; ++b)
+            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return BASED_E_INVALID;
+    }
+    return launch_status(based::launch_prefill_backward(q, k, v, dy, dtype == BASED_BF16, (int)BH, L, d_feat, d_v,
+                                                        eps, dq, dk, dv, workspace,
+                                                        static_cast<hipStream_t>(stream)));
+}
+

@@ -45,4 +45,11 @@ hipError_t launch_swa_decode_step(const void* q, const void* k, const void* v, b
 hipError_t launch_swa_cache_fill(const void* k, const void* v, bool bf16, int BH, int L, int dqk, int dv,
                                  int window, void* kc, void* vc, hipStream_t st);
 
+// Gradients of the prefill output (prefill_backward.hip), fp32 on the vector
+// ALUs; the workspace holds BH*L*(dv+1) floats.
+size_t prefill_backward_workspace_bytes(int BH, int L, int dv);
+hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, const float* dy, bool bf16, int BH,
+                                   int L, int d, int dv_dim, float eps, float* dq, float* dk, float* dv,
+                                   void* workspace, hipStream_t st);
+
 }  // namespace based

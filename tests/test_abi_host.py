@@ -40,6 +40,7 @@ def lib():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for want in ("based_prefill", "based_decode_step", "swa_forward", "swa_cache_fill", "swa_decode_step",
+                 "based_prefill_backward", "based_prefill_backward_workspace_bytes",
                  "based_num_features", "based_prefill_workspace_bytes", "based_status_string"):
         assert want in names, names
 
@@ -165,6 +166,29 @@ def _swa_fill(lib, **kw):
 ])
 def test_swa_fill_rejects(lib, kw, want):
     assert _swa_fill(lib, **kw) == want
+
+
+def _bwd(lib, **kw):
+    a = dict(q=A, k=B_, v=C, dy=Y, dtype=1, B=1, H=2, L=100, d=16, dv=64, eps=1e-6, dq=S, dk=S + (1 << 20),
+             dvo=S + (2 << 20), ws=Z, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.based_prefill_backward(a["q"], a["k"], a["v"], a["dy"], a["dtype"], a["B"], a["H"], a["L"], a["d"],
+                                      a["dv"], a["eps"], a["dq"], a["dk"], a["dvo"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), 1), (dict(dy=None), 1), (dict(ws=None), 1), (dict(dq=S + 4), 1), (dict(wsb=100), 1),
+    (dict(dtype=5), 1), (dict(L=0), 1), (dict(eps=float("nan")), 1), (dict(d=12), 2), (dict(dv=32), 2),
+    (dict(dq=A), 1), (dict(dk=S), 1), (dict(ws=S + (2 << 20)), 1), (dict(dvo=Y), 1),
+])
+def test_backward_rejects(lib, kw, want):
+    assert _bwd(lib, **kw) == want
+
+
+def test_backward_workspace_bytes(lib):
+    assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 16, 64) == 2 * 3 * 100 * 65 * 4
+    assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 12, 64) == 0
+    assert lib.based_prefill_backward_workspace_bytes(0, 3, 100, 16, 64) == 0
 
 
 def test_product_never_imports_oracle():

@@ -365,6 +365,59 @@ def test_swa_wide_windows(dtype, tol, dqk, window, L):
     report(f"swa {dtype} dqk={dqk} w={window} L={L}", ratio(y, oracle.swa(q, k, v, window, scale)), tol)
 
 
+# ---------------------------------------------------------------- backward
+@pytest.mark.parametrize("dtype,tol,B,H,L,d,dv", [
+    (torch.bfloat16, 2e-2, 1, 2, 130, 16, 64), (torch.float32, 1e-4, 1, 2, 130, 16, 64),
+    (torch.float32, 1e-4, 1, 2, 70, 32, 128), (torch.bfloat16, 2e-2, 2, 1, 257, 8, 64),
+    (torch.bfloat16, 2e-2, 1, 3, 33, 24, 128),
+])
+def test_backward_matches_oracle(dtype, tol, B, H, L, d, dv):
+    """dq, dk, dv of the prefill output for a seeded upstream gradient, against
+    the oracle's chain rule (itself pinned to autograd and finite differences)."""
+    based = based_mod()
+    q, k, v = si.custom((B, H, L, d), (B, H, L, dv), seed=2200 + L + d + dv, scale=0.5, dtype=dtype)
+    dy = torch.randn(B, H, L, dv, generator=torch.Generator().manual_seed(2201 + L))
+    dq, dk, dv_ = based.based_prefill_backward(*dev(q, k, v), dy.to(DEV))
+    torch.cuda.synchronize()
+    oq, ok, ov = oracle.la_backward(q, k, v, dy)
+    report(f"backward {dtype} L={L} d={d} dv={dv} dq", ratio(dq, oq), tol)
+    report(f"backward {dtype} L={L} d={d} dv={dv} dk", ratio(dk, ok), tol)
+    report(f"backward {dtype} L={L} d={d} dv={dv} dv", ratio(dv_, ov), tol)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_single_token(dtype):
+    """L = 1: y_0 = v_0 a/(a + eps), so dv_0 = dy_0 a/(a + eps) and dq, dk are
+    of order eps: they come out of the cancellation of terms of order
+    |dy||v|, and fp32 gives them to rounding noise of those terms."""
+    based = based_mod()
+    q, k, v = si.custom((2, 2, 1, 16), (2, 2, 1, 128), seed=2250, scale=1.0, dtype=dtype)
+    dy = torch.randn(2, 2, 1, 128, generator=torch.Generator().manual_seed(2251))
+    dq, dk, dv_ = based.based_prefill_backward(*dev(q, k, v), dy.to(DEV))
+    oq, ok, ov = oracle.la_backward(q, k, v, dy)
+    report(f"backward L=1 {dtype} dv", ratio(dv_, ov), 1e-4)
+    noise = 1e-5 * float(dy.norm(dim=-1).max() * v.float().norm(dim=-1).max() * k.float().norm(dim=-1).max())
+    assert float(dq.abs().max()) <= noise and float(dk.abs().max()) <= noise, (dq.abs().max(), dk.abs().max(), noise)
+    assert np.abs(oq).max() <= noise and np.abs(ok).max() <= noise
+
+
+def test_workload_prefill_360m_backward():
+    """Gradients over the 360M-shaped layer (B=8, H=16, L=2048), 2 sampled heads."""
+    based = based_mod()
+    wl = si.WORKLOADS["prefill_360m"]
+    q, k, v = si.linear_inputs(wl)
+    dy = torch.randn(wl.B, wl.H, wl.L, wl.dv, generator=torch.Generator().manual_seed(2300))
+    dq, dk, dv_ = based.based_prefill_backward(*dev(q, k, v), dy.to(DEV), eps=wl.eps)
+    torch.cuda.synchronize()
+    heads = _sample_heads(wl.B, wl.H, 2, 5)
+    bi = [b for b, _ in heads]
+    hi = [h for _, h in heads]
+    oq, ok, ov = oracle.la_backward(q[bi, hi], k[bi, hi], v[bi, hi], dy[bi, hi], eps=wl.eps)
+    report("prefill_360m backward dq (2 sampled heads)", ratio(dq[bi, hi], oq), wl.tol)
+    report("prefill_360m backward dk (2 sampled heads)", ratio(dk[bi, hi], ok), wl.tol)
+    report("prefill_360m backward dv (2 sampled heads)", ratio(dv_[bi, hi], ov), wl.tol)
+
+
 # ---------------------------------------------------------------- window decode
 def _nan_cache(B, H, window, d, dtype):
     return torch.full((B, H, window, d), float("nan"), dtype=dtype, device=DEV)
