@@ -41,6 +41,7 @@ import synthetic_inputs as si  # noqa: E402
 
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16
+FP32_VECTOR_PEAK = 157.3e12  # flop/s, fp32 vector (FMA = 2 flops)
 METRIC = "tokens/sec for Taylor lin-attn prefill & decode; % of HBM / MFMA peak"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "linear_attention_sequence_taylor_amd", "csrc")
@@ -346,6 +347,31 @@ def bench_other_sizes(based):
     return out
 
 
+def bench_backward(based, wl, reps=5):
+    """Gradients of the prefill output over the workload (fp32 vector ALUs,
+    direct form).  Returns (event seconds per call, executed flops): per
+    causal (i, j) pair 8d + 6d_v + 12 flops (scores twice, weights, g.v,
+    dq, dk, dv and N)."""
+    q, k, v = (x.cuda() for x in si.linear_inputs(wl))
+    dy = torch.randn(wl.B, wl.H, wl.L, wl.dv, device="cuda")
+    outs = (torch.empty(wl.B, wl.H, wl.L, wl.d, device="cuda"), torch.empty(wl.B, wl.H, wl.L, wl.d, device="cuda"),
+            torch.empty(wl.B, wl.H, wl.L, wl.dv, device="cuda"))
+    ws = torch.empty(based.based_prefill_backward_workspace_bytes(wl.B, wl.H, wl.L, wl.dv, wl.d), dtype=torch.uint8,
+                     device="cuda")
+    run = lambda: based.based_prefill_backward(q, k, v, dy, eps=wl.eps, dq=outs[0], dk=outs[1], dv=outs[2],
+                                               workspace=ws)
+    for _ in range(3):
+        run()
+    t = RegionTimer()
+    torch.cuda.synchronize()
+    t.start()
+    for _ in range(reps):
+        run()
+    t.stop()
+    pairs = wl.B * wl.H * wl.L * (wl.L + 1) // 2
+    return t.seconds() / reps, pairs * (8 * wl.d + 6 * wl.dv + 12)
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """Oracle recurrent form on whole heads of the workload, sized to about
     budget_s of host time (at most the full workload)."""
@@ -482,6 +508,12 @@ def main():
                                          "hbm_GBps": lb / lkern / 1e9, "hbm_frac": lb / lkern / HBM_PEAK,
                                          "mfma_frac": prefill_flops(wlong) / lkern / MFMA_BF16_PEAK}
             print(f"[bench] long prefill: {lkern*1e3:.3f} ms", file=sys.stderr, flush=True)
+        bsec, bflops = bench_backward(based, wl)
+        extra["prefill_360m_backward"] = {
+            "kernel_ms": bsec * 1e3, "tokens_per_s": wl.B * wl.L / bsec, "direct_form_flops": bflops,
+            "fp32_tflops": bflops / bsec / 1e12, "alu_frac": bflops / bsec / FP32_VECTOR_PEAK,
+            "note": "dq, dk, dv for a seeded dy; fp32 vector ALUs, direct form (O(L^2) per head)"}
+        print(f"[bench] backward: {bsec*1e3:.2f} ms, {bflops/bsec/1e12:.1f} TFLOP/s fp32", file=sys.stderr, flush=True)
         other = bench_other_sizes(based)
         extra.update(other)
         print("[bench] other sizes: " + ", ".join(f"{k} {v['kernel_us']:.1f} us" for k, v in other.items()),

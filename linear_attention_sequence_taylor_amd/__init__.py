@@ -20,7 +20,7 @@ import torch
 from . import _lib
 
 __all__ = ["based_prefill", "based_decode_step", "swa_forward", "swa_cache_fill", "swa_decode_step",
-           "based_prefill_backward",
+           "based_prefill_backward", "based_prefill_backward_workspace_bytes",
            "based_num_features", "based_prefill_workspace_bytes", "BasedError", "library_path"]
 
 BasedError = _lib.BasedError
@@ -53,6 +53,10 @@ def based_num_features(d_feat: int = D_FEAT) -> int:
 
 def based_prefill_workspace_bytes(B: int, H: int, L: int, d_v: int, d_feat: int = D_FEAT) -> int:
     return _lib.lib().based_prefill_workspace_bytes(B, H, L, d_feat, d_v)
+
+
+def based_prefill_backward_workspace_bytes(B: int, H: int, L: int, d_v: int, d_feat: int = D_FEAT) -> int:
+    return _lib.lib().based_prefill_backward_workspace_bytes(B, H, L, d_feat, d_v)
 
 
 def based_prefill(q, k, v, *, chunk: int = 64, eps: float = 1e-6, initial_state=None,
@@ -239,7 +243,7 @@ def based_prefill_backward(q, k, v, dy, *, eps: float = 1e-6, dq=None, dk=None, 
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _check_tensor(name, t, torch.float32)
     if workspace is None:
-        nbytes = _lib.lib().based_prefill_backward_workspace_bytes(B, H, L, d, d_v)
+        nbytes = based_prefill_backward_workspace_bytes(B, H, L, d_v, d)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     st = _lib.lib().based_prefill_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(), _DTYPES[dt], B,
                                            H, L, d, d_v, eps, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
