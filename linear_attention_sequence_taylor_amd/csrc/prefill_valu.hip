@@ -11,62 +11,71 @@
 // pairwise weight is the closed form phi(q).phi(k) = 1 + s + s^2/2 with
 // s = q.k/sqrt(d') (s4 "Taylor Linear Attention").
 //
-// One workgroup per (batch, head).  The caller's S and z buffers are the
-// working state (updated in place, L2-resident); this path is sized for
-// exactness, not speed.
+// One workgroup per (batch, head, group of 16 value columns), 256 threads.
+// The caller's S (those 16 columns) is the working state; z lives in LDS for
+// the whole sequence (each column group keeps its own copy) and a second
+// kernel writes the final z.  Per chunk, the state goes through LDS in blocks of 32 feature
+// rows: each block is read once, the chunk's readout uses it first (the
+// state before the chunk), then its update is written back.  The features
+// of the block's rows are formed once per block for every token of the
+// chunk (queries and keys) and shared through LDS.  Every feature dim of
+// the pages (8, 16, 24, 32) and every chunk (16, 32, 64) runs here.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace based {
 
-template <typename T, int C, int DV, int D>
-__global__ __launch_bounds__(256) void prefill_valu_kernel(const T* __restrict__ q,
-                                                           const T* __restrict__ k,
-                                                           const T* __restrict__ v, int L,
-                                                           float eps, float* __restrict__ y,
-                                                           float* __restrict__ S,
+constexpr int kCW = 16;  // value columns per workgroup
+constexpr int kFB = 32;  // feature rows per state block
+
+template <typename T, int C, int D>
+__global__ __launch_bounds__(256) void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                           const T* __restrict__ v, int L, int DV, float eps,
+                                                           float* __restrict__ y, float* __restrict__ S,
                                                            float* __restrict__ z, int use_init) {
-    constexpr int kTPT = 256 / C;   // threads per token
-    constexpr int kCPT = DV / kTPT; // columns per thread
     constexpr int kF = Feat<D>::kF;
+    constexpr int kTPT = 256 / C;     // threads per token
+    constexpr int kCPT = kCW / kTPT;  // value columns per thread
     __shared__ float s_q[C][D];
     __shared__ float s_k[C][D];
-    __shared__ float s_v[C][DV];
+    __shared__ float s_v[C][kCW];
+    __shared__ float s_z[kF];
+    __shared__ float s_phq[C][kFB + 1];  // features of the block's rows, per query
+    __shared__ float s_phk[kFB][C + 1];  // and per key
+    __shared__ float s_S[kFB][kCW];
 
-    const int head = blockIdx.x;
+    const int cg = blockIdx.x, head = blockIdx.y;
     const int tid = threadIdx.x;
+    const int c0 = cg * kCW;
     const T* qh = q + (size_t)head * L * D;
     const T* kh = k + (size_t)head * L * D;
-    const T* vh = v + (size_t)head * L * DV;
-    float* yh = y + (size_t)head * L * DV;
-    float* Sh = S + (size_t)head * kF * DV;
+    const T* vh = v + (size_t)head * L * DV + c0;
+    float* yh = y + (size_t)head * L * DV + c0;
+    float* Sh = S + (size_t)head * kF * DV + c0;
     float* zh = z + (size_t)head * kF;
 
-    if (!use_init) {
-        for (int e = tid; e < kF * DV; e += 256) Sh[e] = 0.f;
-        for (int f = tid; f < kF; f += 256) zh[f] = 0.f;
-    }
+    for (int f = tid; f < kF; f += 256) s_z[f] = use_init ? zh[f] : 0.f;
+    if (!use_init)
+        for (int e = tid; e < kF * kCW; e += 256) Sh[(size_t)(e / kCW) * DV + e % kCW] = 0.f;
 
-    const int ti = tid / kTPT;           // token within the chunk
-    const int cb = (tid % kTPT) * kCPT;  // first column of this thread
-
+    const int ti = tid / kTPT;                 // token of this thread in readouts
+    const int cb = (tid % kTPT) * kCPT;        // its first column (of the 16)
     for (int t0 = 0; t0 < L; t0 += C) {
         const int n = min(C, L - t0);
-        __syncthreads();  // state writes of the previous chunk are visible
+        __syncthreads();  // previous chunk (and the state zeroing) done
         for (int e = tid; e < C * D; e += 256) {
             const int t = e / D, a = e % D;
             const bool ok = t < n;
             s_q[t][a] = ok ? load_elem(qh, (size_t)(t0 + t) * D + a) * Feat<D>::kPre : 0.f;
             s_k[t][a] = ok ? load_elem(kh, (size_t)(t0 + t) * D + a) * Feat<D>::kPre : 0.f;
         }
-        for (int e = tid; e < C * DV; e += 256) {
-            const int t = e / DV, c = e % DV;
+        for (int e = tid; e < C * kCW; e += 256) {
+            const int t = e / kCW, c = e % kCW;
             s_v[t][c] = t < n ? load_elem(vh, (size_t)(t0 + t) * DV + c) : 0.f;
         }
         __syncthreads();
 
-        // Output of token ti: on-diagonal (masked closed-form weights) plus
-        // off-diagonal (phi(q) against the state of the earlier chunks).
+        // On-diagonal term: masked closed-form weights.
         float num[kCPT];
 #pragma unroll
         for (int c = 0; c < kCPT; ++c) num[c] = 0.f;
@@ -80,59 +89,121 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(const T* __restrict__
 #pragma unroll
             for (int c = 0; c < kCPT; ++c) num[c] = fmaf(w, s_v[j][cb + c], num[c]);
         }
-        for (int f = 0; f < kF; ++f) {
-            const float pf = taylor_feature<D>(s_q[ti], f);
-            den = fmaf(pf, zh[f], den);
+
+        // Off-diagonal term and state update, one block of feature rows at a
+        // time; the next block's state is loaded into registers while this
+        // one is processed (element e = tid + 256 i of a block: row e / 16,
+        // column e % 16).
+        constexpr int kSPer = kFB * kCW / 256;
+        float nxt[kSPer];
 #pragma unroll
-            for (int c = 0; c < kCPT; ++c) num[c] = fmaf(pf, Sh[(size_t)f * DV + cb + c], num[c]);
+        for (int i = 0; i < kSPer; ++i) {
+            const int e = tid + 256 * i, f = e / kCW, c = e % kCW;
+            nxt[i] = f < kF ? Sh[(size_t)f * DV + c] : 0.f;
+        }
+        for (int f0 = 0; f0 < kF; f0 += kFB) {
+            for (int e = tid; e < C * kFB; e += 256) {
+                const int t = e / kFB, f = e % kFB;
+                const bool ok = f0 + f < kF;
+                s_phq[t][f] = ok ? taylor_feature<D>(s_q[t], f0 + f) : 0.f;
+                s_phk[f][t] = ok && t < n ? taylor_feature<D>(s_k[t], f0 + f) : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < kSPer; ++i) {
+                const int e = tid + 256 * i;
+                s_S[e / kCW][e % kCW] = nxt[i];
+                const int fn = f0 + kFB + e / kCW;  // the same element of the next block
+                nxt[i] = fn < kF ? Sh[(size_t)fn * DV + e % kCW] : 0.f;
+            }
+            __syncthreads();
+            // readout with the state before this chunk
+#pragma unroll 4
+            for (int f = 0; f < kFB; ++f) {
+                const float pf = s_phq[ti][f];
+                den = fmaf(pf, f0 + f < kF ? s_z[f0 + f] : 0.f, den);
+#pragma unroll
+                for (int c = 0; c < kCPT; ++c) num[c] = fmaf(pf, s_S[f][cb + c], num[c]);
+            }
+            __syncthreads();
+            // update with this chunk's keys (t < n)
+            for (int e = tid; e < kFB * kCW; e += 256) {
+                const int f = e / kCW, c = e % kCW;
+                if (f0 + f < kF) {
+                    float acc = 0.f;
+                    for (int t = 0; t < n; ++t) acc = fmaf(s_phk[f][t], s_v[t][c], acc);
+                    Sh[(size_t)(f0 + f) * DV + c] = s_S[f][c] + acc;
+                }
+            }
+            if (tid < kFB && f0 + tid < kF) {
+                float acc = 0.f;
+                for (int t = 0; t < n; ++t) acc += s_phk[tid][t];
+                s_z[f0 + tid] += acc;
+            }
+            __syncthreads();
         }
         if (ti < n) {
 #pragma unroll
             for (int c = 0; c < kCPT; ++c) yh[(size_t)(t0 + ti) * DV + cb + c] = num[c] / (den + eps);
         }
-        __syncthreads();  // every readout used the state before this chunk
-
-        // State update with this chunk: S += phi(K)^T V, z += sum phi(K).
-        for (int e = tid; e < kF * DV; e += 256) {
-            const int f = e / DV, c = e % DV;
-            float acc = 0.f;
-            for (int t = 0; t < n; ++t) acc = fmaf(taylor_feature<D>(s_k[t], f), s_v[t][c], acc);
-            Sh[e] += acc;
-        }
-        for (int f = tid; f < kF; f += 256) {
-            float acc = 0.f;
-            for (int t = 0; t < n; ++t) acc += taylor_feature<D>(s_k[t], f);
-            zh[f] += acc;
-        }
     }
 }
 
-template <typename T, int DV, int D>
-static void launch_valu_dv(const T* q, const T* k, const T* v, int BH, int L, int chunk, float eps,
-                           float* y, float* S, float* z, int use_init, hipStream_t st) {
-    switch (chunk) {
-        case 16:
-            hipLaunchKernelGGL((prefill_valu_kernel<T, 16, DV, D>), dim3(BH), dim3(256), 0, st, q, k, v, L,
-                               eps, y, S, z, use_init);
-            break;
-        case 32:
-            hipLaunchKernelGGL((prefill_valu_kernel<T, 32, DV, D>), dim3(BH), dim3(256), 0, st, q, k, v, L,
-                               eps, y, S, z, use_init);
-            break;
-        default:
-            hipLaunchKernelGGL((prefill_valu_kernel<T, 64, DV, D>), dim3(BH), dim3(256), 0, st, q, k, v, L,
-                               eps, y, S, z, use_init);
-            break;
+// Final normaliser state z = z_init + sum_t phi(k_t), one workgroup per
+// head, launched after the main kernel: the column groups there only read
+// the caller's z (a group that starts late must still see the initial one).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prefill_valu_z_kernel(const T* __restrict__ k, int L, float* __restrict__ z,
+                                                             int use_init) {
+    constexpr int kF = Feat<D>::kF;
+    constexpr int kPer = (kF + 255) / 256;
+    __shared__ float s_k[64][D];
+    const int head = blockIdx.x, tid = threadIdx.x;
+    const T* kh = k + (size_t)head * L * D;
+    float* zh = z + (size_t)head * kF;
+    float acc[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
+    for (int t0 = 0; t0 < L; t0 += 64) {
+        const int n = min(64, L - t0);
+        __syncthreads();
+        for (int e = tid; e < 64 * D; e += 256) {
+            const int t = e / D, a = e % D;
+            s_k[t][a] = t < n ? load_elem(kh, (size_t)(t0 + t) * D + a) * Feat<D>::kPre : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int f = tid + 256 * i;
+            if (f < kF)
+                for (int t = 0; t < n; ++t) acc[i] += taylor_feature<D>(s_k[t], f);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int f = tid + 256 * i;
+        if (f < kF) zh[f] = (use_init ? zh[f] : 0.f) + acc[i];
     }
 }
 
 template <typename T, int D>
 static void launch_valu_d(const T* q, const T* k, const T* v, int BH, int L, int dv, int chunk, float eps,
                           float* y, float* S, float* z, int use_init, hipStream_t st) {
-    if (dv == 64)
-        launch_valu_dv<T, 64, D>(q, k, v, BH, L, chunk, eps, y, S, z, use_init, st);
-    else
-        launch_valu_dv<T, 128, D>(q, k, v, BH, L, chunk, eps, y, S, z, use_init, st);
+    const dim3 grid(dv / kCW, BH);
+    switch (chunk) {
+        case 16:
+            hipLaunchKernelGGL((prefill_valu_kernel<T, 16, D>), grid, dim3(256), 0, st, q, k, v, L, dv, eps, y, S, z,
+                               use_init);
+            break;
+        case 32:
+            hipLaunchKernelGGL((prefill_valu_kernel<T, 32, D>), grid, dim3(256), 0, st, q, k, v, L, dv, eps, y, S, z,
+                               use_init);
+            break;
+        default:
+            hipLaunchKernelGGL((prefill_valu_kernel<T, 64, D>), grid, dim3(256), 0, st, q, k, v, L, dv, eps, y, S, z,
+                               use_init);
+            break;
+    }
+    hipLaunchKernelGGL((prefill_valu_z_kernel<T, D>), dim3(BH), dim3(256), 0, st, k, L, z, use_init);
 }
 
 template <typename T>
