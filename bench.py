@@ -21,7 +21,9 @@ prints one JSON line with:
   a sample of whole heads of the same workload;
 * extra: the next-token step (1.3B-shaped decode, 1024 steps), the w=64
   window kernel with fused add, the window's next-token step on its ring
-  cache, and the 64K-token prefill, each with its own HBM roofline fraction.
+  cache, and the 64K-token prefill, each with its own HBM roofline fraction;
+  the gradients of the prefill over the same layer (matrix-core fraction);
+  and the other feature dims and window sizes.
 """
 from __future__ import annotations
 
@@ -41,7 +43,6 @@ import synthetic_inputs as si  # noqa: E402
 
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16
-FP32_VECTOR_PEAK = 157.3e12  # flop/s, fp32 vector (FMA = 2 flops)
 METRIC = "tokens/sec for Taylor lin-attn prefill & decode; % of HBM / MFMA peak"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "linear_attention_sequence_taylor_amd", "csrc")
@@ -348,10 +349,10 @@ def bench_other_sizes(based):
 
 
 def bench_backward(based, wl, reps=5):
-    """Gradients of the prefill output over the workload (fp32 vector ALUs,
-    direct form).  Returns (event seconds per call, executed flops): per
-    causal (i, j) pair 8d + 6d_v + 12 flops (scores twice, weights, g.v,
-    dq, dk, dv and N)."""
+    """Gradients of the prefill output over the workload (bf16 inputs with
+    feature dim 16: the matrix-core kernels, direct form).  Returns (event
+    seconds per call, algorithmic flops): per causal (i, j) pair
+    8d + 6d_v + 12 flops (scores twice, weights, g.v, dq, dk, dv and N)."""
     q, k, v = (x.cuda() for x in si.linear_inputs(wl))
     dy = torch.randn(wl.B, wl.H, wl.L, wl.dv, device="cuda")
     outs = (torch.empty(wl.B, wl.H, wl.L, wl.d, device="cuda"), torch.empty(wl.B, wl.H, wl.L, wl.d, device="cuda"),
@@ -511,9 +512,10 @@ def main():
         bsec, bflops = bench_backward(based, wl)
         extra["prefill_360m_backward"] = {
             "kernel_ms": bsec * 1e3, "tokens_per_s": wl.B * wl.L / bsec, "direct_form_flops": bflops,
-            "fp32_tflops": bflops / bsec / 1e12, "alu_frac": bflops / bsec / FP32_VECTOR_PEAK,
-            "note": "dq, dk, dv for a seeded dy; fp32 vector ALUs, direct form (O(L^2) per head)"}
-        print(f"[bench] backward: {bsec*1e3:.2f} ms, {bflops/bsec/1e12:.1f} TFLOP/s fp32", file=sys.stderr, flush=True)
+            "tflops": bflops / bsec / 1e12, "mfma_frac": bflops / bsec / MFMA_BF16_PEAK,
+            "note": "dq, dk, dv for a seeded dy; bf16 matrix cores (weights as bf16 hi/lo pairs, fp32 "
+                    "accumulation), direct form (O(L^2) per head)"}
+        print(f"[bench] backward: {bsec*1e3:.2f} ms, {bflops/bsec/1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
         other = bench_other_sizes(based)
         extra.update(other)
         print("[bench] other sizes: " + ", ".join(f"{k} {v['kernel_us']:.1f} us" for k, v in other.items()),

@@ -256,6 +256,9 @@ BASED_API based_status_t based_prefill_backward(const void* q, const void* k, co
     uint64_t BH, BHL;
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
     if (!feat_dim_ok(d_feat) || (d_v != 64 && d_v != 128)) return BASED_E_UNSUPPORTED;
+    // one workgroup of 256 threads per 64 rows of a head: the grid's thread
+    // count must fit 32 bits
+    if (BH * (((uint64_t)L + 63) / 64) * 256 > (uint64_t)INT32_MAX) return BASED_E_INVALID;
     const uint64_t ws_need = based::prefill_backward_workspace_bytes((int)BH, L, d_v);
     if (workspace_bytes < ws_need) return BASED_E_INVALID;
     const uint64_t es = elem_size(dtype);

@@ -48,6 +48,11 @@ hipError_t launch_swa_cache_fill(const void* k, const void* v, bool bf16, int BH
 // Gradients of the prefill output (prefill_backward.hip), fp32 on the vector
 // ALUs; the workspace holds BH*L*(dv+1) floats.
 size_t prefill_backward_workspace_bytes(int BH, int L, int dv);
+// The same on the matrix cores for bf16 inputs with feature dim 16
+// (prefill_backward_mfma.hip); g_ws / h_ws as above.
+hipError_t launch_prefill_backward_mfma(const void* q, const void* k, const void* v, const float* dy, int BH, int L,
+                                        int dv, float eps, float* dq, float* dk, float* dvo, float* g_ws,
+                                        float* h_ws, hipStream_t st);
 hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, const float* dy, bool bf16, int BH,
                                    int L, int d, int dv_dim, float eps, float* dq, float* dk, float* dv,
                                    void* workspace, hipStream_t st);

@@ -15,7 +15,9 @@
 // (every lane of a wave reads the same staged row, a broadcast):
 //   query side: N_i and D_i, then g_i and h_i (to the workspace) and dq_i;
 //   key side:   dk_j and dv_j from the queries at or after j.
-// This is the direct (quadratic) form: O(L^2) work per head.
+// This is the direct (quadratic) form: O(L^2) work per head.  bf16 inputs
+// with feature dim 16 take the matrix-core kernels of
+// prefill_backward_mfma.hip instead (same workspace layout).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,8 +34,9 @@ __global__ __launch_bounds__(kRows) void bwd_query_kernel(const T* __restrict__ 
                                                           float* __restrict__ g_ws, float* __restrict__ h_ws) {
     __shared__ float s_k[kTile][D];
     __shared__ float s_v[kTile][DV];
-    const int head = blockIdx.y;
-    const int i0 = blockIdx.x * kRows;
+    const int nb = (L + kRows - 1) / kRows;
+    const int head = blockIdx.x / nb;
+    const int i0 = (blockIdx.x % nb) * kRows;
     const int i = i0 + threadIdx.x;
     const bool live = i < L;
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
@@ -129,8 +132,9 @@ __global__ __launch_bounds__(kRows) void bwd_key_kernel(const T* __restrict__ q,
     __shared__ float s_q[kTile][D];
     __shared__ float s_g[kTile][DV];
     __shared__ float s_h[kTile];
-    const int head = blockIdx.y;
-    const int j0b = blockIdx.x * kRows;
+    const int nb = (L + kRows - 1) / kRows;
+    const int head = blockIdx.x / nb;
+    const int j0b = (blockIdx.x % nb) * kRows;
     const int j = j0b + threadIdx.x;
     const bool live = j < L;
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
@@ -193,10 +197,13 @@ __global__ __launch_bounds__(kRows) void bwd_key_kernel(const T* __restrict__ q,
 template <typename T, int D, int DV>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const float* dy, int BH, int L, float eps,
                       float* dq, float* dk, float* dv, float* g_ws, float* h_ws, hipStream_t st) {
-    const dim3 grid((L + kRows - 1) / kRows, BH);
+    const dim3 grid((unsigned)(((L + kRows - 1) / kRows) * BH));
     const T* qq = static_cast<const T*>(q);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
+    // bf16 with feature dim 16 runs on the matrix cores
+    if (sizeof(T) == 2 && D == kDFeat) return launch_prefill_backward_mfma(q, k, v, dy, BH, L, DV, eps, dq, dk, dv,
+                                                                          g_ws, h_ws, st);
     hipLaunchKernelGGL((bwd_query_kernel<T, D, DV>), grid, dim3(kRows), 0, st, qq, kk, vv, dy, L, eps, dq, g_ws, h_ws);
     hipLaunchKernelGGL((bwd_key_kernel<T, D, DV>), grid, dim3(kRows), 0, st, qq, kk, vv, L, g_ws, h_ws, dk, dv);
     return hipGetLastError();

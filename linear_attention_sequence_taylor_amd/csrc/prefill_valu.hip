@@ -44,7 +44,8 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(const T* __restrict__
     __shared__ float s_phk[kFB][C + 1];  // and per key
     __shared__ float s_S[kFB][kCW];
 
-    const int cg = blockIdx.x, head = blockIdx.y;
+    const int ncg = DV / kCW;
+    const int cg = blockIdx.x % ncg, head = blockIdx.x / ncg;
     const int tid = threadIdx.x;
     const int c0 = cg * kCW;
     const T* qh = q + (size_t)head * L * D;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256) void prefill_valu_z_kernel(const T* __restrict
 template <typename T, int D>
 static void launch_valu_d(const T* q, const T* k, const T* v, int BH, int L, int dv, int chunk, float eps,
                           float* y, float* S, float* z, int use_init, hipStream_t st) {
-    const dim3 grid(dv / kCW, BH);
+    const dim3 grid((unsigned)(dv / kCW * BH));
     switch (chunk) {
         case 16:
             hipLaunchKernelGGL((prefill_valu_kernel<T, 16, D>), grid, dim3(256), 0, st, q, k, v, L, dv, eps, y, S, z,

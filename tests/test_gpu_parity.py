@@ -369,7 +369,8 @@ def test_swa_wide_windows(dtype, tol, dqk, window, L):
 @pytest.mark.parametrize("dtype,tol,B,H,L,d,dv", [
     (torch.bfloat16, 2e-2, 1, 2, 130, 16, 64), (torch.float32, 1e-4, 1, 2, 130, 16, 64),
     (torch.float32, 1e-4, 1, 2, 70, 32, 128), (torch.bfloat16, 2e-2, 2, 1, 257, 8, 64),
-    (torch.bfloat16, 2e-2, 1, 3, 33, 24, 128),
+    (torch.bfloat16, 2e-2, 1, 3, 33, 24, 128), (torch.bfloat16, 2e-2, 2, 2, 200, 16, 128),
+    (torch.bfloat16, 2e-2, 1, 1, 64, 16, 64), (torch.bfloat16, 2e-2, 1, 2, 3, 16, 64),
 ])
 def test_backward_matches_oracle(dtype, tol, B, H, L, d, dv):
     """dq, dk, dv of the prefill output for a seeded upstream gradient, against
