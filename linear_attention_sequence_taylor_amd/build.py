@@ -29,6 +29,12 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
                 "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+# Per-source extras.  The backward kernels keep MFMA results in ordinary
+# VGPRs (their scores and products feed vector code right away; with AGPR
+# results every value would be copied out first).
+SOURCE_FLAGS = {
+    "prefill_backward_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc() -> str:
@@ -40,7 +46,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     # The host pass does not know the packed-fp32 feature and says so; drop that line.
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"

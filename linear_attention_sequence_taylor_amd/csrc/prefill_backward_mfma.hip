@@ -9,21 +9,27 @@
 //   dq_i = sum_{j<=i} e_ij k_j,  dk_j = sum_{i>=j} e_ij q_i,
 //   dv_j = sum_{i>=j} a_ij g_i.
 //
-// Every product is a 16x16 MFMA tile per wave (16 rows of its own, 16 of the
-// other side at a time).  The operand layouts line up without register
-// transposes: a score tile computed as K Q^T (keys x queries) leaves lane
-// (g, r) with query r and keys 4g..4g+3, which is the A operand of a product
-// over those keys for query row r; the staged tiles supply the other operand
-// (K^T, V^T and G^T copies in LDS where a column of a row-major matrix is
-// needed).  q, k, v are exact in bf16; the weights a, g and e are used as
-// hi/lo bf16 pairs (about 16 significant bits), accumulation is fp32.
+// Every product is a 16-row MFMA tile per wave (16 rows of its own side, 16
+// or 32 of the other side per instruction).  The operand layouts line up
+// without register shuffles: a score tile computed as K Q^T (keys x queries)
+// leaves lane (g, r) with query r and keys 4g..4g+3, which is the A operand
+// of a product over those keys for query row r.  Operands that need a column
+// of a row-major tile (V, K, Q and g as B operands) come from gfx950's
+// transposed LDS read, so every tile is staged once, row-major.  q, k, v are
+// exact in bf16; the weights a, e and g enter as bf16 hi/lo pairs (about 16
+// significant bits); accumulation is fp32.  The 1/4 of s is folded into this
+// wave's own q (or k) row, an exact power-of-two scale of a bf16 value, and
+// the 1/4 of e into the final dq (dk).
 //
 // Query side (one workgroup per 64 queries, wave w: queries 16w..16w+15):
 //   pass 1 over the key tiles at or before the queries: N and D, then g, h
-//   (to the workspace and, as bf16 hi/lo, to this wave's LDS);
+//   (g as bf16 hi/lo planes to the workspace, h in fp32);
 //   pass 2: ga^T = V g^T, e, dq += e K.
 // Key side (one workgroup per 64 keys): over the query tiles at or after the
-// keys: s = Q K^T, dv += a^T g, ga = g V^T, e, dk += e^T Q.
+// keys: s = Q K^T, ga = g V^T, e, dv += a^T g, dk += e^T Q.
+// Only the diagonal tile needs the causal mask; rows past L are staged as
+// zeros (their g and h are zero, so they add nothing on the key side) and
+// never stored.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,9 +38,10 @@ namespace {
 
 constexpr int kT = 64;         // rows per tile (queries or keys)
 constexpr int kD = 16;         // feature dim of this path
-constexpr int kRowQK = 24;     // LDS row stride (bf16) of Q and K tiles
-constexpr int kRowT = 72;      // LDS row stride (bf16) of transposed tiles [dim][64]
-constexpr float kInvSqrtD = 0.25f;
+constexpr int kLdQK = kD + 8;  // LDS row stride (bf16) of Q and K tiles
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define BWD_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -48,20 +55,25 @@ __device__ __forceinline__ bf16x4 ld4(const uint16_t* p) {
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
-__device__ __forceinline__ bf16x8 join44(const uint16_t* p0, const uint16_t* p1) {
-    const uint2 a = *reinterpret_cast<const uint2*>(p0);
-    const uint2 b = *reinterpret_cast<const uint2*>(p1);
-    const u32x4 u = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(bf16x8, u);
+
+// Transposed read of a row-major bf16 tile in LDS (row stride ld elements):
+// lane c of each 16-lane group passes the address of row rb + c/4, columns
+// col0 + 4(c%4) .. +3, and receives rows rb .. rb+3 of column col0 + c
+// (rb may differ between the groups).
+__device__ __forceinline__ uint2 tr4(const uint16_t* tile, int ld, int rb, int col0, int c) {
+    const uint16_t* p = tile + (rb + (c >> 2)) * ld + col0 + 4 * (c & 3);
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(BWD_LDS(s16x4, p)));
 }
+// B operand of a 16x16x32 product whose k index 8g + i stands for row
+// rb + 4g + i (i < 4) and rb + 16 + 4g + i - 4 (i >= 4): the pairing of the
+// A operands built from two 16-row score tiles (join_tiles).
+__device__ __forceinline__ bf16x8 tr_b8(const uint16_t* tile, int ld, int rb, int col0, int g, int c) {
+    const uint2 a = tr4(tile, ld, rb + 4 * g, col0, c);
+    const uint2 b = tr4(tile, ld, rb + 16 + 4 * g, col0, c);
+    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
 // hi = bf16(x), lo = bf16(x - hi).
-__device__ __forceinline__ void hilo4(const float (&x)[4], bf16x4& hi, bf16x4& lo) {
-    const uint32_t h0 = pack_bf16x2(x[0], x[1]), h1 = pack_bf16x2(x[2], x[3]);
-    const uint32_t l0 = pack_bf16x2(x[0] - bf16lo_f32(h0), x[1] - bf16hi_f32(h0));
-    const uint32_t l1 = pack_bf16x2(x[2] - bf16lo_f32(h1), x[3] - bf16hi_f32(h1));
-    hi = __builtin_bit_cast(bf16x4, make_uint2(h0, h1));
-    lo = __builtin_bit_cast(bf16x4, make_uint2(l0, l1));
-}
 __device__ __forceinline__ void hilo8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
     u32x4 h, l;
 #pragma unroll
@@ -72,48 +84,144 @@ __device__ __forceinline__ void hilo8(const float (&x)[8], bf16x8& hi, bf16x8& l
     hi = __builtin_bit_cast(bf16x8, h);
     lo = __builtin_bit_cast(bf16x8, l);
 }
-
-// Stages a [64][W] bf16 tile (rows row0.. of a [L][W] matrix, rows past L
-// zero) row-major into `rm` (row stride W + 8) and, if `tr`, transposed into
-// `tr` ([W][kRowT]).
-template <int W>
-__device__ __forceinline__ void stage_tile(const uint16_t* mat, int L, int row0, uint16_t* rm, uint16_t* tr) {
-    constexpr int kU = W / 8;  // 16-byte units per row
-    for (int e = threadIdx.x; e < kT * kU; e += 256) {
-        const int row = e / kU, u = e % kU;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (row0 + row < L) x = *reinterpret_cast<const u32x4*>(mat + (size_t)(row0 + row) * W + 8 * u);
-        *reinterpret_cast<u32x4*>(rm + row * (W + 8) + 8 * u) = x;
-        if (tr) {
+// The four values of score tile 2p and the four of tile 2p + 1 as one
+// 8-vector (k index 8g + i of tr_b8).
+__device__ __forceinline__ void join_tiles(const float (&a)[4], const float (&b)[4], float (&x)[8]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                tr[(8 * u + 2 * i) * kRowT + row] = (uint16_t)(x[i] & 0xffffu);
-                tr[(8 * u + 2 * i + 1) * kRowT + row] = (uint16_t)(x[i] >> 16);
-            }
-        }
+    for (int i = 0; i < 4; ++i) {
+        x[i] = a[i];
+        x[4 + i] = b[i];
     }
 }
 
+// Four bf16 values times 1/4 (exact unless they underflow).
+__device__ __forceinline__ bf16x4 quarter(uint2 u) {
+    const float f[4] = {bf16lo_f32(u.x), bf16hi_f32(u.x), bf16lo_f32(u.y), bf16hi_f32(u.y)};
+    return __builtin_bit_cast(bf16x4, make_uint2(pack_bf16x2(0.25f * f[0], 0.25f * f[1]),
+                                                 pack_bf16x2(0.25f * f[2], 0.25f * f[3])));
+}
+
+// A [64][W] bf16 tile (rows row0.. of a [L][W] matrix, rows past L zero)
+// held in registers across the workgroup, 16 bytes per piece: loaded from
+// global memory while the previous tile is in use, then stored to LDS with
+// row stride W + 8.
+template <int W>
+struct TileRegs {
+    static constexpr int kU = W / 8;                    // pieces per row
+    static constexpr int kPer = (kT * kU + 255) / 256;  // pieces per thread
+    u32x4 x[kPer];
+
+    __device__ __forceinline__ void load(const uint16_t* mat, int L, int row0) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = threadIdx.x + 256 * i, row = e / kU, u = e % kU;
+            x[i] = u32x4{0u, 0u, 0u, 0u};
+            if (e < kT * kU && row0 + row < L)
+                x[i] = *reinterpret_cast<const u32x4*>(mat + (size_t)(row0 + row) * W + 8 * u);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* dst) const {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = threadIdx.x + 256 * i, row = e / kU, u = e % kU;
+            if (e < kT * kU) *reinterpret_cast<u32x4*>(dst + row * (W + 8) + 8 * u) = x[i];
+        }
+    }
+};
+
+// ---------------------------------------------------------------- query side
 template <int DV>
 struct BwdQSmem {
-    alignas(16) uint16_t q[kT * (kD + 8)];
-    alignas(16) uint16_t k[kT * (kD + 8)];
-    alignas(16) uint16_t kt[kD * kRowT];
+    alignas(16) uint16_t k[kT * kLdQK];
     alignas(16) uint16_t v[kT * (DV + 8)];
-    alignas(16) uint16_t vt[DV * kRowT];
     alignas(16) uint16_t ghi[4][16 * (DV + 8)];  // per wave: g of its 16 queries
     alignas(16) uint16_t glo[4][16 * (DV + 8)];
     float h[4][16];
 };
 
-// ---- query side
+// Pass 1 on one key tile: N (yacc: rows = queries 4g+m, columns 16ct + r)
+// and D - eps (dsum: the same rows, every column) as the product with a
+// column of ones.
+template <int DV, bool DIAG>
+__device__ __forceinline__ void q_pass1(const BwdQSmem<DV>& sm, const bf16x4& qb, int w, int g, int r,
+                                        f32x4 (&yacc)[DV / 16], f32x4& dsum) {
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+    float a[4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        const f32x4 st = mfma16(ld4(&sm.k[(16 * kt + r) * kLdQK + 4 * g]), qb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float s = st[m];
+            float x = fmaf(s, fmaf(s, 0.5f, 1.f), 1.f);
+            if (DIAG) x = 16 * kt + 4 * g + m <= 16 * w + r ? x : 0.f;
+            a[kt][m] = x;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        float x[8];
+        join_tiles(a[2 * p], a[2 * p + 1], x);
+        bf16x8 ahi, alo;
+        hilo8(x, ahi, alo);
+        dsum = mfma32(ahi, ones, dsum);
+        dsum = mfma32(alo, ones, dsum);
+#pragma unroll
+        for (int ct = 0; ct < DV / 16; ++ct) {
+            const bf16x8 vb = tr_b8(sm.v, DV + 8, 32 * p, 16 * ct, g, r);
+            yacc[ct] = mfma32(ahi, vb, yacc[ct]);
+            yacc[ct] = mfma32(alo, vb, yacc[ct]);
+        }
+    }
+}
+
+// Pass 2 on one key tile: dq (rows = queries 4g+m, columns = feature r) +=
+// e4 K with e4 = 4 e.
+template <int DV, bool DIAG>
+__device__ __forceinline__ void q_pass2(const BwdQSmem<DV>& sm, const bf16x4& qb, int w, int g, int r,
+                                        f32x4& dqacc) {
+    const float hr = sm.h[w][r];
+    float e[4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        const f32x4 st = mfma16(ld4(&sm.k[(16 * kt + r) * kLdQK + 4 * g]), qb, f32x4{0.f, 0.f, 0.f, 0.f});
+        // ga^T: rows = keys 16kt + 4g + m, columns = queries r
+        f32x4 ga = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cs = 0; cs < DV / 32; ++cs) {
+            const bf16x8 va = ld8(&sm.v[(16 * kt + r) * (DV + 8) + 32 * cs + 8 * g]);
+            ga = mfma32(va, ld8(&sm.ghi[w][r * (DV + 8) + 32 * cs + 8 * g]), ga);
+            ga = mfma32(va, ld8(&sm.glo[w][r * (DV + 8) + 32 * cs + 8 * g]), ga);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float gh = ga[m] + hr;
+            float x = fmaf(gh, st[m], gh);
+            if (DIAG) x = 16 * kt + 4 * g + m <= 16 * w + r ? x : 0.f;
+            e[kt][m] = x;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        float x[8];
+        join_tiles(e[2 * p], e[2 * p + 1], x);
+        bf16x8 ehi, elo;
+        hilo8(x, ehi, elo);
+        const bf16x8 kb = tr_b8(sm.k, kLdQK, 32 * p, 0, g, r);
+        dqacc = mfma32(ehi, kb, dqacc);
+        dqacc = mfma32(elo, kb, dqacc);
+    }
+}
+
 template <int DV>
 __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(const uint16_t* __restrict__ q,
                                                              const uint16_t* __restrict__ k,
                                                              const uint16_t* __restrict__ v,
                                                              const float* __restrict__ dy, int L, int ntiles,
                                                              float eps, float* __restrict__ dq,
-                                                             float* __restrict__ g_ws, float* __restrict__ h_ws) {
+                                                             uint16_t* __restrict__ ghi_ws,
+                                                             uint16_t* __restrict__ glo_ws,
+                                                             float* __restrict__ h_ws) {
     constexpr int kNV = DV / 16;  // column tiles
     __shared__ BwdQSmem<DV> sm;
     const int BH = gridDim.x / ntiles;
@@ -121,175 +229,171 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(const uint16_t* __r
     const int ti = ntiles - 1 - (int)(blockIdx.x / BH);  // the longest rows first, every head
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-    const uint16_t* qh = q + (size_t)head * L * kD;
     const uint16_t* kh = k + (size_t)head * L * kD;
     const uint16_t* vh = v + (size_t)head * L * DV;
     const int qw0 = ti * kT + 16 * w;  // first query of this wave
     const int qr = qw0 + r;            // this lane's query in score tiles
 
-    stage_tile<kD>(qh, L, ti * kT, sm.q, nullptr);
-    // ---- pass 1: N (yacc, rows = queries 4g+m, columns 16ct + r) and D
+    // B operand of the scores: this lane's query row, dims 4g..4g+3, times 1/4
+    bf16x4 qb = __builtin_bit_cast(bf16x4, make_uint2(0u, 0u));
+    if (qr < L) qb = quarter(*reinterpret_cast<const uint2*>(q + ((size_t)head * L + qr) * kD + 4 * g));
+
+    // ---- pass 1: the key tiles before the diagonal, the next one loading
+    // while the current one is in use, then the diagonal tile
     f32x4 yacc[kNV];
 #pragma unroll
     for (int ct = 0; ct < kNV; ++ct) yacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
-    for (int tj = 0; tj <= ti; ++tj) {
+    f32x4 dsum = {0.f, 0.f, 0.f, 0.f};
+    TileRegs<kD> kreg;
+    TileRegs<DV> vreg;
+    kreg.load(kh, L, 0);
+    vreg.load(vh, L, 0);
+    for (int tj = 0; tj < ti; ++tj) {
         __syncthreads();
-        stage_tile<kD>(kh, L, tj * kT, sm.k, nullptr);
-        stage_tile<DV>(vh, L, tj * kT, sm.v, sm.vt);
+        kreg.store(sm.k);
+        vreg.store(sm.v);
         __syncthreads();
-        const bf16x4 qb = ld4(&sm.q[(16 * w + r) * (kD + 8) + 4 * g]);
-        float a[4][4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const f32x4 st = mfma16(ld4(&sm.k[(16 * kt + r) * (kD + 8) + 4 * g]), qb, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int kg = tj * kT + 16 * kt + 4 * g + m;
-                const float s = st[m] * kInvSqrtD;
-                const float w8 = fmaf(s, fmaf(s, 0.5f, 1.f), 1.f);
-                a[kt][m] = (kg <= qr && kg < L) ? w8 : 0.f;
-                lsum += a[kt][m];
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const float x[8] = {a[2 * p][0],     a[2 * p][1],     a[2 * p][2],     a[2 * p][3],
-                                a[2 * p + 1][0], a[2 * p + 1][1], a[2 * p + 1][2], a[2 * p + 1][3]};
-            bf16x8 ahi, alo;
-            hilo8(x, ahi, alo);
-#pragma unroll
-            for (int ct = 0; ct < kNV; ++ct) {
-                const uint16_t* row = &sm.vt[(16 * ct + r) * kRowT + 32 * p + 4 * g];
-                const bf16x8 vb = join44(row, row + 16);
-                yacc[ct] = mfma32(ahi, vb, yacc[ct]);
-                yacc[ct] = mfma32(alo, vb, yacc[ct]);
-            }
-        }
+        kreg.load(kh, L, (tj + 1) * kT);
+        vreg.load(vh, L, (tj + 1) * kT);
+        q_pass1<DV, false>(sm, qb, w, g, r, yacc, dsum);
     }
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);  // D - eps of query qr, on every lane group
+    __syncthreads();
+    kreg.store(sm.k);
+    vreg.store(sm.v);
+    __syncthreads();
+    kreg.load(kh, L, 0);  // pass 2's first off-diagonal tile
+    vreg.load(vh, L, 0);
+    q_pass1<DV, true>(sm, qb, w, g, r, yacc, dsum);
 
-    // ---- g = dy/D, h = -(dy.y)/D for queries qw0 + 4g + m, columns 16ct + r
-    float gv[kNV][4], hq[4];
+    // ---- g = dy/D and h = -(dy.N)/D^2 for queries qw0 + 4g + m, columns
+    // 16ct + r: g to this wave's LDS rows as bf16 hi/lo, h to LDS and the
+    // workspace
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int qi = qw0 + 4 * g + m;
-        const float inv = 1.f / (__shfl(lsum, 4 * g + m, 64) + eps);
+        const float inv = 1.f / (dsum[m] + eps);
         float dyy = 0.f;
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) {
             const float dyc = qi < L ? dy[((size_t)head * L + qi) * DV + 16 * ct + r] : 0.f;
-            dyy = fmaf(dyc, yacc[ct][m] * inv, dyy);
-            gv[ct][m] = dyc * inv;
-        }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) dyy += __shfl_xor(dyy, off, 64);
-        hq[m] = -dyy * inv;
-        if (qi < L) {
-#pragma unroll
-            for (int ct = 0; ct < kNV; ++ct) g_ws[((size_t)head * L + qi) * DV + 16 * ct + r] = gv[ct][m];
-            if (r == 0) h_ws[(size_t)head * L + qi] = hq[m];
-        }
-    }
-    // this wave's g as bf16 hi/lo rows [16 queries][DV], h per query
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-        for (int ct = 0; ct < kNV; ++ct) {
-            const float x = gv[ct][m];
-            const uint32_t hb = pack_bf16x2(x, 0.f);
-            const uint32_t lb = pack_bf16x2(x - bf16lo_f32(hb), 0.f);
+            dyy = fmaf(dyc, yacc[ct][m], dyy);
+            const float gv = dyc * inv;
+            const uint32_t hb = pack_bf16x2(gv, 0.f);
+            const uint32_t lb = pack_bf16x2(gv - bf16lo_f32(hb), 0.f);
             sm.ghi[w][(4 * g + m) * (DV + 8) + 16 * ct + r] = (uint16_t)(hb & 0xffffu);
             sm.glo[w][(4 * g + m) * (DV + 8) + 16 * ct + r] = (uint16_t)(lb & 0xffffu);
         }
-        if (r == 0) sm.h[w][4 * g + m] = hq[m];
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) dyy += __shfl_xor(dyy, off, 64);
+        const float hq = -dyy * inv * inv;
+        if (r == 0) {
+            sm.h[w][4 * g + m] = hq;
+            if (qi < L) h_ws[(size_t)head * L + qi] = hq;
+        }
+    }
+    __syncthreads();
+    // this wave's g rows to the workspace in 16-byte pieces
+    {
+        constexpr int kU = DV / 8;
+        for (int e = lane; e < 16 * kU; e += 64) {
+            const int row = e / kU, u = e % kU;
+            const int qi = qw0 + row;
+            if (qi < L) {
+                const size_t off = ((size_t)head * L + qi) * DV + 8 * u;
+                *reinterpret_cast<u32x4*>(ghi_ws + off) =
+                    *reinterpret_cast<const u32x4*>(&sm.ghi[w][row * (DV + 8) + 8 * u]);
+                *reinterpret_cast<u32x4*>(glo_ws + off) =
+                    *reinterpret_cast<const u32x4*>(&sm.glo[w][row * (DV + 8) + 8 * u]);
+            }
+        }
     }
 
-    // ---- pass 2: dq (rows = queries 4g+m, columns = feature r)
+    // ---- pass 2: the diagonal tile (still in LDS), then the tiles before it
     f32x4 dqacc = {0.f, 0.f, 0.f, 0.f};
-    for (int tj = 0; tj <= ti; ++tj) {
-        __syncthreads();  // also orders this wave's g/h writes before its reads
-        stage_tile<kD>(kh, L, tj * kT, sm.k, sm.kt);
-        stage_tile<DV>(vh, L, tj * kT, sm.v, nullptr);
+    q_pass2<DV, true>(sm, qb, w, g, r, dqacc);
+    for (int tj = 0; tj < ti; ++tj) {
         __syncthreads();
-        const bf16x4 qb = ld4(&sm.q[(16 * w + r) * (kD + 8) + 4 * g]);
-        const float hr = sm.h[w][r];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const f32x4 st = mfma16(ld4(&sm.k[(16 * kt + r) * (kD + 8) + 4 * g]), qb, f32x4{0.f, 0.f, 0.f, 0.f});
-            // ga^T: rows = keys 16kt + 4g + m, columns = queries r
-            f32x4 ga = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int cs = 0; cs < DV / 32; ++cs) {
-                const bf16x8 va = ld8(&sm.v[(16 * kt + r) * (DV + 8) + 32 * cs + 8 * g]);
-                ga = mfma32(va, ld8(&sm.ghi[w][r * (DV + 8) + 32 * cs + 8 * g]), ga);
-                ga = mfma32(va, ld8(&sm.glo[w][r * (DV + 8) + 32 * cs + 8 * g]), ga);
-            }
-            float e[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int kg = tj * kT + 16 * kt + 4 * g + m;
-                const float s = st[m] * kInvSqrtD;
-                e[m] = (kg <= qr && kg < L) ? (ga[m] + hr) * (1.f + s) * kInvSqrtD : 0.f;
-            }
-            bf16x4 ehi, elo;
-            hilo4(e, ehi, elo);
-            const bf16x4 kb = ld4(&sm.kt[r * kRowT + 16 * kt + 4 * g]);
-            dqacc = mfma16(ehi, kb, dqacc);
-            dqacc = mfma16(elo, kb, dqacc);
-        }
+        kreg.store(sm.k);
+        vreg.store(sm.v);
+        __syncthreads();
+        kreg.load(kh, L, (tj + 1) * kT);
+        vreg.load(vh, L, (tj + 1) * kT);
+        q_pass2<DV, false>(sm, qb, w, g, r, dqacc);
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int qi = qw0 + 4 * g + m;
-        if (qi < L) dq[((size_t)head * L + qi) * kD + r] = dqacc[m];
+        if (qi < L) dq[((size_t)head * L + qi) * kD + r] = 0.25f * dqacc[m];
     }
 }
 
-
+// ---------------------------------------------------------------- key side
 template <int DV>
 struct BwdKSmem {
-    alignas(16) uint16_t q[kT * (kD + 8)];
-    alignas(16) uint16_t qt[kD * kRowT];
-    alignas(16) uint16_t ghi[kT * (DV + 8)];  // g of the query tile, hi / lo, row-major
+    alignas(16) uint16_t q[kT * kLdQK];
+    alignas(16) uint16_t ghi[kT * (DV + 8)];  // g of the query tile, hi / lo
     alignas(16) uint16_t glo[kT * (DV + 8)];
-    alignas(16) uint16_t gthi[DV * kRowT];    // and transposed
-    alignas(16) uint16_t gtlo[DV * kRowT];
-    float h[kT];
+    alignas(16) float h[kT];
 };
 
-// Stages g (fp32 rows row0.. of a [L][DV] matrix, rows past L zero) as bf16
-// hi/lo pairs, row-major and transposed, and h of those rows.
-template <int DV>
-__device__ __forceinline__ void stage_g(const float* gh, const float* hh, int L, int row0, BwdKSmem<DV>& sm) {
-    constexpr int kU = DV / 4;  // float4 units per row
-    for (int e = threadIdx.x; e < kT * kU; e += 256) {
-        const int row = e / kU, u = e % kU;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (row0 + row < L) x = *reinterpret_cast<const f32x4*>(gh + (size_t)(row0 + row) * DV + 4 * u);
-        const float xs[4] = {x[0], x[1], x[2], x[3]};
-        bf16x4 hi, lo;
-        hilo4(xs, hi, lo);
-        const uint2 hu = __builtin_bit_cast(uint2, hi), lu = __builtin_bit_cast(uint2, lo);
-        *reinterpret_cast<uint2*>(&sm.ghi[row * (DV + 8) + 4 * u]) = hu;
-        *reinterpret_cast<uint2*>(&sm.glo[row * (DV + 8) + 4 * u]) = lu;
-        const uint32_t hw[2] = {hu.x, hu.y}, lw[2] = {lu.x, lu.y};
+// One query tile: dv (rows = keys 4g+m, columns 16ct + r) += a^T g and
+// dk (columns = feature r) += e4^T Q with e4 = 4 e.
+template <int DV, bool DIAG>
+__device__ __forceinline__ void k_tile(const BwdKSmem<DV>& sm, const bf16x4& kb, const bf16x8 (&vb)[DV / 32], int w,
+                                       int g, int r, f32x4 (&dvacc)[DV / 16], f32x4& dkacc) {
+    float a[4][4], e[4][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sm.gthi[(4 * u + i) * kRowT + row] = (uint16_t)(hw[i >> 1] >> (16 * (i & 1)));
-            sm.gtlo[(4 * u + i) * kRowT + row] = (uint16_t)(lw[i >> 1] >> (16 * (i & 1)));
+    for (int qt = 0; qt < 4; ++qt) {
+        // scores and ga: rows = queries 16qt + 4g + m, columns = keys r
+        const f32x4 st = mfma16(ld4(&sm.q[(16 * qt + r) * kLdQK + 4 * g]), kb, f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 ga = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cs = 0; cs < DV / 32; ++cs) {
+            ga = mfma32(ld8(&sm.ghi[(16 * qt + r) * (DV + 8) + 32 * cs + 8 * g]), vb[cs], ga);
+            ga = mfma32(ld8(&sm.glo[(16 * qt + r) * (DV + 8) + 32 * cs + 8 * g]), vb[cs], ga);
+        }
+        const f32x4 hq = *reinterpret_cast<const f32x4*>(&sm.h[16 * qt + 4 * g]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float s = st[m], gh = ga[m] + hq[m];
+            float xa = fmaf(s, fmaf(s, 0.5f, 1.f), 1.f), xe = fmaf(gh, s, gh);
+            if (DIAG) {
+                const bool ok = 16 * qt + 4 * g + m >= 16 * w + r;
+                xa = ok ? xa : 0.f;
+                xe = ok ? xe : 0.f;
+            }
+            a[qt][m] = xa;
+            e[qt][m] = xe;
         }
     }
-    if (threadIdx.x < kT) sm.h[threadIdx.x] = row0 + (int)threadIdx.x < L ? hh[row0 + threadIdx.x] : 0.f;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        float xa[8], xe[8];
+        join_tiles(a[2 * p], a[2 * p + 1], xa);
+        join_tiles(e[2 * p], e[2 * p + 1], xe);
+        bf16x8 ahi, alo, ehi, elo;
+        hilo8(xa, ahi, alo);
+        hilo8(xe, ehi, elo);
+#pragma unroll
+        for (int ct = 0; ct < DV / 16; ++ct) {
+            const bf16x8 gbh = tr_b8(sm.ghi, DV + 8, 32 * p, 16 * ct, g, r);
+            const bf16x8 gbl = tr_b8(sm.glo, DV + 8, 32 * p, 16 * ct, g, r);
+            dvacc[ct] = mfma32(ahi, gbh, dvacc[ct]);
+            dvacc[ct] = mfma32(alo, gbh, dvacc[ct]);
+            dvacc[ct] = mfma32(ahi, gbl, dvacc[ct]);
+        }
+        const bf16x8 qb = tr_b8(sm.q, kLdQK, 32 * p, 0, g, r);
+        dkacc = mfma32(ehi, qb, dkacc);
+        dkacc = mfma32(elo, qb, dkacc);
+    }
 }
 
-// ---- key side
 template <int DV>
 __global__ __launch_bounds__(256) void bwd_key_mfma_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v, int L, int ntiles,
-                                                           const float* __restrict__ g_ws,
+                                                           const uint16_t* __restrict__ ghi_ws,
+                                                           const uint16_t* __restrict__ glo_ws,
                                                            const float* __restrict__ h_ws, float* __restrict__ dk,
                                                            float* __restrict__ dvo) {
     constexpr int kNV = DV / 16;
@@ -300,77 +404,56 @@ __global__ __launch_bounds__(256) void bwd_key_mfma_kernel(const uint16_t* __res
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const uint16_t* qh = q + (size_t)head * L * kD;
-    const uint16_t* kh = k + (size_t)head * L * kD;
-    const uint16_t* vh = v + (size_t)head * L * DV;
-    const float* gh = g_ws + (size_t)head * L * DV;
+    const uint16_t* gh = ghi_ws + (size_t)head * L * DV;
+    const uint16_t* gl = glo_ws + (size_t)head * L * DV;
     const float* hh = h_ws + (size_t)head * L;
     const int kw0 = tj * kT + 16 * w;  // first key of this wave
     const int kr = kw0 + r;            // this lane's key in score tiles
 
-    // this lane's key and value row pieces: the B operands of Q K^T and g V^T
+    // this lane's key row (times 1/4) and value row pieces: the B operands
+    // of Q K^T and g V^T
     bf16x4 kb = __builtin_bit_cast(bf16x4, make_uint2(0u, 0u));
     bf16x8 vb[DV / 32];
 #pragma unroll
     for (int cs = 0; cs < DV / 32; ++cs) vb[cs] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     if (kr < L) {
-        kb = ld4(kh + (size_t)kr * kD + 4 * g);
+        kb = quarter(*reinterpret_cast<const uint2*>(k + ((size_t)head * L + kr) * kD + 4 * g));
 #pragma unroll
-        for (int cs = 0; cs < DV / 32; ++cs) vb[cs] = ld8(vh + (size_t)kr * DV + 32 * cs + 8 * g);
+        for (int cs = 0; cs < DV / 32; ++cs) vb[cs] = ld8(v + ((size_t)head * L + kr) * DV + 32 * cs + 8 * g);
     }
     f32x4 dvacc[kNV];
 #pragma unroll
     for (int ct = 0; ct < kNV; ++ct) dvacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 dkacc = {0.f, 0.f, 0.f, 0.f};
 
-    for (int ti = tj; ti < ntiles; ++ti) {
+    // the diagonal tile, then the query tiles after it, the next one loading
+    // while the current one is in use
+    TileRegs<kD> qreg;
+    TileRegs<DV> ghreg, glreg;
+    float hreg = 0.f;
+    auto load = [&](int ti) {
+        qreg.load(qh, L, ti * kT);
+        ghreg.load(gh, L, ti * kT);
+        glreg.load(gl, L, ti * kT);
+        if (threadIdx.x < kT) hreg = ti * kT + (int)threadIdx.x < L ? hh[ti * kT + threadIdx.x] : 0.f;
+    };
+    auto store = [&]() {
+        qreg.store(sm.q);
+        ghreg.store(sm.ghi);
+        glreg.store(sm.glo);
+        if (threadIdx.x < kT) sm.h[threadIdx.x] = hreg;
+    };
+    load(tj);
+    store();
+    __syncthreads();
+    load(tj + 1);
+    k_tile<DV, true>(sm, kb, vb, w, g, r, dvacc, dkacc);
+    for (int ti = tj + 1; ti < ntiles; ++ti) {
         __syncthreads();
-        stage_tile<kD>(qh, L, ti * kT, sm.q, sm.qt);
-        stage_g<DV>(gh, hh, L, ti * kT, sm);
+        store();
         __syncthreads();
-        // a and e for queries ti*64 + 16qt + 4g + m and key kr
-        float a[4][4], e[4][4];
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-            const f32x4 st = mfma16(ld4(&sm.q[(16 * qt + r) * (kD + 8) + 4 * g]), kb, f32x4{0.f, 0.f, 0.f, 0.f});
-            f32x4 ga = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int cs = 0; cs < DV / 32; ++cs) {
-                ga = mfma32(ld8(&sm.ghi[(16 * qt + r) * (DV + 8) + 32 * cs + 8 * g]), vb[cs], ga);
-                ga = mfma32(ld8(&sm.glo[(16 * qt + r) * (DV + 8) + 32 * cs + 8 * g]), vb[cs], ga);
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int qg = ti * kT + 16 * qt + 4 * g + m;
-                const bool ok = qg >= kr && qg < L;
-                const float s = st[m] * kInvSqrtD;
-                a[qt][m] = ok ? fmaf(s, fmaf(s, 0.5f, 1.f), 1.f) : 0.f;
-                e[qt][m] = ok ? (ga[m] + sm.h[16 * qt + 4 * g + m]) * (1.f + s) * kInvSqrtD : 0.f;
-            }
-        }
-        // dv += a^T g and dk += e^T Q, 32 queries per product
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const float xa[8] = {a[2 * p][0],     a[2 * p][1],     a[2 * p][2],     a[2 * p][3],
-                                 a[2 * p + 1][0], a[2 * p + 1][1], a[2 * p + 1][2], a[2 * p + 1][3]};
-            const float xe[8] = {e[2 * p][0],     e[2 * p][1],     e[2 * p][2],     e[2 * p][3],
-                                 e[2 * p + 1][0], e[2 * p + 1][1], e[2 * p + 1][2], e[2 * p + 1][3]};
-            bf16x8 ahi, alo, ehi, elo;
-            hilo8(xa, ahi, alo);
-            hilo8(xe, ehi, elo);
-#pragma unroll
-            for (int ct = 0; ct < kNV; ++ct) {
-                const uint16_t* rh = &sm.gthi[(16 * ct + r) * kRowT + 32 * p + 4 * g];
-                const uint16_t* rl = &sm.gtlo[(16 * ct + r) * kRowT + 32 * p + 4 * g];
-                const bf16x8 gbh = join44(rh, rh + 16), gbl = join44(rl, rl + 16);
-                dvacc[ct] = mfma32(ahi, gbh, dvacc[ct]);
-                dvacc[ct] = mfma32(alo, gbh, dvacc[ct]);
-                dvacc[ct] = mfma32(ahi, gbl, dvacc[ct]);
-            }
-            const uint16_t* rq = &sm.qt[r * kRowT + 32 * p + 4 * g];
-            const bf16x8 qb = join44(rq, rq + 16);
-            dkacc = mfma32(ehi, qb, dkacc);
-            dkacc = mfma32(elo, qb, dkacc);
-        }
+        load(ti + 1);
+        k_tile<DV, false>(sm, kb, vb, w, g, r, dvacc, dkacc);
     }
     // rows = keys kw0 + 4g + m; dv columns 16ct + r, dk feature r
 #pragma unroll
@@ -379,21 +462,26 @@ __global__ __launch_bounds__(256) void bwd_key_mfma_kernel(const uint16_t* __res
         if (kj < L) {
 #pragma unroll
             for (int ct = 0; ct < kNV; ++ct) dvo[((size_t)head * L + kj) * DV + 16 * ct + r] = dvacc[ct][m];
-            dk[((size_t)head * L + kj) * kD + r] = dkacc[m];
+            dk[((size_t)head * L + kj) * kD + r] = 0.25f * dkacc[m];
         }
     }
 }
 
 }  // namespace
 
+// The workspace of prefill_backward.hip (BH*L*DV fp32 for g, then BH*L fp32
+// for h) holds g here as two bf16 planes of BH*L*DV each (hi, then lo).
 template <int DV>
 static void launch_both(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* dy, int BH, int L,
                         float eps, float* dq, float* dk, float* dvo, float* g_ws, float* h_ws, hipStream_t st) {
     const int ntiles = (L + kT - 1) / kT;
     const dim3 grid((unsigned)(ntiles * BH));
-    hipLaunchKernelGGL((bwd_query_mfma_kernel<DV>), grid, dim3(256), 0, st, q, k, v, dy, L, ntiles, eps, dq, g_ws,
-                       h_ws);
-    hipLaunchKernelGGL((bwd_key_mfma_kernel<DV>), grid, dim3(256), 0, st, q, k, v, L, ntiles, g_ws, h_ws, dk, dvo);
+    uint16_t* ghi = reinterpret_cast<uint16_t*>(g_ws);
+    uint16_t* glo = ghi + (size_t)BH * L * DV;
+    hipLaunchKernelGGL((bwd_query_mfma_kernel<DV>), grid, dim3(256), 0, st, q, k, v, dy, L, ntiles, eps, dq, ghi,
+                       glo, h_ws);
+    hipLaunchKernelGGL((bwd_key_mfma_kernel<DV>), grid, dim3(256), 0, st, q, k, v, L, ntiles, ghi, glo, h_ws, dk,
+                       dvo);
 }
 
 hipError_t launch_prefill_backward_mfma(const void* q, const void* k, const void* v, const float* dy, int BH, int L,
