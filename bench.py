@@ -22,6 +22,7 @@ prints one JSON line with:
 * extra: the next-token step (1.3B-shaped decode, 1024 steps), the w=64
   window kernel with fused add, the window's next-token step on its ring
   cache, and the 64K-token prefill, each with its own HBM roofline fraction;
+  the whole 8K hybrid layer fused (and as two passes);
   the gradients of the prefill over the same layer (matrix-core fraction);
   and the other feature dims and window sizes.
 """
@@ -76,6 +77,15 @@ def swa_bytes(wl) -> int:
     es = 2
     per_tok = 2 * wl.d_qk * es + wl.dv * es + 2 * wl.dv * 4
     return wl.B * wl.H * wl.L * per_tok
+
+
+def hybrid_bytes(wl) -> int:
+    """The whole hybrid layer in one pass: both branches' q, k and the shared
+    v read once, y written once (fp32), the final linear-attention state
+    written once."""
+    es = 2
+    per_tok = 2 * wl.d * es + 2 * wl.d_qk * es + wl.dv * es + wl.dv * 4
+    return wl.B * wl.H * wl.L * per_tok + wl.B * wl.H * (F * wl.dv + F) * 4
 
 
 def window_decode_bytes(wl) -> int:
@@ -241,6 +251,41 @@ def bench_swa(based, wl, reps):
         launch(i)
     timer.stop()
     return timer.seconds() / reps
+
+
+def bench_hybrid(based, wl, reps):
+    """The whole hybrid layer (linear attention + window, summed) through
+    based_hybrid_prefill with each path: "auto" (the library's choice),
+    "fused" (one kernel) and "two_pass" (prefill, then the window adding into
+    y).  Two input/output sets alternate (1.4 GB, past the Infinity Cache).
+    Returns {path: event seconds per layer}."""
+    q, k, v = si.linear_inputs(wl)
+    qw, kw = si.window_inputs(wl)
+    sets = make_sets((q, k, qw, kw, v), 2)
+    del q, k, v, qw, kw
+    outs = [(torch.empty(wl.B, wl.H, wl.L, wl.dv, device="cuda"), torch.empty(wl.B, wl.H, F, wl.dv, device="cuda"),
+             torch.empty(wl.B, wl.H, F, device="cuda")) for _ in range(2)]
+    ws = torch.empty(max(based.based_hybrid_prefill_workspace_bytes(wl.B, wl.H, wl.L, wl.dv), 1), dtype=torch.uint8,
+                     device="cuda")
+
+    def layer(i, path):
+        qq, kk, qqw, kkw, vv = sets[i % 2]
+        y, S, z = outs[i % 2]
+        based.based_hybrid_prefill(qq, kk, qqw, kkw, vv, chunk=wl.chunk, eps=wl.eps, window=wl.window,
+                                   scale=wl.swa_scale, path=path, y=y, S=S, z=z, workspace=ws)
+
+    res = {}
+    for path in ("auto", "fused", "two_pass"):
+        for i in range(200):  # untimed warm-up
+            layer(i, path)
+        timer = RegionTimer()
+        torch.cuda.synchronize()
+        timer.start()
+        for i in range(reps):
+            layer(i, path)
+        timer.stop()
+        res[path] = timer.seconds() / reps
+    return res
 
 
 def bench_window_decode(based, wl, n_steps, graph_steps=64, n_sets=16):
@@ -491,6 +536,18 @@ def main():
                                   "hbm_GBps": sb / skern / 1e9, "hbm_frac": sb / skern / HBM_PEAK,
                                   "algorithmic_bytes": sb}
         print(f"[bench] swa: {skern*1e6:.1f} us, {sb/skern/1e9:.0f} GB/s", file=sys.stderr, flush=True)
+        ht = bench_hybrid(based, ww, 100)
+        hb = hybrid_bytes(ww)
+        extra["window_8k_hybrid_layer"] = {
+            "tokens_per_s": ww.B * ww.L / ht["auto"], "kernel_us": ht["auto"] * 1e6,
+            "hbm_GBps": hb / ht["auto"] / 1e9, "hbm_frac": hb / ht["auto"] / HBM_PEAK, "algorithmic_bytes": hb,
+            "fused_us": ht["fused"] * 1e6, "two_pass_us": ht["two_pass"] * 1e6,
+            "note": "linear attention + w=64 window over B=4, H=16, L=8192 through based_hybrid_prefill; kernel_us "
+                    "is the library's own choice (auto), fused_us the one-kernel path (32-column groups with a "
+                    "segment split), two_pass_us based_prefill then the window adding into y; algorithmic bytes "
+                    "are those of one pass"}
+        print(f"[bench] hybrid layer: auto {ht['auto']*1e6:.1f} us, fused {ht['fused']*1e6:.1f} us, two passes "
+              f"{ht['two_pass']*1e6:.1f} us", file=sys.stderr, flush=True)
         wwd = si.WORKLOADS["window_decode_1p3b"]
         wkern = bench_window_decode(based, wwd, args.window_decode_steps)
         wb = window_decode_bytes(wwd)

@@ -14,6 +14,9 @@
  *                      seeing the preceding `window` keys ([1] s4 "Local
  *                      Exact Attention"), with an optional fused add of the
  *                      linear-attention output (BASED pairs the two).
+ *   based_hybrid_prefill  both branches of a BASED layer over one sequence
+ *                      (linear attention + the window, summed) in one pass
+ *                      where a fused kernel exists ([1] s4; s5 fusion).
  *   swa_cache_fill,    the window's next-token step on a w-sized key/value
  *   swa_decode_step    ring cache (same section; App. B "Next Token
  *                      Prediction").
@@ -165,6 +168,46 @@ based_status_t swa_forward(const void *q, const void *k, const void *v,
                            based_dtype_t dtype, int B, int H, int L,
                            int d_qk, int d_v, int window, float scale,
                            const float *add, float *y, void *stream);
+
+/*
+ * based_hybrid_prefill -- a BASED layer's two mixers over one sequence,
+ * summed ([1] s4: Taylor linear attention paired with "Local Exact
+ * Attention"; s5: fuse work and avoid extra passes over HBM):
+ *   y = based_prefill(q, k, v).y + swa_forward(q_win, k_win, v).y
+ * with the final linear-attention state in S, z exactly as based_prefill
+ * (each branch normalised on its own; v is shared).
+ *
+ *   q, k          [B,H,L,d_feat] dtype (the linear branch)
+ *   q_win, k_win  [B,H,L,d_qk] dtype (the window branch)
+ *   v             [B,H,L,d_v] dtype
+ *   chunk, eps, S, z, use_initial_state, workspace: as based_prefill, with
+ *                 the workspace size from
+ *                 based_hybrid_prefill_workspace_bytes
+ *   window, scale: as swa_forward;  y [B,H,L,d_v] fp32 out
+ *   path          BASED_HYBRID_AUTO, _FUSED or _TWO_PASS (below);
+ *                 anything else is BASED_E_INVALID
+ * Supported: what both based_prefill and swa_forward support with d_v = 64.
+ * A fused kernel exists for bf16 with d_feat = 16, d_qk = 64 and
+ * window <= 64 (q, k, q_win, k_win and v read once, y written once); an
+ * initial state with no large enough workspace has none.  The two-pass
+ * form runs the branches in turn on the stream (the window adds into y in
+ * place).  AUTO fuses where a fused kernel exists and the linear branch on
+ * its own would use the same 32-column launch plan (the fused kernel
+ * shares the SIMDs' vector units between the branches, so where the
+ * linear branch alone prefers 64-column groups with a segment split the
+ * two passes are faster); FUSED returns BASED_E_UNSUPPORTED where no fused
+ * kernel exists.
+ * Outputs must not overlap each other or any input (BASED_E_INVALID).
+ */
+enum { BASED_HYBRID_AUTO = 0, BASED_HYBRID_FUSED = 1, BASED_HYBRID_TWO_PASS = 2 };
+size_t based_hybrid_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
+
+based_status_t based_hybrid_prefill(const void *q, const void *k, const void *q_win,
+                                    const void *k_win, const void *v, based_dtype_t dtype,
+                                    int B, int H, int L, int d_feat, int d_qk, int d_v,
+                                    int chunk, float eps, int window, float scale, int path,
+                                    float *y, float *S, float *z, int use_initial_state,
+                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * swa_cache_fill / swa_decode_step -- next-token generation for the

@@ -20,6 +20,7 @@ import torch
 from . import _lib
 
 __all__ = ["based_prefill", "based_decode_step", "swa_forward", "swa_cache_fill", "swa_decode_step",
+           "based_hybrid_prefill", "based_hybrid_prefill_workspace_bytes",
            "based_prefill_backward", "based_prefill_backward_workspace_bytes",
            "based_num_features", "based_prefill_workspace_bytes", "BasedError", "library_path"]
 
@@ -107,6 +108,71 @@ def based_prefill(q, k, v, *, chunk: int = 64, eps: float = 1e-6, initial_state=
                                   d_v, chunk, eps, y.data_ptr(), S.data_ptr(), z.data_ptr(), use_init,
                                   ws_ptr, ws_bytes, _stream_ptr(dev))
     _lib.check("based_prefill", st)
+    return y, S, z
+
+
+def based_hybrid_prefill_workspace_bytes(B: int, H: int, L: int, d_v: int, d_feat: int = D_FEAT) -> int:
+    return _lib.lib().based_hybrid_prefill_workspace_bytes(B, H, L, d_feat, d_v)
+
+
+_HYBRID_PATHS = {"auto": 0, "fused": 1, "two_pass": 2}
+
+
+def based_hybrid_prefill(q, k, q_win, k_win, v, *, chunk: int = 64, eps: float = 1e-6, window: int = 64,
+                         scale: float | None = None, path: str = "auto", initial_state=None, y=None, S=None, z=None,
+                         workspace=None):
+    """The hybrid layer: Taylor linear attention of (q, k, v) plus the
+    causal sliding-window softmax of (q_win, k_win, v), each normalised on
+    its own.  ``path``: "auto" (the fused kernel where it exists and is the
+    faster choice), "fused" (error where none exists) or "two_pass".
+    Returns (y, S, z) as ``based_prefill`` (S, z: the linear branch's final
+    state)."""
+    if path not in _HYBRID_PATHS:
+        raise ValueError(f"path must be one of {sorted(_HYBRID_PATHS)}")
+    _check_tensor("q", q, ndim=4)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    for name, t in (("k", k), ("q_win", q_win), ("k_win", k_win), ("v", v)):
+        _check_tensor(name, t, dt, 4)
+    B, H, L, d = q.shape
+    d_qk = q_win.shape[-1]
+    d_v = v.shape[-1]
+    if (k.shape != q.shape or k_win.shape != q_win.shape or q_win.shape[:3] != (B, H, L)
+            or v.shape[:3] != (B, H, L)):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} q_win{tuple(q_win.shape)} "
+                         f"k_win{tuple(k_win.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = d_qk ** -0.5
+    F = 1 + d + d * d
+    dev = q.device
+    if y is None:
+        y = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev)
+    if S is None:
+        S = torch.empty((B, H, F, d_v), dtype=torch.float32, device=dev)
+    if z is None:
+        z = torch.empty((B, H, F), dtype=torch.float32, device=dev)
+    _check_tensor("y", y, torch.float32)
+    _check_tensor("S", S, torch.float32)
+    _check_tensor("z", z, torch.float32)
+    use_init = 0
+    if initial_state is not None:
+        S0, z0 = initial_state
+        if S0.data_ptr() != S.data_ptr():
+            S.copy_(S0)
+        if z0.data_ptr() != z.data_ptr():
+            z.copy_(z0)
+        use_init = 1
+    if workspace is None and dt == torch.bfloat16:
+        nbytes = based_hybrid_prefill_workspace_bytes(B, H, L, d_v, d)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    st = _lib.lib().based_hybrid_prefill(q.data_ptr(), k.data_ptr(), q_win.data_ptr(), k_win.data_ptr(),
+                                         v.data_ptr(), _DTYPES[dt], B, H, L, d, d_qk, d_v, chunk, eps, window,
+                                         scale, _HYBRID_PATHS[path], y.data_ptr(), S.data_ptr(), z.data_ptr(),
+                                         use_init, ws_ptr, ws_bytes, _stream_ptr(dev))
+    _lib.check("based_hybrid_prefill", st)
     return y, S, z
 
 

@@ -28,6 +28,9 @@ SIGNATURES = {
     "swa_forward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "swa_cache_fill": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "swa_decode_step": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P]),
+    "based_hybrid_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "based_hybrid_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _F, _I, _P, _P, _P,
+                                  _I, _P, _S, _P]),
     "based_prefill_backward_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "based_prefill_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _S, _P]),
 }

@@ -170,6 +170,72 @@ BASED_API based_status_t swa_forward(const void* q, const void* k, const void* v
         based::launch_swa_valu(q, k, v, bf16, (int)BH, L, d_qk, window, scale, add, y, st));
 }
 
+BASED_API size_t based_hybrid_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v) {
+    uint64_t BH, BHL;
+    if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return 0;
+    if (d_feat != kDFeatMfma || d_v != 64) return 0;
+    const size_t a = based::prefill_mfma_workspace_bytes((int)BH, L, d_v);
+    const size_t b = based::hybrid_mfma_workspace_bytes((int)BH, L, d_v);
+    return a > b ? a : b;
+}
+
+BASED_API based_status_t based_hybrid_prefill(const void* q, const void* k, const void* q_win, const void* k_win,
+                                              const void* v, based_dtype_t dtype, int B, int H, int L, int d_feat,
+                                              int d_qk, int d_v, int chunk, float eps, int window, float scale,
+                                              int path, float* y, float* S, float* z, int use_initial_state,
+                                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (path != BASED_HYBRID_AUTO && path != BASED_HYBRID_FUSED && path != BASED_HYBRID_TWO_PASS)
+        return BASED_E_INVALID;
+    if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_E_INVALID;
+    if (!q || !k || !q_win || !k_win || !v || !y || !S || !z) return BASED_E_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_win) || !aligned16(k_win) || !aligned16(v) ||
+        !aligned16(y) || !aligned16(S) || !aligned16(z) || (workspace && !aligned16(workspace)))
+        return BASED_E_INVALID;
+    if (!isfinite(eps) || !isfinite(scale) || chunk < 1 || d_feat < 1 || d_qk < 1 || d_v < 1 || window < 1)
+        return BASED_E_INVALID;
+    uint64_t BH, BHL;
+    if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
+    if (!feat_dim_ok(d_feat) || d_v != 64 || (d_qk != 16 && d_qk != 64) || window > 128)
+        return BASED_E_UNSUPPORTED;
+    const bool bf16 = dtype == BASED_BF16;
+    const bool mfma = bf16 && d_feat == kDFeatMfma;
+    if (chunk != 64 && (mfma || (chunk != 16 && chunk != 32))) return BASED_E_UNSUPPORTED;
+    const uint64_t es = elem_size(dtype);
+    const uint64_t F = (uint64_t)based_num_features(d_feat);
+    const void* ins[5] = {q, k, q_win, k_win, v};
+    const uint64_t in_bytes[5] = {BHL * d_feat * es, BHL * d_feat * es, BHL * d_qk * es, BHL * d_qk * es,
+                                  BHL * d_v * es};
+    const void* outs[3] = {y, S, z};
+    const uint64_t out_bytes[3] = {BHL * d_v * 4, BH * F * d_v * 4, BH * F * 4};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return BASED_E_INVALID;
+        for (int b = 0; b < 5; ++b)
+            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return BASED_E_INVALID;
+    }
+    if (BH * (((uint64_t)L + 63) / 64) > (uint64_t)INT32_MAX / 2) return BASED_E_INVALID;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // The fused pass where it exists and is chosen; otherwise the two
+    // branches in turn (the window adds into y in place).
+    const bool fusable = mfma && d_qk == 64 && window <= 64;
+    if (path == BASED_HYBRID_FUSED && !fusable) return BASED_E_UNSUPPORTED;
+    const bool fuse = path == BASED_HYBRID_FUSED ||
+                      (path == BASED_HYBRID_AUTO && fusable &&
+                       based::hybrid_mfma_preferred((int)BH, L, d_v, use_initial_state != 0, workspace != nullptr));
+    if (fuse) {
+        bool launched = false;
+        const hipError_t e = based::launch_hybrid_mfma(q, k, q_win, k_win, v, (int)BH, L, d_v, eps, window, scale, y,
+                                                       S, z, use_initial_state ? 1 : 0, workspace, workspace_bytes,
+                                                       st, &launched);
+        if (launched) return launch_status(e);
+        if (path == BASED_HYBRID_FUSED) return BASED_E_UNSUPPORTED;
+    }
+    const based_status_t s = based_prefill(q, k, v, dtype, B, H, L, d_feat, d_v, chunk, eps, y, S, z,
+                                           use_initial_state, workspace, workspace_bytes, stream);
+    if (s != BASED_OK) return s;
+    return swa_forward(q_win, k_win, v, dtype, B, H, L, d_qk, d_v, window, scale, y, y, stream);
+}
+
 namespace {
 
 // Shared checks of the window cache entry points.

@@ -23,6 +23,16 @@ hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, bool
 // splits each head into segments of seg_len tokens (a multiple of 64); the
 // workspace then holds one carried state per segment.
 size_t prefill_mfma_workspace_bytes(int BH, int L, int dv);
+// Fused hybrid layer (prefill_mfma.hip): y = linear attention (q, k, v) +
+// the w <= 64 window (q2, k2 of dim 64, the same v), bf16, d' = 16; final
+// state into S, z.  *launched is false when no fused plan fits the
+// arguments (then nothing ran).
+size_t hybrid_mfma_workspace_bytes(int BH, int L, int dv);
+// Whether the fused kernel is the faster choice for this shape.
+bool hybrid_mfma_preferred(int BH, int L, int dv, bool use_init, bool have_ws);
+hipError_t launch_hybrid_mfma(const void* q, const void* k, const void* q2, const void* k2, const void* v, int BH,
+                              int L, int dv, float eps, int window, float scale, float* y, float* S, float* z,
+                              int use_init, void* ws, size_t ws_bytes, hipStream_t st, bool* launched);
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int BH, int L, int dv,
                                float eps, float* y, float* S, float* z, int use_init,
                                void* workspace, size_t workspace_bytes, hipStream_t st);

@@ -47,6 +47,8 @@
 //  * Q, K, V of chunk c+1 are fetched into registers two chunks ahead and
 //    written to the other LDS buffer during chunk c (V and K transposed).
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -98,6 +100,26 @@ struct PrefillSmem {
     // off-diagonal hand-off: [chunk parity][query tile][column tile][lane] f32x4
     alignas(16) float hand[2][4][(DV / 16 + 1) * 64 * 4];
 };
+
+// ---- fused window branch (the hybrid layer): LDS of the four window waves.
+// K of the window branch as [64][64] bf16 tiles (16-byte units XOR-swizzled
+// by the row's low bits) and V (the workgroup's 32 value columns) as
+// row-major [64][32], each in a ring of three chunks: c-1 and c in use,
+// c+1 being written.  The normalised window output of chunk c goes to the
+// on-diagonal wave of its query tile through `hand` (chunk parity).
+constexpr int kWinD = 64;     // window q/k dim
+constexpr int kWinCols = 32;  // value columns per workgroup of the fused layer
+struct WinSmem {
+    alignas(16) uint16_t k[3][kC * kWinD];
+    alignas(16) uint16_t v[3][kC * kWinCols];
+    alignas(16) float hand[2][4][2 * 64 * 4];  // [parity][query tile][column tile][lane] f32x4
+};
+struct WinNone {
+    int unused;
+};
+__device__ __forceinline__ int win_idx(int row, int col) {
+    return row * kWinD + 8 * ((col >> 3) ^ (row & 7)) + (col & 7);
+}
 
 enum { kModeFull = 0, kModeState = 1, kModeSegment = 2 };
 
@@ -621,13 +643,176 @@ __device__ __forceinline__ void offdiag_wave(const uint16_t* __restrict__ qh, co
     }
 }
 
+// ---- window wave DQ of the fused layer: the w <= 64 softmax window of
+// query tile DQ ("Simple linear attention language models balance the
+// recall-throughput tradeoff", s4 "Local Exact Attention") over the keys of
+// chunks c-1 and c.  Interval c stages chunk c+1 (K and V through
+// registers; this wave's q rows of chunk c+1 into registers), computes
+// chunk c and hands the normalised output to the on-diagonal wave of the
+// tile, which adds it when it finishes chunk c in interval c+1.
+struct WinRegs {
+    u32x4 k0, k1, v;
+};
+// t = 0..255 (thread of the window waves): K units t and t + 256 (row =
+// unit / 8, 16-byte unit = unit % 8), V unit t (row t / 4, unit t % 4).
+// Rows are clamped into [0, L): rows outside it only ever meet masked
+// weights (which are exactly 0).
+__device__ __forceinline__ void win_load(WinRegs& rg, const uint16_t* k2h, const uint16_t* v2h, int ldv, int t0,
+                                         int L, int t) {
+    const int rk0 = min(max(t0 + (t >> 3), 0), L - 1);
+    const int rk1 = min(max(t0 + 32 + (t >> 3), 0), L - 1);
+    const int rv = min(max(t0 + (t >> 2), 0), L - 1);
+    rg.k0 = *reinterpret_cast<const u32x4*>(k2h + (size_t)rk0 * kWinD + 8 * (t & 7));
+    rg.k1 = *reinterpret_cast<const u32x4*>(k2h + (size_t)rk1 * kWinD + 8 * (t & 7));
+    rg.v = *reinterpret_cast<const u32x4*>(v2h + (size_t)rv * ldv + 8 * (t & 3));
+}
+__device__ __forceinline__ void win_store(const WinRegs& rg, WinSmem& ws, int slot, int t) {
+    *reinterpret_cast<u32x4*>(&ws.k[slot][win_idx(t >> 3, 8 * (t & 7))]) = rg.k0;
+    *reinterpret_cast<u32x4*>(&ws.k[slot][win_idx(32 + (t >> 3), 8 * (t & 7))]) = rg.k1;
+    *reinterpret_cast<u32x4*>(&ws.v[slot][(t >> 2) * kWinCols + 8 * (t & 3)]) = rg.v;
+}
+// This lane's query row (dims 8g..8g+7 and 32+8g..32+8g+7): the B operand
+// of the two k-steps of the scores.
+__device__ __forceinline__ void win_qload(bf16x8 (&qb)[2], const uint16_t* q2h, int tok, int L, int g) {
+    const uint16_t* row = q2h + (size_t)min(tok, L - 1) * kWinD;
+    qb[0] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 8 * g));
+    qb[1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 32 + 8 * g));
+}
+// Transposed LDS read (ds_read_b64_tr_b16) of a row-major [64][32] V slot:
+// lane c of each 16-lane group passes the address of row rb + c/4, columns
+// col0 + 4(c%4) .. +3, and receives rows rb .. rb+3 of column col0 + c.
+__device__ __forceinline__ uint2 win_vtr(const uint16_t* vs, int rb, int col0, int c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const uint16_t* p = vs + (rb + (c >> 2)) * kWinCols + col0 + 4 * (c & 3);
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) s16x4*)(p)));
+}
+// Window output of query tile DQ for one chunk: o[ct] = sum_j p_ij v_j
+// (rows = queries 4g+m, columns 16ct + r) and o[2] = sum_j p_ij, with
+// p_ij = exp(scale q_i.k_j - max_j) over j in [i - window + 1, i], j >= 0.
+// Key tiles DQ-4 .. DQ of 16 keys (relative to the chunk; negative = the
+// previous chunk) cover every window of the tile.  kg0 is the chunk's first
+// token (global).  Scores are computed as K Q^T: lane (g, r) holds query r,
+// keys 4g..4g+3 of each tile, the A operand of P V.
+// FULL64: window == 64 and the chunk is not the sequence's first, so every
+// key tile but the first (keys 4g+m > r in the window) and the last
+// (4g+m <= r, causal) is wholly inside every query's window.
+template <int DQ, bool FULL64>
+__device__ __forceinline__ void win_block(const WinSmem& ws, int cur, int prev, const bf16x8 (&qb)[2], int kg0,
+                                          int window, float sl2, int g, int r, f32x4 (&o)[3]) {
+    const bf16x8 ones = ones8();
+    const int rho = 16 * DQ + r;
+    float p[5][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int jt = DQ - 4 + i;
+        const uint16_t* kt = &ws.k[jt < 0 ? prev : cur][0];
+        const int row = 16 * ((jt + 4) & 3) + r;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        sc = mfma32(lds_bf16x8(kt + win_idx(row, 8 * g)), qb[0], sc);
+        sc = mfma32(lds_bf16x8(kt + win_idx(row, 32 + 8 * g)), qb[1], sc);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int kap = 16 * jt + 4 * g + m;
+            bool ok;
+            if constexpr (FULL64) ok = i == 0 ? 4 * g + m > r : (i == 4 ? 4 * g + m <= r : true);
+            else ok = kap <= rho && kap > rho - window && kg0 + kap >= 0;
+            p[i][m] = ok ? sc[m] * sl2 : -INFINITY;
+            mx = fmaxf(mx, p[i][m]);
+        }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // finite: the query's own key is always in
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) p[i][m] = __builtin_amdgcn_exp2f(p[i][m] - mx);
+#pragma unroll
+    for (int ct = 0; ct < 3; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+        const bool two = 2 * ks + 1 < 5;
+        float x[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            x[m] = p[2 * ks][m];
+            x[4 + m] = two ? p[two ? 2 * ks + 1 : 0][m] : 0.f;
+        }
+        bf16x8 ahi, alo;
+        pack8_hilo(x, ahi, alo);
+        const int j0 = DQ - 4 + 2 * ks, j1 = j0 + 1;
+        const uint16_t* v0 = &ws.v[j0 < 0 ? prev : cur][0];
+        const uint16_t* v1 = &ws.v[j1 < 0 ? prev : cur][0];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const uint2 a = win_vtr(v0, 16 * ((j0 + 4) & 3) + 4 * g, 16 * ct, r);
+            const uint2 b = two ? win_vtr(v1, 16 * ((j1 + 4) & 3) + 4 * g, 16 * ct, r) : make_uint2(0u, 0u);
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+            o[ct] = mfma32(ahi, vb, o[ct]);
+            o[ct] = mfma32(alo, vb, o[ct]);
+        }
+        o[2] = mfma32(ahi, ones, o[2]);
+        o[2] = mfma32(alo, ones, o[2]);
+    }
+}
+
+template <int DQ, int MODE>
+__device__ __forceinline__ void window_wave(const uint16_t* __restrict__ q2h, const uint16_t* __restrict__ k2h,
+                                            const uint16_t* __restrict__ v2h, int ldv, int L, int tb, int len,
+                                            int window, float sl2, WinSmem& ws) {
+    const int t = threadIdx.x - 768;  // 0..255
+    const int lane = t & 63, g = lane >> 4, r = lane & 15;
+    const int nchunks = (len + kC - 1) / kC;
+    if constexpr (MODE == kModeState) {
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) __syncthreads();
+        return;
+    }
+    WinRegs rg;
+    bf16x8 qc[2], qn[2];
+    // prologue: chunk -1 (the halo of the first chunk) into slot 2, chunk 0 into slot 0
+    win_load(rg, k2h, v2h, ldv, tb - kC, L, t);
+    win_store(rg, ws, 2, t);
+    win_load(rg, k2h, v2h, ldv, tb, L, t);
+    win_store(rg, ws, 0, t);
+    win_qload(qc, q2h, tb + 16 * DQ + r, L, g);
+    __syncthreads();  // first chunk staged
+    for (int c = 0; c < nchunks; ++c) {
+        const bool more = c + 1 < nchunks;
+        if (more) {
+            win_load(rg, k2h, v2h, ldv, tb + (c + 1) * kC, L, t);
+            win_qload(qn, q2h, tb + (c + 1) * kC + 16 * DQ + r, L, g);
+        }
+        f32x4 o[3];
+        if (window == kWinD && tb + c * kC >= kC)
+            win_block<DQ, true>(ws, c % 3, (c + 2) % 3, qc, tb + c * kC, window, sl2, g, r, o);
+        else
+            win_block<DQ, false>(ws, c % 3, (c + 2) % 3, qc, tb + c * kC, window, sl2, g, r, o);
+        f32x4* dst = reinterpret_cast<f32x4*>(&ws.hand[c & 1][DQ][0]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            f32x4 x;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) x[m] = o[ct][m] * __builtin_amdgcn_rcpf(o[2][m]);  // o[2] >= 1
+            dst[ct * 64 + lane] = x;
+        }
+        if (more) {
+            win_store(rg, ws, (c + 1) % 3, t);
+            qc[0] = qn[0];
+            qc[1] = qn[1];
+        }
+        __syncthreads();
+    }
+}
+
 // ---- on-diagonal wave DQ: the intra-chunk term of query tile DQ.  Interval
 // c computes it for chunk c and finishes chunk c-1: the off-diagonal part
 // (handed over during interval c-1) is added, the rows are normalised and
 // stored.
-template <int DQ, int DV, int MODE>
+template <int DQ, int DV, int MODE, bool HYB, class WinT>
 __device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps,
-                                            float* __restrict__ yh, PrefillSmem<DV>& sm) {
+                                            float* __restrict__ yh, PrefillSmem<DV>& sm, const WinT& wsm) {
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (L + kC - 1) / kC;
@@ -645,6 +830,25 @@ __device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps,
 #pragma unroll
         for (int ct = 0; ct < kNCT; ++ct) y[ct] = src[ct * 64 + lane] + yd[ct];
         float* ybase = yh + (size_t)c * kC * ldv;
+        if constexpr (HYB) {
+            // fused layer: plus the window output of the same rows
+            // (normalised on its own), one column tile at a time
+            const f32x4* hw = reinterpret_cast<const f32x4*>(&wsm.hand[c & 1][DQ][0]);
+            float inv[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) inv[m] = __builtin_amdgcn_rcpf(y[kNV][m] + eps);
+#pragma unroll
+            for (int ct = 0; ct < kNV; ++ct) {
+                const f32x4 yw = hw[ct * 64 + lane];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int tq = 16 * DQ + 4 * g + m;
+                    if (tq < nrows)
+                        __builtin_nontemporal_store(fmaf(y[ct][m], inv[m], yw[m]), &ybase[tq * ldv + 16 * ct + r]);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int tq = 16 * DQ + 4 * g + m;
@@ -845,15 +1049,20 @@ __device__ __forceinline__ void ws_load(f32x4 (&acc)[DV / 16 + 1], const float* 
 //   kModeSegment: workgroup (head, s): outputs of segment s starting from
 //                 slot s (after the prefix sum); the last segment writes the
 //                 final state.
-template <int DV, int MODE>
-__global__ __launch_bounds__(768, 1) void prefill_mfma_kernel(const uint16_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ k,
-                                                              const uint16_t* __restrict__ v, int L,
-                                                              int ldv, int ncg, int seg_len, int nseg,
-                                                              float eps, float* __restrict__ y,
-                                                              float* __restrict__ S, float* __restrict__ z,
-                                                              int use_init, float* __restrict__ ws) {
+//   HYB:          the fused hybrid layer (32-column groups only): four more
+//                 waves (12..15) run the w <= 64 window of the same rows with
+//                 their own q2, k2 and the shared v, and the on-diagonal
+//                 waves store y_LA + y_window.
+template <int DV, int MODE, bool HYB = false>
+__global__ __launch_bounds__(HYB ? 1024 : 768, 1) void prefill_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int L, int ldv,
+    int ncg, int seg_len, int nseg, float eps, float* __restrict__ y, float* __restrict__ S, float* __restrict__ z,
+    int use_init, float* __restrict__ ws, const uint16_t* __restrict__ q2, const uint16_t* __restrict__ k2,
+    int window, float win_scale) {
+    static_assert(!HYB || DV == kWinCols, "the fused layer uses 32-column groups");
+    using WinT = std::conditional_t<HYB, WinSmem, WinNone>;
     __shared__ PrefillSmem<DV> sm;
+    __shared__ WinT wsm;
     // Workgroup -> (head, segment, column group), column group fastest.  The
     // 8 XCDs take workgroups round-robin; the remap gives each XCD a
     // contiguous run, so the column groups of a head (same Q, K) share an L2.
@@ -902,15 +1111,29 @@ __global__ __launch_bounds__(768, 1) void prefill_mfma_kernel(const uint16_t* __
         case 1: offdiag_wave<1, DV, MODE>(qh, kh, len, sm); break;
         case 2: offdiag_wave<2, DV, MODE>(qh, kh, len, sm); break;
         case 3: offdiag_wave<3, DV, MODE>(qh, kh, len, sm); break;
-        case 8: ondiag_wave<0, DV, MODE>(len, ldv, eps, yh, sm); break;
-        case 9: ondiag_wave<1, DV, MODE>(len, ldv, eps, yh, sm); break;
-        case 10: ondiag_wave<2, DV, MODE>(len, ldv, eps, yh, sm); break;
-        case 11: ondiag_wave<3, DV, MODE>(len, ldv, eps, yh, sm); break;
+        case 8: ondiag_wave<0, DV, MODE, HYB>(len, ldv, eps, yh, sm, wsm); break;
+        case 9: ondiag_wave<1, DV, MODE, HYB>(len, ldv, eps, yh, sm, wsm); break;
+        case 10: ondiag_wave<2, DV, MODE, HYB>(len, ldv, eps, yh, sm, wsm); break;
+        case 11: ondiag_wave<3, DV, MODE, HYB>(len, ldv, eps, yh, sm, wsm); break;
         case 4: update_wave<0, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
         case 5: update_wave<1, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
         case 6: update_wave<2, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
         case 7: update_wave<3, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
         default: break;
+    }
+    if constexpr (HYB) {
+        // window waves: head-based pointers, global token indices
+        const uint16_t* q2h = q2 + (size_t)head * L * kWinD;
+        const uint16_t* k2h = k2 + (size_t)head * L * kWinD;
+        const uint16_t* v2h = v + (size_t)head * L * ldv + col0;
+        const float sl2 = win_scale * 1.4426950408889634f;
+        switch (w) {
+            case 12: window_wave<0, MODE>(q2h, k2h, v2h, ldv, L, tb, len, window, sl2, wsm); break;
+            case 13: window_wave<1, MODE>(q2h, k2h, v2h, ldv, L, tb, len, window, sl2, wsm); break;
+            case 14: window_wave<2, MODE>(q2h, k2h, v2h, ldv, L, tb, len, window, sl2, wsm); break;
+            case 15: window_wave<3, MODE>(q2h, k2h, v2h, ldv, L, tb, len, window, sl2, wsm); break;
+            default: break;
+        }
     }
 }
 
@@ -980,14 +1203,18 @@ size_t plan_workspace_bytes(const PrefillPlan& pl, int BH) {
     return pl.dvl == 32 ? workspace_bytes_dvl<32>(BH, pl.ncg, pl.nseg) : workspace_bytes_dvl<64>(BH, pl.ncg, pl.nseg);
 }
 
-template <int DVL>
+// HYB: the fused hybrid layer (q2, k2, window, win_scale used); the state
+// pass of a segment split is the plain kernel's.
+template <int DVL, bool HYB = false>
 hipError_t launch_plan(const PrefillPlan& pl, const uint16_t* q, const uint16_t* k, const uint16_t* v, int BH,
                        int L, int dv, float eps, float* y, float* S, float* z, int use_init, void* ws,
-                       hipStream_t st) {
+                       hipStream_t st, const uint16_t* q2 = nullptr, const uint16_t* k2 = nullptr, int window = 0,
+                       float win_scale = 0.f) {
+    constexpr int kThreads = HYB ? 1024 : 768;
     const bool via_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
     if (!via_ws) {
-        hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeFull>), dim3(BH * pl.ncg), dim3(768), 0, st, q, k, v, L,
-                           dv, pl.ncg, L, 1, eps, y, S, z, use_init, nullptr);
+        hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeFull, HYB>), dim3(BH * pl.ncg), dim3(kThreads), 0, st, q, k,
+                           v, L, dv, pl.ncg, L, 1, eps, y, S, z, use_init, nullptr, q2, k2, window, win_scale);
         return hipGetLastError();
     }
     const int nchunks = (L + kC - 1) / kC;
@@ -996,12 +1223,12 @@ hipError_t launch_plan(const PrefillPlan& pl, const uint16_t* q, const uint16_t*
     float* wsf = static_cast<float*>(ws);
     const dim3 grid(BH * pl.ncg * nseg);
     hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeState>), grid, dim3(768), 0, st, q, k, v, L, dv, pl.ncg,
-                       seg_len, nseg, eps, y, S, z, use_init, wsf);
+                       seg_len, nseg, eps, y, S, z, use_init, wsf, nullptr, nullptr, 0, 0.f);
     const size_t slot = ws_slot_floats<DVL>();
     hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH * pl.ncg), dim3(256), 0, st,
                        wsf, nseg, BH * pl.ncg, slot);
-    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeSegment>), grid, dim3(768), 0, st, q, k, v, L, dv, pl.ncg,
-                       seg_len, nseg, eps, y, S, z, use_init, wsf);
+    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeSegment, HYB>), grid, dim3(kThreads), 0, st, q, k, v, L, dv,
+                       pl.ncg, seg_len, nseg, eps, y, S, z, use_init, wsf, q2, k2, window, win_scale);
     return hipGetLastError();
 }
 
@@ -1029,6 +1256,53 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int 
         default:  // no workspace for a carried d_v = 128 state: exact fp32 chunked kernel
             return launch_prefill_valu(q, k, v, true, BH, L, kDFeat, dv, kC, eps, y, S, z, use_init, st);
     }
+}
+
+// ---- fused hybrid layer: 32-column groups (the window waves' LDS fits
+// next to that plan), segments as for the plain prefill at that width.
+static PrefillPlan plan_hybrid(int BH, int L, int dv, bool use_init, bool have_ws) {
+    PrefillPlan pl;
+    const int nchunks = (L + kC - 1) / kC;
+    pl.dvl = kWinCols;
+    pl.ncg = dv / kWinCols;
+    const int units = BH * pl.ncg;
+    pl.nseg = 1;
+    if (units < kTargetWorkgroups && nchunks >= 4)
+        pl.nseg = max(1, min((kTargetWorkgroups + units - 1) / units, nchunks / 2));
+    const bool need_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
+    if (need_ws && !have_ws) {
+        pl.nseg = 1;
+        if (use_init && pl.ncg > 1) pl.dvl = 0;  // no plan: the caller runs the two branches in turn
+    }
+    return pl;
+}
+
+size_t hybrid_mfma_workspace_bytes(int BH, int L, int dv) {
+    const PrefillPlan pl = plan_hybrid(BH, L, dv, true, true);
+    const bool via_ws = pl.nseg > 1 || pl.ncg > 1;
+    return via_ws ? plan_workspace_bytes(pl, BH) : 0;
+}
+
+bool hybrid_mfma_preferred(int BH, int L, int dv, bool use_init, bool have_ws) {
+    // The fused kernel carries the window's vector work on the same SIMDs as
+    // the linear branch, so it pays where the linear branch would take the
+    // same 32-column plan anyway; where that branch's own plan is 64-column
+    // groups with a segment split, the two passes are faster.
+    return plan_prefill(BH, L, dv, use_init, have_ws).dvl == kWinCols;
+}
+
+hipError_t launch_hybrid_mfma(const void* q, const void* k, const void* q2, const void* k2, const void* v, int BH,
+                              int L, int dv, float eps, int window, float scale, float* y, float* S, float* z,
+                              int use_init, void* ws, size_t ws_bytes, hipStream_t st, bool* launched) {
+    PrefillPlan pl = plan_hybrid(BH, L, dv, use_init != 0, ws != nullptr);
+    const bool via_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
+    if (via_ws && ws_bytes < plan_workspace_bytes(pl, BH)) pl = plan_hybrid(BH, L, dv, use_init != 0, false);
+    *launched = pl.dvl == kWinCols;
+    if (!*launched) return hipSuccess;
+    return launch_plan<kWinCols, true>(pl, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                       static_cast<const uint16_t*>(v), BH, L, dv, eps, y, S, z, use_init, ws, st,
+                                       static_cast<const uint16_t*>(q2), static_cast<const uint16_t*>(k2), window,
+                                       scale);
 }
 
 }  // namespace based

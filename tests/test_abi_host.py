@@ -40,7 +40,7 @@ def lib():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for want in ("based_prefill", "based_decode_step", "swa_forward", "swa_cache_fill", "swa_decode_step",
-                 "based_prefill_backward", "based_prefill_backward_workspace_bytes",
+                 "based_hybrid_prefill", "based_hybrid_prefill_workspace_bytes", "based_prefill_backward", "based_prefill_backward_workspace_bytes",
                  "based_num_features", "based_prefill_workspace_bytes", "based_status_string"):
         assert want in names, names
 
@@ -166,6 +166,39 @@ def _swa_fill(lib, **kw):
 ])
 def test_swa_fill_rejects(lib, kw, want):
     assert _swa_fill(lib, **kw) == want
+
+
+V_ = 0x7F6000000000
+
+
+def _hyb(lib, **kw):
+    a = dict(q=A, k=B_, qw=C, kw=C + (1 << 32), v=V_, dtype=1, B=1, H=2, L=100, d=16, dqk=64, dv=64, chunk=64,
+             eps=1e-6, window=64, scale=0.125, path=0, y=Y, S=S, z=Z, init=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.based_hybrid_prefill(a["q"], a["k"], a["qw"], a["kw"], a["v"], a["dtype"], a["B"], a["H"], a["L"],
+                                    a["d"], a["dqk"], a["dv"], a["chunk"], a["eps"], a["window"], a["scale"],
+                                    a["path"], a["y"], a["S"], a["z"], a["init"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), 1), (dict(qw=None), 1), (dict(kw=None), 1), (dict(v=None), 1), (dict(z=None), 1),
+    (dict(y=Y + 4), 1), (dict(kw=C + 8), 1), (dict(ws=Z + (1 << 30) + 4), 1), (dict(dtype=5), 1), (dict(L=0), 1),
+    (dict(eps=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(window=0), 1), (dict(d=12), 2),
+    (dict(dv=128), 2), (dict(dqk=8), 2), (dict(window=200), 2), (dict(chunk=32), 2), (dict(y=A), 1),
+    (dict(S=Y), 1), (dict(z=V_), 1), (dict(y=C + (1 << 32)), 1), (dict(path=3), 1), (dict(path=-1), 1),
+    (dict(path=1, dqk=16), 2), (dict(path=1, dtype=0), 2), (dict(path=1, window=65), 2), (dict(path=1, d=8), 2),
+])
+def test_hybrid_rejects(lib, kw, want):
+    assert _hyb(lib, **kw) == want
+
+
+def test_hybrid_workspace_bytes(lib):
+    # at least what the linear branch alone asks for; zero where no matrix-core plan exists
+    for L in (100, 8192, 65536):
+        assert lib.based_hybrid_prefill_workspace_bytes(4, 16, L, 16, 64) >= lib.based_prefill_workspace_bytes(
+            4, 16, L, 16, 64)
+    assert lib.based_hybrid_prefill_workspace_bytes(4, 16, 8192, 16, 128) == 0
+    assert lib.based_hybrid_prefill_workspace_bytes(4, 16, 8192, 8, 64) == 0
 
 
 def _bwd(lib, **kw):

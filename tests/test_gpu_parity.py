@@ -565,6 +565,111 @@ def test_workload_long_64k():
     report("long_64k S (2 sampled heads)", ratio(S[0, hs], So), wl.tol)
 
 
+# ---------------------------------------------------------------- hybrid layer
+def _hybrid_inputs(B, H, L, seed, dqk=64, dtype=torch.bfloat16):
+    q, k, v = si.custom((B, H, L, 16), (B, H, L, 64), seed=seed, scale=0.5, dtype=dtype)
+    qw, kw, _ = si.custom((B, H, L, dqk), (1, 1, 1, 1), seed=seed + 10, scale=1.0, dtype=dtype)
+    return q, k, v, qw, kw
+
+
+@pytest.mark.parametrize("B,H,L", [(1, 2, 1), (2, 1, 33), (1, 2, 130), (2, 3, 257), (1, 2, 1000), (4, 64, 200)])
+@pytest.mark.parametrize("window", [64, 17])
+def test_hybrid_matches_oracle(B, H, L, window):
+    """y = linear attention + window (each normalised on its own) in one
+    pass, and the linear branch's final state.  The shapes cover one token,
+    one chunk, a ragged tail, the segment split of few heads (the window's
+    halo crosses every segment start) and the unsplit plan of many heads."""
+    based = based_mod()
+    q, k, v, qw, kw = _hybrid_inputs(B, H, L, seed=2400 + L + window + B)
+    y, S, z = based.based_hybrid_prefill(*dev(q, k, qw, kw, v), window=window, scale=0.125, path="fused")
+    torch.cuda.synchronize()
+    yo, So, zo = oracle.la_recurrent(q, k, v)
+    want = yo + oracle.swa(qw, kw, v, window, 0.125)
+    report(f"hybrid B={B} H={H} L={L} w={window} y", ratio(y, want), 2e-2)
+    report(f"hybrid B={B} H={H} L={L} w={window} S", ratio(S, So), 2e-2)
+    report(f"hybrid B={B} H={H} L={L} w={window} z", ratio(z, zo), 2e-2)
+
+
+@pytest.mark.parametrize("ws", ["auto", "none"])
+def test_hybrid_initial_state(ws):
+    """A carried linear-attention state (fused); with no workspace the fused
+    kernel has no plan for two column groups, so "auto" runs the branches in
+    turn and "fused" refuses."""
+    based = based_mod()
+    L = 300
+    q, k, v, qw, kw = _hybrid_inputs(1, 3, L, seed=2450)
+    qp, kp, vp = si.custom((1, 3, 50, 16), (1, 3, 50, 64), seed=2452, scale=0.5)
+    _, S0, z0 = oracle.la_recurrent(qp, kp, vp, want_y=False)
+    S0, z0 = torch.as_tensor(S0, dtype=torch.float32), torch.as_tensor(z0, dtype=torch.float32)
+    kwargs = {"path": "fused"} if ws == "auto" else {"workspace": torch.empty(0, dtype=torch.uint8, device=DEV)}
+    if ws == "none":
+        with pytest.raises(based.BasedError):
+            based.based_hybrid_prefill(*dev(q, k, qw, kw, v), initial_state=tuple(dev(S0, z0)), path="fused", **kwargs)
+    y, S, z = based.based_hybrid_prefill(*dev(q, k, qw, kw, v), initial_state=tuple(dev(S0, z0)), **kwargs)
+    yo, So, zo = oracle.la_recurrent(q, k, v, S0=S0, z0=z0)
+    want = yo + oracle.swa(qw, kw, v, 64, 0.125)
+    report(f"hybrid init-state ws={ws} y", ratio(y, want), 2e-2)
+    report(f"hybrid init-state ws={ws} S", ratio(S, So), 2e-2)
+    report(f"hybrid init-state ws={ws} z", ratio(z, zo), 2e-2)
+
+
+@pytest.mark.parametrize("dtype,tol,dqk,window", [
+    (torch.bfloat16, 2e-2, 16, 64), (torch.bfloat16, 2e-2, 64, 100), (torch.float32, 1e-4, 64, 64),
+])
+def test_hybrid_composed_paths(dtype, tol, dqk, window):
+    """Arguments without a fused kernel (16-dim window q/k, a window over
+    64, fp32) run the two branches in turn; same result."""
+    based = based_mod()
+    q, k, v, qw, kw = _hybrid_inputs(1, 2, 200, seed=2460 + dqk + window, dqk=dqk, dtype=dtype)
+    scale = dqk ** -0.5
+    y, S, z = based.based_hybrid_prefill(*dev(q, k, qw, kw, v), window=window, scale=scale)
+    yo, So, zo = oracle.la_recurrent(q, k, v)
+    report(f"hybrid composed {dtype} dqk={dqk} w={window} y", ratio(y, yo + oracle.swa(qw, kw, v, window, scale)),
+           tol)
+    report(f"hybrid composed {dtype} dqk={dqk} w={window} S", ratio(S, So), tol)
+
+
+def test_workload_window_8k_fused():
+    """The 8K hybrid layer (B=4, H=16, L=8192) through the fused kernel, 3
+    sampled heads against the oracle, and every element against the two
+    branches run in turn (the same arithmetic up to rounding order)."""
+    based = based_mod()
+    wl = si.WORKLOADS["window_8k"]
+    q, k, v = si.linear_inputs(wl)
+    qw, kw = si.window_inputs(wl)
+    qd, kd, vd, qwd, kwd = dev(q, k, v, qw, kw)
+    y, S, z = based.based_hybrid_prefill(qd, kd, qwd, kwd, vd, chunk=wl.chunk, eps=wl.eps, window=wl.window,
+                                         scale=wl.swa_scale, path="fused")
+    y2, S2, z2 = based.based_prefill(qd, kd, vd, chunk=wl.chunk, eps=wl.eps)
+    based.swa_forward(qwd, kwd, vd, window=wl.window, scale=wl.swa_scale, add=y2, y=y2)
+    torch.cuda.synchronize()
+    heads = _sample_heads(wl.B, wl.H, 3, 7)
+    bi = [b for b, _ in heads]
+    hi = [h for _, h in heads]
+    yo, So, zo = oracle.la_recurrent(q[bi, hi], k[bi, hi], v[bi, hi], eps=wl.eps)
+    want = yo + oracle.swa(qw[bi, hi], kw[bi, hi], v[bi, hi], wl.window, wl.swa_scale)
+    report("window_8k fused layer (3 sampled heads) y", ratio(y[bi, hi], want), wl.tol)
+    report("window_8k fused layer (3 sampled heads) S", ratio(S[bi, hi], So), wl.tol)
+    report("window_8k fused vs two passes (all heads)", float((y - y2).abs().max() / y2.pow(2).mean().sqrt()), wl.tol)
+
+
+@pytest.mark.parametrize("B,H,L", [(8, 16, 256), (1, 2, 700)])
+def test_hybrid_paths_agree(B, H, L):
+    """auto, fused and two-pass give the same layer (rounding order aside),
+    on a shape auto fuses (32-column plan) and one it does not fuse."""
+    based = based_mod()
+    q, k, v, qw, kw = _hybrid_inputs(B, H, L, seed=2480 + L)
+    outs = {p: based.based_hybrid_prefill(*dev(q, k, qw, kw, v), scale=0.125, path=p)
+            for p in ("auto", "fused", "two_pass")}
+    torch.cuda.synchronize()
+    ref = outs["two_pass"][0]
+    rms = float(ref.pow(2).mean().sqrt())
+    for p in ("auto", "fused"):
+        report(f"hybrid {p} vs two-pass B={B} H={H} L={L}", float((outs[p][0] - ref).abs().max()) / rms, 2e-2)
+        report(f"hybrid {p} vs two-pass S B={B} H={H} L={L}",
+               float((outs[p][1] - outs["two_pass"][1]).abs().max() / outs["two_pass"][1].pow(2).mean().sqrt()), 2e-2)
+
+
 def test_workload_window_8k():
     based = based_mod()
     wl = si.WORKLOADS["window_8k"]
