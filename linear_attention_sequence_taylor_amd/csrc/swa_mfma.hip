@@ -51,13 +51,15 @@ struct SwaSlots {
     uint16_t *kn, *vn, *qn;
 };
 
-// a[i] for a wave-uniform i, as a chain of selects (no indexed local array).
+// a[(16w + 16j) / 64] for the wave index w (0..3) and a tile offset j that
+// is a constant once the caller's loop is unrolled: one of the two
+// neighbouring entries a[j/4] and a[j/4 + 1], chosen by one scalar compare
+// (a longer select chain is turned into an indexed stack array).
 template <int N>
-__device__ __forceinline__ const uint16_t* pick_slot(const uint16_t* const (&a)[N], int i) {
-    const uint16_t* p = a[0];
-#pragma unroll
-    for (int n = 1; n < N; ++n) p = i == n ? a[n] : p;
-    return p;
+__device__ __forceinline__ const uint16_t* slot_of(const uint16_t* const (&a)[N], int w, int j) {
+    const int b = j >> 2;
+    if (b + 1 >= N) return a[N - 1];
+    return w + (j & 3) >= 4 ? a[b + 1] : a[b];
 }
 
 // Element offset of (row, col) in a [64][D] bf16 tile whose 16-byte units
@@ -220,7 +222,7 @@ __device__ __forceinline__ void swa_tile(const SwaSlots<HALO>& sl, int t, int wi
 #pragma unroll
     for (int j = 0; j < kKT; ++j) {
         const int R = 16 * w + 16 * j;
-        const f32x4 st = score_tile<DQK>(pick_slot(sl.k, R >> 6), R & 63, qs, 16 * w, g, r);
+        const f32x4 st = score_tile<DQK>(slot_of(sl.k, w, j), R & 63, qs, 16 * w, g, r);
         if (window == kHR && q0 >= kHR) {
             // Full window, no key before the sequence start: key 16j + 4g + m
             // is in the window of query r iff it lies in (r, r + 64*HALO], so
@@ -278,8 +280,8 @@ __device__ __forceinline__ void swa_tile(const SwaSlots<HALO>& sl, int t, int wi
         pack8_hilo(a, ahi, alo);
         // key rows of this lane group: R1 + 4g .. +3 (tile 2p), R2 + 4g .. +3 (tile 2p+1)
         const int R1 = 16 * w + 32 * p, R2 = R1 + 16;
-        const uint16_t* v1 = pick_slot(sl.v, R1 >> 6);
-        const uint16_t* v2 = pick_slot(sl.v, R2 >> 6);
+        const uint16_t* v1 = slot_of(sl.v, w, 2 * p);
+        const uint16_t* v2 = slot_of(sl.v, w, 2 * p + 1);
         const int r1 = (R1 & 63) + 4 * g, r2 = (R2 & 63) + 4 * g;
         bf16x8 vb[4];
         // the last k-step has no second key tile: that half of the operand is zero
