@@ -12,7 +12,8 @@
 // Decode step: HBM-bound (each cached key and value is read once per step).
 // One wave per (batch, head), four per workgroup, no workgroup barrier.
 // Lane j scores slot j (and j + 64 for windows over 64) from its key row
-// (16-byte loads); for P.V, lane
+// (16-byte loads; bf16 rows through packed bf16 dot products with fp32
+// sums); for P.V, lane
 // (key group kg, column group cg) accumulates 8 columns over the keys kg,
 // kg + KG, ... and the key groups are summed with lane shuffles.  Key and
 // value loads are all issued before any arithmetic, so a wave waits for
@@ -41,6 +42,18 @@ struct Chunk8<uint16_t> {
     __device__ __forceinline__ float get(int i) const {
         return (i & 1) ? bf16hi_f32(u[i >> 1]) : bf16lo_f32(u[i >> 1]);
     }
+    // acc[i] += the two products of pair i (v_dot2_f32_bf16: bf16 products,
+    // fp32 sum), with no widening of either operand.  Each element is copied
+    // to a scalar before the bit cast: a bit cast of a vector element
+    // expression reads the vector's first element instead.
+    __device__ __forceinline__ void dot_into(const Chunk8& o, float (&acc)[4]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t a = u[i], b = o.u[i];
+            acc[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc[i],
+                                                     false);
+        }
+    }
 };
 template <>
 struct Chunk8<float> {
@@ -51,6 +64,10 @@ struct Chunk8<float> {
     }
     __device__ __forceinline__ void zero() { a = b = f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ __forceinline__ float get(int i) const { return i < 4 ? a[i] : b[i - 4]; }
+    __device__ __forceinline__ void dot_into(const Chunk8& o, float (&acc)[4]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(b[i], o.b[i], fmaf(a[i], o.a[i], acc[i]));
+    }
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -154,11 +171,10 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
     float m = -INFINITY;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        float dot = 0.f;
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < kQC; ++c)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dot = fmaf(qr[c].get(e), kr[r][c].get(e), dot);
+        for (int c = 0; c < kQC; ++c) qr[c].dot_into(kr[r][c], part);
+        const float dot = (part[0] + part[1]) + (part[2] + part[3]);
         s[r] = lane + 64 * r < nvalid ? dot * (scale * kLog2e) : -INFINITY;
         m = fmaxf(m, s[r]);
     }
