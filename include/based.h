@@ -191,12 +191,9 @@ based_status_t swa_forward(const void *q, const void *k, const void *v,
  * window <= 64 (q, k, q_win, k_win and v read once, y written once); an
  * initial state with no large enough workspace has none.  The two-pass
  * form runs the branches in turn on the stream (the window adds into y in
- * place).  AUTO fuses where a fused kernel exists and the linear branch on
- * its own would use the same 32-column launch plan (the fused kernel
- * shares the SIMDs' vector units between the branches, so where the
- * linear branch alone prefers 64-column groups with a segment split the
- * two passes are faster); FUSED returns BASED_E_UNSUPPORTED where no fused
- * kernel exists.
+ * place).  AUTO fuses wherever a fused kernel exists; FUSED returns
+ * BASED_E_UNSUPPORTED where none does; TWO_PASS always runs the branches
+ * in turn.
  * Outputs must not overlap each other or any input (BASED_E_INVALID).
  */
 enum { BASED_HYBRID_AUTO = 0, BASED_HYBRID_FUSED = 1, BASED_HYBRID_TWO_PASS = 2 };

@@ -123,8 +123,8 @@ def based_hybrid_prefill(q, k, q_win, k_win, v, *, chunk: int = 64, eps: float =
                          workspace=None):
     """The hybrid layer: Taylor linear attention of (q, k, v) plus the
     causal sliding-window softmax of (q_win, k_win, v), each normalised on
-    its own.  ``path``: "auto" (the fused kernel where it exists and is the
-    faster choice), "fused" (error where none exists) or "two_pass".
+    its own.  ``path``: "auto" (the fused kernel wherever one exists),
+    "fused" (error where none exists) or "two_pass".
     Returns (y, S, z) as ``based_prefill`` (S, z: the linear branch's final
     state)."""
     if path not in _HYBRID_PATHS:

@@ -219,10 +219,7 @@ BASED_API based_status_t based_hybrid_prefill(const void* q, const void* k, cons
     // branches in turn (the window adds into y in place).
     const bool fusable = mfma && d_qk == 64 && window <= 64;
     if (path == BASED_HYBRID_FUSED && !fusable) return BASED_E_UNSUPPORTED;
-    const bool fuse = path == BASED_HYBRID_FUSED ||
-                      (path == BASED_HYBRID_AUTO && fusable &&
-                       based::hybrid_mfma_preferred((int)BH, L, d_v, use_initial_state != 0, workspace != nullptr));
-    if (fuse) {
+    if (path != BASED_HYBRID_TWO_PASS && fusable) {
         bool launched = false;
         const hipError_t e = based::launch_hybrid_mfma(q, k, q_win, k_win, v, (int)BH, L, d_v, eps, window, scale, y,
                                                        S, z, use_initial_state ? 1 : 0, workspace, workspace_bytes,

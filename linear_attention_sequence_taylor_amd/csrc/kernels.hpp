@@ -28,8 +28,6 @@ size_t prefill_mfma_workspace_bytes(int BH, int L, int dv);
 // state into S, z.  *launched is false when no fused plan fits the
 // arguments (then nothing ran).
 size_t hybrid_mfma_workspace_bytes(int BH, int L, int dv);
-// Whether the fused kernel is the faster choice for this shape.
-bool hybrid_mfma_preferred(int BH, int L, int dv, bool use_init, bool have_ws);
 hipError_t launch_hybrid_mfma(const void* q, const void* k, const void* q2, const void* k2, const void* v, int BH,
                               int L, int dv, float eps, int window, float scale, float* y, float* S, float* z,
                               int use_init, void* ws, size_t ws_bytes, hipStream_t st, bool* launched);

@@ -126,7 +126,8 @@ enum { kModeFull = 0, kModeState = 1, kModeSegment = 2 };
 template <int T, int DV>
 __device__ __forceinline__ void ws_store(const f32x4 (&acc)[DV / 16 + 1], float* slot, int lane);
 template <int T, int DV>
-__device__ __forceinline__ void ws_load(f32x4 (&acc)[DV / 16 + 1], const float* slot, int lane);
+__device__ __forceinline__ void ws_load(f32x4 (&acc)[DV / 16 + 1], const float* slot, int lane, int slot_nct,
+                                        int ct0);
 
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -877,7 +878,8 @@ template <int U, int DV, int MODE>
 __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, const uint16_t* __restrict__ kh,
                                             const uint16_t* __restrict__ vh, int L, int ldv, float* __restrict__ Sh,
                                             float* __restrict__ zh, bool own_z, int use_init, PrefillSmem<DV>& sm,
-                                            const float* ws_in, float* ws_out, bool write_final) {
+                                            const float* ws_in, float* ws_out, bool write_final, int ws_nct,
+                                            int ws_ct0) {
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
     constexpr int kNT = U < 2 ? 3 : 2;
     const int u = threadIdx.x - 256;  // 0..255
@@ -894,9 +896,9 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
 #pragma unroll
         for (int ct = 0; ct < kNCT; ++ct) acc[ti][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (MODE == kModeSegment) {
-        ws_load<U, DV>(acc[0], ws_in, lane);
-        ws_load<U + 4, DV>(acc[1], ws_in, lane);
-        if constexpr (kNT == 3) ws_load<U + 8, DV>(acc[2], ws_in, lane);
+        ws_load<U, DV>(acc[0], ws_in, lane, ws_nct, ws_ct0);
+        ws_load<U + 4, DV>(acc[1], ws_in, lane, ws_nct, ws_ct0);
+        if constexpr (kNT == 3) ws_load<U + 8, DV>(acc[2], ws_in, lane, ws_nct, ws_ct0);
     } else if (MODE == kModeFull && use_init) {
         load_initial<U, DV>(acc[0], Sh, zh, ldv, g, r);
         load_initial<U + 4, DV>(acc[1], Sh, zh, ldv, g, r);
@@ -1032,12 +1034,18 @@ __device__ __forceinline__ void ws_store(const f32x4 (&acc)[DV / 16 + 1], float*
 #pragma unroll
     for (int ct = 0; ct < kNCT; ++ct) p[ct * 64] = acc[ct];
 }
+// A slot may be wider than the reader: slot_nct column tiles per rotation
+// tile (the last one the normaliser), of which the reader takes ct0 ..
+// ct0 + DV/16 - 1 and the normaliser (a 32-column group reading a 64-column
+// slot).  slot_nct = DV/16 + 1, ct0 = 0 is the reader's own layout.
 template <int T, int DV>
-__device__ __forceinline__ void ws_load(f32x4 (&acc)[DV / 16 + 1], const float* slot, int lane) {
-    constexpr int kNCT = DV / 16 + 1;
-    const f32x4* p = reinterpret_cast<const f32x4*>(slot) + (size_t)T * kNCT * 64 + lane;
+__device__ __forceinline__ void ws_load(f32x4 (&acc)[DV / 16 + 1], const float* slot, int lane, int slot_nct,
+                                        int ct0) {
+    constexpr int kNV = DV / 16;
+    const f32x4* p = reinterpret_cast<const f32x4*>(slot) + (size_t)T * slot_nct * 64 + lane;
 #pragma unroll
-    for (int ct = 0; ct < kNCT; ++ct) acc[ct] = p[ct * 64];
+    for (int ct = 0; ct < kNV; ++ct) acc[ct] = p[(ct0 + ct) * 64];
+    acc[kNV] = p[(slot_nct - 1) * 64];
 }
 
 // One workgroup = 12 waves (roles above).  MODE
@@ -1086,9 +1094,18 @@ __global__ __launch_bounds__(HYB ? 1024 : 768, 1) void prefill_mfma_kernel(
     const bool own_z = cg == 0;  // every column group carries z; the first writes it
     float* ws_in = nullptr;
     float* ws_out = nullptr;
+    // The fused layer's segment pass reads the state of a 64-column state
+    // pass (one slot per head and segment): its column group's tiles of it.
+    int ws_nct = DV / 16 + 1, ws_ct0 = 0;
     if (MODE != kModeFull) {
-        ws_in = ws + (((size_t)seg * BH + head) * ncg + cg) * ws_slot_floats<DV>();
-        ws_out = ws + (((size_t)((seg + 1) % nseg) * BH + head) * ncg + cg) * ws_slot_floats<DV>();
+        if (HYB) {
+            ws_nct = 64 / 16 + 1;
+            ws_ct0 = (DV / 16) * cg;
+            ws_in = ws + ((size_t)seg * BH + head) * ws_slot_floats<64>();
+        } else {
+            ws_in = ws + (((size_t)seg * BH + head) * ncg + cg) * ws_slot_floats<DV>();
+            ws_out = ws + (((size_t)((seg + 1) % nseg) * BH + head) * ncg + cg) * ws_slot_floats<DV>();
+        }
     }
     const int w = threadIdx.x >> 6;
     if (MODE == kModeState && seg == nseg - 1) {
@@ -1115,10 +1132,10 @@ __global__ __launch_bounds__(HYB ? 1024 : 768, 1) void prefill_mfma_kernel(
         case 9: ondiag_wave<1, DV, MODE, HYB>(len, ldv, eps, yh, sm, wsm); break;
         case 10: ondiag_wave<2, DV, MODE, HYB>(len, ldv, eps, yh, sm, wsm); break;
         case 11: ondiag_wave<3, DV, MODE, HYB>(len, ldv, eps, yh, sm, wsm); break;
-        case 4: update_wave<0, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
-        case 5: update_wave<1, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
-        case 6: update_wave<2, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
-        case 7: update_wave<3, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final); break;
+        case 4: update_wave<0, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final, ws_nct, ws_ct0); break;
+        case 5: update_wave<1, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final, ws_nct, ws_ct0); break;
+        case 6: update_wave<2, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final, ws_nct, ws_ct0); break;
+        case 7: update_wave<3, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final, ws_nct, ws_ct0); break;
         default: break;
     }
     if constexpr (HYB) {
@@ -1203,18 +1220,14 @@ size_t plan_workspace_bytes(const PrefillPlan& pl, int BH) {
     return pl.dvl == 32 ? workspace_bytes_dvl<32>(BH, pl.ncg, pl.nseg) : workspace_bytes_dvl<64>(BH, pl.ncg, pl.nseg);
 }
 
-// HYB: the fused hybrid layer (q2, k2, window, win_scale used); the state
-// pass of a segment split is the plain kernel's.
-template <int DVL, bool HYB = false>
+template <int DVL>
 hipError_t launch_plan(const PrefillPlan& pl, const uint16_t* q, const uint16_t* k, const uint16_t* v, int BH,
                        int L, int dv, float eps, float* y, float* S, float* z, int use_init, void* ws,
-                       hipStream_t st, const uint16_t* q2 = nullptr, const uint16_t* k2 = nullptr, int window = 0,
-                       float win_scale = 0.f) {
-    constexpr int kThreads = HYB ? 1024 : 768;
+                       hipStream_t st) {
     const bool via_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
     if (!via_ws) {
-        hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeFull, HYB>), dim3(BH * pl.ncg), dim3(kThreads), 0, st, q, k,
-                           v, L, dv, pl.ncg, L, 1, eps, y, S, z, use_init, nullptr, q2, k2, window, win_scale);
+        hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeFull>), dim3(BH * pl.ncg), dim3(768), 0, st, q, k, v, L, dv,
+                           pl.ncg, L, 1, eps, y, S, z, use_init, nullptr, nullptr, nullptr, 0, 0.f);
         return hipGetLastError();
     }
     const int nchunks = (L + kC - 1) / kC;
@@ -1224,11 +1237,14 @@ hipError_t launch_plan(const PrefillPlan& pl, const uint16_t* q, const uint16_t*
     const dim3 grid(BH * pl.ncg * nseg);
     hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeState>), grid, dim3(768), 0, st, q, k, v, L, dv, pl.ncg,
                        seg_len, nseg, eps, y, S, z, use_init, wsf, nullptr, nullptr, 0, 0.f);
+    // (one segment: the slot already holds the initial state; with several,
+    // B*H*ncg is below the workgroup target, well inside the grid's y range)
     const size_t slot = ws_slot_floats<DVL>();
-    hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH * pl.ncg), dim3(256), 0, st,
-                       wsf, nseg, BH * pl.ncg, slot);
-    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeSegment, HYB>), grid, dim3(kThreads), 0, st, q, k, v, L, dv,
-                       pl.ncg, seg_len, nseg, eps, y, S, z, use_init, wsf, q2, k2, window, win_scale);
+    if (nseg > 1)
+        hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH * pl.ncg), dim3(256), 0,
+                           st, wsf, nseg, BH * pl.ncg, slot);
+    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeSegment>), grid, dim3(768), 0, st, q, k, v, L, dv, pl.ncg,
+                       seg_len, nseg, eps, y, S, z, use_init, wsf, nullptr, nullptr, 0, 0.f);
     return hipGetLastError();
 }
 
@@ -1259,16 +1275,18 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int 
 }
 
 // ---- fused hybrid layer: 32-column groups (the window waves' LDS fits
-// next to that plan), segments as for the plain prefill at that width.
+// next to that plan).  Long sequences with few heads split into segments as
+// the plain prefill would at 64 columns: a 64-column state pass and scan
+// (cheaper than two 32-column ones), then the fused 32-column segment pass
+// (two workgroups per head and segment) reads its columns of each slot.
 static PrefillPlan plan_hybrid(int BH, int L, int dv, bool use_init, bool have_ws) {
     PrefillPlan pl;
     const int nchunks = (L + kC - 1) / kC;
     pl.dvl = kWinCols;
     pl.ncg = dv / kWinCols;
-    const int units = BH * pl.ncg;
     pl.nseg = 1;
-    if (units < kTargetWorkgroups && nchunks >= 4)
-        pl.nseg = max(1, min((kTargetWorkgroups + units - 1) / units, nchunks / 2));
+    if (BH * pl.ncg < kTargetWorkgroups && nchunks >= 4)
+        pl.nseg = max(1, min((kTargetWorkgroups + BH - 1) / BH, nchunks / 2));
     const bool need_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
     if (need_ws && !have_ws) {
         pl.nseg = 1;
@@ -1277,18 +1295,41 @@ static PrefillPlan plan_hybrid(int BH, int L, int dv, bool use_init, bool have_w
     return pl;
 }
 
+static size_t hybrid_ws_bytes(const PrefillPlan& pl, int BH) {
+    return (size_t)pl.nseg * BH * ws_slot_floats<64>() * sizeof(float);
+}
+
 size_t hybrid_mfma_workspace_bytes(int BH, int L, int dv) {
     const PrefillPlan pl = plan_hybrid(BH, L, dv, true, true);
     const bool via_ws = pl.nseg > 1 || pl.ncg > 1;
-    return via_ws ? plan_workspace_bytes(pl, BH) : 0;
+    return via_ws ? hybrid_ws_bytes(pl, BH) : 0;
 }
 
-bool hybrid_mfma_preferred(int BH, int L, int dv, bool use_init, bool have_ws) {
-    // The fused kernel carries the window's vector work on the same SIMDs as
-    // the linear branch, so it pays where the linear branch would take the
-    // same 32-column plan anyway; where that branch's own plan is 64-column
-    // groups with a segment split, the two passes are faster.
-    return plan_prefill(BH, L, dv, use_init, have_ws).dvl == kWinCols;
+static hipError_t launch_hybrid_plan(const PrefillPlan& pl, const uint16_t* q, const uint16_t* k,
+                                     const uint16_t* v, int BH, int L, int dv, float eps, float* y, float* S,
+                                     float* z, int use_init, void* ws, hipStream_t st, const uint16_t* q2,
+                                     const uint16_t* k2, int window, float win_scale) {
+    const bool via_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
+    if (!via_ws) {
+        hipLaunchKernelGGL((prefill_mfma_kernel<kWinCols, kModeFull, true>), dim3(BH * pl.ncg), dim3(1024), 0, st, q,
+                           k, v, L, dv, pl.ncg, L, 1, eps, y, S, z, use_init, nullptr, q2, k2, window, win_scale);
+        return hipGetLastError();
+    }
+    const int nchunks = (L + kC - 1) / kC;
+    const int seg_len = ((nchunks + pl.nseg - 1) / pl.nseg) * kC;
+    const int nseg = (L + seg_len - 1) / seg_len;
+    float* wsf = static_cast<float*>(ws);
+    // state pass and scan at 64 columns (d_v = 64: one column group)
+    hipLaunchKernelGGL((prefill_mfma_kernel<64, kModeState>), dim3(BH * nseg), dim3(768), 0, st, q, k, v, L, dv, 1,
+                       seg_len, nseg, eps, y, S, z, use_init, wsf, nullptr, nullptr, 0, 0.f);
+    const size_t slot = ws_slot_floats<64>();
+    if (nseg > 1)
+        hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH), dim3(256), 0, st, wsf,
+                           nseg, BH, slot);
+    hipLaunchKernelGGL((prefill_mfma_kernel<kWinCols, kModeSegment, true>), dim3(BH * pl.ncg * nseg), dim3(1024), 0,
+                       st, q, k, v, L, dv, pl.ncg, seg_len, nseg, eps, y, S, z, use_init, wsf, q2, k2, window,
+                       win_scale);
+    return hipGetLastError();
 }
 
 hipError_t launch_hybrid_mfma(const void* q, const void* k, const void* q2, const void* k2, const void* v, int BH,
@@ -1296,13 +1337,12 @@ hipError_t launch_hybrid_mfma(const void* q, const void* k, const void* q2, cons
                               int use_init, void* ws, size_t ws_bytes, hipStream_t st, bool* launched) {
     PrefillPlan pl = plan_hybrid(BH, L, dv, use_init != 0, ws != nullptr);
     const bool via_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
-    if (via_ws && ws_bytes < plan_workspace_bytes(pl, BH)) pl = plan_hybrid(BH, L, dv, use_init != 0, false);
-    *launched = pl.dvl == kWinCols;
+    if (via_ws && ws_bytes < hybrid_ws_bytes(pl, BH)) pl = plan_hybrid(BH, L, dv, use_init != 0, false);
+    *launched = pl.dvl == kWinCols && dv == 64;
     if (!*launched) return hipSuccess;
-    return launch_plan<kWinCols, true>(pl, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                       static_cast<const uint16_t*>(v), BH, L, dv, eps, y, S, z, use_init, ws, st,
-                                       static_cast<const uint16_t*>(q2), static_cast<const uint16_t*>(k2), window,
-                                       scale);
+    return launch_hybrid_plan(pl, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                              static_cast<const uint16_t*>(v), BH, L, dv, eps, y, S, z, use_init, ws, st,
+                              static_cast<const uint16_t*>(q2), static_cast<const uint16_t*>(k2), window, scale);
 }
 
 }  // namespace based
