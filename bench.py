@@ -44,6 +44,7 @@ import synthetic_inputs as si  # noqa: E402
 
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16
+MFMA_F32_PEAK = 157.3e12   # flop/s, dense fp32 matrix cores
 METRIC = "tokens/sec for Taylor lin-attn prefill & decode; % of HBM / MFMA peak"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "linear_attention_sequence_taylor_amd", "csrc")
@@ -375,7 +376,7 @@ def bench_other_sizes(based):
     out["decode_d32"] = {"kernel_us": sec * 1e6, "hbm_GBps": db / sec / 1e9, "hbm_frac": db / sec / HBM_PEAK,
                          "algorithmic_bytes": db, "note": "feature dim 32, B=128, H=16, d_v=128, bf16 inputs"}
     del S, z, steps
-    # prefill with feature dim 32 (bf16 inputs, fp32 vector-ALU path), B=2, H=16, L=2048, d_v=64
+    # prefill with feature dim 32 (bf16 inputs widened, fp32 matrix cores), B=2, H=16, L=2048, d_v=64
     B, H, L, dv = 2, 16, 2048, 64
     q, k, v = (x.cuda() for x in si.custom((B, H, L, d), (B, H, L, dv), seed=2100, scale=0.5))
     for _ in range(2):
@@ -383,13 +384,18 @@ def bench_other_sizes(based):
     t = RegionTimer()
     torch.cuda.synchronize()
     t.start()
-    for _ in range(5):
+    for _ in range(20):
         based.based_prefill(q, k, v)
     t.stop()
-    sec = t.seconds() / 5
+    sec = t.seconds() / 20
     pb = B * H * L * (2 * d * 2 + dv * 2 + dv * 4) + B * H * (F32 * dv + F32) * 4
+    # per tok-head: 4 F d_v (state update and readout) + the causal intra-chunk term
+    pf = B * H * L * (4 * F32 * dv + 65 * (d + dv))
     out["prefill_d32"] = {"kernel_us": sec * 1e6, "tokens_per_s": B * L / sec, "hbm_frac": pb / sec / HBM_PEAK,
-                          "algorithmic_bytes": pb, "note": "feature dim 32, B=2, H=16, L=2048, fp32 vector-ALU path"}
+                          "algorithmic_bytes": pb, "algorithmic_flops": pf, "tflops": pf / sec / 1e12,
+                          "mfma_f32_frac": pf / sec / MFMA_F32_PEAK,
+                          "note": "feature dim 32, B=2, H=16, L=2048, fp32 arithmetic on the fp32 matrix cores "
+                                  "(128 workgroups: one per head and 16 value columns)"}
     return out
 
 

@@ -111,6 +111,11 @@ BASED_API based_status_t based_prefill(const void* q, const void* k, const void*
     if (mfma)
         return launch_status(based::launch_prefill_mfma(q, k, v, (int)BH, L, d_v, eps, y, S, z, init,
                                                         workspace, workspace_bytes, st));
+    // fp32 inputs or d_feat != 16: fp32 arithmetic throughout; chunk 64 on
+    // the fp32 matrix cores, chunks 16 and 32 on the vector ALUs
+    if (chunk == 64)
+        return launch_status(
+            based::launch_prefill_f32mfma(q, k, v, bf16, (int)BH, L, d_feat, d_v, eps, y, S, z, init, st));
     return launch_status(
         based::launch_prefill_valu(q, k, v, bf16, (int)BH, L, d_feat, d_v, chunk, eps, y, S, z, init, st));
 }

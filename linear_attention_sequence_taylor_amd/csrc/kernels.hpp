@@ -15,6 +15,10 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool 
 
 // fp32 vector-ALU chunked prefill (prefill_valu.hip).  d in {8, 16, 24, 32},
 // chunk in {16, 32, 64}.
+// Chunk-64 prefill for every feature dim in fp32 on the fp32 matrix cores
+// (prefill_f32mfma.hip); bf16 inputs are widened exactly.
+hipError_t launch_prefill_f32mfma(const void* q, const void* k, const void* v, bool bf16, int BH, int L, int d,
+                                  int dv, float eps, float* y, float* S, float* z, int use_init, hipStream_t st);
 hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, bool bf16, int BH, int L, int d,
                                int dv, int chunk, float eps, float* y, float* S, float* z,
                                int use_init, hipStream_t st);

@@ -1269,8 +1269,8 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int 
     switch (pl.dvl) {
         case 32: return launch_plan<32>(pl, qq, kk, vv, BH, L, dv, eps, y, S, z, use_init, ws, st);
         case 64: return launch_plan<64>(pl, qq, kk, vv, BH, L, dv, eps, y, S, z, use_init, ws, st);
-        default:  // no workspace for a carried d_v = 128 state: exact fp32 chunked kernel
-            return launch_prefill_valu(q, k, v, true, BH, L, kDFeat, dv, kC, eps, y, S, z, use_init, st);
+        default:  // no workspace for a carried d_v = 128 state: the fp32 chunked kernel
+            return launch_prefill_f32mfma(q, k, v, true, BH, L, kDFeat, dv, eps, y, S, z, use_init, st);
     }
 }
 
