@@ -93,6 +93,31 @@ def test_prefill_resume_from_state(dtype, tol):
     report(f"resume {dtype} z", ratio(z2, zo), tol)
 
 
+@pytest.mark.parametrize("dtype,tol,d,L", [
+    (torch.float32, 1e-4, 16, 1), (torch.float32, 1e-4, 32, 65), (torch.bfloat16, 2e-2, 8, 257),
+    (torch.float32, 1e-4, 24, 130),
+])
+def test_prefill_fp32_path_initial_state(dtype, tol, d, L):
+    """The fp32 matrix-core prefill (chunk 64, any feature dim) from an
+    asymmetric carried state: outputs, and the state returned as the initial
+    one plus this call's increment, row for row."""
+    based = based_mod()
+    F = 1 + d + d * d
+    q, k, v = si.custom((1, 2, L, d), (1, 2, L, 64), seed=760 + d + L, scale=0.5, dtype=dtype)
+    qp, kp, vp = si.custom((1, 2, 40, d), (1, 2, 40, 64), seed=762 + d, scale=0.5)
+    _, S0, z0 = oracle.la_recurrent(qp, kp, vp, want_y=False)
+    S0, z0 = torch.as_tensor(S0, dtype=torch.float32), torch.as_tensor(z0, dtype=torch.float32)
+    g = torch.Generator().manual_seed(763 + d)
+    P = torch.randn((1, 2, d, d, 64), generator=g)
+    S0[:, :, 1 + d:] += 0.5 * (P - P.transpose(2, 3)).reshape(1, 2, d * d, 64)
+    y, S, z = based.based_prefill(*dev(q, k, v), initial_state=tuple(dev(S0, z0)))
+    yo, So, zo = oracle.la_recurrent(q, k, v, S0=S0, z0=z0)
+    assert S.shape[2] == F
+    report(f"fp32-path init-state {dtype} d={d} L={L} y", ratio(y, yo), tol)
+    report(f"fp32-path init-state {dtype} d={d} L={L} S", ratio(S, So), tol)
+    report(f"fp32-path init-state {dtype} d={d} L={L} z", ratio(z, zo), tol)
+
+
 @pytest.mark.parametrize("L", [70, 900])
 @pytest.mark.parametrize("dv", [64, 128])
 @pytest.mark.parametrize("ws", ["auto", "none"])
