@@ -13,15 +13,22 @@
 // x~ = x d'^(-1/4) (App. D.4: F = 1 + d' + d'^2 rows).
 //
 // One workgroup of 8 waves per (batch, head, 16 value columns) walks the
-// chunks in order.  Internally the feature rows are ordered [1, x~_0 ..
-// x~_(d'-1), 0, 0, 0, x~_a x~_b / sqrt2 (a-major)]: with d' a multiple of 4
-// every 4-row k-step of the quadratic block stays inside one row a.  The
-// rows come in 16-row tiles; per chunk:
+// chunks in order.  The quadratic part of phi(q).phi(k) is symmetric in the
+// pair (a, b), so the state keeps one internal row per unordered pair:
+// internal rows [1, x~_0 .. x~_(d'-1), 0, 0, 0, pairs a <= b (a-major)],
+// T_ab = sum_t k~_a k~_b v_t (update features k~_a k~_b), read out with
+// q~_a q~_b for a < b and q~_a^2 / 2 on the diagonal.  The caller's rows
+// (a, b) and (b, a) are both T_ab / sqrt2; a carried state enters as
+// T_ab = (S_ab + S_ba) / sqrt2 (T_aa = sqrt2 S_aa) and each mirror row gets
+// the same increment back, so its antisymmetric part (which no readout
+// sees) is kept.  F = 1 + d' + d'(d'+1)/2 internal rows instead of 1 + d' +
+// d'^2.  The rows come in 16-row tiles; per chunk:
 //   * scores s = Q~ K~^T for the 10 lower-triangle 16x16 tiles (fp32 MFMA
 //     over d'), masked weights into LDS;
 //   * readout: wave w takes query tile w % 4 and every other feature tile
 //     (w / 4 picks which): phi(Q~) S and phi(Q~).z with the state before
-//     the chunk, read from LDS; the feature values are formed per lane;
+//     the chunk, read from LDS; the feature values are formed per lane
+//     from a table of (a, b, weight) per internal row;
 //   * update: wave w owns feature tiles w, w + 8, ...: S += phi(K~)^T V in
 //     MFMA accumulators, z in per-lane partial sums;
 //   * after a barrier: waves 0..3 add A V (and the row sums of A) for their
@@ -39,6 +46,7 @@ constexpr int kC = 64;      // chunk
 constexpr int kCW = 16;     // value columns per workgroup
 constexpr int kWaves = 8;   // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
+constexpr float kSqrt2 = 1.41421356237309504880f;
 
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -48,42 +56,45 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 template <int D>
 struct FMap {
     static_assert(D % 4 == 0, "feature dim a multiple of 4");
-    static constexpr int kLin = D + 4;  // rows before the quadratic block
-    static constexpr int kRows = kLin + D * D;
+    static constexpr int kLin = D + 4;           // rows before the pair block
+    static constexpr int kPairs = D * (D + 1) / 2;
+    static constexpr int kRows = kLin + kPairs;
     static constexpr int kTiles = (kRows + 15) / 16;
     static constexpr int kRowsPad = 16 * kTiles;
     static constexpr int kOwn = (kTiles + kWaves - 1) / kWaves;  // update tiles per wave
     static constexpr int kF = 1 + D + D * D;                     // the caller's rows
-    // The caller's row of internal row f, or -1 (padding).
-    __device__ static int caller_row(int f) {
-        if (f <= D) return f;
-        if (f < kLin || f >= kRows) return -1;
-        return 1 + D + (f - kLin);
-    }
 };
 
-// phi_f(x) = x[a] x[b] mul for internal row f, where column D of every
-// staged row holds 1: the constant row is x[D] x[D], a linear row
-// x[f-1] x[D], a quadratic row x[a] x[b] / sqrt2, padding rows have mul 0.
-struct FeatIdx {
+// Internal row f: phi_f(x) = x[a] x[b] w, where column D of every staged
+// row holds 1 (the constant row is x[D] x[D], a linear row x[f-1] x[D]).
+// wq / wk are the readout / update weights (0 on padding rows), pair = 1
+// for the pair rows (then a <= b).
+struct RowInfo {
     int a, b;
-    float mul;
+    float wq, wk;
+    bool pair;
 };
 template <int D>
-__device__ __forceinline__ FeatIdx feat_idx(int f) {
-    constexpr int kLin = FMap<D>::kLin, kRows = FMap<D>::kRows;
-    FeatIdx r;
-    if (f >= kLin && f < kRows) {
-        const int e = f - kLin;
-        r.a = e / D;
-        r.b = e - r.a * D;
-        r.mul = kInvSqrt2;
+__device__ __forceinline__ RowInfo row_info(int f) {
+    using M = FMap<D>;
+    RowInfo ri;
+    ri.pair = f >= M::kLin && f < M::kRows;
+    if (ri.pair) {
+        int p = f - M::kLin, a = 0;
+        while (p >= D - a) {  // row a holds pairs (a, a) .. (a, D-1)
+            p -= D - a;
+            ++a;
+        }
+        ri.a = a;
+        ri.b = a + p;
+        ri.wq = p == 0 ? 0.5f : 1.f;
+        ri.wk = 1.f;
     } else {
-        r.a = (f >= 1 && f <= D) ? f - 1 : D;
-        r.b = D;
-        r.mul = f <= D ? 1.f : 0.f;
+        ri.a = (f >= 1 && f <= D) ? f - 1 : D;
+        ri.b = D;
+        ri.wq = ri.wk = f <= D ? 1.f : 0.f;
     }
-    return r;
+    return ri;
 }
 
 template <int D>
@@ -97,6 +108,7 @@ struct F32Smem {
     float a[kC * (kC + 1)];            // masked intra-chunk weights
     float rnum[2][kC * kCW];           // readout halves
     float rden[2][kC];
+    int2 tab[FMap<D>::kRowsPad];       // per internal row: a | b << 8, readout weight bits
 };
 
 // Staging of one chunk: q~, k~ (pre-scaled) and the workgroup's v columns.
@@ -168,9 +180,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32mfma_kernel(const T* _
     float* zh = z + (size_t)head * M::kF;
     const int nchunks = (L + kC - 1) / kC;
 
+    // feature table of the readout
+    for (int f = threadIdx.x; f < M::kRowsPad; f += kThreads) {
+        const RowInfo ri = row_info<D>(f);
+        sm.tab[f] = make_int2(ri.a | (ri.b << 8), __float_as_int(ri.wq));
+    }
     // ---- state: this wave's tiles w + 8u in accumulators (rows 16rt + 4g + m,
     // column r), z as per-lane partial sums (row 16rt + r, this lane group's
-    // tokens; the caller's initial z sits in lane group 0)
+    // tokens; the initial z sits in lane group 0).  A carried state enters
+    // folded onto the pair rows.
+    auto init_row = [&](int f, int col, const float* base, size_t stride) -> float {
+        const RowInfo ri = row_info<D>(f);
+        if (ri.wk == 0.f) return 0.f;
+        if (!ri.pair) return base[(size_t)f * stride + col];
+        const float x = base[(size_t)(1 + D + D * ri.a + ri.b) * stride + col];
+        const float y = base[(size_t)(1 + D + D * ri.b + ri.a) * stride + col];
+        return ri.a == ri.b ? kSqrt2 * x : (x + y) * kInvSqrt2;
+    };
     f32x4 sacc[M::kOwn];
     float zp[M::kOwn];
 #pragma unroll
@@ -180,12 +206,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32mfma_kernel(const T* _
         zp[u] = 0.f;
         if (use_init && rt < M::kTiles) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int cr = M::caller_row(16 * rt + 4 * g + m);
-                if (cr >= 0) sacc[u][m] = Sh[(size_t)cr * dv + r];
-            }
-            const int cr = M::caller_row(16 * rt + r);
-            if (g == 0 && cr >= 0) zp[u] = zh[cr];
+            for (int m = 0; m < 4; ++m) sacc[u][m] = init_row(16 * rt + 4 * g + m, r, Sh, dv);
+            if (g == 0) zp[u] = init_row(16 * rt + r, 0, zh, 1);
         }
     }
     // feature indices of this lane's update row (16rt + r) of every own tile
@@ -193,10 +215,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32mfma_kernel(const T* _
     float um[M::kOwn];
 #pragma unroll
     for (int u = 0; u < M::kOwn; ++u) {
-        const FeatIdx fi = feat_idx<D>(16 * (w + kWaves * u) + r);
-        ua[u] = fi.a;
-        ub[u] = fi.b;
-        um[u] = (w + kWaves * u) < M::kTiles ? fi.mul : 0.f;
+        const RowInfo ri = row_info<D>(16 * (w + kWaves * u) + r);
+        ua[u] = ri.a;
+        ub[u] = ri.b;
+        um[u] = (w + kWaves * u) < M::kTiles ? ri.wk : 0.f;
     }
     // publish the initial state (the state before chunk 0)
     auto publish = [&]() {
@@ -257,17 +279,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32mfma_kernel(const T* _
             for (int rt = half; rt < M::kTiles; rt += 2) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    // rows f0 .. f0+3 (this lane: f0 + g); inside the quadratic
-                    // block they share row a of the outer product
-                    const int f0 = 16 * rt + 4 * j, f = f0 + g;
-                    float phi;
-                    if (f0 >= M::kLin && f0 + 4 <= M::kRows) {
-                        const int e0 = f0 - M::kLin, a = e0 / D;
-                        phi = qrow[a] * qrow[e0 - a * D + g] * kInvSqrt2;
-                    } else {
-                        const FeatIdx fi = feat_idx<D>(f);
-                        phi = qrow[fi.a] * qrow[fi.b] * fi.mul;
-                    }
+                    const int f = 16 * rt + 4 * j + g;
+                    const int2 te = sm.tab[f];
+                    const float phi = qrow[te.x & 255] * qrow[te.x >> 8] * __int_as_float(te.y);
                     num = mfma_f32(phi, sm.s[f * kCW + r], num);
                     den = fmaf(phi, sm.z[f], den);
                 }
@@ -324,21 +338,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32mfma_kernel(const T* _
         __syncthreads();
     }
 
-    // ---- final state in the caller's row order (z from column group 0)
+    // ---- final state in the caller's rows (z from column group 0): a pair
+    // row goes to both mirror rows, as T / sqrt2 or, after a carried state,
+    // as that state plus this call's increment
+    auto store_row = [&](int f, int col, float tv, float* base, size_t stride) {
+        const RowInfo ri = row_info<D>(f);
+        if (ri.wk == 0.f) return;
+        if (!ri.pair) {
+            base[(size_t)f * stride + col] = tv;
+            return;
+        }
+        float* pab = base + (size_t)(1 + D + D * ri.a + ri.b) * stride + col;
+        float* pba = base + (size_t)(1 + D + D * ri.b + ri.a) * stride + col;
+        if (!use_init) {
+            *pab = tv * kInvSqrt2;
+            *pba = tv * kInvSqrt2;
+        } else {
+            const float x = *pab, y = *pba;
+            const float t_init = ri.a == ri.b ? kSqrt2 * x : (x + y) * kInvSqrt2;
+            const float inc = (tv - t_init) * kInvSqrt2;
+            *pab = x + inc;
+            if (ri.a != ri.b) *pba = y + inc;
+        }
+    };
 #pragma unroll
     for (int u = 0; u < M::kOwn; ++u) {
         const int rt = w + kWaves * u;
         if (rt < M::kTiles) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int cr = M::caller_row(16 * rt + 4 * g + m);
-                if (cr >= 0) Sh[(size_t)cr * dv + r] = sacc[u][m];
-            }
+            for (int m = 0; m < 4; ++m) store_row(16 * rt + 4 * g + m, r, sacc[u][m], Sh, dv);
             float zs = zp[u];
             zs += __shfl_xor(zs, 16, 64);
             zs += __shfl_xor(zs, 32, 64);
-            const int cr = M::caller_row(16 * rt + r);
-            if (cg == 0 && g == 0 && cr >= 0) zh[cr] = zs;
+            if (cg == 0 && g == 0) store_row(16 * rt + r, 0, zs, zh, 1);
         }
     }
 }
