@@ -53,7 +53,7 @@
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *     enqueued on it asynchronously; no call synchronises the stream.
  *
- * Sizes: B, H, L >= 1 with B*H <= 2^31 - 1, L <= 2^31 - 1024 and
+ * Sizes: B, H, L >= 1 with B*H <= 2^27, L <= 2^31 - 1024 and
  * B*H*L <= 2^40; anything larger returns BASED_E_INVALID.
  *
  * Errors: arguments are checked before anything is launched; a bad argument

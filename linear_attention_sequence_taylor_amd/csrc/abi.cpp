@@ -45,7 +45,9 @@ based_status_t check_dims(int B, int H, int L, uint64_t* BH, uint64_t* BHL) {
     // L stays 1023 below INT32_MAX so that chunk and tile counts rounded up
     // in int arithmetic (L + 63) / 64 cannot overflow.
     if (B < 1 || H < 1 || L < 1 || L > INT32_MAX - 1023) return BASED_E_INVALID;
-    if (!mul_ok((uint64_t)B, (uint64_t)H, BH) || *BH > (uint64_t)INT32_MAX) return BASED_E_INVALID;
+    // B*H <= 2^27 keeps every grid (at most 16 workgroups per head outside
+    // the segment splits, which only run for few heads) inside 2^31.
+    if (!mul_ok((uint64_t)B, (uint64_t)H, BH) || *BH > ((uint64_t)1 << 27)) return BASED_E_INVALID;
     if (!mul_ok(*BH, (uint64_t)L, BHL) || *BHL > ((uint64_t)1 << 40)) return BASED_E_INVALID;
     return BASED_OK;
 }

@@ -94,6 +94,7 @@ def _prefill(lib, **kw):
     (dict(dtype=7), 1), (dict(B=0), 1), (dict(H=-1), 1), (dict(L=0), 1),
     (dict(B=1 << 20, H=1 << 20), 1), (dict(chunk=0), 1), (dict(eps=float("nan")), 1),
     (dict(L=2**31 - 1), 1), (dict(L=2**31 - 1023), 1), (dict(B=1 << 10, H=1 << 10, L=1 << 21), 1),
+    (dict(B=1 << 14, H=(1 << 13) + 1, L=1), 1),
     (dict(d=12), 2), (dict(d=64), 2), (dict(dv=96), 2), (dict(chunk=32), 2), (dict(dtype=0, chunk=48), 2),
     (dict(d=8, chunk=48), 2),
     (dict(y=A), 1), (dict(S=Y), 1), (dict(z=S + 64), 1),
