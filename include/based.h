@@ -264,9 +264,9 @@ based_status_t swa_decode_step(const void *q, const void *k, const void *v,
  *          (else BASED_E_INVALID); must not overlap anything else
  * Supported: d_feat in {8, 16, 24, 32}; d_v in {64, 128}; B*H*ceil(L/64)*256
  * must not exceed INT32_MAX (else BASED_E_INVALID).  Direct form (O(L^2)
- * work per head), fp32 accumulation: bf16 inputs with d_feat 16 compute the
- * query side (g, h, dq) on the matrix cores with the weights split into
- * bf16 hi/lo pairs; everything else runs in fp32 on the vector ALUs.
+ * work per head) on the matrix cores, fp32 accumulation: bf16 inputs with
+ * d_feat 16 take bf16 products with the weights split into bf16 hi/lo
+ * pairs; every other input takes fp32 products.
  */
 size_t based_prefill_backward_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
 

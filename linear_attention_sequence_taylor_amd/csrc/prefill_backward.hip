@@ -1,5 +1,8 @@
 // prefill_backward.hip -- gradients of causal Taylor linear attention for
-// training-mode prefill (gfx950), fp32 on the vector ALUs.
+// training-mode prefill (gfx950): fp32 inputs and every feature dim, in fp32
+// on the fp32 matrix cores (v_mfma_f32_16x16x4_f32).  bf16 inputs with
+// feature dim 16 take the bf16 matrix-core kernels of
+// prefill_backward_mfma.hip (same workspace layout).
 //
 // "Simple linear attention language models balance the recall-throughput
 // tradeoff", s5 (prefill also serves training) and s4 "Taylor Linear
@@ -10,203 +13,293 @@
 //   e_ij = (g_i . v_j + h_i) (1 + s_ij) / sqrt(d'),
 //   dq_i = sum_{j<=i} e_ij k_j,  dk_j = sum_{i>=j} e_ij q_i,
 //   dv_j = sum_{i>=j} a_ij g_i.
+// This is the direct (quadratic) form: O(L^2) work per head.
 //
-// Two kernels, one thread per row, tiles of the other side staged in LDS
-// (every lane of a wave reads the same staged row, a broadcast):
-//   query side: N_i and D_i, then g_i and h_i (to the workspace) and dq_i;
-//   key side:   dk_j and dv_j from the queries at or after j.
-// This is the direct (quadratic) form: O(L^2) work per head.  bf16 inputs
-// with feature dim 16 take the matrix-core kernels of
-// prefill_backward_mfma.hip instead (same workspace layout).
+// Two kernels, one workgroup of 4 waves per 64 rows, wave w owning rows
+// 16w..16w+15; the other side goes through LDS in 64-row fp32 tiles (row
+// stride width + 4: the row reads and the column reads below then hit 64
+// distinct banks) while the wave's own rows sit in registers:
+//   query side: pass 1 over the key tiles at or before the queries gives N
+//     and D, then g and h (to the workspace); pass 2 gives dq;
+//   key side: over the query tiles at or after the keys, dk and dv.
+// A score tile computed as K Q^T (or Q K^T) leaves lane (g, r) = (lane/16,
+// lane%16) with row r of its own side against rows 4g..4g+3 of the other;
+// a product over those rows then takes its k-step m from lane group g's row
+// 4g + m, so the weights enter the next product without moving between
+// lanes.  Only the diagonal tile is masked; rows past L are staged as zeros
+// (their weights meet zero g rows or are masked) and never stored.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace based {
 namespace {
 
-constexpr int kRows = 128;  // rows (threads) per workgroup
-constexpr int kTile = 32;   // staged rows of the other side
+constexpr int kT = 64;  // rows per tile
 
-template <typename T, int D, int DV>
-__global__ __launch_bounds__(kRows) void bwd_query_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                          const T* __restrict__ v, const float* __restrict__ dy,
-                                                          int L, float eps, float* __restrict__ dq,
-                                                          float* __restrict__ g_ws, float* __restrict__ h_ws) {
-    __shared__ float s_k[kTile][D];
-    __shared__ float s_v[kTile][DV];
-    const int nb = (L + kRows - 1) / kRows;
-    const int head = blockIdx.x / nb;
-    const int i0 = (blockIdx.x % nb) * kRows;
-    const int i = i0 + threadIdx.x;
-    const bool live = i < L;
-    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    const T* qh = q + (size_t)head * L * D;
-    const T* kh = k + (size_t)head * L * D;
-    const T* vh = v + (size_t)head * L * DV;
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
-    float qi[D];
-#pragma unroll
-    for (int e = 0; e < D; ++e) qi[e] = live ? load_elem(qh, (size_t)i * D + e) : 0.f;
-    float acc[DV];
-#pragma unroll
-    for (int c = 0; c < DV; ++c) acc[c] = 0.f;
-    float den = eps;
-    const int jend = min(L, i0 + kRows);  // keys any row of this block can see
+// Feature width padded to whole 16-column output tiles.
+template <int D>
+constexpr int feat_pad() {
+    return D <= 16 ? 16 : 32;
+}
 
-    auto stage = [&](int j0) {
-        __syncthreads();
-        for (int e = threadIdx.x; e < kTile * D; e += kRows) {
-            const int r = e / D, a = e % D;
-            s_k[r][a] = j0 + r < L ? load_elem(kh, (size_t)(j0 + r) * D + a) : 0.f;
-        }
-        for (int e = threadIdx.x; e < kTile * DV; e += kRows) {
-            const int r = e / DV, c = e % DV;
-            s_v[r][c] = j0 + r < L ? load_elem(vh, (size_t)(j0 + r) * DV + c) : 0.f;
-        }
-        __syncthreads();
-    };
-    // ---- N_i and D_i
-    for (int j0 = 0; j0 < jend; j0 += kTile) {
-        stage(j0);
-        const int n = min(kTile, i - j0 + 1);  // keys j0 .. i of this tile
-        for (int r = 0; r < n; ++r) {
-            float s = 0.f;
-#pragma unroll
-            for (int e = 0; e < D; ++e) s = fmaf(qi[e], s_k[r][e], s);
-            s *= inv_sqrt_d;
-            const float a = fmaf(s, fmaf(s, 0.5f, 1.f), 1.f);
-            den += a;
-#pragma unroll
-            for (int c = 0; c < DV; ++c) acc[c] = fmaf(a, s_v[r][c], acc[c]);
-        }
-    }
-    // ---- g_i (in acc) and h_i
-    float h = 0.f;
-    if (live) {
-        const float inv = 1.f / den;
-        const float* dyi = dy + ((size_t)head * L + i) * DV;
-        float* gi = g_ws + ((size_t)head * L + i) * DV;
-        float dyy = 0.f;
-#pragma unroll
-        for (int c = 0; c < DV; ++c) {
-            const float dyc = dyi[c];
-            dyy = fmaf(dyc, acc[c] * inv, dyy);
-            acc[c] = dyc * inv;
-            gi[c] = acc[c];
-        }
-        h = -dyy * inv;
-        h_ws[(size_t)head * L + i] = h;
-    }
-    // ---- dq_i
-    float dqi[D];
-#pragma unroll
-    for (int e = 0; e < D; ++e) dqi[e] = 0.f;
-    for (int j0 = 0; j0 < jend; j0 += kTile) {
-        stage(j0);
-        const int n = min(kTile, i - j0 + 1);
-        for (int r = 0; r < n; ++r) {
-            float s = 0.f;
-#pragma unroll
-            for (int e = 0; e < D; ++e) s = fmaf(qi[e], s_k[r][e], s);
-            s *= inv_sqrt_d;
-            float ga = h;
-#pragma unroll
-            for (int c = 0; c < DV; ++c) ga = fmaf(acc[c], s_v[r][c], ga);
-            const float w = ga * (1.f + s) * inv_sqrt_d;
-#pragma unroll
-            for (int e = 0; e < D; ++e) dqi[e] = fmaf(w, s_k[r][e], dqi[e]);
-        }
-    }
-    if (live) {
-        float* dqo = dq + ((size_t)head * L + i) * D;
-#pragma unroll
-        for (int e = 0; e < D; ++e) dqo[e] = dqi[e];
+// Rows row0.. of a [L][W] matrix as fp32 into a [64][WP + 4] LDS tile
+// (columns W..WP-1 and rows past L zero).
+template <typename T, int W, int WP>
+__device__ __forceinline__ void stage_f32(const T* mat, int L, int row0, float* dst) {
+    constexpr int kLd = WP + 4;
+    for (int e = threadIdx.x; e < kT * WP; e += 256) {
+        const int row = e / WP, c = e % WP;
+        float x = 0.f;
+        if (c < W && row0 + row < L) x = load_elem(mat, (size_t)(row0 + row) * W + c);
+        dst[row * kLd + c] = x;
     }
 }
 
+template <int D, int DV>
+struct BwdQSmemF {
+    static constexpr int kLdK = feat_pad<D>() + 4, kLdV = DV + 4;
+    float k[kT * kLdK];
+    float v[kT * kLdV];
+    float g[4][16 * kLdV];  // per wave: g of its 16 queries
+    float h[4][16];
+};
+
 template <typename T, int D, int DV>
-__global__ __launch_bounds__(kRows) void bwd_key_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                        const T* __restrict__ v, int L,
-                                                        const float* __restrict__ g_ws, const float* __restrict__ h_ws,
-                                                        float* __restrict__ dk, float* __restrict__ dvo) {
-    __shared__ float s_q[kTile][D];
-    __shared__ float s_g[kTile][DV];
-    __shared__ float s_h[kTile];
-    const int nb = (L + kRows - 1) / kRows;
-    const int head = blockIdx.x / nb;
-    const int j0b = (blockIdx.x % nb) * kRows;
-    const int j = j0b + threadIdx.x;
-    const bool live = j < L;
-    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    const T* qh = q + (size_t)head * L * D;
+__global__ __launch_bounds__(256) void bwd_query_f32_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                            const T* __restrict__ v, const float* __restrict__ dy,
+                                                            int L, int ntiles, float eps, float* __restrict__ dq,
+                                                            float* __restrict__ g_ws, float* __restrict__ h_ws) {
+    using SM = BwdQSmemF<D, DV>;
+    constexpr int kKW = feat_pad<D>(), kLdK = SM::kLdK, kLdV = SM::kLdV;
+    constexpr int kNV = DV / 16, kNK = kKW / 16;
+    __shared__ SM sm;
+    const float isd = 1.f / sqrtf((float)D);
+    const int BH = gridDim.x / ntiles;
+    const int head = blockIdx.x % BH;
+    const int ti = ntiles - 1 - (int)(blockIdx.x / BH);  // the longest rows first, every head
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const T* kh = k + (size_t)head * L * D;
     const T* vh = v + (size_t)head * L * DV;
+    const int qw0 = ti * kT + 16 * w;  // first query of this wave
+    const int qr = qw0 + r;            // this lane's query in the score tiles
 
-    float kj[D], vj[DV], dkj[D], dvj[DV];
+    // B operand of the scores: this lane's query, dims 4j + g, / sqrt(d')
+    float qb[D / 4];
 #pragma unroll
-    for (int e = 0; e < D; ++e) {
-        kj[e] = live ? load_elem(kh, (size_t)j * D + e) : 0.f;
-        dkj[e] = 0.f;
-    }
+    for (int j = 0; j < D / 4; ++j) qb[j] = qr < L ? load_elem(q, ((size_t)head * L + qr) * D + 4 * j + g) * isd : 0.f;
+
+    // scores of key tile kt: st[m] = s(key 16kt + 4g + m, query r)
+    auto scores = [&](int kt) {
+        f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < DV; ++c) {
-        vj[c] = live ? load_elem(vh, (size_t)j * DV + c) : 0.f;
-        dvj[c] = 0.f;
-    }
-    // queries from the block's first key on; each thread uses i >= j
-    for (int i0 = (j0b / kTile) * kTile; i0 < L; i0 += kTile) {
+        for (int j = 0; j < D / 4; ++j) st = mfma_f32(sm.k[(16 * kt + r) * kLdK + 4 * j + g], qb[j], st);
+        return st;
+    };
+
+    // ---- pass 1: N (rows = queries 4g+m, columns 16ct + r), and D - eps of
+    // query r over this lane's keys
+    f32x4 yacc[kNV];
+#pragma unroll
+    for (int ct = 0; ct < kNV; ++ct) yacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+    for (int tj = 0; tj <= ti; ++tj) {
         __syncthreads();
-        for (int e = threadIdx.x; e < kTile * D; e += kRows) {
-            const int r = e / D, a = e % D;
-            s_q[r][a] = i0 + r < L ? load_elem(qh, (size_t)(i0 + r) * D + a) : 0.f;
-        }
-        for (int e = threadIdx.x; e < kTile * DV; e += kRows) {
-            const int r = e / DV, c = e % DV;
-            s_g[r][c] = i0 + r < L ? g_ws[((size_t)head * L + i0 + r) * DV + c] : 0.f;
-        }
-        for (int r = threadIdx.x; r < kTile; r += kRows) s_h[r] = i0 + r < L ? h_ws[(size_t)head * L + i0 + r] : 0.f;
+        stage_f32<T, D, kKW>(kh, L, tj * kT, sm.k);
+        stage_f32<T, DV, DV>(vh, L, tj * kT, sm.v);
         __syncthreads();
-        const int rb = max(0, j - i0), re = min(kTile, L - i0);  // queries max(i0, j) .. of this tile
-        for (int r = rb; r < re; ++r) {
-            float s = 0.f;
+        const bool diag = tj == ti;
 #pragma unroll
-            for (int e = 0; e < D; ++e) s = fmaf(s_q[r][e], kj[e], s);
-            s *= inv_sqrt_d;
-            const float a = fmaf(s, fmaf(s, 0.5f, 1.f), 1.f);
-            float ga = s_h[r];
+        for (int kt = 0; kt < 4; ++kt) {
+            const f32x4 st = scores(kt);
 #pragma unroll
-            for (int c = 0; c < DV; ++c) {
-                ga = fmaf(s_g[r][c], vj[c], ga);
-                dvj[c] = fmaf(a, s_g[r][c], dvj[c]);
+            for (int m = 0; m < 4; ++m) {
+                const float s = st[m];
+                float a = fmaf(s, fmaf(s, 0.5f, 1.f), 1.f);
+                if (diag && 16 * kt + 4 * g + m > 16 * w + r) a = 0.f;
+                lsum += a;
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct)
+                    yacc[ct] = mfma_f32(a, sm.v[(16 * kt + 4 * g + m) * kLdV + 16 * ct + r], yacc[ct]);
             }
-            const float w = ga * (1.f + s) * inv_sqrt_d;
-#pragma unroll
-            for (int e = 0; e < D; ++e) dkj[e] = fmaf(w, s_q[r][e], dkj[e]);
         }
     }
-    if (live) {
-        float* dko = dk + ((size_t)head * L + j) * D;
-        float* dvo_j = dvo + ((size_t)head * L + j) * DV;
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);  // D - eps of query qr, on every lane group
+
+    // ---- g = dy/D and h = -(dy.y)/D of queries qw0 + 4g + m (columns 16ct + r)
 #pragma unroll
-        for (int e = 0; e < D; ++e) dko[e] = dkj[e];
+    for (int m = 0; m < 4; ++m) {
+        const int qi = qw0 + 4 * g + m;
+        const float inv = 1.f / (__shfl(lsum, 4 * g + m, 64) + eps);
+        float dyy = 0.f;
 #pragma unroll
-        for (int c = 0; c < DV; ++c) dvo_j[c] = dvj[c];
+        for (int ct = 0; ct < kNV; ++ct) {
+            const float dyc = qi < L ? dy[((size_t)head * L + qi) * DV + 16 * ct + r] : 0.f;
+            dyy = fmaf(dyc, yacc[ct][m], dyy);
+            const float gv = dyc * inv;
+            sm.g[w][(4 * g + m) * kLdV + 16 * ct + r] = gv;
+            if (qi < L) g_ws[((size_t)head * L + qi) * DV + 16 * ct + r] = gv;
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) dyy += __shfl_xor(dyy, off, 64);
+        const float hq = -dyy * inv * inv;
+        if (r == 0) {
+            sm.h[w][4 * g + m] = hq;
+            if (qi < L) h_ws[(size_t)head * L + qi] = hq;
+        }
+    }
+
+    // ---- pass 2: dq (rows = queries 4g+m, columns = features 16ct + r),
+    // from the diagonal tile (still staged) back to the first
+    f32x4 dqacc[kNK];
+#pragma unroll
+    for (int ct = 0; ct < kNK; ++ct) dqacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tj = ti; tj >= 0; --tj) {
+        __syncthreads();  // also orders the g/h writes above before their reads
+        if (tj != ti) {
+            stage_f32<T, D, kKW>(kh, L, tj * kT, sm.k);
+            stage_f32<T, DV, DV>(vh, L, tj * kT, sm.v);
+            __syncthreads();
+        }
+        const bool diag = tj == ti;
+        const float hr = sm.h[w][r];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const f32x4 st = scores(kt);
+            // (g . v): rows = keys 16kt + 4g + m, columns = queries r
+            f32x4 ga = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < DV / 4; ++j)
+                ga = mfma_f32(sm.v[(16 * kt + r) * kLdV + 4 * j + g], sm.g[w][r * kLdV + 4 * j + g], ga);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                float e = (ga[m] + hr) * (1.f + st[m]) * isd;
+                if (diag && 16 * kt + 4 * g + m > 16 * w + r) e = 0.f;
+#pragma unroll
+                for (int ct = 0; ct < kNK; ++ct)
+                    dqacc[ct] = mfma_f32(e, sm.k[(16 * kt + 4 * g + m) * kLdK + 16 * ct + r], dqacc[ct]);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int qi = qw0 + 4 * g + m;
+#pragma unroll
+        for (int ct = 0; ct < kNK; ++ct)
+            if (qi < L && 16 * ct + r < D) dq[((size_t)head * L + qi) * D + 16 * ct + r] = dqacc[ct][m];
+    }
+}
+
+template <int D, int DV>
+struct BwdKSmemF {
+    static constexpr int kLdQ = feat_pad<D>() + 4, kLdG = DV + 4;
+    float q[kT * kLdQ];
+    float g[kT * kLdG];
+    float h[kT];
+};
+
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(256) void bwd_key_f32_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                          const T* __restrict__ v, int L, int ntiles,
+                                                          const float* __restrict__ g_ws,
+                                                          const float* __restrict__ h_ws, float* __restrict__ dk,
+                                                          float* __restrict__ dvo) {
+    using SM = BwdKSmemF<D, DV>;
+    constexpr int kKW = feat_pad<D>(), kLdQ = SM::kLdQ, kLdG = SM::kLdG;
+    constexpr int kNV = DV / 16, kNK = kKW / 16;
+    __shared__ SM sm;
+    const float isd = 1.f / sqrtf((float)D);
+    const int BH = gridDim.x / ntiles;
+    const int head = blockIdx.x % BH;
+    const int tj = blockIdx.x / BH;  // the first keys (the longest loops) first, every head
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const T* qh = q + (size_t)head * L * D;
+    const float* gh = g_ws + (size_t)head * L * DV;
+    const float* hh = h_ws + (size_t)head * L;
+    const int kw0 = tj * kT + 16 * w;  // first key of this wave
+    const int kr = kw0 + r;            // this lane's key in the score tiles
+
+    // this lane's key (/ sqrt(d')) and value: the B operands of Q K^T and
+    // g V^T (dims / columns 4j + g)
+    float kb[D / 4], vb[DV / 4];
+#pragma unroll
+    for (int j = 0; j < D / 4; ++j) kb[j] = kr < L ? load_elem(k, ((size_t)head * L + kr) * D + 4 * j + g) * isd : 0.f;
+#pragma unroll
+    for (int j = 0; j < DV / 4; ++j) vb[j] = kr < L ? load_elem(v, ((size_t)head * L + kr) * DV + 4 * j + g) : 0.f;
+    f32x4 dvacc[kNV], dkacc[kNK];
+#pragma unroll
+    for (int ct = 0; ct < kNV; ++ct) dvacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < kNK; ++ct) dkacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int ti = tj; ti < ntiles; ++ti) {
+        __syncthreads();
+        stage_f32<T, D, kKW>(qh, L, ti * kT, sm.q);
+        stage_f32<float, DV, DV>(gh, L, ti * kT, sm.g);
+        if (threadIdx.x < kT) sm.h[threadIdx.x] = ti * kT + (int)threadIdx.x < L ? hh[ti * kT + threadIdx.x] : 0.f;
+        __syncthreads();
+        const bool diag = ti == tj;
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+            // scores and (g . v): rows = queries 16qt + 4g + m, columns = keys r
+            f32x4 st = {0.f, 0.f, 0.f, 0.f}, ga = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < D / 4; ++j) st = mfma_f32(sm.q[(16 * qt + r) * kLdQ + 4 * j + g], kb[j], st);
+#pragma unroll
+            for (int j = 0; j < DV / 4; ++j) ga = mfma_f32(sm.g[(16 * qt + r) * kLdG + 4 * j + g], vb[j], ga);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int qrow = 16 * qt + 4 * g + m;
+                const float s = st[m];
+                float a = fmaf(s, fmaf(s, 0.5f, 1.f), 1.f);
+                float e = (ga[m] + sm.h[qrow]) * (1.f + s) * isd;
+                if (diag && qrow < 16 * w + r) a = e = 0.f;
+                // dv += a^T g and dk += e^T q (rows = keys 4g+m', columns
+                // 16ct + r): k-step m, lane group g brings query qrow
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) dvacc[ct] = mfma_f32(a, sm.g[qrow * kLdG + 16 * ct + r], dvacc[ct]);
+#pragma unroll
+                for (int ct = 0; ct < kNK; ++ct) dkacc[ct] = mfma_f32(e, sm.q[qrow * kLdQ + 16 * ct + r], dkacc[ct]);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int kj = kw0 + 4 * g + m;
+        if (kj < L) {
+#pragma unroll
+            for (int ct = 0; ct < kNV; ++ct) dvo[((size_t)head * L + kj) * DV + 16 * ct + r] = dvacc[ct][m];
+#pragma unroll
+            for (int ct = 0; ct < kNK; ++ct)
+                if (16 * ct + r < D) dk[((size_t)head * L + kj) * D + 16 * ct + r] = dkacc[ct][m];
+        }
     }
 }
 
 template <typename T, int D, int DV>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const float* dy, int BH, int L, float eps,
                       float* dq, float* dk, float* dv, float* g_ws, float* h_ws, hipStream_t st) {
-    const dim3 grid((unsigned)(((L + kRows - 1) / kRows) * BH));
+    // bf16 with feature dim 16 runs on the bf16 matrix cores
+    if constexpr (sizeof(T) == 2 && D == kDFeat) {
+        return launch_prefill_backward_mfma(q, k, v, dy, BH, L, DV, eps, dq, dk, dv, g_ws, h_ws, st);
+    } else {
+    const int ntiles = (L + kT - 1) / kT;
+    const dim3 grid((unsigned)(ntiles * BH));
     const T* qq = static_cast<const T*>(q);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
-    // bf16 with feature dim 16 runs on the matrix cores
-    if (sizeof(T) == 2 && D == kDFeat) return launch_prefill_backward_mfma(q, k, v, dy, BH, L, DV, eps, dq, dk, dv,
-                                                                          g_ws, h_ws, st);
-    hipLaunchKernelGGL((bwd_query_kernel<T, D, DV>), grid, dim3(kRows), 0, st, qq, kk, vv, dy, L, eps, dq, g_ws, h_ws);
-    hipLaunchKernelGGL((bwd_key_kernel<T, D, DV>), grid, dim3(kRows), 0, st, qq, kk, vv, L, g_ws, h_ws, dk, dv);
+    hipLaunchKernelGGL((bwd_query_f32_kernel<T, D, DV>), grid, dim3(256), 0, st, qq, kk, vv, dy, L, ntiles, eps, dq,
+                       g_ws, h_ws);
+    hipLaunchKernelGGL((bwd_key_f32_kernel<T, D, DV>), grid, dim3(256), 0, st, qq, kk, vv, L, ntiles, g_ws, h_ws, dk,
+                       dv);
     return hipGetLastError();
+    }
 }
 
 template <typename T, int D>

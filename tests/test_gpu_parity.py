@@ -396,6 +396,9 @@ def test_swa_wide_windows(dtype, tol, dqk, window, L):
     (torch.float32, 1e-4, 1, 2, 70, 32, 128), (torch.bfloat16, 2e-2, 2, 1, 257, 8, 64),
     (torch.bfloat16, 2e-2, 1, 3, 33, 24, 128), (torch.bfloat16, 2e-2, 2, 2, 200, 16, 128),
     (torch.bfloat16, 2e-2, 1, 1, 64, 16, 64), (torch.bfloat16, 2e-2, 1, 2, 3, 16, 64),
+    (torch.float32, 1e-4, 1, 2, 257, 8, 64), (torch.float32, 1e-4, 2, 1, 200, 24, 128),
+    (torch.float32, 1e-4, 1, 1, 600, 16, 128), (torch.float32, 1e-4, 1, 2, 65, 32, 64),
+    (torch.bfloat16, 2e-2, 1, 2, 190, 32, 128), (torch.float32, 1e-4, 1, 1, 5, 24, 64),
 ])
 def test_backward_matches_oracle(dtype, tol, B, H, L, d, dv):
     """dq, dk, dv of the prefill output for a seeded upstream gradient, against
