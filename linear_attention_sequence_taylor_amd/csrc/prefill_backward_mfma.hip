@@ -36,9 +36,8 @@
 namespace based {
 namespace {
 
-constexpr int kT = 64;         // rows per tile (queries or keys)
-constexpr int kD = 16;         // feature dim of this path
-constexpr int kLdQK = kD + 8;  // LDS row stride (bf16) of Q and K tiles
+constexpr int kT = 64;  // rows per tile (queries or keys)
+constexpr int kD = 16;  // feature dim of this path
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define BWD_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -56,30 +55,64 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-// Transposed read of a row-major bf16 tile in LDS (row stride ld elements):
-// lane c of each 16-lane group passes the address of row rb + c/4, columns
-// col0 + 4(c%4) .. +3, and receives rows rb .. rb+3 of column col0 + c
-// (rb may differ between the groups).
-__device__ __forceinline__ uint2 tr4(const uint16_t* tile, int ld, int rb, int col0, int c) {
-    const uint16_t* p = tile + (rb + (c >> 2)) * ld + col0 + 4 * (c & 3);
+// LDS tiles are row-major bf16 with W columns and no padding; element
+// (row, col) sits at tile_at<W>(row, col).  Rows are permuted in pieces so
+// that the two read shapes below both hit distinct banks (64 banks of 4
+// bytes; a 16-byte read serves 16 lanes at a time, an 8-byte read 32):
+// 16 consecutive rows at one column piece (the row-operand reads), and 8
+// consecutive rows (from a multiple of 16, or 8 past it) at two adjacent
+// 16-byte pieces (the transposed reads).
+//  - W = 16 (Q, K): four 8-byte slots per row; rows 8..15 of every 16 swap
+//    slots 0,1 with 2,3.
+//  - W = 64, 128 (V, g): 16-byte units; unit index XOR h(row), with h
+//    distinct over 16 rows and h/2 distinct over each aligned 8 rows (and,
+//    for W = 64, over the rows of one parity, which share banks).
+template <int W>
+__device__ __forceinline__ int tile_at(int row, int col) {
+    if constexpr (W == kD) {
+        return row * kD + ((((col >> 2) ^ ((row >> 2) & 2))) << 2) + (col & 3);
+    } else {
+        static_assert(W == 64 || W == 128, "tile width");
+        const int h = W == 64 ? ((((row >> 1) & 3) << 1) | ((row >> 3) & 1)) : (((row & 7) << 1) | ((row >> 3) & 1));
+        return row * W + ((((col >> 3) ^ h)) << 3) + (col & 7);
+    }
+}
+
+// Transposed read of a bf16 tile in LDS: lane c of each 16-lane group
+// passes the address of row rb + c/4, columns col0 + 4(c%4) .. +3, and
+// receives rows rb .. rb+3 of column col0 + c (rb may differ between the
+// groups).
+template <int W>
+__device__ __forceinline__ uint2 tr4(const uint16_t* tile, int rb, int col0, int c) {
+    const uint16_t* p = tile + tile_at<W>(rb + (c >> 2), col0 + 4 * (c & 3));
     return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(BWD_LDS(s16x4, p)));
 }
 // B operand of a 16x16x32 product whose k index 8g + i stands for row
 // rb + 4g + i (i < 4) and rb + 16 + 4g + i - 4 (i >= 4): the pairing of the
 // A operands built from two 16-row score tiles (join_tiles).
-__device__ __forceinline__ bf16x8 tr_b8(const uint16_t* tile, int ld, int rb, int col0, int g, int c) {
-    const uint2 a = tr4(tile, ld, rb + 4 * g, col0, c);
-    const uint2 b = tr4(tile, ld, rb + 16 + 4 * g, col0, c);
+template <int W>
+__device__ __forceinline__ bf16x8 tr_b8(const uint16_t* tile, int rb, int col0, int g, int c) {
+    const uint2 a = tr4<W>(tile, rb + 4 * g, col0, c);
+    const uint2 b = tr4<W>(tile, rb + 16 + 4 * g, col0, c);
     return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
 
-// hi = bf16(x), lo = bf16(x - hi).
+// hi = bf16(x), lo = bf16(x - hi).  Each x - hi is one v_dot2_f32_bf16 of
+// the packed hi pair against (-1, -0) or (-0, -1), plus x: the products are
+// exact and x - hi is representable, so the one rounding changes nothing.
+// (The selectors keep a -0 in the other half: the pair (-1, +0) has the bit
+// pattern of a small integer that is emitted as an inline float constant.)
 __device__ __forceinline__ void hilo8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+    const bf16x2 sel_lo = __builtin_bit_cast(bf16x2, 0x8000bf80u);
+    const bf16x2 sel_hi = __builtin_bit_cast(bf16x2, 0xbf808000u);
     u32x4 h, l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        h[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-        l[i] = pack_bf16x2(x[2 * i] - bf16lo_f32(h[i]), x[2 * i + 1] - bf16hi_f32(h[i]));
+        const uint32_t hp = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        const bf16x2 hb = __builtin_bit_cast(bf16x2, hp);
+        h[i] = hp;
+        l[i] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(hb, sel_lo, x[2 * i], false),
+                           __builtin_amdgcn_fdot2_f32_bf16(hb, sel_hi, x[2 * i + 1], false));
     }
     hi = __builtin_bit_cast(bf16x8, h);
     lo = __builtin_bit_cast(bf16x8, l);
@@ -103,8 +136,8 @@ __device__ __forceinline__ bf16x4 quarter(uint2 u) {
 
 // A [64][W] bf16 tile (rows row0.. of a [L][W] matrix, rows past L zero)
 // held in registers across the workgroup, 16 bytes per piece: loaded from
-// global memory while the previous tile is in use, then stored to LDS with
-// row stride W + 8.
+// global memory while the previous tile is in use, then stored to LDS in
+// the tile_at<W> layout.
 template <int W>
 struct TileRegs {
     static constexpr int kU = W / 8;                    // pieces per row
@@ -124,7 +157,7 @@ struct TileRegs {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int e = threadIdx.x + 256 * i, row = e / kU, u = e % kU;
-            if (e < kT * kU) *reinterpret_cast<u32x4*>(dst + row * (W + 8) + 8 * u) = x[i];
+            if (e < kT * kU) *reinterpret_cast<u32x4*>(dst + tile_at<W>(row, 8 * u)) = x[i];
         }
     }
 };
@@ -132,10 +165,10 @@ struct TileRegs {
 // ---------------------------------------------------------------- query side
 template <int DV>
 struct BwdQSmem {
-    alignas(16) uint16_t k[kT * kLdQK];
-    alignas(16) uint16_t v[kT * (DV + 8)];
-    alignas(16) uint16_t ghi[4][16 * (DV + 8)];  // per wave: g of its 16 queries
-    alignas(16) uint16_t glo[4][16 * (DV + 8)];
+    alignas(16) uint16_t k[kT * kD];
+    alignas(16) uint16_t v[kT * DV];
+    alignas(16) uint16_t ghi[4][16 * DV];  // per wave: g of its 16 queries
+    alignas(16) uint16_t glo[4][16 * DV];
     float h[4][16];
 };
 
@@ -149,7 +182,7 @@ __device__ __forceinline__ void q_pass1(const BwdQSmem<DV>& sm, const bf16x4& qb
     float a[4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-        const f32x4 st = mfma16(ld4(&sm.k[(16 * kt + r) * kLdQK + 4 * g]), qb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 st = mfma16(ld4(&sm.k[tile_at<kD>(16 * kt + r, 4 * g)]), qb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const float s = st[m];
@@ -168,7 +201,7 @@ __device__ __forceinline__ void q_pass1(const BwdQSmem<DV>& sm, const bf16x4& qb
         dsum = mfma32(alo, ones, dsum);
 #pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct) {
-            const bf16x8 vb = tr_b8(sm.v, DV + 8, 32 * p, 16 * ct, g, r);
+            const bf16x8 vb = tr_b8<DV>(sm.v, 32 * p, 16 * ct, g, r);
             yacc[ct] = mfma32(ahi, vb, yacc[ct]);
             yacc[ct] = mfma32(alo, vb, yacc[ct]);
         }
@@ -184,14 +217,14 @@ __device__ __forceinline__ void q_pass2(const BwdQSmem<DV>& sm, const bf16x4& qb
     float e[4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-        const f32x4 st = mfma16(ld4(&sm.k[(16 * kt + r) * kLdQK + 4 * g]), qb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 st = mfma16(ld4(&sm.k[tile_at<kD>(16 * kt + r, 4 * g)]), qb, f32x4{0.f, 0.f, 0.f, 0.f});
         // ga^T: rows = keys 16kt + 4g + m, columns = queries r
         f32x4 ga = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cs = 0; cs < DV / 32; ++cs) {
-            const bf16x8 va = ld8(&sm.v[(16 * kt + r) * (DV + 8) + 32 * cs + 8 * g]);
-            ga = mfma32(va, ld8(&sm.ghi[w][r * (DV + 8) + 32 * cs + 8 * g]), ga);
-            ga = mfma32(va, ld8(&sm.glo[w][r * (DV + 8) + 32 * cs + 8 * g]), ga);
+            const bf16x8 va = ld8(&sm.v[tile_at<DV>(16 * kt + r, 32 * cs + 8 * g)]);
+            ga = mfma32(va, ld8(&sm.ghi[w][tile_at<DV>(r, 32 * cs + 8 * g)]), ga);
+            ga = mfma32(va, ld8(&sm.glo[w][tile_at<DV>(r, 32 * cs + 8 * g)]), ga);
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -207,7 +240,7 @@ __device__ __forceinline__ void q_pass2(const BwdQSmem<DV>& sm, const bf16x4& qb
         join_tiles(e[2 * p], e[2 * p + 1], x);
         bf16x8 ehi, elo;
         hilo8(x, ehi, elo);
-        const bf16x8 kb = tr_b8(sm.k, kLdQK, 32 * p, 0, g, r);
+        const bf16x8 kb = tr_b8<kD>(sm.k, 32 * p, 0, g, r);
         dqacc = mfma32(ehi, kb, dqacc);
         dqacc = mfma32(elo, kb, dqacc);
     }
@@ -280,8 +313,8 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(const uint16_t* __r
             const float gv = dyc * inv;
             const uint32_t hb = pack_bf16x2(gv, 0.f);
             const uint32_t lb = pack_bf16x2(gv - bf16lo_f32(hb), 0.f);
-            sm.ghi[w][(4 * g + m) * (DV + 8) + 16 * ct + r] = (uint16_t)(hb & 0xffffu);
-            sm.glo[w][(4 * g + m) * (DV + 8) + 16 * ct + r] = (uint16_t)(lb & 0xffffu);
+            sm.ghi[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(hb & 0xffffu);
+            sm.glo[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(lb & 0xffffu);
         }
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) dyy += __shfl_xor(dyy, off, 64);
@@ -301,9 +334,9 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(const uint16_t* __r
             if (qi < L) {
                 const size_t off = ((size_t)head * L + qi) * DV + 8 * u;
                 *reinterpret_cast<u32x4*>(ghi_ws + off) =
-                    *reinterpret_cast<const u32x4*>(&sm.ghi[w][row * (DV + 8) + 8 * u]);
+                    *reinterpret_cast<const u32x4*>(&sm.ghi[w][tile_at<DV>(row, 8 * u)]);
                 *reinterpret_cast<u32x4*>(glo_ws + off) =
-                    *reinterpret_cast<const u32x4*>(&sm.glo[w][row * (DV + 8) + 8 * u]);
+                    *reinterpret_cast<const u32x4*>(&sm.glo[w][tile_at<DV>(row, 8 * u)]);
             }
         }
     }
@@ -330,9 +363,9 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(const uint16_t* __r
 // ---------------------------------------------------------------- key side
 template <int DV>
 struct BwdKSmem {
-    alignas(16) uint16_t q[kT * kLdQK];
-    alignas(16) uint16_t ghi[kT * (DV + 8)];  // g of the query tile, hi / lo
-    alignas(16) uint16_t glo[kT * (DV + 8)];
+    alignas(16) uint16_t q[kT * kD];
+    alignas(16) uint16_t ghi[kT * DV];  // g of the query tile, hi / lo
+    alignas(16) uint16_t glo[kT * DV];
     alignas(16) float h[kT];
 };
 
@@ -345,12 +378,12 @@ __device__ __forceinline__ void k_tile(const BwdKSmem<DV>& sm, const bf16x4& kb,
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
         // scores and ga: rows = queries 16qt + 4g + m, columns = keys r
-        const f32x4 st = mfma16(ld4(&sm.q[(16 * qt + r) * kLdQK + 4 * g]), kb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 st = mfma16(ld4(&sm.q[tile_at<kD>(16 * qt + r, 4 * g)]), kb, f32x4{0.f, 0.f, 0.f, 0.f});
         f32x4 ga = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cs = 0; cs < DV / 32; ++cs) {
-            ga = mfma32(ld8(&sm.ghi[(16 * qt + r) * (DV + 8) + 32 * cs + 8 * g]), vb[cs], ga);
-            ga = mfma32(ld8(&sm.glo[(16 * qt + r) * (DV + 8) + 32 * cs + 8 * g]), vb[cs], ga);
+            ga = mfma32(ld8(&sm.ghi[tile_at<DV>(16 * qt + r, 32 * cs + 8 * g)]), vb[cs], ga);
+            ga = mfma32(ld8(&sm.glo[tile_at<DV>(16 * qt + r, 32 * cs + 8 * g)]), vb[cs], ga);
         }
         const f32x4 hq = *reinterpret_cast<const f32x4*>(&sm.h[16 * qt + 4 * g]);
 #pragma unroll
@@ -376,13 +409,13 @@ __device__ __forceinline__ void k_tile(const BwdKSmem<DV>& sm, const bf16x4& kb,
         hilo8(xe, ehi, elo);
 #pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct) {
-            const bf16x8 gbh = tr_b8(sm.ghi, DV + 8, 32 * p, 16 * ct, g, r);
-            const bf16x8 gbl = tr_b8(sm.glo, DV + 8, 32 * p, 16 * ct, g, r);
+            const bf16x8 gbh = tr_b8<DV>(sm.ghi, 32 * p, 16 * ct, g, r);
+            const bf16x8 gbl = tr_b8<DV>(sm.glo, 32 * p, 16 * ct, g, r);
             dvacc[ct] = mfma32(ahi, gbh, dvacc[ct]);
             dvacc[ct] = mfma32(alo, gbh, dvacc[ct]);
             dvacc[ct] = mfma32(ahi, gbl, dvacc[ct]);
         }
-        const bf16x8 qb = tr_b8(sm.q, kLdQK, 32 * p, 0, g, r);
+        const bf16x8 qb = tr_b8<kD>(sm.q, 32 * p, 0, g, r);
         dkacc = mfma32(ehi, qb, dkacc);
         dkacc = mfma32(elo, qb, dkacc);
     }
