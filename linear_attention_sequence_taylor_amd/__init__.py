@@ -48,6 +48,43 @@ def _check_tensor(name, t, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
 
 
+def _check_like(name, t, shape, dtype, device):
+    """A caller-supplied tensor: contiguous, of the given dtype, exact shape
+    and device (the kernels write or read all of it)."""
+    _check_tensor(name, t, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _check_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _workspace(ws, device):
+    """(pointer, bytes) of a caller's workspace: a contiguous device tensor."""
+    if ws is None:
+        return None, 0
+    _check_tensor("workspace", ws)
+    if ws.device != device:
+        raise ValueError(f"workspace must be on {device}, got {ws.device}")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def _initial_state(initial_state, S, z):
+    S0, z0 = initial_state
+    if tuple(S0.shape) != tuple(S.shape) or tuple(z0.shape) != tuple(z.shape):
+        raise ValueError(f"initial_state must have shapes {tuple(S.shape)} and {tuple(z.shape)}, "
+                         f"got {tuple(S0.shape)} and {tuple(z0.shape)}")
+    if S0.data_ptr() != S.data_ptr():
+        S.copy_(S0)
+    if z0.data_ptr() != z.data_ptr():
+        z.copy_(z0)
+
+
 def based_num_features(d_feat: int = D_FEAT) -> int:
     return _lib.lib().based_num_features(d_feat)
 
@@ -82,28 +119,25 @@ def based_prefill(q, k, v, *, chunk: int = 64, eps: float = 1e-6, initial_state=
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     F = 1 + d + d * d  # based_num_features(d), without a library round trip per call
     dev = q.device
+    _check_device(dev, k=k, v=v)
     if y is None:
         y = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev)
     if S is None:
         S = torch.empty((B, H, F, d_v), dtype=torch.float32, device=dev)
     if z is None:
         z = torch.empty((B, H, F), dtype=torch.float32, device=dev)
-    _check_tensor("y", y, torch.float32)
-    _check_tensor("S", S, torch.float32)
-    _check_tensor("z", z, torch.float32)
+    _check_like("y", y, (B, H, L, d_v), torch.float32, dev)
+    _check_like("S", S, (B, H, F, d_v), torch.float32, dev)
+    _check_like("z", z, (B, H, F), torch.float32, dev)
     use_init = 0
     if initial_state is not None:
-        S0, z0 = initial_state
-        if S0.data_ptr() != S.data_ptr():
-            S.copy_(S0)
-        if z0.data_ptr() != z.data_ptr():
-            z.copy_(z0)
+        _initial_state(initial_state, S, z)
         use_init = 1
     if workspace is None and dt == torch.bfloat16:
         nbytes = based_prefill_workspace_bytes(B, H, L, d_v, d)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    ws_ptr, ws_bytes = _workspace(workspace, dev)
     st = _lib.lib().based_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[dt], B, H, L, d,
                                   d_v, chunk, eps, y.data_ptr(), S.data_ptr(), z.data_ptr(), use_init,
                                   ws_ptr, ws_bytes, _stream_ptr(dev))
@@ -146,28 +180,25 @@ def based_hybrid_prefill(q, k, q_win, k_win, v, *, chunk: int = 64, eps: float =
         scale = d_qk ** -0.5
     F = 1 + d + d * d
     dev = q.device
+    _check_device(dev, k=k, q_win=q_win, k_win=k_win, v=v)
     if y is None:
         y = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev)
     if S is None:
         S = torch.empty((B, H, F, d_v), dtype=torch.float32, device=dev)
     if z is None:
         z = torch.empty((B, H, F), dtype=torch.float32, device=dev)
-    _check_tensor("y", y, torch.float32)
-    _check_tensor("S", S, torch.float32)
-    _check_tensor("z", z, torch.float32)
+    _check_like("y", y, (B, H, L, d_v), torch.float32, dev)
+    _check_like("S", S, (B, H, F, d_v), torch.float32, dev)
+    _check_like("z", z, (B, H, F), torch.float32, dev)
     use_init = 0
     if initial_state is not None:
-        S0, z0 = initial_state
-        if S0.data_ptr() != S.data_ptr():
-            S.copy_(S0)
-        if z0.data_ptr() != z.data_ptr():
-            z.copy_(z0)
+        _initial_state(initial_state, S, z)
         use_init = 1
     if workspace is None and dt == torch.bfloat16:
         nbytes = based_hybrid_prefill_workspace_bytes(B, H, L, d_v, d)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    ws_ptr, ws_bytes = _workspace(workspace, dev)
     st = _lib.lib().based_hybrid_prefill(q.data_ptr(), k.data_ptr(), q_win.data_ptr(), k_win.data_ptr(),
                                          v.data_ptr(), _DTYPES[dt], B, H, L, d, d_qk, d_v, chunk, eps, window,
                                          scale, _HYBRID_PATHS[path], y.data_ptr(), S.data_ptr(), z.data_ptr(),
@@ -189,9 +220,16 @@ def based_decode_step(q, k, v, S, z, *, eps: float = 1e-6, y=None):
     _check_tensor("z", z, torch.float32, 3)
     B, H, d = q.shape
     d_v = v.shape[-1]
+    F = 1 + d + d * d
+    dev = q.device
+    if k.shape != q.shape or v.shape[:2] != (B, H):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    _check_device(dev, k=k, v=v)
+    _check_like("S", S, (B, H, F, d_v), torch.float32, dev)
+    _check_like("z", z, (B, H, F), torch.float32, dev)
     if y is None:
-        y = torch.empty((B, H, d_v), dtype=torch.float32, device=q.device)
-    _check_tensor("y", y, torch.float32)
+        y = torch.empty((B, H, d_v), dtype=torch.float32, device=dev)
+    _check_like("y", y, (B, H, d_v), torch.float32, dev)
     st = _lib.lib().based_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[dt], B, H, d,
                                       d_v, eps, S.data_ptr(), z.data_ptr(), y.data_ptr(),
                                       _stream_ptr(q.device))
@@ -211,13 +249,17 @@ def swa_forward(q, k, v, *, window: int = 64, scale: float | None = None, add=No
     _check_tensor("v", v, dt, 4)
     B, H, L, d_qk = q.shape
     d_v = v.shape[-1]
+    dev = q.device
+    if k.shape != q.shape or v.shape[:3] != (B, H, L):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    _check_device(dev, k=k, v=v)
     if scale is None:
         scale = d_qk ** -0.5
     if y is None:
-        y = torch.empty((B, H, L, d_v), dtype=torch.float32, device=q.device)
-    _check_tensor("y", y, torch.float32)
+        y = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev)
+    _check_like("y", y, (B, H, L, d_v), torch.float32, dev)
     if add is not None:
-        _check_tensor("add", add, torch.float32)
+        _check_like("add", add, (B, H, L, d_v), torch.float32, dev)
     st = _lib.lib().swa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[dt], B, H, L, d_qk,
                                 d_v, int(window), float(scale), None if add is None else add.data_ptr(),
                                 y.data_ptr(), _stream_ptr(q.device))
@@ -237,6 +279,9 @@ def swa_cache_fill(k, v, *, window: int = 64, k_cache=None, v_cache=None):
     _check_tensor("v", v, dt, 4)
     B, H, L, d_qk = k.shape
     d_v = v.shape[-1]
+    if v.shape[:3] != (B, H, L):
+        raise ValueError(f"shape mismatch k{tuple(k.shape)} v{tuple(v.shape)}")
+    _check_device(k.device, v=v, k_cache=k_cache, v_cache=v_cache)
     if k_cache is None:
         k_cache = torch.zeros((B, H, window, d_qk), dtype=dt, device=k.device)
     if v_cache is None:
@@ -273,13 +318,15 @@ def swa_decode_step(q, k, v, k_cache, v_cache, pos, *, scale: float | None = Non
         raise ValueError("shape mismatch")
     if tuple(k_cache.shape) != (B, H, window, d_qk) or tuple(v_cache.shape) != (B, H, window, d_v):
         raise ValueError("cache shapes must be [B,H,window,d]")
+    dev = q.device
+    _check_device(dev, k=k, v=v, k_cache=k_cache, v_cache=v_cache, pos=pos)
     if scale is None:
         scale = d_qk ** -0.5
     if y is None:
-        y = torch.empty((B, H, d_v), dtype=torch.float32, device=q.device)
-    _check_tensor("y", y, torch.float32)
+        y = torch.empty((B, H, d_v), dtype=torch.float32, device=dev)
+    _check_like("y", y, (B, H, d_v), torch.float32, dev)
     if add is not None:
-        _check_tensor("add", add, torch.float32)
+        _check_like("add", add, (B, H, d_v), torch.float32, dev)
     st = _lib.lib().swa_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[dt], B, H, d_qk, d_v,
                                     int(window), float(scale), pos.data_ptr(), k_cache.data_ptr(),
                                     v_cache.data_ptr(), None if add is None else add.data_ptr(), y.data_ptr(),
@@ -303,18 +350,20 @@ def based_prefill_backward(q, k, v, dy, *, eps: float = 1e-6, dq=None, dk=None, 
     if k.shape != q.shape or v.shape[:3] != (B, H, L) or dy.shape != v.shape:
         raise ValueError("shape mismatch")
     dev = q.device
+    _check_device(dev, k=k, v=v, dy=dy)
     dq = torch.empty((B, H, L, d), dtype=torch.float32, device=dev) if dq is None else dq
     dk = torch.empty((B, H, L, d), dtype=torch.float32, device=dev) if dk is None else dk
     dv = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_tensor(name, t, torch.float32)
+    _check_like("dq", dq, (B, H, L, d), torch.float32, dev)
+    _check_like("dk", dk, (B, H, L, d), torch.float32, dev)
+    _check_like("dv", dv, (B, H, L, d_v), torch.float32, dev)
     if workspace is None:
         nbytes = based_prefill_backward_workspace_bytes(B, H, L, d_v, d)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = _workspace(workspace, dev)
     st = _lib.lib().based_prefill_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(), _DTYPES[dt], B,
                                            H, L, d, d_v, eps, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                           _stream_ptr(dev))
+                                           ws_ptr, ws_bytes, _stream_ptr(dev))
     _lib.check("based_prefill_backward", st)
     return dq, dk, dv
 
