@@ -476,7 +476,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(every (batch, head) is independent; sharding is described in DESIGN.md). "
+              "(every (batch, head) is independent, so a larger job splits over batch and heads "
+              "with no communication between GPUs). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
