@@ -116,21 +116,14 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
         qr[c].load(q + (size_t)head * DQK + 8 * c);
         knr[c].load(kn + 8 * c);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int slot = lane + 64 * r;
-            if (slot < window) kr[r][c].load(kch + (size_t)slot * DQK + 8 * c);
-            else kr[r][c].zero();
-        }
+        for (int r = 0; r < R; ++r)  // slots past the ring: a row of it, discarded below
+            kr[r][c].load(kch + (size_t)min(lane + 64 * r, window - 1) * DQK + 8 * c);
     }
     vnr.load(vn + 8 * cg);
 #pragma unroll
-    for (int i = 0; i < kKPL; ++i) {
-        const int j = kg + kKG * i;
-        if (j < window) vr[i].load(vch + (size_t)j * DV + 8 * cg);
-        else vr[i].zero();
-    }
+    for (int i = 0; i < kKPL; ++i) vr[i].load(vch + (size_t)min(kg + kKG * i, window - 1) * DV + 8 * cg);
     float ad[8];
-    if (add && kg == 0) {
+    if (add) {  // every key group loads it (the same 32 bytes); key group 0 uses it
         const f32x4 a0 = *reinterpret_cast<const f32x4*>(add + (size_t)head * DV + 8 * cg);
         const f32x4 a1 = *reinterpret_cast<const f32x4*>(add + (size_t)head * DV + 8 * cg + 4);
 #pragma unroll
@@ -159,14 +152,9 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
 #pragma unroll
         for (int c = 0; c < kQC; ++c)
             if (lane + 64 * r == slot_new) kr[r][c] = knr[c];
-#pragma unroll
-    for (int i = 0; i < kKPL; ++i) {
-        const int j = kg + kKG * i;
-        if (j == slot_new) vr[i] = vnr;
-        else if (j >= nvalid) vr[i].zero();
-    }
 
-    // ---- scores and softmax over the valid slots (fp32, base 2)
+    // ---- scores and softmax over the valid slots (fp32, base 2); they need
+    // only the keys, so they run while the value rows are still arriving
     float s[R];
     float m = -INFINITY;
 #pragma unroll
@@ -188,6 +176,12 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
     l = wave_sum(l);
 
     // ---- P.V: this lane's keys, then the sum over key groups
+#pragma unroll
+    for (int i = 0; i < kKPL; ++i) {
+        const int j = kg + kKG * i;
+        if (j == slot_new) vr[i] = vnr;
+        else if (j >= nvalid) vr[i].zero();
+    }
     float acc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = 0.f;
