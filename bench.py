@@ -230,9 +230,10 @@ def bench_decode(based, wl, n_steps):
     return wall / n_steps, timer.seconds() / n_steps
 
 
-def bench_swa(based, wl, reps):
+def bench_swa(based, wl, reps, window=None):
     """Window kernel with fused add, alternating two input/output sets;
     returns event seconds per launch over the timed region."""
+    window = wl.window if window is None else window
     q, k, v = si.linear_inputs(wl)
     qw, kw = si.window_inputs(wl)
     sets = make_sets((qw, kw, v), 2)
@@ -241,7 +242,7 @@ def bench_swa(based, wl, reps):
     ys = [torch.empty_like(adds[0]) for _ in range(2)]
 
     def launch(i):
-        based.swa_forward(*sets[i % 2], window=wl.window, scale=wl.swa_scale, add=adds[i % 2], y=ys[i % 2])
+        based.swa_forward(*sets[i % 2], window=window, scale=wl.swa_scale, add=adds[i % 2], y=ys[i % 2])
 
     for i in range(500):  # untimed warm-up, ~45 ms
         launch(i)
@@ -336,26 +337,13 @@ def bench_other_sizes(based):
     paths that carry them: seeded inputs, event-timed regions.  Returns a
     dict of legs (report only)."""
     out = {}
-    # window 128 over the 8K window workload inputs (matrix cores, two-tile halo)
+    # window 128 over the 8K window workload inputs (matrix cores, two-tile
+    # halo), timed exactly as the w = 64 leg
     ww = si.WORKLOADS["window_8k"]
-    qw, kw = si.window_inputs(ww)
-    v = si.linear_inputs(ww)[2]
-    qd, kd, vd = qw.cuda(), kw.cuda(), v.cuda()
-    del qw, kw, v
-    y = torch.empty(ww.B, ww.H, ww.L, ww.dv, device="cuda")
-    for _ in range(20):
-        based.swa_forward(qd, kd, vd, window=128, scale=ww.swa_scale, add=y, y=y)
-    t = RegionTimer()
-    torch.cuda.synchronize()
-    t.start()
-    for _ in range(20):
-        based.swa_forward(qd, kd, vd, window=128, scale=ww.swa_scale, add=y, y=y)
-    t.stop()
-    sec = t.seconds() / 20
+    sec = bench_swa(based, ww, 100, window=128)
     sb = swa_bytes(ww)
     out["window_8k_w128"] = {"kernel_us": sec * 1e6, "hbm_GBps": sb / sec / 1e9, "hbm_frac": sb / sec / HBM_PEAK,
                              "algorithmic_bytes": sb, "note": "w=128, fused add, matrix cores with a two-tile halo"}
-    del qd, kd, vd, y
     # next-token step with feature dim 32 (F = 1057), the 1.3B decode batch
     # (B=128, H=16, d_v=128; 1.1 GB of fp32 state), from a zero state
     B, H, d, dv, F32 = 128, 16, 32, 128, 1 + 32 + 32 * 32
@@ -379,7 +367,7 @@ def bench_other_sizes(based):
     # prefill with feature dim 32 (bf16 inputs widened, fp32 matrix cores), B=2, H=16, L=2048, d_v=64
     B, H, L, dv = 2, 16, 2048, 64
     q, k, v = (x.cuda() for x in si.custom((B, H, L, d), (B, H, L, dv), seed=2100, scale=0.5))
-    for _ in range(2):
+    for _ in range(100):  # untimed warm-up, ~50 ms
         based.based_prefill(q, k, v)
     t = RegionTimer()
     torch.cuda.synchronize()
@@ -399,7 +387,7 @@ def bench_other_sizes(based):
     return out
 
 
-def bench_backward(based, wl, reps=5):
+def bench_backward(based, wl, reps=40):
     """Gradients of the prefill output over the workload (bf16 inputs with
     feature dim 16: the matrix-core kernels, direct form).  Returns (event
     seconds per call, algorithmic flops): per causal (i, j) pair
@@ -412,7 +400,7 @@ def bench_backward(based, wl, reps=5):
                      device="cuda")
     run = lambda: based.based_prefill_backward(q, k, v, dy, eps=wl.eps, dq=outs[0], dk=outs[1], dv=outs[2],
                                                workspace=ws)
-    for _ in range(3):
+    for _ in range(100):  # untimed warm-up, ~50 ms
         run()
     t = RegionTimer()
     torch.cuda.synchronize()

@@ -131,7 +131,15 @@ __global__ __launch_bounds__(256) void bwd_query_f32_kernel(const T* __restrict_
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);  // D - eps of query qr, on every lane group
 
-    // ---- g = dy/D and h = -(dy.y)/D of queries qw0 + 4g + m (columns 16ct + r)
+    // ---- g = dy/D and h = -(dy.y)/D of queries qw0 + 4g + m (columns 16ct + r);
+    // the dy loads all go out at once (rows past L read row L-1, zeroed)
+    float dyv[4][kNV];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float* dyr = dy + ((size_t)head * L + min(qw0 + 4 * g + m, L - 1)) * DV + r;
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) dyv[m][ct] = dyr[16 * ct];
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int qi = qw0 + 4 * g + m;
@@ -139,7 +147,7 @@ __global__ __launch_bounds__(256) void bwd_query_f32_kernel(const T* __restrict_
         float dyy = 0.f;
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) {
-            const float dyc = qi < L ? dy[((size_t)head * L + qi) * DV + 16 * ct + r] : 0.f;
+            const float dyc = qi < L ? dyv[m][ct] : 0.f;
             dyy = fmaf(dyc, yacc[ct][m], dyy);
             const float gv = dyc * inv;
             sm.g[w][(4 * g + m) * kLdV + 16 * ct + r] = gv;

@@ -300,7 +300,16 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(const uint16_t* __r
 
     // ---- g = dy/D and h = -(dy.N)/D^2 for queries qw0 + 4g + m, columns
     // 16ct + r: g to this wave's LDS rows as bf16 hi/lo, h to LDS and the
-    // workspace
+    // workspace.  The dy loads all go out at once (rows past L read row L-1
+    // and are zeroed), not one per use.
+    float dyv[4][kNV];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int qi = qw0 + 4 * g + m;
+        const float* dyr = dy + ((size_t)head * L + min(qi, L - 1)) * DV + r;
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) dyv[m][ct] = dyr[16 * ct];
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int qi = qw0 + 4 * g + m;
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(const uint16_t* __r
         float dyy = 0.f;
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) {
-            const float dyc = qi < L ? dy[((size_t)head * L + qi) * DV + 16 * ct + r] : 0.f;
+            const float dyc = qi < L ? dyv[m][ct] : 0.f;
             dyy = fmaf(dyc, yacc[ct][m], dyy);
             const float gv = dyc * inv;
             const uint32_t hb = pack_bf16x2(gv, 0.f);
