@@ -46,16 +46,59 @@ constexpr int feat_pad() {
     return D <= 16 ? 16 : 32;
 }
 
-// Rows row0.. of a [L][W] matrix as fp32 into a [64][WP + 4] LDS tile
-// (columns W..WP-1 and rows past L zero).
-template <typename T, int W, int WP>
-__device__ __forceinline__ void stage_f32(const T* mat, int L, int row0, float* dst) {
-    constexpr int kLd = WP + 4;
-    for (int e = threadIdx.x; e < kT * WP; e += 256) {
-        const int row = e / WP, c = e % WP;
-        float x = 0.f;
-        if (c < W && row0 + row < L) x = load_elem(mat, (size_t)(row0 + row) * W + c);
-        dst[row * kLd + c] = x;
+// Rows row0.. of a [L][W] matrix as fp32 into columns 0..W-1 of a
+// [64][WP + 4] LDS tile, rows past L as zeros, in two phases: load issues
+// every 16-byte load of the tile (rows past L read row L-1), store writes
+// them to LDS.  Loading all tiles of an interval before storing any lets
+// their loads overlap instead of each waiting for the one before.  Columns
+// W..WP-1 are left alone: zero_pad zeroes them once.
+template <typename T, int W>
+struct TileStage {
+    static constexpr int kVec = 16 / (int)sizeof(T);  // elements per 16-byte piece
+    static constexpr int kPer = W / kVec;             // pieces per row
+    static constexpr int kN = kT * kPer;
+    static constexpr int kIt = (kN + 255) / 256;
+    u32x4 raw[kIt];
+
+    __device__ __forceinline__ void load(const T* mat, int L, int row0) {
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            if (kN % 256 == 0 || e < kN) {
+                const int row = e / kPer, c = (e % kPer) * kVec;
+                raw[i] = *reinterpret_cast<const u32x4*>(mat + (size_t)min(row0 + row, L - 1) * W + c);
+            }
+        }
+    }
+    template <int WP>
+    __device__ __forceinline__ void store(int L, int row0, float* dst) const {
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            if (kN % 256 == 0 || e < kN) {
+                const int row = e / kPer, c = (e % kPer) * kVec;
+                const bool live = row0 + row < L;
+                f32x4* d = reinterpret_cast<f32x4*>(dst + row * (WP + 4) + c);
+                if constexpr (sizeof(T) == 4) {
+                    d[0] = live ? __builtin_bit_cast(f32x4, raw[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+                } else {
+                    const uint32_t a0 = raw[i][0], a1 = raw[i][1], a2 = raw[i][2], a3 = raw[i][3];
+                    const f32x4 x0 = {bf16lo_f32(a0), bf16hi_f32(a0), bf16lo_f32(a1), bf16hi_f32(a1)};
+                    const f32x4 x1 = {bf16lo_f32(a2), bf16hi_f32(a2), bf16lo_f32(a3), bf16hi_f32(a3)};
+                    d[0] = live ? x0 : f32x4{0.f, 0.f, 0.f, 0.f};
+                    d[1] = live ? x1 : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    }
+};
+// Zeroes columns W..WP-1 of a [64][WP + 4] LDS tile (the feature padding,
+// which staging never writes).
+template <int W, int WP>
+__device__ __forceinline__ void zero_pad(float* dst) {
+    if constexpr (WP > W) {
+        constexpr int kP = WP - W;
+        for (int e = threadIdx.x; e < kT * kP; e += 256) dst[(e / kP) * (WP + 4) + W + e % kP] = 0.f;
     }
 }
 
@@ -107,10 +150,15 @@ __global__ __launch_bounds__(256) void bwd_query_f32_kernel(const T* __restrict_
 #pragma unroll
     for (int ct = 0; ct < kNV; ++ct) yacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
+    zero_pad<D, kKW>(sm.k);
+    TileStage<T, D> kst;
+    TileStage<T, DV> vst;
     for (int tj = 0; tj <= ti; ++tj) {
         __syncthreads();
-        stage_f32<T, D, kKW>(kh, L, tj * kT, sm.k);
-        stage_f32<T, DV, DV>(vh, L, tj * kT, sm.v);
+        kst.load(kh, L, tj * kT);
+        vst.load(vh, L, tj * kT);
+        kst.template store<kKW>(L, tj * kT, sm.k);
+        vst.template store<DV>(L, tj * kT, sm.v);
         __syncthreads();
         const bool diag = tj == ti;
 #pragma unroll
@@ -170,8 +218,10 @@ __global__ __launch_bounds__(256) void bwd_query_f32_kernel(const T* __restrict_
     for (int tj = ti; tj >= 0; --tj) {
         __syncthreads();  // also orders the g/h writes above before their reads
         if (tj != ti) {
-            stage_f32<T, D, kKW>(kh, L, tj * kT, sm.k);
-            stage_f32<T, DV, DV>(vh, L, tj * kT, sm.v);
+            kst.load(kh, L, tj * kT);
+            vst.load(vh, L, tj * kT);
+            kst.template store<kKW>(L, tj * kT, sm.k);
+            vst.template store<DV>(L, tj * kT, sm.v);
             __syncthreads();
         }
         const bool diag = tj == ti;
@@ -246,11 +296,18 @@ __global__ __launch_bounds__(256) void bwd_key_f32_kernel(const T* __restrict__ 
 #pragma unroll
     for (int ct = 0; ct < kNK; ++ct) dkacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    zero_pad<D, kKW>(sm.q);
+    TileStage<T, D> qst;
+    TileStage<float, DV> gst;
     for (int ti = tj; ti < ntiles; ++ti) {
         __syncthreads();
-        stage_f32<T, D, kKW>(qh, L, ti * kT, sm.q);
-        stage_f32<float, DV, DV>(gh, L, ti * kT, sm.g);
-        if (threadIdx.x < kT) sm.h[threadIdx.x] = ti * kT + (int)threadIdx.x < L ? hh[ti * kT + threadIdx.x] : 0.f;
+        float hq = 0.f;
+        if (threadIdx.x < kT) hq = hh[min(ti * kT + (int)threadIdx.x, L - 1)];
+        qst.load(qh, L, ti * kT);
+        gst.load(gh, L, ti * kT);
+        qst.template store<kKW>(L, ti * kT, sm.q);
+        gst.template store<DV>(L, ti * kT, sm.g);
+        if (threadIdx.x < kT) sm.h[threadIdx.x] = ti * kT + (int)threadIdx.x < L ? hq : 0.f;
         __syncthreads();
         const bool diag = ti == tj;
 #pragma unroll
