@@ -112,30 +112,33 @@ struct F32Smem {
 };
 
 // Staging of one chunk: q~, k~ (pre-scaled) and the workgroup's v columns.
+// load issues every element's load unconditionally (the source is selected,
+// tokens past L read token L-1, and the slots past the chunk's elements
+// read a valid element they never store), so all of them are in flight
+// together; the zeroing of tokens past L and the bf16 widening wait for
+// store.
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(uint16_t x) { return bf16_bits_to_f32(x); }
+
 template <typename T, int D>
 struct Stage {
     static constexpr int kQK = kC * D;  // elements of q (and of k)
     static constexpr int kV = kC * kCW;
     static constexpr int kPer = (2 * kQK + kV + kThreads - 1) / kThreads;
-    float x[kPer];
+    T x[kPer];
 
     __device__ __forceinline__ void load(const T* qh, const T* kh, const T* vh, int ldv, int t0, int L) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int e = threadIdx.x + kThreads * i;
-            float val = 0.f;
-            if (e < 2 * kQK) {
-                const int w = e % kQK, t = w / D, c = w % D;
-                const T* src = e < kQK ? qh : kh;
-                if (t0 + t < L) val = load_elem(src, (size_t)(t0 + t) * D + c) * Feat<D>::kPre;
-            } else if (e < 2 * kQK + kV) {
-                const int w = e - 2 * kQK, t = w / kCW, c = w % kCW;
-                if (t0 + t < L) val = load_elem(vh, (size_t)(t0 + t) * ldv + c);
-            }
-            x[i] = val;
+            const bool qk = e < 2 * kQK;
+            const int w = qk ? e % kQK : e - 2 * kQK;
+            const int tok = min(t0 + (qk ? w / D : w / kCW), L - 1);
+            const T* src = qk ? (e < kQK ? qh : kh) + (size_t)tok * D + w % D : vh + (size_t)tok * ldv + w % kCW;
+            x[i] = *src;
         }
     }
-    __device__ __forceinline__ void store(F32Smem<D>& sm, int buf) const {
+    __device__ __forceinline__ void store(F32Smem<D>& sm, int buf, int t0, int L) const {
         constexpr int kLd = F32Smem<D>::kLd;
         if (threadIdx.x < 2 * kC) (threadIdx.x < kC ? sm.q[buf] : sm.k[buf])[(threadIdx.x % kC) * kLd + D] = 1.f;
 #pragma unroll
@@ -143,9 +146,10 @@ struct Stage {
             const int e = threadIdx.x + kThreads * i;
             if (e < 2 * kQK) {
                 const int w = e % kQK, t = w / D, c = w % D;
-                (e < kQK ? sm.q[buf] : sm.k[buf])[t * kLd + c] = x[i];
+                (e < kQK ? sm.q[buf] : sm.k[buf])[t * kLd + c] = t0 + t < L ? widen(x[i]) * Feat<D>::kPre : 0.f;
             } else if (e < 2 * kQK + kV) {
-                sm.v[buf][e - 2 * kQK] = x[i];
+                const int w = e - 2 * kQK;
+                sm.v[buf][w] = t0 + w / kCW < L ? widen(x[i]) : 0.f;
             }
         }
     }
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32mfma_kernel(const T* _
     publish();
     Stage<T, D> st;
     st.load(qh, kh, vh, dv, 0, L);
-    st.store(sm, 0);
+    st.store(sm, 0, 0, L);
     __syncthreads();
 
     const int tt = w & 3, half = w >> 2;  // readout: query tile, feature half
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32mfma_kernel(const T* _
             }
         }
         publish();
-        if (more) st.store(sm, buf ^ 1);
+        if (more) st.store(sm, buf ^ 1, t0 + kC, L);
         __syncthreads();
     }
 
