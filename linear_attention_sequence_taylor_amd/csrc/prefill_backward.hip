@@ -132,9 +132,14 @@ __global__ __launch_bounds__(256) void bwd_query_f32_kernel(const T* __restrict_
     const int qr = qw0 + r;            // this lane's query in the score tiles
 
     // B operand of the scores: this lane's query, dims 4j + g, / sqrt(d')
+    // (all loads first, from row L-1 past the end, then zeroed there)
     float qb[D / 4];
+    const T* qrow = q + ((size_t)head * L + min(qr, L - 1)) * D + g;
+    T qraw[D / 4];
 #pragma unroll
-    for (int j = 0; j < D / 4; ++j) qb[j] = qr < L ? load_elem(q, ((size_t)head * L + qr) * D + 4 * j + g) * isd : 0.f;
+    for (int j = 0; j < D / 4; ++j) qraw[j] = qrow[4 * j];
+#pragma unroll
+    for (int j = 0; j < D / 4; ++j) qb[j] = qr < L ? load_elem(qraw, j) * isd : 0.f;
 
     // scores of key tile kt: st[m] = s(key 16kt + 4g + m, query r)
     auto scores = [&](int kt) {
@@ -285,11 +290,19 @@ __global__ __launch_bounds__(256) void bwd_key_f32_kernel(const T* __restrict__ 
 
     // this lane's key (/ sqrt(d')) and value: the B operands of Q K^T and
     // g V^T (dims / columns 4j + g)
+    // (all loads first, from row L-1 past the end, then zeroed there)
     float kb[D / 4], vb[DV / 4];
+    const T* krow = k + ((size_t)head * L + min(kr, L - 1)) * D + g;
+    const T* vrow = v + ((size_t)head * L + min(kr, L - 1)) * DV + g;
+    T kraw[D / 4], vraw[DV / 4];
 #pragma unroll
-    for (int j = 0; j < D / 4; ++j) kb[j] = kr < L ? load_elem(k, ((size_t)head * L + kr) * D + 4 * j + g) * isd : 0.f;
+    for (int j = 0; j < D / 4; ++j) kraw[j] = krow[4 * j];
 #pragma unroll
-    for (int j = 0; j < DV / 4; ++j) vb[j] = kr < L ? load_elem(v, ((size_t)head * L + kr) * DV + 4 * j + g) : 0.f;
+    for (int j = 0; j < DV / 4; ++j) vraw[j] = vrow[4 * j];
+#pragma unroll
+    for (int j = 0; j < D / 4; ++j) kb[j] = kr < L ? load_elem(kraw, j) * isd : 0.f;
+#pragma unroll
+    for (int j = 0; j < DV / 4; ++j) vb[j] = kr < L ? load_elem(vraw, j) : 0.f;
     f32x4 dvacc[kNV], dkacc[kNK];
 #pragma unroll
     for (int ct = 0; ct < kNV; ++ct) dvacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
