@@ -781,10 +781,11 @@ __device__ __forceinline__ void window_wave(const uint16_t* __restrict__ q2h, co
     __syncthreads();  // first chunk staged
     for (int c = 0; c < nchunks; ++c) {
         const bool more = c + 1 < nchunks;
-        if (more) {
-            win_load(rg, k2h, v2h, ldv, tb + (c + 1) * kC, L, t);
-            win_qload(qn, q2h, tb + (c + 1) * kC + 16 * DQ + r, L, g);
-        }
+        // unconditional (past the last chunk the rows are clamped and the
+        // data unused): a load inside `if (more)` made the join wait for it
+        // before this chunk's products
+        win_load(rg, k2h, v2h, ldv, tb + (c + 1) * kC, L, t);
+        win_qload(qn, q2h, tb + (c + 1) * kC + 16 * DQ + r, L, g);
         f32x4 o[3];
         if (window == kWinD && tb + c * kC >= kC)
             win_block<DQ, true>(ws, c % 3, (c + 2) % 3, qc, tb + c * kC, window, sl2, g, r, o);
