@@ -19,6 +19,11 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool 
 // (prefill_f32mfma.hip); bf16 inputs are widened exactly.
 hipError_t launch_prefill_f32mfma(const void* q, const void* k, const void* v, bool bf16, int BH, int L, int d,
                                   int dv, float eps, float* y, float* S, float* z, int use_init, hipStream_t st);
+// Final normaliser state z = z_init + sum_t phi(k_t) (prefill_valu.hip), one
+// workgroup per head; launched after a prefill whose column groups only
+// read the caller's initial z.
+hipError_t launch_prefill_z(const void* k, bool bf16, int BH, int L, int d, float* z, int use_init,
+                            hipStream_t st);
 hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, bool bf16, int BH, int L, int d,
                                int dv, int chunk, float eps, float* y, float* S, float* z,
                                int use_init, hipStream_t st);

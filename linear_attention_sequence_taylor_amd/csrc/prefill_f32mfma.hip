@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32mfma_kernel(const T* _
                                                                       const T* __restrict__ v, int L, int dv,
                                                                       float eps, float* __restrict__ y,
                                                                       float* __restrict__ S, float* __restrict__ z,
-                                                                      int use_init) {
+                                                                      int use_init, int write_z) {
     using M = FMap<D>;
     constexpr int kLd = F32Smem<D>::kLd;
     __shared__ F32Smem<D> sm;
@@ -342,7 +342,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32mfma_kernel(const T* _
         __syncthreads();
     }
 
-    // ---- final state in the caller's rows (z from column group 0): a pair
+    // ---- final state in the caller's rows (z from column group 0, unless a
+    // carried z is shared by several groups: then every group must read the
+    // caller's z however late it starts, and a later launch writes it): a pair
     // row goes to both mirror rows, as T / sqrt2 or, after a carried state,
     // as that state plus this call's increment
     auto store_row = [&](int f, int col, float tv, float* base, size_t stride) {
@@ -374,27 +376,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32mfma_kernel(const T* _
             float zs = zp[u];
             zs += __shfl_xor(zs, 16, 64);
             zs += __shfl_xor(zs, 32, 64);
-            if (cg == 0 && g == 0) store_row(16 * rt + r, 0, zs, zh, 1);
+            if (write_z && cg == 0 && g == 0) store_row(16 * rt + r, 0, zs, zh, 1);
         }
     }
 }
 
 template <typename T, int D>
 void launch_d(const void* q, const void* k, const void* v, int BH, int L, int dv, float eps, float* y, float* S,
-              float* z, int use_init, hipStream_t st) {
+              float* z, int use_init, int write_z, hipStream_t st) {
     hipLaunchKernelGGL((prefill_f32mfma_kernel<T, D>), dim3((unsigned)(BH * (dv / kCW))), dim3(kThreads), 0, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), L, dv, eps, y,
-                       S, z, use_init);
+                       S, z, use_init, write_z);
 }
 
 template <typename T>
 void launch_t(const void* q, const void* k, const void* v, int BH, int L, int d, int dv, float eps, float* y,
-              float* S, float* z, int use_init, hipStream_t st) {
+              float* S, float* z, int use_init, int write_z, hipStream_t st) {
     switch (d) {
-        case 8: launch_d<T, 8>(q, k, v, BH, L, dv, eps, y, S, z, use_init, st); break;
-        case 24: launch_d<T, 24>(q, k, v, BH, L, dv, eps, y, S, z, use_init, st); break;
-        case 32: launch_d<T, 32>(q, k, v, BH, L, dv, eps, y, S, z, use_init, st); break;
-        default: launch_d<T, 16>(q, k, v, BH, L, dv, eps, y, S, z, use_init, st); break;
+        case 8: launch_d<T, 8>(q, k, v, BH, L, dv, eps, y, S, z, use_init, write_z, st); break;
+        case 24: launch_d<T, 24>(q, k, v, BH, L, dv, eps, y, S, z, use_init, write_z, st); break;
+        case 32: launch_d<T, 32>(q, k, v, BH, L, dv, eps, y, S, z, use_init, write_z, st); break;
+        default: launch_d<T, 16>(q, k, v, BH, L, dv, eps, y, S, z, use_init, write_z, st); break;
     }
 }
 
@@ -402,9 +404,15 @@ void launch_t(const void* q, const void* k, const void* v, int BH, int L, int d,
 
 hipError_t launch_prefill_f32mfma(const void* q, const void* k, const void* v, bool bf16, int BH, int L, int d,
                                   int dv, float eps, float* y, float* S, float* z, int use_init, hipStream_t st) {
-    if (bf16) launch_t<uint16_t>(q, k, v, BH, L, d, dv, eps, y, S, z, use_init, st);
-    else launch_t<float>(q, k, v, BH, L, d, dv, eps, y, S, z, use_init, st);
-    return hipGetLastError();
+    // With a carried z and several column groups, no group may overwrite z
+    // while another may still read it: the groups leave z alone and a
+    // stream-ordered launch adds this call's increment afterwards.
+    const bool z_after = use_init && dv / kCW > 1;
+    if (bf16) launch_t<uint16_t>(q, k, v, BH, L, d, dv, eps, y, S, z, use_init, z_after ? 0 : 1, st);
+    else launch_t<float>(q, k, v, BH, L, d, dv, eps, y, S, z, use_init, z_after ? 0 : 1, st);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !z_after) return e;
+    return launch_prefill_z(k, bf16, BH, L, d, z, use_init, st);
 }
 
 }  // namespace based

@@ -186,6 +186,17 @@ __global__ __launch_bounds__(256) void prefill_valu_z_kernel(const T* __restrict
     }
 }
 
+template <typename T>
+static void launch_z_t(const void* k, int BH, int L, int d, float* z, int use_init, hipStream_t st) {
+    const T* kk = static_cast<const T*>(k);
+    switch (d) {
+        case 8: hipLaunchKernelGGL((prefill_valu_z_kernel<T, 8>), dim3(BH), dim3(256), 0, st, kk, L, z, use_init); break;
+        case 24: hipLaunchKernelGGL((prefill_valu_z_kernel<T, 24>), dim3(BH), dim3(256), 0, st, kk, L, z, use_init); break;
+        case 32: hipLaunchKernelGGL((prefill_valu_z_kernel<T, 32>), dim3(BH), dim3(256), 0, st, kk, L, z, use_init); break;
+        default: hipLaunchKernelGGL((prefill_valu_z_kernel<T, 16>), dim3(BH), dim3(256), 0, st, kk, L, z, use_init); break;
+    }
+}
+
 template <typename T, int D>
 static void launch_valu_d(const T* q, const T* k, const T* v, int BH, int L, int dv, int chunk, float eps,
                           float* y, float* S, float* z, int use_init, hipStream_t st) {
@@ -228,6 +239,13 @@ hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, bool
                                int use_init, hipStream_t st) {
     return bf16 ? launch_valu_t<uint16_t>(q, k, v, BH, L, d, dv, chunk, eps, y, S, z, use_init, st)
                 : launch_valu_t<float>(q, k, v, BH, L, d, dv, chunk, eps, y, S, z, use_init, st);
+}
+
+hipError_t launch_prefill_z(const void* k, bool bf16, int BH, int L, int d, float* z, int use_init,
+                            hipStream_t st) {
+    if (bf16) launch_z_t<uint16_t>(k, BH, L, d, z, use_init, st);
+    else launch_z_t<float>(k, BH, L, d, z, use_init, st);
+    return hipGetLastError();
 }
 
 }  // namespace based
