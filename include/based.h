@@ -115,10 +115,11 @@ size_t based_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
  *   workspace, workspace_bytes  optional scratch (may be NULL/0); see
  *          based_prefill_workspace_bytes.  With too small a workspace the
  *          call still runs, without the segment split.
- * Supported: d_feat in {8, 16, 24, 32} (16 with bf16 inputs on the matrix
- * cores, the others on the vector ALUs in fp32, a slower path); d_v in
- * {64, 128}; L >= 1 (any, not only multiples of chunk).  y must not alias
- * q, k, v, S or z.
+ * Supported: d_feat in {8, 16, 24, 32}; d_v in {64, 128}; L >= 1 (any, not
+ * only multiples of chunk).  bf16 inputs with d_feat = 16 run on the bf16
+ * matrix cores (fp32 accumulation and state); every other input runs in
+ * fp32 throughout: chunk 64 on the fp32 matrix cores, chunks 16 and 32 on
+ * the vector ALUs.  y must not alias q, k, v, S or z.
  */
 based_status_t based_prefill(const void *q, const void *k, const void *v,
                              based_dtype_t dtype, int B, int H, int L,
@@ -161,8 +162,12 @@ based_status_t based_decode_step(const void *q, const void *k, const void *v,
  *          attention output of the same layer); NULL for none; may equal y
  *          for an in-place accumulate
  *   y      [B,H,L,d_v] fp32 out
- * Supported: d_qk in {16, 64}; d_v = 64; 1 <= window <= 128 (bf16 on the
- * matrix cores, fp32 inputs on the vector ALUs in fp32).
+ * Supported: d_qk in {16, 64}; d_v in {64, 128}; any window >= 1 (a
+ * window of L or more keys is plain causal softmax attention).  bf16 inputs
+ * run on the matrix cores (windows up to 128 keys in one pass over a tile's
+ * keys, longer windows with a running-maximum softmax over 64-key tiles);
+ * fp32 inputs, and bf16 heads with L * d_v * 4 >= 2^31, run in fp32 on the
+ * vector ALUs.
  */
 based_status_t swa_forward(const void *q, const void *k, const void *v,
                            based_dtype_t dtype, int B, int H, int L,
@@ -186,10 +191,11 @@ based_status_t swa_forward(const void *q, const void *k, const void *v,
  *   window, scale: as swa_forward;  y [B,H,L,d_v] fp32 out
  *   path          BASED_HYBRID_AUTO, _FUSED or _TWO_PASS (below);
  *                 anything else is BASED_E_INVALID
- * Supported: what both based_prefill and swa_forward support with d_v = 64.
- * A fused kernel exists for bf16 with d_feat = 16, d_qk = 64 and
- * window <= 64 (q, k, q_win, k_win and v read once, y written once); an
- * initial state with no large enough workspace has none.  The two-pass
+ * Supported: what both based_prefill and swa_forward support (d_v in
+ * {64, 128}, any window >= 1).  A fused kernel exists for bf16 with
+ * d_feat = 16, d_qk = 64 and window <= 64 (q, k, q_win, k_win and v read
+ * once, y written once); an initial state with no large enough workspace
+ * has none.  The two-pass
  * form runs the branches in turn on the stream (the window adds into y in
  * place).  AUTO fuses wherever a fused kernel exists; FUSED returns
  * BASED_E_UNSUPPORTED where none does; TWO_PASS always runs the branches

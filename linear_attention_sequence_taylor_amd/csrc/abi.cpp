@@ -16,8 +16,10 @@
 
 namespace {
 
-// The feature dims every path supports; the bf16 matrix-core prefill is
-// built for 16 (its 16-row rotation tiles), the others run on the vector ALUs.
+// The feature dims every path supports.  The bf16 matrix-core prefill is
+// built for 16 (its 16-row rotation tiles); other dims, and fp32 inputs, run
+// in fp32 on the fp32 matrix cores (chunk 64) or the vector ALUs (chunks 16
+// and 32).
 constexpr int kDFeatMfma = 16;
 bool feat_dim_ok(int d) { return d == 8 || d == 16 || d == 24 || d == 32; }
 
@@ -157,7 +159,7 @@ BASED_API based_status_t swa_forward(const void* q, const void* k, const void* v
     uint64_t BH, BHL;
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
     if (d_qk != 16 && d_qk != 64) return BASED_E_UNSUPPORTED;
-    if (d_v != 64 || window > 128) return BASED_E_UNSUPPORTED;
+    if (d_v != 64 && d_v != 128) return BASED_E_UNSUPPORTED;
     const uint64_t es = elem_size(dtype);
     const uint64_t qk_bytes = BHL * d_qk * es, v_bytes = BHL * d_v * es, y_bytes = BHL * d_v * 4;
     if (overlaps(y, y_bytes, q, qk_bytes) || overlaps(y, y_bytes, k, qk_bytes) ||
@@ -165,22 +167,22 @@ BASED_API based_status_t swa_forward(const void* q, const void* k, const void* v
         return BASED_E_INVALID;
     if (add && add != y && overlaps(add, y_bytes, y, y_bytes)) return BASED_E_INVALID;
     const uint64_t tiles = ((uint64_t)L + 63) / 64;
-    if (BH * tiles > (uint64_t)INT32_MAX / 2) return BASED_E_INVALID;
+    if (BH * tiles * (d_v / 64) > (uint64_t)INT32_MAX / 2) return BASED_E_INVALID;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    // The matrix-core kernel addresses a head's fp32 rows with 32-bit byte
-    // offsets (L * 256 bytes); longer heads take the fp32 kernel.
+    // The matrix-core kernels address a head's fp32 rows with 32-bit byte
+    // offsets (L * d_v * 4 bytes); longer heads take the fp32 kernels.
     const bool bf16 = dtype == BASED_BF16;
-    if (bf16 && (uint64_t)L * 256 <= (uint64_t)INT32_MAX)
+    if (bf16 && (uint64_t)L * d_v * 4 <= (uint64_t)INT32_MAX)
         return launch_status(
-            based::launch_swa_mfma(q, k, v, (int)BH, L, d_qk, window, scale, add, y, st));
+            based::launch_swa_mfma(q, k, v, (int)BH, L, d_qk, d_v, window, scale, add, y, st));
     return launch_status(
-        based::launch_swa_valu(q, k, v, bf16, (int)BH, L, d_qk, window, scale, add, y, st));
+        based::launch_swa_valu(q, k, v, bf16, (int)BH, L, d_qk, d_v, window, scale, add, y, st));
 }
 
 BASED_API size_t based_hybrid_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v) {
     uint64_t BH, BHL;
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return 0;
-    if (d_feat != kDFeatMfma || d_v != 64) return 0;
+    if (d_feat != kDFeatMfma || (d_v != 64 && d_v != 128)) return 0;
     const size_t a = based::prefill_mfma_workspace_bytes((int)BH, L, d_v);
     const size_t b = based::hybrid_mfma_workspace_bytes((int)BH, L, d_v);
     return a > b ? a : b;
@@ -202,7 +204,7 @@ BASED_API based_status_t based_hybrid_prefill(const void* q, const void* k, cons
         return BASED_E_INVALID;
     uint64_t BH, BHL;
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return BASED_E_INVALID;
-    if (!feat_dim_ok(d_feat) || d_v != 64 || (d_qk != 16 && d_qk != 64) || window > 128)
+    if (!feat_dim_ok(d_feat) || (d_v != 64 && d_v != 128) || (d_qk != 16 && d_qk != 64))
         return BASED_E_UNSUPPORTED;
     const bool bf16 = dtype == BASED_BF16;
     const bool mfma = bf16 && d_feat == kDFeatMfma;
@@ -220,7 +222,7 @@ BASED_API based_status_t based_hybrid_prefill(const void* q, const void* k, cons
         for (int b = 0; b < 5; ++b)
             if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return BASED_E_INVALID;
     }
-    if (BH * (((uint64_t)L + 63) / 64) > (uint64_t)INT32_MAX / 2) return BASED_E_INVALID;
+    if (BH * (((uint64_t)L + 63) / 64) * (d_v / 64) > (uint64_t)INT32_MAX / 2) return BASED_E_INVALID;
     hipStream_t st = static_cast<hipStream_t>(stream);
     // The fused pass where it exists and is chosen; otherwise the two
     // branches in turn (the window adds into y in place).

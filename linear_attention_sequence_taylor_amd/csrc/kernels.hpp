@@ -44,13 +44,16 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int 
                                float eps, float* y, float* S, float* z, int use_init,
                                void* workspace, size_t workspace_bytes, hipStream_t st);
 
-// fp32 vector-ALU sliding-window softmax (swa_valu.hip).  dqk in {16, 64}.
+// fp32 vector-ALU sliding-window softmax (swa_valu.hip).  dqk in {16, 64},
+// dv in {64, 128}, any window >= 1.
 hipError_t launch_swa_valu(const void* q, const void* k, const void* v, bool bf16, int BH, int L,
-                           int dqk, int window, float scale, const float* add, float* y,
+                           int dqk, int dv, int window, float scale, const float* add, float* y,
                            hipStream_t st);
 
-// bf16 MFMA sliding-window softmax (swa_mfma.hip).  dqk in {16, 64}.
-hipError_t launch_swa_mfma(const void* q, const void* k, const void* v, int BH, int L, int dqk,
+// bf16 MFMA sliding-window softmax (swa_mfma.hip).  dqk in {16, 64}, dv in
+// {64, 128} (64-column slices), any window >= 1 (over 128 keys: the
+// online-softmax kernel); L * dv * 4 must fit in 31 bits.
+hipError_t launch_swa_mfma(const void* q, const void* k, const void* v, int BH, int L, int dqk, int dv,
                            int window, float scale, const float* add, float* y, hipStream_t st);
 
 // Next-token step of the sliding window on its key/value ring cache, and the

@@ -1096,13 +1096,14 @@ __global__ __launch_bounds__(HYB ? 1024 : 768, 1) void prefill_mfma_kernel(
     float* ws_in = nullptr;
     float* ws_out = nullptr;
     // The fused layer's segment pass reads the state of a 64-column state
-    // pass (one slot per head and segment): its column group's tiles of it.
+    // pass (one slot per head, segment and 64-column group): its column
+    // group's tiles of it.
     int ws_nct = DV / 16 + 1, ws_ct0 = 0;
     if (MODE != kModeFull) {
         if (HYB) {
             ws_nct = 64 / 16 + 1;
-            ws_ct0 = (DV / 16) * cg;
-            ws_in = ws + ((size_t)seg * BH + head) * ws_slot_floats<64>();
+            ws_ct0 = (DV / 16) * (cg % 2);
+            ws_in = ws + (((size_t)seg * BH + head) * (ldv / 64) + cg / 2) * ws_slot_floats<64>();
         } else {
             ws_in = ws + (((size_t)seg * BH + head) * ncg + cg) * ws_slot_floats<DV>();
             ws_out = ws + (((size_t)((seg + 1) % nseg) * BH + head) * ncg + cg) * ws_slot_floats<DV>();
@@ -1296,14 +1297,14 @@ static PrefillPlan plan_hybrid(int BH, int L, int dv, bool use_init, bool have_w
     return pl;
 }
 
-static size_t hybrid_ws_bytes(const PrefillPlan& pl, int BH) {
-    return (size_t)pl.nseg * BH * ws_slot_floats<64>() * sizeof(float);
+static size_t hybrid_ws_bytes(const PrefillPlan& pl, int BH, int dv) {
+    return (size_t)pl.nseg * BH * (dv / 64) * ws_slot_floats<64>() * sizeof(float);
 }
 
 size_t hybrid_mfma_workspace_bytes(int BH, int L, int dv) {
     const PrefillPlan pl = plan_hybrid(BH, L, dv, true, true);
     const bool via_ws = pl.nseg > 1 || pl.ncg > 1;
-    return via_ws ? hybrid_ws_bytes(pl, BH) : 0;
+    return via_ws ? hybrid_ws_bytes(pl, BH, dv) : 0;
 }
 
 static hipError_t launch_hybrid_plan(const PrefillPlan& pl, const uint16_t* q, const uint16_t* k,
@@ -1320,13 +1321,14 @@ static hipError_t launch_hybrid_plan(const PrefillPlan& pl, const uint16_t* q, c
     const int seg_len = ((nchunks + pl.nseg - 1) / pl.nseg) * kC;
     const int nseg = (L + seg_len - 1) / seg_len;
     float* wsf = static_cast<float*>(ws);
-    // state pass and scan at 64 columns (d_v = 64: one column group)
-    hipLaunchKernelGGL((prefill_mfma_kernel<64, kModeState>), dim3(BH * nseg), dim3(768), 0, st, q, k, v, L, dv, 1,
-                       seg_len, nseg, eps, y, S, z, use_init, wsf, nullptr, nullptr, 0, 0.f);
+    // state pass and scan at 64 columns (one group per 64 value columns)
+    const int ncg64 = dv / 64;
+    hipLaunchKernelGGL((prefill_mfma_kernel<64, kModeState>), dim3(BH * ncg64 * nseg), dim3(768), 0, st, q, k, v, L,
+                       dv, ncg64, seg_len, nseg, eps, y, S, z, use_init, wsf, nullptr, nullptr, 0, 0.f);
     const size_t slot = ws_slot_floats<64>();
     if (nseg > 1)
-        hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH), dim3(256), 0, st, wsf,
-                           nseg, BH, slot);
+        hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH * ncg64), dim3(256), 0, st,
+                           wsf, nseg, BH * ncg64, slot);
     hipLaunchKernelGGL((prefill_mfma_kernel<kWinCols, kModeSegment, true>), dim3(BH * pl.ncg * nseg), dim3(1024), 0,
                        st, q, k, v, L, dv, pl.ncg, seg_len, nseg, eps, y, S, z, use_init, wsf, q2, k2, window,
                        win_scale);
@@ -1338,8 +1340,8 @@ hipError_t launch_hybrid_mfma(const void* q, const void* k, const void* q2, cons
                               int use_init, void* ws, size_t ws_bytes, hipStream_t st, bool* launched) {
     PrefillPlan pl = plan_hybrid(BH, L, dv, use_init != 0, ws != nullptr);
     const bool via_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
-    if (via_ws && ws_bytes < hybrid_ws_bytes(pl, BH)) pl = plan_hybrid(BH, L, dv, use_init != 0, false);
-    *launched = pl.dvl == kWinCols && dv == 64;
+    if (via_ws && ws_bytes < hybrid_ws_bytes(pl, BH, dv)) pl = plan_hybrid(BH, L, dv, use_init != 0, false);
+    *launched = pl.dvl == kWinCols && (dv == 64 || dv == 128);
     if (!*launched) return hipSuccess;
     return launch_hybrid_plan(pl, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                               static_cast<const uint16_t*>(v), BH, L, dv, eps, y, S, z, use_init, ws, st,

@@ -74,8 +74,11 @@ __device__ __forceinline__ int tile_idx(int row, int col) {
 // rows row0.. of a [L][D] matrix (clamped into [0, L)) into an LDS tile.
 // The DMA puts lane l's 16 bytes at byte 16*l of the block, so each lane
 // fetches the source unit that the swizzle stores there.
+// ld is the source's row stride in elements (D for q and k; the value head
+// dim for a 64-column slice of v).
 template <int D>
-__device__ __forceinline__ void dma_block(const uint16_t* mat, int L, int row0, uint16_t* tile, int b, int lane) {
+__device__ __forceinline__ void dma_block(const uint16_t* mat, int ld, int L, int row0, uint16_t* tile, int b,
+                                          int lane) {
     constexpr int kUnits = D / 8;       // 16-byte units per row
     constexpr int kRows = 64 / kUnits;  // rows per 1 KB block
     const int row = kRows * b + lane / kUnits;
@@ -83,27 +86,28 @@ __device__ __forceinline__ void dma_block(const uint16_t* mat, int L, int row0, 
     const int sw = D == 64 ? (row & 7) : ((row >> 3) & 1);
     const int gu = su ^ sw;
     const int src = min(max(row0 + row, 0), L - 1);
-    __builtin_amdgcn_global_load_lds(mat + (size_t)src * D + 8 * gu, BASED_LDS(void, tile + 512 * b), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(mat + (size_t)src * ld + 8 * gu, BASED_LDS(void, tile + 512 * b), 16, 0, 0);
 }
 
 // Copies of tile t into slots ks, vs (and qs), split over the four waves.
 // with_q = false for the halo before the run.
 template <int DQK>
-__device__ __forceinline__ void dma_tile(const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int L, int t,
-                                         uint16_t* ks, uint16_t* vs, uint16_t* qs, bool with_q, int w, int lane) {
+__device__ __forceinline__ void dma_tile(const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, int ldv, int L,
+                                         int t, uint16_t* ks, uint16_t* vs, uint16_t* qs, bool with_q, int w,
+                                         int lane) {
     const int row0 = t * kQT;
-    dma_block<kDV>(vh, L, row0, vs, 2 * w, lane);
-    dma_block<kDV>(vh, L, row0, vs, 2 * w + 1, lane);
+    dma_block<kDV>(vh, ldv, L, row0, vs, 2 * w, lane);
+    dma_block<kDV>(vh, ldv, L, row0, vs, 2 * w + 1, lane);
     if constexpr (DQK == 64) {
-        dma_block<64>(kh, L, row0, ks, 2 * w, lane);
-        dma_block<64>(kh, L, row0, ks, 2 * w + 1, lane);
+        dma_block<64>(kh, 64, L, row0, ks, 2 * w, lane);
+        dma_block<64>(kh, 64, L, row0, ks, 2 * w + 1, lane);
         if (with_q) {
-            dma_block<64>(qh, L, row0, qs, 2 * w, lane);
-            dma_block<64>(qh, L, row0, qs, 2 * w + 1, lane);
+            dma_block<64>(qh, 64, L, row0, qs, 2 * w, lane);
+            dma_block<64>(qh, 64, L, row0, qs, 2 * w + 1, lane);
         }
     } else {
-        if (w < 2) dma_block<16>(kh, L, row0, ks, w, lane);
-        else if (with_q) dma_block<16>(qh, L, row0, qs, w - 2, lane);
+        if (w < 2) dma_block<16>(kh, 16, L, row0, ks, w, lane);
+        else if (with_q) dma_block<16>(qh, 16, L, row0, qs, w - 2, lane);
     }
 }
 
@@ -300,20 +304,21 @@ __device__ __forceinline__ void swa_tile(const SwaSlots<HALO>& sl, int t, int wi
 // which memory operations have completed.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
-// Byte offset of (query row, column) in a head's [L][64] fp32 array.
-__device__ __forceinline__ int out_off(int row, int col) { return (row * kDV + col) * 4; }
+// Byte offset of (query row, column) in a head's [L][ldv] fp32 array
+// (relative to the workgroup's first column).
+__device__ __forceinline__ int out_off(int row, int col, int ldv) { return (row * ldv + col) * 4; }
 constexpr int kNT = 2;  // buffer access: streaming (nontemporal)
 
 // Fused-add input of one tile for this lane: rows q0 + 4g + m, columns
 // 16ct + r.  Buffer loads: rows past the end read as 0 (range-checked by
 // the resource), so the access needs no branch.
-__device__ __forceinline__ void load_add(__amdgpu_buffer_rsrc_t ra, int q0, int g, int r, float (&a)[16]) {
+__device__ __forceinline__ void load_add(__amdgpu_buffer_rsrc_t ra, int q0, int g, int r, int ldv, float (&a)[16]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
-            a[4 * m + ct] =
-                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, out_off(q0 + 4 * g + m, 16 * ct + r), 0, kNT));
+            a[4 * m + ct] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(ra, out_off(q0 + 4 * g + m, 16 * ct + r, ldv), 0, kNT));
 }
 
 // Barrier without the compiler's release/acquire fences (which would wait
@@ -327,7 +332,7 @@ __device__ __forceinline__ void raw_barrier() {
 template <int DQK, bool ADD, int HALO>
 __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ v, int L, int ntiles,
+                                                       const uint16_t* __restrict__ v, int L, int ldv, int ntiles,
                                                        int tiles_per_wg, int wg_per_head, int window, float scale,
                                                        const float* add, float* y) {
     // K/V ring of HALO + 2 slots: tile tb - HALO + j lives in slot j mod
@@ -342,8 +347,17 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
     uint16_t* const vs[4] = {v0, v1, v2, v3};
     uint16_t* const qs[2] = {q0s, q1s};
 
-    const int head = blockIdx.x / wg_per_head;
-    const int tb = (blockIdx.x % wg_per_head) * tiles_per_wg;
+    // Workgroup -> (head, run, 64-column slice), slice fastest.  The 8 XCDs
+    // take workgroups round-robin; the remap gives each XCD a contiguous
+    // range, so the slices of a run (same Q, K) share an L2.
+    int bid = blockIdx.x;
+    const int total = gridDim.x;
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int ncs = ldv / kDV;  // 64-column slices per head
+    const int col0 = (bid % ncs) * kDV;
+    bid /= ncs;
+    const int head = bid / wg_per_head;
+    const int tb = (bid % wg_per_head) * tiles_per_wg;
     const int te = min(tb + tiles_per_wg, ntiles);
     // The wave index is uniform across the wave: held in a scalar register,
     // the slot choices below are scalar branches, not per-lane selects.
@@ -351,15 +365,16 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const uint16_t* qh = q + (size_t)head * L * DQK;
     const uint16_t* kh = k + (size_t)head * L * DQK;
-    const uint16_t* vh = v + (size_t)head * L * kDV;
+    const uint16_t* vh = v + (size_t)head * L * ldv + col0;
     // Outputs (and the fused-add input) through buffer resources covering
-    // exactly this head: rows past L are dropped (stores) or read as 0, so
-    // every step issues the same memory instructions, with no branches.
-    const int head_bytes = L * kDV * 4;
+    // exactly this head from the slice's first column: rows past L are
+    // dropped (stores) or read as 0, so every step issues the same memory
+    // instructions, with no branches.
+    const int head_bytes = (L * ldv - col0) * 4;
     const __amdgpu_buffer_rsrc_t ry =
-        __builtin_amdgcn_make_buffer_rsrc(y + (size_t)head * L * kDV, (short)0, head_bytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(y + (size_t)head * L * ldv + col0, (short)0, head_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        ADD ? (void*)(add + (size_t)head * L * kDV) : (void*)y, (short)0, ADD ? head_bytes : 0, 0x00020000);
+        ADD ? (void*)(add + (size_t)head * L * ldv + col0) : (void*)y, (short)0, ADD ? head_bytes : 0, 0x00020000);
     const float sl2 = scale * kLog2e;
 
     // Prologue: halo tiles tb-HALO .. tb-1 (K, V) into slots 0 .. HALO-1 and
@@ -368,10 +383,11 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
     // means every copy landed.
     float adda[16], addb[16];
 #pragma unroll
-    for (int h = 0; h < HALO; ++h) dma_tile<DQK>(qh, kh, vh, L, tb - HALO + h, ks[h], vs[h], nullptr, false, w, lane);
-    dma_tile<DQK>(qh, kh, vh, L, tb, ks[HALO], vs[HALO], q0s, true, w, lane);
+    for (int h = 0; h < HALO; ++h)
+        dma_tile<DQK>(qh, kh, vh, ldv, L, tb - HALO + h, ks[h], vs[h], nullptr, false, w, lane);
+    dma_tile<DQK>(qh, kh, vh, ldv, L, tb, ks[HALO], vs[HALO], q0s, true, w, lane);
     if (ADD) {
-        load_add(ra, tb * kQT + 16 * w, g, r, adda);
+        load_add(ra, tb * kQT + 16 * w, g, r, ldv, adda);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
     } else {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -395,8 +411,8 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
         sl.vn = vs[(j + HALO + 1) % kNS];
         sl.qn = qs[(j + 1) % 2];
         if (t + 1 < te) {
-            dma_tile<DQK>(qh, kh, vh, L, t + 1, sl.kn, sl.vn, sl.qn, true, w, lane);
-            if (ADD) load_add(ra, (t + 1) * kQT + 16 * w, g, r, next_add);
+            dma_tile<DQK>(qh, kh, vh, ldv, L, t + 1, sl.kn, sl.vn, sl.qn, true, w, lane);
+            if (ADD) load_add(ra, (t + 1) * kQT + 16 * w, g, r, ldv, next_add);
         }
         f32x4 yacc[4];
         float l;
@@ -408,8 +424,8 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 const float o = yacc[ct][m] * inv + (ADD ? cur_add[4 * m + ct] : 0.f);
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), ry, out_off(q0 + 4 * g + m, 16 * ct + r), 0,
-                                                      kNT);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), ry,
+                                                      out_off(q0 + 4 * g + m, 16 * ct + r, ldv), 0, kNT);
             }
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(ADD ? 32 : 16));
@@ -445,37 +461,218 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
     }
 }
 
+// ---- windows over 128 keys (up to the whole causal prefix).  One workgroup
+// per (head, 64-query tile, 64-column slice) walks the key tiles that meet
+// any of its queries' windows, oldest first, with an online softmax: per
+// key tile the running row maximum m is raised to cover the tile's scores,
+// the probabilities are taken against it, and the partial sums of earlier
+// tiles are scaled down by 2^(m_old - m_new).  K/V tiles alternate between
+// two LDS slots; tile kt+1 is copied in (LDS-DMA) while tile kt is used.
+// Same operand layouts as the run kernel above: S^T = K Q^T per 16-key
+// sub-tile (lane: one query, 4 keys), P as a hi/lo bf16 pair, V through
+// transposed LDS reads.
+template <int DQK>
+struct LongSlot {
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* kn;
+    uint16_t* vn;
+};
+
+template <int DQK>
+__device__ __forceinline__ void dma_kv(const uint16_t* kh, const uint16_t* vh, int ldv, int L, int t, uint16_t* ks,
+                                       uint16_t* vs, int w, int lane) {
+    const int row0 = t * kQT;
+    dma_block<kDV>(vh, ldv, L, row0, vs, 2 * w, lane);
+    dma_block<kDV>(vh, ldv, L, row0, vs, 2 * w + 1, lane);
+    if constexpr (DQK == 64) {
+        dma_block<64>(kh, 64, L, row0, ks, 2 * w, lane);
+        dma_block<64>(kh, 64, L, row0, ks, 2 * w + 1, lane);
+    } else {
+        if (w < 2) dma_block<16>(kh, 16, L, row0, ks, w, lane);
+    }
+}
+
+// Online-softmax update of this wave's 16 queries with key tile kt (keys
+// 64kt .. 64kt+63 in slots ks, vs).  m: running maximum (log2 units) of this
+// lane's query r; lp: this lane's partial sum of probabilities.
+template <int DQK>
+__device__ __forceinline__ void long_tile(const uint16_t* ks, const uint16_t* vs, const uint16_t* qs, int kt, int qi,
+                                          int window, float sl2, int w, int g, int r, float& m, float& lp,
+                                          f32x4 (&yacc)[4]) {
+    float s[4][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 st = score_tile<DQK>(ks, 16 * j, qs, 16 * w, g, r);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+            const int key = kt * kQT + 16 * j + 4 * g + mm;
+            const bool ok = key <= qi && key > qi - window;
+            s[j][mm] = ok ? st[mm] * sl2 : -INFINITY;
+            mt = fmaxf(mt, s[j][mm]);
+        }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(m, mt);
+    // no key of this query seen yet: keep every weight at 0 without NaN
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float corr = __builtin_amdgcn_exp2f(m - mu);  // m = -inf: 0
+    m = mn;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+            s[j][mm] = __builtin_amdgcn_exp2f(s[j][mm] - mu);
+            acc += s[j][mm];
+        }
+    lp = lp * corr + acc;
+    // rows of yacc are the queries 4g + mm: their scale factors
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+        const float c = __shfl(corr, 4 * g + mm, 64);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) yacc[ct][mm] *= c;
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        float a[8];
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+            a[mm] = s[2 * p][mm];
+            a[4 + mm] = s[2 * p + 1][mm];
+        }
+        bf16x8 ahi, alo;
+        pack8_hilo(a, ahi, alo);
+        bf16x8 vb[4];
+        v_kstep<true>(vs, 32 * p + 4 * g, vs, 32 * p + 16 + 4 * g, r, vb);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) yacc[ct] = mfma32(ahi, vb[ct], yacc[ct]);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) yacc[ct] = mfma32(alo, vb[ct], yacc[ct]);
+    }
+}
+
+template <int DQK, bool ADD>
+__global__ __launch_bounds__(256) void swa_long_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v, int L, int ldv, int ntiles,
+                                                       int window, float scale, const float* add, float* y) {
+    __shared__ alignas(16) uint16_t k0[kQT * DQK], k1[kQT * DQK];
+    __shared__ alignas(16) uint16_t v0[kQT * kDV], v1[kQT * kDV];
+    __shared__ alignas(16) uint16_t qs[kQT * DQK];
+
+    int bid = blockIdx.x;
+    const int total = gridDim.x;
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int ncs = ldv / kDV;
+    const int col0 = (bid % ncs) * kDV;
+    bid /= ncs;
+    const int head = bid / ntiles;
+    const int qt = ntiles - 1 - bid % ntiles;  // the longest key ranges first
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const uint16_t* qh = q + (size_t)head * L * DQK;
+    const uint16_t* kh = k + (size_t)head * L * DQK;
+    const uint16_t* vh = v + (size_t)head * L * ldv + col0;
+    const int head_bytes = (L * ldv - col0) * 4;
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(y + (size_t)head * L * ldv + col0, (short)0, head_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        ADD ? (void*)(add + (size_t)head * L * ldv + col0) : (void*)y, (short)0, ADD ? head_bytes : 0, 0x00020000);
+    const float sl2 = scale * kLog2e;
+    const int q0 = qt * kQT + 16 * w;  // first query of the wave
+    const int qi = q0 + r;             // this lane's query
+    const int kt_lo = max(0, qt * kQT - window + 1) / kQT;
+
+    // prologue: Q of the tile, K/V of the first key tile into slot 0
+    if constexpr (DQK == 64) {
+        dma_block<64>(qh, 64, L, qt * kQT, qs, 2 * w, lane);
+        dma_block<64>(qh, 64, L, qt * kQT, qs, 2 * w + 1, lane);
+    } else {
+        if (w >= 2) dma_block<16>(qh, 16, L, qt * kQT, qs, w - 2, lane);
+    }
+    dma_kv<DQK>(kh, vh, ldv, L, kt_lo, k0, v0, w, lane);
+    float adda[16];
+    if (ADD) load_add(ra, q0, g, r, ldv, adda);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    raw_barrier();
+
+    f32x4 yacc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) yacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lp = 0.f;
+    // Key tiles in pairs, so that each slot is a fixed array in each half.
+    for (int kt = kt_lo; kt <= qt; kt += 2) {
+        if (kt + 1 <= qt) dma_kv<DQK>(kh, vh, ldv, L, kt + 1, k1, v1, w, lane);
+        long_tile<DQK>(k0, v0, qs, kt, qi, window, sl2, w, g, r, m, lp, yacc);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        raw_barrier();
+        if (kt + 1 > qt) break;
+        if (kt + 2 <= qt) dma_kv<DQK>(kh, vh, ldv, L, kt + 2, k0, v0, w, lane);
+        long_tile<DQK>(k1, v1, qs, kt + 1, qi, window, sl2, w, g, r, m, lp, yacc);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        raw_barrier();
+    }
+    float l = lp;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+        const float inv = __builtin_amdgcn_rcpf(__shfl(l, 4 * g + mm, 64));  // l >= 1: the max key has p = 1
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const float o = yacc[ct][mm] * inv + (ADD ? adda[4 * mm + ct] : 0.f);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), ry,
+                                                  out_off(q0 + 4 * g + mm, 16 * ct + r, ldv), 0, kNT);
+        }
+    }
+}
+
 template <int DQK, bool ADD>
 void launch_halo(int halo, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const uint16_t* v, int L,
-                 int ntiles, int tpw, int wg_per_head, int window, float scale, const float* add, float* y) {
+                 int ldv, int ntiles, int tpw, int wg_per_head, int window, float scale, const float* add, float* y) {
     if (halo == 1)
-        hipLaunchKernelGGL((swa_mfma_kernel<DQK, ADD, 1>), grid, dim3(256), 0, st, q, k, v, L, ntiles, tpw,
+        hipLaunchKernelGGL((swa_mfma_kernel<DQK, ADD, 1>), grid, dim3(256), 0, st, q, k, v, L, ldv, ntiles, tpw,
                            wg_per_head, window, scale, add, y);
     else
-        hipLaunchKernelGGL((swa_mfma_kernel<DQK, ADD, 2>), grid, dim3(256), 0, st, q, k, v, L, ntiles, tpw,
+        hipLaunchKernelGGL((swa_mfma_kernel<DQK, ADD, 2>), grid, dim3(256), 0, st, q, k, v, L, ldv, ntiles, tpw,
                            wg_per_head, window, scale, add, y);
 }
 
 }  // namespace
 
-hipError_t launch_swa_mfma(const void* q, const void* k, const void* v, int BH, int L, int dqk, int window,
+hipError_t launch_swa_mfma(const void* q, const void* k, const void* v, int BH, int L, int dqk, int dv, int window,
                            float scale, const float* add, float* y, hipStream_t st) {
     const int ntiles = (L + kQT - 1) / kQT;
+    const int ncs = dv / kDV;  // 64-column slices: each recomputes the scores of its tiles
     // Tiles per workgroup: long runs amortise the halo and the pipeline
     // fill; keep about two workgroups per compute unit.
-    const int tpw = max(1, min(16, (BH * ntiles + 511) / 512));
+    const int tpw = max(1, min(16, (BH * ncs * ntiles + 511) / 512));
     const int wg_per_head = (ntiles + tpw - 1) / tpw;
-    const dim3 grid(BH * wg_per_head);
+    const dim3 grid(BH * wg_per_head * ncs);
     const int halo = window > kQT ? 2 : 1;  // key tiles of 64 before the query tile
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     const uint16_t* vv = static_cast<const uint16_t*>(v);
+    if (window > 2 * kQT) {
+        const dim3 lgrid(BH * ntiles * ncs);
+        if (dqk == 16) {
+            if (add) hipLaunchKernelGGL((swa_long_kernel<16, true>), lgrid, dim3(256), 0, st, qq, kk, vv, L, dv, ntiles, window, scale, add, y);
+            else hipLaunchKernelGGL((swa_long_kernel<16, false>), lgrid, dim3(256), 0, st, qq, kk, vv, L, dv, ntiles, window, scale, add, y);
+        } else {
+            if (add) hipLaunchKernelGGL((swa_long_kernel<64, true>), lgrid, dim3(256), 0, st, qq, kk, vv, L, dv, ntiles, window, scale, add, y);
+            else hipLaunchKernelGGL((swa_long_kernel<64, false>), lgrid, dim3(256), 0, st, qq, kk, vv, L, dv, ntiles, window, scale, add, y);
+        }
+        return hipGetLastError();
+    }
     if (dqk == 16) {
-        if (add) launch_halo<16, true>(halo, grid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
-        else launch_halo<16, false>(halo, grid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
+        if (add) launch_halo<16, true>(halo, grid, st, qq, kk, vv, L, dv, ntiles, tpw, wg_per_head, window, scale, add, y);
+        else launch_halo<16, false>(halo, grid, st, qq, kk, vv, L, dv, ntiles, tpw, wg_per_head, window, scale, add, y);
     } else {
-        if (add) launch_halo<64, true>(halo, grid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
-        else launch_halo<64, false>(halo, grid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
+        if (add) launch_halo<64, true>(halo, grid, st, qq, kk, vv, L, dv, ntiles, tpw, wg_per_head, window, scale, add, y);
+        else launch_halo<64, false>(halo, grid, st, qq, kk, vv, L, dv, ntiles, tpw, wg_per_head, window, scale, add, y);
     }
     return hipGetLastError();
 }

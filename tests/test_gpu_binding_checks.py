@@ -38,8 +38,9 @@ def test_prefill_output_shapes(based):
         based.based_prefill(q, k, v, z=_f32(B, H * F))
     with pytest.raises(ValueError, match="initial_state must have shapes"):
         based.based_prefill(q, k, v, initial_state=(_f32(F, DV), _f32(B, H, F)))
+    # (this shape's launch plan uses no workspace at all)
     with pytest.raises(ValueError, match="workspace must be on"):
-        based.based_prefill(q, k, v, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+        based.based_prefill(q, k, v, workspace=torch.zeros(16, dtype=torch.uint8))
     with pytest.raises(ValueError, match="v must be on"):
         based.based_prefill(q, k, v.cpu())
 
@@ -87,8 +88,13 @@ def test_backward_output_shapes(based):
         based.based_prefill_backward(q, k, v, dy, dq=_f32(B, H, L, 8))
     with pytest.raises(ValueError, match="dv must have shape"):
         based.based_prefill_backward(q, k, v, dy, dv=_f32(B, H, L - 1, DV))
+    # a host workspace must be refused by the binding; it is also too small,
+    # so should that check ever let it through, the library's size check
+    # refuses the call before any launch
     with pytest.raises(ValueError, match="workspace must be on"):
-        based.based_prefill_backward(q, k, v, dy, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+        based.based_prefill_backward(q, k, v, dy, workspace=torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(based.BasedError):
+        based.based_prefill_backward(q, k, v, dy, workspace=torch.zeros(16, dtype=torch.uint8, device=DEV))
 
 
 def test_valid_calls_still_run(based):

@@ -425,6 +425,34 @@ def test_swa_wide_windows(dtype, tol, dqk, window, L):
     report(f"swa {dtype} dqk={dqk} w={window} L={L}", ratio(y, oracle.swa(q, k, v, window, scale)), tol)
 
 
+@pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, 2e-2), (torch.float32, 1e-4)])
+@pytest.mark.parametrize("dqk", [16, 64])
+@pytest.mark.parametrize("dv", [64, 128])
+@pytest.mark.parametrize("window,L", [(1, 70), (64, 200), (129, 300), (256, 700), (700, 700), (10**9, 900),
+                                      (128, 1)])
+def test_swa_any_window_width(dtype, tol, dqk, dv, window, L):
+    """Every window (1, 64, over 128 keys, the whole causal prefix, one far
+    beyond the sequence) at 64 and 128 value columns, with a fused add."""
+    based = based_mod()
+    q, k, v = si.custom((1, 3, L, dqk), (1, 3, L, dv), seed=1950 + window % 1000 + L + dqk + dv, scale=1.0,
+                        dtype=dtype)
+    base = torch.randn(1, 3, L, dv, generator=torch.Generator().manual_seed(1951))
+    scale = dqk ** -0.5
+    y = based.swa_forward(*dev(q, k, v), window=window, scale=scale, add=base.to(DEV))
+    want = oracle.swa(q, k, v, window, scale) + base.double().numpy()
+    report(f"swa {dtype} dqk={dqk} dv={dv} w={window} L={L}", ratio(y, want), tol)
+
+
+def test_swa_full_causal_many_heads():
+    """w >= L (plain causal softmax attention) over B*H = 48 heads, d_v =
+    128: many workgroups, the longest key ranges scheduled first; every
+    element against the oracle."""
+    based = based_mod()
+    q, k, v = si.custom((4, 12, 1500, 64), (4, 12, 1500, 128), seed=1960, scale=1.0)
+    y = based.swa_forward(*dev(q, k, v), window=1500, scale=0.125)
+    report("swa full causal 48 heads dv=128", ratio(y, oracle.swa(q, k, v, 1500, 0.125)), 2e-2)
+
+
 # ---------------------------------------------------------------- backward
 @pytest.mark.parametrize("dtype,tol,B,H,L,d,dv", [
     (torch.bfloat16, 2e-2, 1, 2, 130, 16, 64), (torch.float32, 1e-4, 1, 2, 130, 16, 64),
@@ -690,6 +718,47 @@ def test_hybrid_composed_paths(dtype, tol, dqk, window):
     report(f"hybrid composed {dtype} dqk={dqk} w={window} y", ratio(y, yo + oracle.swa(qw, kw, v, window, scale)),
            tol)
     report(f"hybrid composed {dtype} dqk={dqk} w={window} S", ratio(S, So), tol)
+
+
+@pytest.mark.parametrize("path", ["fused", "two_pass"])
+@pytest.mark.parametrize("B,H,L,window", [(1, 2, 130, 64), (2, 3, 1000, 64), (8, 16, 1024, 64), (1, 2, 300, 200)])
+def test_hybrid_dv128(path, B, H, L, window):
+    """Value width 128 (the 1.3B layer's), fused (four 32-column groups, the
+    segment split for few heads) and as two passes; (8, 16, 1024) is the
+    1.3B-shaped layer at a reduced batch.  A window over 64 keys has no
+    fused kernel: "fused" must refuse it."""
+    based = based_mod()
+    q, k, _ = si.custom((B, H, L, 16), (1, 1, 1, 1), seed=2490 + L + B, scale=0.5)
+    v = si.randn((B, H, L, 128), 2493 + L, 1.0, torch.bfloat16)
+    qw, kw, _ = si.custom((B, H, L, 64), (1, 1, 1, 1), seed=2495 + L, scale=1.0)
+    if path == "fused" and window > 64:
+        with pytest.raises(based.BasedError):
+            based.based_hybrid_prefill(*dev(q, k, qw, kw, v), window=window, scale=0.125, path=path)
+        return
+    y, S, z = based.based_hybrid_prefill(*dev(q, k, qw, kw, v), window=window, scale=0.125, path=path)
+    torch.cuda.synchronize()
+    yo, So, zo = oracle.la_recurrent(q, k, v)
+    want = yo + oracle.swa(qw, kw, v, window, 0.125)
+    report(f"hybrid dv=128 {path} B={B} H={H} L={L} w={window} y", ratio(y, want), 2e-2)
+    report(f"hybrid dv=128 {path} B={B} H={H} L={L} w={window} S", ratio(S, So), 2e-2)
+    report(f"hybrid dv=128 {path} B={B} H={H} L={L} w={window} z", ratio(z, zo), 2e-2)
+
+
+def test_hybrid_dv128_initial_state():
+    """d_v = 128, a carried state, fused (through the workspace)."""
+    based = based_mod()
+    L = 400
+    q, k, _ = si.custom((1, 3, L, 16), (1, 1, 1, 1), seed=2497, scale=0.5)
+    v = si.randn((1, 3, L, 128), 2498, 1.0, torch.bfloat16)
+    qw, kw, _ = si.custom((1, 3, L, 64), (1, 1, 1, 1), seed=2499, scale=1.0)
+    qp, kp, vp = si.custom((1, 3, 50, 16), (1, 3, 50, 128), seed=2500, scale=0.5)
+    _, S0, z0 = oracle.la_recurrent(qp, kp, vp, want_y=False)
+    S0, z0 = torch.as_tensor(S0, dtype=torch.float32), torch.as_tensor(z0, dtype=torch.float32)
+    y, S, z = based.based_hybrid_prefill(*dev(q, k, qw, kw, v), initial_state=tuple(dev(S0, z0)), path="fused")
+    yo, So, zo = oracle.la_recurrent(q, k, v, S0=S0, z0=z0)
+    report("hybrid dv=128 init-state y", ratio(y, yo + oracle.swa(qw, kw, v, 64, 0.125)), 2e-2)
+    report("hybrid dv=128 init-state S", ratio(S, So), 2e-2)
+    report("hybrid dv=128 init-state z", ratio(z, zo), 2e-2)
 
 
 def test_workload_window_8k_fused():
