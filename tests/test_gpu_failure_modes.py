@@ -79,11 +79,20 @@ def test_decode_nonfinite_input(based, where):
     torch.cuda.synchronize()
     for b, h in ((0, 0), (0, 2), (1, 0), (1, 1)):
         assert _same(y[b, h], yc[b, h]) and _same(S[b, h], Sc[b, h]) and _same(z[b, h], zc[b, h])
-    assert torch.isnan(y[1, 2]).all()
     if where == "q":
-        assert _same(S[1, 2], Sc[1, 2]) and _same(z[1, 2], zc[1, 2])  # the query is not part of the update
+        # the query enters every column of the readout, not the update
+        assert torch.isnan(y[1, 2]).all()
+        assert _same(S[1, 2], Sc[1, 2]) and _same(z[1, 2], zc[1, 2])
+    elif where == "k":
+        # features with k_3 are NaN: every state column and the normaliser
+        assert torch.isnan(y[1, 2]).all()
+        assert torch.isnan(S[1, 2]).any(dim=0).all() and torch.isnan(z[1, 2]).any()
     else:
-        assert torch.isnan(S[1, 2]).any()
+        # v column 3 reaches state column 3 and output column 3 only
+        keep = [c for c in range(128) if c != 3]
+        assert torch.isnan(y[1, 2, 3]) and _same(y[1, 2, keep], yc[1, 2, keep])
+        assert torch.isnan(S[1, 2, :, 3]).all() and _same(S[1, 2][:, keep], Sc[1, 2][:, keep])
+        assert _same(z[1, 2], zc[1, 2])
 
 
 @pytest.mark.parametrize("window", [64, 300])
