@@ -45,8 +45,10 @@
  * Memory, layout, ownership (all entry points):
  *   - Every pointer argument is a DEVICE pointer (HIP global memory) unless
  *     stated otherwise.  The caller allocates, owns and frees every buffer;
- *     the library never allocates or frees device memory, keeps no pointer
- *     after a call returns and holds no global state.  Calls are reentrant.
+ *     the library never allocates or frees device memory and keeps no
+ *     pointer after a call returns.  Calls are reentrant; the one exception
+ *     is based_prefill_noalloc, whose static scratch buffer (one per GPU) is
+ *     shared by all its calls on that GPU.
  *   - Tensors are dense and row-major: [B, H, L, dim] (prefill, window) or
  *     [B, H, dim] (decode).  Element type of q, k, v is `dtype`; outputs and
  *     state are always fp32.  Pointers must be 16-byte aligned.
@@ -76,7 +78,9 @@ typedef enum {
     BASED_OK = 0,
     BASED_E_INVALID = 1,     /* null/misaligned pointer, non-positive size, overflow */
     BASED_E_UNSUPPORTED = 2, /* d_feat, d_v, d_qk, chunk or dtype not implemented */
-    BASED_E_LAUNCH = 3       /* the HIP runtime rejected a kernel launch */
+    BASED_E_LAUNCH = 3,      /* the HIP runtime rejected a kernel launch */
+    BASED_E_TOO_LARGE = 4    /* needs more scratch than based_prefill_noalloc's
+                                static buffer holds */
 } based_status_t;
 
 typedef enum { BASED_F32 = 0, BASED_BF16 = 1 } based_dtype_t;
@@ -128,6 +132,31 @@ based_status_t based_prefill(const void *q, const void *k, const void *v,
                              int use_initial_state,
                              void *workspace, size_t workspace_bytes,
                              void *stream);
+
+/*
+ * based_prefill_noalloc -- based_prefill for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, semantics and errors as
+ * based_prefill, without the workspace: the segment split (and an initial
+ * state shared by several column groups) uses a static device buffer of
+ * BASED_PREFILL_NOALLOC_SCRATCH_BYTES inside this library instead.  The call
+ * allocates nothing.  Each GPU holds its own buffer from the first call on
+ * it until the process ends; its device address is taken on that first call
+ * (the stream's device).
+ *   - A call whose launch plan needs more scratch than the buffer holds
+ *     returns BASED_E_TOO_LARGE before anything is launched (every call
+ *     without an initial state fits; with one, the need grows with B*H).
+ *   - All calls on one GPU share that GPU's buffer: calls that overlap in
+ *     time on one GPU (other streams, other threads) race, and the caller
+ *     must order them.  Consecutive calls on one stream are safe; no call
+ *     needs the buffer's previous contents.
+ */
+#define BASED_PREFILL_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+based_status_t based_prefill_noalloc(const void *q, const void *k, const void *v,
+                                     based_dtype_t dtype, int B, int H, int L,
+                                     int d_feat, int d_v, int chunk, float eps,
+                                     float *y, float *S, float *z,
+                                     int use_initial_state, void *stream);
 
 /*
  * based_decode_step -- one next-token step for every (batch, head), in

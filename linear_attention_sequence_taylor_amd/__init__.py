@@ -19,7 +19,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["based_prefill", "based_decode_step", "swa_forward", "swa_cache_fill", "swa_decode_step",
+__all__ = ["based_prefill", "based_prefill_noalloc", "based_decode_step", "swa_forward", "swa_cache_fill", "swa_decode_step",
            "based_hybrid_prefill", "based_hybrid_prefill_workspace_bytes",
            "based_prefill_backward", "based_prefill_backward_workspace_bytes",
            "based_num_features", "based_prefill_workspace_bytes", "BasedError", "library_path"]
@@ -142,6 +142,47 @@ def based_prefill(q, k, v, *, chunk: int = 64, eps: float = 1e-6, initial_state=
                                   d_v, chunk, eps, y.data_ptr(), S.data_ptr(), z.data_ptr(), use_init,
                                   ws_ptr, ws_bytes, _stream_ptr(dev))
     _lib.check("based_prefill", st)
+    return y, S, z
+
+
+def based_prefill_noalloc(q, k, v, *, chunk: int = 64, eps: float = 1e-6, initial_state=None, y=None, S=None,
+                          z=None):
+    """based_prefill without a workspace: the library's static per-GPU
+    scratch buffer stands in for it, and the C call allocates nothing (pass
+    y, S, z to keep this function from allocating them).  Calls overlapping
+    in time on one GPU race on that buffer.  Raises BasedError
+    (BASED_E_TOO_LARGE) when the call needs more scratch than the buffer
+    holds."""
+    _check_tensor("q", q, ndim=4)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor("k", k, dt, 4)
+    _check_tensor("v", v, dt, 4)
+    B, H, L, d = q.shape
+    d_v = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != (B, H, L):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    F = 1 + d + d * d
+    dev = q.device
+    _check_device(dev, k=k, v=v)
+    if y is None:
+        y = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev)
+    if S is None:
+        S = torch.empty((B, H, F, d_v), dtype=torch.float32, device=dev)
+    if z is None:
+        z = torch.empty((B, H, F), dtype=torch.float32, device=dev)
+    _check_like("y", y, (B, H, L, d_v), torch.float32, dev)
+    _check_like("S", S, (B, H, F, d_v), torch.float32, dev)
+    _check_like("z", z, (B, H, F), torch.float32, dev)
+    use_init = 0
+    if initial_state is not None:
+        _initial_state(initial_state, S, z)
+        use_init = 1
+    st = _lib.lib().based_prefill_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[dt], B, H, L, d, d_v,
+                                          chunk, eps, y.data_ptr(), S.data_ptr(), z.data_ptr(), use_init,
+                                          _stream_ptr(dev))
+    _lib.check("based_prefill_noalloc", st)
     return y, S, z
 
 

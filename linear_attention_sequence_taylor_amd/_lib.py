@@ -11,7 +11,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbased.so")
 
-BASED_OK, BASED_E_INVALID, BASED_E_UNSUPPORTED, BASED_E_LAUNCH = 0, 1, 2, 3
+BASED_OK, BASED_E_INVALID, BASED_E_UNSUPPORTED, BASED_E_LAUNCH, BASED_E_TOO_LARGE = 0, 1, 2, 3, 4
 BASED_F32, BASED_BF16 = 0, 1
 
 # Every function the header declares, with (restype, argtypes).
@@ -24,6 +24,7 @@ SIGNATURES = {
     "based_status_string": (ctypes.c_char_p, [_I]),
     "based_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "based_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P, _S, _P]),
+    "based_prefill_noalloc": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P]),
     "based_decode_step": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P]),
     "swa_forward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "swa_cache_fill": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),

@@ -67,6 +67,9 @@ BASED_API const char* based_status_string(based_status_t s) {
         case BASED_E_INVALID: return "BASED_E_INVALID: malformed argument (null/misaligned pointer, bad size, overlap)";
         case BASED_E_UNSUPPORTED: return "BASED_E_UNSUPPORTED: shape, dtype or chunk not implemented";
         case BASED_E_LAUNCH: return "BASED_E_LAUNCH: HIP kernel launch failed";
+        case BASED_E_TOO_LARGE:
+            return "BASED_E_TOO_LARGE: the call needs more scratch than the static buffer of based_prefill_noalloc "
+                   "holds (BASED_PREFILL_NOALLOC_SCRATCH_BYTES); use based_prefill with a workspace";
     }
     return "BASED_E_UNKNOWN";
 }

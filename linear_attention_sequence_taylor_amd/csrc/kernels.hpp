@@ -32,6 +32,9 @@ hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, bool
 // splits each head into segments of seg_len tokens (a multiple of 64); the
 // workspace then holds one carried state per segment.
 size_t prefill_mfma_workspace_bytes(int BH, int L, int dv);
+// Workspace bytes the launch plan of this shape uses when one is available
+// (0: the plan needs none), for a call with or without an initial state.
+size_t prefill_mfma_plan_bytes(int BH, int L, int dv, int use_init);
 // Fused hybrid layer (prefill_mfma.hip): y = linear attention (q, k, v) +
 // the w <= 64 window (q2, k2 of dim 64, the same v), bf16, d' = 16; final
 // state into S, z.  *launched is false when no fused plan fits the

@@ -1259,6 +1259,12 @@ size_t prefill_mfma_workspace_bytes(int BH, int L, int dv) {
     return via_ws ? plan_workspace_bytes(pl, BH) : 0;
 }
 
+size_t prefill_mfma_plan_bytes(int BH, int L, int dv, int use_init) {
+    const PrefillPlan pl = plan_prefill(BH, L, dv, use_init != 0, true);
+    const bool via_ws = pl.nseg > 1 || (use_init && pl.ncg > 1);
+    return via_ws ? plan_workspace_bytes(pl, BH) : 0;
+}
+
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int BH, int L, int dv,
                                float eps, float* y, float* S, float* z, int use_init, void* ws,
                                size_t ws_bytes, hipStream_t st) {

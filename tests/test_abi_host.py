@@ -58,8 +58,9 @@ def test_num_features_and_strings(lib):
     assert lib.based_num_features(16) == 273
     assert lib.based_num_features(8) == 73
     assert lib.based_num_features(0) == -1
-    for s in range(4):
+    for s in range(5):
         assert lib.based_status_string(s)
+    assert b"TOO_LARGE" in lib.based_status_string(4)
     assert b"UNKNOWN" in lib.based_status_string(99)
 
 
