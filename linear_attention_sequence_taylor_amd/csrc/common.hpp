@@ -47,6 +47,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16lo_f32(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf16hi_f32(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 
+// The lo half of a hi/lo bf16 split of two floats: given the hi pair
+// hp = pack_bf16x2(x0, x1), the bf16 pair of the remainders x - hi, so that
+// x ~= hi + lo to about 16 mantissa bits.  Each x - hi is one
+// v_dot2_f32_bf16 of the packed pair against (-1, -0) or (-0, -1) plus x:
+// the products are exact and x - hi is representable, so its one rounding
+// changes nothing.  (The selectors keep a -0 in the other half: the pair
+// (-1, +0) has the bit pattern of a small integer that the assembler would
+// emit as an inline float constant.)
+__device__ __forceinline__ uint32_t lo_pair_of(uint32_t hp, float x0, float x1) {
+    const bf16x2 sel0 = __builtin_bit_cast(bf16x2, 0x8000bf80u);
+    const bf16x2 sel1 = __builtin_bit_cast(bf16x2, 0xbf808000u);
+    const bf16x2 hb = __builtin_bit_cast(bf16x2, hp);
+    return pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(hb, sel0, x0, false),
+                       __builtin_amdgcn_fdot2_f32_bf16(hb, sel1, x1, false));
+}
+
 // Sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -150,17 +150,14 @@ __device__ __forceinline__ bf16x8 pack8(const float (&a)[8]) {
 }
 // hi = bf16(a), lo = bf16(a - hi): a ~= hi + lo to ~16 mantissa bits.
 __device__ __forceinline__ void pack8_hilo(const float (&a)[8], bf16x8& hi, bf16x8& lo) {
-    float l[8];
-    u32x4 h;
+    u32x4 h, l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t p = pack_bf16x2(a[2 * i], a[2 * i + 1]);
-        h[i] = p;
-        l[2 * i] = a[2 * i] - bf16lo_f32(p);
-        l[2 * i + 1] = a[2 * i + 1] - bf16hi_f32(p);
+        h[i] = pack_bf16x2(a[2 * i], a[2 * i + 1]);
+        l[i] = lo_pair_of(h[i], a[2 * i], a[2 * i + 1]);
     }
     hi = __builtin_bit_cast(bf16x8, h);
-    lo = pack8(l);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 __device__ __forceinline__ void unpack8(const u32x4& u, float (&x)[8]) {
 #pragma unroll
@@ -270,8 +267,8 @@ __device__ __forceinline__ void publish_last(const f32x4 (&a)[DV / 16 + 1], Pref
         if (ct == kNV && r != 0) continue;
         const uint32_t h01 = pack_bf16x2(a[ct][0], a[ct][1]);
         const uint32_t h23 = pack_bf16x2(a[ct][2], a[ct][3]);
-        const uint32_t l01 = pack_bf16x2(a[ct][0] - bf16lo_f32(h01), a[ct][1] - bf16hi_f32(h01));
-        const uint32_t l23 = pack_bf16x2(a[ct][2] - bf16lo_f32(h23), a[ct][3] - bf16hi_f32(h23));
+        const uint32_t l01 = lo_pair_of(h01, a[ct][0], a[ct][1]);
+        const uint32_t l23 = lo_pair_of(h23, a[ct][2], a[ct][3]);
         uint2* hi = ct < kNV
                         ? reinterpret_cast<uint2*>(&sm.s_hi[sbuf][(16 * ct + r) * kSRow + 8 * unit_swz(16 + g, r) + 4 * H])
                         : reinterpret_cast<uint2*>(&sm.z_hi[sbuf][8 * (16 + g) + 4 * H]);
@@ -512,8 +509,12 @@ struct StagePipe {
 };
 
 // ---- on-diagonal term of query tile DQ (rows 16DQ..16DQ+15) of one chunk:
-// s^T for key tiles 0..DQ, causal weights 1 + s + s^2/2 (hi/lo bf16 pair)
-// times V and the ones column, in MFMA accumulator layout.
+// for key tiles 0..DQ, t = 4 + q.k (raw q, k: the MFMA accumulator starts
+// at 4), so that t^2 + 16 = 16(1 + s)^2 + 16 = 32(1 + s + s^2/2) with
+// s = q.k/4: one FMA per causal weight, which enters (as a hi/lo bf16 pair)
+// times V and the ones column, in MFMA accumulator layout.  The sums are
+// 32 times the method's on-diagonal numerator and denominator; the
+// off-diagonal part is scaled to match when the two are combined.
 template <int DQ, int DV>
 __device__ __forceinline__ void diag_block(const PrefillSmem<DV>& sm, int buf, int lane, int g, int r,
                                           f32x4 (&y)[DV / 16 + 1]) {
@@ -529,11 +530,11 @@ __device__ __forceinline__ void diag_block(const PrefillSmem<DV>& sm, int buf, i
 #pragma unroll
     for (int j = 0; j <= DQ; ++j) {
         const bf16x4 ka = lds_bf16x4(k_l + qk_idx(16 * j + r, 4 * g));
-        const f32x4 s = mfma16(ka, qb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 t = mfma16(ka, qb, f32x4{4.f, 4.f, 4.f, 4.f});
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            // s[m] = q_query . k_key (raw), key = 16j + 4g + m, query = 16DQ + r
-            const float w = fmaf(s[m], fmaf(s[m], 1.f / 32.f, 0.25f), 1.f);
+            // t[m] = 4 + q_query . k_key (raw), key = 16j + 4g + m, query = 16DQ + r
+            const float w = fmaf(t[m], t[m], 16.f);
             wgt[j][m] = (j == DQ && 4 * g + m > r) ? 0.f : w;
         }
     }
@@ -825,12 +826,19 @@ __device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps,
         return;
     }
     // Chunk c's rows: add the off-diagonal part, normalise, store.  nrows
-    // is the number of valid rows of the chunk (64 except at the end).
+    // is the number of valid rows of the chunk (64 except at the end).  The
+    // on-diagonal sums yd are 32 times the method's (see diag_block): the
+    // off-diagonal part is scaled by 32 and so is eps (exact powers of two).
+    const float eps32 = 32.f * eps;
     auto finish = [&](int c, const f32x4 (&yd)[kNCT], int nrows) {
         const f32x4* src = reinterpret_cast<const f32x4*>(&sm.hand[c & 1][DQ][0]);
         f32x4 y[kNCT];
 #pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct) y[ct] = src[ct * 64 + lane] + yd[ct];
+        for (int ct = 0; ct < kNCT; ++ct) {
+            const f32x4 x = src[ct * 64 + lane];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) y[ct][m] = fmaf(x[m], 32.f, yd[ct][m]);
+        }
         float* ybase = yh + (size_t)c * kC * ldv;
         if constexpr (HYB) {
             // fused layer: plus the window output of the same rows
@@ -838,7 +846,7 @@ __device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps,
             const f32x4* hw = reinterpret_cast<const f32x4*>(&wsm.hand[c & 1][DQ][0]);
             float inv[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) inv[m] = __builtin_amdgcn_rcpf(y[kNV][m] + eps);
+            for (int m = 0; m < 4; ++m) inv[m] = __builtin_amdgcn_rcpf(y[kNV][m] + eps32);
 #pragma unroll
             for (int ct = 0; ct < kNV; ++ct) {
                 const f32x4 yw = hw[ct * 64 + lane];
@@ -854,7 +862,7 @@ __device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps,
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int tq = 16 * DQ + 4 * g + m;
-            const float inv = __builtin_amdgcn_rcpf(y[kNV][m] + eps);
+            const float inv = __builtin_amdgcn_rcpf(y[kNV][m] + eps32);
             if (tq < nrows) {
 #pragma unroll
                 for (int ct = 0; ct < kNV; ++ct)
@@ -862,16 +870,21 @@ __device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps,
             }
         }
     };
-    f32x4 ydprev[kNCT];
-    for (int c = 0; c < nchunks; ++c) {
-        f32x4 yd[kNCT];
-        diag_block<DQ, DV>(sm, c & 1, lane, g, r, yd);
-        if (c > 0) finish(c - 1, ydprev, kC);
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct) ydprev[ct] = yd[ct];
+    // Two chunks per iteration with two accumulator sets, so that no
+    // register copy carries a chunk's term to the next interval.
+    f32x4 ya[kNCT], yb[kNCT];
+    for (int c = 0; c < nchunks; c += 2) {
+        diag_block<DQ, DV>(sm, 0, lane, g, r, ya);  // chunk c (even: buffer 0)
+        if (c > 0) finish(c - 1, yb, kC);
         __syncthreads();
+        if (c + 1 < nchunks) {
+            diag_block<DQ, DV>(sm, 1, lane, g, r, yb);
+            finish(c, ya, kC);
+            __syncthreads();
+        }
     }
-    finish(nchunks - 1, ydprev, L - (nchunks - 1) * kC);
+    if (nchunks & 1) finish(nchunks - 1, ya, L - (nchunks - 1) * kC);
+    else finish(nchunks - 1, yb, L - (nchunks - 1) * kC);
 }
 
 // ---- update wave U: state rotation tiles U, U+4 (, U+8).
@@ -1156,8 +1169,300 @@ __global__ __launch_bounds__(HYB ? 1024 : 768, 1) void prefill_mfma_kernel(
     }
 }
 
+// ---- state pass of the segment split.  A segment's state increment is a
+// plain sum over its tokens, sum_t psi(k_t) [v_t | 1]^T, with no order to
+// respect between chunks, so it needs none of the prefill's roles.  Ten
+// waves: wave w owns the rotation tiles 2p, 2p + 1 (p = w mod 5; all their
+// column tiles) over the k-step h = w / 5 of every chunk (tokens 32h ..
+// 32h + 31), and the two waves of a tile pair add their sums at the end.
+// The chunks come from a ring of LDS slots filled by asynchronous global ->
+// LDS copies several chunks ahead (the pass is bound by reading K and V;
+// the prefill's two-chunk register prefetch left it waiting on memory).
+// Operands come straight from the row-major copies through transposed LDS
+// reads (ds_read_b64_tr_b16): K^T gives each lane its feature dim for 8
+// tokens (the DPP products of psi_k), V^T the B operand.  The contraction
+// index k = 8g + i of lane group g stands for token 4g + i (i < 4) or
+// 16 + 4g + (i - 4) of the k-step, so that the 32 lanes a read serves at
+// once cover 8 consecutive rows: no bank conflicts with the row swizzle of
+// the V slots.  K is used raw, so quadratic rows come out 16 times and
+// linear rows 4 times the readout units; the scale is applied once before
+// the store.  Segments handled here are whole (a multiple of 64 tokens,
+// inside the sequence): only the last segment can be ragged, and it needs
+// no state pass.
+constexpr int kStateWaves = 10;
+
+template <int DV>
+struct StateRingT {
+    static constexpr int kRing = DV == 64 ? 7 : 12;  // 70 KB / 72 KB: two workgroups per CU
+    alignas(16) uint16_t k[kRing][kC * kDFeat];      // [64][16] row-major
+    alignas(16) uint16_t v[kRing][kC * DV];           // [64][DV], 16-byte units XOR-swizzled by row
+};
+
+#define BASED_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Element offset of (row, col) in a [64][DV] V slot.  DV = 64: 8 units per
+// row, swizzled by row & 7; DV = 32: 4 units, rows r and r + 4 (which share
+// banks) get the unit pairs {0,1} and {2,3} swapped.
+template <int DV>
+__device__ __forceinline__ int sv_idx(int row, int col) {
+    const int sw = DV == 64 ? (row & 7) : (((row >> 2) & 1) << 1);
+    return row * DV + 8 * ((col >> 3) ^ sw) + (col & 7);
+}
+
+// Copy of 1 KB block b of chunk t (64 tokens from t0) into its ring slot:
+// blocks 0, 1 are K (32 rows each), blocks 2.. are V (64 / (DV/8) rows
+// each).  The DMA writes lane l's 16 bytes at byte 16 l of the block, so a
+// lane fetches the source unit the swizzle stores there.
+template <int DV>
+__device__ __forceinline__ void state_dma(const uint16_t* kh, const uint16_t* vh, int ldv, int t0,
+                                          StateRingT<DV>& rg, int slot, int b, int lane) {
+    if (b < 2) {
+        const int row = 32 * b + (lane >> 1);
+        __builtin_amdgcn_global_load_lds(kh + (size_t)(t0 + row) * kDFeat + 8 * (lane & 1),
+                                         BASED_LDS_PTR(void, &rg.k[slot][512 * b]), 16, 0, 0);
+    } else {
+        constexpr int kUnits = DV / 8, kRows = 64 / kUnits;
+        const int vb = b - 2;
+        const int row = kRows * vb + lane / kUnits;
+        const int pu = lane % kUnits;  // the unit this lane's 16 bytes land in
+        const int gu = (sv_idx<DV>(row, 8 * pu) - row * DV) >> 3;  // the swizzle is an involution
+        __builtin_amdgcn_global_load_lds(vh + (size_t)(t0 + row) * ldv + 8 * gu,
+                                         BASED_LDS_PTR(void, &rg.v[slot][512 * vb]), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)BASED_LDS_PTR(const void, p);
+}
+
+// One k-step (32 tokens from row tb) of the slot: this lane's 8 K values
+// (feature dim r of its group's tokens, see above) and the B operand of each
+// value column tile (the same tokens, column 16ct + r).  One asm block with
+// its own wait: the compiler cannot tell these reads from the copies in
+// flight into other slots and would otherwise wait for all of them.
+template <int DV>
+__device__ __forceinline__ void state_reads(const StateRingT<DV>& rg, int slot, int tb, int g, int r, uint2 (&kk)[2],
+                                            bf16x8 (&vb)[DV / 16]) {
+    const int row0 = tb + 4 * g + (r >> 2), row1 = row0 + 16, col = 4 * (r & 3);
+    const uint32_t k0 = lds_addr(&rg.k[slot][row0 * kDFeat + col]);
+    const uint32_t k1 = lds_addr(&rg.k[slot][row1 * kDFeat + col]);
+    uint32_t va[DV / 16][2];
+#pragma unroll
+    for (int ct = 0; ct < DV / 16; ++ct) {
+        va[ct][0] = lds_addr(&rg.v[slot][sv_idx<DV>(row0, 16 * ct + col)]);
+        va[ct][1] = lds_addr(&rg.v[slot][sv_idx<DV>(row1, 16 * ct + col)]);
+    }
+    uint2 x[DV / 8];
+    if constexpr (DV == 64) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %10\n\t"
+            "ds_read_b64_tr_b16 %1, %11\n\t"
+            "ds_read_b64_tr_b16 %2, %12\n\t"
+            "ds_read_b64_tr_b16 %3, %13\n\t"
+            "ds_read_b64_tr_b16 %4, %14\n\t"
+            "ds_read_b64_tr_b16 %5, %15\n\t"
+            "ds_read_b64_tr_b16 %6, %16\n\t"
+            "ds_read_b64_tr_b16 %7, %17\n\t"
+            "ds_read_b64_tr_b16 %8, %18\n\t"
+            "ds_read_b64_tr_b16 %9, %19\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]),
+              "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+            : "v"(k0), "v"(k1), "v"(va[0][0]), "v"(va[0][1]), "v"(va[1][0]), "v"(va[1][1]), "v"(va[2][0]),
+              "v"(va[2][1]), "v"(va[3][0]), "v"(va[3][1])
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %6\n\t"
+            "ds_read_b64_tr_b16 %1, %7\n\t"
+            "ds_read_b64_tr_b16 %2, %8\n\t"
+            "ds_read_b64_tr_b16 %3, %9\n\t"
+            "ds_read_b64_tr_b16 %4, %10\n\t"
+            "ds_read_b64_tr_b16 %5, %11\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+            : "v"(k0), "v"(k1), "v"(va[0][0]), "v"(va[0][1]), "v"(va[1][0]), "v"(va[1][1])
+            : "memory");
+    }
+#pragma unroll
+    for (int ct = 0; ct < DV / 16; ++ct)
+        vb[ct] = __builtin_bit_cast(bf16x8, u32x4{x[2 * ct].x, x[2 * ct].y, x[2 * ct + 1].x, x[2 * ct + 1].y});
+}
+
+// s_waitcnt with vmcnt = n (0..15) and the other counters left alone.
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+#define BASED_WVM(N) \
+    case N: __builtin_amdgcn_s_waitcnt((N) | 0x70 | 0xF00); break;
+        BASED_WVM(0) BASED_WVM(1) BASED_WVM(2) BASED_WVM(3) BASED_WVM(4) BASED_WVM(5) BASED_WVM(6) BASED_WVM(7)
+        BASED_WVM(8) BASED_WVM(9) BASED_WVM(10)
+#undef BASED_WVM
+        default: __builtin_amdgcn_s_waitcnt(11 | 0x70 | 0xF00); break;
+    }
+}
+
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Readout units of rotation tile T from the raw-k sums: quadratic rows
+// 1/16, linear rows (tile 9) 1/4, the constant (tile 8, row 8) 1.
+template <int T>
+__device__ __forceinline__ float raw_scale(int row) {
+    if (T == 9) return 0.25f;
+    if (T == 8 && row == 8) return 1.f;
+    return 1.f / 16.f;
+}
+
+// Tiles T0 = 2P, 2P + 1 over k-step H of every chunk; the H = 1 wave hands
+// its sums to the H = 0 wave, which writes the slot.
+template <int P, int H, int DV>
+__device__ __forceinline__ void state_pair(const uint16_t* kh, const uint16_t* vh, int ldv, int nch,
+                                           StateRingT<DV>& rg, float* ws_out) {
+    constexpr int kNV = DV / 16, kNCT = kNV + 1, kRing = StateRingT<DV>::kRing;
+    constexpr int T0 = 2 * P, T1 = 2 * P + 1;
+    constexpr int kBlocks = 2 + DV / 8;  // 1 KB copies per chunk
+    const int w = P + 5 * H;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const bf16x8 ones = ones8();
+    f32x4 a0[kNCT], a1[kNCT];
+#pragma unroll
+    for (int ct = 0; ct < kNCT; ++ct) a0[ct] = a1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t8[i] = r == 8 ? 1.f : 0.f;
+    const bool copies = w < kBlocks;
+    const int first = min(kRing - 1, nch);
+    for (int c = 0; c < first; ++c)
+        if (copies) state_dma<DV>(kh, vh, ldv, c * kC, rg, c, w, lane);
+    for (int c = 0; c < nch; ++c) {
+        // this wave's copy of chunk c has landed once at most the copies of
+        // the chunks after it are outstanding; the barrier makes every
+        // wave's copy visible and frees the slot of chunk c - 1
+        if (copies) wait_vm(min(kRing - 2, nch - 1 - c));
+        raw_barrier();
+        if (copies && c + kRing - 1 < nch)
+            state_dma<DV>(kh, vh, ldv, (c + kRing - 1) * kC, rg, (c + kRing - 1) % kRing, w, lane);
+        uint2 kk[2];
+        bf16x8 vb[kNV];
+        state_reads<DV>(rg, c % kRing, 32 * H, g, r, kk, vb);
+        float kv[8];
+        kv[0] = bf16lo_f32(kk[0].x);
+        kv[1] = bf16hi_f32(kk[0].x);
+        kv[2] = bf16lo_f32(kk[0].y);
+        kv[3] = bf16hi_f32(kk[0].y);
+        kv[4] = bf16lo_f32(kk[1].x);
+        kv[5] = bf16hi_f32(kk[1].x);
+        kv[6] = bf16lo_f32(kk[1].y);
+        kv[7] = bf16hi_f32(kk[1].y);
+        const bf16x8 f0 = psi_k<T0>(kv, t8);
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) a0[ct] = mfma32(f0, vb[ct], a0[ct]);
+        a0[kNV] = mfma32(f0, ones, a0[kNV]);
+        const bf16x8 f1 = psi_k<T1>(kv, t8);
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) a1[ct] = mfma32(f1, vb[ct], a1[ct]);
+        a1[kNV] = mfma32(f1, ones, a1[kNV]);
+    }
+    // the H = 1 waves' sums through LDS (the ring is free after the barrier)
+    raw_barrier();
+    f32x4* xch = reinterpret_cast<f32x4*>(&rg.k[0][0]) + (size_t)P * 2 * kNCT * 64;
+    if (H == 1) {
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct) {
+            xch[ct * 64 + lane] = a0[ct];
+            xch[(kNCT + ct) * 64 + lane] = a1[ct];
+        }
+    }
+    __syncthreads();
+    if (H == 0) {
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct) {
+            a0[ct] += xch[ct * 64 + lane];
+            a1[ct] += xch[(kNCT + ct) * 64 + lane];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                a0[ct][m] *= raw_scale<T0>(4 * g + m);
+                a1[ct][m] *= raw_scale<T1>(4 * g + m);
+            }
+        }
+        ws_store<T0, DV>(a0, ws_out, lane);
+        ws_store<T1, DV>(a1, ws_out, lane);
+    }
+}
+
+template <int T, int DV>
+__device__ __forceinline__ void init_tile(const float* Sh, const float* zh, int ldv, int use_init, float* ws_out) {
+    constexpr int kNCT = DV / 16 + 1;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    f32x4 acc[kNCT];
+#pragma unroll
+    for (int ct = 0; ct < kNCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (use_init) load_initial<T, DV>(acc, Sh, zh, ldv, g, r);
+    ws_store<T, DV>(acc, ws_out, lane);
+}
+
+// Workgroup (head, segment s, column group), mapped as the prefill's: for
+// s < nseg - 1 the increment of segment s into slot s + 1; for s = nseg - 1
+// the caller's initial state (or zeros) into slot 0.
+template <int DV>
+__global__ __launch_bounds__(64 * kStateWaves, 2) void segment_state_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int L, int ldv, int ncg, int seg_len, int nseg,
+    const float* __restrict__ S, const float* __restrict__ z, int use_init, float* __restrict__ ws) {
+    static_assert(sizeof(StateRingT<DV>) >= 5 * 2 * (DV / 16 + 1) * 64 * 16, "exchange area");
+    __shared__ StateRingT<DV> rg;
+    const int total = gridDim.x;
+    int b = blockIdx.x;
+    if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);
+    const int cg = b % ncg;
+    const int hs = b / ncg;
+    const int seg = hs % nseg;
+    const int head = hs / nseg;
+    const int BH = total / (ncg * nseg);
+    const int col0 = cg * DV;
+    float* ws_out = ws + (((size_t)((seg + 1) % nseg) * BH + head) * ncg + cg) * ws_slot_floats<DV>();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (seg == nseg - 1) {
+        const float* Sh = S + (size_t)head * kNumFeat * ldv + col0;
+        const float* zh = z + (size_t)head * kNumFeat;
+        switch (w) {
+            case 0: init_tile<0, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 1: init_tile<1, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 2: init_tile<2, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 3: init_tile<3, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 4: init_tile<4, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 5: init_tile<5, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 6: init_tile<6, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 7: init_tile<7, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            case 8: init_tile<8, DV>(Sh, zh, ldv, use_init, ws_out); break;
+            default: init_tile<9, DV>(Sh, zh, ldv, use_init, ws_out); break;
+        }
+        return;
+    }
+    const int tb = seg * seg_len;
+    const uint16_t* kh = k + ((size_t)head * L + tb) * kDFeat;
+    const uint16_t* vh = v + ((size_t)head * L + tb) * ldv + col0;
+    const int nch = seg_len / kC;
+    switch (w) {
+        case 0: state_pair<0, 0, DV>(kh, vh, ldv, nch, rg, ws_out); break;
+        case 1: state_pair<1, 0, DV>(kh, vh, ldv, nch, rg, ws_out); break;
+        case 2: state_pair<2, 0, DV>(kh, vh, ldv, nch, rg, ws_out); break;
+        case 3: state_pair<3, 0, DV>(kh, vh, ldv, nch, rg, ws_out); break;
+        case 4: state_pair<4, 0, DV>(kh, vh, ldv, nch, rg, ws_out); break;
+        case 5: state_pair<0, 1, DV>(kh, vh, ldv, nch, rg, ws_out); break;
+        case 6: state_pair<1, 1, DV>(kh, vh, ldv, nch, rg, ws_out); break;
+        case 7: state_pair<2, 1, DV>(kh, vh, ldv, nch, rg, ws_out); break;
+        case 8: state_pair<3, 1, DV>(kh, vh, ldv, nch, rg, ws_out); break;
+        default: state_pair<4, 1, DV>(kh, vh, ldv, nch, rg, ws_out); break;
+    }
+}
+
 // Inclusive prefix over segment slots, per head: slot s <- slot s-1 + slot s.
-// After it, slot s holds the state entering segment s.
+// After it, slot s holds the state entering segment s.  Each thread owns one
+// 16-byte element of a slot and walks the segments eight at a time, all
+// eight loads issued before the adds and stores.
 __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ ws, int nseg, int BH,
                                                            size_t slot_floats) {
     const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -1166,10 +1471,15 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ w
     f32x4* p = reinterpret_cast<f32x4*>(ws + (size_t)head * slot_floats + e);
     const size_t stride = (size_t)BH * slot_floats / 4;  // in f32x4
     f32x4 run = p[0];
-    for (int sidx = 1; sidx < nseg; ++sidx) {
-        f32x4 x = p[sidx * stride];
-        run += x;
-        p[sidx * stride] = run;
+    for (int s0 = 1; s0 < nseg; s0 += 8) {
+        f32x4 x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = s0 + i < nseg ? p[(size_t)(s0 + i) * stride] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            run += x[i];
+            if (s0 + i < nseg) p[(size_t)(s0 + i) * stride] = run;
+        }
     }
 }
 
@@ -1237,8 +1547,8 @@ hipError_t launch_plan(const PrefillPlan& pl, const uint16_t* q, const uint16_t*
     const int nseg = (L + seg_len - 1) / seg_len;
     float* wsf = static_cast<float*>(ws);
     const dim3 grid(BH * pl.ncg * nseg);
-    hipLaunchKernelGGL((prefill_mfma_kernel<DVL, kModeState>), grid, dim3(768), 0, st, q, k, v, L, dv, pl.ncg,
-                       seg_len, nseg, eps, y, S, z, use_init, wsf, nullptr, nullptr, 0, 0.f);
+    hipLaunchKernelGGL((segment_state_kernel<DVL>), grid, dim3(64 * kStateWaves), 0, st, k, v, L, dv, pl.ncg, seg_len,
+                       nseg, S, z, use_init, wsf);
     // (one segment: the slot already holds the initial state; with several,
     // B*H*ncg is below the workgroup target, well inside the grid's y range)
     const size_t slot = ws_slot_floats<DVL>();
@@ -1329,8 +1639,8 @@ static hipError_t launch_hybrid_plan(const PrefillPlan& pl, const uint16_t* q, c
     float* wsf = static_cast<float*>(ws);
     // state pass and scan at 64 columns (one group per 64 value columns)
     const int ncg64 = dv / 64;
-    hipLaunchKernelGGL((prefill_mfma_kernel<64, kModeState>), dim3(BH * ncg64 * nseg), dim3(768), 0, st, q, k, v, L,
-                       dv, ncg64, seg_len, nseg, eps, y, S, z, use_init, wsf, nullptr, nullptr, 0, 0.f);
+    hipLaunchKernelGGL((segment_state_kernel<64>), dim3(BH * ncg64 * nseg), dim3(64 * kStateWaves), 0, st, k, v, L,
+                       dv, ncg64, seg_len, nseg, S, z, use_init, wsf);
     const size_t slot = ws_slot_floats<64>();
     if (nseg > 1)
         hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((slot / 4 + 255) / 256), BH * ncg64), dim3(256), 0, st,

@@ -123,7 +123,7 @@ __device__ __forceinline__ void pack8_hilo(const float (&a)[8], bf16x8& hi, bf16
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         h[i] = pack_bf16x2(a[2 * i], a[2 * i + 1]);
-        l[i] = pack_bf16x2(a[2 * i] - bf16lo_f32(h[i]), a[2 * i + 1] - bf16hi_f32(h[i]));
+        l[i] = lo_pair_of(h[i], a[2 * i], a[2 * i + 1]);
     }
     hi = __builtin_bit_cast(bf16x8, h);
     lo = __builtin_bit_cast(bf16x8, l);
