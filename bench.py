@@ -1,30 +1,39 @@
 """Throughput of the Taylor linear attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config cfg2] [--no-extra] [--no-cpu]
 
-A step is one ``based_prefill`` call over one batch of the workload
-(default: the BASED-360M-shaped prefill layer, B=8, H=16, L=2048, d'=16,
-d_v=64, bf16, chunk 64), inputs already resident in HBM.  Steps cycle over
-four distinct input/output buffer sets so that consecutive steps do not
-re-read the previous step's data from the 256 MB Infinity Cache.  Rank 0
-prints one JSON line with:
+A step is one ``based_prefill`` call over one batch of the headline
+workload (default cfg2: the BASED-360M-shaped prefill layer, B=8, H=16,
+L=2048, d'=16, d_v=64, bf16, chunk 64), inputs already resident in HBM.
+Steps cycle over four distinct input/output buffer sets so that consecutive
+steps do not re-read the previous step's data from the 256 MB Infinity
+Cache.  Before anything is timed the GPU runs the step untimed for a fixed
+wall-clock time (the settle phase: the first ~20 ms of work run at the idle
+clock), then W warm-up steps; the K timed steps are captured once in a HIP
+graph and replayed, so that host-side launch gaps do not enter the step
+time.  Rank 0 prints one JSON line with:
 
 * value: tokens/s (tokens = B*L per step, each token covering all H heads);
 * roofline: the prefill kernel's algorithmic bytes per launch / its mean
-  launch duration (HIP events on the launch stream around the timed loop,
+  launch duration (HIP events on the launch stream around the timed replay,
   over the number of launches), against 8 TB/s HBM (the kernel's
   arithmetic intensity is below the bf16 MFMA ridge), plus its algorithmic
-  flop rate against the 2.5 PFLOP/s dense bf16 MFMA peak; `traffic` comes
-  from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary when that
-  summary was taken on the current kernel source;
+  flop rate against the 2.5 PFLOP/s dense bf16 MFMA peak and the median,
+  p10 and p90 of single launches; `traffic` comes from the committed
+  rocprofv3 FETCH_SIZE/WRITE_SIZE summary when that summary was taken on
+  the current kernel source;
 * cpu_baseline: the fp64 oracle (recurrent form) timed on the host cores on
-  a sample of whole heads of the same workload;
-* extra: the next-token step (1.3B-shaped decode, 1024 steps), the w=64
-  window kernel with fused add, the window's next-token step on its ring
-  cache, and the 64K-token prefill, each with its own HBM roofline fraction;
-  the whole 8K hybrid layer fused (and as two passes);
-  the gradients of the prefill over the same layer (matrix-core fraction);
-  and the other feature dims and window sizes.
+  a sample of whole heads of the same workload, with the thread count, the
+  CPU model and a one-core rate;
+* extra: every other configuration, each leg with its own roofline (bytes
+  or flops per launch, mean and median/p10/p90 launch time, fraction of
+  peak, counter traffic where a summary exists) and, where the oracle has
+  the routine, its CPU rate on a sample: the 1.3B decode (its 1024-token
+  setup prefill at d_v = 128, then 1024 next-token steps), the 8K window
+  layer (linear branch, window branch with fused add, the fused hybrid
+  layer), the 64K prefill, the tiny fp32 layer, the window's next-token
+  step, the gradients of the prefill and the other feature dims and window
+  sizes.
 """
 from __future__ import annotations
 
@@ -165,6 +174,63 @@ def launch_distribution(launch, n: int) -> dict:
     return {"median_us": pct(0.5), "p10_us": pct(0.1), "p90_us": pct(0.9), "launches": n}
 
 
+def settle(fn, seconds: float) -> int:
+    """Runs fn(i) untimed for a wall-clock time (the GPU leaves its idle
+    clock state only after ~20 ms of continuous work); returns the count."""
+    t_end = time.perf_counter() + seconds
+    i = 0
+    while time.perf_counter() < t_end:
+        fn(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
+def time_leg(fn, n: int, settle_s: float = 0.1, dist_n: int = 30):
+    """Mean launch seconds of fn over n launches (events around the region on
+    the launch stream), after a settle phase, and the per-launch
+    distribution of a separate pass."""
+    settle(fn, settle_s)
+    timer = RegionTimer()
+    torch.cuda.synchronize()
+    timer.start()
+    for i in range(n):
+        fn(i)
+    timer.stop()
+    mean = timer.seconds() / n
+    return mean, launch_distribution(fn, dist_n)
+
+
+def roofline(nbytes: float, sec: float, traffic=None, flops: float | None = None, flop_peak: float = None,
+             flop_unit: str = "bf16 MFMA") -> dict:
+    """HBM roofline of one launch (algorithmic bytes / mean launch time), with
+    the flop rate against a matrix-core peak where the kernel has one."""
+    out = {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+           "frac": nbytes / sec / HBM_PEAK, "traffic": traffic, "algorithmic_bytes": nbytes}
+    if flops is not None:
+        out.update({"algorithmic_flops": flops, "tflops": flops / sec / 1e12,
+                    "mfma_frac": flops / sec / (flop_peak or MFMA_BF16_PEAK), "mfma_peak": flop_unit})
+    return out
+
+
+def cpu_info() -> dict:
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count()
+    return {"cpu_model": model, "nproc": avail, "os_cpu_count": os.cpu_count()}
+
+
 def make_sets(tensors, n):
     out = [tuple(t.to("cuda") for t in tensors)]
     for _ in range(n - 1):
@@ -173,31 +239,48 @@ def make_sets(tensors, n):
 
 
 # ---------------------------------------------------------------- legs
-def bench_prefill(based, wl, steps, warmup):
-    """Returns (wall seconds per step, mean launch seconds from the events
-    around the timed region, per-launch distribution)."""
+def prefill_sets(based, wl, n_sets=N_SETS):
     q, k, v = si.linear_inputs(wl)
-    ins = make_sets((q, k, v), N_SETS)
-    outs = []
-    for _ in range(N_SETS):
-        outs.append((torch.empty(wl.B, wl.H, wl.L, wl.dv, device="cuda"),
-                     torch.empty(wl.B, wl.H, F, wl.dv, device="cuda"),
-                     torch.empty(wl.B, wl.H, F, device="cuda")))
+    ins = make_sets((q, k, v), n_sets)
+    outs = [(torch.empty(wl.B, wl.H, wl.L, wl.dv, device="cuda"), torch.empty(wl.B, wl.H, F, wl.dv, device="cuda"),
+             torch.empty(wl.B, wl.H, F, device="cuda")) for _ in range(n_sets)]
     nbytes = based.based_prefill_workspace_bytes(wl.B, wl.H, wl.L, wl.dv)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
     def step(i):
-        (qq, kk, vv), (y, S, z) = ins[i % N_SETS], outs[i % N_SETS]
+        (qq, kk, vv), (y, S, z) = ins[i % n_sets], outs[i % n_sets]
         based.based_prefill(qq, kk, vv, chunk=wl.chunk, eps=wl.eps, y=y, S=S, z=z, workspace=ws)
 
+    return step
+
+
+def bench_prefill(based, wl, steps, warmup, settle_s=0.3):
+    """The headline leg.  Settle phase, W warm-up steps, then K steps
+    captured in a HIP graph and replayed once: returns (wall seconds per
+    step, mean launch seconds from events around the replay, per-launch
+    distribution)."""
+    step = prefill_sets(based, wl)
+    settle(step, settle_s)
     for i in range(warmup):
         step(i)
+    # capture on a side stream after an eager run there (as torch requires)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(i)
+    g.replay()  # untimed: first replay of a new graph
+    settle(step, 0.05)
     timer = RegionTimer()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     timer.start()
-    for i in range(steps):
-        step(i)
+    g.replay()
     timer.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -205,18 +288,38 @@ def bench_prefill(based, wl, steps, warmup):
     return wall / steps, timer.seconds() / steps, dist
 
 
+def bench_prefill_leg(based, wl, n=50):
+    """A prefill workload as an extra leg: mean launch time and distribution."""
+    return time_leg(prefill_sets(based, wl), n, settle_s=0.15, dist_n=30)
+
+
 def bench_decode(based, wl, n_steps):
-    """1024-token prefill, then n_steps next-token steps timed as one region.
-    Returns (wall seconds per step, event seconds per step)."""
+    """1024-token prefill (the d_v = 128 setup, timed as its own leg), then
+    n_steps next-token steps timed as one region, and a per-step
+    distribution on a copy of the state.  Returns (setup mean seconds,
+    setup distribution, wall seconds per step, event seconds per step, step
+    distribution)."""
     q, k, v = si.linear_inputs(wl)
-    _, S, z = based.based_prefill(*(t.cuda() for t in (q, k, v)), chunk=wl.chunk, eps=wl.eps)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
     del q, k, v
+    S = torch.empty(wl.B, wl.H, F, wl.dv, device="cuda")
+    z = torch.empty(wl.B, wl.H, F, device="cuda")
+    yp = torch.empty(wl.B, wl.H, wl.L, wl.dv, device="cuda")
+    ws = torch.empty(max(1, based.based_prefill_workspace_bytes(wl.B, wl.H, wl.L, wl.dv)), dtype=torch.uint8,
+                     device="cuda")
+
+    def setup(i):
+        based.based_prefill(qd, kd, vd, chunk=wl.chunk, eps=wl.eps, y=yp, S=S, z=z, workspace=ws)
+
+    setup_s, setup_dist = time_leg(setup, 10, settle_s=0.1, dist_n=10)
+    setup(0)
+    del qd, kd, vd, yp
     step_in = [tuple(t.cuda() for t in si.decode_inputs(wl, t)) for t in range(n_steps)]
     y = torch.empty(wl.B, wl.H, wl.dv, device="cuda")
-    # untimed warm-up (~50 ms, out of the idle clock state) on a copy of the state
+    # untimed settle on a copy of the state
     S2, z2 = S.clone(), z.clone()
-    for t in range(500):
-        based.based_decode_step(*step_in[t % n_steps], S2, z2, eps=wl.eps, y=y)
+    settle(lambda t: based.based_decode_step(*step_in[t % n_steps], S2, z2, eps=wl.eps, y=y), 0.1)
+    dist = launch_distribution(lambda t: based.based_decode_step(*step_in[t % n_steps], S2, z2, eps=wl.eps, y=y), 50)
     del S2, z2
     timer = RegionTimer()
     torch.cuda.synchronize()
@@ -227,12 +330,12 @@ def bench_decode(based, wl, n_steps):
     timer.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall / n_steps, timer.seconds() / n_steps
+    return setup_s, setup_dist, wall / n_steps, timer.seconds() / n_steps, dist
 
 
 def bench_swa(based, wl, reps, window=None):
     """Window kernel with fused add, alternating two input/output sets;
-    returns event seconds per launch over the timed region."""
+    returns (mean launch seconds over the timed region, distribution)."""
     window = wl.window if window is None else window
     q, k, v = si.linear_inputs(wl)
     qw, kw = si.window_inputs(wl)
@@ -244,15 +347,7 @@ def bench_swa(based, wl, reps, window=None):
     def launch(i):
         based.swa_forward(*sets[i % 2], window=window, scale=wl.swa_scale, add=adds[i % 2], y=ys[i % 2])
 
-    for i in range(500):  # untimed warm-up, ~45 ms
-        launch(i)
-    timer = RegionTimer()
-    torch.cuda.synchronize()
-    timer.start()
-    for i in range(reps):
-        launch(i)
-    timer.stop()
-    return timer.seconds() / reps
+    return time_leg(launch, reps, settle_s=0.1, dist_n=30)
 
 
 def bench_hybrid(based, wl, reps):
@@ -278,15 +373,9 @@ def bench_hybrid(based, wl, reps):
 
     res = {}
     for path in ("auto", "fused", "two_pass"):
-        for i in range(200):  # untimed warm-up
-            layer(i, path)
-        timer = RegionTimer()
-        torch.cuda.synchronize()
-        timer.start()
-        for i in range(reps):
-            layer(i, path)
-        timer.stop()
-        res[path] = timer.seconds() / reps
+        sec, dist = time_leg(lambda i: layer(i, path), reps, settle_s=0.1, dist_n=20)
+        res[path] = sec
+        res[path + "_dist"] = dist
     return res
 
 
@@ -340,7 +429,7 @@ def bench_other_sizes(based):
     # window 128 over the 8K window workload inputs (matrix cores, two-tile
     # halo), timed exactly as the w = 64 leg
     ww = si.WORKLOADS["window_8k"]
-    sec = bench_swa(based, ww, 100, window=128)
+    sec, _ = bench_swa(based, ww, 100, window=128)
     sb = swa_bytes(ww)
     out["window_8k_w128"] = {"kernel_us": sec * 1e6, "hbm_GBps": sb / sec / 1e9, "hbm_frac": sb / sec / HBM_PEAK,
                              "algorithmic_bytes": sb, "note": "w=128, fused add, matrix cores with a two-tile halo"}
@@ -412,18 +501,24 @@ def bench_backward(based, wl, reps=40):
     return t.seconds() / reps, pairs * (8 * wl.d + 6 * wl.dv + 12)
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """Oracle recurrent form on whole heads of the workload, sized to about
-    budget_s of host time (at most the full workload)."""
+def _oracle():
     import oracle
 
     oracle.build()
+    return oracle
+
+
+def cpu_baseline(wl, budget_s=8.0):
+    """Oracle recurrent form on whole heads of the workload, sized to about
+    budget_s of host time (at most the full workload), OpenMP over heads on
+    every host core; plus one head alone (one core)."""
+    oracle = _oracle()
     q, k, v = (t.reshape(-1, wl.L, t.shape[-1]) for t in si.linear_inputs(wl))
     threads = oracle.num_threads()
     t0 = time.perf_counter()
-    oracle.la_recurrent(q[:2], k[:2], v[:2], eps=wl.eps)  # two heads run on two threads
-    per_head = time.perf_counter() - t0
-    rounds = max(1, int(budget_s / max(per_head, 1e-9)))
+    oracle.la_recurrent(q[:1], k[:1], v[:1], eps=wl.eps)  # one head: one thread
+    one = time.perf_counter() - t0
+    rounds = max(1, int(budget_s / max(one, 1e-9)))
     n_heads = min(q.shape[0], threads * rounds)
     t0 = time.perf_counter()
     oracle.la_recurrent(q[:n_heads], k[:n_heads], v[:n_heads], eps=wl.eps)
@@ -431,20 +526,89 @@ def cpu_baseline(wl, budget_s=12.0):
     tokens = n_heads * wl.L / wl.H  # a token covers all H heads
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_heads} of {q.shape[0]} heads x {wl.L} tokens of {wl.name} "
-                      f"(fp64 recurrent form, OpenMP over heads), {dt:.1f} s; tokens = head-tokens / H"}
+                      f"(fp64 recurrent form, OpenMP over heads), {dt:.1f} s; tokens = head-tokens / H",
+            "single_core_tokens_per_s": wl.L / wl.H / one, **cpu_info()}
+
+
+def cpu_heads(fn, n_heads, threads):
+    """Seconds of fn over a sample (called once; OpenMP over its heads) and of
+    fn over one head (one core)."""
+    t0 = time.perf_counter()
+    fn(1)
+    one = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    fn(n_heads)
+    return time.perf_counter() - t0, one
+
+
+def cpu_legs() -> dict:
+    """The oracle on a sample of every other configuration (a batch of one:
+    the config's H heads; values drawn for that shape), timed on the host
+    cores: tokens/s on all cores and on one."""
+    oracle = _oracle()
+    th = oracle.num_threads()
+    out = {"threads": th, **cpu_info()}
+    # 1.3B decode: the 1024-token prefill and 1024 next-token steps of every head of one sequence
+    wl = si.WORKLOADS["decode_1p3b"]
+    q, k, v = (t[0] for t in si.linear_inputs(wl, B=1))
+    steps = [tuple(t[0] for t in si.decode_inputs(wl, t, B=1)) for t in range(wl.decode_steps)]
+    dt, one = cpu_heads(lambda n: oracle.la_recurrent(q[:n], k[:n], v[:n], eps=wl.eps), wl.H, th)
+    _, S, z = oracle.la_recurrent(q, k, v, eps=wl.eps, want_y=False)
+
+    def dec(n):
+        Sx, zx = S[:n], z[:n]
+        for qt, kt, vt in steps:
+            _, Sx, zx = oracle.decode_step(qt[:n], kt[:n], vt[:n], Sx, zx, eps=wl.eps)
+
+    ddt, done = cpu_heads(dec, wl.H, th)
+    out["decode_1p3b"] = {
+        "prefill_tokens_per_s": wl.L / dt, "prefill_single_core_tokens_per_s": wl.L / wl.H / one,
+        "decode_tokens_per_s": wl.decode_steps / ddt, "decode_single_core_tokens_per_s": wl.decode_steps / wl.H / done,
+        "sample": f"1 of {wl.B} sequences ({wl.H} heads): la_recurrent over {wl.L} tokens ({dt:.2f} s), then "
+                  f"{wl.decode_steps} decode_step calls ({ddt:.2f} s); tokens = head-tokens / H"}
+    # 8K window layer: both branches over every head of one sequence
+    wl = si.WORKLOADS["window_8k"]
+    q, k, v = (t[0] for t in si.linear_inputs(wl, B=1))
+    qw, kw = (t[0] for t in si.window_inputs(wl, B=1))
+    dt, one = cpu_heads(lambda n: oracle.la_recurrent(q[:n], k[:n], v[:n], eps=wl.eps, want_y=True), wl.H, th)
+    sdt, sone = cpu_heads(lambda n: oracle.swa(qw[:n], kw[:n], v[:n], wl.window, wl.swa_scale), wl.H, th)
+    out["window_8k"] = {"linear_tokens_per_s": wl.L / dt, "linear_single_core_tokens_per_s": wl.L / wl.H / one,
+                        "window_tokens_per_s": wl.L / sdt, "window_single_core_tokens_per_s": wl.L / wl.H / sone,
+                        "sample": f"1 of {wl.B} sequences ({wl.H} heads x {wl.L} tokens): la_recurrent {dt:.2f} s, "
+                                  f"swa (brute force) {sdt:.2f} s"}
+    # 64K sequence: every head
+    wl = si.WORKLOADS["long_64k"]
+    q, k, v = (t[0] for t in si.linear_inputs(wl))
+    dt, one = cpu_heads(lambda n: oracle.la_recurrent(q[:n], k[:n], v[:n], eps=wl.eps), wl.H, th)
+    out["long_64k"] = {"tokens_per_s": wl.L / dt, "single_core_tokens_per_s": wl.L / wl.H / one,
+                       "sample": f"the whole workload ({wl.H} heads x {wl.L} tokens), la_recurrent {dt:.2f} s"}
+    # tiny fp32 layer: the closed (quadratic) form and the window
+    wl = si.WORKLOADS["tiny_f32"]
+    q, k, v = si.linear_inputs(wl)
+    t0 = time.perf_counter()
+    oracle.la_quadratic(q, k, v, eps=wl.eps)
+    oracle.swa(q, k, v, wl.window, wl.swa_scale)
+    dt = time.perf_counter() - t0
+    out["tiny_f32"] = {"tokens_per_s": wl.L / dt, "sample": f"the whole layer (la_quadratic + swa), {dt*1e3:.1f} ms"}
+    return out
+
+
+CONFIGS = {"cfg1": "tiny_f32", "cfg2": "prefill_360m", "cfg3": "decode_1p3b", "cfg4": "window_8k", "cfg5": "long_64k"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU leaves its idle clock state only after ~20 ms of continuous
-    # work (the first 50 prefill launches run ~75% slower), so the default
-    # untimed warm-up is 1000 steps (~45 ms) before 400 timed ones.
+    # A settle phase of fixed wall time runs before the warm-up steps, so the
+    # timed steps never see the idle clock whatever --warmup is.
     ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="prefill_360m", choices=["prefill_360m", "long_64k"])
-    ap.add_argument("--no-extra", action="store_true", help="skip decode/window/64K legs")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg5"],
+                    help="headline prefill workload: cfg2 (360M-shaped layer) or cfg5 (64K sequence); the other "
+                         "configurations are extra legs")
+    ap.add_argument("--workload", default=None, choices=["prefill_360m", "long_64k"], help="same, by name")
+    ap.add_argument("--no-extra", action="store_true", help="skip every leg but the headline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--window-decode-steps", type=int, default=4096)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -471,7 +635,7 @@ def main():
 
     import linear_attention_sequence_taylor_amd as based
 
-    wl = si.WORKLOADS[args.workload]
+    wl = si.WORKLOADS[args.workload or CONFIGS[args.config]]
     print(f"[bench] workload {wl.name}: {wl.description}", file=sys.stderr, flush=True)
     step_s, kern_s, dist = bench_prefill(based, wl, args.steps, args.warmup)
     tokens = wl.B * wl.L
@@ -502,7 +666,8 @@ def main():
             "traffic": read_traffic(f"prefill_mfma_{wl.name}_pmc.txt", digest),
             "kernel": "based_prefill (bf16 MFMA)",
             "kernel_ms": kern_s * 1e3,
-            "kernel_timing": "HIP events around the timed region on the launch stream / steps",
+            "kernel_timing": "HIP events on the launch stream around one replay of the K steps captured in a HIP "
+                             "graph, / K; before it a 0.3 s settle phase and W warm-up steps",
             "single_launch_us": dist,
             "algorithmic_bytes": abytes,
             "algorithmic_flops": aflops,
@@ -516,66 +681,99 @@ def main():
 
     if not args.no_extra:
         extra = {}
+        # cfg3: the 1.3B decode, its d_v = 128 setup prefill and 1024 steps
         wd = si.WORKLOADS["decode_1p3b"]
-        dstep, dkern = bench_decode(based, wd, args.decode_steps)
+        ssec, sdist, dstep, dkern, ddist = bench_decode(based, wd, args.decode_steps)
         db = decode_bytes(wd)
         extra["decode_1p3b"] = {
             "tokens_per_s": wd.B / dstep, "ms_per_step": dstep * 1e3, "kernel_us": dkern * 1e6,
-            "hbm_GBps": db / dkern / 1e9, "hbm_frac": db / dkern / HBM_PEAK, "algorithmic_bytes": db,
-            "steps": args.decode_steps, "note": "1024-token prefill then next-token steps; fp32 state"}
-        print(f"[bench] decode: {dkern*1e6:.1f} us/step, {db/dkern/1e9:.0f} GB/s", file=sys.stderr, flush=True)
+            "step_us": ddist, "steps": args.decode_steps,
+            "roofline": roofline(db, dkern, read_traffic("decode_step_decode_1p3b_pmc.txt",
+                                                         source_digest("decode.hip", "common.hpp"))),
+            "setup_prefill": {"kernel_us": ssec * 1e6, "launch_us": sdist, "tokens_per_s": wd.B * wd.L / ssec,
+                              "roofline": roofline(prefill_bytes(wd), ssec, None, prefill_flops(wd)),
+                              "note": "B=128, H=16, L=1024, d_v=128 prefill that builds the decode state"},
+            "note": "1024-token prefill then next-token steps; fp32 state; events around the step loop"}
+        print(f"[bench] decode: setup prefill {ssec*1e6:.1f} us, {dkern*1e6:.1f} us/step", file=sys.stderr,
+              flush=True)
+        # cfg4: the 8K layer -- linear branch, window branch (fused add), whole layer
         ww = si.WORKLOADS["window_8k"]
-        skern = bench_swa(based, ww, 100)
+        lsec, ldist = bench_prefill_leg(based, ww, 40)
+        skern, sdist2 = bench_swa(based, ww, 100)
         sb = swa_bytes(ww)
-        extra["window_8k_swa"] = {"tokens_per_s": ww.B * ww.L / skern, "kernel_us": skern * 1e6,
-                                  "hbm_GBps": sb / skern / 1e9, "hbm_frac": sb / skern / HBM_PEAK,
-                                  "algorithmic_bytes": sb}
-        print(f"[bench] swa: {skern*1e6:.1f} us, {sb/skern/1e9:.0f} GB/s", file=sys.stderr, flush=True)
         ht = bench_hybrid(based, ww, 100)
         hb = hybrid_bytes(ww)
-        extra["window_8k_hybrid_layer"] = {
-            "tokens_per_s": ww.B * ww.L / ht["auto"], "kernel_us": ht["auto"] * 1e6,
-            "hbm_GBps": hb / ht["auto"] / 1e9, "hbm_frac": hb / ht["auto"] / HBM_PEAK, "algorithmic_bytes": hb,
-            "fused_us": ht["fused"] * 1e6, "two_pass_us": ht["two_pass"] * 1e6,
-            "note": "linear attention + w=64 window over B=4, H=16, L=8192 through based_hybrid_prefill; kernel_us "
-                    "is the library's own choice (auto), fused_us the one-kernel path (32-column groups with a "
-                    "segment split), two_pass_us based_prefill then the window adding into y; algorithmic bytes "
-                    "are those of one pass"}
-        print(f"[bench] hybrid layer: auto {ht['auto']*1e6:.1f} us, fused {ht['fused']*1e6:.1f} us, two passes "
-              f"{ht['two_pass']*1e6:.1f} us", file=sys.stderr, flush=True)
+        extra["window_8k"] = {
+            "linear_branch": {"kernel_us": lsec * 1e6, "launch_us": ldist, "tokens_per_s": ww.B * ww.L / lsec,
+                              "roofline": roofline(prefill_bytes(ww), lsec, None, prefill_flops(ww))},
+            "window_branch": {"kernel_us": skern * 1e6, "launch_us": sdist2, "tokens_per_s": ww.B * ww.L / skern,
+                              "roofline": roofline(sb, skern, read_traffic("swa_mfma_window_8k_pmc.txt",
+                                                                           source_digest("swa_mfma.hip",
+                                                                                         "common.hpp")))},
+            "hybrid_layer": {"kernel_us": ht["auto"] * 1e6, "launch_us": ht["auto_dist"],
+                             "tokens_per_s": ww.B * ww.L / ht["auto"],
+                             "roofline": roofline(hb, ht["auto"], read_traffic(
+                                 "prefill_mfma_hybrid_window_8k_pmc.txt",
+                                 source_digest("prefill_mfma.hip", "common.hpp"))),
+                             "fused_us": ht["fused"] * 1e6, "two_pass_us": ht["two_pass"] * 1e6,
+                             "note": "linear attention + w=64 window through based_hybrid_prefill; kernel_us is the "
+                                     "library's own choice (auto), fused_us the one-kernel path, two_pass_us "
+                                     "based_prefill then the window adding into y; algorithmic bytes are those of "
+                                     "one pass"}}
+        print(f"[bench] 8K layer: linear {lsec*1e6:.1f} us, window {skern*1e6:.1f} us, hybrid auto "
+              f"{ht['auto']*1e6:.1f} / fused {ht['fused']*1e6:.1f} / two passes {ht['two_pass']*1e6:.1f} us",
+              file=sys.stderr, flush=True)
+        # cfg5: the 64K sequence (or cfg2 when the headline is cfg5)
+        other = si.WORKLOADS["prefill_360m" if wl.name == "long_64k" else "long_64k"]
+        osec, odist = bench_prefill_leg(based, other, 40 if other.name == "long_64k" else 200)
+        extra[other.name] = {"kernel_us": osec * 1e6, "launch_us": odist, "tokens_per_s": other.B * other.L / osec,
+                             "roofline": roofline(prefill_bytes(other), osec, read_traffic(
+                                 f"prefill_mfma_{other.name}_pmc.txt", digest), prefill_flops(other))}
+        print(f"[bench] {other.name}: {osec*1e6:.1f} us", file=sys.stderr, flush=True)
+        # cfg1: the tiny fp32 layer (linear attention + window, summed)
+        wt = si.WORKLOADS["tiny_f32"]
+        tq, tk, tv = (t.cuda() for t in si.linear_inputs(wt))
+        ty = torch.empty(1, 1, wt.L, wt.dv, device="cuda")
+        tS, tz = torch.empty(1, 1, F, wt.dv, device="cuda"), torch.empty(1, 1, F, device="cuda")
+
+        def tiny(i):
+            based.based_prefill(tq, tk, tv, chunk=wt.chunk, eps=wt.eps, y=ty, S=tS, z=tz)
+            based.swa_forward(tq, tk, tv, window=wt.window, scale=wt.swa_scale, add=ty, y=ty)
+
+        tsec, tdist = time_leg(tiny, 200, settle_s=0.05, dist_n=30)
+        extra["tiny_f32"] = {"layer_us": tsec * 1e6, "launch_us": tdist, "tokens_per_s": wt.L / tsec,
+                             "note": "fp32 inputs: prefill (fp32 matrix cores) then the window adding into y; "
+                                     "launch-latency bound (256 tokens)"}
+        # window next-token step, gradients, other sizes
         wwd = si.WORKLOADS["window_decode_1p3b"]
         wkern = bench_window_decode(based, wwd, args.window_decode_steps)
         wb = window_decode_bytes(wwd)
         extra["window_decode_1p3b"] = {
-            "tokens_per_s": wwd.B / wkern, "kernel_us": wkern * 1e6, "hbm_GBps": wb / wkern / 1e9,
-            "hbm_frac": wb / wkern / HBM_PEAK, "algorithmic_bytes": wb, "steps": args.window_decode_steps,
+            "tokens_per_s": wwd.B / wkern, "kernel_us": wkern * 1e6, "steps": args.window_decode_steps,
+            "roofline": roofline(wb, wkern, read_traffic("swa_decode_window_decode_1p3b_pmc.txt",
+                                                         source_digest("swa_decode.hip", "common.hpp"))),
             "note": "w=64 ring, B=128, H=16, d_qk=64, d_v=128, fused add; HIP graph of 64 steps "
                     "replayed, 16 cache sets"}
-        print(f"[bench] window decode: {wkern*1e6:.1f} us/step, {wb/wkern/1e9:.0f} GB/s", file=sys.stderr,
-              flush=True)
-        if wl.name != "long_64k":
-            wlong = si.WORKLOADS["long_64k"]
-            lstep, lkern, _ = bench_prefill(based, wlong, 50, 100)
-            lb = prefill_bytes(wlong)
-            extra["long_64k_prefill"] = {"tokens_per_s": wlong.B * wlong.L / lstep, "kernel_ms": lkern * 1e3,
-                                         "hbm_GBps": lb / lkern / 1e9, "hbm_frac": lb / lkern / HBM_PEAK,
-                                         "mfma_frac": prefill_flops(wlong) / lkern / MFMA_BF16_PEAK}
-            print(f"[bench] long prefill: {lkern*1e3:.3f} ms", file=sys.stderr, flush=True)
-        bsec, bflops = bench_backward(based, wl)
+        print(f"[bench] window decode: {wkern*1e6:.1f} us/step", file=sys.stderr, flush=True)
+        w2 = si.WORKLOADS["prefill_360m"]
+        bsec, bflops = bench_backward(based, w2)
         extra["prefill_360m_backward"] = {
-            "kernel_ms": bsec * 1e3, "tokens_per_s": wl.B * wl.L / bsec, "direct_form_flops": bflops,
+            "kernel_ms": bsec * 1e3, "tokens_per_s": w2.B * w2.L / bsec, "direct_form_flops": bflops,
             "tflops": bflops / bsec / 1e12, "mfma_frac": bflops / bsec / MFMA_BF16_PEAK,
             "note": "dq, dk, dv for a seeded dy; bf16 matrix cores (weights as bf16 hi/lo pairs, fp32 "
                     "accumulation), direct form (O(L^2) per head)"}
         print(f"[bench] backward: {bsec*1e3:.2f} ms, {bflops/bsec/1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
-        other = bench_other_sizes(based)
-        extra.update(other)
-        print("[bench] other sizes: " + ", ".join(f"{k} {v['kernel_us']:.1f} us" for k, v in other.items()),
+        oth = bench_other_sizes(based)
+        extra.update(oth)
+        print("[bench] other sizes: " + ", ".join(f"{k} {v['kernel_us']:.1f} us" for k, v in oth.items()),
               file=sys.stderr, flush=True)
         line["extra"] = extra
 
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl)
+        if not args.no_extra:
+            line["extra"]["cpu_baselines"] = cpu_legs()
+            print("[bench] cpu baselines done", file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
 
 

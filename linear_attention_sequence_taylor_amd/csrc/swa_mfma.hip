@@ -329,12 +329,13 @@ __device__ __forceinline__ void raw_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int DQK, bool ADD, int HALO>
+template <int DQK, bool ADD, int HALO, int NCS>
 __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ v, int L, int ldv, int ntiles,
+                                                       const uint16_t* __restrict__ v, int L, int ntiles,
                                                        int tiles_per_wg, int wg_per_head, int window, float scale,
                                                        const float* add, float* y) {
+    constexpr int ldv = kDV * NCS;  // row stride of v, y and add: NCS slices of 64 columns
     // K/V ring of HALO + 2 slots: tile tb - HALO + j lives in slot j mod
     // (HALO + 2); Q of tile tb + j in slot j mod 2.  (The fourth slot is a
     // placeholder when HALO = 1.)
@@ -347,15 +348,10 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
     uint16_t* const vs[4] = {v0, v1, v2, v3};
     uint16_t* const qs[2] = {q0s, q1s};
 
-    // Workgroup -> (head, run, 64-column slice), slice fastest.  The 8 XCDs
-    // take workgroups round-robin; the remap gives each XCD a contiguous
-    // range, so the slices of a run (same Q, K) share an L2.
+    // Workgroup -> (head, run, 64-column slice), slice fastest.
     int bid = blockIdx.x;
-    const int total = gridDim.x;
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int ncs = ldv / kDV;  // 64-column slices per head
-    const int col0 = (bid % ncs) * kDV;
-    bid /= ncs;
+    const int col0 = (bid % NCS) * kDV;
+    bid /= NCS;
     const int head = bid / wg_per_head;
     const int tb = (bid % wg_per_head) * tiles_per_wg;
     const int te = min(tb + tiles_per_wg, ntiles);
@@ -555,10 +551,11 @@ __device__ __forceinline__ void long_tile(const uint16_t* ks, const uint16_t* vs
     }
 }
 
-template <int DQK, bool ADD>
+template <int DQK, bool ADD, int NCS>
 __global__ __launch_bounds__(256) void swa_long_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ v, int L, int ldv, int ntiles,
-                                                       int window, float scale, const float* add, float* y) {
+                                                       const uint16_t* __restrict__ v, int L, int ntiles, int window,
+                                                       float scale, const float* add, float* y) {
+    constexpr int ldv = kDV * NCS;
     __shared__ alignas(16) uint16_t k0[kQT * DQK], k1[kQT * DQK];
     __shared__ alignas(16) uint16_t v0[kQT * kDV], v1[kQT * kDV];
     __shared__ alignas(16) uint16_t qs[kQT * DQK];
@@ -566,9 +563,8 @@ __global__ __launch_bounds__(256) void swa_long_kernel(const uint16_t* __restric
     int bid = blockIdx.x;
     const int total = gridDim.x;
     if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int ncs = ldv / kDV;
-    const int col0 = (bid % ncs) * kDV;
-    bid /= ncs;
+    const int col0 = (bid % NCS) * kDV;
+    bid /= NCS;
     const int head = bid / ntiles;
     const int qt = ntiles - 1 - bid % ntiles;  // the longest key ranges first
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -630,15 +626,31 @@ __global__ __launch_bounds__(256) void swa_long_kernel(const uint16_t* __restric
     }
 }
 
-template <int DQK, bool ADD>
-void launch_halo(int halo, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const uint16_t* v, int L,
-                 int ldv, int ntiles, int tpw, int wg_per_head, int window, float scale, const float* add, float* y) {
-    if (halo == 1)
-        hipLaunchKernelGGL((swa_mfma_kernel<DQK, ADD, 1>), grid, dim3(256), 0, st, q, k, v, L, ldv, ntiles, tpw,
+template <int DQK, bool ADD, int NCS>
+void launch_ncs(int halo, bool long_window, dim3 grid, dim3 lgrid, hipStream_t st, const uint16_t* q,
+                const uint16_t* k, const uint16_t* v, int L, int ntiles, int tpw, int wg_per_head, int window,
+                float scale, const float* add, float* y) {
+    if (long_window)
+        hipLaunchKernelGGL((swa_long_kernel<DQK, ADD, NCS>), lgrid, dim3(256), 0, st, q, k, v, L, ntiles, window, scale,
+                           add, y);
+    else if (halo == 1)
+        hipLaunchKernelGGL((swa_mfma_kernel<DQK, ADD, 1, NCS>), grid, dim3(256), 0, st, q, k, v, L, ntiles, tpw,
                            wg_per_head, window, scale, add, y);
     else
-        hipLaunchKernelGGL((swa_mfma_kernel<DQK, ADD, 2>), grid, dim3(256), 0, st, q, k, v, L, ldv, ntiles, tpw,
+        hipLaunchKernelGGL((swa_mfma_kernel<DQK, ADD, 2, NCS>), grid, dim3(256), 0, st, q, k, v, L, ntiles, tpw,
                            wg_per_head, window, scale, add, y);
+}
+
+template <int DQK, bool ADD>
+void launch_dqk(int ncs, int halo, bool long_window, dim3 grid, dim3 lgrid, hipStream_t st, const uint16_t* q,
+                const uint16_t* k, const uint16_t* v, int L, int ntiles, int tpw, int wg_per_head, int window,
+                float scale, const float* add, float* y) {
+    if (ncs == 1)
+        launch_ncs<DQK, ADD, 1>(halo, long_window, grid, lgrid, st, q, k, v, L, ntiles, tpw, wg_per_head, window,
+                                scale, add, y);
+    else
+        launch_ncs<DQK, ADD, 2>(halo, long_window, grid, lgrid, st, q, k, v, L, ntiles, tpw, wg_per_head, window,
+                                scale, add, y);
 }
 
 }  // namespace
@@ -652,27 +664,18 @@ hipError_t launch_swa_mfma(const void* q, const void* k, const void* v, int BH, 
     const int tpw = max(1, min(16, (BH * ncs * ntiles + 511) / 512));
     const int wg_per_head = (ntiles + tpw - 1) / tpw;
     const dim3 grid(BH * wg_per_head * ncs);
-    const int halo = window > kQT ? 2 : 1;  // key tiles of 64 before the query tile
+    const dim3 lgrid(BH * ntiles * ncs);
+    const int halo = window > kQT ? 2 : 1;    // key tiles of 64 before the query tile
+    const bool long_window = window > 2 * kQT;  // the online-softmax kernel over 64-key tiles
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     const uint16_t* vv = static_cast<const uint16_t*>(v);
-    if (window > 2 * kQT) {
-        const dim3 lgrid(BH * ntiles * ncs);
-        if (dqk == 16) {
-            if (add) hipLaunchKernelGGL((swa_long_kernel<16, true>), lgrid, dim3(256), 0, st, qq, kk, vv, L, dv, ntiles, window, scale, add, y);
-            else hipLaunchKernelGGL((swa_long_kernel<16, false>), lgrid, dim3(256), 0, st, qq, kk, vv, L, dv, ntiles, window, scale, add, y);
-        } else {
-            if (add) hipLaunchKernelGGL((swa_long_kernel<64, true>), lgrid, dim3(256), 0, st, qq, kk, vv, L, dv, ntiles, window, scale, add, y);
-            else hipLaunchKernelGGL((swa_long_kernel<64, false>), lgrid, dim3(256), 0, st, qq, kk, vv, L, dv, ntiles, window, scale, add, y);
-        }
-        return hipGetLastError();
-    }
     if (dqk == 16) {
-        if (add) launch_halo<16, true>(halo, grid, st, qq, kk, vv, L, dv, ntiles, tpw, wg_per_head, window, scale, add, y);
-        else launch_halo<16, false>(halo, grid, st, qq, kk, vv, L, dv, ntiles, tpw, wg_per_head, window, scale, add, y);
+        if (add) launch_dqk<16, true>(ncs, halo, long_window, grid, lgrid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
+        else launch_dqk<16, false>(ncs, halo, long_window, grid, lgrid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
     } else {
-        if (add) launch_halo<64, true>(halo, grid, st, qq, kk, vv, L, dv, ntiles, tpw, wg_per_head, window, scale, add, y);
-        else launch_halo<64, false>(halo, grid, st, qq, kk, vv, L, dv, ntiles, tpw, wg_per_head, window, scale, add, y);
+        if (add) launch_dqk<64, true>(ncs, halo, long_window, grid, lgrid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
+        else launch_dqk<64, false>(ncs, halo, long_window, grid, lgrid, st, qq, kk, vv, L, ntiles, tpw, wg_per_head, window, scale, add, y);
     }
     return hipGetLastError();
 }
