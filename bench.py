@@ -593,6 +593,59 @@ def cpu_legs() -> dict:
     return out
 
 
+def profile_leg(name: str, launches: int = 8) -> None:
+    """Launches of one leg's library call, untimed, for counter passes: each
+    dispatch of the call's kernels is one launch of that call."""
+    import linear_attention_sequence_taylor_amd as based
+
+    if name in ("prefill_360m", "long_64k", "setup_1p3b", "linear_8k"):
+        wl = si.WORKLOADS[{"setup_1p3b": "decode_1p3b", "linear_8k": "window_8k"}.get(name, name)]
+        step = prefill_sets(based, wl)
+    elif name == "hybrid_8k":
+        wl = si.WORKLOADS["window_8k"]
+        q, k, v = si.linear_inputs(wl)
+        qw, kw = si.window_inputs(wl)
+        sets = make_sets((q, k, qw, kw, v), 2)
+        ws = torch.empty(max(based.based_hybrid_prefill_workspace_bytes(wl.B, wl.H, wl.L, wl.dv), 1),
+                         dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            based.based_hybrid_prefill(*sets[i % 2], chunk=wl.chunk, eps=wl.eps, window=wl.window, scale=wl.swa_scale,
+                                       workspace=ws)
+    elif name == "decode_1p3b":
+        wl = si.WORKLOADS["decode_1p3b"]
+        S = torch.zeros(wl.B, wl.H, F, wl.dv, device="cuda")
+        z = torch.zeros(wl.B, wl.H, F, device="cuda")
+        steps = [tuple(t.cuda() for t in si.decode_inputs(wl, t)) for t in range(4)]
+
+        def step(i):
+            based.based_decode_step(*steps[i % 4], S, z, eps=wl.eps)
+    elif name == "window_8k":
+        wl = si.WORKLOADS["window_8k"]
+        qw, kw = si.window_inputs(wl)
+        v = si.linear_inputs(wl)[2]
+        sets = make_sets((qw, kw, v), 2)
+        adds = [torch.randn(wl.B, wl.H, wl.L, wl.dv, device="cuda") for _ in range(2)]
+
+        def step(i):
+            based.swa_forward(*sets[i % 2], window=wl.window, scale=wl.swa_scale, add=adds[i % 2])
+    else:
+        wl = si.WORKLOADS["window_decode_1p3b"]
+        _, k = si.window_inputs(wl)
+        v = si.linear_inputs(wl)[2]
+        caches = [based.swa_cache_fill(k.cuda(), v.cuda(), window=wl.window) for _ in range(8)]
+        steps = [tuple(t.cuda() for t in si.window_decode_inputs(wl, t)) for t in range(8)]
+        pos = torch.full((wl.B,), wl.L, dtype=torch.int64, device="cuda")
+        add = torch.randn(wl.B, wl.H, wl.dv, device="cuda")
+
+        def step(i):
+            based.swa_decode_step(*steps[i % 8], *caches[i % 8], pos, scale=wl.swa_scale, add=add)
+    for i in range(launches):
+        step(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_leg": name, "launches": launches}), flush=True)
+
+
 CONFIGS = {"cfg1": "tiny_f32", "cfg2": "prefill_360m", "cfg3": "decode_1p3b", "cfg4": "window_8k", "cfg5": "long_64k"}
 
 
@@ -611,6 +664,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--window-decode-steps", type=int, default=4096)
+    ap.add_argument("--profile-leg", default=None,
+                    choices=["prefill_360m", "long_64k", "hybrid_8k", "decode_1p3b", "window_8k", "window_decode_1p3b",
+                             "setup_1p3b", "linear_8k"],
+                    help="only launch one leg's kernels a few times (untimed), for rocprofv3 counter passes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to calibrate "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE against known bytes")
@@ -623,6 +680,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
+        return
+
+    if args.profile_leg:
+        profile_leg(args.profile_leg)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -691,7 +752,8 @@ def main():
             "roofline": roofline(db, dkern, read_traffic("decode_step_decode_1p3b_pmc.txt",
                                                          source_digest("decode.hip", "common.hpp"))),
             "setup_prefill": {"kernel_us": ssec * 1e6, "launch_us": sdist, "tokens_per_s": wd.B * wd.L / ssec,
-                              "roofline": roofline(prefill_bytes(wd), ssec, None, prefill_flops(wd)),
+                              "roofline": roofline(prefill_bytes(wd), ssec, read_traffic(
+                                  "prefill_mfma_decode_1p3b_setup_pmc.txt", digest), prefill_flops(wd)),
                               "note": "B=128, H=16, L=1024, d_v=128 prefill that builds the decode state"},
             "note": "1024-token prefill then next-token steps; fp32 state; events around the step loop"}
         print(f"[bench] decode: setup prefill {ssec*1e6:.1f} us, {dkern*1e6:.1f} us/step", file=sys.stderr,
@@ -705,7 +767,8 @@ def main():
         hb = hybrid_bytes(ww)
         extra["window_8k"] = {
             "linear_branch": {"kernel_us": lsec * 1e6, "launch_us": ldist, "tokens_per_s": ww.B * ww.L / lsec,
-                              "roofline": roofline(prefill_bytes(ww), lsec, None, prefill_flops(ww))},
+                              "roofline": roofline(prefill_bytes(ww), lsec, read_traffic(
+                                  "prefill_mfma_window_8k_linear_pmc.txt", digest), prefill_flops(ww))},
             "window_branch": {"kernel_us": skern * 1e6, "launch_us": sdist2, "tokens_per_s": ww.B * ww.L / skern,
                               "roofline": roofline(sb, skern, read_traffic("swa_mfma_window_8k_pmc.txt",
                                                                            source_digest("swa_mfma.hip",
