@@ -1193,7 +1193,8 @@ constexpr int kStateWaves = 10;
 
 template <int DV>
 struct StateRingT {
-    static constexpr int kRing = DV == 64 ? 7 : 12;  // 70 KB / 72 KB: two workgroups per CU
+    static constexpr int kRing = DV == 64 ? 8 : 12;  // 80 KB / 72 KB
+    static constexpr int kGroup = 2;                 // chunks per barrier interval
     alignas(16) uint16_t k[kRing][kC * kDFeat];      // [64][16] row-major
     alignas(16) uint16_t v[kRing][kC * DV];           // [64][DV], 16-byte units XOR-swizzled by row
 };
@@ -1333,38 +1334,50 @@ __device__ __forceinline__ void state_pair(const uint16_t* kh, const uint16_t* v
     float t8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) t8[i] = r == 8 ? 1.f : 0.f;
+    constexpr int G = StateRingT<DV>::kGroup;
     const bool copies = w < kBlocks;
-    const int first = min(kRing - 1, nch);
+    // chunks are taken G per barrier interval (the last group of an odd
+    // chunk count has one); the copies of the chunks up to kRing - G ahead
+    // are in flight meanwhile
+    const int first = min(kRing - G, nch);
     for (int c = 0; c < first; ++c)
         if (copies) state_dma<DV>(kh, vh, ldv, c * kC, rg, c, w, lane);
-    for (int c = 0; c < nch; ++c) {
-        // this wave's copy of chunk c has landed once at most the copies of
-        // the chunks after it are outstanding; the barrier makes every
-        // wave's copy visible and frees the slot of chunk c - 1
-        if (copies) wait_vm(min(kRing - 2, nch - 1 - c));
+    for (int c0 = 0; c0 < nch; c0 += G) {
+        // this wave's copies of chunks c0 .. c0 + G - 1 have landed once at
+        // most the copies of the chunks after them are outstanding; the
+        // barrier makes every wave's copies visible and frees the slots of
+        // the previous group
+        if (copies) wait_vm(min(c0 + kRing - G, nch) - min(c0 + G, nch));
         raw_barrier();
-        if (copies && c + kRing - 1 < nch)
-            state_dma<DV>(kh, vh, ldv, (c + kRing - 1) * kC, rg, (c + kRing - 1) % kRing, w, lane);
-        uint2 kk[2];
-        bf16x8 vb[kNV];
-        state_reads<DV>(rg, c % kRing, 32 * H, g, r, kk, vb);
-        float kv[8];
-        kv[0] = bf16lo_f32(kk[0].x);
-        kv[1] = bf16hi_f32(kk[0].x);
-        kv[2] = bf16lo_f32(kk[0].y);
-        kv[3] = bf16hi_f32(kk[0].y);
-        kv[4] = bf16lo_f32(kk[1].x);
-        kv[5] = bf16hi_f32(kk[1].x);
-        kv[6] = bf16lo_f32(kk[1].y);
-        kv[7] = bf16hi_f32(kk[1].y);
-        const bf16x8 f0 = psi_k<T0>(kv, t8);
 #pragma unroll
-        for (int ct = 0; ct < kNV; ++ct) a0[ct] = mfma32(f0, vb[ct], a0[ct]);
-        a0[kNV] = mfma32(f0, ones, a0[kNV]);
-        const bf16x8 f1 = psi_k<T1>(kv, t8);
+        for (int j = 0; j < G; ++j) {
+            const int cn = c0 + kRing - G + j;
+            if (copies && cn < nch) state_dma<DV>(kh, vh, ldv, cn * kC, rg, cn % kRing, w, lane);
+        }
 #pragma unroll
-        for (int ct = 0; ct < kNV; ++ct) a1[ct] = mfma32(f1, vb[ct], a1[ct]);
-        a1[kNV] = mfma32(f1, ones, a1[kNV]);
+        for (int j = 0; j < G; ++j) {
+            if (c0 + j >= nch) break;
+            uint2 kk[2];
+            bf16x8 vb[kNV];
+            state_reads<DV>(rg, (c0 + j) % kRing, 32 * H, g, r, kk, vb);
+            float kv[8];
+            kv[0] = bf16lo_f32(kk[0].x);
+            kv[1] = bf16hi_f32(kk[0].x);
+            kv[2] = bf16lo_f32(kk[0].y);
+            kv[3] = bf16hi_f32(kk[0].y);
+            kv[4] = bf16lo_f32(kk[1].x);
+            kv[5] = bf16hi_f32(kk[1].x);
+            kv[6] = bf16lo_f32(kk[1].y);
+            kv[7] = bf16hi_f32(kk[1].y);
+            const bf16x8 f0 = psi_k<T0>(kv, t8);
+#pragma unroll
+            for (int ct = 0; ct < kNV; ++ct) a0[ct] = mfma32(f0, vb[ct], a0[ct]);
+            a0[kNV] = mfma32(f0, ones, a0[kNV]);
+            const bf16x8 f1 = psi_k<T1>(kv, t8);
+#pragma unroll
+            for (int ct = 0; ct < kNV; ++ct) a1[ct] = mfma32(f1, vb[ct], a1[ct]);
+            a1[kNV] = mfma32(f1, ones, a1[kNV]);
+        }
     }
     // the H = 1 waves' sums through LDS (the ring is free after the barrier)
     raw_barrier();
@@ -1408,7 +1421,7 @@ __device__ __forceinline__ void init_tile(const float* Sh, const float* zh, int 
 // s < nseg - 1 the increment of segment s into slot s + 1; for s = nseg - 1
 // the caller's initial state (or zeros) into slot 0.
 template <int DV>
-__global__ __launch_bounds__(64 * kStateWaves, 2) void segment_state_kernel(
+__global__ __launch_bounds__(64 * kStateWaves) void segment_state_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int L, int ldv, int ncg, int seg_len, int nseg,
     const float* __restrict__ S, const float* __restrict__ z, int use_init, float* __restrict__ ws) {
     static_assert(sizeof(StateRingT<DV>) >= 5 * 2 * (DV / 16 + 1) * 64 * 16, "exchange area");
