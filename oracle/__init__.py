@@ -56,6 +56,7 @@ def _load():
         lib.oracle_swa.argtypes = [P, P, P, I, I, I, I, I, D, P]
         lib.oracle_swa_cache_fill.argtypes = [P, P, I, I, I, I, I, P, P]
         lib.oracle_la_backward.argtypes = [P, P, P, P, I, I, I, I, D, P, P, P]
+        lib.oracle_la_backward_recurrent.argtypes = [P, P, P, P, I, I, I, I, D, P, P, P]
         lib.oracle_swa_decode_step.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_longlong), I, I, I, I, D,
                                                P, P, P]
         _lib = lib
@@ -209,3 +210,18 @@ def la_backward(q, k, v, dy, eps: float = 1e-6):
     _load().oracle_la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dy), BH, L, d, dv, eps, _ptr(dq), _ptr(dk), _ptr(dvo))
     return dq, dk, dvo
 
+
+def la_backward_recurrent(q, k, v, dy, eps: float = 1e-6):
+    """The gradients of la_backward by the recurrent (feature) form, O(L F dv)
+    per head: a forward sweep with the state S, z and a backward sweep with
+    the sums of phi(q_i) dy_i / D_i over later queries."""
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    *lead, L, d = q.shape
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dvo = np.empty_like(v)
+    _load().oracle_la_backward_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(dy), BH, L, d, dv, eps, _ptr(dq),
+                                         _ptr(dk), _ptr(dvo))
+    return dq, dk, dvo

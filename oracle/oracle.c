@@ -295,3 +295,90 @@ void oracle_la_backward(const double *q, const double *k, const double *v, const
     }
 }
 
+/* J_phi(x)^T u: the gradient of sum_f u_f phi_f(x) with respect to the raw
+ * vector x, for the feature map of oracle_taylor_features (x~ = x d^(-1/4);
+ * d phi_lin[a] / dx_c = pre [a == c]; d phi_quad[a][b] / dx_c =
+ * pre ([a == c] x~_b + [b == c] x~_a) / sqrt(2)). */
+static void taylor_jacobian_t(const double *x, int d, const double *u, double *out) {
+    const double pre = 1.0 / sqrt(sqrt((double)d));
+    const double inv_sqrt2 = 1.0 / sqrt(2.0);
+    for (int c = 0; c < d; ++c) {
+        double acc = u[1 + c];
+        for (int b = 0; b < d; ++b)
+            acc += (u[1 + d + c * d + b] + u[1 + d + b * d + c]) * (x[b] * pre) * inv_sqrt2;
+        out[c] = acc * pre;
+    }
+}
+
+/* The same gradients as oracle_la_backward, by the recurrent (feature) form:
+ * the chain rule through y_i = phi(q_i)^T S_i / (phi(q_i).z_i + eps) with
+ * S_i = sum_{j<=i} phi(k_j) v_j^T, z_i = sum_{j<=i} phi(k_j):
+ *   forward over i:  g_i = dy_i / D_i,  h_i = -(dy_i . y_i) / D_i,
+ *                    dq_i = J_phi(q_i)^T (S_i g_i + h_i z_i);
+ *   backward over j: R_j = sum_{i>=j} phi(q_i) g_i^T,  r_j = sum_{i>=j} phi(q_i) h_i,
+ *                    dk_j = J_phi(k_j)^T (R_j v_j + r_j),  dv_j = R_j^T phi(k_j).
+ * O(L F dv) per head. */
+void oracle_la_backward_recurrent(const double *q, const double *k, const double *v, const double *dy,
+                                  int BH, int L, int d, int dv, double eps,
+                                  double *dq, double *dk, double *dv_out) {
+    const int F = oracle_num_features(d);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < BH; ++h) {
+        const double *qh = q + (size_t)h * L * d;
+        const double *kh = k + (size_t)h * L * d;
+        const double *vh = v + (size_t)h * L * dv;
+        const double *dyh = dy + (size_t)h * L * dv;
+        double *dqh = dq + (size_t)h * L * d;
+        double *dkh = dk + (size_t)h * L * d;
+        double *dvh = dv_out + (size_t)h * L * dv;
+        double *S = (double *)calloc((size_t)F * dv, sizeof(double));
+        double *z = (double *)calloc((size_t)F, sizeof(double));
+        double *phiq = (double *)malloc(sizeof(double) * F);
+        double *phik = (double *)malloc(sizeof(double) * F);
+        double *u = (double *)malloc(sizeof(double) * F);
+        double *y = (double *)malloc(sizeof(double) * dv);
+        double *gN = (double *)malloc(sizeof(double) * (size_t)L * dv);
+        double *gD = (double *)malloc(sizeof(double) * (size_t)L);
+        for (int i = 0; i < L; ++i) {
+            recurrent_token(qh + (size_t)i * d, kh + (size_t)i * d, vh + (size_t)i * dv, d, dv, eps, S, z, y,
+                            phiq, phik);
+            double den = eps;
+            for (int f = 0; f < F; ++f) den += phiq[f] * z[f];
+            double dy_dot_y = 0.0;
+            for (int c = 0; c < dv; ++c) {
+                gN[(size_t)i * dv + c] = dyh[(size_t)i * dv + c] / den;
+                dy_dot_y += dyh[(size_t)i * dv + c] * y[c];
+            }
+            gD[i] = -dy_dot_y / den;
+            for (int f = 0; f < F; ++f) {
+                double acc = gD[i] * z[f];
+                for (int c = 0; c < dv; ++c) acc += S[(size_t)f * dv + c] * gN[(size_t)i * dv + c];
+                u[f] = acc;
+            }
+            taylor_jacobian_t(qh + (size_t)i * d, d, u, dqh + (size_t)i * d);
+        }
+        /* reverse sweep: S and z now hold R and r */
+        memset(S, 0, sizeof(double) * (size_t)F * dv);
+        memset(z, 0, sizeof(double) * (size_t)F);
+        for (int j = L - 1; j >= 0; --j) {
+            oracle_taylor_features(qh + (size_t)j * d, d, phiq);
+            for (int f = 0; f < F; ++f) {
+                z[f] += phiq[f] * gD[j];
+                for (int c = 0; c < dv; ++c) S[(size_t)f * dv + c] += phiq[f] * gN[(size_t)j * dv + c];
+            }
+            oracle_taylor_features(kh + (size_t)j * d, d, phik);
+            for (int f = 0; f < F; ++f) {
+                double acc = z[f];
+                for (int c = 0; c < dv; ++c) acc += S[(size_t)f * dv + c] * vh[(size_t)j * dv + c];
+                u[f] = acc;
+            }
+            taylor_jacobian_t(kh + (size_t)j * d, d, u, dkh + (size_t)j * d);
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int f = 0; f < F; ++f) acc += phik[f] * S[(size_t)f * dv + c];
+                dvh[(size_t)j * dv + c] = acc;
+            }
+        }
+        free(S); free(z); free(phiq); free(phik); free(u); free(y); free(gN); free(gD);
+    }
+}

@@ -105,6 +105,16 @@ void oracle_la_backward(const double *q, const double *k, const double *v, const
                         int BH, int L, int d, int dv, double eps,
                         double *dq, double *dk, double *dv_out);
 
+/* The same gradients by the recurrent (feature) form, O(L F dv) per head:
+ * a forward sweep with S_i, z_i gives D_i, y_i, g_i = dy_i / D_i,
+ * h_i = -(dy_i . y_i) / D_i and dq_i = J_phi(q_i)^T (S_i g_i + h_i z_i); a
+ * backward sweep with R_j = sum_{i>=j} phi(q_i) g_i^T and
+ * r_j = sum_{i>=j} phi(q_i) h_i gives dk_j = J_phi(k_j)^T (R_j v_j + r_j) and
+ * dv_j = R_j^T phi(k_j).  Shapes as oracle_la_backward. */
+void oracle_la_backward_recurrent(const double *q, const double *k, const double *v, const double *dy,
+                                  int BH, int L, int d, int dv, double eps,
+                                  double *dq, double *dk, double *dv_out);
+
 /* Number of OpenMP threads the routines above use. */
 int oracle_num_threads(void);
 

@@ -45,6 +45,14 @@ MUTANTS = {
     "bwd_exclusive_causal": ("for (int j = i; j >= 0; --j) {", "for (int j = i - 1; j >= 0; --j) {"),
     "bwd_dk_from_key": ("dkh[(size_t)j * d + e] += gs * qh[(size_t)i * d + e];",
                         "dkh[(size_t)j * d + e] += gs * kh[(size_t)i * d + e];"),
+    "rbwd_jacobian_one_side": ("acc += (u[1 + d + c * d + b] + u[1 + d + b * d + c]) * (x[b] * pre) * inv_sqrt2;",
+                               "acc += u[1 + d + c * d + b] * (x[b] * pre) * inv_sqrt2;"),
+    "rbwd_jacobian_prescale": ("const double pre = 1.0 / sqrt(sqrt((double)d));", "const double pre = 1.0 / sqrt((double)d);"),
+    "rbwd_dq_no_normaliser": ("double acc = gD[i] * z[f];", "double acc = 0.0 * z[f];"),
+    "rbwd_reverse_exclusive": ("oracle_taylor_features(kh + (size_t)j * d, d, phik);\n            for (int f = 0; f < F; ++f) {\n                double acc = z[f];",
+                               "oracle_taylor_features(kh + (size_t)j * d, d, phik);\n            for (int f = 0; f < F; ++f) {\n                double acc = z[f] - phiq[f] * gD[j];"),
+    "rbwd_dv_from_query": ("for (int f = 0; f < F; ++f) acc += phik[f] * S[(size_t)f * dv + c];",
+                           "for (int f = 0; f < F; ++f) acc += phiq[f] * S[(size_t)f * dv + c];"),
 }
 
 # pins that take only the oracle module
@@ -64,6 +72,8 @@ PIN_FUNCS = [
     lambda m: pins.test_p8_window_decode_continues_window(m, 64, 10),
     lambda m: pins.test_p9_backward_matches_autograd(m, 16, 37, 8),
     pins.test_p9_backward_finite_differences,
+    lambda m: pins.test_p10_recurrent_backward_matches_autograd(m, 16, 37, 8),
+    pins.test_p10_recurrent_backward_equals_closed_form,
     pins.test_hand_taylor_cases,
     pins.test_hand_window_cases,
 ]

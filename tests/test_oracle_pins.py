@@ -365,6 +365,36 @@ def test_p9_backward_finite_differences(oracle_mod):
             assert abs(fd - grads[name][idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grads[name][idx])
 
 
+# ---------------------------------------------------------------- P10
+@pytest.mark.parametrize("d,L,dv", [(16, 37, 8), (8, 20, 16), (16, 2, 4), (24, 9, 5)])
+def test_p10_recurrent_backward_matches_autograd(oracle_mod, d, L, dv):
+    """The recurrent-form backward (forward sweep for dq, reverse sweep for dk
+    and dv) against autograd through the closed-form forward."""
+    rng = _rng(80 + d + L)
+    q = rng.standard_normal((2, 2, L, d))
+    k = rng.standard_normal((2, 2, L, d))
+    v = rng.standard_normal((2, 2, L, dv))
+    dy = rng.standard_normal((2, 2, L, dv))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    (_torch_forward(tq, tk, tv, 1e-6) * torch.from_numpy(dy)).sum().backward()
+    got = oracle_mod.la_backward_recurrent(q, k, v, dy)
+    for g, want in zip(got, (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(g, want.numpy(), rtol=1e-9, atol=1e-10)
+
+
+def test_p10_recurrent_backward_equals_closed_form(oracle_mod):
+    """At a length spanning several 64-token chunks with a ragged tail, the
+    two backward forms agree to rounding."""
+    rng = _rng(90)
+    L, d, dv = 150, 16, 64
+    q = 0.5 * rng.standard_normal((1, 2, L, d))
+    k = 0.5 * rng.standard_normal((1, 2, L, d))
+    v = rng.standard_normal((1, 2, L, dv))
+    dy = rng.standard_normal((1, 2, L, dv))
+    for a, b in zip(oracle_mod.la_backward(q, k, v, dy), oracle_mod.la_backward_recurrent(q, k, v, dy)):
+        np.testing.assert_allclose(b, a, rtol=1e-9, atol=1e-11 * np.abs(a).max())
+
+
 # ---------------------------------------------------------------- P7
 def test_p7_small_logits_approach_softmax(oracle_mod):
     """With q scaled by t -> 0 the Taylor weights approach exp(s); the gap to
