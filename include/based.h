@@ -297,18 +297,32 @@ based_status_t swa_decode_step(const void *q, const void *k, const void *v,
  *   dq, dk [B,H,L,d_feat] fp32 out;  dv [B,H,L,d_v] fp32 out
  *   workspace  required, at least based_prefill_backward_workspace_bytes
  *          (else BASED_E_INVALID); must not overlap anything else
+ *   form   BASED_BACKWARD_AUTO, _DIRECT or _CHUNKED (below); anything else
+ *          is BASED_E_INVALID
  * Supported: d_feat in {8, 16, 24, 32}; d_v in {64, 128}; B*H*ceil(L/64)*256
- * must not exceed INT32_MAX (else BASED_E_INVALID).  Direct form (O(L^2)
- * work per head) on the matrix cores, fp32 accumulation: bf16 inputs with
- * d_feat 16 take bf16 products with the weights split into bf16 hi/lo
- * pairs; every other input takes fp32 products.
+ * must not exceed INT32_MAX (else BASED_E_INVALID).  Two forms, both on the
+ * matrix cores with fp32 accumulation:
+ *   DIRECT   the sums above pair by pair, O(L^2) work per head; bf16 inputs
+ *            with d_feat 16 take bf16 products with the weights split into
+ *            bf16 hi/lo pairs, every other input fp32 products;
+ *   CHUNKED  linear in L through the recurrent form ([1] s2): with the
+ *            prefix state S_i, z_i and the suffix sums
+ *            R_j = sum_{i>=j} phi(q_i) g_i^T, r_j = sum_{i>=j} phi(q_i) h_i,
+ *            dq_i = J(q_i)^T (S_i g_i + h_i z_i), dk_j = J(k_j)^T (R_j v_j + r_j),
+ *            dv_j = R_j^T phi(k_j) (J: the Jacobian of phi), pairs within a
+ *            64-token chunk taken directly; bf16 inputs with d_feat 16 and
+ *            d_v 64 only (else BASED_E_UNSUPPORTED), every non-input operand
+ *            a bf16 hi/lo pair.
+ * AUTO takes CHUNKED where it is supported and L >= 1024, else DIRECT.  The
+ * workspace size covers either form.
  */
+enum { BASED_BACKWARD_AUTO = 0, BASED_BACKWARD_DIRECT = 1, BASED_BACKWARD_CHUNKED = 2 };
 size_t based_prefill_backward_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
 
 based_status_t based_prefill_backward(const void *q, const void *k, const void *v,
                                       const float *dy, based_dtype_t dtype, int B, int H,
-                                      int L, int d_feat, int d_v, float eps, float *dq,
-                                      float *dk, float *dv, void *workspace,
+                                      int L, int d_feat, int d_v, float eps, int form,
+                                      float *dq, float *dk, float *dv, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus

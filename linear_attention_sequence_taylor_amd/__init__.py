@@ -376,9 +376,18 @@ def swa_decode_step(q, k, v, k_cache, v_cache, pos, *, scale: float | None = Non
     return y
 
 
-def based_prefill_backward(q, k, v, dy, *, eps: float = 1e-6, dq=None, dk=None, dv=None, workspace=None):
+_BACKWARD_FORMS = {"auto": 0, "direct": 1, "chunked": 2}
+
+
+def based_prefill_backward(q, k, v, dy, *, eps: float = 1e-6, form: str = "auto", dq=None, dk=None, dv=None,
+                           workspace=None):
     """Gradients (dq, dk, dv), fp32, of based_prefill's output y for the
-    upstream gradient dy [B,H,L,d_v] (fp32), from a zero initial state."""
+    upstream gradient dy [B,H,L,d_v] (fp32), from a zero initial state.
+    ``form``: "direct" (pair by pair, O(L^2)), "chunked" (linear in L through
+    the carried state; bf16, d' = 16, d_v = 64) or "auto" (chunked where it
+    is supported and faster)."""
+    if form not in _BACKWARD_FORMS:
+        raise ValueError(f"form must be one of {sorted(_BACKWARD_FORMS)}")
     _check_tensor("q", q, ndim=4)
     dt = q.dtype
     if dt not in _DTYPES:
@@ -403,7 +412,8 @@ def based_prefill_backward(q, k, v, dy, *, eps: float = 1e-6, dq=None, dk=None, 
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     ws_ptr, ws_bytes = _workspace(workspace, dev)
     st = _lib.lib().based_prefill_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(), _DTYPES[dt], B,
-                                           H, L, d, d_v, eps, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                           H, L, d, d_v, eps, _BACKWARD_FORMS[form], dq.data_ptr(), dk.data_ptr(),
+                                           dv.data_ptr(),
                                            ws_ptr, ws_bytes, _stream_ptr(dev))
     _lib.check("based_prefill_backward", st)
     return dq, dk, dv

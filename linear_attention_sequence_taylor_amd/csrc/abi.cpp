@@ -315,14 +315,25 @@ BASED_API size_t based_prefill_backward_workspace_bytes(int B, int H, int L, int
     uint64_t BH, BHL;
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return 0;
     if (!feat_dim_ok(d_feat) || (d_v != 64 && d_v != 128)) return 0;
-    return based::prefill_backward_workspace_bytes((int)BH, L, d_v);
+    const size_t direct = based::prefill_backward_workspace_bytes((int)BH, L, d_v);
+    if (d_feat == 16 && d_v == 64) {
+        const size_t chunked = based::prefill_backward_chunked_workspace_bytes((int)BH, L);
+        return chunked > direct ? chunked : direct;
+    }
+    return direct;
 }
+
+// The automatic choice takes the chunked form from this length on (where it
+// is the faster one).
+static const int kBackwardChunkedMinL = 1024;
 
 BASED_API based_status_t based_prefill_backward(const void* q, const void* k, const void* v, const float* dy,
                                                 based_dtype_t dtype, int B, int H, int L, int d_feat, int d_v,
-                                                float eps, float* dq, float* dk, float* dv, void* workspace,
-                                                size_t workspace_bytes, void* stream) {
+                                                float eps, int form, float* dq, float* dk, float* dv,
+                                                void* workspace, size_t workspace_bytes, void* stream) {
     if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_E_INVALID;
+    if (form != BASED_BACKWARD_AUTO && form != BASED_BACKWARD_DIRECT && form != BASED_BACKWARD_CHUNKED)
+        return BASED_E_INVALID;
     if (!q || !k || !v || !dy || !dq || !dk || !dv || !workspace) return BASED_E_INVALID;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dy) || !aligned16(dq) || !aligned16(dk) ||
         !aligned16(dv) || !aligned16(workspace))
@@ -334,7 +345,12 @@ BASED_API based_status_t based_prefill_backward(const void* q, const void* k, co
     // one workgroup of 256 threads per 64 rows of a head: the grid's thread
     // count must fit 32 bits
     if (BH * (((uint64_t)L + 63) / 64) * 256 > (uint64_t)INT32_MAX) return BASED_E_INVALID;
-    const uint64_t ws_need = based::prefill_backward_workspace_bytes((int)BH, L, d_v);
+    const bool chunk_ok = dtype == BASED_BF16 && d_feat == 16 && d_v == 64;
+    if (form == BASED_BACKWARD_CHUNKED && !chunk_ok) return BASED_E_UNSUPPORTED;
+    const bool chunked = form == BASED_BACKWARD_CHUNKED || (form == BASED_BACKWARD_AUTO && chunk_ok &&
+                                                            L >= kBackwardChunkedMinL);
+    const uint64_t ws_need = chunked ? based::prefill_backward_chunked_workspace_bytes((int)BH, L)
+                                     : based::prefill_backward_workspace_bytes((int)BH, L, d_v);
     if (workspace_bytes < ws_need) return BASED_E_INVALID;
     const uint64_t es = elem_size(dtype);
     const uint64_t qk_bytes = BHL * d_feat * es, v_bytes = BHL * d_v * es;
@@ -349,6 +365,9 @@ BASED_API based_status_t based_prefill_backward(const void* q, const void* k, co
         for (int b = 0; b < 4; ++b)
             if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return BASED_E_INVALID;
     }
+    if (chunked)
+        return launch_status(based::launch_prefill_backward_chunked(q, k, v, dy, (int)BH, L, eps, dq, dk, dv,
+                                                                    workspace, static_cast<hipStream_t>(stream)));
     return launch_status(based::launch_prefill_backward(q, k, v, dy, dtype == BASED_BF16, (int)BH, L, d_feat, d_v,
                                                         eps, dq, dk, dv, workspace,
                                                         static_cast<hipStream_t>(stream)));

@@ -68,8 +68,9 @@ hipError_t launch_swa_decode_step(const void* q, const void* k, const void* v, b
 hipError_t launch_swa_cache_fill(const void* k, const void* v, bool bf16, int BH, int L, int dqk, int dv,
                                  int window, void* kc, void* vc, hipStream_t st);
 
-// Gradients of the prefill output (prefill_backward.hip), fp32 on the vector
-// ALUs; the workspace holds BH*L*(dv+1) floats.
+// Gradients of the prefill output, direct (quadratic) form
+// (prefill_backward.hip: fp32 inputs or feature dims other than 16, on the
+// fp32 matrix cores); the workspace holds BH*L*(dv+1) floats.
 size_t prefill_backward_workspace_bytes(int BH, int L, int dv);
 // The same on the matrix cores for bf16 inputs with feature dim 16
 // (prefill_backward_mfma.hip); g_ws / h_ws as above.
@@ -79,5 +80,13 @@ hipError_t launch_prefill_backward_mfma(const void* q, const void* k, const void
 hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, const float* dy, bool bf16, int BH,
                                    int L, int d, int dv_dim, float eps, float* dq, float* dk, float* dv,
                                    void* workspace, hipStream_t st);
+// The same gradients in linear time through the carried state
+// (prefill_backward_mfma.hip, chunked form): bf16 inputs, feature dim 16,
+// dv 64.  The workspace starts with the direct form's g and h and adds two
+// sets of per-segment states when a head is split into segments.
+size_t prefill_backward_chunked_workspace_bytes(int BH, int L);
+hipError_t launch_prefill_backward_chunked(const void* q, const void* k, const void* v, const float* dy, int BH,
+                                           int L, float eps, float* dq, float* dk, float* dvo, void* workspace,
+                                           hipStream_t st);
 
 }  // namespace based

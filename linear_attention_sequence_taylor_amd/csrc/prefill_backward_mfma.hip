@@ -30,6 +30,8 @@
 // Only the diagonal tile needs the causal mask; rows past L are staged as
 // zeros (their g and h are zero, so they add nothing on the key side) and
 // never stored.
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -509,6 +511,684 @@ __global__ __launch_bounds__(256) void bwd_key_mfma_kernel(const uint16_t* __res
     }
 }
 
+// ================================================================ chunked form
+// The same gradients in time linear in L, through the recurrent form of the
+// output ("Simple linear attention language models balance the
+// recall-throughput tradeoff", s2 "Preliminaries": the prefix state
+// S_i = sum_{j<=i} phi(k_j) v_j^T, z_i = sum_{j<=i} phi(k_j)):
+//   dq_i = J(q_i)^T (S_i g_i + h_i z_i),
+//   dk_j = J(k_j)^T (R_j v_j + r_j),   dv_j = R_j^T phi(k_j),
+// with R_j = sum_{i>=j} phi(q_i) g_i^T and r_j = sum_{i>=j} phi(q_i) h_i.
+// Pairs inside one 64-token chunk are the direct form's diagonal tile
+// (q_pass1, q_pass2 and k_tile above); the carried state stands for the
+// earlier chunks (S, z) or the later ones (R, r).
+//
+// Features are the symmetric monomials m(x) of the raw 16-vector x, in ten
+// rotation tiles of 16 rows (slot (t, r)):
+//   t = 0: x_r^2;  t = 1..7: x_r x_((r+t) mod 16);  t = 8: x_r x_(r+8) on
+//   rows r < 8, the constant 1 on row 8, nothing on rows 9..15;  t = 9: x_r.
+// Each unordered pair a != b appears once (one of (b - a) mod 16 and its
+// complement lies in 1..8).  With the coefficients c = 1/32 (squares), 1/16
+// (pairs), 1/4 (linear terms) and 1 (constant), sum_f c_f m_f(q) m_f(k) is
+// 1 + s + s^2/2 for s = q.k/4.  The states hold raw monomial sums; the
+// coefficients, powers of two and so exact, are applied when a state is
+// published to LDS (S^c = c S, z^c = c z and likewise for R, r).  Then
+// y_i D_i = m(q_i) S^c + intra, D_i = m(q_i) z^c + intra + eps, and
+// J(q)^T (S g + h z) above becomes J_m(q)^T (S^c g + h z^c) with J_m the
+// Jacobian of the raw monomials (likewise for k with R^c, r^c).
+//
+// Three products on the matrix cores (16x16x32 bf16, fp32 accumulation):
+//   update       state += m(X)^T M over a chunk's tokens (M = V or g): lane
+//                (g, r) builds feature row r for 8 tokens of a k-step from a
+//                transposed read of X and its DPP row rotations;
+//   readout      Y = m(X) S^c for a wave's 16 tokens (A = the lane's token's
+//                features, B = the published state);
+//   contraction  U = M S^c^T (A = rows of M, B = the published state by
+//                transposed reads), then J_m^T U on the vector ALUs with DPP
+//                row rotations (lane r = feature row r = component r).
+// Every operand that is not an exact bf16 input is a bf16 hi/lo pair
+// (features, g, published states): with single bf16 operands the gradients
+// of early tokens, where D is small, miss the tolerance.
+//
+// Launches (segments of cps chunks; one workgroup per (segment, head)):
+//   1. segment sums of m(k) v^T and m(k) (every segment but the last);
+//   2. exclusive prefix over the segments: S, z at each segment start;
+//   3. query sweep, chunk by chunk: y and D, g and h (to the workspace), dq;
+//   4. segment sums of m(q) g^T and m(q) h (every segment but the first);
+//   5. exclusive suffix over the segments: R, r after each segment;
+//   6. key sweep, last chunk first: dk, dv.
+// With one segment per head, 1, 2, 4 and 5 are skipped.
+constexpr int kNTile = 10;
+constexpr int kSlot = 16 * kNTile;                   // 160 state rows
+constexpr int kStateFloats = kSlot * 64 + kSlot;     // one (segment, head) state, d_v = 64
+
+// Value of lane (r - N) mod 16 of this lane's 16-lane row (1 <= N <= 15).
+template <int N>
+__device__ __forceinline__ float ror16(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
+// Coefficient of slot (t, row).
+__device__ __forceinline__ float slot_coef(int t, int row) {
+    if (t == 0) return 1.f / 32.f;
+    if (t < 8) return 1.f / 16.f;
+    if (t == 9) return 0.25f;
+    return row < 8 ? 1.f / 16.f : (row == 8 ? 1.f : 0.f);
+}
+// Published position of slot (t, row): the readout's k-step J covers tiles
+// 2J and 2J + 1, its k = 8g + i being row 4g + (i & 3) of tile 2J + (i >> 2).
+__device__ __forceinline__ int slot_pos(int t, int row) {
+    return 32 * (t >> 1) + 8 * (row >> 2) + 4 * (t & 1) + (row & 3);
+}
+// LDS offset (bf16 elements) of (value column c, position p) in a published
+// plane: rows of 160, 16-byte units XOR-swizzled by bits 2..3 of c, so that
+// the readout's 16-byte reads (16 columns, one unit), the contraction's
+// transposed reads (4 columns x 4 units) and the publish writes (16
+// columns) each hit 16 distinct 4-bank groups.
+__device__ __forceinline__ int pub_at(int c, int p) {
+    return c * kSlot + ((((p >> 3) ^ ((c >> 2) & 3))) << 3) + (p & 7);
+}
+
+// A state published for the readout and the contraction.
+struct PubState {
+    alignas(16) uint16_t hi[64 * kSlot];
+    alignas(16) uint16_t lo[64 * kSlot];
+    alignas(16) uint16_t zhi[kSlot];  // normaliser, position order
+    alignas(16) uint16_t zlo[kSlot];
+    alignas(16) float z[kSlot];
+};
+
+// ---- update: feature rows of one tile for 8 tokens (x[i] = x_r of token i)
+template <int T>
+__device__ __forceinline__ void mono_rows(const float (&x)[8], int r, float (&a)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if constexpr (T == 0) {
+            a[i] = x[i] * x[i];
+        } else if constexpr (T < 8) {
+            a[i] = x[i] * ror16<16 - T>(x[i]);
+        } else if constexpr (T == 8) {
+            const float p = x[i] * ror16<8>(x[i]);
+            a[i] = r < 8 ? p : (r == 8 ? 1.f : 0.f);
+        } else {
+            a[i] = x[i];
+        }
+    }
+}
+
+__device__ __forceinline__ void unpack_b8(const bf16x8& b, float (&x)[8]) {
+    const u32x4 u = __builtin_bit_cast(u32x4, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16lo_f32(u[i]);
+        x[2 * i + 1] = bf16hi_f32(u[i]);
+    }
+}
+
+// One tile T of the update at k-step ks: acc[ct] += m(X)_T^T M for the
+// column tiles [CT0, CT0 + NCT), and zacc += sum_i m_i w_i (if ZSUM).
+template <int T, int CT0, int NCT, bool MHILO, bool ZSUM>
+__device__ __forceinline__ void update_tile(const float (&x)[8], const float (&w8)[8], const bf16x8 (&bh)[4],
+                                            const bf16x8 (&bl)[4], int r, f32x4* acc, float& zacc) {
+    float a[8];
+    mono_rows<T>(x, r, a);
+    if constexpr (ZSUM) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) zacc = fmaf(a[i], w8[i], zacc);
+    }
+    bf16x8 ah, al;
+    hilo8(a, ah, al);
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+        acc[j] = mfma32(ah, bh[CT0 + j], acc[j]);
+        acc[j] = mfma32(al, bh[CT0 + j], acc[j]);
+        if constexpr (MHILO) acc[j] = mfma32(ah, bl[CT0 + j], acc[j]);
+    }
+}
+
+// The update of wave W over one staged chunk (d_v = 64).  Wave W owns
+// tiles 2W and 2W + 1 at every column tile (acc[0..3], acc[4..7]) and tile
+// 8 + W/2 at column tiles 2(W%2), 2(W%2) + 1 (acc[8], acc[9]); zacc[0..2]
+// are the matching normaliser rows (the third only on even W, so that each
+// row is summed once).  X is [64][16] in tile_at<16> layout, M [64][64] in
+// tile_at<64> layout (hi, and lo if MHILO); token weights wtok (the
+// normaliser's per-token factor) come from LDS if given, else they are the
+// validity of the chunk's tokens (t0 + token < L).
+template <int W, bool MHILO>
+__device__ __forceinline__ void update_wave(const uint16_t* xt, const uint16_t* mhi, const uint16_t* mlo,
+                                            const float* wtok, int t0, int L, int g, int r, f32x4 (&acc)[10],
+                                            float (&zacc)[3]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        float x[8], w8[8];
+        unpack_b8(tr_b8<kD>(xt, 32 * ks, 0, g, r), x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int tok = 32 * ks + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
+            w8[i] = wtok ? wtok[tok] : (t0 + tok < L ? 1.f : 0.f);
+        }
+        bf16x8 bh[4], bl[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            bh[ct] = tr_b8<64>(mhi, 32 * ks, 16 * ct, g, r);
+            if constexpr (MHILO) bl[ct] = tr_b8<64>(mlo, 32 * ks, 16 * ct, g, r);
+        }
+        update_tile<2 * W, 0, 4, MHILO, true>(x, w8, bh, bl, r, &acc[0], zacc[0]);
+        update_tile<2 * W + 1, 0, 4, MHILO, true>(x, w8, bh, bl, r, &acc[4], zacc[1]);
+        update_tile<8 + W / 2, 2 * (W % 2), 2, MHILO, W % 2 == 0>(x, w8, bh, bl, r, &acc[8], zacc[2]);
+    }
+}
+template <bool MHILO>
+__device__ __forceinline__ void update_any(int w, const uint16_t* xt, const uint16_t* mhi, const uint16_t* mlo,
+                                           const float* wtok, int t0, int L, int g, int r, f32x4 (&acc)[10],
+                                           float (&zacc)[3]) {
+    switch (w) {
+        case 0: update_wave<0, MHILO>(xt, mhi, mlo, wtok, t0, L, g, r, acc, zacc); break;
+        case 1: update_wave<1, MHILO>(xt, mhi, mlo, wtok, t0, L, g, r, acc, zacc); break;
+        case 2: update_wave<2, MHILO>(xt, mhi, mlo, wtok, t0, L, g, r, acc, zacc); break;
+        default: update_wave<3, MHILO>(xt, mhi, mlo, wtok, t0, L, g, r, acc, zacc); break;
+    }
+}
+
+// Tile t and column tile ct of the acc index j of wave w (see update_wave).
+__device__ __forceinline__ int acc_tile(int w, int j) { return j < 8 ? 2 * w + (j >> 2) : 8 + (w >> 1); }
+__device__ __forceinline__ int acc_ct(int w, int j) { return j < 8 ? (j & 3) : 2 * (w & 1) + (j - 8); }
+__device__ __forceinline__ int z_tile(int w, int i) { return i < 2 ? 2 * w + i : 8 + (w >> 1); }
+__device__ __forceinline__ bool z_owned(int w, int i) { return i < 2 || (w & 1) == 0; }
+
+// Publish the wave's part of the state (times the slot coefficients) as
+// bf16 hi/lo planes, and its normaliser rows (the lane-group partial sums
+// added up) in fp32 and hi/lo.
+__device__ __forceinline__ void publish_state(int w, const f32x4 (&acc)[10], const float (&zacc)[3], PubState& ps,
+                                              int g, int r) {
+#pragma unroll
+    for (int j = 0; j < 10; ++j) {
+        const int t = acc_tile(w, j), ct = acc_ct(w, j);
+        float v[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) v[m] = slot_coef(t, 4 * g + m) * acc[j][m];
+        const uint32_t h0 = pack_bf16x2(v[0], v[1]), h1 = pack_bf16x2(v[2], v[3]);
+        const int off = pub_at(16 * ct + r, 32 * (t >> 1) + 8 * g + 4 * (t & 1));
+        *reinterpret_cast<uint2*>(&ps.hi[off]) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(&ps.lo[off]) = make_uint2(lo_pair_of(h0, v[0], v[1]), lo_pair_of(h1, v[2], v[3]));
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        float zt = zacc[i] + __shfl_xor(zacc[i], 16, 64);
+        zt += __shfl_xor(zt, 32, 64);
+        if (g == 0 && z_owned(w, i)) {
+            const int t = z_tile(w, i), p = slot_pos(t, r);
+            const float zc = slot_coef(t, r) * zt;
+            const uint32_t hp = pack_bf16x2(zc, 0.f);
+            ps.z[p] = zc;
+            ps.zhi[p] = (uint16_t)(hp & 0xffffu);
+            ps.zlo[p] = (uint16_t)(lo_pair_of(hp, zc, 0.f) & 0xffffu);
+        }
+    }
+}
+
+// A (segment, head) state in the workspace: raw sums S[f][c] (f = 16t + row)
+// then z[f], fp32.
+__device__ __forceinline__ void state_load(int w, const float* slot, int g, int r, f32x4 (&acc)[10],
+                                           float (&zacc)[3]) {
+#pragma unroll
+    for (int j = 0; j < 10; ++j) {
+        const int t = acc_tile(w, j), ct = acc_ct(w, j);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[j][m] = slot ? slot[(16 * t + 4 * g + m) * 64 + 16 * ct + r] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        zacc[i] = slot && g == 0 && z_owned(w, i) ? slot[kSlot * 64 + 16 * z_tile(w, i) + r] : 0.f;
+}
+__device__ __forceinline__ void state_store(int w, const f32x4 (&acc)[10], const float (&zacc)[3], float* slot,
+                                            int g, int r) {
+#pragma unroll
+    for (int j = 0; j < 10; ++j) {
+        const int t = acc_tile(w, j), ct = acc_ct(w, j);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) slot[(16 * t + 4 * g + m) * 64 + 16 * ct + r] = acc[j][m];
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        float zt = zacc[i] + __shfl_xor(zacc[i], 16, 64);
+        zt += __shfl_xor(zt, 32, 64);
+        if (g == 0 && z_owned(w, i)) slot[kSlot * 64 + 16 * z_tile(w, i) + r] = zt;
+    }
+}
+
+// ---- readout: Y (rows = the wave's tokens 4g + m, columns 16ct + r) +=
+// m(x) S^c, and D - eps += m(x) z^c (every column) if WITH_D.
+// xr[j] = x_((j + 4g) mod 16) of the lane's token (row r of the wave).
+template <int J>
+__device__ __forceinline__ void mono_readout(const float (&xr)[16], int g, float (&a)[8]) {
+    constexpr int T0 = 2 * J, T1 = 2 * J + 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (T0 == 0) a[i] = xr[i] * xr[i];
+        else if constexpr (T0 < 8) a[i] = xr[i] * xr[i + T0];
+        else a[i] = g < 2 ? xr[i] * xr[i + 8] : ((g == 2 && i == 0) ? 1.f : 0.f);
+        if constexpr (T1 < 8) a[4 + i] = xr[i] * xr[i + T1];
+        else a[4 + i] = xr[i];
+    }
+}
+template <int J, bool WITH_D>
+__device__ __forceinline__ void readout_step(const PubState& ps, const float (&xr)[16], int g, int r,
+                                             f32x4 (&y)[4], f32x4& dsum) {
+    float a[8];
+    mono_readout<J>(xr, g, a);
+    bf16x8 ah, al;
+    hilo8(a, ah, al);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        const int off = pub_at(16 * ct + r, 32 * J + 8 * g);
+        const bf16x8 bh = ld8(&ps.hi[off]), bl = ld8(&ps.lo[off]);
+        y[ct] = mfma32(ah, bh, y[ct]);
+        y[ct] = mfma32(al, bh, y[ct]);
+        y[ct] = mfma32(ah, bl, y[ct]);
+    }
+    if constexpr (WITH_D) {
+        const bf16x8 zh = ld8(&ps.zhi[32 * J + 8 * g]), zl = ld8(&ps.zlo[32 * J + 8 * g]);
+        dsum = mfma32(ah, zh, dsum);
+        dsum = mfma32(al, zh, dsum);
+        dsum = mfma32(ah, zl, dsum);
+    }
+}
+template <bool WITH_D>
+__device__ __forceinline__ void readout(const PubState& ps, const float (&xr)[16], int g, int r, f32x4 (&y)[4],
+                                        f32x4& dsum) {
+    readout_step<0, WITH_D>(ps, xr, g, r, y, dsum);
+    readout_step<1, WITH_D>(ps, xr, g, r, y, dsum);
+    readout_step<2, WITH_D>(ps, xr, g, r, y, dsum);
+    readout_step<3, WITH_D>(ps, xr, g, r, y, dsum);
+    readout_step<4, WITH_D>(ps, xr, g, r, y, dsum);
+}
+
+// ---- contraction and Jacobian
+// B operand of U = M S^c^T for tile T and k-step cs: lane (g, c16) gets
+// columns 32cs + 8g + i of slot (T, c16).  Each transposed read hands lane
+// c16 rows j = 0..3 of the element that lane 4j + c16/4 addressed at its
+// position c16 % 4, so lane 4j + q addresses column c0 + j at the four
+// consecutive positions of slots (T, 4q .. 4q + 3).
+__device__ __forceinline__ bf16x8 pub_tr(const uint16_t* plane, int T, int cs, int g, int c16) {
+    const int j = c16 >> 2, qq = c16 & 3;
+    const int c0 = 32 * cs + 8 * g + j, p = 32 * (T >> 1) + 8 * qq + 4 * (T & 1);
+    const uint2 a = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(BWD_LDS(s16x4, plane + pub_at(c0, p))));
+    const uint2 b = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(BWD_LDS(s16x4, plane + pub_at(c0 + 4, p))));
+    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
+// dx[m] += J_m(x)^T u for tile T: lane (g, r) holds u[m] at slot (T, r) of
+// token 4g + m and xj[m] = x_r of that token; dx[m] is component r.
+template <int T>
+__device__ __forceinline__ void jac_tile(const f32x4& u, const float (&xj)[4], int r, float (&dx)[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float uu = u[m];
+        if constexpr (T == 0) {
+            dx[m] = fmaf(2.f * xj[m], uu, dx[m]);
+        } else if constexpr (T < 8) {
+            // x_r x_(r+T): d/dx_r = x_(r+T) here, d/dx_(r+T) = x_r moved T lanes on
+            dx[m] = fmaf(ror16<16 - T>(xj[m]), uu, dx[m]);
+            dx[m] += ror16<T>(xj[m] * uu);
+        } else if constexpr (T == 8) {
+            const float u8 = r < 8 ? uu : 0.f;
+            dx[m] = fmaf(ror16<8>(xj[m]), u8, dx[m]);
+            dx[m] += ror16<8>(xj[m] * u8);
+        } else {
+            dx[m] += uu;
+        }
+    }
+}
+
+template <int T, bool AHILO>
+__device__ __forceinline__ void contract_tile(const PubState& ps, const bf16x8 (&ah)[2], const bf16x8 (&al)[2],
+                                              const float (&zw)[4], const float (&xj)[4], int g, int r,
+                                              float (&dx)[4]) {
+    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+        const bf16x8 bh = pub_tr(ps.hi, T, cs, g, r), bl = pub_tr(ps.lo, T, cs, g, r);
+        u = mfma32(ah[cs], bh, u);
+        u = mfma32(ah[cs], bl, u);
+        if constexpr (AHILO) u = mfma32(al[cs], bh, u);
+    }
+    const float zc = ps.z[slot_pos(T, r)];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) u[m] = fmaf(zw[m], zc, u[m]);
+    jac_tile<T>(u, xj, r, dx);
+}
+// dx += J_m^T (M S^c^T + zw z^c) over all ten tiles.  M's rows are the
+// wave's tokens: ah/al[cs] = M[row r][32cs + 8g .. +7] (hi/lo if AHILO).
+template <bool AHILO, int... Ts>
+__device__ __forceinline__ void contract_all(std::integer_sequence<int, Ts...>, const PubState& ps,
+                                             const bf16x8 (&ah)[2], const bf16x8 (&al)[2], const float (&zw)[4],
+                                             const float (&xj)[4], int g, int r, float (&dx)[4]) {
+    (contract_tile<Ts, AHILO>(ps, ah, al, zw, xj, g, r, dx), ...);
+}
+
+// This lane's token row x[16] rotated by 4g (xr[j] = x_((j + 4g) mod 16)),
+// zero past L; and x_r of tokens base + 4g + m.
+__device__ __forceinline__ void token_rows(const uint16_t* xh, int tok, int base, int L, int g, int r,
+                                           float (&xr)[16], float (&xj)[4]) {
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+        uint2 u = make_uint2(0u, 0u);
+        if (tok < L) u = *reinterpret_cast<const uint2*>(xh + (size_t)tok * kD + 4 * ((pp + g) & 3));
+        xr[4 * pp] = bf16lo_f32(u.x);
+        xr[4 * pp + 1] = bf16hi_f32(u.x);
+        xr[4 * pp + 2] = bf16lo_f32(u.y);
+        xr[4 * pp + 3] = bf16hi_f32(u.y);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int t = base + 4 * g + m;
+        xj[m] = t < L ? bf16_bits_to_f32(xh[(size_t)t * kD + r]) : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------- segment sums
+// Launch 1 (KEYS: m(k) v^T, m(k) over the valid tokens) or 4 (m(q) g^T,
+// m(q) h) for segments seg0 .. seg0 + gridDim.x/BH - 1.
+template <bool KEYS>
+__global__ __launch_bounds__(256) void bwd_segsum_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ mhi,
+                                                         const uint16_t* __restrict__ mlo,
+                                                         const float* __restrict__ hw, int BH, int L, int nch,
+                                                         int cps, int seg0, float* __restrict__ states) {
+    __shared__ BwdKSmem<64> sm;  // q: X, ghi/glo: M, h: token weights
+    const int head = blockIdx.x % BH, seg = seg0 + (int)(blockIdx.x / BH);
+    const int c_begin = seg * cps, c_end = min(nch, c_begin + cps);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const uint16_t* xh = x + (size_t)head * L * kD;
+    const uint16_t* mh = mhi + (size_t)head * L * 64;
+    const uint16_t* ml = KEYS ? nullptr : mlo + (size_t)head * L * 64;
+    const float* hh = KEYS ? nullptr : hw + (size_t)head * L;
+    f32x4 acc[10];
+    float zacc[3];
+    state_load(w, nullptr, g, r, acc, zacc);
+    TileRegs<kD> xreg;
+    TileRegs<64> mreg, lreg;
+    float hreg = 0.f;
+    auto load = [&](int c) {
+        xreg.load(xh, L, c * kT);
+        mreg.load(mh, L, c * kT);
+        if (!KEYS) {
+            lreg.load(ml, L, c * kT);
+            if (threadIdx.x < kT) hreg = c * kT + (int)threadIdx.x < L ? hh[c * kT + threadIdx.x] : 0.f;
+        }
+    };
+    load(c_begin);
+    for (int c = c_begin; c < c_end; ++c) {
+        __syncthreads();
+        xreg.store(sm.q);
+        mreg.store(sm.ghi);
+        if (!KEYS) {
+            lreg.store(sm.glo);
+            if (threadIdx.x < kT) sm.h[threadIdx.x] = hreg;
+        }
+        __syncthreads();
+        if (c + 1 < c_end) load(c + 1);
+        update_any<!KEYS>(w, sm.q, sm.ghi, sm.glo, KEYS ? nullptr : sm.h, c * kT, L, g, r, acc, zacc);
+    }
+    state_store(w, acc, zacc, states + ((size_t)seg * BH + head) * kStateFloats, g, r);
+}
+
+// Launches 2 and 5: each (segment, head) state becomes the sum of the
+// states of the segments before it (REVERSE: after it).  Segments without
+// a sum of their own (the last one forward, the first one in reverse)
+// count as zero.
+__global__ __launch_bounds__(256) void bwd_scan_kernel(float* __restrict__ states, int BH, int nseg, int reverse) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)BH * kStateFloats) return;
+    const size_t head = i / kStateFloats, e = i % kStateFloats;
+    float run = 0.f;
+    for (int n = 0; n < nseg; ++n) {
+        const int s = reverse ? nseg - 1 - n : n;
+        float* p = states + ((size_t)s * BH + head) * kStateFloats + e;
+        const bool has = reverse ? s > 0 : s < nseg - 1;
+        const float xv = has ? *p : 0.f;
+        *p = run;
+        run += xv;
+    }
+}
+
+// ---------------------------------------------------------------- query sweep
+struct QSweepSmem {
+    BwdQSmem<64> t;
+    PubState s;
+};
+
+__global__ __launch_bounds__(256) void bwd_qsweep_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v,
+                                                         const float* __restrict__ dy, int BH, int L, int nch,
+                                                         int cps, float eps, const float* __restrict__ s_init,
+                                                         float* __restrict__ dq, uint16_t* __restrict__ ghi_ws,
+                                                         uint16_t* __restrict__ glo_ws, float* __restrict__ h_ws) {
+    constexpr int DV = 64, kNV = 4;
+    __shared__ QSweepSmem sm;
+    const int head = blockIdx.x % BH, seg = blockIdx.x / BH;
+    const int c_begin = seg * cps, c_end = min(nch, c_begin + cps);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const uint16_t* qh = q + (size_t)head * L * kD;
+    const uint16_t* kh = k + (size_t)head * L * kD;
+    const uint16_t* vh = v + (size_t)head * L * DV;
+
+    f32x4 acc[10];
+    float zacc[3];
+    state_load(w, s_init && seg > 0 ? s_init + ((size_t)seg * BH + head) * kStateFloats : nullptr, g, r, acc, zacc);
+    TileRegs<kD> kreg;
+    TileRegs<DV> vreg;
+    kreg.load(kh, L, c_begin * kT);
+    vreg.load(vh, L, c_begin * kT);
+    kreg.store(sm.t.k);
+    vreg.store(sm.t.v);
+    publish_state(w, acc, zacc, sm.s, g, r);
+    __syncthreads();
+    for (int c = c_begin; c < c_end; ++c) {
+        const int t0 = c * kT;
+        if (c + 1 < c_end) {
+            kreg.load(kh, L, t0 + kT);
+            vreg.load(vh, L, t0 + kT);
+        }
+        const int qw0 = t0 + 16 * w;  // first query of this wave
+        const int qr = qw0 + r;       // this lane's query in score tiles and the readout
+        bf16x4 qb = __builtin_bit_cast(bf16x4, make_uint2(0u, 0u));
+        if (qr < L) qb = quarter(*reinterpret_cast<const uint2*>(qh + (size_t)qr * kD + 4 * g));
+        float xr[16], xj[4];
+        token_rows(qh, qr, qw0, L, g, r, xr, xj);
+
+        // y D and D: the chunk's own keys (diagonal tile), then the state
+        f32x4 yacc[kNV];
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) yacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 dsum = {0.f, 0.f, 0.f, 0.f};
+        q_pass1<DV, true>(sm.t, qb, w, g, r, yacc, dsum);
+        readout<true>(sm.s, xr, g, r, yacc, dsum);
+
+        // g = dy/D, h = -(dy.y D)/D^2 (rows qw0 + 4g + m, columns 16ct + r)
+        float dyv[4][kNV];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int qi = qw0 + 4 * g + m;
+            const float* dyr = dy + ((size_t)head * L + min(qi, L - 1)) * DV + r;
+#pragma unroll
+            for (int ct = 0; ct < kNV; ++ct) dyv[m][ct] = dyr[16 * ct];
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int qi = qw0 + 4 * g + m;
+            const float inv = 1.f / (dsum[m] + eps);
+            float dyy = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < kNV; ++ct) {
+                const float dyc = qi < L ? dyv[m][ct] : 0.f;
+                dyy = fmaf(dyc, yacc[ct][m], dyy);
+                const float gv = dyc * inv;
+                const uint32_t hb = pack_bf16x2(gv, 0.f);
+                sm.t.ghi[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(hb & 0xffffu);
+                sm.t.glo[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(lo_pair_of(hb, gv, 0.f) & 0xffffu);
+            }
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) dyy += __shfl_xor(dyy, off, 64);
+            const float hq = -dyy * inv * inv;
+            if (r == 0) {
+                sm.t.h[w][4 * g + m] = hq;
+                if (qi < L) h_ws[(size_t)head * L + qi] = hq;
+            }
+        }
+        __syncthreads();
+        {
+            constexpr int kU = DV / 8;
+            for (int e = lane; e < 16 * kU; e += 64) {
+                const int row = e / kU, u = e % kU;
+                const int qi = qw0 + row;
+                if (qi < L) {
+                    const size_t off = ((size_t)head * L + qi) * DV + 8 * u;
+                    *reinterpret_cast<u32x4*>(ghi_ws + off) =
+                        *reinterpret_cast<const u32x4*>(&sm.t.ghi[w][tile_at<DV>(row, 8 * u)]);
+                    *reinterpret_cast<u32x4*>(glo_ws + off) =
+                        *reinterpret_cast<const u32x4*>(&sm.t.glo[w][tile_at<DV>(row, 8 * u)]);
+                }
+            }
+        }
+
+        // dq: the state part J_m^T (S^c g + h z^c), then the diagonal tile
+        bf16x8 gah[2], gal[2];
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+            gah[cs] = ld8(&sm.t.ghi[w][tile_at<DV>(r, 32 * cs + 8 * g)]);
+            gal[cs] = ld8(&sm.t.glo[w][tile_at<DV>(r, 32 * cs + 8 * g)]);
+        }
+        float hz[4], dx[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) hz[m] = sm.t.h[w][4 * g + m];
+        contract_all<true>(std::make_integer_sequence<int, kNTile>{}, sm.s, gah, gal, hz, xj, g, r, dx);
+        f32x4 dqacc = {0.f, 0.f, 0.f, 0.f};
+        q_pass2<DV, true>(sm.t, qb, w, g, r, dqacc);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int qi = qw0 + 4 * g + m;
+            if (qi < L) dq[((size_t)head * L + qi) * kD + r] = fmaf(0.25f, dqacc[m], dx[m]);
+        }
+
+        // the state after this chunk
+        update_any<false>(w, sm.t.k, sm.t.v, nullptr, nullptr, t0, L, g, r, acc, zacc);
+        __syncthreads();
+        if (c + 1 < c_end) {
+            kreg.store(sm.t.k);
+            vreg.store(sm.t.v);
+            publish_state(w, acc, zacc, sm.s, g, r);
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- key sweep
+struct KSweepSmem {
+    BwdKSmem<64> t;
+    PubState s;
+};
+
+__global__ __launch_bounds__(256) void bwd_ksweep_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v, int BH, int L, int nch,
+                                                         int cps, const uint16_t* __restrict__ ghi_ws,
+                                                         const uint16_t* __restrict__ glo_ws,
+                                                         const float* __restrict__ h_ws,
+                                                         const float* __restrict__ r_init, float* __restrict__ dk,
+                                                         float* __restrict__ dvo) {
+    constexpr int DV = 64, kNV = 4;
+    __shared__ KSweepSmem sm;
+    const int head = blockIdx.x % BH, seg = blockIdx.x / BH;
+    const int nseg = (nch + cps - 1) / cps;
+    const int c_begin = seg * cps, c_end = min(nch, c_begin + cps);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const uint16_t* qh = q + (size_t)head * L * kD;
+    const uint16_t* kh = k + (size_t)head * L * kD;
+    const uint16_t* vh = v + (size_t)head * L * DV;
+    const uint16_t* gh = ghi_ws + (size_t)head * L * DV;
+    const uint16_t* gl = glo_ws + (size_t)head * L * DV;
+    const float* hh = h_ws + (size_t)head * L;
+
+    f32x4 acc[10];
+    float zacc[3];
+    state_load(w, r_init && seg < nseg - 1 ? r_init + ((size_t)seg * BH + head) * kStateFloats : nullptr, g, r, acc,
+               zacc);
+    TileRegs<kD> qreg;
+    TileRegs<DV> ghreg, glreg;
+    float hreg = 0.f;
+    auto load = [&](int c) {
+        qreg.load(qh, L, c * kT);
+        ghreg.load(gh, L, c * kT);
+        glreg.load(gl, L, c * kT);
+        if (threadIdx.x < kT) hreg = c * kT + (int)threadIdx.x < L ? hh[c * kT + threadIdx.x] : 0.f;
+    };
+    auto store = [&]() {
+        qreg.store(sm.t.q);
+        ghreg.store(sm.t.ghi);
+        glreg.store(sm.t.glo);
+        if (threadIdx.x < kT) sm.t.h[threadIdx.x] = hreg;
+    };
+    load(c_end - 1);
+    store();
+    publish_state(w, acc, zacc, sm.s, g, r);
+    __syncthreads();
+    for (int c = c_end - 1; c >= c_begin; --c) {
+        const int t0 = c * kT;
+        if (c > c_begin) load(c - 1);
+        const int kw0 = t0 + 16 * w;  // first key of this wave
+        const int kr = kw0 + r;       // this lane's key
+        bf16x4 kb = __builtin_bit_cast(bf16x4, make_uint2(0u, 0u));
+        bf16x8 vb[2];
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) vb[cs] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        if (kr < L) {
+            kb = quarter(*reinterpret_cast<const uint2*>(kh + (size_t)kr * kD + 4 * g));
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs) vb[cs] = ld8(vh + (size_t)kr * DV + 32 * cs + 8 * g);
+        }
+        float xr[16], xj[4];
+        token_rows(kh, kr, kw0, L, g, r, xr, xj);
+
+        // dv: the chunk's own queries (diagonal tile), then m(k) R^c
+        f32x4 dvacc[kNV];
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) dvacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 dkacc = {0.f, 0.f, 0.f, 0.f}, unused = {0.f, 0.f, 0.f, 0.f};
+        k_tile<DV, true>(sm.t, kb, vb, w, g, r, dvacc, dkacc);
+        readout<false>(sm.s, xr, g, r, dvacc, unused);
+        // dk: J_m^T (R^c v + r^c)
+        const float ones[4] = {1.f, 1.f, 1.f, 1.f};
+        float dx[4] = {0.f, 0.f, 0.f, 0.f};
+        contract_all<false>(std::make_integer_sequence<int, kNTile>{}, sm.s, vb, vb, ones, xj, g, r, dx);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int kj = kw0 + 4 * g + m;
+            if (kj < L) {
+#pragma unroll
+                for (int ct = 0; ct < kNV; ++ct) dvo[((size_t)head * L + kj) * DV + 16 * ct + r] = dvacc[ct][m];
+                dk[((size_t)head * L + kj) * kD + r] = fmaf(0.25f, dkacc[m], dx[m]);
+            }
+        }
+
+        // R, r with this chunk's queries
+        update_any<true>(w, sm.t.q, sm.t.ghi, sm.t.glo, sm.t.h, t0, L, g, r, acc, zacc);
+        __syncthreads();
+        if (c > c_begin) {
+            store();
+            publish_state(w, acc, zacc, sm.s, g, r);
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 // The workspace of prefill_backward.hip (BH*L*DV fp32 for g, then BH*L fp32
@@ -534,6 +1214,58 @@ hipError_t launch_prefill_backward_mfma(const void* q, const void* k, const void
     const uint16_t* vv = static_cast<const uint16_t*>(v);
     if (dv == 64) launch_both<64>(qq, kk, vv, dy, BH, L, eps, dq, dk, dvo, g_ws, h_ws, st);
     else launch_both<128>(qq, kk, vv, dy, BH, L, eps, dq, dk, dvo, g_ws, h_ws, st);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- chunked launch plan
+// Segments of cps chunks so that (segments x heads) fills the chip about
+// twice with 256-thread workgroups.
+static void chunk_plan(int BH, int L, int& nch, int& cps, int& nseg) {
+    nch = (L + kT - 1) / kT;
+    const long long want = ((long long)nch * BH + 511) / 512;
+    cps = (int)(want < 1 ? 1 : want);
+    nseg = (nch + cps - 1) / cps;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t prefill_backward_chunked_workspace_bytes(int BH, int L) {
+    int nch, cps, nseg;
+    chunk_plan(BH, L, nch, cps, nseg);
+    const size_t base = align256((size_t)BH * L * (64 + 1) * sizeof(float));
+    return nseg > 1 ? base + 2 * align256((size_t)nseg * BH * kStateFloats * sizeof(float)) : base;
+}
+
+hipError_t launch_prefill_backward_chunked(const void* q, const void* k, const void* v, const float* dy, int BH,
+                                           int L, float eps, float* dq, float* dk, float* dvo, void* workspace,
+                                           hipStream_t st) {
+    int nch, cps, nseg;
+    chunk_plan(BH, L, nch, cps, nseg);
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const uint16_t* kk = static_cast<const uint16_t*>(k);
+    const uint16_t* vv = static_cast<const uint16_t*>(v);
+    char* base = static_cast<char*>(workspace);
+    uint16_t* ghi = reinterpret_cast<uint16_t*>(base);
+    uint16_t* glo = ghi + (size_t)BH * L * 64;
+    float* h_ws = reinterpret_cast<float*>(glo + (size_t)BH * L * 64);
+    const size_t sbytes = align256((size_t)nseg * BH * kStateFloats * sizeof(float));
+    float* s_states = reinterpret_cast<float*>(base + align256((size_t)BH * L * (64 + 1) * sizeof(float)));
+    float* r_states = reinterpret_cast<float*>(reinterpret_cast<char*>(s_states) + sbytes);
+    const unsigned scan_blocks = (unsigned)(((size_t)BH * kStateFloats + 255) / 256);
+    if (nseg > 1) {
+        hipLaunchKernelGGL((bwd_segsum_kernel<true>), dim3((unsigned)(BH * (nseg - 1))), dim3(256), 0, st, kk, vv,
+                           nullptr, nullptr, BH, L, nch, cps, 0, s_states);
+        hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, st, s_states, BH, nseg, 0);
+    }
+    hipLaunchKernelGGL(bwd_qsweep_kernel, dim3((unsigned)(BH * nseg)), dim3(256), 0, st, qq, kk, vv, dy, BH, L, nch,
+                       cps, eps, nseg > 1 ? s_states : nullptr, dq, ghi, glo, h_ws);
+    if (nseg > 1) {
+        hipLaunchKernelGGL((bwd_segsum_kernel<false>), dim3((unsigned)(BH * (nseg - 1))), dim3(256), 0, st, qq, ghi,
+                           glo, h_ws, BH, L, nch, cps, 1, r_states);
+        hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, st, r_states, BH, nseg, 1);
+    }
+    hipLaunchKernelGGL(bwd_ksweep_kernel, dim3((unsigned)(BH * nseg)), dim3(256), 0, st, qq, kk, vv, BH, L, nch, cps,
+                       ghi, glo, h_ws, nseg > 1 ? r_states : nullptr, dk, dvo);
     return hipGetLastError();
 }
 

@@ -227,17 +227,23 @@ def test_hybrid_workspace_bytes(lib):
 
 
 def _bwd(lib, **kw):
-    a = dict(q=A, k=B_, v=C, dy=Y, dtype=1, B=1, H=2, L=100, d=16, dv=64, eps=1e-6, dq=S, dk=S + (1 << 20),
+    a = dict(q=A, k=B_, v=C, dy=Y, dtype=1, B=1, H=2, L=100, d=16, dv=64, eps=1e-6, form=0, dq=S, dk=S + (1 << 20),
              dvo=S + (2 << 20), ws=Z, wsb=1 << 20, stream=None)
     a.update(kw)
     return lib.based_prefill_backward(a["q"], a["k"], a["v"], a["dy"], a["dtype"], a["B"], a["H"], a["L"], a["d"],
-                                      a["dv"], a["eps"], a["dq"], a["dk"], a["dvo"], a["ws"], a["wsb"], a["stream"])
+                                      a["dv"], a["eps"], a["form"], a["dq"], a["dk"], a["dvo"], a["ws"], a["wsb"],
+                                      a["stream"])
 
 
 @pytest.mark.parametrize("kw,want", [
     (dict(q=None), 1), (dict(dy=None), 1), (dict(ws=None), 1), (dict(dq=S + 4), 1), (dict(wsb=100), 1),
     (dict(dtype=5), 1), (dict(L=0), 1), (dict(eps=float("nan")), 1), (dict(d=12), 2), (dict(dv=32), 2),
     (dict(dq=A), 1), (dict(dk=S), 1), (dict(ws=S + (2 << 20)), 1), (dict(dvo=Y), 1),
+    # the form: unknown values, and the chunked form outside bf16 / d' 16 / d_v 64
+    (dict(form=3), 1), (dict(form=-1), 1), (dict(form=2, dtype=0), 2), (dict(form=2, d=8), 2),
+    (dict(form=2, dv=128), 2),
+    # the chunked form's workspace is larger than the direct form's
+    (dict(form=2, wsb=2 * 100 * 65 * 4), 1),
 ])
 @fake_addresses
 def test_backward_rejects(lib, kw, want):
@@ -245,7 +251,11 @@ def test_backward_rejects(lib, kw, want):
 
 
 def test_backward_workspace_bytes(lib):
-    assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 16, 64) == 2 * 3 * 100 * 65 * 4
+    # direct form: g and h; d' 16 with d_v 64 also covers the chunked form's
+    # per-segment states
+    assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 16, 128) == 2 * 3 * 100 * 129 * 4
+    assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 8, 64) == 2 * 3 * 100 * 65 * 4
+    assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 16, 64) > 2 * 3 * 100 * 65 * 4
     assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 12, 64) == 0
     assert lib.based_prefill_backward_workspace_bytes(0, 3, 100, 16, 64) == 0
 

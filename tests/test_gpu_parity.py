@@ -477,17 +477,38 @@ def test_backward_matches_oracle(dtype, tol, B, H, L, d, dv):
     report(f"backward {dtype} L={L} d={d} dv={dv} dv", ratio(dv_, ov), tol)
 
 
+@pytest.mark.parametrize("B,H,L", [(1, 2, 3), (1, 1, 64), (2, 1, 65), (1, 2, 130), (1, 3, 257), (2, 2, 700),
+                                   (2, 4, 4100)])
+def test_backward_chunked_matches_oracle(B, H, L):
+    """The chunked (linear-time) form, bf16 with d' = 16 and d_v = 64: every
+    element of dq, dk, dv against the oracle.  The shapes span one chunk,
+    ragged tails, one segment per chunk, and (8 heads of 4100 tokens)
+    segments of two chunks ending in a one-chunk segment."""
+    based = based_mod()
+    q, k, v = si.custom((B, H, L, 16), (B, H, L, 64), seed=2400 + L + H, scale=0.5)
+    dy = torch.randn(B, H, L, 64, generator=torch.Generator().manual_seed(2401 + L))
+    dq, dk, dv_ = based.based_prefill_backward(*dev(q, k, v), dy.to(DEV), form="chunked")
+    torch.cuda.synchronize()
+    want = oracle.la_backward(q, k, v, dy) if L <= 1000 else oracle.la_backward_recurrent(q, k, v, dy)
+    for name, got, w in zip(("dq", "dk", "dv"), (dq, dk, dv_), want):
+        report(f"chunked backward B={B} H={H} L={L} {name}", ratio(got, w), 2e-2)
+
+
+@pytest.mark.parametrize("form", ["direct", "chunked"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_backward_single_token(dtype):
+def test_backward_single_token(dtype, form):
     """L = 1: y_0 = v_0 a/(a + eps), so dv_0 = dy_0 a/(a + eps) and dq, dk are
     of order eps: they come out of the cancellation of terms of order
     |dy||v|, and fp32 gives them to rounding noise of those terms."""
+    if form == "chunked" and dtype != torch.bfloat16:
+        pytest.skip("the chunked form takes bf16 inputs")
     based = based_mod()
-    q, k, v = si.custom((2, 2, 1, 16), (2, 2, 1, 128), seed=2250, scale=1.0, dtype=dtype)
-    dy = torch.randn(2, 2, 1, 128, generator=torch.Generator().manual_seed(2251))
-    dq, dk, dv_ = based.based_prefill_backward(*dev(q, k, v), dy.to(DEV))
+    dvd = 128 if form == "direct" else 64
+    q, k, v = si.custom((2, 2, 1, 16), (2, 2, 1, dvd), seed=2250, scale=1.0, dtype=dtype)
+    dy = torch.randn(2, 2, 1, dvd, generator=torch.Generator().manual_seed(2251))
+    dq, dk, dv_ = based.based_prefill_backward(*dev(q, k, v), dy.to(DEV), form=form)
     oq, ok, ov = oracle.la_backward(q, k, v, dy)
-    report(f"backward L=1 {dtype} dv", ratio(dv_, ov), 1e-4)
+    report(f"backward L=1 {dtype} {form} dv", ratio(dv_, ov), 1e-4)
     noise = 1e-5 * float(dy.norm(dim=-1).max() * v.float().norm(dim=-1).max() * k.float().norm(dim=-1).max())
     assert float(dq.abs().max()) <= noise and float(dk.abs().max()) <= noise, (dq.abs().max(), dk.abs().max(), noise)
     assert np.abs(oq).max() <= noise and np.abs(ok).max() <= noise
@@ -495,17 +516,37 @@ def test_backward_single_token(dtype):
 
 def test_workload_prefill_360m_backward():
     """Gradients over the 360M-shaped layer (B=8, H=16, L=2048): dq, dk, dv
-    of all 128 heads against the oracle's chain rule."""
+    of all 128 heads in both forms (chunked: segments of 8 chunks) against
+    the oracle's chain rule."""
     based = based_mod()
     wl = si.WORKLOADS["prefill_360m"]
     q, k, v = si.linear_inputs(wl)
     dy = torch.randn(wl.B, wl.H, wl.L, wl.dv, generator=torch.Generator().manual_seed(2300))
+    oq, ok, ov = oracle.la_backward(q, k, v, dy, eps=wl.eps)
+    for form in ("direct", "chunked"):
+        dq, dk, dv_ = based.based_prefill_backward(*dev(q, k, v), dy.to(DEV), eps=wl.eps, form=form)
+        torch.cuda.synchronize()
+        report(f"prefill_360m backward {form} dq (all heads)", ratio(dq, oq), wl.tol)
+        report(f"prefill_360m backward {form} dk (all heads)", ratio(dk, ok), wl.tol)
+        report(f"prefill_360m backward {form} dv (all heads)", ratio(dv_, ov), wl.tol)
+        del dq, dk, dv_
+
+
+@pytest.mark.timeout(900)
+def test_workload_long_64k_backward():
+    """Gradients over the 64K sequence (B=1, H=16, L=65536, outlier keys)
+    in the chunked form (segments of 32 chunks): every element of dq, dk,
+    dv of all 16 heads against the oracle's recurrent-form gradients."""
+    based = based_mod()
+    wl = si.WORKLOADS["long_64k"]
+    q, k, v = si.linear_inputs(wl)
+    dy = torch.randn(wl.B, wl.H, wl.L, wl.dv, generator=torch.Generator().manual_seed(2350))
     dq, dk, dv_ = based.based_prefill_backward(*dev(q, k, v), dy.to(DEV), eps=wl.eps)
     torch.cuda.synchronize()
-    oq, ok, ov = oracle.la_backward(q, k, v, dy, eps=wl.eps)
-    report("prefill_360m backward dq (all heads)", ratio(dq, oq), wl.tol)
-    report("prefill_360m backward dk (all heads)", ratio(dk, ok), wl.tol)
-    report("prefill_360m backward dv (all heads)", ratio(dv_, ov), wl.tol)
+    oq, ok, ov = oracle.la_backward_recurrent(q, k, v, dy, eps=wl.eps)
+    report("long_64k backward dq (all heads)", ratio(dq, oq), wl.tol)
+    report("long_64k backward dk (all heads)", ratio(dk, ok), wl.tol)
+    report("long_64k backward dv (all heads)", ratio(dv_, ov), wl.tol)
 
 
 # ---------------------------------------------------------------- window decode
