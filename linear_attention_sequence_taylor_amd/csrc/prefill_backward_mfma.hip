@@ -182,8 +182,11 @@ __device__ __forceinline__ void q_pass1(const BwdQSmem<DV>& sm, const bf16x4& qb
                                         f32x4 (&yacc)[DV / 16], f32x4& dsum) {
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
     float a[4][4];
+    // On the diagonal tile, key pair p (tiles 2p, 2p + 1) meets this wave's
+    // queries only if 2p <= w (w is wave-uniform).
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
+        if (DIAG && 2 * (kt >> 1) > w) continue;
         const f32x4 st = mfma16(ld4(&sm.k[tile_at<kD>(16 * kt + r, 4 * g)]), qb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -195,6 +198,7 @@ __device__ __forceinline__ void q_pass1(const BwdQSmem<DV>& sm, const bf16x4& qb
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
+        if (DIAG && 2 * p > w) continue;
         float x[8];
         join_tiles(a[2 * p], a[2 * p + 1], x);
         bf16x8 ahi, alo;
@@ -219,6 +223,7 @@ __device__ __forceinline__ void q_pass2(const BwdQSmem<DV>& sm, const bf16x4& qb
     float e[4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
+        if (DIAG && 2 * (kt >> 1) > w) continue;  // as in q_pass1
         const f32x4 st = mfma16(ld4(&sm.k[tile_at<kD>(16 * kt + r, 4 * g)]), qb, f32x4{0.f, 0.f, 0.f, 0.f});
         // ga^T: rows = keys 16kt + 4g + m, columns = queries r
         f32x4 ga = {0.f, 0.f, 0.f, 0.f};
@@ -238,6 +243,7 @@ __device__ __forceinline__ void q_pass2(const BwdQSmem<DV>& sm, const bf16x4& qb
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
+        if (DIAG && 2 * p > w) continue;
         float x[8];
         join_tiles(e[2 * p], e[2 * p + 1], x);
         bf16x8 ehi, elo;
@@ -386,8 +392,11 @@ template <int DV, bool DIAG>
 __device__ __forceinline__ void k_tile(const BwdKSmem<DV>& sm, const bf16x4& kb, const bf16x8 (&vb)[DV / 32], int w,
                                        int g, int r, f32x4 (&dvacc)[DV / 16], f32x4& dkacc) {
     float a[4][4], e[4][4];
+    // On the diagonal tile, query pair p (tiles 2p, 2p + 1) meets this
+    // wave's keys only if 2p + 1 >= w (w is wave-uniform).
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
+        if (DIAG && 2 * (qt >> 1) + 1 < w) continue;
         // scores and ga: rows = queries 16qt + 4g + m, columns = keys r
         const f32x4 st = mfma16(ld4(&sm.q[tile_at<kD>(16 * qt + r, 4 * g)]), kb, f32x4{0.f, 0.f, 0.f, 0.f});
         f32x4 ga = {0.f, 0.f, 0.f, 0.f};
@@ -412,6 +421,7 @@ __device__ __forceinline__ void k_tile(const BwdKSmem<DV>& sm, const bf16x4& kb,
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
+        if (DIAG && 2 * p + 1 < w) continue;
         float xa[8], xe[8];
         join_tiles(a[2 * p], a[2 * p + 1], xa);
         join_tiles(e[2 * p], e[2 * p + 1], xe);
@@ -580,14 +590,31 @@ __device__ __forceinline__ float slot_coef(int t, int row) {
 __device__ __forceinline__ int slot_pos(int t, int row) {
     return 32 * (t >> 1) + 8 * (row >> 2) + 4 * (t & 1) + (row & 3);
 }
-// LDS offset (bf16 elements) of (value column c, position p) in a published
-// plane: rows of 160, 16-byte units XOR-swizzled by bits 2..3 of c, so that
-// the readout's 16-byte reads (16 columns, one unit), the contraction's
+// A published plane holds value column c at row c (160 bf16 per row),
+// position p at 16-byte unit (p >> 3) XOR ((c >> 2) & 3), so that the
+// readout's 16-byte reads (16 columns, one unit), the contraction's
 // transposed reads (4 columns x 4 units) and the publish writes (16
-// columns) each hit 16 distinct 4-bank groups.
-__device__ __forceinline__ int pub_at(int c, int p) {
-    return c * kSlot + ((((p >> 3) ^ ((c >> 2) & 3))) << 3) + (p & 7);
-}
+// columns) each hit 16 distinct 4-bank groups (PubLane below).
+
+// Per-lane LDS offsets into a published plane, fixed for the kernel: with
+// them every access of the readout, the publish and the contraction is the
+// lane's offset plus a constant.
+//  - rw: column r at unit g, swizzled: readout k-step J and column tile ct
+//    read rw + 2560 ct + 32 J; publish of tile t at column tile ct writes
+//    rw + 2560 ct + 32 (t >> 1) + 4 (t & 1).
+//  - tr[h]: the contraction's transposed read of rows 8g + 4h + j (j =
+//    c16 / 4) at slot group 4 (c16 % 4); tile T, k-step cs read
+//    tr[h] + 5120 cs + 32 (T >> 1) + 4 (T & 1).
+struct PubLane {
+    int rw, tr[2], zp;
+    __device__ __forceinline__ PubLane(int g, int r) {
+        rw = r * kSlot + ((g ^ (r >> 2)) << 3);
+        const int j = r >> 2, qq = r & 3;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) tr[h] = (8 * g + 4 * h + j) * kSlot + ((qq ^ ((2 * g + h) & 3)) << 3);
+        zp = 8 * (r >> 2) + (r & 3);  // slot_pos(T, r) - 32 (T >> 1) - 4 (T & 1)
+    }
+};
 
 // A state published for the readout and the contraction.
 struct PubState {
@@ -633,8 +660,9 @@ __device__ __forceinline__ void update_tile(const float (&x)[8], const float (&w
     float a[8];
     mono_rows<T>(x, r, a);
     if constexpr (ZSUM) {
+        // key side (M exact): the plain feature sums; query side: weighted by h
 #pragma unroll
-        for (int i = 0; i < 8; ++i) zacc = fmaf(a[i], w8[i], zacc);
+        for (int i = 0; i < 8; ++i) zacc = MHILO ? fmaf(a[i], w8[i], zacc) : zacc + a[i];
     }
     bf16x8 ah, al;
     hilo8(a, ah, al);
@@ -651,21 +679,26 @@ __device__ __forceinline__ void update_tile(const float (&x)[8], const float (&w
 // 8 + W/2 at column tiles 2(W%2), 2(W%2) + 1 (acc[8], acc[9]); zacc[0..2]
 // are the matching normaliser rows (the third only on even W, so that each
 // row is summed once).  X is [64][16] in tile_at<16> layout, M [64][64] in
-// tile_at<64> layout (hi, and lo if MHILO); token weights wtok (the
-// normaliser's per-token factor) come from LDS if given, else they are the
-// validity of the chunk's tokens (t0 + token < L).
+// tile_at<64> layout (hi, and lo if MHILO).  The key side (M = V, exact)
+// sums plain features: padded tokens have x = 0 and v = 0, so only the
+// constant row counts them, and that row is replaced by the token count
+// when published or stored.  The query side (M = g hi/lo) weights the
+// normaliser by h (wtok, LDS), zero on padded tokens.
 template <int W, bool MHILO>
 __device__ __forceinline__ void update_wave(const uint16_t* xt, const uint16_t* mhi, const uint16_t* mlo,
-                                            const float* wtok, int t0, int L, int g, int r, f32x4 (&acc)[10],
-                                            float (&zacc)[3]) {
+                                            const float* wtok, int g, int r, f32x4 (&acc)[10], float (&zacc)[3]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         float x[8], w8[8];
         unpack_b8(tr_b8<kD>(xt, 32 * ks, 0, g, r), x);
+        if constexpr (MHILO) {
+            const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wtok[32 * ks + 4 * g]);
+            const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wtok[32 * ks + 16 + 4 * g]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int tok = 32 * ks + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
-            w8[i] = wtok ? wtok[tok] : (t0 + tok < L ? 1.f : 0.f);
+            for (int i = 0; i < 4; ++i) {
+                w8[i] = w0[i];
+                w8[4 + i] = w1[i];
+            }
         }
         bf16x8 bh[4], bl[4];
 #pragma unroll
@@ -680,13 +713,12 @@ __device__ __forceinline__ void update_wave(const uint16_t* xt, const uint16_t* 
 }
 template <bool MHILO>
 __device__ __forceinline__ void update_any(int w, const uint16_t* xt, const uint16_t* mhi, const uint16_t* mlo,
-                                           const float* wtok, int t0, int L, int g, int r, f32x4 (&acc)[10],
-                                           float (&zacc)[3]) {
+                                           const float* wtok, int g, int r, f32x4 (&acc)[10], float (&zacc)[3]) {
     switch (w) {
-        case 0: update_wave<0, MHILO>(xt, mhi, mlo, wtok, t0, L, g, r, acc, zacc); break;
-        case 1: update_wave<1, MHILO>(xt, mhi, mlo, wtok, t0, L, g, r, acc, zacc); break;
-        case 2: update_wave<2, MHILO>(xt, mhi, mlo, wtok, t0, L, g, r, acc, zacc); break;
-        default: update_wave<3, MHILO>(xt, mhi, mlo, wtok, t0, L, g, r, acc, zacc); break;
+        case 0: update_wave<0, MHILO>(xt, mhi, mlo, wtok, g, r, acc, zacc); break;
+        case 1: update_wave<1, MHILO>(xt, mhi, mlo, wtok, g, r, acc, zacc); break;
+        case 2: update_wave<2, MHILO>(xt, mhi, mlo, wtok, g, r, acc, zacc); break;
+        default: update_wave<3, MHILO>(xt, mhi, mlo, wtok, g, r, acc, zacc); break;
     }
 }
 
@@ -699,31 +731,46 @@ __device__ __forceinline__ bool z_owned(int w, int i) { return i < 2 || (w & 1) 
 // Publish the wave's part of the state (times the slot coefficients) as
 // bf16 hi/lo planes, and its normaliser rows (the lane-group partial sums
 // added up) in fp32 and hi/lo.
-__device__ __forceinline__ void publish_state(int w, const f32x4 (&acc)[10], const float (&zacc)[3], PubState& ps,
-                                              int g, int r) {
+// zconst >= 0 replaces the constant feature's normaliser row (the number of
+// tokens summed, which the key-side update counts with the padding).
+template <int W>
+__device__ __forceinline__ void publish_wave(const f32x4 (&acc)[10], const float (&zacc)[3], PubState& ps,
+                                             const PubLane& pl, int g, int r, float zconst) {
 #pragma unroll
     for (int j = 0; j < 10; ++j) {
-        const int t = acc_tile(w, j), ct = acc_ct(w, j);
+        const int t = j < 8 ? 2 * W + (j >> 2) : 8 + (W >> 1), ct = j < 8 ? (j & 3) : 2 * (W & 1) + (j - 8);
         float v[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) v[m] = slot_coef(t, 4 * g + m) * acc[j][m];
         const uint32_t h0 = pack_bf16x2(v[0], v[1]), h1 = pack_bf16x2(v[2], v[3]);
-        const int off = pub_at(16 * ct + r, 32 * (t >> 1) + 8 * g + 4 * (t & 1));
+        const int off = pl.rw + 2560 * ct + 32 * (t >> 1) + 4 * (t & 1);
         *reinterpret_cast<uint2*>(&ps.hi[off]) = make_uint2(h0, h1);
         *reinterpret_cast<uint2*>(&ps.lo[off]) = make_uint2(lo_pair_of(h0, v[0], v[1]), lo_pair_of(h1, v[2], v[3]));
     }
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
+        if (i == 2 && (W & 1)) continue;
         float zt = zacc[i] + __shfl_xor(zacc[i], 16, 64);
         zt += __shfl_xor(zt, 32, 64);
-        if (g == 0 && z_owned(w, i)) {
-            const int t = z_tile(w, i), p = slot_pos(t, r);
+        const int t = i < 2 ? 2 * W + i : 8 + (W >> 1);
+        if (t == 8 && r == 8 && zconst >= 0.f) zt = zconst;
+        if (g == 0) {
+            const int p = slot_pos(t, r);
             const float zc = slot_coef(t, r) * zt;
             const uint32_t hp = pack_bf16x2(zc, 0.f);
             ps.z[p] = zc;
             ps.zhi[p] = (uint16_t)(hp & 0xffffu);
             ps.zlo[p] = (uint16_t)(lo_pair_of(hp, zc, 0.f) & 0xffffu);
         }
+    }
+}
+__device__ __forceinline__ void publish_state(int w, const f32x4 (&acc)[10], const float (&zacc)[3], PubState& ps,
+                                              const PubLane& pl, int g, int r, float zconst) {
+    switch (w) {
+        case 0: publish_wave<0>(acc, zacc, ps, pl, g, r, zconst); break;
+        case 1: publish_wave<1>(acc, zacc, ps, pl, g, r, zconst); break;
+        case 2: publish_wave<2>(acc, zacc, ps, pl, g, r, zconst); break;
+        default: publish_wave<3>(acc, zacc, ps, pl, g, r, zconst); break;
     }
 }
 
@@ -742,7 +789,7 @@ __device__ __forceinline__ void state_load(int w, const float* slot, int g, int 
         zacc[i] = slot && g == 0 && z_owned(w, i) ? slot[kSlot * 64 + 16 * z_tile(w, i) + r] : 0.f;
 }
 __device__ __forceinline__ void state_store(int w, const f32x4 (&acc)[10], const float (&zacc)[3], float* slot,
-                                            int g, int r) {
+                                            int g, int r, float zconst) {
 #pragma unroll
     for (int j = 0; j < 10; ++j) {
         const int t = acc_tile(w, j), ct = acc_ct(w, j);
@@ -753,6 +800,7 @@ __device__ __forceinline__ void state_store(int w, const f32x4 (&acc)[10], const
     for (int i = 0; i < 3; ++i) {
         float zt = zacc[i] + __shfl_xor(zacc[i], 16, 64);
         zt += __shfl_xor(zt, 32, 64);
+        if (z_tile(w, i) == 8 && r == 8 && zconst >= 0.f) zt = zconst;
         if (g == 0 && z_owned(w, i)) slot[kSlot * 64 + 16 * z_tile(w, i) + r] = zt;
     }
 }
@@ -773,7 +821,7 @@ __device__ __forceinline__ void mono_readout(const float (&xr)[16], int g, float
     }
 }
 template <int J, bool WITH_D>
-__device__ __forceinline__ void readout_step(const PubState& ps, const float (&xr)[16], int g, int r,
+__device__ __forceinline__ void readout_step(const PubState& ps, const PubLane& pl, const float (&xr)[16], int g,
                                              f32x4 (&y)[4], f32x4& dsum) {
     float a[8];
     mono_readout<J>(xr, g, a);
@@ -781,7 +829,7 @@ __device__ __forceinline__ void readout_step(const PubState& ps, const float (&x
     hilo8(a, ah, al);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-        const int off = pub_at(16 * ct + r, 32 * J + 8 * g);
+        const int off = pl.rw + 2560 * ct + 32 * J;
         const bf16x8 bh = ld8(&ps.hi[off]), bl = ld8(&ps.lo[off]);
         y[ct] = mfma32(ah, bh, y[ct]);
         y[ct] = mfma32(al, bh, y[ct]);
@@ -795,13 +843,13 @@ __device__ __forceinline__ void readout_step(const PubState& ps, const float (&x
     }
 }
 template <bool WITH_D>
-__device__ __forceinline__ void readout(const PubState& ps, const float (&xr)[16], int g, int r, f32x4 (&y)[4],
-                                        f32x4& dsum) {
-    readout_step<0, WITH_D>(ps, xr, g, r, y, dsum);
-    readout_step<1, WITH_D>(ps, xr, g, r, y, dsum);
-    readout_step<2, WITH_D>(ps, xr, g, r, y, dsum);
-    readout_step<3, WITH_D>(ps, xr, g, r, y, dsum);
-    readout_step<4, WITH_D>(ps, xr, g, r, y, dsum);
+__device__ __forceinline__ void readout(const PubState& ps, const PubLane& pl, const float (&xr)[16], int g,
+                                        f32x4 (&y)[4], f32x4& dsum) {
+    readout_step<0, WITH_D>(ps, pl, xr, g, y, dsum);
+    readout_step<1, WITH_D>(ps, pl, xr, g, y, dsum);
+    readout_step<2, WITH_D>(ps, pl, xr, g, y, dsum);
+    readout_step<3, WITH_D>(ps, pl, xr, g, y, dsum);
+    readout_step<4, WITH_D>(ps, pl, xr, g, y, dsum);
 }
 
 // ---- contraction and Jacobian
@@ -810,13 +858,13 @@ __device__ __forceinline__ void readout(const PubState& ps, const float (&xr)[16
 // c16 rows j = 0..3 of the element that lane 4j + c16/4 addressed at its
 // position c16 % 4, so lane 4j + q addresses column c0 + j at the four
 // consecutive positions of slots (T, 4q .. 4q + 3).
-__device__ __forceinline__ bf16x8 pub_tr(const uint16_t* plane, int T, int cs, int g, int c16) {
-    const int j = c16 >> 2, qq = c16 & 3;
-    const int c0 = 32 * cs + 8 * g + j, p = 32 * (T >> 1) + 8 * qq + 4 * (T & 1);
+template <int T>
+__device__ __forceinline__ bf16x8 pub_tr(const uint16_t* plane, const PubLane& pl, int cs) {
+    constexpr int kc = 32 * (T >> 1) + 4 * (T & 1);
     const uint2 a = __builtin_bit_cast(
-        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(BWD_LDS(s16x4, plane + pub_at(c0, p))));
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(BWD_LDS(s16x4, plane + pl.tr[0] + 5120 * cs + kc)));
     const uint2 b = __builtin_bit_cast(
-        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(BWD_LDS(s16x4, plane + pub_at(c0 + 4, p))));
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(BWD_LDS(s16x4, plane + pl.tr[1] + 5120 * cs + kc)));
     return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
 
@@ -844,49 +892,90 @@ __device__ __forceinline__ void jac_tile(const f32x4& u, const float (&xj)[4], i
 }
 
 template <int T, bool AHILO>
-__device__ __forceinline__ void contract_tile(const PubState& ps, const bf16x8 (&ah)[2], const bf16x8 (&al)[2],
-                                              const float (&zw)[4], const float (&xj)[4], int g, int r,
-                                              float (&dx)[4]) {
+__device__ __forceinline__ void contract_tile(const PubState& ps, const PubLane& pl, const bf16x8 (&ah)[2],
+                                              const bf16x8 (&al)[2], const float (&zw)[4], const float (&xj)[4],
+                                              int r, float (&dx)[4]) {
     f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cs = 0; cs < 2; ++cs) {
-        const bf16x8 bh = pub_tr(ps.hi, T, cs, g, r), bl = pub_tr(ps.lo, T, cs, g, r);
+        const bf16x8 bh = pub_tr<T>(ps.hi, pl, cs), bl = pub_tr<T>(ps.lo, pl, cs);
         u = mfma32(ah[cs], bh, u);
         u = mfma32(ah[cs], bl, u);
         if constexpr (AHILO) u = mfma32(al[cs], bh, u);
     }
-    const float zc = ps.z[slot_pos(T, r)];
+    const float zc = ps.z[pl.zp + 32 * (T >> 1) + 4 * (T & 1)];
 #pragma unroll
     for (int m = 0; m < 4; ++m) u[m] = fmaf(zw[m], zc, u[m]);
     jac_tile<T>(u, xj, r, dx);
 }
 // dx += J_m^T (M S^c^T + zw z^c) over all ten tiles.  M's rows are the
 // wave's tokens: ah/al[cs] = M[row r][32cs + 8g .. +7] (hi/lo if AHILO).
-template <bool AHILO, int... Ts>
-__device__ __forceinline__ void contract_all(std::integer_sequence<int, Ts...>, const PubState& ps,
-                                             const bf16x8 (&ah)[2], const bf16x8 (&al)[2], const float (&zw)[4],
-                                             const float (&xj)[4], int g, int r, float (&dx)[4]) {
-    (contract_tile<Ts, AHILO>(ps, ah, al, zw, xj, g, r, dx), ...);
+// (A loop over the tiles rather than an unrolled sequence: unrolled, the
+// compiler issues every tile's LDS reads up front and runs out of
+// registers.)
+template <bool AHILO>
+__device__ __forceinline__ void contract_all(const PubState& ps, const PubLane& pl, const bf16x8 (&ah)[2],
+                                             const bf16x8 (&al)[2], const float (&zw)[4], const float (&xj)[4],
+                                             int r, float (&dx)[4]) {
+#pragma unroll 1
+    for (int t = 0; t < kNTile; ++t) {
+        switch (t) {
+            case 0: contract_tile<0, AHILO>(ps, pl, ah, al, zw, xj, r, dx); break;
+            case 1: contract_tile<1, AHILO>(ps, pl, ah, al, zw, xj, r, dx); break;
+            case 2: contract_tile<2, AHILO>(ps, pl, ah, al, zw, xj, r, dx); break;
+            case 3: contract_tile<3, AHILO>(ps, pl, ah, al, zw, xj, r, dx); break;
+            case 4: contract_tile<4, AHILO>(ps, pl, ah, al, zw, xj, r, dx); break;
+            case 5: contract_tile<5, AHILO>(ps, pl, ah, al, zw, xj, r, dx); break;
+            case 6: contract_tile<6, AHILO>(ps, pl, ah, al, zw, xj, r, dx); break;
+            case 7: contract_tile<7, AHILO>(ps, pl, ah, al, zw, xj, r, dx); break;
+            case 8: contract_tile<8, AHILO>(ps, pl, ah, al, zw, xj, r, dx); break;
+            default: contract_tile<9, AHILO>(ps, pl, ah, al, zw, xj, r, dx); break;
+        }
+    }
 }
 
-// This lane's token row x[16] rotated by 4g (xr[j] = x_((j + 4g) mod 16)),
-// zero past L; and x_r of tokens base + 4g + m.
-__device__ __forceinline__ void token_rows(const uint16_t* xh, int tok, int base, int L, int g, int r,
-                                           float (&xr)[16], float (&xj)[4]) {
+// The global-memory inputs of one wave's 16 tokens for a chunk, loaded one
+// chunk ahead of their use: this lane's token row rotated by 4g (pieces of
+// 4 dims), x_r of tokens base + 4g + m, and the 4 dims 4g..4g+3 of the
+// lane's token (the score operand).  Zero past L.
+struct TokenRegs {
+    uint2 rot[4];
+    uint16_t xj[4];
+    uint2 sc;
+    __device__ __forceinline__ void load(const uint16_t* xh, int tok, int base, int L, int g, int r) {
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-        uint2 u = make_uint2(0u, 0u);
-        if (tok < L) u = *reinterpret_cast<const uint2*>(xh + (size_t)tok * kD + 4 * ((pp + g) & 3));
-        xr[4 * pp] = bf16lo_f32(u.x);
-        xr[4 * pp + 1] = bf16hi_f32(u.x);
-        xr[4 * pp + 2] = bf16lo_f32(u.y);
-        xr[4 * pp + 3] = bf16hi_f32(u.y);
-    }
+        for (int pp = 0; pp < 4; ++pp) {
+            rot[pp] = make_uint2(0u, 0u);
+            if (tok < L) rot[pp] = *reinterpret_cast<const uint2*>(xh + (size_t)tok * kD + 4 * ((pp + g) & 3));
+        }
+        // the score operand is piece g of the row, which is rot[0]
+        sc = rot[0];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int t = base + 4 * g + m;
-        xj[m] = t < L ? bf16_bits_to_f32(xh[(size_t)t * kD + r]) : 0.f;
+        for (int m = 0; m < 4; ++m) {
+            const int t = base + 4 * g + m;
+            xj[m] = t < L ? xh[(size_t)t * kD + r] : (uint16_t)0;
+        }
     }
+    // xr[j] = x_((j + 4g) mod 16) of the lane's token; xj[m] = x_r of token 4g + m
+    __device__ __forceinline__ void unpack(float (&xr)[16], float (&xjf)[4]) const {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+            xr[4 * pp] = bf16lo_f32(rot[pp].x);
+            xr[4 * pp + 1] = bf16hi_f32(rot[pp].x);
+            xr[4 * pp + 2] = bf16lo_f32(rot[pp].y);
+            xr[4 * pp + 3] = bf16hi_f32(rot[pp].y);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xjf[m] = bf16_bits_to_f32(xj[m]);
+    }
+};
+
+// Make this wave's LDS writes visible to its own later reads (no other
+// wave takes part): LDS serves one wave's accesses in order, so only the
+// compiler's ordering is at stake.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 }
 
 // ---------------------------------------------------------------- segment sums
@@ -898,7 +987,7 @@ __global__ __launch_bounds__(256) void bwd_segsum_kernel(const uint16_t* __restr
                                                          const uint16_t* __restrict__ mlo,
                                                          const float* __restrict__ hw, int BH, int L, int nch,
                                                          int cps, int seg0, float* __restrict__ states) {
-    __shared__ BwdKSmem<64> sm;  // q: X, ghi/glo: M, h: token weights
+    __shared__ BwdKSmem<64> sm[2];  // per chunk parity; q: X, ghi/glo: M, h: token weights
     const int head = blockIdx.x % BH, seg = seg0 + (int)(blockIdx.x / BH);
     const int c_begin = seg * cps, c_end = min(nch, c_begin + cps);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -921,20 +1010,30 @@ __global__ __launch_bounds__(256) void bwd_segsum_kernel(const uint16_t* __restr
             if (threadIdx.x < kT) hreg = c * kT + (int)threadIdx.x < L ? hh[c * kT + threadIdx.x] : 0.f;
         }
     };
+    auto store = [&](BwdKSmem<64>& b) {
+        xreg.store(b.q);
+        mreg.store(b.ghi);
+        if (!KEYS) {
+            lreg.store(b.glo);
+            if (threadIdx.x < kT) b.h[threadIdx.x] = hreg;
+        }
+    };
+    // chunk c is staged in sm[c & 1] one iteration ahead, its global loads
+    // two iterations ahead; one barrier per chunk
     load(c_begin);
+    store(sm[c_begin & 1]);
+    if (c_begin + 1 < c_end) load(c_begin + 1);
     for (int c = c_begin; c < c_end; ++c) {
         __syncthreads();
-        xreg.store(sm.q);
-        mreg.store(sm.ghi);
-        if (!KEYS) {
-            lreg.store(sm.glo);
-            if (threadIdx.x < kT) sm.h[threadIdx.x] = hreg;
+        if (c + 1 < c_end) {
+            store(sm[(c + 1) & 1]);
+            if (c + 2 < c_end) load(c + 2);
         }
-        __syncthreads();
-        if (c + 1 < c_end) load(c + 1);
-        update_any<!KEYS>(w, sm.q, sm.ghi, sm.glo, KEYS ? nullptr : sm.h, c * kT, L, g, r, acc, zacc);
+        const BwdKSmem<64>& b = sm[c & 1];
+        update_any<!KEYS>(w, b.q, b.ghi, b.glo, b.h, g, r, acc, zacc);
     }
-    state_store(w, acc, zacc, states + ((size_t)seg * BH + head) * kStateFloats, g, r);
+    state_store(w, acc, zacc, states + ((size_t)seg * BH + head) * kStateFloats, g, r,
+                KEYS ? (float)(min(L, c_end * kT) - c_begin * kT) : -1.f);
 }
 
 // Launches 2 and 5: each (segment, head) state becomes the sum of the
@@ -957,12 +1056,20 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(float* __restrict__ state
 }
 
 // ---------------------------------------------------------------- query sweep
+// kSweepBuf = 2: the staged chunk and the published state double-buffered
+// by chunk parity, one barrier per chunk, but 1 workgroup per CU by LDS;
+// kSweepBuf = 1: single buffers and a second barrier before they are
+// rewritten, 2 workgroups per CU.  A sweep is a chain of dependent steps,
+// so the second workgroup's latency hiding wins (about 1.4x measured on
+// the 360M-shaped layer).
+constexpr int kSweepBuf = 1;
+__device__ __forceinline__ int sbuf(int c) { return c & (kSweepBuf - 1); }
 struct QSweepSmem {
-    BwdQSmem<64> t;
-    PubState s;
+    BwdQSmem<64> t[kSweepBuf];
+    PubState s[kSweepBuf];
 };
 
-__global__ __launch_bounds__(256) void bwd_qsweep_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_qsweep_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          const float* __restrict__ dy, int BH, int L, int nch,
@@ -986,40 +1093,51 @@ __global__ __launch_bounds__(256) void bwd_qsweep_kernel(const uint16_t* __restr
     TileRegs<DV> vreg;
     kreg.load(kh, L, c_begin * kT);
     vreg.load(vh, L, c_begin * kT);
-    kreg.store(sm.t.k);
-    vreg.store(sm.t.v);
-    publish_state(w, acc, zacc, sm.s, g, r);
+    // this wave's queries, one chunk ahead
+    TokenRegs qreg;
+    auto load_q = [&](int c) {
+        const int qw0 = c * kT + 16 * w;
+        qreg.load(qh, qw0 + r, qw0, L, g, r);
+    };
+    load_q(c_begin);
+    kreg.store(sm.t[sbuf(c_begin)].k);
+    vreg.store(sm.t[sbuf(c_begin)].v);
+    const PubLane pl(g, r);
+    publish_state(w, acc, zacc, sm.s[sbuf(c_begin)], pl, g, r, (float)(c_begin * kT));
     __syncthreads();
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * kT;
+        BwdQSmem<DV>& tt = sm.t[sbuf(c)];
+        const PubState& ss = sm.s[sbuf(c)];
         if (c + 1 < c_end) {
             kreg.load(kh, L, t0 + kT);
             vreg.load(vh, L, t0 + kT);
         }
         const int qw0 = t0 + 16 * w;  // first query of this wave
-        const int qr = qw0 + r;       // this lane's query in score tiles and the readout
-        bf16x4 qb = __builtin_bit_cast(bf16x4, make_uint2(0u, 0u));
-        if (qr < L) qb = quarter(*reinterpret_cast<const uint2*>(qh + (size_t)qr * kD + 4 * g));
         float xr[16], xj[4];
-        token_rows(qh, qr, qw0, L, g, r, xr, xj);
+        qreg.unpack(xr, xj);
+        const bf16x4 qb = quarter(qreg.sc);  // this lane's query, dims 4g..4g+3, times 1/4
+        // dy rows qw0 + 4g + m, columns 16ct + r (zero past L), in flight
+        // during the products below
+        float dyc[4][kNV];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int qi = qw0 + 4 * g + m;
+            const float* dyr = dy + ((size_t)head * L + min(qi, L - 1)) * DV + r;
+#pragma unroll
+            for (int ct = 0; ct < kNV; ++ct) dyc[m][ct] = qi < L ? dyr[16 * ct] : 0.f;
+        }
+        if (c + 1 < c_end) load_q(c + 1);
 
         // y D and D: the chunk's own keys (diagonal tile), then the state
         f32x4 yacc[kNV];
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) yacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 dsum = {0.f, 0.f, 0.f, 0.f};
-        q_pass1<DV, true>(sm.t, qb, w, g, r, yacc, dsum);
-        readout<true>(sm.s, xr, g, r, yacc, dsum);
+        q_pass1<DV, true>(tt, qb, w, g, r, yacc, dsum);
+        readout<true>(ss, pl, xr, g, yacc, dsum);
 
         // g = dy/D, h = -(dy.y D)/D^2 (rows qw0 + 4g + m, columns 16ct + r)
-        float dyv[4][kNV];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int qi = qw0 + 4 * g + m;
-            const float* dyr = dy + ((size_t)head * L + min(qi, L - 1)) * DV + r;
-#pragma unroll
-            for (int ct = 0; ct < kNV; ++ct) dyv[m][ct] = dyr[16 * ct];
-        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int qi = qw0 + 4 * g + m;
@@ -1027,22 +1145,21 @@ __global__ __launch_bounds__(256) void bwd_qsweep_kernel(const uint16_t* __restr
             float dyy = 0.f;
 #pragma unroll
             for (int ct = 0; ct < kNV; ++ct) {
-                const float dyc = qi < L ? dyv[m][ct] : 0.f;
-                dyy = fmaf(dyc, yacc[ct][m], dyy);
-                const float gv = dyc * inv;
+                dyy = fmaf(dyc[m][ct], yacc[ct][m], dyy);
+                const float gv = dyc[m][ct] * inv;
                 const uint32_t hb = pack_bf16x2(gv, 0.f);
-                sm.t.ghi[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(hb & 0xffffu);
-                sm.t.glo[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(lo_pair_of(hb, gv, 0.f) & 0xffffu);
+                tt.ghi[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(hb & 0xffffu);
+                tt.glo[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(lo_pair_of(hb, gv, 0.f) & 0xffffu);
             }
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) dyy += __shfl_xor(dyy, off, 64);
             const float hq = -dyy * inv * inv;
             if (r == 0) {
-                sm.t.h[w][4 * g + m] = hq;
+                tt.h[w][4 * g + m] = hq;
                 if (qi < L) h_ws[(size_t)head * L + qi] = hq;
             }
         }
-        __syncthreads();
+        wave_lds_fence();
         {
             constexpr int kU = DV / 8;
             for (int e = lane; e < 16 * kU; e += 64) {
@@ -1051,9 +1168,9 @@ __global__ __launch_bounds__(256) void bwd_qsweep_kernel(const uint16_t* __restr
                 if (qi < L) {
                     const size_t off = ((size_t)head * L + qi) * DV + 8 * u;
                     *reinterpret_cast<u32x4*>(ghi_ws + off) =
-                        *reinterpret_cast<const u32x4*>(&sm.t.ghi[w][tile_at<DV>(row, 8 * u)]);
+                        *reinterpret_cast<const u32x4*>(&tt.ghi[w][tile_at<DV>(row, 8 * u)]);
                     *reinterpret_cast<u32x4*>(glo_ws + off) =
-                        *reinterpret_cast<const u32x4*>(&sm.t.glo[w][tile_at<DV>(row, 8 * u)]);
+                        *reinterpret_cast<const u32x4*>(&tt.glo[w][tile_at<DV>(row, 8 * u)]);
                 }
             }
         }
@@ -1062,15 +1179,15 @@ __global__ __launch_bounds__(256) void bwd_qsweep_kernel(const uint16_t* __restr
         bf16x8 gah[2], gal[2];
 #pragma unroll
         for (int cs = 0; cs < 2; ++cs) {
-            gah[cs] = ld8(&sm.t.ghi[w][tile_at<DV>(r, 32 * cs + 8 * g)]);
-            gal[cs] = ld8(&sm.t.glo[w][tile_at<DV>(r, 32 * cs + 8 * g)]);
+            gah[cs] = ld8(&tt.ghi[w][tile_at<DV>(r, 32 * cs + 8 * g)]);
+            gal[cs] = ld8(&tt.glo[w][tile_at<DV>(r, 32 * cs + 8 * g)]);
         }
         float hz[4], dx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) hz[m] = sm.t.h[w][4 * g + m];
-        contract_all<true>(std::make_integer_sequence<int, kNTile>{}, sm.s, gah, gal, hz, xj, g, r, dx);
+        for (int m = 0; m < 4; ++m) hz[m] = tt.h[w][4 * g + m];
+        contract_all<true>(ss, pl, gah, gal, hz, xj, r, dx);
         f32x4 dqacc = {0.f, 0.f, 0.f, 0.f};
-        q_pass2<DV, true>(sm.t, qb, w, g, r, dqacc);
+        q_pass2<DV, true>(tt, qb, w, g, r, dqacc);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int qi = qw0 + 4 * g + m;
@@ -1078,12 +1195,12 @@ __global__ __launch_bounds__(256) void bwd_qsweep_kernel(const uint16_t* __restr
         }
 
         // the state after this chunk
-        update_any<false>(w, sm.t.k, sm.t.v, nullptr, nullptr, t0, L, g, r, acc, zacc);
-        __syncthreads();
+        update_any<false>(w, tt.k, tt.v, nullptr, nullptr, g, r, acc, zacc);
+        if (kSweepBuf == 1) __syncthreads();
         if (c + 1 < c_end) {
-            kreg.store(sm.t.k);
-            vreg.store(sm.t.v);
-            publish_state(w, acc, zacc, sm.s, g, r);
+            kreg.store(sm.t[sbuf(c + 1)].k);
+            vreg.store(sm.t[sbuf(c + 1)].v);
+            publish_state(w, acc, zacc, sm.s[sbuf(c + 1)], pl, g, r, (float)(t0 + kT));
         }
         __syncthreads();
     }
@@ -1091,11 +1208,11 @@ __global__ __launch_bounds__(256) void bwd_qsweep_kernel(const uint16_t* __restr
 
 // ---------------------------------------------------------------- key sweep
 struct KSweepSmem {
-    BwdKSmem<64> t;
-    PubState s;
+    BwdKSmem<64> t[kSweepBuf];
+    PubState s[kSweepBuf];
 };
 
-__global__ __launch_bounds__(256) void bwd_ksweep_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_ksweep_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, int BH, int L, int nch,
                                                          int cps, const uint16_t* __restrict__ ghi_ws,
@@ -1130,44 +1247,55 @@ __global__ __launch_bounds__(256) void bwd_ksweep_kernel(const uint16_t* __restr
         glreg.load(gl, L, c * kT);
         if (threadIdx.x < kT) hreg = c * kT + (int)threadIdx.x < L ? hh[c * kT + threadIdx.x] : 0.f;
     };
-    auto store = [&]() {
-        qreg.store(sm.t.q);
-        ghreg.store(sm.t.ghi);
-        glreg.store(sm.t.glo);
-        if (threadIdx.x < kT) sm.t.h[threadIdx.x] = hreg;
+    auto store = [&](BwdKSmem<DV>& b) {
+        qreg.store(b.q);
+        ghreg.store(b.ghi);
+        glreg.store(b.glo);
+        if (threadIdx.x < kT) b.h[threadIdx.x] = hreg;
+    };
+    // this wave's keys and their value rows, one chunk ahead
+    TokenRegs kregs;
+    u32x4 vrow[2];
+    auto load_k = [&](int c) {
+        const int kw0 = c * kT + 16 * w, kr = kw0 + r;
+        kregs.load(kh, kr, kw0, L, g, r);
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+            vrow[cs] = u32x4{0u, 0u, 0u, 0u};
+            if (kr < L) vrow[cs] = *reinterpret_cast<const u32x4*>(vh + (size_t)kr * DV + 32 * cs + 8 * g);
+        }
     };
     load(c_end - 1);
-    store();
-    publish_state(w, acc, zacc, sm.s, g, r);
+    load_k(c_end - 1);
+    store(sm.t[sbuf(c_end - 1)]);
+    const PubLane pl(g, r);
+    publish_state(w, acc, zacc, sm.s[sbuf(c_end - 1)], pl, g, r, -1.f);
     __syncthreads();
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int t0 = c * kT;
+        const BwdKSmem<DV>& tt = sm.t[sbuf(c)];
+        const PubState& ss = sm.s[sbuf(c)];
         if (c > c_begin) load(c - 1);
         const int kw0 = t0 + 16 * w;  // first key of this wave
-        const int kr = kw0 + r;       // this lane's key
-        bf16x4 kb = __builtin_bit_cast(bf16x4, make_uint2(0u, 0u));
+        const bf16x4 kb = quarter(kregs.sc);  // this lane's key, dims 4g..4g+3, times 1/4
         bf16x8 vb[2];
 #pragma unroll
-        for (int cs = 0; cs < 2; ++cs) vb[cs] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        if (kr < L) {
-            kb = quarter(*reinterpret_cast<const uint2*>(kh + (size_t)kr * kD + 4 * g));
-#pragma unroll
-            for (int cs = 0; cs < 2; ++cs) vb[cs] = ld8(vh + (size_t)kr * DV + 32 * cs + 8 * g);
-        }
+        for (int cs = 0; cs < 2; ++cs) vb[cs] = __builtin_bit_cast(bf16x8, vrow[cs]);
         float xr[16], xj[4];
-        token_rows(kh, kr, kw0, L, g, r, xr, xj);
+        kregs.unpack(xr, xj);
+        if (c > c_begin) load_k(c - 1);
 
         // dv: the chunk's own queries (diagonal tile), then m(k) R^c
         f32x4 dvacc[kNV];
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) dvacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 dkacc = {0.f, 0.f, 0.f, 0.f}, unused = {0.f, 0.f, 0.f, 0.f};
-        k_tile<DV, true>(sm.t, kb, vb, w, g, r, dvacc, dkacc);
-        readout<false>(sm.s, xr, g, r, dvacc, unused);
+        k_tile<DV, true>(tt, kb, vb, w, g, r, dvacc, dkacc);
+        readout<false>(ss, pl, xr, g, dvacc, unused);
         // dk: J_m^T (R^c v + r^c)
         const float ones[4] = {1.f, 1.f, 1.f, 1.f};
         float dx[4] = {0.f, 0.f, 0.f, 0.f};
-        contract_all<false>(std::make_integer_sequence<int, kNTile>{}, sm.s, vb, vb, ones, xj, g, r, dx);
+        contract_all<false>(ss, pl, vb, vb, ones, xj, r, dx);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int kj = kw0 + 4 * g + m;
@@ -1179,11 +1307,11 @@ __global__ __launch_bounds__(256) void bwd_ksweep_kernel(const uint16_t* __restr
         }
 
         // R, r with this chunk's queries
-        update_any<true>(w, sm.t.q, sm.t.ghi, sm.t.glo, sm.t.h, t0, L, g, r, acc, zacc);
-        __syncthreads();
+        update_any<true>(w, tt.q, tt.ghi, tt.glo, tt.h, g, r, acc, zacc);
+        if (kSweepBuf == 1) __syncthreads();
         if (c > c_begin) {
-            store();
-            publish_state(w, acc, zacc, sm.s, g, r);
+            store(sm.t[sbuf(c - 1)]);
+            publish_state(w, acc, zacc, sm.s[sbuf(c - 1)], pl, g, r, -1.f);
         }
         __syncthreads();
     }
