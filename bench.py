@@ -476,29 +476,47 @@ def bench_other_sizes(based):
     return out
 
 
-def bench_backward(based, wl, reps=40):
-    """Gradients of the prefill output over the workload (bf16 inputs with
-    feature dim 16: the matrix-core kernels, direct form).  Returns (event
-    seconds per call, algorithmic flops): per causal (i, j) pair
-    8d + 6d_v + 12 flops (scores twice, weights, g.v, dq, dk, dv and N)."""
+SYM_FEATURES = 1 + 16 + 16 * 17 // 2  # 153 distinct Taylor features for d' = 16
+
+
+def backward_flops(wl, form: str) -> float:
+    """Algorithmic flops of the gradients over a workload.  Direct form: per
+    causal (i, j) pair 8d + 6d_v + 12 (scores twice, weights, g.v, dq, dk,
+    dv and N).  Chunked form (64-token chunks): per token six products
+    with the 153 distinct features of d' = 16 (readout y, g S^T, S update,
+    R update, R v, phi(k) R: 2 x 153 x d_v flops each) plus the direct
+    form's pairs inside the token's chunk (65/2 per token on average)."""
+    per_pair = 8 * wl.d + 6 * wl.dv + 12
+    if form == "direct":
+        return wl.B * wl.H * wl.L * (wl.L + 1) // 2 * per_pair
+    return wl.B * wl.H * wl.L * (6 * 2 * SYM_FEATURES * wl.dv + (wl.chunk + 1) / 2 * per_pair)
+
+
+def backward_bytes(wl) -> float:
+    """Algorithmic HBM bytes of the gradients: q, k, v (bf16) and dy (fp32)
+    read once, dq, dk, dv (fp32) written once."""
+    return wl.B * wl.H * wl.L * (2 * (2 * wl.d + wl.dv) + 4 * wl.dv + 4 * (2 * wl.d + wl.dv))
+
+
+def backward_sets(based, wl, form: str):
+    """One gradient call over the workload (bf16 inputs with feature dim 16,
+    a seeded dy), as fn(i) for time_leg."""
     q, k, v = (x.cuda() for x in si.linear_inputs(wl))
-    dy = torch.randn(wl.B, wl.H, wl.L, wl.dv, device="cuda")
+    dy = torch.randn(wl.B, wl.H, wl.L, wl.dv, generator=torch.Generator().manual_seed(2300)).cuda()
     outs = (torch.empty(wl.B, wl.H, wl.L, wl.d, device="cuda"), torch.empty(wl.B, wl.H, wl.L, wl.d, device="cuda"),
             torch.empty(wl.B, wl.H, wl.L, wl.dv, device="cuda"))
     ws = torch.empty(based.based_prefill_backward_workspace_bytes(wl.B, wl.H, wl.L, wl.dv, wl.d), dtype=torch.uint8,
                      device="cuda")
-    run = lambda: based.based_prefill_backward(q, k, v, dy, eps=wl.eps, dq=outs[0], dk=outs[1], dv=outs[2],
-                                               workspace=ws)
-    for _ in range(100):  # untimed warm-up, ~50 ms
-        run()
-    t = RegionTimer()
-    torch.cuda.synchronize()
-    t.start()
-    for _ in range(reps):
-        run()
-    t.stop()
-    pairs = wl.B * wl.H * wl.L * (wl.L + 1) // 2
-    return t.seconds() / reps, pairs * (8 * wl.d + 6 * wl.dv + 12)
+
+    def run(i):
+        based.based_prefill_backward(q, k, v, dy, eps=wl.eps, form=form, dq=outs[0], dk=outs[1], dv=outs[2],
+                                     workspace=ws)
+    return run
+
+
+def bench_backward(based, wl, form: str, n: int):
+    """Mean seconds per gradient call and the per-call distribution."""
+    return time_leg(backward_sets(based, wl, form), n, settle_s=0.1, dist_n=10)
 
 
 def _oracle():
@@ -620,6 +638,9 @@ def profile_leg(name: str, launches: int = 8) -> None:
 
         def step(i):
             based.based_decode_step(*steps[i % 4], S, z, eps=wl.eps)
+    elif name in ("backward_360m", "backward_64k"):
+        wl = si.WORKLOADS["prefill_360m" if name == "backward_360m" else "long_64k"]
+        step = backward_sets(based, wl, "chunked")
     elif name == "window_8k":
         wl = si.WORKLOADS["window_8k"]
         qw, kw = si.window_inputs(wl)
@@ -666,7 +687,7 @@ def main():
     ap.add_argument("--window-decode-steps", type=int, default=4096)
     ap.add_argument("--profile-leg", default=None,
                     choices=["prefill_360m", "long_64k", "hybrid_8k", "decode_1p3b", "window_8k", "window_decode_1p3b",
-                             "setup_1p3b", "linear_8k"],
+                             "setup_1p3b", "linear_8k", "backward_360m", "backward_64k"],
                     help="only launch one leg's kernels a few times (untimed), for rocprofv3 counter passes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to calibrate "
@@ -818,14 +839,20 @@ def main():
             "note": "w=64 ring, B=128, H=16, d_qk=64, d_v=128, fused add; HIP graph of 64 steps "
                     "replayed, 16 cache sets"}
         print(f"[bench] window decode: {wkern*1e6:.1f} us/step", file=sys.stderr, flush=True)
-        w2 = si.WORKLOADS["prefill_360m"]
-        bsec, bflops = bench_backward(based, w2)
-        extra["prefill_360m_backward"] = {
-            "kernel_ms": bsec * 1e3, "tokens_per_s": w2.B * w2.L / bsec, "direct_form_flops": bflops,
-            "tflops": bflops / bsec / 1e12, "mfma_frac": bflops / bsec / MFMA_BF16_PEAK,
-            "note": "dq, dk, dv for a seeded dy; bf16 matrix cores (weights as bf16 hi/lo pairs, fp32 "
-                    "accumulation), direct form (O(L^2) per head)"}
-        print(f"[bench] backward: {bsec*1e3:.2f} ms, {bflops/bsec/1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        for bname, forms in (("prefill_360m", ("chunked", "direct")), ("long_64k", ("chunked",))):
+            bw = si.WORKLOADS[bname]
+            leg = {}
+            for form in forms:
+                bsec, bdist = bench_backward(based, bw, form, 30 if bname == "long_64k" else 100)
+                leg[form] = {"kernel_us": bsec * 1e6, "tokens_per_s": bw.B * bw.L / bsec, "dist_us": bdist,
+                             "roofline": roofline(backward_bytes(bw), bsec, None, backward_flops(bw, form))}
+                print(f"[bench] backward {bname} {form}: {bsec*1e6:.1f} us", file=sys.stderr, flush=True)
+            leg["auto_form"] = "chunked"
+            leg["note"] = ("dq, dk, dv for a seeded dy, bf16 inputs, fp32 accumulation on the bf16 matrix cores "
+                           "(non-input operands as bf16 hi/lo pairs).  chunked: linear in L through the carried "
+                           "state (segment sums, scans, query sweep, key sweep); direct: pair by pair, O(L^2) "
+                           "per head.  Flops are each form's own algorithmic count (backward_flops).")
+            extra[f"{bname}_backward"] = leg
         oth = bench_other_sizes(based)
         extra.update(oth)
         print("[bench] other sizes: " + ", ".join(f"{k} {v['kernel_us']:.1f} us" for k, v in oth.items()),
