@@ -121,7 +121,7 @@ __device__ __forceinline__ int win_idx(int row, int col) {
     return row * kWinD + 8 * ((col >> 3) ^ (row & 7)) + (col & 7);
 }
 
-enum { kModeFull = 0, kModeState = 1, kModeSegment = 2 };
+enum { kModeFull = 0, kModeSegment = 2 };
 
 template <int T, int DV>
 __device__ __forceinline__ void ws_store(const f32x4 (&acc)[DV / 16 + 1], float* slot, int lane);
@@ -571,10 +571,10 @@ __device__ __forceinline__ void offdiag_wave(const uint16_t* __restrict__ qh, co
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (L + kC - 1) / kC;
-    // Q and K staging: waves 0, 1 (K) and 2, 3 (Q); only K without outputs
+    // Q and K staging: waves 0, 1 (K) and 2, 3 (Q)
     StagePipe<DV, false, true> pipe;
     pipe.vu = -1;
-    pipe.t = (MODE == kModeState && W >= 2) ? -1 : (int)threadIdx.x;
+    pipe.t = (int)threadIdx.x;
     pipe.qh = qh;
     pipe.kh = kh;
     pipe.vh = nullptr;
@@ -584,58 +584,56 @@ __device__ __forceinline__ void offdiag_wave(const uint16_t* __restrict__ qh, co
 
     __syncthreads();  // first chunk staged, initial state published
     auto step = [&](int c, typename StagePipe<DV, false, true>::Regs& regs) {
-        if (MODE != kModeState) {
-            const int buf = c & 1;
-            f32x4 y[kNCT];
+        const int buf = c & 1;
+        f32x4 y[kNCT];
 #pragma unroll
-            for (int ct = 0; ct < kNCT; ++ct) y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-            float qr[16];
-            const float* qf = &sm.qf[buf][0];
+        for (int ct = 0; ct < kNCT; ++ct) y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float qr[16];
+        const float* qf = &sm.qf[buf][0];
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(qf + qf_idx(16 * W + r, 4 * ((g + cc) & 3)));
-                qr[4 * cc + 0] = x[0];
-                qr[4 * cc + 1] = x[1];
-                qr[4 * cc + 2] = x[2];
-                qr[4 * cc + 3] = x[3];
-            }
-            const uint16_t* shi = &sm.s_hi[buf][0];
-            const uint16_t* slo = &sm.s_lo[buf][0];
-#define BASED_READOUT_STEP(J)                                                                             \
-    {                                                                                                     \
-        float a[8];                                                                                       \
-        psi_q<J>(qr, g, a);                                                                               \
-        const bf16x8 ahi = pack8(a);                                                                      \
-        _Pragma("unroll") for (int ct = 0; ct < kNV; ++ct)                                                \
-            y[ct] = mfma32(ahi, lds_bf16x8(shi + (16 * ct + r) * kSRow + 8 * unit_swz(4 * (J) + g, r)), y[ct]); \
-        y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_hi[buf][8 * (4 * (J) + g)]), y[kNV]);                       \
-    }
-            BASED_READOUT_STEP(0)
-            BASED_READOUT_STEP(1)
-            BASED_READOUT_STEP(2)
-            BASED_READOUT_STEP(3)
-#undef BASED_READOUT_STEP
-            // last feature k-step (pairs (r, r+8), constant, linear): hi/lo on both sides
-            float a[8];
-            psi_q<4>(qr, g, a);
-            bf16x8 ahi, alo;
-            pack8_hilo(a, ahi, alo);
-            bf16x8 sb[kNCT];
-#pragma unroll
-            for (int ct = 0; ct < kNV; ++ct) sb[ct] = lds_bf16x8(shi + (16 * ct + r) * kSRow + 8 * unit_swz(16 + g, r));
-            sb[kNV] = lds_bf16x8(&sm.z_hi[buf][8 * (16 + g)]);
-#pragma unroll
-            for (int ct = 0; ct < kNCT; ++ct) y[ct] = mfma32(ahi, sb[ct], y[ct]);
-#pragma unroll
-            for (int ct = 0; ct < kNCT; ++ct) y[ct] = mfma32(alo, sb[ct], y[ct]);
-#pragma unroll
-            for (int ct = 0; ct < kNV; ++ct)
-                y[ct] = mfma32(ahi, lds_bf16x8(slo + (16 * ct + r) * kLoRow + 8 * unit_swz(g, r)), y[ct]);
-            y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_lo[buf][8 * g]), y[kNV]);
-            f32x4* dst = reinterpret_cast<f32x4*>(&sm.hand[buf][W][0]);
-#pragma unroll
-            for (int ct = 0; ct < kNCT; ++ct) dst[ct * 64 + lane] = y[ct];
+        for (int cc = 0; cc < 4; ++cc) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(qf + qf_idx(16 * W + r, 4 * ((g + cc) & 3)));
+            qr[4 * cc + 0] = x[0];
+            qr[4 * cc + 1] = x[1];
+            qr[4 * cc + 2] = x[2];
+            qr[4 * cc + 3] = x[3];
         }
+        const uint16_t* shi = &sm.s_hi[buf][0];
+        const uint16_t* slo = &sm.s_lo[buf][0];
+#define BASED_READOUT_STEP(J)                                                                             \
+{                                                                                                     \
+    float a[8];                                                                                       \
+    psi_q<J>(qr, g, a);                                                                               \
+    const bf16x8 ahi = pack8(a);                                                                      \
+    _Pragma("unroll") for (int ct = 0; ct < kNV; ++ct)                                                \
+        y[ct] = mfma32(ahi, lds_bf16x8(shi + (16 * ct + r) * kSRow + 8 * unit_swz(4 * (J) + g, r)), y[ct]); \
+    y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_hi[buf][8 * (4 * (J) + g)]), y[kNV]);                       \
+}
+        BASED_READOUT_STEP(0)
+        BASED_READOUT_STEP(1)
+        BASED_READOUT_STEP(2)
+        BASED_READOUT_STEP(3)
+#undef BASED_READOUT_STEP
+        // last feature k-step (pairs (r, r+8), constant, linear): hi/lo on both sides
+        float a[8];
+        psi_q<4>(qr, g, a);
+        bf16x8 ahi, alo;
+        pack8_hilo(a, ahi, alo);
+        bf16x8 sb[kNCT];
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) sb[ct] = lds_bf16x8(shi + (16 * ct + r) * kSRow + 8 * unit_swz(16 + g, r));
+        sb[kNV] = lds_bf16x8(&sm.z_hi[buf][8 * (16 + g)]);
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct) y[ct] = mfma32(ahi, sb[ct], y[ct]);
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct) y[ct] = mfma32(alo, sb[ct], y[ct]);
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct)
+            y[ct] = mfma32(ahi, lds_bf16x8(slo + (16 * ct + r) * kLoRow + 8 * unit_swz(g, r)), y[ct]);
+        y[kNV] = mfma32(ahi, lds_bf16x8(&sm.z_lo[buf][8 * g]), y[kNV]);
+        f32x4* dst = reinterpret_cast<f32x4*>(&sm.hand[buf][W][0]);
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct) dst[ct * 64 + lane] = y[ct];
         pipe.advance(regs, sm, c, nchunks);
         __syncthreads();
     };
@@ -766,11 +764,6 @@ __device__ __forceinline__ void window_wave(const uint16_t* __restrict__ q2h, co
     const int t = threadIdx.x - 768;  // 0..255
     const int lane = t & 63, g = lane >> 4, r = lane & 15;
     const int nchunks = (len + kC - 1) / kC;
-    if constexpr (MODE == kModeState) {
-        __syncthreads();
-        for (int c = 0; c < nchunks; ++c) __syncthreads();
-        return;
-    }
     WinRegs rg;
     bf16x8 qc[2], qn[2];
     // prologue: chunk -1 (the halo of the first chunk) into slot 2, chunk 0 into slot 0
@@ -821,10 +814,6 @@ __device__ __forceinline__ void ondiag_wave(int L, int ldv, float eps,
     const int nchunks = (L + kC - 1) / kC;
 
     __syncthreads();  // first chunk staged, initial state published
-    if constexpr (MODE == kModeState) {
-        for (int c = 0; c < nchunks; ++c) __syncthreads();
-        return;
-    }
     // Chunk c's rows: add the off-diagonal part, normalise, store.  nrows
     // is the number of valid rows of the chunk (64 except at the end).  The
     // on-diagonal sums yd are 32 times the method's (see diag_block): the
@@ -892,8 +881,7 @@ template <int U, int DV, int MODE>
 __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, const uint16_t* __restrict__ kh,
                                             const uint16_t* __restrict__ vh, int L, int ldv, float* __restrict__ Sh,
                                             float* __restrict__ zh, bool own_z, int use_init, PrefillSmem<DV>& sm,
-                                            const float* ws_in, float* ws_out, bool write_final, int ws_nct,
-                                            int ws_ct0) {
+                                            const float* ws_in, bool write_final, int ws_nct, int ws_ct0) {
     constexpr int kNV = DV / 16, kNCT = kNV + 1;
     constexpr int kNT = U < 2 ? 3 : 2;
     const int u = threadIdx.x - 256;  // 0..255
@@ -929,10 +917,8 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
     pipe.ldv = ldv;
     pipe.L = L;
     pipe.prologue(sm, nchunks);
-    if (MODE != kModeState) {
-        publish_pair<U, DV>(acc[0], acc[1], sm, 0, g, r);
-        if constexpr (kNT == 3) publish_last<U, DV>(acc[2], sm, 0, g, r);
-    }
+    publish_pair<U, DV>(acc[0], acc[1], sm, 0, g, r);
+    if constexpr (kNT == 3) publish_last<U, DV>(acc[2], sm, 0, g, r);
     __syncthreads();
 
     const bf16x8 ones = ones8();
@@ -984,11 +970,8 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
         pipe.advance(regs, sm, c, nchunks);
 
         // ---- publish the state after this chunk for the next readout
-        if (MODE != kModeState) {
-            const int wbuf = buf ^ 1;
-            publish_pair<U, DV>(acc[0], acc[1], sm, wbuf, g, r);
-            if constexpr (kNT == 3) publish_last<U, DV>(acc[2], sm, wbuf, g, r);
-        }
+        publish_pair<U, DV>(acc[0], acc[1], sm, buf ^ 1, g, r);
+        if constexpr (kNT == 3) publish_last<U, DV>(acc[2], sm, buf ^ 1, g, r);
         __syncthreads();
     };
     for (int c = 0; c < nchunks; c += 2) {
@@ -1001,38 +984,11 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
     if constexpr (U == 0) {
         if (g == 2) acc[2][kNV][0] -= (float)(nchunks * kC - L);
     }
-    if (MODE == kModeState) {
-        ws_store<U, DV>(acc[0], ws_out, lane);
-        ws_store<U + 4, DV>(acc[1], ws_out, lane);
-        if constexpr (kNT == 3) ws_store<U + 8, DV>(acc[2], ws_out, lane);
-    } else if (write_final) {
+    if (write_final) {
         store_final<U, DV>(acc[0], Sh, zh, ldv, own_z, use_init, g, r);
         store_final<U + 4, DV>(acc[1], Sh, zh, ldv, own_z, use_init, g, r);
         if constexpr (kNT == 3) store_final<U + 8, DV>(acc[2], Sh, zh, ldv, own_z, use_init, g, r);
     }
-}
-
-// Initial state of every segment split (state-only pass, last segment slot):
-// the caller's state in readout units, or zero.
-template <int U, int DV>
-__device__ __forceinline__ void init_to_workspace(const float* Sh, const float* zh, int ldv, int use_init,
-                                                  float* ws_out) {
-    constexpr int kNCT = DV / 16 + 1;
-    constexpr int kNT = U < 2 ? 3 : 2;
-    const int lane = (threadIdx.x - 256) & 63, g = lane >> 4, r = lane & 15;
-    f32x4 acc[kNT][kNCT];
-#pragma unroll
-    for (int ti = 0; ti < kNT; ++ti)
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct) acc[ti][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (use_init) {
-        load_initial<U, DV>(acc[0], Sh, zh, ldv, g, r);
-        load_initial<U + 4, DV>(acc[1], Sh, zh, ldv, g, r);
-        if constexpr (kNT == 3) load_initial<U + 8, DV>(acc[2], Sh, zh, ldv, g, r);
-    }
-    ws_store<U, DV>(acc[0], ws_out, lane);
-    ws_store<U + 4, DV>(acc[1], ws_out, lane);
-    if constexpr (kNT == 3) ws_store<U + 8, DV>(acc[2], ws_out, lane);
 }
 
 // Workspace: one state per (segment slot, head) in accumulator layout,
@@ -1065,9 +1021,6 @@ __device__ __forceinline__ void ws_load(f32x4 (&acc)[DV / 16 + 1], const float* 
 // One workgroup = 12 waves (roles above).  MODE
 //   kModeFull:    one workgroup per (head, column group) walks the whole
 //                 sequence.
-//   kModeState:   workgroup (head, s), s < nseg-1: state increment of
-//                 segment s into slot s+1; s = nseg-1: the initial state
-//                 into slot 0.
 //   kModeSegment: workgroup (head, s): outputs of segment s starting from
 //                 slot s (after the prefix sum); the last segment writes the
 //                 final state.
@@ -1107,7 +1060,6 @@ __global__ __launch_bounds__(HYB ? 1024 : 768, 1) void prefill_mfma_kernel(
     float* zh = z + (size_t)head * kNumFeat;
     const bool own_z = cg == 0;  // every column group carries z; the first writes it
     float* ws_in = nullptr;
-    float* ws_out = nullptr;
     // The fused layer's segment pass reads the state of a 64-column state
     // pass (one slot per head, segment and 64-column group): its column
     // group's tiles of it.
@@ -1119,21 +1071,9 @@ __global__ __launch_bounds__(HYB ? 1024 : 768, 1) void prefill_mfma_kernel(
             ws_in = ws + (((size_t)seg * BH + head) * (ldv / 64) + cg / 2) * ws_slot_floats<64>();
         } else {
             ws_in = ws + (((size_t)seg * BH + head) * ncg + cg) * ws_slot_floats<DV>();
-            ws_out = ws + (((size_t)((seg + 1) % nseg) * BH + head) * ncg + cg) * ws_slot_floats<DV>();
         }
     }
     const int w = threadIdx.x >> 6;
-    if (MODE == kModeState && seg == nseg - 1) {
-        // This workgroup's slot job is the initial state (no sweep, no barrier).
-        switch (w) {
-            case 4: init_to_workspace<0, DV>(Sh, zh, ldv, use_init, ws_out); break;
-            case 5: init_to_workspace<1, DV>(Sh, zh, ldv, use_init, ws_out); break;
-            case 6: init_to_workspace<2, DV>(Sh, zh, ldv, use_init, ws_out); break;
-            case 7: init_to_workspace<3, DV>(Sh, zh, ldv, use_init, ws_out); break;
-            default: break;
-        }
-        return;
-    }
     const bool write_final = MODE == kModeFull || seg == nseg - 1;
     // Waves w, w + 4 and w + 8 share a SIMD: the off-diagonal wave of query
     // tile w, update wave w (three state tiles for w < 2) and the
@@ -1147,10 +1087,10 @@ __global__ __launch_bounds__(HYB ? 1024 : 768, 1) void prefill_mfma_kernel(
         case 9: ondiag_wave<1, DV, MODE, HYB>(len, ldv, eps, yh, sm, wsm); break;
         case 10: ondiag_wave<2, DV, MODE, HYB>(len, ldv, eps, yh, sm, wsm); break;
         case 11: ondiag_wave<3, DV, MODE, HYB>(len, ldv, eps, yh, sm, wsm); break;
-        case 4: update_wave<0, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final, ws_nct, ws_ct0); break;
-        case 5: update_wave<1, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final, ws_nct, ws_ct0); break;
-        case 6: update_wave<2, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final, ws_nct, ws_ct0); break;
-        case 7: update_wave<3, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, ws_out, write_final, ws_nct, ws_ct0); break;
+        case 4: update_wave<0, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, write_final, ws_nct, ws_ct0); break;
+        case 5: update_wave<1, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, write_final, ws_nct, ws_ct0); break;
+        case 6: update_wave<2, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, write_final, ws_nct, ws_ct0); break;
+        case 7: update_wave<3, DV, MODE>(qh, kh, vh, len, ldv, Sh, zh, own_z, use_init, sm, ws_in, write_final, ws_nct, ws_ct0); break;
         default: break;
     }
     if constexpr (HYB) {
