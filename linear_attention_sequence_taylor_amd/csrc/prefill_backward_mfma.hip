@@ -788,6 +788,22 @@ __device__ __forceinline__ void state_load(int w, const float* slot, int g, int 
     for (int i = 0; i < 3; ++i)
         zacc[i] = slot && g == 0 && z_owned(w, i) ? slot[kSlot * 64 + 16 * z_tile(w, i) + r] : 0.f;
 }
+// The sum of n states at first, first + step, ... (n = 0: zero): a
+// sweep's carried-in state straight from the segment sums, without a scan
+// launch, when there are few segments.
+__device__ __forceinline__ void state_load_sum(int w, const float* first, size_t step, int n, int g, int r,
+                                               f32x4 (&acc)[10], float (&zacc)[3]) {
+    state_load(w, n > 0 ? first : nullptr, g, r, acc, zacc);
+    for (int i = 1; i < n; ++i) {
+        f32x4 a2[10];
+        float z2[3];
+        state_load(w, first + i * step, g, r, a2, z2);
+#pragma unroll
+        for (int j = 0; j < 10; ++j) acc[j] += a2[j];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) zacc[j] += z2[j];
+    }
+}
 __device__ __forceinline__ void state_store(int w, const f32x4 (&acc)[10], const float (&zacc)[3], float* slot,
                                             int g, int r, float zconst) {
 #pragma unroll
@@ -1074,7 +1090,8 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_qsweep_kernel(const ui
                                                          const uint16_t* __restrict__ v,
                                                          const float* __restrict__ dy, int BH, int L, int nch,
                                                          int cps, float eps, const float* __restrict__ s_init,
-                                                         float* __restrict__ dq, uint16_t* __restrict__ ghi_ws,
+                                                         int fold, float* __restrict__ dq,
+                                                         uint16_t* __restrict__ ghi_ws,
                                                          uint16_t* __restrict__ glo_ws, float* __restrict__ h_ws) {
     constexpr int DV = 64, kNV = 4;
     __shared__ QSweepSmem sm;
@@ -1088,7 +1105,14 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_qsweep_kernel(const ui
 
     f32x4 acc[10];
     float zacc[3];
-    state_load(w, s_init && seg > 0 ? s_init + ((size_t)seg * BH + head) * kStateFloats : nullptr, g, r, acc, zacc);
+    // the state before this segment: its scanned slot, or (fold) the sum of
+    // the earlier segments' slots
+    if (fold)
+        state_load_sum(w, s_init ? s_init + (size_t)head * kStateFloats : nullptr, (size_t)BH * kStateFloats,
+                       s_init ? seg : 0, g, r, acc, zacc);
+    else
+        state_load(w, s_init && seg > 0 ? s_init + ((size_t)seg * BH + head) * kStateFloats : nullptr, g, r, acc,
+                   zacc);
     TileRegs<kD> kreg;
     TileRegs<DV> vreg;
     kreg.load(kh, L, c_begin * kT);
@@ -1218,7 +1242,8 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_ksweep_kernel(const ui
                                                          int cps, const uint16_t* __restrict__ ghi_ws,
                                                          const uint16_t* __restrict__ glo_ws,
                                                          const float* __restrict__ h_ws,
-                                                         const float* __restrict__ r_init, float* __restrict__ dk,
+                                                         const float* __restrict__ r_init, int fold,
+                                                         float* __restrict__ dk,
                                                          float* __restrict__ dvo) {
     constexpr int DV = 64, kNV = 4;
     __shared__ KSweepSmem sm;
@@ -1236,8 +1261,14 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_ksweep_kernel(const ui
 
     f32x4 acc[10];
     float zacc[3];
-    state_load(w, r_init && seg < nseg - 1 ? r_init + ((size_t)seg * BH + head) * kStateFloats : nullptr, g, r, acc,
-               zacc);
+    // the sums after this segment: its scanned slot, or (fold) the sum of
+    // the later segments' slots
+    if (fold)
+        state_load_sum(w, r_init ? r_init + ((size_t)(seg + 1) * BH + head) * kStateFloats : nullptr,
+                       (size_t)BH * kStateFloats, r_init ? nseg - 1 - seg : 0, g, r, acc, zacc);
+    else
+        state_load(w, r_init && seg < nseg - 1 ? r_init + ((size_t)seg * BH + head) * kStateFloats : nullptr, g, r,
+                   acc, zacc);
     TileRegs<kD> qreg;
     TileRegs<DV> ghreg, glreg;
     float hreg = 0.f;
@@ -1357,6 +1388,9 @@ static void chunk_plan(int BH, int L, int& nch, int& cps, int& nseg) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Up to this many segments the sweeps add up the segment sums themselves.
+static constexpr int kFoldSegments = 8;
+
 size_t prefill_backward_chunked_workspace_bytes(int BH, int L) {
     int nch, cps, nseg;
     chunk_plan(BH, L, nch, cps, nseg);
@@ -1380,20 +1414,23 @@ hipError_t launch_prefill_backward_chunked(const void* q, const void* k, const v
     float* s_states = reinterpret_cast<float*>(base + align256((size_t)BH * L * (64 + 1) * sizeof(float)));
     float* r_states = reinterpret_cast<float*>(reinterpret_cast<char*>(s_states) + sbytes);
     const unsigned scan_blocks = (unsigned)(((size_t)BH * kStateFloats + 255) / 256);
+    // With few segments each sweep sums the earlier (later) segments' slots
+    // itself instead of a scan launch.
+    const int fold = nseg <= kFoldSegments;
     if (nseg > 1) {
         hipLaunchKernelGGL((bwd_segsum_kernel<true>), dim3((unsigned)(BH * (nseg - 1))), dim3(256), 0, st, kk, vv,
                            nullptr, nullptr, BH, L, nch, cps, 0, s_states);
-        hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, st, s_states, BH, nseg, 0);
+        if (!fold) hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, st, s_states, BH, nseg, 0);
     }
     hipLaunchKernelGGL(bwd_qsweep_kernel, dim3((unsigned)(BH * nseg)), dim3(256), 0, st, qq, kk, vv, dy, BH, L, nch,
-                       cps, eps, nseg > 1 ? s_states : nullptr, dq, ghi, glo, h_ws);
+                       cps, eps, nseg > 1 ? s_states : nullptr, fold, dq, ghi, glo, h_ws);
     if (nseg > 1) {
         hipLaunchKernelGGL((bwd_segsum_kernel<false>), dim3((unsigned)(BH * (nseg - 1))), dim3(256), 0, st, qq, ghi,
                            glo, h_ws, BH, L, nch, cps, 1, r_states);
-        hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, st, r_states, BH, nseg, 1);
+        if (!fold) hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, st, r_states, BH, nseg, 1);
     }
     hipLaunchKernelGGL(bwd_ksweep_kernel, dim3((unsigned)(BH * nseg)), dim3(256), 0, st, qq, kk, vv, BH, L, nch, cps,
-                       ghi, glo, h_ws, nseg > 1 ? r_states : nullptr, dk, dvo);
+                       ghi, glo, h_ws, nseg > 1 ? r_states : nullptr, fold, dk, dvo);
     return hipGetLastError();
 }
 
