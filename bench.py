@@ -844,8 +844,12 @@ def main():
             leg = {}
             for form in forms:
                 bsec, bdist = bench_backward(based, bw, form, 30 if bname == "long_64k" else 100)
+                traffic = None
+                if form == "chunked":
+                    traffic = read_traffic(f"prefill_backward_mfma_{'backward_360m' if bname == 'prefill_360m' else 'backward_64k'}"
+                                           "_pmc.txt", source_digest("prefill_backward_mfma.hip", "common.hpp"))
                 leg[form] = {"kernel_us": bsec * 1e6, "tokens_per_s": bw.B * bw.L / bsec, "dist_us": bdist,
-                             "roofline": roofline(backward_bytes(bw), bsec, None, backward_flops(bw, form))}
+                             "roofline": roofline(backward_bytes(bw), bsec, traffic, backward_flops(bw, form))}
                 print(f"[bench] backward {bname} {form}: {bsec*1e6:.1f} us", file=sys.stderr, flush=True)
             leg["auto_form"] = "chunked"
             leg["note"] = ("dq, dk, dv for a seeded dy, bf16 inputs, fp32 accumulation on the bf16 matrix cores "
