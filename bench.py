@@ -254,12 +254,11 @@ def prefill_sets(based, wl, n_sets=N_SETS):
     return step
 
 
-def bench_prefill(based, wl, steps, warmup, settle_s=0.3):
+def bench_headline(step, steps, warmup, settle_s=0.3):
     """The headline leg.  Settle phase, W warm-up steps, then K steps
     captured in a HIP graph and replayed once: returns (wall seconds per
     step, mean launch seconds from events around the replay, per-launch
     distribution)."""
-    step = prefill_sets(based, wl)
     settle(step, settle_s)
     for i in range(warmup):
         step(i)
@@ -286,6 +285,62 @@ def bench_prefill(based, wl, steps, warmup, settle_s=0.3):
     wall = time.perf_counter() - t0
     dist = launch_distribution(step, min(max(steps, 20), 50))
     return wall / steps, timer.seconds() / steps, dist
+
+
+def headline_spec(based, cfg: str) -> dict:
+    """The step of the headline configuration: the library call(s) of one
+    step over synthetic inputs of the configuration's shape, tokens per step,
+    algorithmic bytes (and flops where the matrix cores carry the leg), the
+    counter summary behind `traffic` and the JSON `config`."""
+    wl = si.WORKLOADS[CONFIGS[cfg]]
+    conf = {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d_feat": wl.d, "d_v": wl.dv, "chunk": wl.chunk,
+            "scale": wl.scale, "parallelism": "single GPU"}
+    if cfg in ("cfg2", "cfg5"):
+        return {"wl": wl, "step": prefill_sets(based, wl), "tokens": wl.B * wl.L, "bytes": prefill_bytes(wl),
+                "flops": prefill_flops(wl), "kernel": "based_prefill (bf16 MFMA)",
+                "traffic": (f"prefill_mfma_{wl.name}_pmc.txt", ("prefill_mfma.hip", "common.hpp")), "config": conf}
+    if cfg == "cfg3":
+        # the state of a 1024-token prefix, then steps cycling over 4 input sets
+        q, k, v = (t.cuda() for t in si.linear_inputs(wl))
+        S = torch.empty(wl.B, wl.H, F, wl.dv, device="cuda")
+        z = torch.empty(wl.B, wl.H, F, device="cuda")
+        based.based_prefill(q, k, v, chunk=wl.chunk, eps=wl.eps, S=S, z=z)
+        del q, k, v
+        ins = [tuple(t.cuda() for t in si.decode_inputs(wl, t)) for t in range(N_SETS)]
+        y = torch.empty(wl.B, wl.H, wl.dv, device="cuda")
+
+        def step(i):
+            based.based_decode_step(*ins[i % N_SETS], S, z, eps=wl.eps, y=y)
+        conf.update({"L": 1, "prefix": wl.L})
+        return {"wl": wl, "step": step, "tokens": wl.B, "bytes": decode_bytes(wl), "flops": None,
+                "kernel": "based_decode_step", "traffic": ("decode_step_decode_1p3b_pmc.txt", ("decode.hip", "common.hpp")),
+                "config": conf}
+    if cfg == "cfg4":
+        q, k, v = si.linear_inputs(wl)
+        qw, kw = si.window_inputs(wl)
+        sets = make_sets((q, k, qw, kw, v), 2)
+        ws = torch.empty(max(based.based_hybrid_prefill_workspace_bytes(wl.B, wl.H, wl.L, wl.dv), 1),
+                         dtype=torch.uint8, device="cuda")
+        ys = [torch.empty(wl.B, wl.H, wl.L, wl.dv, device="cuda") for _ in range(2)]
+
+        def step(i):
+            based.based_hybrid_prefill(*sets[i % 2], chunk=wl.chunk, eps=wl.eps, window=wl.window,
+                                       scale=wl.swa_scale, y=ys[i % 2], workspace=ws)
+        conf.update({"window": wl.window, "d_qk": wl.d_qk})
+        return {"wl": wl, "step": step, "tokens": wl.B * wl.L, "bytes": hybrid_bytes(wl), "flops": None,
+                "kernel": "based_hybrid_prefill", "config": conf,
+                "traffic": ("prefill_mfma_hybrid_window_8k_pmc.txt", ("prefill_mfma.hip", "common.hpp"))}
+    # cfg1: the tiny fp32 layer, linear attention then the window adding into y
+    q, k, v = (t.cuda() for t in si.linear_inputs(wl))
+    y = torch.empty(1, 1, wl.L, wl.dv, device="cuda")
+    S, z = torch.empty(1, 1, F, wl.dv, device="cuda"), torch.empty(1, 1, F, device="cuda")
+
+    def step(i):
+        based.based_prefill(q, k, v, chunk=wl.chunk, eps=wl.eps, y=y, S=S, z=z)
+        based.swa_forward(q, k, v, window=wl.window, scale=wl.swa_scale, add=y, y=y)
+    conf.update({"window": wl.window})
+    return {"wl": wl, "step": step, "tokens": wl.L, "bytes": prefill_bytes(wl) + swa_bytes(wl), "flops": None,
+            "kernel": "based_prefill + swa_forward (fp32)", "traffic": None, "config": conf}
 
 
 def bench_prefill_leg(based, wl, n=50):
@@ -548,6 +603,49 @@ def cpu_baseline(wl, budget_s=8.0):
             "single_core_tokens_per_s": wl.L / wl.H / one, **cpu_info()}
 
 
+def cpu_baseline_for(cfg: str, wl) -> dict:
+    """The oracle timed on the headline configuration's own work: the
+    prefill configurations through cpu_baseline; the 1.3B next-token steps,
+    the 8K hybrid layer and the tiny layer on a bounded sample of them."""
+    if cfg in ("cfg2", "cfg5"):
+        return cpu_baseline(wl)
+    oracle = _oracle()
+    th = oracle.num_threads()
+    if cfg == "cfg3":
+        # one sequence (all H heads) from the oracle's state of its 1024-token prefix, 64 steps
+        q, k, v = (t[0] for t in si.linear_inputs(wl, B=1))
+        _, S, z = oracle.la_recurrent(q, k, v, eps=wl.eps, want_y=False)
+        steps = [tuple(t[0] for t in si.decode_inputs(wl, i, B=1)) for i in range(wl.decode_steps)]
+
+        def dec(n):
+            Sx, zx = S[:n], z[:n]
+            for qt, kt, vt in steps:
+                _, Sx, zx = oracle.decode_step(qt[:n], kt[:n], vt[:n], Sx, zx, eps=wl.eps)
+        dt, one = cpu_heads(dec, wl.H, th)
+        return {"value": len(steps) / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
+                "sample": f"1 of {wl.B} sequences ({wl.H} heads), {len(steps)} decode_step calls from the state of "
+                          f"its {wl.L}-token prefix, {dt:.2f} s",
+                "single_core_tokens_per_s": len(steps) / wl.H / one, **cpu_info()}
+    if cfg == "cfg4":
+        q, k, v = (t[0] for t in si.linear_inputs(wl, B=1))
+        qw, kw = (t[0] for t in si.window_inputs(wl, B=1))
+
+        def layer(n):
+            oracle.la_recurrent(q[:n], k[:n], v[:n], eps=wl.eps)
+            oracle.swa(qw[:n], kw[:n], v[:n], wl.window, wl.swa_scale)
+        dt, one = cpu_heads(layer, wl.H, th)
+        return {"value": wl.L / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
+                "sample": f"1 of {wl.B} sequences ({wl.H} heads x {wl.L} tokens): la_recurrent then swa, {dt:.2f} s",
+                "single_core_tokens_per_s": wl.L / wl.H / one, **cpu_info()}
+    q, k, v = si.linear_inputs(wl)
+    t0 = time.perf_counter()
+    oracle.la_quadratic(q, k, v, eps=wl.eps)
+    oracle.swa(q, k, v, wl.window, wl.swa_scale)
+    dt = time.perf_counter() - t0
+    return {"value": wl.L / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole layer (la_quadratic + swa; one head, one thread), {dt*1e3:.1f} ms", **cpu_info()}
+
+
 def cpu_heads(fn, n_heads, threads):
     """Seconds of fn over a sample (called once; OpenMP over its heads) and of
     fn over one head (one core)."""
@@ -677,10 +775,11 @@ def main():
     # timed steps never see the idle clock whatever --warmup is.
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg5"],
-                    help="headline prefill workload: cfg2 (360M-shaped layer) or cfg5 (64K sequence); the other "
-                         "configurations are extra legs")
-    ap.add_argument("--workload", default=None, choices=["prefill_360m", "long_64k"], help="same, by name")
+    ap.add_argument("--config", default="cfg2", choices=sorted(CONFIGS),
+                    help="headline configuration: cfg2 (360M-shaped prefill layer, the default), cfg5 (64K "
+                         "sequence), cfg3 (1.3B next-token steps), cfg4 (8K hybrid layer through "
+                         "based_hybrid_prefill) or cfg1 (the tiny fp32 layer); the others are extra legs")
+    ap.add_argument("--workload", default=None, choices=sorted(CONFIGS.values()), help="same, by name")
     ap.add_argument("--no-extra", action="store_true", help="skip every leg but the headline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--decode-steps", type=int, default=1024)
@@ -717,12 +816,19 @@ def main():
 
     import linear_attention_sequence_taylor_amd as based
 
-    wl = si.WORKLOADS[args.workload or CONFIGS[args.config]]
+    cfg = args.config
+    if args.workload:
+        cfg = {name: c for c, name in CONFIGS.items()}[args.workload]
+    spec = headline_spec(based, cfg)
+    wl = spec["wl"]
     print(f"[bench] workload {wl.name}: {wl.description}", file=sys.stderr, flush=True)
-    step_s, kern_s, dist = bench_prefill(based, wl, args.steps, args.warmup)
-    tokens = wl.B * wl.L
-    abytes, aflops = prefill_bytes(wl), prefill_flops(wl)
+    step_s, kern_s, dist = bench_headline(spec["step"], args.steps, args.warmup)
+    tokens = spec["tokens"]
+    abytes, aflops = spec["bytes"], spec["flops"]
     digest = source_digest("prefill_mfma.hip", "common.hpp")
+    traffic = None
+    if spec["traffic"]:
+        traffic = read_traffic(spec["traffic"][0], source_digest(*spec["traffic"][1]))
     achieved = abytes / kern_s
     line = {
         "metric": METRIC,
@@ -735,30 +841,30 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic (seeded N(0,1)*scale, bf16-rounded)",
-        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d_feat": wl.d,
-                   "d_v": wl.dv, "chunk": wl.chunk, "scale": wl.scale, "parallelism": "single GPU"},
+        "dtype": {"bf16": "bf16", "f32": "f32"}.get(wl.dtype, wl.dtype),
+        "data": "synthetic (seeded N(0,1)*scale" + (", bf16-rounded)" if wl.dtype == "bf16" else ")"),
+        "config": spec["config"],
         "roofline": {
             "bound": "hbm",
             "achieved": achieved / 1e9,
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK,
-            "traffic": read_traffic(f"prefill_mfma_{wl.name}_pmc.txt", digest),
-            "kernel": "based_prefill (bf16 MFMA)",
+            "traffic": traffic,
+            "kernel": spec["kernel"],
             "kernel_ms": kern_s * 1e3,
             "kernel_timing": "HIP events on the launch stream around one replay of the K steps captured in a HIP "
                              "graph, / K; before it a 0.3 s settle phase and W warm-up steps",
             "single_launch_us": dist,
             "algorithmic_bytes": abytes,
-            "algorithmic_flops": aflops,
-            "mfma_tflops": aflops / kern_s / 1e12,
-            "mfma_frac": aflops / kern_s / MFMA_BF16_PEAK,
-            "kernel_source_sha256_16": digest,
         },
     }
-    print(f"[bench] prefill {wl.name}: {kern_s*1e6:.1f} us/launch, {achieved/1e9:.0f} GB/s", file=sys.stderr,
+    if aflops is not None:
+        line["roofline"].update({"algorithmic_flops": aflops, "mfma_tflops": aflops / kern_s / 1e12,
+                                 "mfma_frac": aflops / kern_s / MFMA_BF16_PEAK})
+    if spec["traffic"]:
+        line["roofline"]["kernel_source_sha256_16"] = source_digest(*spec["traffic"][1])
+    print(f"[bench] headline {wl.name}: {kern_s*1e6:.1f} us/step, {achieved/1e9:.0f} GB/s", file=sys.stderr,
           flush=True)
 
     if not args.no_extra:
@@ -808,12 +914,16 @@ def main():
               f"{ht['auto']*1e6:.1f} / fused {ht['fused']*1e6:.1f} / two passes {ht['two_pass']*1e6:.1f} us",
               file=sys.stderr, flush=True)
         # cfg5: the 64K sequence (or cfg2 when the headline is cfg5)
-        other = si.WORKLOADS["prefill_360m" if wl.name == "long_64k" else "long_64k"]
-        osec, odist = bench_prefill_leg(based, other, 40 if other.name == "long_64k" else 200)
-        extra[other.name] = {"kernel_us": osec * 1e6, "launch_us": odist, "tokens_per_s": other.B * other.L / osec,
-                             "roofline": roofline(prefill_bytes(other), osec, read_traffic(
-                                 f"prefill_mfma_{other.name}_pmc.txt", digest), prefill_flops(other))}
-        print(f"[bench] {other.name}: {osec*1e6:.1f} us", file=sys.stderr, flush=True)
+        for oname in ("prefill_360m", "long_64k"):
+            if oname == wl.name:
+                continue
+            other = si.WORKLOADS[oname]
+            osec, odist = bench_prefill_leg(based, other, 40 if other.name == "long_64k" else 200)
+            extra[other.name] = {"kernel_us": osec * 1e6, "launch_us": odist,
+                                 "tokens_per_s": other.B * other.L / osec,
+                                 "roofline": roofline(prefill_bytes(other), osec, read_traffic(
+                                     f"prefill_mfma_{other.name}_pmc.txt", digest), prefill_flops(other))}
+            print(f"[bench] {other.name}: {osec*1e6:.1f} us", file=sys.stderr, flush=True)
         # cfg1: the tiny fp32 layer (linear attention + window, summed)
         wt = si.WORKLOADS["tiny_f32"]
         tq, tk, tv = (t.cuda() for t in si.linear_inputs(wt))
@@ -864,7 +974,7 @@ def main():
         line["extra"] = extra
 
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl)
+        line["cpu_baseline"] = cpu_baseline_for(cfg, wl)
         if not args.no_extra:
             line["extra"]["cpu_baselines"] = cpu_legs()
             print("[bench] cpu baselines done", file=sys.stderr, flush=True)
