@@ -1,5 +1,7 @@
 // prefill_backward_mfma.hip -- gradients of causal Taylor linear attention on
-// the gfx950 matrix cores (bf16 inputs, feature dim 16, fp32 accumulation).
+// the gfx950 matrix cores (bf16 inputs, feature dim 16, fp32 accumulation),
+// in two forms: the direct form below (pair by pair, O(L^2) per head) and the
+// chunked form further down (linear in L through the carried state, d_v 64).
 //
 // Same quantities as prefill_backward.hip ("Simple linear attention language
 // models balance the recall-throughput tradeoff", s5 and s4 "Taylor Linear
@@ -30,8 +32,6 @@
 // Only the diagonal tile needs the causal mask; rows past L are staged as
 // zeros (their g and h are zero, so they add nothing on the key side) and
 // never stored.
-#include <utility>
-
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -567,7 +567,9 @@ __global__ __launch_bounds__(256) void bwd_key_mfma_kernel(const uint16_t* __res
 //   4. segment sums of m(q) g^T and m(q) h (every segment but the first);
 //   5. exclusive suffix over the segments: R, r after each segment;
 //   6. key sweep, last chunk first: dk, dv.
-// With one segment per head, 1, 2, 4 and 5 are skipped.
+// With one segment per head, 1, 2, 4 and 5 are skipped; with at most
+// kFoldSegments segments, 2 and 5 are: each sweep adds up the earlier (or
+// later) segments' sums itself when it loads its carried-in state.
 constexpr int kNTile = 10;
 constexpr int kSlot = 16 * kNTile;                   // 160 state rows
 constexpr int kStateFloats = kSlot * 64 + kSlot;     // one (segment, head) state, d_v = 64
