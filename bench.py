@@ -215,6 +215,30 @@ def roofline(nbytes: float, sec: float, traffic=None, flops: float | None = None
     return out
 
 
+def counter_mfma_busy(name: str, sec: float):
+    """Matrix-core busy fraction from the committed SQ counter summary of the
+    workload's prefill kernel (SQ_VALU_MFMA_BUSY_CYCLES: SIMD-cycles with an
+    MFMA in flight, summed over the chip), over 1024 SIMDs x the mean launch
+    time at the 2.4 GHz peak engine clock; None if the summary is absent or
+    taken on other kernel sources.  It counts the hi/lo pairs' extra
+    products, which the algorithmic fraction does not."""
+    path = os.path.join(PROFILES, f"sq_counters_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if not line.startswith("#"):
+            parts = line.replace(":", " ").split()
+            if len(parts) >= 2:
+                vals[parts[0]] = parts[1]
+    if vals.get("kernel_source_sha256_16") != source_digest("prefill_mfma.hip", "common.hpp"):
+        return None
+    try:
+        return float(vals["SQ_VALU_MFMA_BUSY_CYCLES"]) / (1024 * sec * 2.4e9)
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_info() -> dict:
     model = None
     try:
@@ -862,6 +886,9 @@ def main():
     if aflops is not None:
         line["roofline"].update({"algorithmic_flops": aflops, "mfma_tflops": aflops / kern_s / 1e12,
                                  "mfma_frac": aflops / kern_s / MFMA_BF16_PEAK})
+    busy = counter_mfma_busy(wl.name, kern_s)
+    if busy is not None:
+        line["roofline"]["counter_mfma_busy_frac"] = busy
     if spec["traffic"]:
         line["roofline"]["kernel_source_sha256_16"] = source_digest(*spec["traffic"][1])
     print(f"[bench] headline {wl.name}: {kern_s*1e6:.1f} us/step, {achieved/1e9:.0f} GB/s", file=sys.stderr,
