@@ -310,9 +310,11 @@ based_status_t swa_decode_step(const void *q, const void *k, const void *v,
  *            R_j = sum_{i>=j} phi(q_i) g_i^T, r_j = sum_{i>=j} phi(q_i) h_i,
  *            dq_i = J(q_i)^T (S_i g_i + h_i z_i), dk_j = J(k_j)^T (R_j v_j + r_j),
  *            dv_j = R_j^T phi(k_j) (J: the Jacobian of phi), pairs within a
- *            64-token chunk taken directly; bf16 inputs with d_feat 16 and
- *            d_v 64 only (else BASED_E_UNSUPPORTED), every non-input operand
- *            a bf16 hi/lo pair.
+ *            64-token chunk taken directly; bf16 inputs with d_feat 16 only
+ *            (else BASED_E_UNSUPPORTED), every non-input operand a bf16
+ *            hi/lo pair.  d_v 128 runs once per 64-column half of v, dy
+ *            and dv (each half with its own h, the sums of which are the
+ *            full h), the second run adding into dq and dk.
  * AUTO takes CHUNKED where it is supported and L >= 1024, else DIRECT.  The
  * workspace size covers either form.
  */

@@ -384,7 +384,7 @@ def based_prefill_backward(q, k, v, dy, *, eps: float = 1e-6, form: str = "auto"
     """Gradients (dq, dk, dv), fp32, of based_prefill's output y for the
     upstream gradient dy [B,H,L,d_v] (fp32), from a zero initial state.
     ``form``: "direct" (pair by pair, O(L^2)), "chunked" (linear in L through
-    the carried state; bf16, d' = 16, d_v = 64) or "auto" (chunked where it
+    the carried state; bf16, d' = 16) or "auto" (chunked where it
     is supported and faster)."""
     if form not in _BACKWARD_FORMS:
         raise ValueError(f"form must be one of {sorted(_BACKWARD_FORMS)}")

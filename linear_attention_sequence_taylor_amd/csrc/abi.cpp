@@ -316,7 +316,7 @@ BASED_API size_t based_prefill_backward_workspace_bytes(int B, int H, int L, int
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return 0;
     if (!feat_dim_ok(d_feat) || (d_v != 64 && d_v != 128)) return 0;
     const size_t direct = based::prefill_backward_workspace_bytes((int)BH, L, d_v);
-    if (d_feat == 16 && d_v == 64) {
+    if (d_feat == 16) {
         const size_t chunked = based::prefill_backward_chunked_workspace_bytes((int)BH, L);
         return chunked > direct ? chunked : direct;
     }
@@ -345,7 +345,7 @@ BASED_API based_status_t based_prefill_backward(const void* q, const void* k, co
     // one workgroup of 256 threads per 64 rows of a head: the grid's thread
     // count must fit 32 bits
     if (BH * (((uint64_t)L + 63) / 64) * 256 > (uint64_t)INT32_MAX) return BASED_E_INVALID;
-    const bool chunk_ok = dtype == BASED_BF16 && d_feat == 16 && d_v == 64;
+    const bool chunk_ok = dtype == BASED_BF16 && d_feat == 16;
     if (form == BASED_BACKWARD_CHUNKED && !chunk_ok) return BASED_E_UNSUPPORTED;
     const bool chunked = form == BASED_BACKWARD_CHUNKED || (form == BASED_BACKWARD_AUTO && chunk_ok &&
                                                             L >= kBackwardChunkedMinL);
@@ -366,7 +366,7 @@ BASED_API based_status_t based_prefill_backward(const void* q, const void* k, co
             if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return BASED_E_INVALID;
     }
     if (chunked)
-        return launch_status(based::launch_prefill_backward_chunked(q, k, v, dy, (int)BH, L, eps, dq, dk, dv,
+        return launch_status(based::launch_prefill_backward_chunked(q, k, v, dy, (int)BH, L, d_v, eps, dq, dk, dv,
                                                                     workspace, static_cast<hipStream_t>(stream)));
     return launch_status(based::launch_prefill_backward(q, k, v, dy, dtype == BASED_BF16, (int)BH, L, d_feat, d_v,
                                                         eps, dq, dk, dv, workspace,

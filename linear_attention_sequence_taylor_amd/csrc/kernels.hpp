@@ -82,11 +82,12 @@ hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, 
                                    void* workspace, hipStream_t st);
 // The same gradients in linear time through the carried state
 // (prefill_backward_mfma.hip, chunked form): bf16 inputs, feature dim 16,
-// dv 64.  The workspace starts with the direct form's g and h and adds two
-// sets of per-segment states when a head is split into segments.
+// dv 64 or 128 (128 as two passes over the column halves).  The workspace
+// holds g and h of one 64-column pass and adds two sets of per-segment
+// states when a head is split into segments; it does not depend on dv.
 size_t prefill_backward_chunked_workspace_bytes(int BH, int L);
 hipError_t launch_prefill_backward_chunked(const void* q, const void* k, const void* v, const float* dy, int BH,
-                                           int L, float eps, float* dq, float* dk, float* dvo, void* workspace,
-                                           hipStream_t st);
+                                           int L, int dv, float eps, float* dq, float* dk, float* dvo,
+                                           void* workspace, hipStream_t st);
 
 }  // namespace based

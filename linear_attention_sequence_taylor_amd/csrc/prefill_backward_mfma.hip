@@ -1,7 +1,8 @@
 // prefill_backward_mfma.hip -- gradients of causal Taylor linear attention on
 // the gfx950 matrix cores (bf16 inputs, feature dim 16, fp32 accumulation),
 // in two forms: the direct form below (pair by pair, O(L^2) per head) and the
-// chunked form further down (linear in L through the carried state, d_v 64).
+// chunked form further down (linear in L through the carried state; d_v 64,
+// and 128 as one pass per column half).
 //
 // Same quantities as prefill_backward.hip ("Simple linear attention language
 // models balance the recall-throughput tradeoff", s5 and s4 "Taylor Linear
@@ -136,23 +137,23 @@ __device__ __forceinline__ bf16x4 quarter(uint2 u) {
                                                  pack_bf16x2(0.25f * f[2], 0.25f * f[3])));
 }
 
-// A [64][W] bf16 tile (rows row0.. of a [L][W] matrix, rows past L zero)
-// held in registers across the workgroup, 16 bytes per piece: loaded from
-// global memory while the previous tile is in use, then stored to LDS in
-// the tile_at<W> layout.
+// A [64][W] bf16 tile (rows row0.. of a [L][ld] matrix, ld = W unless
+// given, rows past L zero) held in registers across the workgroup, 16 bytes
+// per piece: loaded from global memory while the previous tile is in use,
+// then stored to LDS in the tile_at<W> layout.
 template <int W>
 struct TileRegs {
     static constexpr int kU = W / 8;                    // pieces per row
     static constexpr int kPer = (kT * kU + 255) / 256;  // pieces per thread
     u32x4 x[kPer];
 
-    __device__ __forceinline__ void load(const uint16_t* mat, int L, int row0) {
+    __device__ __forceinline__ void load(const uint16_t* mat, int L, int row0, int ld = W) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int e = threadIdx.x + 256 * i, row = e / kU, u = e % kU;
             x[i] = u32x4{0u, 0u, 0u, 0u};
             if (e < kT * kU && row0 + row < L)
-                x[i] = *reinterpret_cast<const u32x4*>(mat + (size_t)(row0 + row) * W + 8 * u);
+                x[i] = *reinterpret_cast<const u32x4*>(mat + (size_t)(row0 + row) * ld + 8 * u);
         }
     }
     __device__ __forceinline__ void store(uint16_t* dst) const {
@@ -1003,15 +1004,15 @@ template <bool KEYS>
 __global__ __launch_bounds__(256) void bwd_segsum_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ mhi,
                                                          const uint16_t* __restrict__ mlo,
-                                                         const float* __restrict__ hw, int BH, int L, int nch,
-                                                         int cps, int seg0, float* __restrict__ states) {
+                                                         const float* __restrict__ hw, int BH, int L, int ldv,
+                                                         int nch, int cps, int seg0, float* __restrict__ states) {
     __shared__ BwdKSmem<64> sm[2];  // per chunk parity; q: X, ghi/glo: M, h: token weights
     const int head = blockIdx.x % BH, seg = seg0 + (int)(blockIdx.x / BH);
     const int c_begin = seg * cps, c_end = min(nch, c_begin + cps);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const uint16_t* xh = x + (size_t)head * L * kD;
-    const uint16_t* mh = mhi + (size_t)head * L * 64;
+    const uint16_t* mh = KEYS ? mhi + (size_t)head * L * ldv : mhi + (size_t)head * L * 64;
     const uint16_t* ml = KEYS ? nullptr : mlo + (size_t)head * L * 64;
     const float* hh = KEYS ? nullptr : hw + (size_t)head * L;
     f32x4 acc[10];
@@ -1022,7 +1023,7 @@ __global__ __launch_bounds__(256) void bwd_segsum_kernel(const uint16_t* __restr
     float hreg = 0.f;
     auto load = [&](int c) {
         xreg.load(xh, L, c * kT);
-        mreg.load(mh, L, c * kT);
+        mreg.load(mh, L, c * kT, KEYS ? ldv : 64);
         if (!KEYS) {
             lreg.load(ml, L, c * kT);
             if (threadIdx.x < kT) hreg = c * kT + (int)threadIdx.x < L ? hh[c * kT + threadIdx.x] : 0.f;
@@ -1090,9 +1091,9 @@ struct QSweepSmem {
 __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_qsweep_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
-                                                         const float* __restrict__ dy, int BH, int L, int nch,
-                                                         int cps, float eps, const float* __restrict__ s_init,
-                                                         int fold, float* __restrict__ dq,
+                                                         const float* __restrict__ dy, int BH, int L, int ldv,
+                                                         int nch, int cps, float eps, const float* __restrict__ s_init,
+                                                         int fold, int accumulate, float* __restrict__ dq,
                                                          uint16_t* __restrict__ ghi_ws,
                                                          uint16_t* __restrict__ glo_ws, float* __restrict__ h_ws) {
     constexpr int DV = 64, kNV = 4;
@@ -1103,7 +1104,7 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_qsweep_kernel(const ui
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const uint16_t* qh = q + (size_t)head * L * kD;
     const uint16_t* kh = k + (size_t)head * L * kD;
-    const uint16_t* vh = v + (size_t)head * L * DV;
+    const uint16_t* vh = v + (size_t)head * L * ldv;
 
     f32x4 acc[10];
     float zacc[3];
@@ -1118,7 +1119,7 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_qsweep_kernel(const ui
     TileRegs<kD> kreg;
     TileRegs<DV> vreg;
     kreg.load(kh, L, c_begin * kT);
-    vreg.load(vh, L, c_begin * kT);
+    vreg.load(vh, L, c_begin * kT, ldv);
     // this wave's queries, one chunk ahead
     TokenRegs qreg;
     auto load_q = [&](int c) {
@@ -1137,7 +1138,7 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_qsweep_kernel(const ui
         const PubState& ss = sm.s[sbuf(c)];
         if (c + 1 < c_end) {
             kreg.load(kh, L, t0 + kT);
-            vreg.load(vh, L, t0 + kT);
+            vreg.load(vh, L, t0 + kT, ldv);
         }
         const int qw0 = t0 + 16 * w;  // first query of this wave
         float xr[16], xj[4];
@@ -1149,7 +1150,7 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_qsweep_kernel(const ui
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int qi = qw0 + 4 * g + m;
-            const float* dyr = dy + ((size_t)head * L + min(qi, L - 1)) * DV + r;
+            const float* dyr = dy + ((size_t)head * L + min(qi, L - 1)) * ldv + r;
 #pragma unroll
             for (int ct = 0; ct < kNV; ++ct) dyc[m][ct] = qi < L ? dyr[16 * ct] : 0.f;
         }
@@ -1217,7 +1218,10 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_qsweep_kernel(const ui
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int qi = qw0 + 4 * g + m;
-            if (qi < L) dq[((size_t)head * L + qi) * kD + r] = fmaf(0.25f, dqacc[m], dx[m]);
+            if (qi < L) {
+                float* o = &dq[((size_t)head * L + qi) * kD + r];
+                *o = fmaf(0.25f, dqacc[m], dx[m]) + (accumulate ? *o : 0.f);
+            }
         }
 
         // the state after this chunk
@@ -1240,11 +1244,11 @@ struct KSweepSmem {
 
 __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_ksweep_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ v, int BH, int L, int nch,
-                                                         int cps, const uint16_t* __restrict__ ghi_ws,
+                                                         const uint16_t* __restrict__ v, int BH, int L, int ldv,
+                                                         int nch, int cps, const uint16_t* __restrict__ ghi_ws,
                                                          const uint16_t* __restrict__ glo_ws,
                                                          const float* __restrict__ h_ws,
-                                                         const float* __restrict__ r_init, int fold,
+                                                         const float* __restrict__ r_init, int fold, int accumulate,
                                                          float* __restrict__ dk,
                                                          float* __restrict__ dvo) {
     constexpr int DV = 64, kNV = 4;
@@ -1256,7 +1260,7 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_ksweep_kernel(const ui
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const uint16_t* qh = q + (size_t)head * L * kD;
     const uint16_t* kh = k + (size_t)head * L * kD;
-    const uint16_t* vh = v + (size_t)head * L * DV;
+    const uint16_t* vh = v + (size_t)head * L * ldv;
     const uint16_t* gh = ghi_ws + (size_t)head * L * DV;
     const uint16_t* gl = glo_ws + (size_t)head * L * DV;
     const float* hh = h_ws + (size_t)head * L;
@@ -1295,7 +1299,7 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_ksweep_kernel(const ui
 #pragma unroll
         for (int cs = 0; cs < 2; ++cs) {
             vrow[cs] = u32x4{0u, 0u, 0u, 0u};
-            if (kr < L) vrow[cs] = *reinterpret_cast<const u32x4*>(vh + (size_t)kr * DV + 32 * cs + 8 * g);
+            if (kr < L) vrow[cs] = *reinterpret_cast<const u32x4*>(vh + (size_t)kr * ldv + 32 * cs + 8 * g);
         }
     };
     load(c_end - 1);
@@ -1334,8 +1338,9 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_ksweep_kernel(const ui
             const int kj = kw0 + 4 * g + m;
             if (kj < L) {
 #pragma unroll
-                for (int ct = 0; ct < kNV; ++ct) dvo[((size_t)head * L + kj) * DV + 16 * ct + r] = dvacc[ct][m];
-                dk[((size_t)head * L + kj) * kD + r] = fmaf(0.25f, dkacc[m], dx[m]);
+                for (int ct = 0; ct < kNV; ++ct) dvo[((size_t)head * L + kj) * ldv + 16 * ct + r] = dvacc[ct][m];
+                float* o = &dk[((size_t)head * L + kj) * kD + r];
+                *o = fmaf(0.25f, dkacc[m], dx[m]) + (accumulate ? *o : 0.f);
             }
         }
 
@@ -1400,14 +1405,19 @@ size_t prefill_backward_chunked_workspace_bytes(int BH, int L) {
     return nseg > 1 ? base + 2 * align256((size_t)nseg * BH * kStateFloats * sizeof(float)) : base;
 }
 
+// d_v = 128 runs the d_v = 64 pipeline on each half of the value columns:
+// with half c's own y_c, g_c = dy_c / D and h_c = -(dy_c . y_c) / D (D does
+// not depend on the columns), the gradients are linear in (g, h) = sums of
+// the halves' terms, so dq and dk are the sums of the two passes' (the
+// second pass adds into them) and dv is the two halves side by side.  The
+// passes reuse the workspace one after the other on the stream.
 hipError_t launch_prefill_backward_chunked(const void* q, const void* k, const void* v, const float* dy, int BH,
-                                           int L, float eps, float* dq, float* dk, float* dvo, void* workspace,
-                                           hipStream_t st) {
+                                           int L, int dv, float eps, float* dq, float* dk, float* dvo,
+                                           void* workspace, hipStream_t st) {
     int nch, cps, nseg;
     chunk_plan(BH, L, nch, cps, nseg);
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
-    const uint16_t* vv = static_cast<const uint16_t*>(v);
     char* base = static_cast<char*>(workspace);
     uint16_t* ghi = reinterpret_cast<uint16_t*>(base);
     uint16_t* glo = ghi + (size_t)BH * L * 64;
@@ -1419,20 +1429,25 @@ hipError_t launch_prefill_backward_chunked(const void* q, const void* k, const v
     // With few segments each sweep sums the earlier (later) segments' slots
     // itself instead of a scan launch.
     const int fold = nseg <= kFoldSegments;
-    if (nseg > 1) {
-        hipLaunchKernelGGL((bwd_segsum_kernel<true>), dim3((unsigned)(BH * (nseg - 1))), dim3(256), 0, st, kk, vv,
-                           nullptr, nullptr, BH, L, nch, cps, 0, s_states);
-        if (!fold) hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, st, s_states, BH, nseg, 0);
+    for (int half = 0; half < dv / 64; ++half) {
+        const uint16_t* vv = static_cast<const uint16_t*>(v) + 64 * half;
+        const float* dyh = dy + 64 * half;
+        float* dvh = dvo + 64 * half;
+        if (nseg > 1) {
+            hipLaunchKernelGGL((bwd_segsum_kernel<true>), dim3((unsigned)(BH * (nseg - 1))), dim3(256), 0, st, kk, vv,
+                               nullptr, nullptr, BH, L, dv, nch, cps, 0, s_states);
+            if (!fold) hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, st, s_states, BH, nseg, 0);
+        }
+        hipLaunchKernelGGL(bwd_qsweep_kernel, dim3((unsigned)(BH * nseg)), dim3(256), 0, st, qq, kk, vv, dyh, BH, L,
+                           dv, nch, cps, eps, nseg > 1 ? s_states : nullptr, fold, half, dq, ghi, glo, h_ws);
+        if (nseg > 1) {
+            hipLaunchKernelGGL((bwd_segsum_kernel<false>), dim3((unsigned)(BH * (nseg - 1))), dim3(256), 0, st, qq,
+                               ghi, glo, h_ws, BH, L, 64, nch, cps, 1, r_states);
+            if (!fold) hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, st, r_states, BH, nseg, 1);
+        }
+        hipLaunchKernelGGL(bwd_ksweep_kernel, dim3((unsigned)(BH * nseg)), dim3(256), 0, st, qq, kk, vv, BH, L, dv,
+                           nch, cps, ghi, glo, h_ws, nseg > 1 ? r_states : nullptr, fold, half, dk, dvh);
     }
-    hipLaunchKernelGGL(bwd_qsweep_kernel, dim3((unsigned)(BH * nseg)), dim3(256), 0, st, qq, kk, vv, dy, BH, L, nch,
-                       cps, eps, nseg > 1 ? s_states : nullptr, fold, dq, ghi, glo, h_ws);
-    if (nseg > 1) {
-        hipLaunchKernelGGL((bwd_segsum_kernel<false>), dim3((unsigned)(BH * (nseg - 1))), dim3(256), 0, st, qq, ghi,
-                           glo, h_ws, BH, L, nch, cps, 1, r_states);
-        if (!fold) hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, st, r_states, BH, nseg, 1);
-    }
-    hipLaunchKernelGGL(bwd_ksweep_kernel, dim3((unsigned)(BH * nseg)), dim3(256), 0, st, qq, kk, vv, BH, L, nch, cps,
-                       ghi, glo, h_ws, nseg > 1 ? r_states : nullptr, fold, dk, dvo);
     return hipGetLastError();
 }
 

@@ -239,11 +239,12 @@ def _bwd(lib, **kw):
     (dict(q=None), 1), (dict(dy=None), 1), (dict(ws=None), 1), (dict(dq=S + 4), 1), (dict(wsb=100), 1),
     (dict(dtype=5), 1), (dict(L=0), 1), (dict(eps=float("nan")), 1), (dict(d=12), 2), (dict(dv=32), 2),
     (dict(dq=A), 1), (dict(dk=S), 1), (dict(ws=S + (2 << 20)), 1), (dict(dvo=Y), 1),
-    # the form: unknown values, and the chunked form outside bf16 / d' 16 / d_v 64
+    # the form: unknown values, and the chunked form outside bf16 / d' 16
     (dict(form=3), 1), (dict(form=-1), 1), (dict(form=2, dtype=0), 2), (dict(form=2, d=8), 2),
-    (dict(form=2, dv=128), 2),
-    # the chunked form's workspace is larger than the direct form's
-    (dict(form=2, wsb=2 * 100 * 65 * 4), 1),
+    (dict(form=2, d=8, dv=128), 2),
+    # the chunked form's workspace is larger than the direct form's at d_v 64
+    # and the same at d_v 128
+    (dict(form=2, wsb=2 * 100 * 65 * 4), 1), (dict(form=2, dv=128, wsb=2 * 100 * 65 * 4), 1),
 ])
 @fake_addresses
 def test_backward_rejects(lib, kw, want):
@@ -251,9 +252,13 @@ def test_backward_rejects(lib, kw, want):
 
 
 def test_backward_workspace_bytes(lib):
-    # direct form: g and h; d' 16 with d_v 64 also covers the chunked form's
-    # per-segment states
-    assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 16, 128) == 2 * 3 * 100 * 129 * 4
+    # direct form: g and h; d' 16 also covers the chunked form's per-segment
+    # states (the same for both d_v: one 64-column pass at a time)
+    assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 16, 128) >= 2 * 3 * 100 * 129 * 4
+    for L in (100, 4096, 65536):
+        assert lib.based_prefill_backward_workspace_bytes(2, 3, L, 16, 128) >= \
+            lib.based_prefill_backward_workspace_bytes(2, 3, L, 16, 64)
+    assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 8, 128) == 2 * 3 * 100 * 129 * 4
     assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 8, 64) == 2 * 3 * 100 * 65 * 4
     assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 16, 64) > 2 * 3 * 100 * 65 * 4
     assert lib.based_prefill_backward_workspace_bytes(2, 3, 100, 12, 64) == 0

@@ -494,21 +494,36 @@ def test_backward_chunked_matches_oracle(B, H, L):
         report(f"chunked backward B={B} H={H} L={L} {name}", ratio(got, w), 2e-2)
 
 
+@pytest.mark.parametrize("B,H,L", [(1, 2, 3), (2, 1, 65), (1, 3, 257), (2, 2, 700), (2, 4, 4100)])
+def test_backward_chunked_dv128_matches_oracle(B, H, L):
+    """The chunked form at d_v = 128 (one pass per 64-column half, the second
+    adding into dq and dk): every element of dq, dk, dv against the oracle,
+    at one chunk, ragged tails and segmented heads."""
+    based = based_mod()
+    q, k, v = si.custom((B, H, L, 16), (B, H, L, 128), seed=2450 + L + H, scale=0.5)
+    dy = torch.randn(B, H, L, 128, generator=torch.Generator().manual_seed(2451 + L))
+    dq, dk, dv_ = based.based_prefill_backward(*dev(q, k, v), dy.to(DEV), form="chunked")
+    torch.cuda.synchronize()
+    want = oracle.la_backward(q, k, v, dy) if L <= 1000 else oracle.la_backward_recurrent(q, k, v, dy)
+    for name, got, w in zip(("dq", "dk", "dv"), (dq, dk, dv_), want):
+        report(f"chunked backward d_v=128 B={B} H={H} L={L} {name}", ratio(got, w), 2e-2)
+
+
 @pytest.mark.parametrize("form", ["direct", "chunked"])
+@pytest.mark.parametrize("dvd", [64, 128])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_backward_single_token(dtype, form):
+def test_backward_single_token(dtype, dvd, form):
     """L = 1: y_0 = v_0 a/(a + eps), so dv_0 = dy_0 a/(a + eps) and dq, dk are
     of order eps: they come out of the cancellation of terms of order
     |dy||v|, and fp32 gives them to rounding noise of those terms."""
     if form == "chunked" and dtype != torch.bfloat16:
         pytest.skip("the chunked form takes bf16 inputs")
     based = based_mod()
-    dvd = 128 if form == "direct" else 64
     q, k, v = si.custom((2, 2, 1, 16), (2, 2, 1, dvd), seed=2250, scale=1.0, dtype=dtype)
     dy = torch.randn(2, 2, 1, dvd, generator=torch.Generator().manual_seed(2251))
     dq, dk, dv_ = based.based_prefill_backward(*dev(q, k, v), dy.to(DEV), form=form)
     oq, ok, ov = oracle.la_backward(q, k, v, dy)
-    report(f"backward L=1 {dtype} {form} dv", ratio(dv_, ov), 1e-4)
+    report(f"backward L=1 {dtype} d_v={dvd} {form} dv", ratio(dv_, ov), 1e-4)
     noise = 1e-5 * float(dy.norm(dim=-1).max() * v.float().norm(dim=-1).max() * k.float().norm(dim=-1).max())
     assert float(dq.abs().max()) <= noise and float(dk.abs().max()) <= noise, (dq.abs().max(), dk.abs().max(), noise)
     assert np.abs(oq).max() <= noise and np.abs(ok).max() <= noise
@@ -529,6 +544,31 @@ def test_workload_prefill_360m_backward():
         report(f"prefill_360m backward {form} dq (all heads)", ratio(dq, oq), wl.tol)
         report(f"prefill_360m backward {form} dk (all heads)", ratio(dk, ok), wl.tol)
         report(f"prefill_360m backward {form} dv (all heads)", ratio(dv_, ov), wl.tol)
+        del dq, dk, dv_
+
+
+def test_workload_1p3b_backward_sampled_heads():
+    """Gradients over the 1.3B-shaped layer (B=128, H=16, L=1024, d_v=128)
+    in both forms (the chunked one as two column-half passes): dq, dk, dv
+    of 8 seeded (batch, head) pairs against the oracle's chain rule on those
+    heads alone (heads do not interact), and every output finite."""
+    based = based_mod()
+    wl = si.WORKLOADS["decode_1p3b"]
+    q, k, v = si.linear_inputs(wl)
+    dy = torch.randn(wl.B, wl.H, wl.L, wl.dv, generator=torch.Generator().manual_seed(2320))
+    rng = np.random.default_rng(2321)
+    picks = [(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(8)]
+    sel = lambda x: torch.stack([x[b, h] for b, h in picks])[None]
+    oq, ok, ov = oracle.la_backward(sel(q), sel(k), sel(v), sel(dy), eps=wl.eps)
+    qd, kd, vd = dev(q, k, v)
+    dyd = dy.to(DEV)
+    for form in ("direct", "chunked"):
+        print(f"[1p3b backward] form={form}", flush=True)
+        dq, dk, dv_ = based.based_prefill_backward(qd, kd, vd, dyd, eps=wl.eps, form=form)
+        torch.cuda.synchronize()
+        for name, got, w in zip(("dq", "dk", "dv"), (dq, dk, dv_), (oq, ok, ov)):
+            assert bool(torch.isfinite(got).all()), (form, name)
+            report(f"decode_1p3b-shaped backward {form} {name} (8 heads)", ratio(sel(got.cpu()), w), wl.tol)
         del dq, dk, dv_
 
 

@@ -137,7 +137,7 @@ def test_random_backward(based, case):
     dtype = BF16 if rng.random() < 0.6 else F32
     form = "direct"
     if rng.random() < 0.6:  # the chunked form's inputs
-        d, dv, dtype, form = 16, 64, BF16, "chunked"
+        d, dtype, form = 16, BF16, "chunked"
     if L == 1:
         L = 2  # at L = 1, dq and dk are rounding noise (tested on their own)
     print(f"[property] backward case {case}: B={B} H={H} L={L} d={d} dv={dv} {dtype} {form}", flush=True)
