@@ -976,13 +976,14 @@ def main():
             "note": "w=64 ring, B=128, H=16, d_qk=64, d_v=128, fused add; HIP graph of 64 steps "
                     "replayed, 16 cache sets"}
         print(f"[bench] window decode: {wkern*1e6:.1f} us/step", file=sys.stderr, flush=True)
-        for bname, forms in (("prefill_360m", ("chunked", "direct")), ("long_64k", ("chunked",))):
+        for bname, forms in (("prefill_360m", ("chunked", "direct")), ("long_64k", ("chunked",)),
+                             ("decode_1p3b", ("chunked", "direct"))):
             bw = si.WORKLOADS[bname]
             leg = {}
             for form in forms:
-                bsec, bdist = bench_backward(based, bw, form, 30 if bname == "long_64k" else 100)
+                bsec, bdist = bench_backward(based, bw, form, 100 if bname == "prefill_360m" else 30)
                 traffic = None
-                if form == "chunked":
+                if form == "chunked" and bname != "decode_1p3b":
                     traffic = read_traffic(f"prefill_backward_mfma_{'backward_360m' if bname == 'prefill_360m' else 'backward_64k'}"
                                            "_pmc.txt", source_digest("prefill_backward_mfma.hip", "common.hpp"))
                 leg[form] = {"kernel_us": bsec * 1e6, "tokens_per_s": bw.B * bw.L / bsec, "dist_us": bdist,
@@ -993,7 +994,12 @@ def main():
                            "(non-input operands as bf16 hi/lo pairs).  chunked: linear in L through the carried "
                            "state (segment sums, scans, query sweep, key sweep); direct: pair by pair, O(L^2) "
                            "per head.  Flops are each form's own algorithmic count (backward_flops).")
-            extra[f"{bname}_backward"] = leg
+            if bname == "decode_1p3b":
+                leg["note"] += ("  The 1.3B-shaped layer (B=128, H=16, L=1024, d_v=128) of the decode workload's "
+                                "prefill; the chunked form runs once per 64-column half of v.")
+                extra["layer_1p3b_backward"] = leg
+            else:
+                extra[f"{bname}_backward"] = leg
         oth = bench_other_sizes(based)
         extra.update(oth)
         print("[bench] other sizes: " + ", ".join(f"{k} {v['kernel_us']:.1f} us" for k, v in oth.items()),
