@@ -260,16 +260,19 @@ based_status_t based_hybrid_prefill(const void *q, const void *k, const void *q_
  *      e_t = exp(scale * q.k_t - m), m = max_t scale * q.k_t,
  *      over the tokens t held in their slots (the new token included) --
  *      exactly row pos of swa_forward on the whole sequence.
- * A slot that does not hold one of those tokens is never read, so a cache
- * only needs the fill (or nothing, when decoding starts at position 0).
+ * What a slot holds that is not one of those tokens never reaches y (it may
+ * be loaded and is then discarded), so a cache only needs the fill (or
+ * nothing, when decoding starts at position 0).
  *   q     [B,H,d_qk] dtype;  pos [B] int64 device array, not modified
  *         (the caller advances it); pos[b] < 0 gives NaN outputs for b and
  *         leaves its cache untouched
  *   add   optional [B,H,d_v] fp32 added to y (e.g. the linear-attention
  *         decode output); NULL or equal to y for in place
  *   y     [B,H,d_v] fp32 out
- * Supported: d_qk in {16, 64}; d_v in {64, 128}; 1 <= window <= 128.  The
- * caches, y and the inputs must not overlap (add may equal y).
+ * Supported: d_qk in {16, 64}; d_v in {64, 128}; any window >= 1 (up to
+ * 128 one wave per (batch, head); wider, one workgroup of four waves per
+ * (batch, head), an online softmax over rounds of 64 slots).  The caches,
+ * y and the inputs must not overlap (add may equal y).
  */
 based_status_t swa_cache_fill(const void *k, const void *v, based_dtype_t dtype,
                               int B, int H, int L, int d_qk, int d_v, int window,

@@ -252,7 +252,7 @@ based_status_t check_window_cache(based_dtype_t dtype, int d_qk, int d_v, int wi
     if (dtype != BASED_F32 && dtype != BASED_BF16) return BASED_E_INVALID;
     if (window < 1 || d_qk < 1 || d_v < 1) return BASED_E_INVALID;
     if (d_qk != 16 && d_qk != 64) return BASED_E_UNSUPPORTED;
-    if ((d_v != 64 && d_v != 128) || window > 128) return BASED_E_UNSUPPORTED;
+    if (d_v != 64 && d_v != 128) return BASED_E_UNSUPPORTED;
     return BASED_OK;
 }
 

@@ -10,7 +10,8 @@
 // the token at position p lives in slot p mod window.
 //
 // Decode step: HBM-bound (each cached key and value is read once per step).
-// One wave per (batch, head), four per workgroup, no workgroup barrier.
+// Windows up to 128: one wave per (batch, head), four per workgroup, no
+// workgroup barrier (wider windows: swa_decode_long_kernel below).
 // Lane j scores slot j (and j + 64 for windows over 64) from its key row
 // (16-byte loads; bf16 rows through packed bf16 dot products with fp32
 // sums); for P.V, lane
@@ -217,6 +218,129 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
     copy_units(vn, vch + (size_t)slot_new * DV, kVU, lane);
 }
 
+// Windows over 128 slots: one workgroup of four waves per (batch, head).
+// The valid slots are taken in rounds of 64 (lane j scores slot 64 n + j of
+// round n), wave w taking rounds w, w + 4, ...; each wave keeps an online
+// softmax (running maximum m, sum l and the unnormalised P.V of its 8
+// columns per lane, rescaled by exp2(m_old - m_new) when the maximum
+// grows), and the four are merged through LDS after one barrier.  Slot
+// loads do not depend on the position, as above; the new token's slot is
+// written after the barrier, when every wave's loads have been consumed.
+template <typename T, int DQK, int DV>
+__global__ __launch_bounds__(256) void swa_decode_long_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                              const T* __restrict__ v,
+                                                              const long long* __restrict__ pos, int H,
+                                                              int window, float scale, T* __restrict__ kc,
+                                                              T* __restrict__ vc, const float* add,
+                                                              float* __restrict__ y) {
+    constexpr int kQC = DQK / 8, kCG = DV / 8, kKG = 64 / kCG, kKPL = 64 / kKG;
+    constexpr int kKU = DQK * sizeof(T) / 16, kVU = DV * sizeof(T) / 16;
+    __shared__ float part_acc[4][DV];
+    __shared__ float part_ml[4][2];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const size_t head = blockIdx.x;
+    const int cg = lane % kCG, kg = lane / kCG;
+    float* yh = y + head * DV;
+    const T* kn = k + head * DQK;
+    const T* vn = v + head * DV;
+    T* kch = kc + head * (size_t)window * DQK;
+    T* vch = vc + head * (size_t)window * DV;
+    const long long p = pos[head / H];
+    if (p < 0) {  // no valid position: NaN outputs, cache untouched
+        if (w == 0 && kg == 0) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) yh[8 * cg + c] = __builtin_nanf("");
+        }
+        return;
+    }
+    const int slot_new = (int)(p % window);
+    const int nvalid = p + 1 < window ? (int)p + 1 : window;
+    const int nround = (nvalid + 63) / 64;
+    Chunk8<T> qr[kQC], knr[kQC], vnr;
+#pragma unroll
+    for (int c = 0; c < kQC; ++c) {
+        qr[c].load(q + head * DQK + 8 * c);
+        knr[c].load(kn + 8 * c);
+    }
+    vnr.load(vn + 8 * cg);
+    float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+    for (int n = w; n < nround; n += 4) {
+        const int j = 64 * n + lane;  // this lane's slot for the scores
+        Chunk8<T> kr[kQC], vr[kKPL];
+#pragma unroll
+        for (int c = 0; c < kQC; ++c) kr[c].load(kch + (size_t)min(j, window - 1) * DQK + 8 * c);
+#pragma unroll
+        for (int i = 0; i < kKPL; ++i) vr[i].load(vch + (size_t)min(64 * n + kg + kKG * i, window - 1) * DV + 8 * cg);
+        if (j == slot_new) {
+#pragma unroll
+            for (int c = 0; c < kQC; ++c) kr[c] = knr[c];
+        }
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < kQC; ++c) qr[c].dot_into(kr[c], part);
+        const float dot = (part[0] + part[1]) + (part[2] + part[3]);
+        const float sc = j < nvalid ? dot * (scale * kLog2e) : -INFINITY;
+        const float mn = fmaxf(m, wave_max(sc));  // finite: slot 64 n is valid
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        const float pe = j < nvalid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
+        l = l * alpha + wave_sum(pe);
+        m = mn;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+#pragma unroll
+        for (int i = 0; i < kKPL; ++i) {
+            const int jj = 64 * n + kg + kKG * i;
+            if (jj == slot_new) vr[i] = vnr;
+            else if (jj >= nvalid) vr[i].zero();
+            const float pj = __shfl(pe, kg + kKG * i, 64);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = fmaf(pj, vr[i].get(c), acc[c]);
+        }
+    }
+#pragma unroll
+    for (int off = kCG; off < 64; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
+    if (kg == 0) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) part_acc[w][8 * cg + c] = acc[c];
+    }
+    if (lane == 0) {
+        part_ml[w][0] = m;
+        part_ml[w][1] = l;
+    }
+    __syncthreads();
+    if (w == 0 && kg == 0) {
+        // waves without a round hold m = -inf, l = 0 and weigh exp2(-inf) = 0
+        float mx = part_ml[0][0];
+#pragma unroll
+        for (int u = 1; u < 4; ++u) mx = fmaxf(mx, part_ml[u][0]);
+        float den = 0.f, o[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float e = __builtin_amdgcn_exp2f(part_ml[u][0] - mx);
+            den = fmaf(e, part_ml[u][1], den);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) o[c] = fmaf(e, part_acc[u][8 * cg + c], o[c]);
+        }
+        const float inv = 1.f / den;  // den >= 1: the maximum key has weight 1
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float a = add ? add[head * DV + 8 * cg + c] : 0.f;
+            yh[8 * cg + c] = fmaf(o[c], inv, a);
+        }
+    }
+    if (w == 1) {
+        copy_units(kn, kch + (size_t)slot_new * DQK, kKU, lane);
+        copy_units(vn, vch + (size_t)slot_new * DV, kVU, lane);
+    }
+}
+
 // The slots of the last min(L, window) tokens of a prefix, one workgroup per
 // (batch, head).
 template <typename T, int DQK, int DV>
@@ -248,7 +372,14 @@ hipError_t decode_dv(const void* q, const void* k, const void* v, const long lon
     const T* vv = static_cast<const T*>(v);
     T* kcc = static_cast<T*>(kc);
     T* vcc = static_cast<T*>(vc);
-    if (window <= 64) {
+    if (window > 128) {
+        if (dv == 64)
+            hipLaunchKernelGGL((swa_decode_long_kernel<T, DQK, 64>), dim3(BH), dim3(256), 0, st, qq, kk, vv, pos, H,
+                               window, scale, kcc, vcc, add, y);
+        else
+            hipLaunchKernelGGL((swa_decode_long_kernel<T, DQK, 128>), dim3(BH), dim3(256), 0, st, qq, kk, vv, pos,
+                               H, window, scale, kcc, vcc, add, y);
+    } else if (window <= 64) {
         if (dv == 64)
             hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 64, 1>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH,
                                window, scale, kcc, vcc, add, y);

@@ -165,8 +165,10 @@ def _swa_dec(lib, **kw):
 @pytest.mark.parametrize("kw,want", [
     (dict(q=None), 1), (dict(pos=None), 1), (dict(kc=None), 1), (dict(y=None), 1), (dict(pos=S + 4), 1),
     (dict(kc=Y + 8), 1), (dict(dtype=3), 1), (dict(B=0), 1), (dict(window=0), 1), (dict(scale=float("inf")), 1),
-    (dict(dqk=32), 2), (dict(dv=96), 2), (dict(window=129), 2), (dict(vc=Y + 64), 1), (dict(y=Y), 1),
+    (dict(dqk=32), 2), (dict(dv=96), 2), (dict(vc=Y + 64), 1), (dict(y=Y), 1),
     (dict(kc=A), 1), (dict(y=S), 1), (dict(add=S + (1 << 20) + 16), 1),
+    # a wide window's key ring (3 MiB) reaching into the value ring
+    (dict(window=4096, vc=Y + (1 << 20)), 1),
 ])
 @fake_addresses
 def test_swa_decode_rejects(lib, kw, want):
@@ -182,7 +184,7 @@ def _swa_fill(lib, **kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(k=None), 1), (dict(vc=None), 1), (dict(kc=Y + 2), 1), (dict(L=0), 1), (dict(window=0), 1),
-    (dict(dqk=8), 2), (dict(dv=32), 2), (dict(window=200), 2), (dict(vc=Y + 64), 1), (dict(kc=A), 1),
+    (dict(dqk=8), 2), (dict(dv=32), 2), (dict(vc=Y + 64), 1), (dict(kc=A), 1),
     (dict(L=2**31 - 1), 1),
 ])
 @fake_addresses

@@ -599,6 +599,9 @@ def _nan_cache(B, H, window, d, dtype):
     (torch.bfloat16, 64, 64, 64, 0), (torch.float32, 64, 64, 64, 64), (torch.float32, 16, 128, 1, 5),
     (torch.float32, 64, 128, 33, 200), (torch.bfloat16, 64, 128, 128, 200), (torch.float32, 16, 64, 100, 10),
     (torch.bfloat16, 64, 64, 128, 0),
+    # windows over 128: the online-softmax kernel, one or several rounds per wave
+    (torch.bfloat16, 64, 128, 129, 300), (torch.float32, 16, 64, 200, 10), (torch.bfloat16, 64, 64, 300, 0),
+    (torch.float32, 64, 128, 257, 600), (torch.bfloat16, 16, 128, 600, 1500),
 ])
 def test_swa_decode_continues_window(dtype, dqk, dv, window, L):
     """Ring filled from a prefix (two sequences, prefixes L and L + 5; none
@@ -641,17 +644,20 @@ def test_swa_decode_continues_window(dtype, dqk, dv, window, L):
     np.testing.assert_array_equal(vc.double().cpu().numpy(), ovc)
 
 
-def test_swa_decode_add_and_invalid_position():
+@pytest.mark.parametrize("window", [64, 300])
+def test_swa_decode_add_and_invalid_position(window):
     """add (fused sum, in place on y); a negative position gives NaN outputs
-    for its sequence and leaves that sequence's cache untouched."""
+    for its sequence and leaves that sequence's cache untouched (the
+    one-wave kernel and, at w = 300, the workgroup-per-head kernel; the
+    prefix is 16 tokens longer than the window, so the ring has wrapped)."""
     based = based_mod()
-    B, H, window = 2, 2, 64
+    B, H, P = 2, 2, window + 16
     q, k, v = si.custom((B, H, 64), (B, H, 64), seed=1700)
-    kp, vp = si.custom((B, H, 80, 64), (B, H, 80, 64), seed=1701)[1:]
+    kp, vp = si.custom((B, H, P, 64), (B, H, P, 64), seed=1701)[1:]
     kc, vc = based.swa_cache_fill(*dev(kp, vp), window=window)
     kc0, vc0 = kc.clone(), vc.clone()
     base = torch.randn(B, H, 64, generator=torch.Generator().manual_seed(7)).to(DEV)
-    pos = torch.tensor([80, -1], dtype=torch.int64, device=DEV)
+    pos = torch.tensor([P, -1], dtype=torch.int64, device=DEV)
     y_plain = based.swa_decode_step(*dev(q, k, v), kc0, vc0, pos)
     y = base.clone()
     based.swa_decode_step(*dev(q, k, v), kc, vc, pos, add=y, y=y)
@@ -659,8 +665,8 @@ def test_swa_decode_add_and_invalid_position():
     assert torch.isnan(y[1]).all() and torch.isnan(y_plain[1]).all()
     assert torch.equal(kc[1], kc0[1]) and torch.equal(vc[1], vc0[1])
     okc, ovc = oracle.swa_cache_fill(kp[:1], vp[:1], window)
-    yo, _, _ = oracle.swa_decode_step(q[:1], k[:1], v[:1], okc, ovc, [80], window, 0.125)
-    report("swa decode add (valid sequence)", ratio(y_plain[:1], yo), 2e-2)
+    yo, _, _ = oracle.swa_decode_step(q[:1], k[:1], v[:1], okc, ovc, [P], window, 0.125)
+    report(f"swa decode add w={window} (valid sequence)", ratio(y_plain[:1], yo), 2e-2)
 
 
 @pytest.mark.timeout(600)
