@@ -500,6 +500,60 @@ def bench_window_decode(based, wl, n_steps, graph_steps=64, n_sets=16):
     return timer.seconds() / (reps * graph_steps)
 
 
+def bench_layer_decode(based, wd, ww, n_steps, graph_steps=64):
+    """One BASED-1.3B layer's next-token step: the linear-attention step
+    (state from a 1024-token prefill) and then the window step on the same
+    token (shared v; its ring filled from the same prefix), adding into the
+    linear output.  HIP graph of 64 layer steps, replayed; returns event
+    seconds per layer step."""
+    q, k, v = si.linear_inputs(wd)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    del q, k, v
+    S = torch.empty(wd.B, wd.H, F, wd.dv, device="cuda")
+    z = torch.empty(wd.B, wd.H, F, device="cuda")
+    yp = torch.empty(wd.B, wd.H, wd.L, wd.dv, device="cuda")
+    ws = torch.empty(max(1, based.based_prefill_workspace_bytes(wd.B, wd.H, wd.L, wd.dv)), dtype=torch.uint8,
+                     device="cuda")
+    based.based_prefill(qd, kd, vd, chunk=wd.chunk, eps=wd.eps, y=yp, S=S, z=z, workspace=ws)
+    del yp, ws
+    kw = si.randn((wd.B, wd.H, wd.L, ww.d_qk), 1000 * ww.index + 11, 1.0, torch.bfloat16).cuda()
+    kc, vc = based.swa_cache_fill(kw, vd, window=ww.window)
+    del qd, kd, vd, kw
+    steps = []
+    for t in range(graph_steps):
+        ql, kl, vl = (x.cuda() for x in si.decode_inputs(wd, t))
+        qw, kww = (x.cuda() for x in si.window_decode_inputs(ww, t)[:2])
+        steps.append((ql, kl, vl, qw, kww))
+    pos = [torch.full((wd.B,), wd.L + t, dtype=torch.int64, device="cuda") for t in range(graph_steps)]
+    y = torch.empty(wd.B, wd.H, wd.dv, device="cuda")
+
+    def run_all():
+        for t in range(graph_steps):
+            ql, kl, vl, qw, kww = steps[t]
+            based.based_decode_step(ql, kl, vl, S, z, eps=wd.eps, y=y)
+            based.swa_decode_step(qw, kww, vl, kc, vc, pos[t], scale=ww.swa_scale, add=y, y=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    for _ in range(3):  # untimed warm-up
+        g.replay()
+    reps = max(1, n_steps // graph_steps)
+    timer = RegionTimer()
+    torch.cuda.synchronize()
+    timer.start()
+    for _ in range(reps):
+        g.replay()
+    timer.stop()
+    return timer.seconds() / (reps * graph_steps)
+
+
 def bench_other_sizes(based):
     """The pages' other design points (feature dim 32, window 128), on the
     paths that carry them: seeded inputs, event-timed regions.  Returns a
@@ -976,6 +1030,17 @@ def main():
             "note": "w=64 ring, B=128, H=16, d_qk=64, d_v=128, fused add; HIP graph of 64 steps "
                     "replayed, 16 cache sets"}
         print(f"[bench] window decode: {wkern*1e6:.1f} us/step", file=sys.stderr, flush=True)
+        wd3 = si.WORKLOADS["decode_1p3b"]
+        lsec = bench_layer_decode(based, wd3, wwd, 256)
+        lb = decode_bytes(wd3) + window_decode_bytes(wwd)
+        extra["layer_decode_1p3b"] = {
+            "tokens_per_s": wd3.B / lsec, "layer_step_us": lsec * 1e6, "steps": 256,
+            "roofline": roofline(lb, lsec),
+            "note": "one BASED-1.3B layer's next-token step: the linear-attention step (fp32 state 273x128 per "
+                    "head, read and written once) then the w=64 window step on the same token adding into its "
+                    "output; B=128, H=16; HIP graph of 64 layer steps replayed 4 times; bytes are the two "
+                    "launches' algorithmic bytes"}
+        print(f"[bench] layer decode: {lsec*1e6:.1f} us/step", file=sys.stderr, flush=True)
         for bname, forms in (("prefill_360m", ("chunked", "direct")), ("long_64k", ("chunked",)),
                              ("decode_1p3b", ("chunked", "direct"))):
             bw = si.WORKLOADS[bname]
