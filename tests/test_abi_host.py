@@ -54,6 +54,33 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
 
 
+def test_header_is_plain_c_and_links(lib, tmp_path):
+    """include/based.h compiles as C99 and as C++, and a C program linked
+    against libbased.so (no Python) calls its host-only functions."""
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("no host C compiler")
+    src = tmp_path / "use.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "based.h"\n'
+        "int main(void) {\n"
+        '  printf("%d %d %s\\n", based_num_features(16), based_num_features(32), based_status_string(BASED_E_INVALID));\n'
+        '  printf("%zu\\n", based_prefill_backward_workspace_bytes(1, 1, 64, 16, 64));\n'
+        "  return 0;\n}\n")
+    inc = os.path.join(ROOT, "include")
+    for comp, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
+        subprocess.run([comp, std, "-Wall", "-Werror", "-fsyntax-only", "-x", "c" if comp == "gcc" else "c++",
+                        "-I", inc, str(src)], check=True)
+    exe = tmp_path / "use"
+    subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-o", str(exe), "-L", PKG, "-lbased",
+                    "-Wl,-rpath," + PKG], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, timeout=60).stdout.split("\n")
+    assert out[0].split()[:2] == ["273", "1057"] and "INVALID" in out[0]
+    assert int(out[1]) == lib.based_prefill_backward_workspace_bytes(1, 1, 64, 16, 64) > 0
+
+
 def test_num_features_and_strings(lib):
     assert lib.based_num_features(16) == 273
     assert lib.based_num_features(8) == 73
