@@ -218,6 +218,154 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
     copy_units(vn, vch + (size_t)slot_new * DV, kVU, lane);
 }
 
+// d_qk = 64 and windows up to 64 R slots: one workgroup of four waves per
+// (batch, head), wave w taking the 16 R slots [16 R w, 16 R (w + 1)) of the
+// ring, so each wave loads a quarter of the rows and more waves share a SIMD
+// (the one-wave form above leaves each wave a long chain of dependent steps
+// with few waves to hide it).  Scores: lane (s, p) takes slot s of the
+// wave's block and the 8-dim pieces p, p + P, ... of its key row (P = 64 /
+// (16 R) lanes per slot, so one load instruction of the P lanes of a slot
+// reads 16 P contiguous bytes), the parts added across lanes.  P.V: lane (kg, cg) takes 8 columns
+// of the keys kg, kg + KG, ... of the block.  Each wave's (max, sum, P.V)
+// goes to LDS and one wave merges the four after a barrier; slots beyond
+// the valid ones weigh zero through selects, as above.
+template <typename T, int DV, int R>
+__global__ __launch_bounds__(256) void swa_decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                               const T* __restrict__ v,
+                                                               const long long* __restrict__ pos, int H,
+                                                               int window, float scale, T* __restrict__ kc,
+                                                               T* __restrict__ vc, const float* add,
+                                                               float* __restrict__ y) {
+    constexpr int DQK = 64;
+    constexpr int kSPW = 16 * R;             // slots per wave
+    constexpr int kP = 64 / kSPW;            // lanes per slot in the scores
+    constexpr int kDPL = DQK / kP;           // dims per lane in the scores
+    constexpr int kQC = kDPL / 8;            // chunks of 8 dims per lane
+    constexpr int kCG = DV / 8, kKG = 64 / kCG, kKPL = kSPW / kKG;
+    constexpr int kKU = DQK * sizeof(T) / 16, kVU = DV * sizeof(T) / 16;
+    __shared__ float part_acc[4][DV];
+    __shared__ float part_ml[4][2];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const size_t head = blockIdx.x;
+    const int sl = lane / kP, pp = lane % kP;
+    const int cg = lane % kCG, kg = lane / kCG;
+    const int base = kSPW * w;  // first slot of this wave's block
+    float* yh = y + head * DV;
+    const T* kn = k + head * DQK;
+    const T* vn = v + head * DV;
+    T* kch = kc + head * (size_t)window * DQK;
+    T* vch = vc + head * (size_t)window * DV;
+
+    // ---- loads, all issued before the position is known (slots past the
+    // ring read its last row and are discarded below)
+    const long long p = pos[head / H];
+    const int j = base + sl;  // this lane's slot in the scores
+    Chunk8<T> qr[kQC], kr[kQC], knr[kQC], vr[kKPL], vnr;
+#pragma unroll
+    for (int c = 0; c < kQC; ++c) {
+        qr[c].load(q + head * DQK + 8 * (pp + kP * c));
+        knr[c].load(kn + 8 * (pp + kP * c));
+        kr[c].load(kch + (size_t)min(j, window - 1) * DQK + 8 * (pp + kP * c));
+    }
+    vnr.load(vn + 8 * cg);
+#pragma unroll
+    for (int i = 0; i < kKPL; ++i) vr[i].load(vch + (size_t)min(base + kg + kKG * i, window - 1) * DV + 8 * cg);
+    if (p < 0) {  // no valid position: NaN outputs, cache untouched
+        if (w == 0 && kg == 0) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) yh[8 * cg + c] = __builtin_nanf("");
+        }
+        return;
+    }
+    const int slot_new = (int)(p % window);
+    const int nvalid = p + 1 < window ? (int)p + 1 : window;
+    if (j == slot_new) {
+#pragma unroll
+        for (int c = 0; c < kQC; ++c) kr[c] = knr[c];
+    }
+
+    // ---- scores and this wave's softmax statistics (a wave whose block
+    // holds no valid slot ends with m = -inf, l = 0, P.V = 0)
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kQC; ++c) qr[c].dot_into(kr[c], part);
+    float dot = (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+    for (int off = 1; off < kP; off <<= 1) dot += __shfl_xor(dot, off, 64);
+    const bool valid = j < nvalid;
+    const float sc = valid ? dot * (scale * kLog2e) : -INFINITY;
+    const float m = wave_max(sc);
+    const float pe = valid ? __builtin_amdgcn_exp2f(sc - m) : 0.f;
+    const float l = wave_sum(pp == 0 ? pe : 0.f);
+
+    // ---- P.V over the block, then the sum over key groups
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kKPL; ++i) {
+        const int jj = base + kg + kKG * i;
+        if (jj == slot_new) vr[i] = vnr;
+        else if (jj >= nvalid) vr[i].zero();
+        const float pj = __shfl(pe, (kg + kKG * i) * kP, 64);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = fmaf(pj, vr[i].get(c), acc[c]);
+    }
+#pragma unroll
+    for (int off = kCG; off < 64; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
+    if (kg == 0) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) part_acc[w][8 * cg + c] = acc[c];
+    }
+    if (lane == 0) {
+        part_ml[w][0] = m;
+        part_ml[w][1] = l;
+    }
+    __syncthreads();
+    if (w == 0 && kg == 0) {
+        // wave 0's block holds slot 0, which is always valid: mx is finite
+        float mx = part_ml[0][0];
+#pragma unroll
+        for (int u = 1; u < 4; ++u) mx = fmaxf(mx, part_ml[u][0]);
+        float den = 0.f, o[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float e = __builtin_amdgcn_exp2f(part_ml[u][0] - mx);
+            den = fmaf(e, part_ml[u][1], den);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) o[c] = fmaf(e, part_acc[u][8 * cg + c], o[c]);
+        }
+        const float inv = 1.f / den;  // den >= 1: the maximum key has weight 1
+        f32x4 o0, o1;
+        if (add) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(add + head * DV + 8 * cg);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(add + head * DV + 8 * cg + 4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                o0[c] = fmaf(o[c], inv, a0[c]);
+                o1[c] = fmaf(o[4 + c], inv, a1[c]);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                o0[c] = o[c] * inv;
+                o1[c] = o[4 + c] * inv;
+            }
+        }
+        *reinterpret_cast<f32x4*>(yh + 8 * cg) = o0;
+        *reinterpret_cast<f32x4*>(yh + 8 * cg + 4) = o1;
+    }
+    if (w == 1) {
+        copy_units(kn, kch + (size_t)slot_new * DQK, kKU, lane);
+        copy_units(vn, vch + (size_t)slot_new * DV, kVU, lane);
+    }
+}
+
 // Windows over 128 slots: one workgroup of four waves per (batch, head).
 // The valid slots are taken in rounds of 64 (lane j scores slot 64 n + j of
 // round n), wave w taking rounds w, w + 4, ...; each wave keeps an online
@@ -366,34 +514,39 @@ __global__ __launch_bounds__(256) void swa_cache_fill_kernel(const T* __restrict
 template <typename T, int DQK>
 hipError_t decode_dv(const void* q, const void* k, const void* v, const long long* pos, int H, int BH, int dv,
                      int window, float scale, void* kc, void* vc, const float* add, float* y, hipStream_t st) {
-    const dim3 grid((BH + 3) / 4);
     const T* qq = static_cast<const T*>(q);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
     T* kcc = static_cast<T*>(kc);
     T* vcc = static_cast<T*>(vc);
+    // a workgroup per (batch, head), or (the wave form) four heads per workgroup
+#define BASED_SWA_DEC(KERNEL, GRID) \
+    hipLaunchKernelGGL((KERNEL), dim3(GRID), dim3(256), 0, st, qq, kk, vv, pos, H, window, scale, kcc, vcc, add, y)
+#define BASED_SWA_DEC_WAVE(KERNEL) \
+    hipLaunchKernelGGL((KERNEL), dim3((BH + 3) / 4), dim3(256), 0, st, qq, kk, vv, pos, H, BH, window, scale, kcc, \
+                       vcc, add, y)
     if (window > 128) {
-        if (dv == 64)
-            hipLaunchKernelGGL((swa_decode_long_kernel<T, DQK, 64>), dim3(BH), dim3(256), 0, st, qq, kk, vv, pos, H,
-                               window, scale, kcc, vcc, add, y);
-        else
-            hipLaunchKernelGGL((swa_decode_long_kernel<T, DQK, 128>), dim3(BH), dim3(256), 0, st, qq, kk, vv, pos,
-                               H, window, scale, kcc, vcc, add, y);
-    } else if (window <= 64) {
-        if (dv == 64)
-            hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 64, 1>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH,
-                               window, scale, kcc, vcc, add, y);
-        else
-            hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 128, 1>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH,
-                               window, scale, kcc, vcc, add, y);
+        if (dv == 64) BASED_SWA_DEC((swa_decode_long_kernel<T, DQK, 64>), BH);
+        else BASED_SWA_DEC((swa_decode_long_kernel<T, DQK, 128>), BH);
+    } else if constexpr (DQK == 64) {
+        if (window <= 64) {
+            if (dv == 64) BASED_SWA_DEC((swa_decode_split_kernel<T, 64, 1>), BH);
+            else BASED_SWA_DEC((swa_decode_split_kernel<T, 128, 1>), BH);
+        } else {
+            if (dv == 64) BASED_SWA_DEC((swa_decode_split_kernel<T, 64, 2>), BH);
+            else BASED_SWA_DEC((swa_decode_split_kernel<T, 128, 2>), BH);
+        }
     } else {
-        if (dv == 64)
-            hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 64, 2>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH,
-                               window, scale, kcc, vcc, add, y);
-        else
-            hipLaunchKernelGGL((swa_decode_kernel<T, DQK, 128, 2>), grid, dim3(256), 0, st, qq, kk, vv, pos, H, BH,
-                               window, scale, kcc, vcc, add, y);
+        if (window <= 64) {
+            if (dv == 64) BASED_SWA_DEC_WAVE((swa_decode_kernel<T, DQK, 64, 1>));
+            else BASED_SWA_DEC_WAVE((swa_decode_kernel<T, DQK, 128, 1>));
+        } else {
+            if (dv == 64) BASED_SWA_DEC_WAVE((swa_decode_kernel<T, DQK, 64, 2>));
+            else BASED_SWA_DEC_WAVE((swa_decode_kernel<T, DQK, 128, 2>));
+        }
     }
+#undef BASED_SWA_DEC
+#undef BASED_SWA_DEC_WAVE
     return hipGetLastError();
 }
 
