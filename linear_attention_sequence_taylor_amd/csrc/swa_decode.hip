@@ -271,6 +271,12 @@ __global__ __launch_bounds__(256) void swa_decode_split_kernel(const T* __restri
     vnr.load(vn + 8 * cg);
 #pragma unroll
     for (int i = 0; i < kKPL; ++i) vr[i].load(vch + (size_t)min(base + kg + kKG * i, window - 1) * DV + 8 * cg);
+    // the fused-add input of the lanes that write y, in flight with the rest
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+    if (add && w == 0 && kg == 0) {
+        a0 = *reinterpret_cast<const f32x4*>(add + head * DV + 8 * cg);
+        a1 = *reinterpret_cast<const f32x4*>(add + head * DV + 8 * cg + 4);
+    }
     if (p < 0) {  // no valid position: NaN outputs, cache untouched
         if (w == 0 && kg == 0) {
 #pragma unroll
@@ -341,21 +347,11 @@ __global__ __launch_bounds__(256) void swa_decode_split_kernel(const T* __restri
             for (int c = 0; c < 8; ++c) o[c] = fmaf(e, part_acc[u][8 * cg + c], o[c]);
         }
         const float inv = 1.f / den;  // den >= 1: the maximum key has weight 1
-        f32x4 o0, o1;
-        if (add) {
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(add + head * DV + 8 * cg);
-            const f32x4 a1 = *reinterpret_cast<const f32x4*>(add + head * DV + 8 * cg + 4);
+        f32x4 o0, o1;  // a0, a1 are zero without add
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                o0[c] = fmaf(o[c], inv, a0[c]);
-                o1[c] = fmaf(o[4 + c], inv, a1[c]);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                o0[c] = o[c] * inv;
-                o1[c] = o[4 + c] * inv;
-            }
+        for (int c = 0; c < 4; ++c) {
+            o0[c] = fmaf(o[c], inv, a0[c]);
+            o1[c] = fmaf(o[4 + c], inv, a1[c]);
         }
         *reinterpret_cast<f32x4*>(yh + 8 * cg) = o0;
         *reinterpret_cast<f32x4*>(yh + 8 * cg + 4) = o1;
