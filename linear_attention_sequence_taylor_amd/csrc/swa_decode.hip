@@ -408,6 +408,11 @@ __global__ __launch_bounds__(256) void swa_decode_long_kernel(const T* __restric
         knr[c].load(kn + 8 * c);
     }
     vnr.load(vn + 8 * cg);
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;  // fused-add input of the lanes that write y
+    if (add && w == 0 && kg == 0) {
+        a0 = *reinterpret_cast<const f32x4*>(add + head * DV + 8 * cg);
+        a1 = *reinterpret_cast<const f32x4*>(add + head * DV + 8 * cg + 4);
+    }
     float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = 0.f;
@@ -473,11 +478,14 @@ __global__ __launch_bounds__(256) void swa_decode_long_kernel(const T* __restric
             for (int c = 0; c < 8; ++c) o[c] = fmaf(e, part_acc[u][8 * cg + c], o[c]);
         }
         const float inv = 1.f / den;  // den >= 1: the maximum key has weight 1
+        f32x4 o0, o1;  // a0, a1 are zero without add
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const float a = add ? add[head * DV + 8 * cg + c] : 0.f;
-            yh[8 * cg + c] = fmaf(o[c], inv, a);
+        for (int c = 0; c < 4; ++c) {
+            o0[c] = fmaf(o[c], inv, a0[c]);
+            o1[c] = fmaf(o[4 + c], inv, a1[c]);
         }
+        *reinterpret_cast<f32x4*>(yh + 8 * cg) = o0;
+        *reinterpret_cast<f32x4*>(yh + 8 * cg + 4) = o1;
     }
     if (w == 1) {
         copy_units(kn, kch + (size_t)slot_new * DQK, kKU, lane);
