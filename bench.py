@@ -589,13 +589,17 @@ def bench_other_sizes(based):
     # prefill with feature dim 32 (bf16 inputs widened, fp32 matrix cores), B=2, H=16, L=2048, d_v=64
     B, H, L, dv = 2, 16, 2048, 64
     q, k, v = (x.cuda() for x in si.custom((B, H, L, d), (B, H, L, dv), seed=2100, scale=0.5))
+    outs = dict(y=torch.empty(B, H, L, dv, device="cuda"), S=torch.empty(B, H, F32, dv, device="cuda"),
+                z=torch.empty(B, H, F32, device="cuda"),
+                workspace=torch.empty(max(1, based.based_prefill_workspace_bytes(B, H, L, dv, d)), dtype=torch.uint8,
+                                      device="cuda"))
     for _ in range(100):  # untimed warm-up, ~50 ms
-        based.based_prefill(q, k, v)
+        based.based_prefill(q, k, v, **outs)
     t = RegionTimer()
     torch.cuda.synchronize()
     t.start()
     for _ in range(20):
-        based.based_prefill(q, k, v)
+        based.based_prefill(q, k, v, **outs)
     t.stop()
     sec = t.seconds() / 20
     pb = B * H * L * (2 * d * 2 + dv * 2 + dv * 4) + B * H * (F32 * dv + F32) * 4
@@ -604,8 +608,9 @@ def bench_other_sizes(based):
     out["prefill_d32"] = {"kernel_us": sec * 1e6, "tokens_per_s": B * L / sec, "hbm_frac": pb / sec / HBM_PEAK,
                           "algorithmic_bytes": pb, "algorithmic_flops": pf, "tflops": pf / sec / 1e12,
                           "mfma_f32_frac": pf / sec / MFMA_F32_PEAK,
-                          "note": "feature dim 32, B=2, H=16, L=2048, fp32 arithmetic on the fp32 matrix cores "
-                                  "(128 workgroups: one per head and 16 value columns)"}
+                          "note": "feature dim 32, B=2, H=16, L=2048, fp32 arithmetic on the fp32 matrix cores; "
+                                  "each head in 2 sequence segments (a state-only pass over the first, the prefix, "
+                                  "then 256 workgroups: one per head, segment and 16 value columns)"}
     return out
 
 

@@ -94,9 +94,10 @@ const char *based_status_string(based_status_t s);
 
 /* Size in bytes of the optional workspace that lets based_prefill split
  * long sequences into segments processed in parallel (carried states are
- * combined by a prefix sum over segments).  0 means the call never uses a
- * workspace for this shape (always for d_feat != 16).  Host-only; launches
- * nothing. */
+ * combined by a prefix sum over segments), enough for whichever path the
+ * call takes (the bf16 matrix cores for d_feat 16, the fp32 matrix cores
+ * for every other input at chunk 64).  0 means the call never uses a
+ * workspace for this shape.  Host-only; launches nothing. */
 size_t based_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
 
 /*

@@ -133,7 +133,7 @@ def based_prefill(q, k, v, *, chunk: int = 64, eps: float = 1e-6, initial_state=
     if initial_state is not None:
         _initial_state(initial_state, S, z)
         use_init = 1
-    if workspace is None and dt == torch.bfloat16:
+    if workspace is None and chunk == 64:
         nbytes = based_prefill_workspace_bytes(B, H, L, d_v, d)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -235,7 +235,7 @@ def based_hybrid_prefill(q, k, q_win, k_win, v, *, chunk: int = 64, eps: float =
     if initial_state is not None:
         _initial_state(initial_state, S, z)
         use_init = 1
-    if workspace is None and dt == torch.bfloat16:
+    if workspace is None and chunk == 64:
         nbytes = based_hybrid_prefill_workspace_bytes(B, H, L, d_v, d)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)

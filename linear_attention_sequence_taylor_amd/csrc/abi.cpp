@@ -77,8 +77,13 @@ BASED_API const char* based_status_string(based_status_t s) {
 BASED_API size_t based_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v) {
     uint64_t BH, BHL;
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return 0;
-    if (d_feat != kDFeatMfma || (d_v != 64 && d_v != 128)) return 0;
-    return based::prefill_mfma_workspace_bytes((int)BH, L, d_v);
+    if (!feat_dim_ok(d_feat) || (d_v != 64 && d_v != 128)) return 0;
+    // the fp32 matrix-core path (fp32 inputs, or any d_feat != 16) and, for
+    // d_feat = 16, the bf16 matrix-core plan: enough for whichever runs
+    const size_t f32 = based::prefill_f32mfma_workspace_bytes((int)BH, L, d_feat, d_v);
+    if (d_feat != kDFeatMfma) return f32;
+    const size_t bf = based::prefill_mfma_workspace_bytes((int)BH, L, d_v);
+    return bf > f32 ? bf : f32;
 }
 
 BASED_API based_status_t based_prefill(const void* q, const void* k, const void* v,
@@ -122,7 +127,8 @@ BASED_API based_status_t based_prefill(const void* q, const void* k, const void*
     // the fp32 matrix cores, chunks 16 and 32 on the vector ALUs
     if (chunk == 64)
         return launch_status(
-            based::launch_prefill_f32mfma(q, k, v, bf16, (int)BH, L, d_feat, d_v, eps, y, S, z, init, st));
+            based::launch_prefill_f32mfma(q, k, v, bf16, (int)BH, L, d_feat, d_v, eps, y, S, z, init, workspace,
+                                          workspace_bytes, st));
     return launch_status(
         based::launch_prefill_valu(q, k, v, bf16, (int)BH, L, d_feat, d_v, chunk, eps, y, S, z, init, st));
 }
@@ -185,9 +191,10 @@ BASED_API based_status_t swa_forward(const void* q, const void* k, const void* v
 BASED_API size_t based_hybrid_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v) {
     uint64_t BH, BHL;
     if (check_dims(B, H, L, &BH, &BHL) != BASED_OK) return 0;
-    if (d_feat != kDFeatMfma || (d_v != 64 && d_v != 128)) return 0;
-    const size_t a = based::prefill_mfma_workspace_bytes((int)BH, L, d_v);
-    const size_t b = based::hybrid_mfma_workspace_bytes((int)BH, L, d_v);
+    if (!feat_dim_ok(d_feat) || (d_v != 64 && d_v != 128)) return 0;
+    // the linear branch run alone (based_prefill's need) or the fused pass
+    const size_t a = based_prefill_workspace_bytes(B, H, L, d_feat, d_v);
+    const size_t b = d_feat == kDFeatMfma ? based::hybrid_mfma_workspace_bytes((int)BH, L, d_v) : 0;
     return a > b ? a : b;
 }
 

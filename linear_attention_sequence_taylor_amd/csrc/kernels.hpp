@@ -16,9 +16,14 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool 
 // fp32 vector-ALU chunked prefill (prefill_valu.hip).  d in {8, 16, 24, 32},
 // chunk in {16, 32, 64}.
 // Chunk-64 prefill for every feature dim in fp32 on the fp32 matrix cores
-// (prefill_f32mfma.hip); bf16 inputs are widened exactly.
+// (prefill_f32mfma.hip); bf16 inputs are widened exactly.  With a workspace
+// of prefill_f32mfma_workspace_bytes (0: the shape is never split) few
+// heads are split into sequence segments; without one, or with too small a
+// one, each head runs as one segment.
+size_t prefill_f32mfma_workspace_bytes(int BH, int L, int d, int dv);
 hipError_t launch_prefill_f32mfma(const void* q, const void* k, const void* v, bool bf16, int BH, int L, int d,
-                                  int dv, float eps, float* y, float* S, float* z, int use_init, hipStream_t st);
+                                  int dv, float eps, float* y, float* S, float* z, int use_init, void* workspace,
+                                  size_t workspace_bytes, hipStream_t st);
 // Final normaliser state z = z_init + sum_t phi(k_t) (prefill_valu.hip), one
 // workgroup per head; launched after a prefill whose column groups only
 // read the caller's initial z.

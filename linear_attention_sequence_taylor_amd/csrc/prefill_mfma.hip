@@ -1541,7 +1541,7 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, int 
         case 32: return launch_plan<32>(pl, qq, kk, vv, BH, L, dv, eps, y, S, z, use_init, ws, st);
         case 64: return launch_plan<64>(pl, qq, kk, vv, BH, L, dv, eps, y, S, z, use_init, ws, st);
         default:  // no workspace for a carried d_v = 128 state: the fp32 chunked kernel
-            return launch_prefill_f32mfma(q, k, v, true, BH, L, kDFeat, dv, eps, y, S, z, use_init, st);
+            return launch_prefill_f32mfma(q, k, v, true, BH, L, kDFeat, dv, eps, y, S, z, use_init, nullptr, 0, st);
     }
 }
 

@@ -96,6 +96,17 @@ def test_workspace_bytes_host_only(lib):
     assert lib.based_prefill_workspace_bytes(0, 1, 256, 16, 64) == 0
     assert lib.based_prefill_workspace_bytes(1, 1, 256, 8, 64) == 0
     assert lib.based_prefill_workspace_bytes(1, 1, 2**31 - 1, 16, 64) == 0
+    # the fp32 matrix-core path: 32 heads x 4 groups of 16 columns fill half
+    # the chip, so each head runs as 2 segments, one slot of F (d_v + 1)
+    # floats (rounded up to 64) per (head, segment)
+    F = 1 + 32 + 32 * 32
+    slot = (F * 65 + 63) // 64 * 64
+    assert lib.based_prefill_workspace_bytes(2, 16, 2048, 32, 64) == 32 * 2 * slot * 4
+    assert lib.based_prefill_workspace_bytes(8, 16, 2048, 32, 64) == 0  # 512 groups: no split
+    assert lib.based_prefill_workspace_bytes(2, 16, 500, 32, 64) == 0   # under 16 chunks: no split
+    # d_feat 16 covers the bf16 plan and the fp32 path, whichever runs
+    assert lib.based_prefill_workspace_bytes(1, 2, 4096, 16, 64) >= lib.based_prefill_workspace_bytes(1, 2, 4096, 8, 64)
+    assert lib.based_hybrid_prefill_workspace_bytes(2, 16, 2048, 32, 64) == 32 * 2 * slot * 4
 
 
 # Fake, never-dereferenced device addresses; each call below fails validation.

@@ -138,6 +138,43 @@ def test_prefill_fp32_path_initial_state(dtype, tol, d, L):
     report(f"fp32-path init-state {dtype} d={d} L={L} z", ratio(z, zo), tol)
 
 
+@pytest.mark.parametrize("B,H,L,d,dtype,tol,dv,init", [
+    (1, 2, 2048, 32, torch.float32, 1e-4, 64, False),   # 4 segments of 8 chunks
+    (1, 1, 1500, 8, torch.bfloat16, 2e-2, 128, True),   # 2 segments, ragged tail
+    (2, 3, 1100, 24, torch.float32, 1e-4, 64, True),    # 2 segments, ragged tail
+    (1, 2, 1030, 16, torch.float32, 1e-4, 128, False),  # 9 + 8 chunks, the last one 6 tokens
+])
+def test_prefill_fp32_path_segments(B, H, L, d, dtype, tol, dv, init):
+    """The fp32 matrix-core prefill split into sequence segments (few heads,
+    long sequences): a state-only pass per segment, the prefix over
+    segments from the caller's (asymmetric) initial state, and the output
+    pass from the carried-in states.  y, S and z of every head against the
+    oracle, with the default workspace and with none (one segment per
+    head)."""
+    based = based_mod()
+    q, k, v = si.custom((B, H, L, d), (B, H, L, dv), seed=780 + d + L, scale=0.5, dtype=dtype)
+    kw, S0, z0 = {}, None, None
+    if init:
+        qp, kp, vp = si.custom((B, H, 40, d), (B, H, 40, dv), seed=782 + d, scale=0.5)
+        _, S0, z0 = oracle.la_recurrent(qp, kp, vp, want_y=False)
+        S0, z0 = torch.as_tensor(S0, dtype=torch.float32), torch.as_tensor(z0, dtype=torch.float32)
+        P = torch.randn((B, H, d, d, dv), generator=torch.Generator().manual_seed(783 + d))
+        S0[:, :, 1 + d:] += 0.5 * (P - P.transpose(2, 3)).reshape(B, H, d * d, dv)
+    assert based.based_prefill_workspace_bytes(B, H, L, dv, d) > 0, "shape expected to split"
+    yo, So, zo = oracle.la_recurrent(q, k, v, S0=S0, z0=z0)
+    for ws in ("auto", "none"):
+        if init:
+            kw["initial_state"] = tuple(dev(S0, z0))
+        if ws == "none":
+            kw["workspace"] = torch.empty(0, dtype=torch.uint8, device=DEV)
+        y, S, z = based.based_prefill(*dev(q, k, v), **kw)
+        torch.cuda.synchronize()
+        name = f"fp32-path segments {dtype} d={d} L={L} dv={dv} init={init} ws={ws}"
+        report(f"{name} y", ratio(y, yo), tol)
+        report(f"{name} S", ratio(S, So), tol)
+        report(f"{name} z", ratio(z, zo), tol)
+
+
 @pytest.mark.parametrize("dtype,tol,d", [(torch.float32, 1e-4, 16), (torch.bfloat16, 2e-2, 8)])
 def test_prefill_fp32_path_resume_many_groups(dtype, tol, d):
     """The fp32 matrix-core prefill resuming from a carried state with far
