@@ -262,18 +262,23 @@ def test_prefill_long_few_heads(dv, init):
     report(f"long few-heads dv={dv} init={init} z", ratio(z, zo), 2e-2)
 
 
-@pytest.mark.parametrize("L,H", [(300, 2), (2048, 4)])
-def test_prefill_graph_replay(L, H):
+@pytest.mark.parametrize("L,H,d,dtype", [(300, 2, 16, torch.bfloat16), (2048, 4, 16, torch.bfloat16),
+                                         (2048, 2, 8, torch.bfloat16), (1500, 2, 16, torch.float32)])
+def test_prefill_graph_replay(L, H, d, dtype):
     """Captured in a HIP graph (as the benchmark runs it), every replay gives
     the eager result bit for bit, with eager work and synchronisation in
-    between replays.  (2048, 4) takes the segment split and its workspace."""
+    between replays.  (2048, 4) takes the segment split of the bf16 matrix
+    cores and its workspace; d' = 8 and the fp32 inputs, the segment split
+    of the fp32 matrix-core path (state-only pass, prefix, output pass)."""
     based = based_mod()
-    q, k, v = dev(*si.custom((1, H, L, 16), (1, H, L, 64), seed=810 + L, scale=0.5))
-    nbytes = based.based_prefill_workspace_bytes(1, H, L, 64)
+    F = 1 + d + d * d
+    q, k, v = dev(*si.custom((1, H, L, d), (1, H, L, 64), seed=810 + L, scale=0.5, dtype=dtype))
+    nbytes = based.based_prefill_workspace_bytes(1, H, L, 64, d)
+    assert L < 1024 or nbytes > 0
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
     y = torch.empty(1, H, L, 64, device=DEV)
-    S = torch.empty(1, H, 273, 64, device=DEV)
-    z = torch.empty(1, H, 273, device=DEV)
+    S = torch.empty(1, H, F, 64, device=DEV)
+    z = torch.empty(1, H, F, device=DEV)
     ref = [t.clone() for t in based.based_prefill(q, k, v, y=y, S=S, z=z, workspace=ws)]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
