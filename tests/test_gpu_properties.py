@@ -72,6 +72,38 @@ def test_random_prefill(based, case):
     _check(f"prefill case {case} z", z, zo, tol)
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_random_long_prefill_fp32_path(based, case):
+    """The fp32 matrix-core prefill on few heads and long sequences, where it
+    splits each head into segments (random count and ragged last segment),
+    with or without a carried initial state, against the oracle (y, S, z)."""
+    rng = np.random.default_rng(7600 + case)
+    B, H = (int(x) for x in rng.integers(1, 3, 2))
+    L = int(rng.integers(1024, 3000))
+    d = int(rng.choice([8, 24, 32]))
+    dv = int(rng.choice([64, 128]))
+    dtype = BF16 if rng.random() < 0.5 else F32
+    if dtype == F32 and rng.random() < 0.3:
+        d = 16
+    with_init = bool(rng.random() < 0.5)
+    print(f"[property] long fp32-path prefill case {case}: B={B} H={H} L={L} d={d} dv={dv} {dtype} "
+          f"init={with_init}", flush=True)
+    assert based.based_prefill_workspace_bytes(B, H, L, dv, d) > 0, "expected a segment split"
+    q, k, v = si.custom((B, H, L, d), (B, H, L, dv), seed=7700 + 3 * case, scale=0.5, dtype=dtype)
+    S0 = z0 = init = None
+    if with_init:
+        pq, pk, pv = si.custom((B, H, 37, d), (B, H, 37, dv), seed=7800 + 3 * case, scale=0.5, dtype=dtype)
+        _, S0, z0 = oracle.la_recurrent(pq, pk, pv, want_y=False)
+        init = (torch.from_numpy(S0).float().to(DEV), torch.from_numpy(z0).float().to(DEV))
+    y, S, z = based.based_prefill(*_dev(q, k, v), initial_state=init)
+    torch.cuda.synchronize()
+    yo, So, zo = oracle.la_recurrent(q, k, v, S0=S0, z0=z0)
+    tol = 2e-2 if dtype == BF16 else 1e-4
+    _check(f"long fp32-path prefill case {case} y", y, yo, tol)
+    _check(f"long fp32-path prefill case {case} S", S, So, tol)
+    _check(f"long fp32-path prefill case {case} z", z, zo, tol)
+
+
 @pytest.mark.parametrize("case", range(16))
 def test_random_decode_continues_prefill(based, case):
     """A random prefix through based_prefill, then a random number of
