@@ -119,7 +119,9 @@ size_t based_prefill_workspace_bytes(int B, int H, int L, int d_feat, int d_v);
  *                               last token (the handoff to based_decode_step)
  *   workspace, workspace_bytes  optional scratch (may be NULL/0); see
  *          based_prefill_workspace_bytes.  With too small a workspace the
- *          call still runs, without the segment split.
+ *          call still runs, without the segment split.  Its first
+ *          min(workspace_bytes, based_prefill_workspace_bytes) bytes must
+ *          not overlap q, k, v, y, S or z (else BASED_E_INVALID).
  * Supported: d_feat in {8, 16, 24, 32}; d_v in {64, 128}; L >= 1 (any, not
  * only multiples of chunk).  bf16 inputs with d_feat = 16 run on the bf16
  * matrix cores (fp32 accumulation and state); every other input runs in

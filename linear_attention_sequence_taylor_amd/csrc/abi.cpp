@@ -117,6 +117,16 @@ BASED_API based_status_t based_prefill(const void* q, const void* k, const void*
         overlaps(z, z_bytes, k, qk_bytes) || overlaps(z, z_bytes, v, v_bytes))
         return BASED_E_INVALID;
     if (workspace && !aligned16(workspace)) return BASED_E_INVALID;
+    // the part of the workspace a launch plan may use must not overlap
+    // anything else
+    if (workspace && workspace_bytes) {
+        const uint64_t need = based_prefill_workspace_bytes(B, H, L, d_feat, d_v);
+        const uint64_t used = need < workspace_bytes ? need : workspace_bytes;
+        const void* other[6] = {y, S, z, q, k, v};
+        const uint64_t other_bytes[6] = {y_bytes, S_bytes, z_bytes, qk_bytes, qk_bytes, v_bytes};
+        for (int i = 0; i < 6; ++i)
+            if (used && overlaps(workspace, used, other[i], other_bytes[i])) return BASED_E_INVALID;
+    }
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int init = use_initial_state ? 1 : 0;
@@ -233,6 +243,14 @@ BASED_API based_status_t based_hybrid_prefill(const void* q, const void* k, cons
             if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return BASED_E_INVALID;
     }
     if (BH * (((uint64_t)L + 63) / 64) * (d_v / 64) > (uint64_t)INT32_MAX / 2) return BASED_E_INVALID;
+    if (workspace && workspace_bytes) {  // the part a plan may use overlaps nothing else
+        const uint64_t need = based_hybrid_prefill_workspace_bytes(B, H, L, d_feat, d_v);
+        const uint64_t used = need < workspace_bytes ? need : workspace_bytes;
+        for (int a = 0; a < 3; ++a)
+            if (used && overlaps(workspace, used, outs[a], out_bytes[a])) return BASED_E_INVALID;
+        for (int b = 0; b < 5; ++b)
+            if (used && overlaps(workspace, used, ins[b], in_bytes[b])) return BASED_E_INVALID;
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     // The fused pass where it exists and is chosen; otherwise the two
     // branches in turn (the window adds into y in place).

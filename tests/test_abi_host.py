@@ -151,6 +151,10 @@ def _prefill(lib, **kw):
     (dict(d=12), 2), (dict(d=64), 2), (dict(dv=96), 2), (dict(chunk=32), 2), (dict(dtype=0, chunk=48), 2),
     (dict(d=8, chunk=48), 2),
     (dict(y=A), 1), (dict(S=Y), 1), (dict(z=S + 64), 1),
+    # a workspace overlapping y (bf16 plan) or S (fp32 path, d' 32), within
+    # the part the call's plan may use
+    (dict(H=2, L=4096, ws=Y + 256, wsb=1 << 30), 1),
+    (dict(dtype=0, d=32, H=2, L=4096, ws=S - (1 << 20), wsb=1 << 30), 1),
 ])
 @fake_addresses
 def test_prefill_rejects(lib, kw, want):
@@ -249,6 +253,8 @@ def _hyb(lib, **kw):
     (dict(dv=96), 2), (dict(dqk=8), 2), (dict(path=1, window=200), 2), (dict(chunk=32), 2), (dict(y=A), 1),
     (dict(S=Y), 1), (dict(z=V_), 1), (dict(y=C + (1 << 32)), 1), (dict(path=3), 1), (dict(path=-1), 1),
     (dict(path=1, dqk=16), 2), (dict(path=1, dtype=0), 2), (dict(path=1, window=65), 2), (dict(path=1, d=8), 2),
+    # a workspace overlapping the window keys, within the part a plan may use
+    (dict(L=4096, ws=C + (1 << 32) + 256, wsb=1 << 30), 1),
 ])
 @fake_addresses
 def test_hybrid_rejects(lib, kw, want):
