@@ -310,6 +310,48 @@ def test_prefill_deterministic():
         assert torch.equal(x, w)
 
 
+@pytest.mark.parametrize("H,L,d,dtype,tol", [
+    (2, 4096, 16, torch.bfloat16, 2e-2),  # bf16 matrix cores, segment split
+    (2, 2048, 32, torch.float32, 1e-4),   # fp32 matrix cores, segment split
+    (3, 333, 8, torch.bfloat16, 2e-2),    # fp32 matrix cores, one segment
+])
+def test_prefill_zero_queries_running_mean(H, L, d, dtype, tol):
+    """Closed form, independent of the oracle: with q = 0 every weight
+    phi(q).phi(k) is 1, so y_i = (sum_{j<=i} v_j) / (i + 1 + eps), a causal
+    running mean, whatever the keys; the final z is sum_j phi(k_j) and
+    S = sum_j phi(k_j) v_j^T, whose constant row is sum_j v_j and count
+    row z_0 = L."""
+    based = based_mod()
+    _, k, v = si.custom((1, H, L, d), (1, H, L, 64), seed=820 + d, scale=0.5, dtype=dtype)
+    q = torch.zeros_like(k)
+    y, S, z = based.based_prefill(*dev(q, k, v))
+    torch.cuda.synchronize()
+    vd = v.double()
+    cnt = torch.arange(1, L + 1, dtype=torch.float64).view(1, 1, L, 1)
+    want = vd.cumsum(2) / (cnt + 1e-6)
+    report(f"zero queries d={d} {dtype} L={L}: y vs running mean", ratio(y, want.numpy()), tol)
+    report(f"zero queries d={d} {dtype} L={L}: S constant row vs sum of v", ratio(S[:, :, 0], vd.sum(2).numpy()), tol)
+    assert torch.allclose(z[:, :, 0].double().cpu(), torch.full((1, H), float(L), dtype=torch.float64), rtol=1e-6)
+
+
+@pytest.mark.parametrize("window,dtype,tol,dv", [(64, torch.bfloat16, 2e-2, 64), (64, torch.float32, 1e-4, 128),
+                                                 (129, torch.bfloat16, 2e-2, 128), (7, torch.bfloat16, 2e-2, 64)])
+def test_swa_zero_queries_window_mean(window, dtype, tol, dv):
+    """Closed form, independent of the oracle: with q = 0 every logit is 0,
+    so y_i is the plain mean of the last min(i + 1, w) values."""
+    based = based_mod()
+    B, H, L = 1, 3, 700
+    _, k, v = si.custom((B, H, L, 64), (B, H, L, dv), seed=830 + window, scale=1.0, dtype=dtype)
+    q = torch.zeros_like(k)
+    y = based.swa_forward(*dev(q, k, v), window=window, scale=0.125)
+    torch.cuda.synchronize()
+    c = torch.cat([torch.zeros(B, H, 1, dv, dtype=torch.float64), v.double().cumsum(2)], dim=2)
+    i = torch.arange(L)
+    j0 = (i - window + 1).clamp(min=0)
+    want = (c[:, :, i + 1] - c[:, :, j0]) / (i - j0 + 1).double().view(1, 1, L, 1)
+    report(f"window zero queries w={window} {dtype} dv={dv}: y vs window mean", ratio(y, want.numpy()), tol)
+
+
 # ---------------------------------------------------------------- decode
 @pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, 2e-2), (torch.float32, 1e-4)])
 @pytest.mark.parametrize("dv", [64, 128])
