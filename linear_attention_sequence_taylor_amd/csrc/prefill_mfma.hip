@@ -74,6 +74,13 @@ constexpr float kSqrt2 = 1.41421356237309504880f;
 __device__ __forceinline__ int vt_idx(int row, int tok) {  // V^T: 8 tokens per unit
     return row * kTRow + 8 * ((tok >> 3) ^ ((row >> 1) & 7)) + (tok & 7);
 }
+// Position in V^T of token t of a chunk: within each 32-token half, the
+// 4-token groups g and g + 4 (tokens 4g..4g+3 and 16+4g..16+4g+3) sit side
+// by side, the k-slice that lane group g of a 16x16x32 product takes on
+// both the intra-chunk weights (two 16-key score tiles) and the update.
+__device__ __forceinline__ int vt_pos(int t) {
+    return (t & 32) | (((t >> 2) & 3) << 3) | (((t >> 4) & 1) << 2) | (t & 3);
+}
 __device__ __forceinline__ int kt_idx(int row, int tok) {  // K^T fp32: 4 tokens per unit
     return row * kKtRow + 4 * ((tok >> 2) ^ (row & 1)) + (tok & 3);
 }
@@ -171,12 +178,6 @@ __device__ __forceinline__ bf16x8 lds_bf16x8(const uint16_t* p) {
 }
 __device__ __forceinline__ bf16x4 lds_bf16x4(const uint16_t* p) {
     return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(p));
-}
-__device__ __forceinline__ bf16x8 join44(const uint16_t* p0, const uint16_t* p1) {
-    const uint2 a = *reinterpret_cast<const uint2*>(p0);
-    const uint2 b = *reinterpret_cast<const uint2*>(p1);
-    u32x4 u = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(bf16x8, u);
 }
 __device__ __forceinline__ bf16x8 ones8() {
     u32x4 u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -462,8 +463,8 @@ __device__ __forceinline__ void v_store(const VStage<DV>& st, PrefillSmem<DV>& s
         const u32x4 v0 = keep_if(st.v0[ps], oka), v1 = keep_if(st.v1[ps], okb);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            vt[vt_idx(8 * cb + 2 * e, 2 * p) >> 1] = lo_pair(v0[e], v1[e]);
-            vt[vt_idx(8 * cb + 2 * e + 1, 2 * p) >> 1] = hi_pair(v0[e], v1[e]);
+            vt[vt_idx(8 * cb + 2 * e, vt_pos(2 * p)) >> 1] = lo_pair(v0[e], v1[e]);
+            vt[vt_idx(8 * cb + 2 * e + 1, vt_pos(2 * p)) >> 1] = hi_pair(v0[e], v1[e]);
         }
     }
 }
@@ -551,7 +552,7 @@ __device__ __forceinline__ void diag_block(const PrefillSmem<DV>& sm, int buf, i
         bf16x8 vb[kNV];
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct)
-            vb[ct] = join44(vt_l + vt_idx(16 * ct + r, 32 * p + 4 * g), vt_l + vt_idx(16 * ct + r, 32 * p + 16 + 4 * g));
+            vb[ct] = lds_bf16x8(vt_l + vt_idx(16 * ct + r, 32 * p + 8 * g));  // tokens 32p + {4g.., 16+4g..}
         // hi parts of every column tile first, then the lo parts, so
         // consecutive MFMAs never depend on each other
 #pragma unroll
@@ -936,8 +937,9 @@ __device__ __forceinline__ void update_wave(const uint16_t* __restrict__ qh, con
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             float kv[8];
-            const f32x4 k0 = *reinterpret_cast<const f32x4*>(kt_l + kt_idx(r, 32 * s + 8 * g));
-            const f32x4 k1 = *reinterpret_cast<const f32x4*>(kt_l + kt_idx(r, 32 * s + 8 * g + 4));
+            // tokens 32s + 4g.. and 32s + 16 + 4g.. (the V^T slice at 32s + 8g)
+            const f32x4 k0 = *reinterpret_cast<const f32x4*>(kt_l + kt_idx(r, 32 * s + 4 * g));
+            const f32x4 k1 = *reinterpret_cast<const f32x4*>(kt_l + kt_idx(r, 32 * s + 16 + 4 * g));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 kv[i] = k0[i];
