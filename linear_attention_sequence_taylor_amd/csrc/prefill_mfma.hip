@@ -415,10 +415,12 @@ __device__ __forceinline__ void qk_load(QKStage& st, const uint16_t* qh, const u
     const uint16_t* src = t < 128 ? kh : qh;
     st.a = *reinterpret_cast<const u32x4*>(src + (size_t)tok * kDFeat + 8 * (t & 1));
 }
-template <int DV>
+// MASK: the chunk runs past L and its rows there are zeroed (a full chunk
+// takes the branch without the selects).
+template <int DV, bool MASK>
 __device__ __forceinline__ void qk_store(const QKStage& in, PrefillSmem<DV>& sm, int buf, int t0, int L, int t) {
     const int tok = (t & 127) >> 1, half = t & 1;
-    const u32x4 a = keep_if(in.a, t0 + tok < L);
+    const u32x4 a = MASK ? keep_if(in.a, t0 + tok < L) : in.a;
     uint16_t* rowm = t < 128 ? &sm.k[buf][0] : &sm.q[buf][0];
     *reinterpret_cast<u32x4*>(rowm + qk_idx(tok, 8 * half)) = a;
     if (t < 128) {
@@ -451,7 +453,7 @@ __device__ __forceinline__ void v_load(VStage<DV>& st, const uint16_t* vh, int l
         st.v1[ps] = *reinterpret_cast<const u32x4*>(vh + (size_t)tb * ldv + 8 * cb);
     }
 }
-template <int DV>
+template <int DV, bool MASK>
 __device__ __forceinline__ void v_store(const VStage<DV>& st, PrefillSmem<DV>& sm, int buf, int t0, int L, int u) {
     const int p = u & 31;
     const bool oka = t0 + 2 * p < L, okb = t0 + 2 * p + 1 < L;
@@ -460,7 +462,8 @@ __device__ __forceinline__ void v_store(const VStage<DV>& st, PrefillSmem<DV>& s
     for (int ps = 0; ps < VStage<DV>::kPass; ++ps) {
         const int cb = (u >> 5) + 8 * ps;
         if (8 * cb >= DV) continue;
-        const u32x4 v0 = keep_if(st.v0[ps], oka), v1 = keep_if(st.v1[ps], okb);
+        const u32x4 v0 = MASK ? keep_if(st.v0[ps], oka) : st.v0[ps];
+        const u32x4 v1 = MASK ? keep_if(st.v1[ps], okb) : st.v1[ps];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             vt[vt_idx(8 * cb + 2 * e, vt_pos(2 * p)) >> 1] = lo_pair(v0[e], v1[e]);
@@ -490,8 +493,13 @@ struct StagePipe {
         if (DO_QK && t >= 0) qk_load(rg.qk, qh, kh, t0, L, t);
     }
     __device__ __forceinline__ void store(const Regs& rg, PrefillSmem<DV>& sm, int buf, int t0) {
-        if (DO_V && vu >= 0) v_store<DV>(rg.v, sm, buf, t0, L, vu);
-        if (DO_QK && t >= 0) qk_store<DV>(rg.qk, sm, buf, t0, L, t);
+        if (t0 + kC <= L) {  // uniform: a full chunk needs no zeroing
+            if (DO_V && vu >= 0) v_store<DV, false>(rg.v, sm, buf, t0, L, vu);
+            if (DO_QK && t >= 0) qk_store<DV, false>(rg.qk, sm, buf, t0, L, t);
+        } else {
+            if (DO_V && vu >= 0) v_store<DV, true>(rg.v, sm, buf, t0, L, vu);
+            if (DO_QK && t >= 0) qk_store<DV, true>(rg.qk, sm, buf, t0, L, t);
+        }
     }
     // chunk 0 into LDS buffer 0; chunks 1 and 2 in flight
     __device__ __forceinline__ void prologue(PrefillSmem<DV>& sm, int nchunks) {
