@@ -402,8 +402,10 @@ __device__ __forceinline__ u32x4 keep_if(const u32x4& x, bool ok) {
     for (int i = 0; i < 4; ++i) r[i] = ok ? x[i] : 0u;
     return r;
 }
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+// (a & 0xffff) | (b << 16) and (a >> 16) | (b & 0xffff0000), one byte
+// permute each (v_perm_b32 numbers src1's bytes 0-3 and src0's 4-7)
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 // Unconditional 16-byte loads: rows past the end are clamped to the last
 // row and zeroed when stored, so no branch sits between prefetch and use.
