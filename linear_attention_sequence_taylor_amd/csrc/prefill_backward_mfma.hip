@@ -576,9 +576,11 @@ constexpr int kSlot = 16 * kNTile;                   // 160 state rows
 constexpr int kStateFloats = kSlot * 64 + kSlot;     // one (segment, head) state, d_v = 64
 
 // Value of lane (r - N) mod 16 of this lane's 16-lane row (1 <= N <= 15).
+// A rotation reads a valid lane everywhere, so no old value is kept (a
+// kept old value would cost a register move before every rotation).
 template <int N>
 __device__ __forceinline__ float ror16(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xf, 0xf, true));
 }
 
 // Coefficient of slot (t, row).
