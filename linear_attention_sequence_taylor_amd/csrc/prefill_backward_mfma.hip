@@ -765,7 +765,7 @@ __device__ __forceinline__ void publish_wave(const f32x4 (&acc)[10], const float
             const uint32_t hp = pack_bf16x2(zc, 0.f);
             ps.z[p] = zc;
             ps.zhi[p] = (uint16_t)(hp & 0xffffu);
-            ps.zlo[p] = (uint16_t)(lo_pair_of(hp, zc, 0.f) & 0xffffu);
+            ps.zlo[p] = (uint16_t)(pack_bf16x2(zc - bf16lo_f32(hp), 0.f) & 0xffffu);  // zc - hi is exact
         }
     }
 }
@@ -1171,14 +1171,21 @@ __global__ __launch_bounds__(256, 3 - kSweepBuf) void bwd_qsweep_kernel(const ui
         for (int m = 0; m < 4; ++m) {
             const int qi = qw0 + 4 * g + m;
             const float inv = 1.f / (dsum[m] + eps);
-            float dyy = 0.f;
+            float dyy = 0.f, gv[kNV];
 #pragma unroll
             for (int ct = 0; ct < kNV; ++ct) {
                 dyy = fmaf(dyc[m][ct], yacc[ct][m], dyy);
-                const float gv = dyc[m][ct] * inv;
-                const uint32_t hb = pack_bf16x2(gv, 0.f);
+                gv[ct] = dyc[m][ct] * inv;
+            }
+            // hi/lo pairs two columns at a time (one conversion per pair)
+#pragma unroll
+            for (int ct = 0; ct < kNV; ct += 2) {
+                const uint32_t hb = pack_bf16x2(gv[ct], gv[ct + 1]);
+                const uint32_t lb = lo_pair_of(hb, gv[ct], gv[ct + 1]);
                 tt.ghi[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(hb & 0xffffu);
-                tt.glo[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(lo_pair_of(hb, gv, 0.f) & 0xffffu);
+                tt.ghi[w][tile_at<DV>(4 * g + m, 16 * ct + 16 + r)] = (uint16_t)(hb >> 16);
+                tt.glo[w][tile_at<DV>(4 * g + m, 16 * ct + r)] = (uint16_t)(lb & 0xffffu);
+                tt.glo[w][tile_at<DV>(4 * g + m, 16 * ct + 16 + r)] = (uint16_t)(lb >> 16);
             }
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) dyy += __shfl_xor(dyy, off, 64);
