@@ -1188,53 +1188,67 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)BASED_LDS_PTR(const void, p);
 }
 
-// One k-step (32 tokens from row tb) of the slot: this lane's 8 K values
-// (feature dim r of its group's tokens, see above) and the B operand of each
-// value column tile (the same tokens, column 16ct + r).  One asm block with
-// its own wait: the compiler cannot tell these reads from the copies in
-// flight into other slots and would otherwise wait for all of them.
+// LDS byte addresses of this lane's reads in ring slot 0 for one k-step (32
+// tokens from row tb): its 8 K values (feature dim r of its group's tokens,
+// see above) and the B operand of each value column tile (the same tokens,
+// column 16ct + r).  Slot s lies s slot sizes further on, which the reads
+// add as an immediate offset, so the addresses are computed once.
 template <int DV>
-__device__ __forceinline__ void state_reads(const StateRingT<DV>& rg, int slot, int tb, int g, int r, uint2 (&kk)[2],
-                                            bf16x8 (&vb)[DV / 16]) {
+struct StateReadBase {
+    uint32_t k0, k1, va[DV / 16][2];
+};
+template <int DV>
+__device__ __forceinline__ StateReadBase<DV> state_read_base(const StateRingT<DV>& rg, int tb, int g, int r) {
+    StateReadBase<DV> b;
     const int row0 = tb + 4 * g + (r >> 2), row1 = row0 + 16, col = 4 * (r & 3);
-    const uint32_t k0 = lds_addr(&rg.k[slot][row0 * kDFeat + col]);
-    const uint32_t k1 = lds_addr(&rg.k[slot][row1 * kDFeat + col]);
-    uint32_t va[DV / 16][2];
+    b.k0 = lds_addr(&rg.k[0][row0 * kDFeat + col]);
+    b.k1 = lds_addr(&rg.k[0][row1 * kDFeat + col]);
 #pragma unroll
     for (int ct = 0; ct < DV / 16; ++ct) {
-        va[ct][0] = lds_addr(&rg.v[slot][sv_idx<DV>(row0, 16 * ct + col)]);
-        va[ct][1] = lds_addr(&rg.v[slot][sv_idx<DV>(row1, 16 * ct + col)]);
+        b.va[ct][0] = lds_addr(&rg.v[0][sv_idx<DV>(row0, 16 * ct + col)]);
+        b.va[ct][1] = lds_addr(&rg.v[0][sv_idx<DV>(row1, 16 * ct + col)]);
     }
+    return b;
+}
+
+// The reads of one k-step in ring slot SLOT.  One asm block with its own
+// wait: the compiler cannot tell these reads from the copies in flight into
+// other slots and would otherwise wait for all of them.
+template <int DV, int SLOT>
+__device__ __forceinline__ void state_reads(const StateReadBase<DV>& b, uint2 (&kk)[2], bf16x8 (&vb)[DV / 16]) {
+    constexpr int kOff = SLOT * kC * kDFeat * 2, vOff = SLOT * kC * DV * 2;  // bytes
+    static_assert(kOff < 65536 && vOff < 65536, "slot offset fits the immediate field");
     uint2 x[DV / 8];
     if constexpr (DV == 64) {
         asm volatile(
-            "ds_read_b64_tr_b16 %0, %10\n\t"
-            "ds_read_b64_tr_b16 %1, %11\n\t"
-            "ds_read_b64_tr_b16 %2, %12\n\t"
-            "ds_read_b64_tr_b16 %3, %13\n\t"
-            "ds_read_b64_tr_b16 %4, %14\n\t"
-            "ds_read_b64_tr_b16 %5, %15\n\t"
-            "ds_read_b64_tr_b16 %6, %16\n\t"
-            "ds_read_b64_tr_b16 %7, %17\n\t"
-            "ds_read_b64_tr_b16 %8, %18\n\t"
-            "ds_read_b64_tr_b16 %9, %19\n\t"
+            "ds_read_b64_tr_b16 %0, %10 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %1, %11 offset:%20\n\t"
+            "ds_read_b64_tr_b16 %2, %12 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %3, %13 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %4, %14 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %5, %15 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %6, %16 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %7, %17 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %8, %18 offset:%21\n\t"
+            "ds_read_b64_tr_b16 %9, %19 offset:%21\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]),
               "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
-            : "v"(k0), "v"(k1), "v"(va[0][0]), "v"(va[0][1]), "v"(va[1][0]), "v"(va[1][1]), "v"(va[2][0]),
-              "v"(va[2][1]), "v"(va[3][0]), "v"(va[3][1])
+            : "v"(b.k0), "v"(b.k1), "v"(b.va[0][0]), "v"(b.va[0][1]), "v"(b.va[1][0]), "v"(b.va[1][1]),
+              "v"(b.va[2][0]), "v"(b.va[2][1]), "v"(b.va[3][0]), "v"(b.va[3][1]), "i"(kOff), "i"(vOff)
             : "memory");
     } else {
         asm volatile(
-            "ds_read_b64_tr_b16 %0, %6\n\t"
-            "ds_read_b64_tr_b16 %1, %7\n\t"
-            "ds_read_b64_tr_b16 %2, %8\n\t"
-            "ds_read_b64_tr_b16 %3, %9\n\t"
-            "ds_read_b64_tr_b16 %4, %10\n\t"
-            "ds_read_b64_tr_b16 %5, %11\n\t"
+            "ds_read_b64_tr_b16 %0, %6 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %1, %7 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %2, %8 offset:%13\n\t"
+            "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+            "ds_read_b64_tr_b16 %4, %10 offset:%13\n\t"
+            "ds_read_b64_tr_b16 %5, %11 offset:%13\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
-            : "v"(k0), "v"(k1), "v"(va[0][0]), "v"(va[0][1]), "v"(va[1][0]), "v"(va[1][1])
+            : "v"(b.k0), "v"(b.k1), "v"(b.va[0][0]), "v"(b.va[0][1]), "v"(b.va[1][0]), "v"(b.va[1][1]),
+              "i"(kOff), "i"(vOff)
             : "memory");
     }
 #pragma unroll
@@ -1251,6 +1265,17 @@ __device__ __forceinline__ void wait_vm(int n) {
         BASED_WVM(8) BASED_WVM(9) BASED_WVM(10)
 #undef BASED_WVM
         default: __builtin_amdgcn_s_waitcnt(11 | 0x70 | 0xF00); break;
+    }
+}
+
+// f(integral_constant<Q>, cb + QG) for Q = Q0 .. NQ - 1 while cb + QG < nch.
+template <int Q, int NQ, int G, typename F>
+__device__ __forceinline__ void for_groups(F& f, int cb, int nch) {
+    if constexpr (Q < NQ) {
+        if (cb + Q * G < nch) {
+            f(std::integral_constant<int, Q>{}, cb + Q * G);
+            for_groups<Q + 1, NQ, G>(f, cb, nch);
+        }
     }
 }
 
@@ -1294,7 +1319,36 @@ __device__ __forceinline__ void state_pair(const uint16_t* kh, const uint16_t* v
     const int first = min(kRing - G, nch);
     for (int c = 0; c < first; ++c)
         if (copies) state_dma<DV>(kh, vh, ldv, c * kC, rg, c, w, lane);
-    for (int c0 = 0; c0 < nch; c0 += G) {
+    const StateReadBase<DV> rb = state_read_base<DV>(rg, 32 * H, g, r);
+    // the products of one chunk, staged in ring slot S
+    auto chunk = [&](auto slot) {
+        constexpr int S = decltype(slot)::value;
+        uint2 kk[2];
+        bf16x8 vb[kNV];
+        state_reads<DV, S>(rb, kk, vb);
+        float kv[8];
+        kv[0] = bf16lo_f32(kk[0].x);
+        kv[1] = bf16hi_f32(kk[0].x);
+        kv[2] = bf16lo_f32(kk[0].y);
+        kv[3] = bf16hi_f32(kk[0].y);
+        kv[4] = bf16lo_f32(kk[1].x);
+        kv[5] = bf16hi_f32(kk[1].x);
+        kv[6] = bf16lo_f32(kk[1].y);
+        kv[7] = bf16hi_f32(kk[1].y);
+        const bf16x8 f0 = psi_k<T0>(kv, t8);
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) a0[ct] = mfma32(f0, vb[ct], a0[ct]);
+        a0[kNV] = mfma32(f0, ones, a0[kNV]);
+        const bf16x8 f1 = psi_k<T1>(kv, t8);
+#pragma unroll
+        for (int ct = 0; ct < kNV; ++ct) a1[ct] = mfma32(f1, vb[ct], a1[ct]);
+        a1[kNV] = mfma32(f1, ones, a1[kNV]);
+    };
+    // group Q of a ring turn: chunks c0 = cb + QG .. + G - 1 (slots QG..),
+    // the copies of the chunks kRing - G further on issued first.  The loop
+    // runs whole ring turns, so every slot index is a constant.
+    auto group = [&](auto q, int c0) {
+        constexpr int Q = decltype(q)::value;
         // this wave's copies of chunks c0 .. c0 + G - 1 have landed once at
         // most the copies of the chunks after them are outstanding; the
         // barrier makes every wave's copies visible and frees the slots of
@@ -1304,33 +1358,13 @@ __device__ __forceinline__ void state_pair(const uint16_t* kh, const uint16_t* v
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const int cn = c0 + kRing - G + j;
-            if (copies && cn < nch) state_dma<DV>(kh, vh, ldv, cn * kC, rg, cn % kRing, w, lane);
+            if (copies && cn < nch) state_dma<DV>(kh, vh, ldv, cn * kC, rg, (Q * G + kRing - G + j) % kRing, w, lane);
         }
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            if (c0 + j >= nch) break;
-            uint2 kk[2];
-            bf16x8 vb[kNV];
-            state_reads<DV>(rg, (c0 + j) % kRing, 32 * H, g, r, kk, vb);
-            float kv[8];
-            kv[0] = bf16lo_f32(kk[0].x);
-            kv[1] = bf16hi_f32(kk[0].x);
-            kv[2] = bf16lo_f32(kk[0].y);
-            kv[3] = bf16hi_f32(kk[0].y);
-            kv[4] = bf16lo_f32(kk[1].x);
-            kv[5] = bf16hi_f32(kk[1].x);
-            kv[6] = bf16lo_f32(kk[1].y);
-            kv[7] = bf16hi_f32(kk[1].y);
-            const bf16x8 f0 = psi_k<T0>(kv, t8);
-#pragma unroll
-            for (int ct = 0; ct < kNV; ++ct) a0[ct] = mfma32(f0, vb[ct], a0[ct]);
-            a0[kNV] = mfma32(f0, ones, a0[kNV]);
-            const bf16x8 f1 = psi_k<T1>(kv, t8);
-#pragma unroll
-            for (int ct = 0; ct < kNV; ++ct) a1[ct] = mfma32(f1, vb[ct], a1[ct]);
-            a1[kNV] = mfma32(f1, ones, a1[kNV]);
-        }
-    }
+        chunk(std::integral_constant<int, (Q * G) % kRing>{});
+        if (c0 + 1 < nch) chunk(std::integral_constant<int, (Q * G + 1) % kRing>{});
+    };
+    static_assert(G == 2 && kRing % G == 0, "two chunks per interval, whole groups per ring turn");
+    for (int cb = 0; cb < nch; cb += kRing) for_groups<0, kRing / G, G>(group, cb, nch);
     // the H = 1 waves' sums through LDS (the ring is free after the barrier)
     raw_barrier();
     f32x4* xch = reinterpret_cast<f32x4*>(&rg.k[0][0]) + (size_t)P * 2 * kNCT * 64;
