@@ -875,14 +875,15 @@ def test_hybrid_initial_state(ws):
     report(f"hybrid init-state ws={ws} z", ratio(z, zo), 2e-2)
 
 
-@pytest.mark.parametrize("dtype,tol,dqk,window", [
-    (torch.bfloat16, 2e-2, 16, 64), (torch.bfloat16, 2e-2, 64, 100), (torch.float32, 1e-4, 64, 64),
+@pytest.mark.parametrize("dtype,tol,dqk,window,L", [
+    (torch.bfloat16, 2e-2, 16, 64, 200), (torch.bfloat16, 2e-2, 64, 100, 200), (torch.float32, 1e-4, 64, 64, 200),
+    (torch.float32, 1e-4, 64, 64, 2100),  # the linear branch split into segments (fp32 matrix cores)
 ])
-def test_hybrid_composed_paths(dtype, tol, dqk, window):
+def test_hybrid_composed_paths(dtype, tol, dqk, window, L):
     """Arguments without a fused kernel (16-dim window q/k, a window over
     64, fp32) run the two branches in turn; same result."""
     based = based_mod()
-    q, k, v, qw, kw = _hybrid_inputs(1, 2, 200, seed=2460 + dqk + window, dqk=dqk, dtype=dtype)
+    q, k, v, qw, kw = _hybrid_inputs(1, 2, L, seed=2460 + dqk + window, dqk=dqk, dtype=dtype)
     scale = dqk ** -0.5
     y, S, z = based.based_hybrid_prefill(*dev(q, k, qw, kw, v), window=window, scale=scale)
     yo, So, zo = oracle.la_recurrent(q, k, v)
