@@ -13,8 +13,6 @@ namespace based {
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool bf16, int BH, int d,
                               int dv, float eps, float* S, float* z, float* y, hipStream_t st);
 
-// fp32 vector-ALU chunked prefill (prefill_valu.hip).  d in {8, 16, 24, 32},
-// chunk in {16, 32, 64}.
 // Chunk-64 prefill for every feature dim in fp32 on the fp32 matrix cores
 // (prefill_f32mfma.hip); bf16 inputs are widened exactly.  With a workspace
 // of prefill_f32mfma_workspace_bytes (0: the shape is never split) few
@@ -29,6 +27,8 @@ hipError_t launch_prefill_f32mfma(const void* q, const void* k, const void* v, b
 // read the caller's initial z.
 hipError_t launch_prefill_z(const void* k, bool bf16, int BH, int L, int d, float* z, int use_init,
                             hipStream_t st);
+// fp32 vector-ALU chunked prefill (prefill_valu.hip).  d in {8, 16, 24, 32},
+// chunk in {16, 32, 64}.
 hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, bool bf16, int BH, int L, int d,
                                int dv, int chunk, float eps, float* y, float* S, float* z,
                                int use_init, hipStream_t st);
@@ -66,7 +66,7 @@ hipError_t launch_swa_mfma(const void* q, const void* k, const void* v, int BH, 
 
 // Next-token step of the sliding window on its key/value ring cache, and the
 // fill of that cache from a prefix (swa_decode.hip).  dqk in {16, 64}, dv in
-// {64, 128}, window <= 64; pos is a device array [B].
+// {64, 128}, any window >= 1; pos is a device array [B].
 hipError_t launch_swa_decode_step(const void* q, const void* k, const void* v, bool bf16, const long long* pos,
                                   int H, int BH, int dqk, int dv, int window, float scale, void* kc, void* vc,
                                   const float* add, float* y, hipStream_t st);
