@@ -42,8 +42,9 @@
 //    same MFMAs in the same register layout as the numerator.
 //  * Readout of chunk c uses the state before c, double-buffered in LDS.
 //    The linear/constant rows (the last feature k-step) are stored as a
-//    hi/lo bf16 pair and read against a hi/lo psi(Q); the on-diagonal
-//    weights 1 + s + s^2/2 are a hi/lo bf16 pair too.
+//    hi/lo bf16 pair and read against a single-bf16 psi(Q) (exact for the
+//    constant and linear terms); the on-diagonal weights 1 + s + s^2/2
+//    are a hi/lo bf16 pair.
 //  * Q, K, V of chunk c+1 are fetched into registers two chunks ahead and
 //    written to the other LDS buffer during chunk c (V and K transposed).
 
@@ -625,19 +626,20 @@ __device__ __forceinline__ void offdiag_wave(const uint16_t* __restrict__ qh, co
         BASED_READOUT_STEP(2)
         BASED_READOUT_STEP(3)
 #undef BASED_READOUT_STEP
-        // last feature k-step (pairs (r, r+8), constant, linear): hi/lo on both sides
+        // last feature k-step (pairs (r, r+8), constant, linear): the state
+        // side as a hi/lo pair (its constant and linear rows carry the
+        // largest sums); the features in single bf16, where the constant
+        // and the linear terms (raw bf16 q) are exact and the pairs are
+        // rounded like every other pair feature
         float a[8];
         psi_q<4>(qr, g, a);
-        bf16x8 ahi, alo;
-        pack8_hilo(a, ahi, alo);
+        const bf16x8 ahi = pack8(a);
         bf16x8 sb[kNCT];
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct) sb[ct] = lds_bf16x8(shi + (16 * ct + r) * kSRow + 8 * unit_swz(16 + g, r));
         sb[kNV] = lds_bf16x8(&sm.z_hi[buf][8 * (16 + g)]);
 #pragma unroll
         for (int ct = 0; ct < kNCT; ++ct) y[ct] = mfma32(ahi, sb[ct], y[ct]);
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct) y[ct] = mfma32(alo, sb[ct], y[ct]);
 #pragma unroll
         for (int ct = 0; ct < kNV; ++ct)
             y[ct] = mfma32(ahi, lds_bf16x8(slo + (16 * ct + r) * kLoRow + 8 * unit_swz(g, r)), y[ct]);
