@@ -57,6 +57,9 @@ MFMA_F32_PEAK = 157.3e12   # flop/s, dense fp32 matrix cores
 METRIC = "tokens/sec for Taylor lin-attn prefill & decode; % of HBM / MFMA peak"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "linear_attention_sequence_taylor_amd", "csrc")
+# the sources of the bf16 prefill and fused hybrid kernels (their counter
+# summaries are valid while these are unchanged)
+PREFILL_SOURCES = ("prefill_mfma.hip", "prefill_mfma_kernels.hpp", "prefill_mfma_ilp.hip", "common.hpp")
 N_SETS = 4
 F = 273
 
@@ -231,7 +234,7 @@ def counter_mfma_busy(name: str, sec: float):
             parts = line.replace(":", " ").split()
             if len(parts) >= 2:
                 vals[parts[0]] = parts[1]
-    if vals.get("kernel_source_sha256_16") != source_digest("prefill_mfma.hip", "common.hpp"):
+    if vals.get("kernel_source_sha256_16") != source_digest(*PREFILL_SOURCES):
         return None
     try:
         return float(vals["SQ_VALU_MFMA_BUSY_CYCLES"]) / (1024 * sec * 2.4e9)
@@ -322,7 +325,7 @@ def headline_spec(based, cfg: str) -> dict:
     if cfg in ("cfg2", "cfg5"):
         return {"wl": wl, "step": prefill_sets(based, wl), "tokens": wl.B * wl.L, "bytes": prefill_bytes(wl),
                 "flops": prefill_flops(wl), "kernel": "based_prefill (bf16 MFMA)",
-                "traffic": (f"prefill_mfma_{wl.name}_pmc.txt", ("prefill_mfma.hip", "common.hpp")), "config": conf}
+                "traffic": (f"prefill_mfma_{wl.name}_pmc.txt", PREFILL_SOURCES), "config": conf}
     if cfg == "cfg3":
         # the state of a 1024-token prefix, then steps cycling over 4 input sets
         q, k, v = (t.cuda() for t in si.linear_inputs(wl))
@@ -353,7 +356,7 @@ def headline_spec(based, cfg: str) -> dict:
         conf.update({"window": wl.window, "d_qk": wl.d_qk})
         return {"wl": wl, "step": step, "tokens": wl.B * wl.L, "bytes": hybrid_bytes(wl), "flops": None,
                 "kernel": "based_hybrid_prefill", "config": conf,
-                "traffic": ("prefill_mfma_hybrid_window_8k_pmc.txt", ("prefill_mfma.hip", "common.hpp"))}
+                "traffic": ("prefill_mfma_hybrid_window_8k_pmc.txt", PREFILL_SOURCES)}
     # cfg1: the tiny fp32 layer, linear attention then the window adding into y
     q, k, v = (t.cuda() for t in si.linear_inputs(wl))
     y = torch.empty(1, 1, wl.L, wl.dv, device="cuda")
@@ -908,7 +911,7 @@ def main():
     step_s, kern_s, dist = bench_headline(spec["step"], args.steps, args.warmup)
     tokens = spec["tokens"]
     abytes, aflops = spec["bytes"], spec["flops"]
-    digest = source_digest("prefill_mfma.hip", "common.hpp")
+    digest = source_digest(*PREFILL_SOURCES)
     traffic = None
     if spec["traffic"]:
         traffic = read_traffic(spec["traffic"][0], source_digest(*spec["traffic"][1]))
@@ -990,7 +993,7 @@ def main():
                              "tokens_per_s": ww.B * ww.L / ht["auto"],
                              "roofline": roofline(hb, ht["auto"], read_traffic(
                                  "prefill_mfma_hybrid_window_8k_pmc.txt",
-                                 source_digest("prefill_mfma.hip", "common.hpp"))),
+                                 source_digest(*PREFILL_SOURCES))),
                              "fused_us": ht["fused"] * 1e6, "two_pass_us": ht["two_pass"] * 1e6,
                              "note": "linear attention + w=64 window through based_hybrid_prefill; kernel_us is the "
                                      "library's own choice (auto), fused_us the one-kernel path, two_pass_us "
