@@ -57,6 +57,7 @@ MFMA_F32_PEAK = 157.3e12   # flop/s, dense fp32 matrix cores
 METRIC = "tokens/sec for Taylor lin-attn prefill & decode; % of HBM / MFMA peak"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "linear_attention_sequence_taylor_amd", "csrc")
+BUILD_SCRIPT = os.path.join(ROOT, "linear_attention_sequence_taylor_amd", "build.py")
 # the sources of the bf16 prefill and fused hybrid kernels (their counter
 # summaries are valid while these are unchanged)
 PREFILL_SOURCES = ("prefill_mfma.hip", "prefill_mfma_kernels.hpp", "prefill_mfma_ilp.hip", "common.hpp")
@@ -112,9 +113,11 @@ def window_decode_bytes(wl) -> int:
 
 # ---------------------------------------------------------------- helpers
 def source_digest(*names) -> str:
+    """Digest of the named csrc/ files and of the build script (whose
+    per-source compiler flags change the kernels as much as the sources do)."""
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(CSRC, n), "rb") as f:
+    for path in [os.path.join(CSRC, n) for n in names] + [BUILD_SCRIPT]:
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
