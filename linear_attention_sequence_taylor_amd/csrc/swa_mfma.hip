@@ -382,6 +382,12 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
     for (int h = 0; h < HALO; ++h)
         dma_tile<DQK>(qh, kh, vh, ldv, L, tb - HALO + h, ks[h], vs[h], nullptr, false, w, lane);
     dma_tile<DQK>(qh, kh, vh, ldv, L, tb, ks[HALO], vs[HALO], q0s, true, w, lane);
+    // The counted waits below need the copies issued before every other
+    // vector-memory access that follows them in the source: nothing may be
+    // scheduled across this point (the add loads would otherwise be free to
+    // move above the copies, and the wait would then let copies still be in
+    // flight at the barrier).
+    __builtin_amdgcn_sched_barrier(0);
     if (ADD) {
         load_add(ra, tb * kQT + 16 * w, g, r, ldv, adda);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
@@ -408,6 +414,7 @@ __global__ __launch_bounds__(256) void swa_mfma_kernel(const uint16_t* __restric
         sl.qn = qs[(j + 1) % 2];
         if (t + 1 < te) {
             dma_tile<DQK>(qh, kh, vh, ldv, L, t + 1, sl.kn, sl.vn, sl.qn, true, w, lane);
+            __builtin_amdgcn_sched_barrier(0);  // the copies first (see the prologue)
             if (ADD) load_add(ra, (t + 1) * kQT + 16 * w, g, r, ldv, next_add);
         }
         f32x4 yacc[4];
