@@ -33,12 +33,10 @@ COMMON_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisib
 # VGPRs (their scores and products feed vector code right away; with AGPR
 # results every value would be copied out first), and are scheduled for
 # instruction-level parallelism (the chunked form ran 4% shorter, with
-# bit-identical results), as is the window kernel (1% shorter on the 8K
-# layer).  prefill_mfma_ilp.hip holds the prefill instances that run
-# faster under the iterative form of that scheduler.
+# bit-identical results).  prefill_mfma_ilp.hip holds the prefill
+# instances that run faster under the iterative form of that scheduler.
 SOURCE_FLAGS = {
     "prefill_backward_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-    "swa_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "prefill_mfma_ilp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
