@@ -334,3 +334,21 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libbased.so")
     with pytest.raises(ImportError):
         _lib.lib()
+
+
+def test_build_flags_name_existing_sources():
+    """Every per-source flag set in the build script names a source that is
+    compiled (a misspelt name would silently drop its flags), and the
+    packed-fp32 forms are off for all device code."""
+    from linear_attention_sequence_taylor_amd import build
+
+    sources = set(os.listdir(build.CSRC))
+    assert set(build.SOURCE_FLAGS) <= sources
+    assert all(name.endswith((".hip", ".cpp")) for name in build.SOURCE_FLAGS)
+    assert "-packed-fp32-ops" in build.DEVICE_FLAGS
+    # the scheduler choice per unit: the two hottest prefill instances under
+    # the iterative ILP scheduler, the bf16 gradients under max-ilp, the
+    # rest under the default one
+    assert "-amdgpu-sched-strategy=iterative-ilp" in build.SOURCE_FLAGS["prefill_mfma_ilp.hip"]
+    assert "-amdgpu-sched-strategy=max-ilp" in build.SOURCE_FLAGS["prefill_backward_mfma.hip"]
+    assert "prefill_mfma.hip" not in build.SOURCE_FLAGS
