@@ -10,6 +10,30 @@
 namespace based {
 namespace {
 
+// Inclusive prefix over segment slots, per head: slot s <- slot s-1 + slot s.
+// After it, slot s holds the state entering segment s.  Each thread owns one
+// 16-byte element of a slot and walks the segments eight at a time, all
+// eight loads issued before the adds and stores.
+__global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ ws, int nseg, int BH,
+                                                           size_t slot_floats) {
+    const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int head = blockIdx.y;
+    if (e >= slot_floats) return;
+    f32x4* p = reinterpret_cast<f32x4*>(ws + (size_t)head * slot_floats + e);
+    const size_t stride = (size_t)BH * slot_floats / 4;  // in f32x4
+    f32x4 run = p[0];
+    for (int s0 = 1; s0 < nseg; s0 += 8) {
+        f32x4 x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = s0 + i < nseg ? p[(size_t)(s0 + i) * stride] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            run += x[i];
+            if (s0 + i < nseg) p[(size_t)(s0 + i) * stride] = run;
+        }
+    }
+}
+
 // Launch shape.  Value columns are split into groups of `dvl` (each group
 // carries its own copy of the normaliser tile and recomputes the features),
 // and long sequences into segments, until there are enough workgroups for
