@@ -852,6 +852,41 @@ def test_hybrid_matches_oracle(B, H, L, window):
     report(f"hybrid B={B} H={H} L={L} w={window} z", ratio(z, zo), 2e-2)
 
 
+@pytest.mark.parametrize("L1,T,window", [(200, 24, 64), (37, 40, 64), (130, 16, 17)])
+def test_hybrid_prefill_then_layer_steps(L1, T, window):
+    """The serving path of one layer ("Simple linear attention language
+    models balance the recall-throughput tradeoff", App. B, Forward /
+    Generation Prefill then Next Token Prediction): based_hybrid_prefill
+    over the first L1 tokens, then swa_cache_fill of the window's ring, then
+    T per-token layer steps (based_decode_step on the prefill's state, and
+    swa_decode_step adding into its output).  Every output row, of the
+    prefill and of the steps, is compared with the oracle run over the whole
+    L1 + T tokens (linear attention plus the window, each normalised on its
+    own), and so is the state after the last step."""
+    based = based_mod()
+    B, H, L = 2, 3, L1 + T
+    q, k, v, qw, kw = _hybrid_inputs(B, H, L, seed=2900 + L1 + T + window)
+    scale = 0.125
+    yo, So, zo = oracle.la_recurrent(q, k, v)
+    want = yo + oracle.swa(qw, kw, v, window, scale)
+    qd, kd, vd, qwd, kwd = dev(q, k, v, qw, kw)
+    pre = [x[:, :, :L1].contiguous() for x in (qd, kd, qwd, kwd, vd)]
+    y1, S, z = based.based_hybrid_prefill(*pre, window=window, scale=scale)
+    kc, vc = based.swa_cache_fill(pre[3], pre[4], window=window)
+    steps = []
+    for t in range(L1, L):
+        pos = torch.full((B,), t, dtype=torch.int64, device=DEV)
+        y_la = based.based_decode_step(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(),
+                                       S, z)
+        steps.append(based.swa_decode_step(qwd[:, :, t].contiguous(), kwd[:, :, t].contiguous(),
+                                           vd[:, :, t].contiguous(), kc, vc, pos, scale=scale, add=y_la))
+    torch.cuda.synchronize()
+    got = torch.cat([y1.cpu(), torch.stack([y.cpu() for y in steps], dim=2)], dim=2)
+    report(f"hybrid prefill {L1} + {T} layer steps w={window} y", ratio(got, want), 2e-2)
+    report(f"hybrid prefill {L1} + {T} layer steps w={window} S", ratio(S, So), 2e-2)
+    report(f"hybrid prefill {L1} + {T} layer steps w={window} z", ratio(z, zo), 2e-2)
+
+
 @pytest.mark.parametrize("ws", ["auto", "none"])
 def test_hybrid_initial_state(ws):
     """A carried linear-attention state (fused); with no workspace the fused
