@@ -301,6 +301,97 @@ def test_prefill_graph_replay(L, H, d, dtype):
         torch.cuda.synchronize()
 
 
+def _replay_matches(g, outs, ref, reset=None, eager=None):
+    """Replay g three times: before each replay the outputs are poisoned
+    (and `reset` restores in-place state); after it every output must equal
+    the eager result bit for bit; eager work runs in between."""
+    for rep in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        if reset:
+            reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (got, want) in enumerate(zip(outs, ref)):
+            assert torch.equal(got, want), f"replay {rep}: output {i} differs from the eager result"
+        if eager:
+            eager()
+        torch.cuda.synchronize()
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up off the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def test_hybrid_and_backward_graph_replay():
+    """The multi-launch calls under HIP graph capture: the hybrid layer on
+    its segment plan (state pass, prefix, fused segment pass) and the
+    chunked gradients (segment sums, query sweep, key sweep), each with a
+    caller workspace; every replay equals the eager result bit for bit."""
+    based = based_mod()
+    B, H, L = 1, 4, 2048
+    q, k, v, qw, kw = dev(*_hybrid_inputs(B, H, L, seed=3100))
+    F = 1 + 16 + 16 * 16
+    y, S, z = (torch.empty(B, H, L, 64, device=DEV), torch.empty(B, H, F, 64, device=DEV),
+               torch.empty(B, H, F, device=DEV))
+    wsh = torch.empty(max(1, based.based_hybrid_prefill_workspace_bytes(B, H, L, 64)), dtype=torch.uint8, device=DEV)
+    run_h = lambda: based.based_hybrid_prefill(q, k, qw, kw, v, window=64, scale=0.125, y=y, S=S, z=z,  # noqa: E731
+                                               workspace=wsh)
+    ref = [t.clone() for t in run_h()]
+    _replay_matches(_capture(run_h), (y, S, z), ref, eager=lambda: based.based_prefill(q[:, :1], k[:, :1], v[:, :1]))
+
+    dy = torch.randn(B, H, L, 64, generator=torch.Generator().manual_seed(3101)).to(DEV)
+    dq, dk, dv = (torch.empty(B, H, L, 16, device=DEV), torch.empty(B, H, L, 16, device=DEV),
+                  torch.empty(B, H, L, 64, device=DEV))
+    wsb = torch.empty(based.based_prefill_backward_workspace_bytes(B, H, L, 64), dtype=torch.uint8, device=DEV)
+    run_b = lambda: based.based_prefill_backward(q, k, v, dy, form="chunked", dq=dq, dk=dk, dv=dv,  # noqa: E731
+                                                 workspace=wsb)
+    ref = [t.clone() for t in run_b()]
+    _replay_matches(_capture(run_b), (dq, dk, dv), ref, eager=lambda: based.based_prefill(q[:, :1], k[:, :1], v[:, :1]))
+
+
+def test_layer_step_graph_replay():
+    """One layer's next-token step under HIP graph capture: the linear
+    decode step (state updated in place, restored before each replay) and
+    the window step adding into its output (ring cache updated in place, the
+    same slot each replay)."""
+    based = based_mod()
+    B, H, L, window = 4, 8, 100, 64
+    q, k, v, qw, kw = dev(*_hybrid_inputs(B, H, L + 1, seed=3200))
+    _, S, z = based.based_prefill(q[:, :, :L].contiguous(), k[:, :, :L].contiguous(), v[:, :, :L].contiguous())
+    kc, vc = based.swa_cache_fill(kw[:, :, :L].contiguous(), v[:, :, :L].contiguous(), window=window)
+    S0, z0 = S.clone(), z.clone()
+    qt, kt, vt = (x[:, :, L].contiguous() for x in (q, k, v))
+    qwt, kwt = (x[:, :, L].contiguous() for x in (qw, kw))
+    pos = torch.full((B,), L, dtype=torch.int64, device=DEV)
+    y_la = torch.empty(B, H, 64, device=DEV)
+    y = torch.empty(B, H, 64, device=DEV)
+
+    def step():
+        based.based_decode_step(qt, kt, vt, S, z, y=y_la)
+        based.swa_decode_step(qwt, kwt, vt, kc, vc, pos, scale=0.125, add=y_la, y=y)
+
+    def reset():
+        S.copy_(S0)
+        z.copy_(z0)
+
+    step()
+    ref = [y.clone(), S.clone(), z.clone()]
+    g = _capture(step)  # the state is restored eagerly before each replay
+    _replay_matches(g, (y,), ref[:1], reset=reset)
+    assert torch.equal(S, ref[1]) and torch.equal(z, ref[2])
+
+
 def test_prefill_deterministic():
     based = based_mod()
     q, k, v = dev(*si.custom((2, 2, 300, 16), (2, 2, 300, 64), seed=800, scale=0.5))
