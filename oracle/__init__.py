@@ -57,6 +57,7 @@ def _load():
         lib.oracle_swa_cache_fill.argtypes = [P, P, I, I, I, I, I, P, P]
         lib.oracle_la_backward.argtypes = [P, P, P, P, I, I, I, I, D, P, P, P]
         lib.oracle_la_backward_recurrent.argtypes = [P, P, P, P, I, I, I, I, D, P, P, P]
+        lib.oracle_swa_backward.argtypes = [P, P, P, P, I, I, I, I, I, D, P, P, P]
         lib.oracle_swa_decode_step.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_longlong), I, I, I, I, D,
                                                P, P, P]
         _lib = lib
@@ -208,6 +209,23 @@ def la_backward(q, k, v, dy, eps: float = 1e-6):
     dk = np.empty_like(k)
     dvo = np.empty_like(v)
     _load().oracle_la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dy), BH, L, d, dv, eps, _ptr(dq), _ptr(dk), _ptr(dvo))
+    return dq, dk, dvo
+
+
+def swa_backward(q, k, v, dy, window: int = 64, scale: float | None = None):
+    """Gradients (dq, dk, dv) of swa(q, k, v, window, scale) for the upstream
+    gradient dy (shapes as the inputs and the output)."""
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    *lead, L, dqk = q.shape
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dvo = np.empty_like(v)
+    _load().oracle_swa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dy), BH, L, dqk, dv, int(window), float(scale),
+                                _ptr(dq), _ptr(dk), _ptr(dvo))
     return dq, dk, dvo
 
 

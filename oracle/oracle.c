@@ -295,6 +295,69 @@ void oracle_la_backward(const double *q, const double *k, const double *v, const
     }
 }
 
+/* Gradients of the sliding-window softmax output (oracle_swa) for an
+ * upstream gradient dy ([BASED s4 "Local Exact Attention"]; training-mode
+ * prefill, [BASED s5]).  With P_ij = exp(l_ij - m_i) / sum_j' exp(l_ij' - m_i)
+ * over the window of query i and l_ij = scale q_i . k_j, the chain rule
+ * through y_i = sum_j P_ij v_j gives
+ *   dv_j = sum_i P_ij dy_i,   dP_ij = dy_i . v_j,   D_i = sum_j P_ij dP_ij,
+ *   dl_ij = P_ij (dP_ij - D_i),
+ *   dq_i = scale sum_j dl_ij k_j,   dk_j = scale sum_i dl_ij q_i.
+ * q,k [BH,L,dqk], v,dy [BH,L,dv]. */
+void oracle_swa_backward(const double *q, const double *k, const double *v, const double *dy,
+                         int BH, int L, int dqk, int dv, int window, double scale,
+                         double *dq, double *dk, double *dv_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < BH; ++h) {
+        const double *qh = q + (size_t)h * L * dqk;
+        const double *kh = k + (size_t)h * L * dqk;
+        const double *vh = v + (size_t)h * L * dv;
+        const double *dyh = dy + (size_t)h * L * dv;
+        double *dqh = dq + (size_t)h * L * dqk;
+        double *dkh = dk + (size_t)h * L * dqk;
+        double *dvh = dv_out + (size_t)h * L * dv;
+        double *p = (double *)malloc(sizeof(double) * (size_t)(window > 0 ? window : 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(window > 0 ? window : 1));
+        for (size_t e = 0; e < (size_t)L * dqk; ++e) dqh[e] = dkh[e] = 0.0;
+        for (size_t e = 0; e < (size_t)L * dv; ++e) dvh[e] = 0.0;
+        for (int i = 0; i < L; ++i) {
+            const int j0 = i + 1 - window < 0 ? 0 : i + 1 - window;  /* first key in the window */
+            const int n = i - j0 + 1;
+            double m = -INFINITY;
+            for (int jj = 0; jj < n; ++jj) {
+                double dot = 0.0;
+                for (int e = 0; e < dqk; ++e) dot += qh[(size_t)i * dqk + e] * kh[(size_t)(j0 + jj) * dqk + e];
+                p[jj] = scale * dot;
+                if (p[jj] > m) m = p[jj];
+            }
+            double l = 0.0;
+            for (int jj = 0; jj < n; ++jj) {
+                p[jj] = exp(p[jj] - m);
+                l += p[jj];
+            }
+            double D = 0.0;
+            for (int jj = 0; jj < n; ++jj) {
+                p[jj] /= l;
+                double dot = 0.0;
+                for (int c = 0; c < dv; ++c) dot += dyh[(size_t)i * dv + c] * vh[(size_t)(j0 + jj) * dv + c];
+                dp[jj] = dot;
+                D += p[jj] * dot;
+            }
+            for (int jj = 0; jj < n; ++jj) {
+                const int j = j0 + jj;
+                const double dl = p[jj] * (dp[jj] - D) * scale;
+                for (int e = 0; e < dqk; ++e) {
+                    dqh[(size_t)i * dqk + e] += dl * kh[(size_t)j * dqk + e];
+                    dkh[(size_t)j * dqk + e] += dl * qh[(size_t)i * dqk + e];
+                }
+                for (int c = 0; c < dv; ++c) dvh[(size_t)j * dv + c] += p[jj] * dyh[(size_t)i * dv + c];
+            }
+        }
+        free(p);
+        free(dp);
+    }
+}
+
 /* J_phi(x)^T u: the gradient of sum_f u_f phi_f(x) with respect to the raw
  * vector x, for the feature map of oracle_taylor_features (x~ = x d^(-1/4);
  * d phi_lin[a] / dx_c = pre [a == c]; d phi_quad[a][b] / dx_c =

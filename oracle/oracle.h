@@ -118,6 +118,12 @@ void oracle_la_backward_recurrent(const double *q, const double *k, const double
 /* Number of OpenMP threads the routines above use. */
 int oracle_num_threads(void);
 
+/* Gradients (dq, dk, dv) of oracle_swa for the upstream gradient dy, by the
+ * chain rule through the window's softmax.  O(L w) per head. */
+void oracle_swa_backward(const double *q, const double *k, const double *v, const double *dy,
+                         int BH, int L, int dqk, int dv, int window, double scale,
+                         double *dq, double *dk, double *dv_out);
+
 #ifdef __cplusplus
 }
 #endif

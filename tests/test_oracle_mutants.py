@@ -53,6 +53,15 @@ MUTANTS = {
                                "oracle_taylor_features(kh + (size_t)j * d, d, phik);\n            for (int f = 0; f < F; ++f) {\n                double acc = z[f] - phiq[f] * gD[j];"),
     "rbwd_dv_from_query": ("for (int f = 0; f < F; ++f) acc += phik[f] * S[(size_t)f * dv + c];",
                            "for (int f = 0; f < F; ++f) acc += phiq[f] * S[(size_t)f * dv + c];"),
+    "swabwd_one_key_short": ("const int j0 = i + 1 - window < 0 ? 0 : i + 1 - window;",
+                             "const int j0 = i + 2 - window < 0 ? 0 : i + 2 - window;"),
+    "swabwd_no_D": ("const double dl = p[jj] * (dp[jj] - D) * scale;", "const double dl = p[jj] * dp[jj] * scale;"),
+    "swabwd_no_scale": ("const double dl = p[jj] * (dp[jj] - D) * scale;", "const double dl = p[jj] * (dp[jj] - D);"),
+    "swabwd_unnormalised": ("                p[jj] /= l;\n", ""),
+    "swabwd_dk_from_key": ("dkh[(size_t)j * dqk + e] += dl * qh[(size_t)i * dqk + e];",
+                           "dkh[(size_t)j * dqk + e] += dl * kh[(size_t)i * dqk + e];"),
+    "swabwd_dv_unweighted": ("dvh[(size_t)j * dv + c] += p[jj] * dyh[(size_t)i * dv + c];",
+                             "dvh[(size_t)j * dv + c] += dyh[(size_t)i * dv + c];"),
 }
 
 # pins that take only the oracle module
@@ -76,6 +85,9 @@ PIN_FUNCS = [
     pins.test_p10_recurrent_backward_equals_closed_form,
     pins.test_hand_taylor_cases,
     pins.test_hand_window_cases,
+    lambda m: pins.test_p11_window_backward_matches_autograd(m, 5, 16, 40),
+    pins.test_p11_window_backward_finite_differences,
+    pins.test_p11_window_backward_special_cases,
 ]
 
 

@@ -20,6 +20,9 @@ Which pin guards which part of the oracle:
       equals the library's band-masked softmax attention at each position
   P9  gradients: torch autograd through a plain fp64 forward, and central
       finite differences of the oracle's own forward
+  P11 window gradients: torch autograd through the library's band-masked
+      softmax attention, central finite differences of the oracle's window,
+      w = 1 (y = v), and the key-shift invariance of every row's softmax
   hand hand-worked rational cases in tests/golden/hand_cases.json
 """
 import json
@@ -451,3 +454,71 @@ def test_hand_window_cases(oracle_mod):
             want = np.array([_frac(x) for x in sub["y"]])
             got = oracle_mod.swa(q, k, v, window=sub["window"], scale=case["scale"])[0, 0, :, 0]
             np.testing.assert_allclose(got, want, rtol=1e-14)
+
+
+# ---------------------------------------------------------------- P11
+def _sdpa_band_torch(tq, tk, tv, window, scale):
+    L = tq.shape[-2]
+    i = torch.arange(L)[:, None]
+    j = torch.arange(L)[None, :]
+    allowed = (j <= i) & (j > i - window)
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=allowed, scale=scale)
+
+
+@pytest.mark.parametrize("window,dqk,L", [(64, 64, 150), (5, 16, 40), (1, 8, 12), (300, 16, 70)])
+def test_p11_window_backward_matches_autograd(oracle_mod, window, dqk, L):
+    """The library's softmax attention (band mask, fp64) differentiated by
+    autograd: an implementation of the forward that shares nothing with the
+    oracle's loops."""
+    rng = _rng(90 + window + dqk)
+    q = 2 * rng.standard_normal((2, 2, L, dqk))
+    k = 2 * rng.standard_normal((2, 2, L, dqk))
+    v = rng.standard_normal((2, 2, L, 7))
+    dy = rng.standard_normal((2, 2, L, 7))
+    scale = 1 / math.sqrt(dqk)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    (_sdpa_band_torch(tq, tk, tv, window, scale) * torch.from_numpy(dy)).sum().backward()
+    got = oracle_mod.swa_backward(q, k, v, dy, window, scale)
+    for g, want in zip(got, (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(g, want.numpy(), rtol=1e-9, atol=1e-11)
+
+
+def test_p11_window_backward_finite_differences(oracle_mod):
+    """Central differences of sum(y * dy), y from the oracle's own window
+    forward, at random coordinates of q, k and v."""
+    rng = _rng(91)
+    L, dqk, dv, window = 29, 8, 5, 6
+    q = rng.standard_normal((1, 1, L, dqk))
+    k = rng.standard_normal((1, 1, L, dqk))
+    v = rng.standard_normal((1, 1, L, dv))
+    dy = rng.standard_normal((1, 1, L, dv))
+    grads = dict(zip("qkv", oracle_mod.swa_backward(q, k, v, dy, window, 0.4)))
+    h = 1e-5
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        for _ in range(10):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            args_p, args_m = dict(q=q, k=k, v=v), dict(q=q, k=k, v=v)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p[name], args_m[name] = xp, xm
+            fd = (float((oracle_mod.swa(**args_p, window=window, scale=0.4) * dy).sum())
+                  - float((oracle_mod.swa(**args_m, window=window, scale=0.4) * dy).sum())) / (2 * h)
+            assert abs(fd - grads[name][idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grads[name][idx])
+
+
+def test_p11_window_backward_special_cases(oracle_mod):
+    """w = 1: every query sees only its own key, y = v, so dq = dk = 0 and
+    dv = dy exactly.  Any window: shifting every key by the same vector c
+    moves each row's logits by one constant (q_i . c), which the softmax
+    ignores, so the key gradients sum to zero over the sequence."""
+    rng = _rng(92)
+    q, k = rng.standard_normal((2, 1, 3, 33, 16))
+    v, dy = rng.standard_normal((2, 1, 3, 33, 10))
+    dq, dk, dv = oracle_mod.swa_backward(q, k, v, dy, 1, 0.25)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_array_equal(dv, dy)
+    for window in (2, 7, 33, 100):
+        dq, dk, dv = oracle_mod.swa_backward(q, k, v, dy, window, 0.25)
+        np.testing.assert_allclose(dk.sum(axis=-2), 0.0, atol=1e-12 * max(1.0, np.abs(dk).max()) * 33)
+        assert np.abs(dk).max() > 1e-3
