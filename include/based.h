@@ -22,6 +22,8 @@
  *                      Prediction").
  *   based_prefill_backward  gradients of the prefill output (training-mode
  *                      prefill, s5).
+ *   swa_backward       gradients of the window's output (s4 "Local Exact
+ *                      Attention"; training-mode prefill, s5).
  *
  * [1] "Simple linear attention language models balance the recall-throughput
  *     tradeoff" (arXiv 2402.18668v2).
@@ -332,6 +334,35 @@ based_status_t based_prefill_backward(const void *q, const void *k, const void *
                                       int L, int d_feat, int d_v, float eps, int form,
                                       float *dq, float *dk, float *dv, void *workspace,
                                       size_t workspace_bytes, void *stream);
+
+/*
+ * based_swa_backward -- gradients of swa_forward's output y (without the
+ * fused add, whose gradient is dy itself) for an upstream gradient dy
+ * (training-mode prefill; [1] s4 "Local Exact Attention", s5).  With
+ * P_ij = softmax_j(scale q_i.k_j) over j in (i - window, i], y_i =
+ * sum_j P_ij v_j:
+ *   dv_j = sum_i P_ij dy_i,   dP_ij = dy_i . v_j,   D_i = sum_j P_ij dP_ij,
+ *   dS_ij = P_ij (dP_ij - D_i),
+ *   dq_i = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i.
+ *
+ *   q, k  [B,H,L,d_qk] dtype;  v [B,H,L,d_v] dtype
+ *   dy    [B,H,L,d_v] fp32
+ *   dq, dk [B,H,L,d_qk] fp32 out;  dv [B,H,L,d_v] fp32 out
+ *   workspace  required, at least based_swa_backward_workspace_bytes (16
+ *          bytes per (batch, head, query): the row statistics the key side
+ *          reads), else BASED_E_INVALID; must not overlap anything else
+ * Supported: bf16 inputs, d_qk 64, d_v in {64, 128}, window 1..64 (else
+ * BASED_E_UNSUPPORTED); B*H*ceil(L/64)*256 must not exceed INT32_MAX (else
+ * BASED_E_INVALID).  Two launches on the bf16 matrix cores with fp32
+ * accumulation (the query side, then the key side); P, dS and dy enter the
+ * products as bf16 hi/lo pairs.
+ */
+size_t based_swa_backward_workspace_bytes(int B, int H, int L);
+
+based_status_t based_swa_backward(const void *q, const void *k, const void *v, const float *dy,
+                                  based_dtype_t dtype, int B, int H, int L, int d_qk, int d_v,
+                                  int window, float scale, float *dq, float *dk, float *dv,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

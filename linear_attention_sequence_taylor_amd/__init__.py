@@ -418,3 +418,42 @@ def based_prefill_backward(q, k, v, dy, *, eps: float = 1e-6, form: str = "auto"
     _lib.check("based_prefill_backward", st)
     return dq, dk, dv
 
+
+def swa_backward_workspace_bytes(B: int, H: int, L: int) -> int:
+    return _lib.lib().based_swa_backward_workspace_bytes(B, H, L)
+
+
+def swa_backward(q, k, v, dy, *, window: int = 64, scale: float | None = None, dq=None, dk=None, dv=None,
+                 workspace=None):
+    """Gradients (dq, dk, dv), fp32, of swa_forward's output for the upstream
+    gradient dy [B,H,L,d_v] (fp32): bf16 q, k [B,H,L,64], v [B,H,L,d_v]
+    with d_v 64 or 128, windows 1..64."""
+    _check_tensor("q", q, ndim=4)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor("k", k, dt, 4)
+    _check_tensor("v", v, dt, 4)
+    _check_tensor("dy", dy, torch.float32, 4)
+    B, H, L, d_qk = q.shape
+    d_v = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != (B, H, L) or dy.shape != v.shape:
+        raise ValueError("shape mismatch")
+    dev = q.device
+    _check_device(dev, k=k, v=v, dy=dy)
+    if scale is None:
+        scale = d_qk ** -0.5
+    dq = torch.empty((B, H, L, d_qk), dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty((B, H, L, d_qk), dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev) if dv is None else dv
+    _check_like("dq", dq, (B, H, L, d_qk), torch.float32, dev)
+    _check_like("dk", dk, (B, H, L, d_qk), torch.float32, dev)
+    _check_like("dv", dv, (B, H, L, d_v), torch.float32, dev)
+    if workspace is None:
+        workspace = torch.empty(max(swa_backward_workspace_bytes(B, H, L), 16), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = _workspace(workspace, dev)
+    st = _lib.lib().based_swa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr(), _DTYPES[dt], B, H, L,
+                                       d_qk, d_v, int(window), float(scale), dq.data_ptr(), dk.data_ptr(),
+                                       dv.data_ptr(), ws_ptr, ws_bytes, _stream_ptr(dev))
+    _lib.check("based_swa_backward", st)
+    return dq, dk, dv

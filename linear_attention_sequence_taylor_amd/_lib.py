@@ -34,6 +34,8 @@ SIGNATURES = {
                                   _I, _P, _S, _P]),
     "based_prefill_backward_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "based_prefill_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _S, _P]),
+    "based_swa_backward_workspace_bytes": (_S, [_I, _I, _I]),
+    "based_swa_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _S, _P]),
 }
 
 _lib = None

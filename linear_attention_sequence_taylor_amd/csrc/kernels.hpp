@@ -95,4 +95,13 @@ hipError_t launch_prefill_backward_chunked(const void* q, const void* k, const v
                                            int L, int dv, float eps, float* dq, float* dk, float* dvo,
                                            void* workspace, hipStream_t st);
 
+// Gradients of the sliding-window softmax (swa_backward.hip): bf16 inputs,
+// d_qk = 64, dv in {64, 128}, windows 1..64; dy fp32, outputs fp32.  The
+// workspace holds 16 bytes per (head, query) for the row statistics the key
+// side reads.
+size_t swa_backward_workspace_bytes(int BH, int L);
+hipError_t launch_swa_backward(const void* q, const void* k, const void* v, const float* dy, int BH, int L, int dv,
+                               int window, float scale, float* dq, float* dk, float* dvo, void* workspace,
+                               hipStream_t st);
+
 }  // namespace based

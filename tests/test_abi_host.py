@@ -41,6 +41,7 @@ def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for want in ("based_prefill", "based_decode_step", "swa_forward", "swa_cache_fill", "swa_decode_step",
                  "based_hybrid_prefill", "based_hybrid_prefill_workspace_bytes", "based_prefill_backward", "based_prefill_backward_workspace_bytes",
+                 "based_swa_backward", "based_swa_backward_workspace_bytes",
                  "based_num_features", "based_prefill_workspace_bytes", "based_status_string"):
         assert want in names, names
 
@@ -295,6 +296,32 @@ def _bwd(lib, **kw):
 @fake_addresses
 def test_backward_rejects(lib, kw, want):
     assert _bwd(lib, **kw) == want
+
+
+def _swabwd(lib, **kw):
+    a = dict(q=A, k=B_, v=C, dy=Y, dtype=1, B=1, H=2, L=100, dqk=64, dv=64, window=64, scale=0.125, dq=S,
+             dk=S + (1 << 20), dvo=S + (2 << 20), ws=Z, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.based_swa_backward(a["q"], a["k"], a["v"], a["dy"], a["dtype"], a["B"], a["H"], a["L"], a["dqk"],
+                                  a["dv"], a["window"], a["scale"], a["dq"], a["dk"], a["dvo"], a["ws"], a["wsb"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), 1), (dict(dy=None), 1), (dict(ws=None), 1), (dict(dq=S + 4), 1), (dict(wsb=100), 1),
+    (dict(dtype=5), 1), (dict(L=0), 1), (dict(scale=float("nan")), 1), (dict(window=0), 1),
+    (dict(dq=A), 1), (dict(dk=S), 1), (dict(ws=S + (2 << 20)), 1), (dict(dvo=Y), 1),
+    # well formed, outside what the kernels implement
+    (dict(dtype=0), 2), (dict(dqk=16), 2), (dict(dv=96), 2), (dict(window=65), 2),
+])
+@fake_addresses
+def test_swa_backward_rejects(lib, kw, want):
+    assert _swabwd(lib, **kw) == want
+
+
+def test_swa_backward_workspace_bytes(lib):
+    assert lib.based_swa_backward_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 16
+    assert lib.based_swa_backward_workspace_bytes(2, 3, 0) == 0
 
 
 def test_backward_workspace_bytes(lib):

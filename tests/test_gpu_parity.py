@@ -978,6 +978,45 @@ def test_hybrid_prefill_then_layer_steps(L1, T, window):
     report(f"hybrid prefill {L1} + {T} layer steps w={window} z", ratio(z, zo), 2e-2)
 
 
+@pytest.mark.parametrize("B,H,L", [(1, 2, 1), (2, 1, 37), (1, 3, 130), (2, 2, 333)])
+@pytest.mark.parametrize("window", [64, 17, 1])
+@pytest.mark.parametrize("dv", [64, 128])
+def test_swa_backward_matches_oracle(B, H, L, window, dv):
+    """Gradients of the window (bf16, d_qk = 64) against the oracle's chain
+    rule through the softmax: one token, ragged tails, one and several
+    64-row tiles, windows of 64, 17 and 1 keys (w = 1: dq = dk = 0,
+    dv = dy)."""
+    based = based_mod()
+    q, k, v = si.custom((B, H, L, 64), (B, H, L, dv), seed=3300 + L + window + dv, scale=1.0)
+    dy = torch.randn(B, H, L, dv, generator=torch.Generator().manual_seed(3301 + L))
+    a = based.swa_backward(*dev(q, k, v, dy), window=window, scale=0.125)
+    b = based.swa_backward(*dev(q, k, v, dy), window=window, scale=0.125)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    want = oracle.swa_backward(q, k, v, dy, window, 0.125)
+    for name, got, w in zip(("dq", "dk", "dv"), a, want):
+        if not np.any(w):
+            assert not torch.any(got), name  # w = 1: exactly zero
+            continue
+        report(f"swa backward B={B} H={H} L={L} w={window} dv={dv} {name}", ratio(got, w), 2e-2)
+
+
+def test_swa_backward_window_8k_heads():
+    """The 8K layer's window branch (L = 8192, d_qk = d_v = 64, w = 64) on
+    four heads, every element against the oracle."""
+    based = based_mod()
+    wl = si.WORKLOADS["window_8k"]
+    _, _, v = si.linear_inputs(wl, B=1, H=4)
+    q, k = si.window_inputs(wl, B=1, H=4)
+    dy = torch.randn(1, 4, wl.L, wl.dv, generator=torch.Generator().manual_seed(3302))
+    got = based.swa_backward(*dev(q, k, v, dy), window=wl.window, scale=wl.swa_scale)
+    torch.cuda.synchronize()
+    want = oracle.swa_backward(q, k, v, dy, wl.window, wl.swa_scale)
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        report(f"swa backward 8K layer (4 heads) {name}", ratio(g, w), 2e-2)
+
+
 @pytest.mark.parametrize("ws", ["auto", "none"])
 def test_hybrid_initial_state(ws):
     """A carried linear-attention state (fused); with no workspace the fused
