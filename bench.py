@@ -32,8 +32,8 @@ time.  Rank 0 prints one JSON line with:
   setup prefill at d_v = 128, then 1024 next-token steps), the 8K window
   layer (linear branch, window branch with fused add, the fused hybrid
   layer), the 64K prefill, the tiny fp32 layer, the window's next-token
-  step, the gradients of the prefill and the other feature dims and window
-  sizes.
+  step, the gradients of the prefill and of the window, and the other
+  feature dims and window sizes.
 """
 from __future__ import annotations
 
@@ -663,6 +663,37 @@ def bench_backward(based, wl, form: str, n: int):
     return time_leg(backward_sets(based, wl, form), n, settle_s=0.1, dist_n=10)
 
 
+def swa_backward_bytes(wl) -> int:
+    """Algorithmic HBM bytes of the window's gradients: q, k, v (bf16) and dy
+    (fp32) read once, dq, dk, dv (fp32) written once."""
+    return wl.B * wl.H * wl.L * (2 * (2 * wl.d_qk + wl.dv) + 4 * wl.dv + 4 * (2 * wl.d_qk + wl.dv))
+
+
+def swa_backward_flops(wl) -> int:
+    """Algorithmic flops of the window's gradients: per (query, key) pair
+    inside the window, the score, dy . v, and the dq, dk, dv updates
+    (2 flop per multiply-add each: 6 d_qk + 4 d_v)."""
+    pairs = sum(min(wl.window, i + 1) for i in range(wl.L))
+    return wl.B * wl.H * pairs * (6 * wl.d_qk + 4 * wl.dv)
+
+
+def bench_swa_backward(based, wl, n: int):
+    """Mean seconds per window-gradient call and the per-call distribution."""
+    _, _, v = si.linear_inputs(wl)
+    q, k = si.window_inputs(wl)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    dy = torch.randn(wl.B, wl.H, wl.L, wl.dv, generator=torch.Generator().manual_seed(2301)).cuda()
+    outs = (torch.empty(wl.B, wl.H, wl.L, wl.d_qk, device="cuda"), torch.empty(wl.B, wl.H, wl.L, wl.d_qk, device="cuda"),
+            torch.empty(wl.B, wl.H, wl.L, wl.dv, device="cuda"))
+    ws = torch.empty(based.swa_backward_workspace_bytes(wl.B, wl.H, wl.L), dtype=torch.uint8, device="cuda")
+
+    def fn(i):
+        based.swa_backward(q, k, v, dy, window=wl.window, scale=wl.swa_scale, dq=outs[0], dk=outs[1], dv=outs[2],
+                           workspace=ws)
+
+    return time_leg(fn, n, settle_s=0.1, dist_n=10)
+
+
 def _oracle():
     import oracle
 
@@ -1076,6 +1107,15 @@ def main():
                 extra["layer_1p3b_backward"] = leg
             else:
                 extra[f"{bname}_backward"] = leg
+        ww8 = si.WORKLOADS["window_8k"]
+        wsec, wdist = bench_swa_backward(based, ww8, 100)
+        extra["window_8k_backward"] = {
+            "kernel_us": wsec * 1e6, "tokens_per_s": ww8.B * ww8.L / wsec, "dist_us": wdist,
+            "roofline": roofline(swa_backward_bytes(ww8), wsec, None, swa_backward_flops(ww8)),
+            "note": "dq, dk, dv of the w=64 window of the 8K layer (B=4, H=16, L=8192, d_qk=d_v=64) for a seeded "
+                    "dy: query side then key side on the bf16 matrix cores, P, dS and dy as bf16 hi/lo pairs; "
+                    "flops are the window-exact pairs' (swa_backward_flops)"}
+        print(f"[bench] window backward window_8k: {wsec*1e6:.1f} us", file=sys.stderr, flush=True)
         oth = bench_other_sizes(based)
         extra.update(oth)
         print("[bench] other sizes: " + ", ".join(f"{k} {v['kernel_us']:.1f} us" for k, v in oth.items()),

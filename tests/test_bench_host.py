@@ -107,6 +107,17 @@ def test_backward_counts():
     assert bench.backward_flops(wl, "chunked") == pytest.approx(chunked, rel=1e-12)
 
 
+def test_window_backward_counts():
+    wl = si.WORKLOADS["window_8k"]
+    # q, k (64 bf16 each), v (64 bf16) and dy (64 fp32) read; dq, dk (64 fp32 each), dv (64 fp32) written
+    per_tok = (64 + 64 + 64) * 2 + 64 * 4 + (64 + 64 + 64) * 4
+    assert per_tok == 1408
+    assert bench.swa_backward_bytes(wl) == 4 * 16 * 8192 * 1408
+    # window-exact pairs: 1 + 2 + ... + 64 for the first 64 queries, then 64 each
+    pairs = 64 * 65 // 2 + (8192 - 64) * 64
+    assert bench.swa_backward_flops(wl) == 4 * 16 * pairs * (6 * 64 + 4 * 64)
+
+
 def test_read_traffic(tmp_path):
     p = tmp_path / "summary.txt"
     p.write_text("# a comment: with a colon\n"
