@@ -677,8 +677,9 @@ def swa_backward_flops(wl) -> int:
     return wl.B * wl.H * pairs * (6 * wl.d_qk + 4 * wl.dv)
 
 
-def bench_swa_backward(based, wl, n: int):
-    """Mean seconds per window-gradient call and the per-call distribution."""
+def swa_backward_sets(based, wl):
+    """One window-gradient call over the workload (bf16 q, k, v, a seeded
+    fp32 dy), as fn(i) for time_leg."""
     _, _, v = si.linear_inputs(wl)
     q, k = si.window_inputs(wl)
     q, k, v = q.cuda(), k.cuda(), v.cuda()
@@ -691,7 +692,12 @@ def bench_swa_backward(based, wl, n: int):
         based.swa_backward(q, k, v, dy, window=wl.window, scale=wl.swa_scale, dq=outs[0], dk=outs[1], dv=outs[2],
                            workspace=ws)
 
-    return time_leg(fn, n, settle_s=0.1, dist_n=10)
+    return fn
+
+
+def bench_swa_backward(based, wl, n: int):
+    """Mean seconds per window-gradient call and the per-call distribution."""
+    return time_leg(swa_backward_sets(based, wl), n, settle_s=0.1, dist_n=10)
 
 
 def _oracle():
@@ -829,6 +835,19 @@ def cpu_legs() -> dict:
     return out
 
 
+# gradient legs with a counter summary: leg name -> (workload, form)
+BACKWARD_PROFILE_LEGS = {"backward_360m": ("prefill_360m", "chunked"), "backward_360m_direct": ("prefill_360m", "direct"),
+                         "backward_64k": ("long_64k", "chunked"), "backward_1p3b": ("decode_1p3b", "chunked"),
+                         "backward_1p3b_direct": ("decode_1p3b", "direct")}
+BACKWARD_SOURCES = ("prefill_backward_mfma.hip", "common.hpp")
+
+
+def backward_summary(wname: str, form: str) -> str:
+    """Name of the counter summary of one gradient leg."""
+    leg = next(k for k, v in BACKWARD_PROFILE_LEGS.items() if v == (wname, form))
+    return f"prefill_backward_mfma_{leg}_pmc.txt"
+
+
 def profile_leg(name: str, launches: int = 8) -> None:
     """Launches of one leg's library call, untimed, for counter passes: each
     dispatch of the call's kernels is one launch of that call."""
@@ -856,9 +875,11 @@ def profile_leg(name: str, launches: int = 8) -> None:
 
         def step(i):
             based.based_decode_step(*steps[i % 4], S, z, eps=wl.eps)
-    elif name in ("backward_360m", "backward_64k"):
-        wl = si.WORKLOADS["prefill_360m" if name == "backward_360m" else "long_64k"]
-        step = backward_sets(based, wl, "chunked")
+    elif name in BACKWARD_PROFILE_LEGS:
+        wname, form = BACKWARD_PROFILE_LEGS[name]
+        step = backward_sets(based, si.WORKLOADS[wname], form)
+    elif name == "window_backward_8k":
+        step = swa_backward_sets(based, si.WORKLOADS["window_8k"])
     elif name == "window_8k":
         wl = si.WORKLOADS["window_8k"]
         qw, kw = si.window_inputs(wl)
@@ -906,7 +927,7 @@ def main():
     ap.add_argument("--window-decode-steps", type=int, default=4096)
     ap.add_argument("--profile-leg", default=None,
                     choices=["prefill_360m", "long_64k", "hybrid_8k", "decode_1p3b", "window_8k", "window_decode_1p3b",
-                             "setup_1p3b", "linear_8k", "backward_360m", "backward_64k"],
+                             "setup_1p3b", "linear_8k", "window_backward_8k", *BACKWARD_PROFILE_LEGS],
                     help="only launch one leg's kernels a few times (untimed), for rocprofv3 counter passes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to calibrate "
@@ -1075,9 +1096,14 @@ def main():
         wd3 = si.WORKLOADS["decode_1p3b"]
         lsec = bench_layer_decode(based, wd3, wwd, 256)
         lb = decode_bytes(wd3) + window_decode_bytes(wwd)
+        # the layer step's launches are the two legs' launches, so its counter
+        # traffic is the sum of their summaries' (None if either is stale)
+        lparts = (read_traffic("decode_step_decode_1p3b_pmc.txt", source_digest("decode.hip", "common.hpp")),
+                  read_traffic("swa_decode_window_decode_1p3b_pmc.txt", source_digest("swa_decode.hip", "common.hpp")))
+        ltraffic = None if None in lparts else sum(lparts)
         extra["layer_decode_1p3b"] = {
             "tokens_per_s": wd3.B / lsec, "layer_step_us": lsec * 1e6, "steps": 256,
-            "roofline": roofline(lb, lsec),
+            "roofline": roofline(lb, lsec, ltraffic),
             "note": "one BASED-1.3B layer's next-token step: the linear-attention step (fp32 state 273x128 per "
                     "head, read and written once) then the w=64 window step on the same token adding into its "
                     "output; B=128, H=16; HIP graph of 64 layer steps replayed 4 times; bytes are the two "
@@ -1089,10 +1115,7 @@ def main():
             leg = {}
             for form in forms:
                 bsec, bdist = bench_backward(based, bw, form, 100 if bname == "prefill_360m" else 30)
-                traffic = None
-                if form == "chunked" and bname != "decode_1p3b":
-                    traffic = read_traffic(f"prefill_backward_mfma_{'backward_360m' if bname == 'prefill_360m' else 'backward_64k'}"
-                                           "_pmc.txt", source_digest("prefill_backward_mfma.hip", "common.hpp"))
+                traffic = read_traffic(backward_summary(bname, form), source_digest(*BACKWARD_SOURCES))
                 leg[form] = {"kernel_us": bsec * 1e6, "tokens_per_s": bw.B * bw.L / bsec, "dist_us": bdist,
                              "roofline": roofline(backward_bytes(bw), bsec, traffic, backward_flops(bw, form))}
                 print(f"[bench] backward {bname} {form}: {bsec*1e6:.1f} us", file=sys.stderr, flush=True)
@@ -1111,7 +1134,9 @@ def main():
         wsec, wdist = bench_swa_backward(based, ww8, 100)
         extra["window_8k_backward"] = {
             "kernel_us": wsec * 1e6, "tokens_per_s": ww8.B * ww8.L / wsec, "dist_us": wdist,
-            "roofline": roofline(swa_backward_bytes(ww8), wsec, None, swa_backward_flops(ww8)),
+            "roofline": roofline(swa_backward_bytes(ww8), wsec,
+                                 read_traffic("swa_backward_window_8k_pmc.txt", source_digest("swa_backward.hip", "common.hpp")),
+                                 swa_backward_flops(ww8)),
             "note": "dq, dk, dv of the w=64 window of the 8K layer (B=4, H=16, L=8192, d_qk=d_v=64) for a seeded "
                     "dy: query side then key side on the bf16 matrix cores, P, dS and dy as bf16 hi/lo pairs; "
                     "flops are the window-exact pairs' (swa_backward_flops)"}
