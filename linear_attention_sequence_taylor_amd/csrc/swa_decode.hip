@@ -39,6 +39,7 @@ template <>
 struct Chunk8<uint16_t> {
     u32x4 u;
     __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<u32x4*>(p) = u; }
     __device__ __forceinline__ void zero() { u = u32x4{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ float get(int i) const {
         return (i & 1) ? bf16hi_f32(u[i >> 1]) : bf16lo_f32(u[i >> 1]);
@@ -62,6 +63,10 @@ struct Chunk8<float> {
     __device__ __forceinline__ void load(const float* p) {
         a = *reinterpret_cast<const f32x4*>(p);
         b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ void store(float* p) const {
+        *reinterpret_cast<f32x4*>(p) = a;
+        *reinterpret_cast<f32x4*>(p + 4) = b;
     }
     __device__ __forceinline__ void zero() { a = b = f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ __forceinline__ float get(int i) const { return i < 4 ? a[i] : b[i - 4]; }
@@ -242,7 +247,6 @@ __global__ __launch_bounds__(256) void swa_decode_split_kernel(const T* __restri
     constexpr int kDPL = DQK / kP;           // dims per lane in the scores
     constexpr int kQC = kDPL / 8;            // chunks of 8 dims per lane
     constexpr int kCG = DV / 8, kKG = 64 / kCG, kKPL = kSPW / kKG;
-    constexpr int kKU = DQK * sizeof(T) / 16, kVU = DV * sizeof(T) / 16;
     __shared__ float part_acc[4][DV];
     __shared__ float part_ml[4][2];
     const int lane = threadIdx.x & 63;
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(256) void swa_decode_split_kernel(const T* __restri
 
     // ---- loads, all issued before the position is known (slots past the
     // ring read its last row and are discarded below)
-    const long long p = pos[head / H];
+    const long long p = pos[blockIdx.x / (unsigned)H];  // 32-bit division: the grid is B * H < 2^31
     const int j = base + sl;  // this lane's slot in the scores
     Chunk8<T> qr[kQC], kr[kQC], knr[kQC], vr[kKPL], vnr;
 #pragma unroll
@@ -356,9 +360,15 @@ __global__ __launch_bounds__(256) void swa_decode_split_kernel(const T* __restri
         *reinterpret_cast<f32x4*>(yh + 8 * cg) = o0;
         *reinterpret_cast<f32x4*>(yh + 8 * cg + 4) = o1;
     }
+    // the new token into its slot, from the registers every wave loaded it
+    // into (lanes s = 0 hold the key's pieces, lanes kg = 0 the value's), so
+    // the last step of the workgroup waits on no load
     if (w == 1) {
-        copy_units(kn, kch + (size_t)slot_new * DQK, kKU, lane);
-        copy_units(vn, vch + (size_t)slot_new * DV, kVU, lane);
+        if (sl == 0) {
+#pragma unroll
+            for (int c = 0; c < kQC; ++c) knr[c].store(kch + (size_t)slot_new * DQK + 8 * (pp + kP * c));
+        }
+        if (kg == 0) vnr.store(vch + (size_t)slot_new * DV + 8 * cg);
     }
 }
 
