@@ -148,6 +148,16 @@ def test_committed_summaries_are_readable():
         assert bench.read_traffic(n, digest) == float(vals["hbm_bytes_per_launch"]) > 0, n
 
 
+def test_every_gradient_leg_has_a_summary():
+    """Each gradient leg that bench.py can profile has a committed counter
+    summary under the name the bench reads, and the window gradients too."""
+    for wname, form in bench.BACKWARD_PROFILE_LEGS.values():
+        n = bench.backward_summary(wname, form)
+        assert os.path.exists(os.path.join(bench.PROFILES, n)), n
+    assert os.path.exists(os.path.join(bench.PROFILES, "swa_backward_window_8k_pmc.txt"))
+    assert bench.backward_summary("prefill_360m", "chunked") == "prefill_backward_mfma_backward_360m_pmc.txt"
+
+
 def test_source_digest_shape():
     d = bench.source_digest("prefill_mfma.hip")
     assert len(d) == 16 and d != bench.source_digest("decode.hip")
